@@ -1,0 +1,255 @@
+/*
+ * qmm.h -- C ABI of the quantized projection matmul library (libqmm.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the quantized projection matmul of a decoder LLM:
+ *   - an int8 x int8 product with int32 accumulation and the zero-point
+ *     correction epilogue, plus optional bias, requantisation or fp32 output;
+ *   - per-column int8 weight packing (scale = amax/127) and per-row int8
+ *     activation quantisation;
+ *   - 4-bit q4_1 block weights (bf16 scale and min per 32 values) decoded
+ *     inside the kernels, including the mixture-of-experts form that reads
+ *     top-k expert ids through a strided view.
+ *
+ * Sources (web pages, by title and section):
+ *  [P1] "The ONNX pack: weights to Q4NX, matmuls to our kernels, no VitisAI"
+ *  [P2] "int8 inference" (onemodel docs), "Product kernel (Int8Gemm)"
+ *  [P4] "NPU engine: full ELFs, no xclbin", "Q4NX chunks"
+ *  [P5] "Zaya 8B Q4NX on the AMD NPU"
+ *
+ * Common rules for every entry point:
+ *   - Pointers named as device pointers refer to GPU memory owned by the
+ *     caller; the library never frees or retains them after the call.
+ *   - Matrices are row-major with an explicit leading dimension in elements.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     call only enqueues work on it and returns; nothing synchronises unless
+ *     stated.
+ *   - All arguments are checked on the host before anything is enqueued.  On
+ *     an error status nothing is enqueued and no output is written.
+ *   - QMM_ERR_UNSUPPORTED means well-formed but not covered (the caller is
+ *     expected to fall back, as the pages' execution provider does for a
+ *     shape it has no kernel for: [P1] "What the graph gives us").
+ *   - Results do not depend on the launch configuration: integer outputs are
+ *     exact, and floating-point outputs are bitwise reproducible run to run.
+ *   - The library keeps no state between calls and allocates no device
+ *     memory; calls on different streams may run concurrently as long as they
+ *     do not share an output or a workspace.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QMM_OK = 0,
+    QMM_ERR_INVALID = 1,     /* null pointer, bad size, ld < width, bad zero point   */
+    QMM_ERR_UNSUPPORTED = 2, /* valid but not covered (e.g. q4_1 with K % 32 != 0)   */
+    QMM_ERR_WORKSPACE = 3,   /* workspace or packed buffer smaller than required     */
+    QMM_ERR_HIP = 4          /* a HIP launch failed; see qmm_last_hip_error()         */
+} qmm_status;
+
+typedef enum { QMM_S8 = 0, QMM_U8 = 1 } qmm_i8type;
+
+/* Output selectors for qmm_epilogue.outputs (bitwise OR). */
+enum {
+    QMM_OUT_I32 = 1, /* corrected int32 accumulator                               */
+    QMM_OUT_F32 = 2, /* fp32: Y * row_scale[m] * col_scale[n] * scale + bias_f32[n] */
+    QMM_OUT_I8 = 4,  /* requantised int8                                          */
+    QMM_OUT_U8 = 8   /* requantised uint8 (exclusive with QMM_OUT_I8)             */
+};
+
+/*
+ * Epilogue of int8_gemm ([P2] "Product kernel": zero-point correction,
+ * optional bias, requantisation or float conversion; [P1] "Why it folds
+ * without a new kernel" and "What works today": per-axis scales land in the
+ * same epilogue, the output scale folds into one multiply per element, the
+ * result rounds half to even and the output zero point is added after
+ * rounding).
+ *
+ * With Y the corrected int32 accumulator (wrapping int32 arithmetic) and
+ *   mult = fl32(fl32(rs[m] * cs[n]) * scale)   (rs = row_scale or 1,
+ *                                               cs = col_scale or the packed
+ *                                               weight's column scales)
+ * the outputs are
+ *   I32 : y_i32[m*ld_i32 + n] = Y
+ *   F32 : y_f32[m*ld_f32 + n] = fl32(Y) * mult + bias_f32[n]      (bias 0 if NULL)
+ *   I8/U8: acc = Y + bias_i32[n] (int32);  v = fl32(fl32(acc) * mult);
+ *          y_q8[m*ld_q8 + n] = clamp(rne(v) + zp_out, -128..127 or 0..255)
+ * Any combination of I32, F32 and one of I8/U8 may be requested at once.
+ */
+typedef struct {
+    uint32_t outputs;
+    int32_t *y_i32;          /* device, M x N, used with QMM_OUT_I32          */
+    int64_t ld_i32;
+    float *y_f32;            /* device, M x N, used with QMM_OUT_F32          */
+    int64_t ld_f32;
+    void *y_q8;              /* device, M x N int8/uint8, with QMM_OUT_I8/U8  */
+    int64_t ld_q8;
+    const float *row_scale;  /* device [M] or NULL (= 1)                      */
+    const float *col_scale;  /* device [N] or NULL (= packed column scales)   */
+    float scale;             /* per-tensor factor (e.g. s_x*s_w/s_y)          */
+    const float *bias_f32;   /* device [N] or NULL; F32 output only           */
+    const int32_t *bias_i32; /* device [N] or NULL; I8/U8 output only         */
+    int32_t zp_out;          /* I8: -128..127, U8: 0..255                     */
+} qmm_epilogue;
+
+/* ------------------------------------------------------ int8 weight pack --- */
+
+/* Bytes of a packed int8 weight buffer for a K x N weight. */
+size_t qmm_pack_b_int8_bytes(int64_t K, int64_t N);
+
+/*
+ * pack_b_int8: [P1] "The three layers of the pack": quantise each weight
+ * column to int8 with scale = amax/127 and store the column scales alongside
+ * the packed buffer; done once per (tensor, K, N).
+ *   W       device fp32 K x N, leading dimension ldw >= N (one column per
+ *           output feature n).
+ *   packed  device buffer of at least qmm_pack_b_int8_bytes(K, N) bytes,
+ *           256-byte aligned.  Receives a 64-byte header, the codes in the
+ *           library's tile layout, fp32 scale[N] and int32 colsum[N].
+ * Per column: s = fl32(amax/127), q = clamp(rne(fl32(w/s)), -127, 127); an
+ * all-zero column gets s = 0 and codes 0; colsum[n] = sum_k q.
+ */
+qmm_status pack_b_int8(const float *W, int64_t K, int64_t N, int64_t ldw,
+                       void *packed, size_t packed_bytes, void *stream);
+
+/*
+ * pack_b_int8_raw: pack an already-quantised int8/uint8 weight ([P2]
+ * "Product kernel": B is stored as int8 and a uint8 B is shifted by 128).
+ * Codes are B (int8) or B - 128 (uint8); scales are 1; colsum is the sum of
+ * the shifted codes ([P1] "What works today": the weight column sum is
+ * computed once and kept).
+ */
+qmm_status pack_b_int8_raw(const void *B, qmm_i8type bt, int64_t K, int64_t N, int64_t ldb,
+                           void *packed, size_t packed_bytes, void *stream);
+
+/*
+ * qmm_packed_b_check: synchronously read the header of a packed buffer and
+ * check that it was written by this layout version for this K and N
+ * (QMM_ERR_INVALID otherwise).  Optional; int8_gemm does not read the header.
+ */
+qmm_status qmm_packed_b_check(const void *packed, int64_t K, int64_t N, void *stream);
+
+/*
+ * quantize_rows_int8: [P1] "The three layers of the pack", item 2: every
+ * matmul input is quantised per row with amax/127.
+ *   X  device fp32 M x K (ldx >= K);  Xq device int8 M x K (ldq >= K);
+ *   row_scale device fp32 [M].  Same rule as pack_b_int8, along rows.
+ */
+qmm_status quantize_rows_int8(const float *X, int64_t M, int64_t K, int64_t ldx,
+                              int8_t *Xq, int64_t ldq, float *row_scale, void *stream);
+
+/* ----------------------------------------------------------- int8 GEMM --- */
+
+/* Workspace bytes int8_gemm needs for an M x K x N product (may be 0). */
+size_t qmm_int8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/*
+ * int8_gemm: [P2] "Product kernel (Int8Gemm)":
+ *   S[m,n] = sum_k A'[m,k] * B'[k,n]        (int32; primes = shifted domain,
+ *                                            A' = A - 128 for uint8 A)
+ *   Y[m,n] = S - zA'*colSum[n] - zB'*(rowSum[m] - K*zA')
+ * which equals sum_k (A[m,k]-zA)(B[k,n]-zB) exactly whenever that value fits
+ * in int32 (always for K <= 33025), then the epilogue above.
+ *   A        device, M x K int8 or uint8 (at), leading dimension lda >= K.
+ *   zA       activation zero point in at's range.
+ *   packedB  buffer written by pack_b_int8 / pack_b_int8_raw for this K, N.
+ *   bt       element type the packed weight was given in (QMM_S8 for
+ *            pack_b_int8); zB is in that type's range.
+ *   workspace  device, >= qmm_int8_gemm_workspace_bytes(M,K,N) bytes, 256-byte
+ *            aligned, ZERO-FILLED before its first use.  Its first 64 KiB
+ *            hold split-K arrival counters that every call returns to zero;
+ *            the rest is scratch.  So one workspace serves any sequence of
+ *            calls, whatever their shapes, without clearing.  Calls that
+ *            overlap in time must not share a workspace.  Needs N <= 262144
+ *            when the size query is non-zero (else QMM_ERR_UNSUPPORTED).
+ * K must satisfy K*255*128 < 2^31 ([P2]: the sums cannot overflow below that
+ * bound), else QMM_ERR_UNSUPPORTED.  M = 0 or N = 0 is a no-op.
+ */
+qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t lda, int32_t zA,
+                     const void *packedB, qmm_i8type bt, int64_t N, int32_t zB,
+                     const qmm_epilogue *ep, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* ---------------------------------------------------------------- q4_1 --- */
+
+/*
+ * Canonical q4_1 block ([P4] "Q4NX chunks"; [P5] "Round 26": W = q*scale +
+ * min with bf16 scale and min per (row, 32-col) block): 32 consecutive k of
+ * one output column n, 20 bytes:
+ *   bytes 0-1  d  (bf16, little endian), bytes 2-3  m (bf16),
+ *   bytes 4-19 codes: byte j holds element j (low nibble) and j+16 (high).
+ * value(k) = q(k) * d + m.  A K x N weight is the array blocks[N][K/32].
+ */
+#define QMM_Q4_1_BLOCK_BYTES 20
+
+/* Bytes of the device layout of a K x N q4_1 weight. */
+size_t qmm_q4_1_packed_bytes(int64_t K, int64_t N);
+
+/*
+ * q4_1_repack: copy canonical blocks (device, [N][K/32] x 20 bytes) into the
+ * library's tile layout (layout only, no arithmetic; [P5] "Milestones": one
+ * raw blob plus a tile-major layout read by the kernel).  K % 32 != 0 gives
+ * QMM_ERR_UNSUPPORTED.
+ */
+qmm_status q4_1_repack(const void *blocks, int64_t K, int64_t N,
+                       void *packed, size_t packed_bytes, void *stream);
+
+/* Workspace bytes q4_1_matmul needs for M rows. */
+size_t qmm_q4_1_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/*
+ * q4_1_matmul: Y[m,n] = sum_k X[m,k] * (q[k,n]*d + m) with X fp32 (M x K,
+ * ldx >= K), the weight in the layout written by q4_1_repack, Y fp32 (M x N,
+ * ldy >= N).  Codes are decoded inside the kernel and kept exact; the
+ * relative Frobenius error against exact arithmetic is below 1e-5.
+ * workspace: device, >= qmm_q4_1_matmul_workspace_bytes(M,K,N), zero-filled
+ * before its first use (same counter-region rule as int8_gemm).
+ */
+qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx,
+                       const void *Wpacked, int64_t N, float *Y, int64_t ldy,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes q4_1_matmul_id needs. */
+size_t qmm_q4_1_matmul_id_workspace_bytes(int64_t n_tokens, int64_t n_used, int64_t n_expert,
+                                          int64_t K, int64_t N);
+
+/*
+ * q4_1_matmul_id: MUL_MAT_ID over stacked q4_1 experts ([P5] "The bugs that
+ * were the work": the ids are a strided view and must be read through the
+ * stride; "What's next": the shared activation form [k, ntokens]).
+ * For t < n_tokens and s < n_used:
+ *   e = ids[t*ids_row_stride + s];   Y[t*ldy_token + s*ldy_slot + n] = X[t] . W_e[:, n]
+ *   X         device fp32 n_tokens x K (ldx >= K)
+ *   Wexperts  device, n_expert weights in the q4_1_repack layout, expert e
+ *             at byte offset e*expert_stride (>= qmm_q4_1_packed_bytes(K,N))
+ *   ids       device int32, row stride ids_row_stride >= n_used; every used
+ *             id must lie in [0, n_expert) (a precondition: not checked)
+ * Tokens routed to each expert are grouped on the device (counting sort) and
+ * run in one grouped launch.  workspace: zero-filled before its first use
+ * (same counter-region rule as int8_gemm).
+ */
+qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t ldx,
+                          const void *Wexperts, int64_t n_expert, int64_t N, size_t expert_stride,
+                          const int32_t *ids, int64_t ids_row_stride, int64_t n_used,
+                          float *Y, int64_t ldy_slot, int64_t ldy_token,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------- helpers --- */
+
+const char *qmm_status_string(qmm_status s);
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int qmm_last_hip_error(void);
+/* Name of the kernel variant the last call on this thread launched
+ * (diagnostics; "" before the first call). */
+const char *qmm_last_variant(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMM_H */

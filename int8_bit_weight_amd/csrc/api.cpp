@@ -1,0 +1,232 @@
+// api.cpp -- the C ABI of libqmm.so: argument checks, launch planning and
+// dispatch to the HIP kernels.  Everything is checked before anything is
+// enqueued; on an error status nothing runs and no output is touched.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "qmm.h"
+#include "qmm_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+thread_local const char *g_last_variant = "";
+
+qmm_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return QMM_OK;
+    g_last_hip_error = (int)e;
+    return QMM_ERR_HIP;
+}
+
+int env_int(const char *name, int dflt) {
+    const char *v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return std::atoi(v);
+}
+
+bool trace_on() {
+    static int t = env_int("QMM_TRACE", 0);
+    return t != 0;
+}
+
+}  // namespace
+
+namespace qmm {
+
+// Decode (M <= 32): one wavefront per (16-column strip, run of TPW k tiles),
+// grouped WAVES to a workgroup along k.  TPW grows with the weight so that
+// about 2048 wavefronts (8 per CU) are in flight; all of a wavefront's loads
+// are issued at once.  Prefill (M > 32): 128 x 128 MFMA tiles.
+// QMM_DECODE_WAVES / QMM_DECODE_TPW override the choice (tuning only; the
+// results are identical for every choice).
+Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N) {
+    Int8Plan pl{};
+    const PackedBLayout L = packed_b_layout(K, N);
+    if (M <= 32) {
+        pl.variant = 0;
+        pl.mt = M <= 16 ? 1 : 2;
+        const int64_t tiles = L.NS * L.KT;
+        int tpw = (int)ceil_div(tiles, 2048);
+        tpw = tpw <= 1 ? 1 : (tpw <= 2 ? 2 : 4);
+        int waves = 4;
+        waves = env_int("QMM_DECODE_WAVES", waves);
+        tpw = env_int("QMM_DECODE_TPW", tpw);
+        if (waves != 4 && waves != 8 && waves != 16) waves = 4;
+        if (tpw != 1 && tpw != 2 && tpw != 4) tpw = 1;
+        pl.waves = waves;
+        pl.tpw = tpw;
+        const int64_t per_wg = (int64_t)waves * tpw;
+        pl.S = (int)ceil_div(L.KT, per_wg);
+        pl.grid = L.NS * pl.S;
+        if (pl.S > 1) {
+            const int64_t ne = (int64_t)pl.mt * 256;
+            pl.ws_counters_off = 0;
+            pl.ws_partials_off = kCounterBytes;
+            pl.ws_rowsum_off = pl.ws_partials_off + round_up(L.NS * pl.S * ne * 4, 256);
+            pl.ws_bytes = pl.ws_rowsum_off + round_up(L.NS * pl.S * pl.mt * 16 * 4, 256);
+        }
+    } else {
+        pl.variant = 1;
+        pl.grid = ceil_div(L.NS, 8) * ceil_div(M, 128);
+    }
+    return pl;
+}
+
+}  // namespace qmm
+
+using namespace qmm;
+
+extern "C" {
+
+const char *qmm_status_string(qmm_status s) {
+    switch (s) {
+        case QMM_OK: return "ok";
+        case QMM_ERR_INVALID: return "invalid argument";
+        case QMM_ERR_UNSUPPORTED: return "unsupported case";
+        case QMM_ERR_WORKSPACE: return "workspace or buffer too small";
+        case QMM_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+int qmm_last_hip_error(void) { return g_last_hip_error; }
+const char *qmm_last_variant(void) { return g_last_variant; }
+
+size_t qmm_pack_b_int8_bytes(int64_t K, int64_t N) {
+    if (K < 0 || N < 0) return 0;
+    return (size_t)packed_b_layout(K, N).total;
+}
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static bool k_in_bound(int64_t K) { return K * 255 * 128 < ((int64_t)1 << 31); }
+
+qmm_status pack_b_int8(const float *W, int64_t K, int64_t N, int64_t ldw, void *packed,
+                       size_t packed_bytes, void *stream) {
+    if (K <= 0 || N <= 0 || ldw < N || !W || !packed || !aligned(packed, 256) || !aligned(W, 4))
+        return QMM_ERR_INVALID;
+    if (K > INT32_MAX / 2 || N > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+    const PackedBLayout L = packed_b_layout(K, N);
+    if (packed_bytes < (size_t)L.total) return QMM_ERR_WORKSPACE;
+    g_last_variant = "pack_b_f32";
+    return hip_status(launch_pack_b_f32(W, ldw, L, packed, (hipStream_t)stream));
+}
+
+qmm_status pack_b_int8_raw(const void *B, qmm_i8type bt, int64_t K, int64_t N, int64_t ldb,
+                           void *packed, size_t packed_bytes, void *stream) {
+    if (K <= 0 || N <= 0 || ldb < N || !B || !packed || !aligned(packed, 256) ||
+        (bt != QMM_S8 && bt != QMM_U8))
+        return QMM_ERR_INVALID;
+    if (K > INT32_MAX / 2 || N > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+    const PackedBLayout L = packed_b_layout(K, N);
+    if (packed_bytes < (size_t)L.total) return QMM_ERR_WORKSPACE;
+    g_last_variant = "pack_b_raw";
+    return hip_status(launch_pack_b_raw(B, bt == QMM_U8, ldb, L, packed, (hipStream_t)stream));
+}
+
+qmm_status qmm_packed_b_check(const void *packed, int64_t K, int64_t N, void *stream) {
+    if (!packed || K <= 0 || N <= 0) return QMM_ERR_INVALID;
+    PackedHeader h;
+    hipError_t e = hipMemcpyAsync(&h, packed, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    const PackedBLayout L = packed_b_layout(K, N);
+    if (h.magic != kPackMagic || h.version != kPackVersion || h.K != K || h.N != N || h.Kp != L.Kp ||
+        h.Np != L.Np || h.scale_off != L.scale_off || h.colsum_off != L.colsum_off || h.kind > kPackRawU8)
+        return QMM_ERR_INVALID;
+    return QMM_OK;
+}
+
+qmm_status quantize_rows_int8(const float *X, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
+                              int64_t ldq, float *row_scale, void *stream) {
+    if (M < 0 || K <= 0 || ldx < K || ldq < K) return QMM_ERR_INVALID;
+    if (M == 0) return QMM_OK;
+    if (!X || !Xq || !row_scale || !aligned(X, 4) || !aligned(row_scale, 4)) return QMM_ERR_INVALID;
+    if (M > INT32_MAX || K > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+    g_last_variant = "quantize_rows";
+    return hip_status(launch_quantize_rows(X, M, K, ldx, Xq, ldq, row_scale, (hipStream_t)stream));
+}
+
+size_t qmm_int8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M <= 0 || K <= 0 || N <= 0) return 0;
+    return (size_t)plan_int8_gemm(M, K, N).ws_bytes;
+}
+
+qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t lda, int32_t zA,
+                     const void *packedB, qmm_i8type bt, int64_t N, int32_t zB,
+                     const qmm_epilogue *ep, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    if (M < 0 || N < 0 || K <= 0 || !ep || (at != QMM_S8 && at != QMM_U8) ||
+        (bt != QMM_S8 && bt != QMM_U8))
+        return QMM_ERR_INVALID;
+    if (lda < K) return QMM_ERR_INVALID;
+    const int32_t za_lo = at == QMM_U8 ? 0 : -128, zb_lo = bt == QMM_U8 ? 0 : -128;
+    if (zA < za_lo || zA > za_lo + 255 || zB < zb_lo || zB > zb_lo + 255) return QMM_ERR_INVALID;
+    const uint32_t outs = ep->outputs;
+    if (outs == 0 || (outs & ~15u) || ((outs & QMM_OUT_I8) && (outs & QMM_OUT_U8))) return QMM_ERR_INVALID;
+    if (!k_in_bound(K) || M > INT32_MAX || N > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return QMM_OK;
+    if (!A || !packedB || !aligned(packedB, 256)) return QMM_ERR_INVALID;
+    if ((outs & QMM_OUT_I32) && (!ep->y_i32 || ep->ld_i32 < N || !aligned(ep->y_i32, 4))) return QMM_ERR_INVALID;
+    if ((outs & QMM_OUT_F32) && (!ep->y_f32 || ep->ld_f32 < N || !aligned(ep->y_f32, 4))) return QMM_ERR_INVALID;
+    if ((outs & (QMM_OUT_I8 | QMM_OUT_U8))) {
+        if (!ep->y_q8 || ep->ld_q8 < N) return QMM_ERR_INVALID;
+        const int32_t lo = (outs & QMM_OUT_U8) ? 0 : -128;
+        if (ep->zp_out < lo || ep->zp_out > lo + 255) return QMM_ERR_INVALID;
+    }
+    const PackedBLayout L = packed_b_layout(K, N);
+    const Int8Plan plan = plan_int8_gemm(M, K, N);
+    if (plan.ws_bytes > 0 && L.NS * 4 > kCounterBytes) return QMM_ERR_UNSUPPORTED;
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
+        return QMM_ERR_WORKSPACE;
+
+    Int8GemmParams p{};
+    p.A = (const int8_t *)A;
+    p.lda = lda;
+    p.M = (int)M;
+    p.K = (int)K;
+    p.N = (int)N;
+    p.a_u8 = at == QMM_U8;
+    p.a_vec = aligned(A, 16) && (lda % 16 == 0);
+    p.zAs = zA - (at == QMM_U8 ? 128 : 0);
+    p.zBs = zB - (bt == QMM_U8 ? 128 : 0);
+    const int8_t *base = (const int8_t *)packedB;
+    p.codes = base + L.codes_off;
+    p.colsum = (const int32_t *)(base + L.colsum_off);
+    p.KT = (int)L.KT;
+    p.NS = (int)L.NS;
+    p.outputs = outs;
+    p.y_i32 = ep->y_i32;
+    p.ld_i32 = ep->ld_i32;
+    p.y_f32 = ep->y_f32;
+    p.ld_f32 = ep->ld_f32;
+    p.y_q8 = (int8_t *)ep->y_q8;
+    p.ld_q8 = ep->ld_q8;
+    p.q8_u8 = (outs & QMM_OUT_U8) != 0;
+    p.row_scale = ep->row_scale;
+    p.col_scale = ep->col_scale ? ep->col_scale : (const float *)(base + L.scale_off);
+    p.scale = ep->scale;
+    p.bias_f32 = ep->bias_f32;
+    p.bias_i32 = ep->bias_i32;
+    p.zp_out = ep->zp_out;
+    p.S = plan.variant == 0 ? plan.S : 1;
+    p.tiles_per_wg = plan.waves * plan.tpw;
+    if (plan.ws_bytes > 0) {
+        int8_t *ws = (int8_t *)workspace;
+        p.counters = (uint32_t *)(ws + plan.ws_counters_off);
+        p.partials = (int32_t *)(ws + plan.ws_partials_off);
+        p.rowsum_part = (int32_t *)(ws + plan.ws_rowsum_off);
+    }
+    const char *variant = "";
+    qmm_status st = hip_status(launch_int8_gemm(plan, p, (hipStream_t)stream, &variant));
+    g_last_variant = variant;
+    if (trace_on())
+        fprintf(stderr, "qmm int8_gemm variant=%s M=%lld K=%lld N=%lld grid=%lld S=%d waves=%d tpw=%d\n",
+                variant, (long long)M, (long long)K, (long long)N, (long long)plan.grid, plan.S,
+                plan.waves, plan.tpw);
+    return st;
+}
+
+}  // extern "C"

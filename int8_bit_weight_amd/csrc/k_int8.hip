@@ -1,0 +1,494 @@
+// k_int8.hip -- int8 path kernels for gfx950 (CDNA4, wave64):
+//   * packB: per-column int8 quantisation into the MFMA tile layout
+//   * per-row int8 activation quantisation
+//   * int8 x int8 -> int32 GEMM with the zero-point correction epilogue,
+//     a decode variant (M <= 32, HBM streaming of the weight tiles, split-K
+//     over workgroups with an in-kernel last-arriver reduction) and a prefill
+//     variant (LDS-staged tiles, v_mfma_i32_16x16x64_i8).
+//
+// Arithmetic follows "int8 inference" (onemodel docs), "Product kernel
+// (Int8Gemm)", and "The ONNX pack: weights to Q4NX, matmuls to our kernels,
+// no VitisAI", sections "The three layers of the pack", "Why it folds
+// without a new kernel" and "What works today, and what does not".
+#include "qmm_internal.h"
+
+namespace qmm {
+
+namespace {
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Symmetric int8 code of x for scale s (s > 0): clamp(rne(x / s), -127, 127).
+// The division is IEEE correctly rounded (hipcc's default for fp32 '/').
+__device__ __forceinline__ int quant_code(float x, float s) {
+    float r = rintf(x / s);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// ---------------------------------------------------------------- packB ---
+// One workgroup per 16-column strip.  Pass 1: column amax (fp32 source).
+// Pass 2: each thread produces the 16 codes of one MFMA lane chunk (16
+// consecutive k of one column) and stores them with one 16-byte store.
+template <bool RAW>
+__global__ __launch_bounds__(256) void k_pack_b(const void *__restrict__ Bsrc, int64_t ld, int u8,
+                                                int K, int N, int KT, int8_t *__restrict__ codes,
+                                                float *__restrict__ scale,
+                                                int32_t *__restrict__ colsum,
+                                                PackedHeader *__restrict__ header, PackedHeader h) {
+    const int strip = blockIdx.x;
+    const int t = threadIdx.x;
+    const int c = t & 15;
+    const int r = t >> 4;
+    const int n = strip * kTileN + c;
+    __shared__ float s_part[16][17];
+    __shared__ int s_sum[16][17];
+    __shared__ float s_scale[16];
+
+    if (blockIdx.x == 0 && t == 0) *header = h;
+
+    if (!RAW) {
+        const float *W = (const float *)Bsrc;
+        float amax = 0.0f;
+        if (n < N)
+            for (int k = r; k < K; k += 16) amax = fmaxf(amax, fabsf(W[(int64_t)k * ld + n]));
+        s_part[r][c] = amax;
+        __syncthreads();
+        if (t < 16) {
+            float a = 0.0f;
+            for (int i = 0; i < 16; ++i) a = fmaxf(a, s_part[i][t]);
+            s_scale[t] = (a == 0.0f) ? 0.0f : a / 127.0f;
+        }
+    } else if (t < 16) {
+        s_scale[t] = (strip * kTileN + t < N) ? 1.0f : 0.0f;
+    }
+    __syncthreads();
+    const float s = s_scale[c];
+
+    const int lane = t & 63;
+    const int g = lane >> 4;
+    int csum = 0;
+    for (int tile = t >> 6; tile < KT; tile += 4) {
+        const int k0 = tile * kTileK + g * 16;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int k = k0 + j;
+            int q = 0;
+            if (n < N && k < K) {
+                if (RAW) {
+                    const uint8_t b = ((const uint8_t *)Bsrc)[(int64_t)k * ld + n];
+                    q = u8 ? (int)b - 128 : (int)(int8_t)b;
+                } else if (s > 0.0f) {
+                    q = quant_code(((const float *)Bsrc)[(int64_t)k * ld + n], s);
+                }
+            }
+            csum += q;
+            w[j >> 2] |= (uint32_t)(q & 0xFF) << (8 * (j & 3));
+        }
+        v4i out = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        *(v4i *)(codes + ((int64_t)strip * KT + tile) * kTileBytes + lane * 16) = out;
+    }
+    s_sum[r][c] = csum;
+    __syncthreads();
+    if (t < 16) {
+        int acc = 0;
+        for (int i = 0; i < 16; ++i) acc += s_sum[i][t];
+        colsum[strip * kTileN + t] = acc;
+        scale[strip * kTileN + t] = s_scale[t];
+    }
+}
+
+// ------------------------------------------------------- row quantiser ---
+// One workgroup (256 threads) per row.
+__global__ __launch_bounds__(256) void k_quantize_rows(const float *__restrict__ X, int64_t ldx,
+                                                       int K, int8_t *__restrict__ Xq, int64_t ldq,
+                                                       float *__restrict__ row_scale) {
+    const int64_t m = blockIdx.x;
+    const int t = threadIdx.x;
+    const float *x = X + m * ldx;
+    __shared__ float s_red[4];
+    float amax = 0.0f;
+    for (int k = t; k < K; k += 256) amax = fmaxf(amax, fabsf(x[k]));
+    amax = wave_max_f(amax);
+    if ((t & 63) == 0) s_red[t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float s = (amax == 0.0f) ? 0.0f : amax / 127.0f;
+    int8_t *q = Xq + m * ldq;
+    for (int k = t; k < K; k += 256) q[k] = (s > 0.0f) ? (int8_t)quant_code(x[k], s) : (int8_t)0;
+    if (t == 0) row_scale[m] = s;
+}
+
+// ------------------------------------------------------------- epilogue ---
+// Zero-point correction in wrapping int32, then the requested outputs.
+//   Y    = S - zA'*colsum[n] - zB'*(rowsum[m] - K*zA')
+//   mult = fl32(fl32(rs[m]*cs[n]) * scale)
+//   F32  = fma(fl32(Y), mult, bias_f32[n])
+//   I8/U8: v = fl32(fl32(Y + bias_i32[n]) * mult); clamp(rne(v) + zp_out)
+__device__ __forceinline__ void epilogue_store(const Int8GemmParams &p, int m, int n, uint32_t S,
+                                               int32_t rowsum, bool has_zb) {
+    uint32_t Y = S - (uint32_t)p.zAs * (uint32_t)p.colsum[n];
+    if (has_zb) Y -= (uint32_t)p.zBs * ((uint32_t)rowsum - (uint32_t)p.K * (uint32_t)p.zAs);
+    const int32_t y = (int32_t)Y;
+    if (p.outputs & QMM_OUT_I32) p.y_i32[(int64_t)m * p.ld_i32 + n] = y;
+    if (p.outputs & (QMM_OUT_F32 | QMM_OUT_I8 | QMM_OUT_U8)) {
+        const float rs = p.row_scale ? p.row_scale[m] : 1.0f;
+        const float rc = rs * p.col_scale[n];
+        const float mult = rc * p.scale;
+        if (p.outputs & QMM_OUT_F32) {
+            const float b = p.bias_f32 ? p.bias_f32[n] : 0.0f;
+            p.y_f32[(int64_t)m * p.ld_f32 + n] = fmaf((float)y, mult, b);
+        }
+        if (p.outputs & (QMM_OUT_I8 | QMM_OUT_U8)) {
+            const uint32_t acc = Y + (uint32_t)(p.bias_i32 ? p.bias_i32[n] : 0);
+            float v = (float)(int32_t)acc * mult;
+            v = fminf(fmaxf(v, -65536.0f), 65536.0f);
+            int q = (int)rintf(v) + p.zp_out;
+            const int lo = p.q8_u8 ? 0 : -128, hi = p.q8_u8 ? 255 : 127;
+            q = q < lo ? lo : (q > hi ? hi : q);
+            p.y_q8[(int64_t)m * p.ld_q8 + n] = (int8_t)(uint8_t)q;
+        }
+    }
+}
+
+// 16 bytes of A' (shifted domain) for row `row`, k = k0 .. k0+15; zero where
+// row >= M or k >= K.  uint8 A is shifted by flipping the top bit.
+__device__ __forceinline__ v4i load_a16(const Int8GemmParams &p, int row, int k0) {
+    v4i v = {0, 0, 0, 0};
+    if (row >= p.M || k0 >= p.K) return v;
+    const int8_t *src = p.A + (int64_t)row * p.lda + k0;
+    const uint32_t flip = p.a_u8 ? 0x80808080u : 0u;
+    if (p.a_vec && k0 + 16 <= p.K) {
+        v = *(const v4i *)src;
+        v[0] ^= flip;
+        v[1] ^= flip;
+        v[2] ^= flip;
+        v[3] ^= flip;
+        return v;
+    }
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < 16; ++j) {
+        if (k0 + j < p.K) {
+            const uint32_t b = (uint8_t)src[j] ^ (flip & 0xFFu);
+            w[j >> 2] |= b << (8 * (j & 3));
+        }
+    }
+    v[0] = (int)w[0];
+    v[1] = (int)w[1];
+    v[2] = (int)w[2];
+    v[3] = (int)w[3];
+    return v;
+}
+
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// --------------------------------------------------------- decode GEMM ---
+// M <= 16*MT.  Workgroup = WAVES wavefronts on one 16-column strip and a
+// range of WAVES*TPW k tiles (wave w takes tiles w, w+WAVES, ...).  Every
+// wave issues all of its weight-tile and activation loads before its first
+// MFMA.  The waves' partial 16x16 tiles are summed in LDS; with S > 1 splits
+// per strip, each workgroup stores its partial in the workspace and the last
+// one to arrive (agent-scope counter) sums all S partials in a fixed order
+// and runs the epilogue, then resets the counter to 0.
+template <int MT, int WAVES, int TPW, bool HAS_ZB>
+__global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
+    constexpr int NE = MT * 256;  // elements of the (MT*16) x 16 output tile
+    constexpr int NT = WAVES * 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int split = blockIdx.x % p.S;
+    const int strip = blockIdx.x / p.S;
+    const int kt_begin = split * p.tiles_per_wg;
+    const int kt_end = min(p.KT, kt_begin + p.tiles_per_wg);
+
+    v4i bf[TPW];
+    v4i af[TPW][MT];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int kt = kt_begin + wave + i * WAVES;
+        if (kt < kt_end) {
+            bf[i] = *(const v4i *)(p.codes + ((int64_t)strip * p.KT + kt) * kTileBytes + lane * 16);
+#pragma unroll
+            for (int r = 0; r < MT; ++r)
+                af[i][r] = load_a16(p, r * 16 + (lane & 15), kt * kTileK + (lane >> 4) * 16);
+        } else {
+            bf[i] = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int r = 0; r < MT; ++r) af[i][r] = v4i{0, 0, 0, 0};
+        }
+    }
+    v4i acc[MT];
+    v4i accr[MT];
+#pragma unroll
+    for (int r = 0; r < MT; ++r) {
+        acc[r] = v4i{0, 0, 0, 0};
+        accr[r] = v4i{0, 0, 0, 0};
+    }
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+#pragma unroll
+        for (int r = 0; r < MT; ++r) {
+            acc[r] = mfma_i8(af[i][r], bf[i], acc[r]);
+            if (HAS_ZB) accr[r] = mfma_i8(af[i][r], ones, accr[r]);
+        }
+    }
+
+    __shared__ int32_t s_red[WAVES][MT * 16][17];
+    __shared__ int32_t s_redr[WAVES][MT * 16];
+    __shared__ int32_t s_rowsum[MT * 16];
+    __shared__ int s_last;
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = r * 16 + 4 * (lane >> 4) + i;
+            s_red[wave][row][lane & 15] = acc[r][i];
+            if (HAS_ZB && (lane & 15) == 0) s_redr[wave][row] = accr[r][i];
+        }
+    __syncthreads();
+
+    constexpr int EPT = (NE + NT - 1) / NT;  // elements per thread
+    int32_t val[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int e = threadIdx.x + j * NT;
+        int32_t v = 0;
+        if (e < NE) {
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) v += s_red[w][e >> 4][e & 15];
+        }
+        val[j] = v;
+    }
+    int32_t rsum = 0;
+    if (HAS_ZB && threadIdx.x < MT * 16) {
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) rsum += s_redr[w][threadIdx.x];
+    }
+
+    if (p.S > 1) {
+        const int64_t slot = (int64_t)strip * p.S + split;
+        int32_t *part = p.partials + slot * NE;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int e = threadIdx.x + j * NT;
+            if (e < NE) part[e] = val[j];
+        }
+        if (HAS_ZB && threadIdx.x < MT * 16) p.rowsum_part[slot * (MT * 16) + threadIdx.x] = rsum;
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(&p.counters[strip], 1u, __ATOMIC_ACQ_REL,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == (uint32_t)(p.S - 1));
+        }
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+        const int32_t *base = p.partials + (int64_t)strip * p.S * NE;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int e = threadIdx.x + j * NT;
+            int32_t v = 0;
+            if (e < NE)
+                for (int s2 = 0; s2 < p.S; ++s2) v += base[(int64_t)s2 * NE + e];
+            val[j] = v;
+        }
+        if (HAS_ZB && threadIdx.x < MT * 16) {
+            rsum = 0;
+            const int32_t *rb = p.rowsum_part + (int64_t)strip * p.S * (MT * 16);
+            for (int s2 = 0; s2 < p.S; ++s2) rsum += rb[s2 * (MT * 16) + threadIdx.x];
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&p.counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (HAS_ZB) {
+        if (threadIdx.x < MT * 16) s_rowsum[threadIdx.x] = rsum;
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int e = threadIdx.x + j * NT;
+        const int m = e >> 4;
+        const int n = strip * kTileN + (e & 15);
+        if (e < NE && m < p.M && n < p.N)
+            epilogue_store(p, m, n, (uint32_t)val[j], HAS_ZB ? s_rowsum[m] : 0, HAS_ZB);
+    }
+}
+
+// -------------------------------------------------------- prefill GEMM ---
+// 128 x 128 output tile per workgroup, k step 64, 4 wavefronts in a 2 x 2
+// grid each owning 64 x 64 (4 x 4 MFMA tiles of 16 x 16).  A and B tiles are
+// double-buffered in LDS; the next tile's global loads are issued before the
+// current tile's MFMAs.  A rows in LDS are 64 bytes with the 16-byte chunk
+// index XOR-swizzled by (row/2)%4 so a wavefront's 16-byte reads of 16 rows
+// spread over all banks; B tiles are copied as is (already lane-ordered).
+constexpr int PF_BM = 128, PF_BN = 128;
+
+__device__ __forceinline__ int swz_a(int row, int kc) { return row * 64 + ((kc ^ ((row >> 1) & 3)) << 4); }
+
+template <bool HAS_ZB>
+__global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
+    __shared__ __attribute__((aligned(16))) int8_t sA[2][PF_BM * kTileK];
+    __shared__ __attribute__((aligned(16))) int8_t sB[2][(PF_BN / kTileN) * kTileBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * PF_BM;
+    const int strip0 = blockIdx.x * (PF_BN / kTileN);
+
+    v4i ra[2], rb[2];
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + 256 * i;
+            ra[i] = load_a16(p, m0 + (c >> 2), kt * kTileK + (c & 3) * 16);
+            const int f = c >> 6;
+            const int strip = strip0 + f;
+            if (strip < p.NS)
+                rb[i] = *(const v4i *)(p.codes + ((int64_t)strip * p.KT + kt) * kTileBytes + (c & 63) * 16);
+            else
+                rb[i] = v4i{0, 0, 0, 0};
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + 256 * i;
+            *(v4i *)(&sA[buf][swz_a(c >> 2, c & 3)]) = ra[i];
+            *(v4i *)(&sB[buf][(c >> 6) * kTileBytes + (c & 63) * 16]) = rb[i];
+        }
+    };
+
+    v4i acc[4][4];
+    v4i accr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        accr[i] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    }
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < p.KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < p.KT) gload(kt + 1);
+        v4i a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = wm * 64 + i * 16 + (lane & 15);
+            a[i] = *(const v4i *)(&sA[buf][swz_a(row, lane >> 4)]);
+            b[i] = *(const v4i *)(&sB[buf][(wn * 4 + i) * kTileBytes + lane * 16]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_i8(a[i], b[j], acc[i][j]);
+            if (HAS_ZB) accr[i] = mfma_i8(a[i], ones, accr[i]);
+        }
+        if (kt + 1 < p.KT) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + v;
+                const int n = (strip0 + wn * 4 + j) * kTileN + (lane & 15);
+                if (m < p.M && n < p.N)
+                    epilogue_store(p, m, n, (uint32_t)acc[i][j][v], HAS_ZB ? accr[i][v] : 0, HAS_ZB);
+            }
+}
+
+template <int MT, int WAVES, int TPW>
+hipError_t launch_decode(const Int8GemmParams &p, int64_t grid, hipStream_t s) {
+    if (p.zBs != 0)
+        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, true>), dim3((unsigned)grid), dim3(WAVES * 64), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, false>), dim3((unsigned)grid), dim3(WAVES * 64), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int MT, int WAVES>
+hipError_t launch_decode_tpw(const Int8GemmParams &p, int tpw, int64_t grid, hipStream_t s) {
+    switch (tpw) {
+        case 1: return launch_decode<MT, WAVES, 1>(p, grid, s);
+        case 2: return launch_decode<MT, WAVES, 2>(p, grid, s);
+        case 4: return launch_decode<MT, WAVES, 4>(p, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int MT>
+hipError_t launch_decode_waves(const Int8GemmParams &p, int waves, int tpw, int64_t grid,
+                               hipStream_t s) {
+    switch (waves) {
+        case 4: return launch_decode_tpw<MT, 4>(p, tpw, grid, s);
+        case 8: return launch_decode_tpw<MT, 8>(p, tpw, grid, s);
+        case 16: return launch_decode_tpw<MT, 16>(p, tpw, grid, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ launchers ---
+
+hipError_t launch_pack_b_f32(const float *W, int64_t ldw, const PackedBLayout &L, void *packed,
+                             hipStream_t s) {
+    PackedHeader h = {kPackMagic, kPackVersion, kPackF32, 0u, L.K, L.N, L.Kp, L.Np, L.scale_off, L.colsum_off};
+    int8_t *base = (int8_t *)packed;
+    hipLaunchKernelGGL((k_pack_b<false>), dim3((unsigned)L.NS), dim3(256), 0, s, (const void *)W, ldw, 0,
+                       (int)L.K, (int)L.N, (int)L.KT, base + L.codes_off, (float *)(base + L.scale_off),
+                       (int32_t *)(base + L.colsum_off), (PackedHeader *)base, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_b_raw(const void *B, int u8, int64_t ldb, const PackedBLayout &L,
+                             void *packed, hipStream_t s) {
+    PackedHeader h = {kPackMagic, kPackVersion, u8 ? (uint32_t)kPackRawU8 : (uint32_t)kPackRawS8, 0u,
+                      L.K, L.N, L.Kp, L.Np, L.scale_off, L.colsum_off};
+    int8_t *base = (int8_t *)packed;
+    hipLaunchKernelGGL((k_pack_b<true>), dim3((unsigned)L.NS), dim3(256), 0, s, B, ldb, u8, (int)L.K,
+                       (int)L.N, (int)L.KT, base + L.codes_off, (float *)(base + L.scale_off),
+                       (int32_t *)(base + L.colsum_off), (PackedHeader *)base, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const float *X, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
+                                int64_t ldq, float *row_scale, hipStream_t s) {
+    hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)M), dim3(256), 0, s, X, ldx, (int)K, Xq, ldq, row_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
+                            const char **variant) {
+    if (plan.variant == 0) {
+        *variant = plan.mt == 1 ? "int8_decode_m16" : "int8_decode_m32";
+        if (plan.mt == 1) return launch_decode_waves<1>(p, plan.waves, plan.tpw, plan.grid, s);
+        return launch_decode_waves<2>(p, plan.waves, plan.tpw, plan.grid, s);
+    }
+    *variant = "int8_prefill_128x128";
+    dim3 grid((unsigned)ceil_div(p.NS, PF_BN / kTileN), (unsigned)ceil_div(p.M, PF_BM));
+    if (p.zBs != 0)
+        hipLaunchKernelGGL((k_int8_prefill<true>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_int8_prefill<false>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace qmm

@@ -1,0 +1,133 @@
+// qmm_internal.h -- device layouts and launcher declarations shared by the
+// host dispatcher (api.cpp) and the HIP kernels.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmm.h"
+
+namespace qmm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// ------------------------------------------------------------------------
+// Packed int8 weight.  The codes of a K x N weight are stored as 1 KiB tiles
+// of 64 k x 16 n.  Inside a tile, 16-byte chunk `lane` (0..63) holds the 16
+// consecutive k = 16*(lane/16) .. +15 of column lane%16: exactly the B operand
+// one wavefront lane feeds to v_mfma_i32_16x16x64_i8, so a wavefront reads a
+// tile with one fully coalesced 16-byte load per lane.  Tiles of one 16-column
+// strip are contiguous along k (strip-major), so a K-range of one strip is one
+// contiguous run of HBM.
+//   byte offset of (k, n) = 64 + ((n/16)*KT + k/64)*1024
+//                           + ((k%64)/16)*256 + (n%16)*16 + (k%16)
+// followed by fp32 scale[Np] and int32 colsum[Np].  K is padded to a multiple
+// of 64 and N to 16 with zero codes.
+// ------------------------------------------------------------------------
+constexpr int kTileK = 64;
+constexpr int kTileN = 16;
+constexpr int kTileBytes = 1024;
+constexpr int64_t kHeaderBytes = 64;
+constexpr uint32_t kPackMagic = 0x31424d51u;  // "QMB1"
+constexpr uint32_t kPackVersion = 1;
+
+enum PackKind : uint32_t { kPackF32 = 0, kPackRawS8 = 1, kPackRawU8 = 2 };
+
+struct PackedHeader {
+    uint32_t magic, version, kind, reserved;
+    int64_t K, N, Kp, Np;
+    int64_t scale_off, colsum_off;
+};
+static_assert(sizeof(PackedHeader) == 64, "header is 64 bytes");
+
+struct PackedBLayout {
+    int64_t K, N, Kp, Np, KT, NS;
+    int64_t codes_off, scale_off, colsum_off, total;
+};
+
+inline PackedBLayout packed_b_layout(int64_t K, int64_t N) {
+    PackedBLayout L;
+    L.K = K;
+    L.N = N;
+    L.Kp = round_up(K > 0 ? K : 1, kTileK);
+    L.Np = round_up(N > 0 ? N : 1, kTileN);
+    L.KT = L.Kp / kTileK;
+    L.NS = L.Np / kTileN;
+    L.codes_off = kHeaderBytes;
+    L.scale_off = L.codes_off + L.Kp * L.Np;
+    L.colsum_off = L.scale_off + 4 * L.Np;
+    L.total = L.colsum_off + 4 * L.Np;
+    return L;
+}
+
+// ------------------------------------------------------------------------
+// int8 GEMM launch parameters (passed by value as the kernel argument).
+// ------------------------------------------------------------------------
+struct Int8GemmParams {
+    const int8_t *A;      // raw bytes of A (int8 or uint8)
+    int64_t lda;
+    int M, K, N;
+    int a_u8;             // 1: A is uint8 (flip the top bit to shift by 128)
+    int a_vec;            // 1: A and lda allow aligned 16-byte loads
+    int32_t zAs, zBs;     // zero points in the shifted (int8) domain
+    const int8_t *codes;  // packed tiles
+    const int32_t *colsum;
+    int KT, NS;           // k tiles, n strips
+    // epilogue
+    uint32_t outputs;
+    int32_t *y_i32;
+    int64_t ld_i32;
+    float *y_f32;
+    int64_t ld_f32;
+    int8_t *y_q8;
+    int64_t ld_q8;
+    int q8_u8;
+    const float *row_scale;  // NULL = 1
+    const float *col_scale;  // never NULL (defaults to the packed scales)
+    float scale;
+    const float *bias_f32;
+    const int32_t *bias_i32;
+    int32_t zp_out;
+    // split-K bookkeeping (decode path)
+    int S;                 // WG splits per strip
+    int tiles_per_wg;
+    uint32_t *counters;    // [NS]
+    int32_t *partials;     // [NS][S][MT*16][16]
+    int32_t *rowsum_part;  // [NS][S][MT*16]
+};
+
+// Every workspace starts with a fixed 64 KiB region of split-K arrival
+// counters (one uint32 per 16-column strip, so N <= 262144 on the split
+// path).  Kernels return each counter they use to zero, and nothing else is
+// ever stored there, so a zero-filled workspace stays valid for any later
+// call whatever its shape.  Everything after the region is scratch that a
+// call fully writes before it reads.
+constexpr int64_t kCounterBytes = 65536;
+
+struct Int8Plan {
+    int variant;      // 0 = decode (M <= 32), 1 = prefill
+    int mt;           // 16-row tiles (decode)
+    int waves;        // waves per workgroup (decode)
+    int tpw;          // k tiles per wave (decode)
+    int S;            // splits per strip (decode)
+    int64_t grid;
+    int64_t ws_counters_off, ws_partials_off, ws_rowsum_off, ws_bytes;
+};
+
+Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N);
+
+hipError_t launch_pack_b_f32(const float *W, int64_t ldw, const PackedBLayout &L, void *packed,
+                             hipStream_t s);
+hipError_t launch_pack_b_raw(const void *B, int u8, int64_t ldb, const PackedBLayout &L,
+                             void *packed, hipStream_t s);
+hipError_t launch_quantize_rows(const float *X, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
+                                int64_t ldq, float *row_scale, hipStream_t s);
+hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
+                            const char **variant);
+
+}  // namespace qmm

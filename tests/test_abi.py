@@ -1,0 +1,102 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point
+that include/qmm.h declares, and rejects malformed arguments on the host
+without touching a GPU (every case below fails validation before any HIP
+call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "qmm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def q():
+    import int8_bit_weight_amd as q
+    return q
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ["pack_b_int8", "pack_b_int8_raw", "quantize_rows_int8", "int8_gemm", "q4_1_repack",
+              "q4_1_matmul", "q4_1_matmul_id", "qmm_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(q):
+    for n in _declared_functions():
+        assert hasattr(q.lib, n), n
+
+
+def test_status_strings(q):
+    for s in range(5):
+        assert q.lib.qmm_status_string(s)
+
+
+def test_size_queries(q):
+    assert q.lib.qmm_pack_b_int8_bytes(1024, 1024) == 64 + 1024 * 1024 + 8 * 1024
+    assert q.lib.qmm_pack_b_int8_bytes(100, 17) == 64 + 128 * 32 + 8 * 32
+    assert q.lib.qmm_int8_gemm_workspace_bytes(2048, 4096, 4096) == 0  # prefill: no split-K
+    assert q.lib.qmm_int8_gemm_workspace_bytes(16, 1024, 1024) > 0
+
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: each call below fails validation first
+
+
+def _ep(q, **kw):
+    ep = q.qmm_epilogue()
+    ep.outputs = kw.get("outputs", q.QMM_OUT_I32)
+    ep.y_i32 = kw.get("y_i32", 4096)
+    ep.ld_i32 = kw.get("ld_i32", 64)
+    ep.zp_out = kw.get("zp_out", 0)
+    ep.y_q8 = kw.get("y_q8", 4096)
+    ep.ld_q8 = kw.get("ld_q8", 64)
+    return ep
+
+
+def _gemm(q, M=4, K=64, N=64, lda=64, zA=0, zB=0, at=0, bt=0, ep=None, A=FAKE, B=FAKE):
+    ep = ep or _ep(q)
+    return q.lib.int8_gemm(A, at, M, K, lda, zA, B, bt, N, zB, ctypes.byref(ep), None, 0, None)
+
+
+def test_int8_gemm_rejections(q):
+    INV, UNS = q.QMM_ERR_INVALID, q.QMM_ERR_UNSUPPORTED
+    assert _gemm(q, M=-1) == INV
+    assert _gemm(q, K=0) == INV
+    assert _gemm(q, lda=63) == INV
+    assert _gemm(q, zA=128) == INV                 # int8 A: zero point in [-128, 127]
+    assert _gemm(q, at=1, zA=-1) == INV            # uint8 A: zero point in [0, 255]
+    assert _gemm(q, bt=1, zB=256) == INV
+    assert _gemm(q, at=2) == INV
+    assert _gemm(q, ep=_ep(q, outputs=0)) == INV
+    assert _gemm(q, ep=_ep(q, outputs=q.QMM_OUT_I8 | q.QMM_OUT_U8)) == INV
+    assert _gemm(q, ep=_ep(q, outputs=q.QMM_OUT_I8, zp_out=128)) == INV
+    assert _gemm(q, ep=_ep(q, ld_i32=63)) == INV
+    assert _gemm(q, A=None) == INV
+    assert _gemm(q, B=ctypes.c_void_p(4096 + 16)) == INV   # packed buffer must be 256-byte aligned
+    # page bound K*255*128 < 2^31
+    assert _gemm(q, K=65794, lda=65794) == UNS
+    # decode shapes need a workspace
+    assert _gemm(q, M=16, K=1024, N=1024, lda=1024, ep=_ep(q, ld_i32=1024)) == q.QMM_ERR_WORKSPACE
+    # empty products are a no-op
+    assert _gemm(q, M=0) == q.QMM_OK
+
+
+def test_pack_and_quantize_rejections(q):
+    INV = q.QMM_ERR_INVALID
+    assert q.lib.pack_b_int8(FAKE, 0, 16, 16, FAKE, 1 << 20, None) == INV
+    assert q.lib.pack_b_int8(FAKE, 64, 16, 15, FAKE, 1 << 20, None) == INV
+    assert q.lib.pack_b_int8(None, 64, 16, 16, FAKE, 1 << 20, None) == INV
+    assert q.lib.pack_b_int8(FAKE, 64, 16, 16, ctypes.c_void_p(4096 + 64), 1 << 20, None) == INV
+    assert q.lib.pack_b_int8(FAKE, 64, 16, 16, FAKE, 100, None) == q.QMM_ERR_WORKSPACE
+    assert q.lib.pack_b_int8_raw(FAKE, 3, 64, 16, 16, FAKE, 1 << 20, None) == INV
+    assert q.lib.quantize_rows_int8(FAKE, 4, 64, 63, FAKE, 64, FAKE, None) == INV
+    assert q.lib.quantize_rows_int8(FAKE, 0, 64, 64, FAKE, 64, FAKE, None) == q.QMM_OK

@@ -1,0 +1,275 @@
+"""GPU parity of the int8 path against the CPU oracle, through the C ABI.
+
+Integer outputs (codes, scales, column sums, int32 accumulators, requantised
+int8) must match bit for bit; fp32 epilogue outputs must satisfy
+max|dY| <= 2e-6 * max|Y| against the oracle's fp64 value.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from gpu_util import max_rel_err, to_dev, to_np, torch_dev, unpack_int8_codes
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 2e-6
+
+
+@pytest.fixture(scope="module")
+def q():
+    import int8_bit_weight_amd as q
+    return q
+
+
+def _packed_np(p):
+    return to_np(p.data)
+
+
+def _check_pack(q, orc, W, raw=False):
+    Wd = to_dev(W)
+    p = q.pack_b_int8_raw(Wd) if raw else q.pack_b_int8(Wd)
+    assert q.last_variant() == ("pack_b_raw" if raw else "pack_b_f32")
+    K, N = W.shape
+    codes, scale, colsum, (Kp, Np) = unpack_int8_codes(_packed_np(p), K, N)
+    Q, s, cs = orc.pack_b_raw(W) if raw else orc.pack_b_int8(W)
+    assert np.array_equal(codes[:K, :N], Q)
+    assert (codes[K:, :] == 0).all() and (codes[:, N:] == 0).all()
+    assert np.array_equal(scale[:N].view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(colsum[:N], cs)
+    return p, (Q, s, cs)
+
+
+@pytest.mark.parametrize("K,N", [(1024, 1024), (100, 37), (64, 16), (3072, 1024), (1, 1), (1056, 17)])
+def test_pack_b_int8_bit_exact(q, orc, K, N):
+    W = wl.normal_f32(np.random.default_rng(K * 7 + N), (K, N), 0.02)
+    if N > 3:
+        W[:, 2] = 0.0               # all-zero column
+        W[5 % K, 3] = 127.0         # scale exactly 1 on column 3
+    _check_pack(q, orc, W)
+
+
+@pytest.mark.parametrize("dtype", [np.int8, np.uint8])
+def test_pack_b_raw_bit_exact(q, orc, dtype):
+    g = np.random.default_rng(3)
+    B = (wl.uniform_u8(g, (200, 40)) if dtype == np.uint8 else wl.uniform_i8(g, (200, 40)))
+    _check_pack(q, orc, B, raw=True)
+
+
+@pytest.mark.parametrize("M,K", [(1, 1024), (16, 1024), (32, 3072), (3, 100), (7, 1)])
+def test_quantize_rows_bit_exact(q, orc, M, K):
+    X = wl.normal_f32(np.random.default_rng(M * 31 + K), (M, K))
+    X[0, :] = 0.0
+    if M > 2:
+        X[2, K // 2] = 127.0
+    Xq, rs = q.quantize_rows_int8(to_dev(X))
+    Qo, so = orc.quantize_rows_int8(X)
+    assert np.array_equal(to_np(Xq), Qo)
+    assert np.array_equal(to_np(rs).view(np.uint32), so.view(np.uint32))
+
+
+def _gemm_case(q, orc, A, zA, B, zB, *, rs=None, bias=None, scale=1.0, requant=None, expect_variant=None):
+    """Run the GPU product with I32 + F32 (+ optional requant) outputs and
+    compare with the oracle.  B is a raw int8/uint8 K x N weight."""
+    import torch
+    M, K = A.shape
+    N = B.shape[1]
+    dev = torch_dev()
+    p = q.pack_b_int8_raw(to_dev(B))
+    Ad = to_dev(A)
+    y32 = torch.full((M, N), -7, dtype=torch.int32, device=dev)
+    yf = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    kw = dict(out_i32=y32, out_f32=yf, scale=scale)
+    if rs is not None:
+        kw["row_scale"] = to_dev(rs)
+    if bias is not None:
+        kw["bias_f32"] = to_dev(bias)
+    yq = None
+    if requant is not None:
+        yq = torch.zeros((M, N), dtype=torch.uint8 if requant["u8"] else torch.int8, device=dev)
+        kw.update(out_q8=yq, q8_unsigned=requant["u8"], bias_i32=to_dev(requant["bias_i32"]),
+                  zp_out=requant["zp_out"])
+    q.int8_gemm(Ad, zA, p, zB, **kw)
+    if expect_variant:
+        assert q.last_variant() == expect_variant
+    Y64 = orc.int8_gemm_i64(A, zA, B, zB)
+    assert np.abs(Y64).max() < 2 ** 31
+    assert np.array_equal(to_np(y32), Y64.astype(np.int32))
+    ref = orc.epilogue_f64(Y64, rs, None, scale, bias)
+    assert max_rel_err(to_np(yf), ref) <= F32_TOL
+    if requant is not None:
+        refq = orc.requant(Y64, rs, None, scale, requant["bias_i32"], requant["zp_out"], requant["u8"])
+        assert np.array_equal(to_np(yq), refq)
+    return y32, yf
+
+
+def test_int8_product_config(q, orc):
+    """uint8 A (zA), int8 B (zB), int32 and fp32 outputs, scale 1e-3 and N(0,1) bias."""
+    d = wl.int8_product_inputs()
+    _gemm_case(q, orc, d["A"], d["zA"], d["B"], d["zB"], bias=d["bias"], scale=d["scale"],
+               expect_variant="int8_decode_m16")
+
+
+@pytest.mark.parametrize("u8", [False, True])
+def test_int8_requant_config(q, orc, u8):
+    d = wl.int8_requant_inputs()
+    zp = d["zp_out"] + (128 if u8 else 0)
+    _gemm_case(q, orc, d["A"], d["zA"], d["B"], d["zB"], scale=d["scale"],
+               requant=dict(u8=u8, bias_i32=d["bias_i32"], zp_out=zp))
+
+
+EDGE_M = [1, 2, 3, 17, 33]
+EDGE_K = [32, 64, 96, 1056]
+EDGE_N = [1, 15, 17]
+
+
+@pytest.mark.parametrize("M,K,N", list(itertools.product(EDGE_M, EDGE_K, EDGE_N)))
+def test_int8_edge_shapes(q, orc, M, K, N):
+    g = np.random.default_rng(M * 1000 + K * 10 + N)
+    a_u8, b_u8 = bool(g.integers(0, 2)), bool(g.integers(0, 2))
+    A = wl.uniform_u8(g, (M, K)) if a_u8 else wl.uniform_i8(g, (M, K))
+    B = wl.uniform_u8(g, (K, N)) if b_u8 else wl.uniform_i8(g, (K, N))
+    zA = int(g.integers(0, 256)) - (0 if a_u8 else 128)
+    zB = int(g.integers(0, 256)) - (0 if b_u8 else 128)
+    rs = g.uniform(0.5, 1.5, M).astype(np.float32)
+    bias = wl.normal_f32(g, (N,))
+    _gemm_case(q, orc, A, zA, B, zB, rs=rs, bias=bias, scale=np.float32(1e-4),
+               expect_variant="int8_decode_m16" if M <= 16 else ("int8_decode_m32" if M <= 32 else None))
+
+
+@pytest.mark.parametrize("zA,zB", [(0, 0), (255, -128), (0, 127), (128, 0), (255, 127)])
+def test_int8_extreme_zero_points(q, orc, zA, zB):
+    g = np.random.default_rng(zA * 3 + zB)
+    A = wl.uniform_u8(g, (16, 1024))
+    A[0, :] = 255
+    A[1, :] = 0
+    B = wl.uniform_i8(g, (1024, 64))
+    B[:, 0] = -128
+    B[:, 1] = 127
+    _gemm_case(q, orc, A, zA, B, zB)
+
+
+def test_int8_unaligned_lda_and_strided_outputs(q, orc):
+    """A with lda = K + 3 (byte-load path), outputs with ld > N."""
+    import torch
+    g = np.random.default_rng(77)
+    M, K, N = 9, 200, 40
+    Afull = wl.uniform_i8(g, (M, K + 3))
+    B = wl.uniform_i8(g, (K, N))
+    dev = torch_dev()
+    Ad = to_dev(Afull)[:, :K]
+    p = q.pack_b_int8_raw(to_dev(B))
+    y = torch.zeros((M, N + 5), dtype=torch.int32, device=dev)
+    q.int8_gemm(Ad, -3, p, 11, out_i32=y[:, :N])
+    ref = orc.int8_gemm_i64(np.ascontiguousarray(Afull[:, :K]), -3, B, 11)
+    out = to_np(y)
+    assert np.array_equal(out[:, :N], ref.astype(np.int32))
+    assert (out[:, N:] == 0).all()
+
+
+def test_int8_empty_is_noop(q):
+    import torch
+    dev = torch_dev()
+    p = q.pack_b_int8_raw(torch.zeros((64, 16), dtype=torch.int8, device=dev))
+    y = torch.full((1, 16), 5, dtype=torch.int32, device=dev)
+    q.int8_gemm(torch.zeros((0, 64), dtype=torch.int8, device=dev), 0, p, 0, out_i32=y[:0])
+    assert (to_np(y) == 5).all()
+
+
+# ----------------------------------------------- Qwen3-0.6B projections ---
+
+@pytest.mark.parametrize("proj", range(len(wl.QWEN3_0_6B_PROJECTIONS)))
+def test_projection_pipeline(q, orc, proj):
+    """The decode path as the benchmark runs it: packB of fp32 N(0,0.02)
+    weights, per-row quantisation of fp32 N(0,1) activations, int8 product,
+    fp32 output -- at M = 1, 16, 32, each step against the oracle."""
+    import torch
+    name, K, N = wl.QWEN3_0_6B_PROJECTIONS[proj]
+    W = wl.projection_weight(0, proj)
+    p, (Qb, sb, _) = _check_pack(q, orc, W)
+    for M in wl.DECODE_ROWS:
+        X = wl.projection_activations(M, K, seed_index=proj * 10 + M)
+        Xq, rs = q.quantize_rows_int8(to_dev(X))
+        Qa, sa = orc.quantize_rows_int8(X)
+        assert np.array_equal(to_np(Xq), Qa)
+        assert np.array_equal(to_np(rs).view(np.uint32), sa.view(np.uint32))
+        y = torch.empty((M, N), dtype=torch.float32, device=torch_dev())
+        y32 = torch.empty((M, N), dtype=torch.int32, device=torch_dev())
+        q.int8_gemm(Xq, 0, p, 0, out_f32=y, out_i32=y32, row_scale=rs)
+        assert q.last_variant() == ("int8_decode_m16" if M <= 16 else "int8_decode_m32")
+        Y64 = orc.int8_gemm_i64(Qa, 0, Qb, 0)
+        assert np.array_equal(to_np(y32), Y64.astype(np.int32))
+        ref = orc.epilogue_f64(Y64, sa, sb)
+        assert max_rel_err(to_np(y), ref) <= F32_TOL, (name, M)
+
+
+def test_decode_workspace_reuse_and_determinism(q, orc):
+    """Back-to-back calls that share one workspace give identical bits (the
+    split-K counters are left at zero by every call)."""
+    import torch
+    d = wl.int8_product_inputs(seed_index=3)
+    p = q.pack_b_int8_raw(to_dev(d["B"]))
+    A = to_dev(d["A"])
+    outs = []
+    for _ in range(3):
+        yf = torch.empty((16, 1024), dtype=torch.float32, device=torch_dev())
+        q.int8_gemm(A, d["zA"], p, d["zB"], out_f32=yf, scale=d["scale"], bias_f32=to_dev(d["bias"]))
+        outs.append(to_np(yf))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+
+
+# ------------------------------------------------------------- prefill ---
+
+@pytest.mark.parametrize("M,K,N,zA,zB", [(160, 1056, 272, 0, 0), (200, 96, 40, 5, -7), (33, 64, 17, -128, 127),
+                                          (128, 128, 128, 0, 3), (257, 320, 129, 17, 0)])
+def test_prefill_full_compare(q, orc, M, K, N, zA, zB):
+    g = np.random.default_rng(M + K + N)
+    A = wl.uniform_i8(g, (M, K))
+    B = wl.uniform_i8(g, (K, N))
+    rs = (g.uniform(0.5, 1.5, M) / 127).astype(np.float32)
+    _gemm_case(q, orc, A, zA, B, zB, rs=rs, bias=wl.normal_f32(g, (N,)), scale=np.float32(0.01),
+               expect_variant="int8_prefill_128x128")
+
+
+@pytest.mark.parametrize("shape", range(len(wl.PREFILL_SHAPES)))
+def test_prefill_full_size_sampled(q, orc, shape):
+    """M = 2048 tokens at the 8B-class shapes: packB of fp32 N(0,0.02)
+    weights (bit-exact), int32 and fp32 outputs checked on 4096 sampled
+    positions (plus the four corners) against the oracle."""
+    import torch
+    K, N = wl.PREFILL_SHAPES[shape]
+    d = wl.prefill_inputs(K, N, seed_index=shape)
+    p, (Qb, sb, _) = _check_pack(q, orc, d["W"])
+    dev = torch_dev()
+    y32 = torch.empty((wl.PREFILL_M, N), dtype=torch.int32, device=dev)
+    yf = torch.empty((wl.PREFILL_M, N), dtype=torch.float32, device=dev)
+    q.int8_gemm(to_dev(d["A"]), 0, p, 0, out_i32=y32, out_f32=yf, row_scale=to_dev(d["rs"]))
+    assert q.last_variant() == "int8_prefill_128x128"
+    g = np.random.default_rng(99 + shape)
+    im = np.concatenate([g.integers(0, wl.PREFILL_M, 4096), [0, 0, wl.PREFILL_M - 1, wl.PREFILL_M - 1]])
+    in_ = np.concatenate([g.integers(0, N, 4096), [0, N - 1, 0, N - 1]])
+    ref = orc.int8_gemm_at(d["A"], 0, Qb, 0, im, in_)
+    got32 = to_np(y32)[im, in_]
+    assert np.array_equal(got32, ref.astype(np.int32))
+    reff = ref.astype(np.float64) * d["rs"][im].astype(np.float64) * sb[in_].astype(np.float64)
+    gotf = to_np(yf)[im, in_]
+    assert np.abs(gotf - reff).max() <= F32_TOL * np.abs(reff).max()
+
+
+def test_workspace_shared_across_shapes(q, orc):
+    """Regression: one zero-filled workspace reused by decode calls of
+    different shapes (different split counts and strip counts)."""
+    import torch
+    ws = torch.zeros(4 << 20, dtype=torch.uint8, device=torch_dev())
+    g = np.random.default_rng(5)
+    for (M, K, N) in [(16, 1024, 2048), (1, 1024, 3072), (32, 3072, 1024), (16, 2048, 1024), (1, 64, 4096)]:
+        assert q.lib.qmm_int8_gemm_workspace_bytes(M, K, N) <= ws.numel()
+        A = wl.uniform_i8(g, (M, K))
+        B = wl.uniform_i8(g, (K, N))
+        p = q.pack_b_int8_raw(to_dev(B))
+        y = torch.empty((M, N), dtype=torch.int32, device=torch_dev())
+        q.int8_gemm(to_dev(A), 1, p, -2, out_i32=y, ws=ws)
+        assert np.array_equal(to_np(y), orc.int8_gemm_i64(A, 1, B, -2).astype(np.int32)), (M, K, N)
+    assert (to_np(ws[:65536]) == 0).all()
