@@ -161,13 +161,9 @@ size_t qmm_int8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
  *   packedB  buffer written by pack_b_int8 / pack_b_int8_raw for this K, N.
  *   bt       element type the packed weight was given in (QMM_S8 for
  *            pack_b_int8); zB is in that type's range.
- *   workspace  device, >= qmm_int8_gemm_workspace_bytes(M,K,N) bytes, 256-byte
- *            aligned, ZERO-FILLED before its first use.  Its first 64 KiB
- *            hold split-K arrival counters that every call returns to zero;
- *            the rest is scratch.  So one workspace serves any sequence of
- *            calls, whatever their shapes, without clearing.  Calls that
- *            overlap in time must not share a workspace.  Needs N <= 262144
- *            when the size query is non-zero (else QMM_ERR_UNSUPPORTED).
+ *   workspace  device scratch of qmm_int8_gemm_workspace_bytes(M,K,N) bytes
+ *            (256-byte aligned, zero-filled before its first use); NULL when
+ *            that size is 0, which it is for every current kernel variant.
  * K must satisfy K*255*128 < 2^31 ([P2]: the sums cannot overflow below that
  * bound), else QMM_ERR_UNSUPPORTED.  M = 0 or N = 0 is a no-op.
  */

@@ -186,14 +186,18 @@ def packed_b_scales(p: PackedInt8):
     return scale, colsum
 
 
-def quantize_rows_int8(X, stream=None):
-    """Per-row int8 quantisation of fp32 X [M, K]: returns (Xq int8, row_scale f32)."""
+def quantize_rows_int8(X, out=None, stream=None):
+    """Per-row int8 quantisation of fp32 X [M, K]: returns (Xq int8, row_scale f32).
+    `out` may supply preallocated (Xq, row_scale) tensors."""
     torch = _torch()
     M, K = X.shape
-    Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
-    rs = torch.empty((M,), dtype=torch.float32, device=X.device)
-    _check("quantize_rows_int8", lib.quantize_rows_int8(_ptr(X), M, K, X.stride(0), _ptr(Xq), K, _ptr(rs),
-                                                        _stream(stream)))
+    if out is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+        rs = torch.empty((M,), dtype=torch.float32, device=X.device)
+    else:
+        Xq, rs = out
+    _check("quantize_rows_int8", lib.quantize_rows_int8(_ptr(X), M, K, X.stride(0), _ptr(Xq), Xq.stride(0),
+                                                        _ptr(rs), _stream(stream)))
     return Xq, rs
 
 

@@ -35,38 +35,28 @@ bool trace_on() {
 
 namespace qmm {
 
-// Decode (M <= 32): one wavefront per (16-column strip, run of TPW k tiles),
-// grouped WAVES to a workgroup along k.  TPW grows with the weight so that
-// about 2048 wavefronts (8 per CU) are in flight; all of a wavefront's loads
-// are issued at once.  Prefill (M > 32): 128 x 128 MFMA tiles.
-// QMM_DECODE_WAVES / QMM_DECODE_TPW override the choice (tuning only; the
-// results are identical for every choice).
+// Decode (M <= 32): one workgroup per 16-column strip of the weight, with
+// WAVES wavefronts (4, 8 or 16) splitting its k tiles and TPW (1, 2 or 4)
+// tiles per wavefront per round, chosen so one round covers as much of K as
+// possible.  Prefill (M > 32): 128 x 128 MFMA tiles.  QMM_DECODE_WAVES /
+// QMM_DECODE_TPW override the choice (tuning only: integer results are exact
+// and the fp32 epilogue does not depend on the choice either).
 Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N) {
     Int8Plan pl{};
     const PackedBLayout L = packed_b_layout(K, N);
     if (M <= 32) {
         pl.variant = 0;
         pl.mt = M <= 16 ? 1 : 2;
-        const int64_t tiles = L.NS * L.KT;
-        int tpw = (int)ceil_div(tiles, 2048);
+        int waves = L.KT <= 4 ? 4 : (L.KT <= 8 ? 8 : 16);
+        int tpw = (int)ceil_div(L.KT, waves);
         tpw = tpw <= 1 ? 1 : (tpw <= 2 ? 2 : 4);
-        int waves = 4;
         waves = env_int("QMM_DECODE_WAVES", waves);
         tpw = env_int("QMM_DECODE_TPW", tpw);
-        if (waves != 4 && waves != 8 && waves != 16) waves = 4;
-        if (tpw != 1 && tpw != 2 && tpw != 4) tpw = 1;
+        if (waves != 4 && waves != 8 && waves != 16) waves = 16;
+        if (tpw != 1 && tpw != 2 && tpw != 4) tpw = 4;
         pl.waves = waves;
         pl.tpw = tpw;
-        const int64_t per_wg = (int64_t)waves * tpw;
-        pl.S = (int)ceil_div(L.KT, per_wg);
-        pl.grid = L.NS * pl.S;
-        if (pl.S > 1) {
-            const int64_t ne = (int64_t)pl.mt * 256;
-            pl.ws_counters_off = 0;
-            pl.ws_partials_off = kCounterBytes;
-            pl.ws_rowsum_off = pl.ws_partials_off + round_up(L.NS * pl.S * ne * 4, 256);
-            pl.ws_bytes = pl.ws_rowsum_off + round_up(L.NS * pl.S * pl.mt * 16 * 4, 256);
-        }
+        pl.grid = L.NS;
     } else {
         pl.variant = 1;
         pl.grid = ceil_div(L.NS, 8) * ceil_div(M, 128);
@@ -178,7 +168,6 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
     }
     const PackedBLayout L = packed_b_layout(K, N);
     const Int8Plan plan = plan_int8_gemm(M, K, N);
-    if (plan.ws_bytes > 0 && L.NS * 4 > kCounterBytes) return QMM_ERR_UNSUPPORTED;
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
         return QMM_ERR_WORKSPACE;
 
@@ -211,21 +200,13 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
     p.bias_f32 = ep->bias_f32;
     p.bias_i32 = ep->bias_i32;
     p.zp_out = ep->zp_out;
-    p.S = plan.variant == 0 ? plan.S : 1;
-    p.tiles_per_wg = plan.waves * plan.tpw;
-    if (plan.ws_bytes > 0) {
-        int8_t *ws = (int8_t *)workspace;
-        p.counters = (uint32_t *)(ws + plan.ws_counters_off);
-        p.partials = (int32_t *)(ws + plan.ws_partials_off);
-        p.rowsum_part = (int32_t *)(ws + plan.ws_rowsum_off);
-    }
     const char *variant = "";
     qmm_status st = hip_status(launch_int8_gemm(plan, p, (hipStream_t)stream, &variant));
     g_last_variant = variant;
     if (trace_on())
-        fprintf(stderr, "qmm int8_gemm variant=%s M=%lld K=%lld N=%lld grid=%lld S=%d waves=%d tpw=%d\n",
-                variant, (long long)M, (long long)K, (long long)N, (long long)plan.grid, plan.S,
-                plan.waves, plan.tpw);
+        fprintf(stderr, "qmm int8_gemm variant=%s M=%lld K=%lld N=%lld grid=%lld waves=%d tpw=%d\n",
+                variant, (long long)M, (long long)K, (long long)N, (long long)plan.grid, plan.waves,
+                plan.tpw);
     return st;
 }
 

@@ -2,9 +2,9 @@
 //   * packB: per-column int8 quantisation into the MFMA tile layout
 //   * per-row int8 activation quantisation
 //   * int8 x int8 -> int32 GEMM with the zero-point correction epilogue,
-//     a decode variant (M <= 32, HBM streaming of the weight tiles, split-K
-//     over workgroups with an in-kernel last-arriver reduction) and a prefill
-//     variant (LDS-staged tiles, v_mfma_i32_16x16x64_i8).
+//     a decode variant (M <= 32: HBM streaming of the weight tiles, one
+//     workgroup per 16-column strip, k split over its wavefronts) and a
+//     prefill variant (LDS-staged tiles, v_mfma_i32_16x16x64_i8).
 //
 // Arithmetic follows "int8 inference" (onemodel docs), "Product kernel
 // (Int8Gemm)", and "The ONNX pack: weights to Q4NX, matmuls to our kernels,
@@ -190,40 +190,23 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 }
 
 // --------------------------------------------------------- decode GEMM ---
-// M <= 16*MT.  Workgroup = WAVES wavefronts on one 16-column strip and a
-// range of WAVES*TPW k tiles (wave w takes tiles w, w+WAVES, ...).  Every
-// wave issues all of its weight-tile and activation loads before its first
-// MFMA.  The waves' partial 16x16 tiles are summed in LDS; with S > 1 splits
-// per strip, each workgroup stores its partial in the workspace and the last
-// one to arrive (agent-scope counter) sums all S partials in a fixed order
-// and runs the epilogue, then resets the counter to 0.
+// M <= 16*MT.  One workgroup per 16-column strip; its WAVES wavefronts split
+// the k tiles round-robin (wave w takes tiles w, w+WAVES, ...), TPW tiles per
+// round.  Each wave issues all TPW weight-tile loads (one 16-byte load per
+// lane per tile, a contiguous 1 KiB per tile) and the matching activation
+// loads before its first MFMA, so a whole round is in flight at once.  The
+// waves' 16x16 int32 tiles are summed in LDS in wave order and the epilogue
+// runs in the same workgroup: no cross-workgroup traffic, no atomics, no
+// fences, no workspace.
 template <int MT, int WAVES, int TPW, bool HAS_ZB>
 __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
     constexpr int NE = MT * 256;  // elements of the (MT*16) x 16 output tile
     constexpr int NT = WAVES * 64;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int split = blockIdx.x % p.S;
-    const int strip = blockIdx.x / p.S;
-    const int kt_begin = split * p.tiles_per_wg;
-    const int kt_end = min(p.KT, kt_begin + p.tiles_per_wg);
+    const int strip = blockIdx.x;
+    const int8_t *strip_codes = p.codes + (int64_t)strip * p.KT * kTileBytes + lane * 16;
 
-    v4i bf[TPW];
-    v4i af[TPW][MT];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int kt = kt_begin + wave + i * WAVES;
-        if (kt < kt_end) {
-            bf[i] = *(const v4i *)(p.codes + ((int64_t)strip * p.KT + kt) * kTileBytes + lane * 16);
-#pragma unroll
-            for (int r = 0; r < MT; ++r)
-                af[i][r] = load_a16(p, r * 16 + (lane & 15), kt * kTileK + (lane >> 4) * 16);
-        } else {
-            bf[i] = v4i{0, 0, 0, 0};
-#pragma unroll
-            for (int r = 0; r < MT; ++r) af[i][r] = v4i{0, 0, 0, 0};
-        }
-    }
     v4i acc[MT];
     v4i accr[MT];
 #pragma unroll
@@ -232,19 +215,36 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
         accr[r] = v4i{0, 0, 0, 0};
     }
     const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+
+    for (int base = wave; base < p.KT; base += WAVES * TPW) {
+        v4i bf[TPW];
+        v4i af[TPW][MT];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
+        for (int i = 0; i < TPW; ++i) {
+            const int kt = base + i * WAVES;
+            bf[i] = kt < p.KT ? *(const v4i *)(strip_codes + (int64_t)kt * kTileBytes) : v4i{0, 0, 0, 0};
+        }
 #pragma unroll
-        for (int r = 0; r < MT; ++r) {
-            acc[r] = mfma_i8(af[i][r], bf[i], acc[r]);
-            if (HAS_ZB) accr[r] = mfma_i8(af[i][r], ones, accr[r]);
+        for (int i = 0; i < TPW; ++i) {
+            const int kt = base + i * WAVES;
+#pragma unroll
+            for (int r = 0; r < MT; ++r)
+                af[i][r] = kt < p.KT ? load_a16(p, r * 16 + (lane & 15), kt * kTileK + (lane >> 4) * 16)
+                                     : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+#pragma unroll
+            for (int r = 0; r < MT; ++r) {
+                acc[r] = mfma_i8(af[i][r], bf[i], acc[r]);
+                if (HAS_ZB) accr[r] = mfma_i8(af[i][r], ones, accr[r]);
+            }
         }
     }
 
     __shared__ int32_t s_red[WAVES][MT * 16][17];
     __shared__ int32_t s_redr[WAVES][MT * 16];
     __shared__ int32_t s_rowsum[MT * 16];
-    __shared__ int s_last;
 #pragma unroll
     for (int r = 0; r < MT; ++r)
 #pragma unroll
@@ -254,72 +254,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
             if (HAS_ZB && (lane & 15) == 0) s_redr[wave][row] = accr[r][i];
         }
     __syncthreads();
-
-    constexpr int EPT = (NE + NT - 1) / NT;  // elements per thread
-    int32_t val[EPT];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int e = threadIdx.x + j * NT;
-        int32_t v = 0;
-        if (e < NE) {
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w) v += s_red[w][e >> 4][e & 15];
-        }
-        val[j] = v;
-    }
-    int32_t rsum = 0;
-    if (HAS_ZB && threadIdx.x < MT * 16) {
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) rsum += s_redr[w][threadIdx.x];
-    }
-
-    if (p.S > 1) {
-        const int64_t slot = (int64_t)strip * p.S + split;
-        int32_t *part = p.partials + slot * NE;
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const int e = threadIdx.x + j * NT;
-            if (e < NE) part[e] = val[j];
-        }
-        if (HAS_ZB && threadIdx.x < MT * 16) p.rowsum_part[slot * (MT * 16) + threadIdx.x] = rsum;
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t prev = __hip_atomic_fetch_add(&p.counters[strip], 1u, __ATOMIC_ACQ_REL,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (prev == (uint32_t)(p.S - 1));
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        const int32_t *base = p.partials + (int64_t)strip * p.S * NE;
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const int e = threadIdx.x + j * NT;
-            int32_t v = 0;
-            if (e < NE)
-                for (int s2 = 0; s2 < p.S; ++s2) v += base[(int64_t)s2 * NE + e];
-            val[j] = v;
-        }
-        if (HAS_ZB && threadIdx.x < MT * 16) {
-            rsum = 0;
-            const int32_t *rb = p.rowsum_part + (int64_t)strip * p.S * (MT * 16);
-            for (int s2 = 0; s2 < p.S; ++s2) rsum += rb[s2 * (MT * 16) + threadIdx.x];
-        }
-        if (threadIdx.x == 0)
-            __hip_atomic_store(&p.counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
     if (HAS_ZB) {
-        if (threadIdx.x < MT * 16) s_rowsum[threadIdx.x] = rsum;
+        if (threadIdx.x < MT * 16) {
+            int32_t rsum = 0;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) rsum += s_redr[w][threadIdx.x];
+            s_rowsum[threadIdx.x] = rsum;
+        }
         __syncthreads();
     }
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        const int e = threadIdx.x + j * NT;
+    for (int e = threadIdx.x; e < NE; e += NT) {
         const int m = e >> 4;
         const int n = strip * kTileN + (e & 15);
-        if (e < NE && m < p.M && n < p.N)
-            epilogue_store(p, m, n, (uint32_t)val[j], HAS_ZB ? s_rowsum[m] : 0, HAS_ZB);
+        if (m < p.M && n < p.N) {
+            int32_t v = 0;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) v += s_red[w][m][e & 15];
+            epilogue_store(p, m, n, (uint32_t)v, HAS_ZB ? s_rowsum[m] : 0, HAS_ZB);
+        }
     }
 }
 
@@ -415,31 +367,30 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
 }
 
 template <int MT, int WAVES, int TPW>
-hipError_t launch_decode(const Int8GemmParams &p, int64_t grid, hipStream_t s) {
+hipError_t launch_decode(const Int8GemmParams &p, hipStream_t s) {
     if (p.zBs != 0)
-        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, true>), dim3((unsigned)grid), dim3(WAVES * 64), 0, s, p);
+        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, true>), dim3((unsigned)p.NS), dim3(WAVES * 64), 0, s, p);
     else
-        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, false>), dim3((unsigned)grid), dim3(WAVES * 64), 0, s, p);
+        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, false>), dim3((unsigned)p.NS), dim3(WAVES * 64), 0, s, p);
     return hipGetLastError();
 }
 
 template <int MT, int WAVES>
-hipError_t launch_decode_tpw(const Int8GemmParams &p, int tpw, int64_t grid, hipStream_t s) {
+hipError_t launch_decode_tpw(const Int8GemmParams &p, int tpw, hipStream_t s) {
     switch (tpw) {
-        case 1: return launch_decode<MT, WAVES, 1>(p, grid, s);
-        case 2: return launch_decode<MT, WAVES, 2>(p, grid, s);
-        case 4: return launch_decode<MT, WAVES, 4>(p, grid, s);
+        case 1: return launch_decode<MT, WAVES, 1>(p, s);
+        case 2: return launch_decode<MT, WAVES, 2>(p, s);
+        case 4: return launch_decode<MT, WAVES, 4>(p, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int MT>
-hipError_t launch_decode_waves(const Int8GemmParams &p, int waves, int tpw, int64_t grid,
-                               hipStream_t s) {
+hipError_t launch_decode_waves(const Int8GemmParams &p, int waves, int tpw, hipStream_t s) {
     switch (waves) {
-        case 4: return launch_decode_tpw<MT, 4>(p, tpw, grid, s);
-        case 8: return launch_decode_tpw<MT, 8>(p, tpw, grid, s);
-        case 16: return launch_decode_tpw<MT, 16>(p, tpw, grid, s);
+        case 4: return launch_decode_tpw<MT, 4>(p, tpw, s);
+        case 8: return launch_decode_tpw<MT, 8>(p, tpw, s);
+        case 16: return launch_decode_tpw<MT, 16>(p, tpw, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -479,8 +430,8 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
                             const char **variant) {
     if (plan.variant == 0) {
         *variant = plan.mt == 1 ? "int8_decode_m16" : "int8_decode_m32";
-        if (plan.mt == 1) return launch_decode_waves<1>(p, plan.waves, plan.tpw, plan.grid, s);
-        return launch_decode_waves<2>(p, plan.waves, plan.tpw, plan.grid, s);
+        if (plan.mt == 1) return launch_decode_waves<1>(p, plan.waves, plan.tpw, s);
+        return launch_decode_waves<2>(p, plan.waves, plan.tpw, s);
     }
     *variant = "int8_prefill_128x128";
     dim3 grid((unsigned)ceil_div(p.NS, PF_BN / kTileN), (unsigned)ceil_div(p.M, PF_BM));

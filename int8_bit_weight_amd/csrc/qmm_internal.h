@@ -93,30 +93,15 @@ struct Int8GemmParams {
     const float *bias_f32;
     const int32_t *bias_i32;
     int32_t zp_out;
-    // split-K bookkeeping (decode path)
-    int S;                 // WG splits per strip
-    int tiles_per_wg;
-    uint32_t *counters;    // [NS]
-    int32_t *partials;     // [NS][S][MT*16][16]
-    int32_t *rowsum_part;  // [NS][S][MT*16]
 };
-
-// Every workspace starts with a fixed 64 KiB region of split-K arrival
-// counters (one uint32 per 16-column strip, so N <= 262144 on the split
-// path).  Kernels return each counter they use to zero, and nothing else is
-// ever stored there, so a zero-filled workspace stays valid for any later
-// call whatever its shape.  Everything after the region is scratch that a
-// call fully writes before it reads.
-constexpr int64_t kCounterBytes = 65536;
 
 struct Int8Plan {
     int variant;      // 0 = decode (M <= 32), 1 = prefill
     int mt;           // 16-row tiles (decode)
     int waves;        // waves per workgroup (decode)
-    int tpw;          // k tiles per wave (decode)
-    int S;            // splits per strip (decode)
+    int tpw;          // k tiles per wave per round (decode)
     int64_t grid;
-    int64_t ws_counters_off, ws_partials_off, ws_rowsum_off, ws_bytes;
+    int64_t ws_bytes; // workspace the plan needs (0 for every current variant)
 };
 
 Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N);

@@ -45,7 +45,7 @@ def test_size_queries(q):
     assert q.lib.qmm_pack_b_int8_bytes(1024, 1024) == 64 + 1024 * 1024 + 8 * 1024
     assert q.lib.qmm_pack_b_int8_bytes(100, 17) == 64 + 128 * 32 + 8 * 32
     assert q.lib.qmm_int8_gemm_workspace_bytes(2048, 4096, 4096) == 0  # prefill: no split-K
-    assert q.lib.qmm_int8_gemm_workspace_bytes(16, 1024, 1024) > 0
+    assert q.lib.qmm_int8_gemm_workspace_bytes(16, 1024, 1024) == 0  # decode: no cross-workgroup split
 
 
 FAKE = ctypes.c_void_p(4096)  # never dereferenced: each call below fails validation first
@@ -84,8 +84,6 @@ def test_int8_gemm_rejections(q):
     assert _gemm(q, B=ctypes.c_void_p(4096 + 16)) == INV   # packed buffer must be 256-byte aligned
     # page bound K*255*128 < 2^31
     assert _gemm(q, K=65794, lda=65794) == UNS
-    # decode shapes need a workspace
-    assert _gemm(q, M=16, K=1024, N=1024, lda=1024, ep=_ep(q, ld_i32=1024)) == q.QMM_ERR_WORKSPACE
     # empty products are a no-op
     assert _gemm(q, M=0) == q.QMM_OK
 

@@ -265,11 +265,10 @@ def test_workspace_shared_across_shapes(q, orc):
     ws = torch.zeros(4 << 20, dtype=torch.uint8, device=torch_dev())
     g = np.random.default_rng(5)
     for (M, K, N) in [(16, 1024, 2048), (1, 1024, 3072), (32, 3072, 1024), (16, 2048, 1024), (1, 64, 4096)]:
-        assert q.lib.qmm_int8_gemm_workspace_bytes(M, K, N) <= ws.numel()
         A = wl.uniform_i8(g, (M, K))
         B = wl.uniform_i8(g, (K, N))
         p = q.pack_b_int8_raw(to_dev(B))
         y = torch.empty((M, N), dtype=torch.int32, device=torch_dev())
         q.int8_gemm(to_dev(A), 1, p, -2, out_i32=y, ws=ws)
         assert np.array_equal(to_np(y), orc.int8_gemm_i64(A, 1, B, -2).astype(np.int32)), (M, K, N)
-    assert (to_np(ws[:65536]) == 0).all()
+    assert (to_np(ws) == 0).all()
