@@ -3,6 +3,7 @@
 // enqueued; on an error status nothing runs and no output is touched.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
@@ -34,6 +35,12 @@ bool trace_on() {
 }  // namespace
 
 namespace qmm {
+
+qmm_status record_status(hipError_t e, const char *variant) {
+    g_last_variant = variant;
+    if (trace_on()) fprintf(stderr, "qmm %s\n", variant);
+    return hip_status(e);
+}
 
 // Decode (M <= 32): one workgroup per 16-column strip of the weight, with
 // WAVES wavefronts (4, 8 or 16) splitting its k tiles and TPW (1, 2 or 4)

@@ -1,0 +1,191 @@
+// api_q4.cpp -- C ABI of the q4_1 path: argument checks, launch planning and
+// dispatch.  Everything is checked before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+
+#include "qmm.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+// Set by every entry point (defined in api.cpp).
+qmm_status record_status(hipError_t e, const char *variant);
+
+// Dense q4_1: rows run in launches of up to 32 (two 16-row MFMA tiles).  A
+// workgroup is 4 wavefronts x 4 strips = 256 columns and a k range of `qps`
+// records; the k range is split S ways so that about `target` workgroups are
+// in flight, and the S partial results are summed in split order by a
+// second kernel.  Fewer splits at larger M keep the partial traffic (S*M*N
+// floats) small next to the weight bytes.
+Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
+    Q4Plan pl{};
+    const Q4Layout L = q4_layout(K, N);
+    pl.rows_per_launch = M < 32 ? M : 32;
+    pl.mt = pl.rows_per_launch <= 16 ? 1 : 2;
+    pl.waves = 4;
+    const int64_t groups = ceil_div(L.NS, 4 * pl.waves);
+    const int64_t target = pl.rows_per_launch <= 4 ? 512 : 256;
+    int64_t S = ceil_div(target, groups);
+    const int64_t max_s = ceil_div(L.NQ, 2);
+    if (S > max_s) S = max_s;
+    if (S < 1) S = 1;
+    int64_t qps = ceil_div(L.NQ, S);
+    qps = round_up(qps, 2);
+    S = ceil_div(L.NQ, qps);
+    pl.S = (int)S;
+    pl.qps = (int)qps;
+    pl.grid = groups * S;
+    pl.ws_xsp_off = 0;
+    pl.ws_xs_off = round_up(M * L.NB * 3 * 32 * 2, 256);
+    pl.ws_part_off = pl.ws_xs_off + round_up(M * L.NB * 4, 256);
+    pl.ws_bytes = pl.ws_part_off + (S > 1 ? round_up(S * pl.rows_per_launch * N * 4, 256) : 0);
+    return pl;
+}
+
+MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N) {
+    MoePlan pl{};
+    const Q4Layout L = q4_layout(K, N);
+    const int64_t P = T * n_used;
+    pl.rpc = 32;
+    pl.max_chunks = ceil_div(P, pl.rpc) + E;
+    pl.ws_xsp_off = 0;
+    pl.ws_xs_off = round_up(T * L.NB * 3 * 32 * 2, 256);
+    pl.ws_sorted_off = pl.ws_xs_off + round_up(T * L.NB * 4, 256);
+    pl.ws_chunk_off = pl.ws_sorted_off + round_up(P * 4, 256);
+    pl.ws_misc_off = pl.ws_chunk_off + round_up(pl.max_chunks * 3 * 4, 256);
+    pl.ws_bytes = pl.ws_misc_off + 256;
+    return pl;
+}
+
+}  // namespace qmm
+
+using namespace qmm;
+
+static bool aligned_to(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+extern "C" {
+
+size_t qmm_q4_1_packed_bytes(int64_t K, int64_t N) {
+    if (K <= 0 || N <= 0 || K % 32 != 0) return 0;
+    return (size_t)q4_layout(K, N).total;
+}
+
+qmm_status q4_1_repack(const void *blocks, int64_t K, int64_t N, void *packed, size_t packed_bytes,
+                       void *stream) {
+    if (K <= 0 || N <= 0 || !blocks || !packed || !aligned_to(packed, 256)) return QMM_ERR_INVALID;
+    if (K % 32 != 0) return QMM_ERR_UNSUPPORTED;
+    if (K > INT32_MAX / 2 || N > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+    const Q4Layout L = q4_layout(K, N);
+    if (packed_bytes < (size_t)L.total) return QMM_ERR_WORKSPACE;
+    return record_status(launch_q4_repack((const uint8_t *)blocks, L, (uint8_t *)packed, (hipStream_t)stream),
+                         "q4_repack");
+}
+
+size_t qmm_q4_1_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M <= 0 || K <= 0 || N <= 0 || K % 32 != 0) return 0;
+    return (size_t)plan_q4_matmul(M, K, N).ws_bytes;
+}
+
+qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx, const void *Wpacked, int64_t N,
+                       float *Y, int64_t ldy, void *workspace, size_t workspace_bytes, void *stream) {
+    if (M < 0 || K <= 0 || N < 0 || ldx < K || ldy < N) return QMM_ERR_INVALID;
+    if (K % 32 != 0) return QMM_ERR_UNSUPPORTED;
+    if (M > INT32_MAX / 2 || K > INT32_MAX / 2 || N > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return QMM_OK;
+    if (!X || !Wpacked || !Y || !aligned_to(Wpacked, 256) || !aligned_to(X, 4) || !aligned_to(Y, 4))
+        return QMM_ERR_INVALID;
+    const Q4Layout L = q4_layout(K, N);
+    const Q4Plan pl = plan_q4_matmul(M, K, N);
+    if (!workspace || workspace_bytes < (size_t)pl.ws_bytes || !aligned_to(workspace, 256))
+        return QMM_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *ws = (uint8_t *)workspace;
+    uint16_t *xsp = (uint16_t *)(ws + pl.ws_xsp_off);
+    float *xs = (float *)(ws + pl.ws_xs_off);
+    hipError_t e = launch_q4_xsplit(X, ldx, M, L.NB, xsp, xs, s);
+    const char *variant = "";
+    for (int64_t r0 = 0; r0 < M && e == hipSuccess; r0 += pl.rows_per_launch) {
+        const int64_t rows = (M - r0) < pl.rows_per_launch ? (M - r0) : pl.rows_per_launch;
+        Q4Params p{};
+        p.recs = (const uint8_t *)Wpacked;
+        p.NQ = (int)L.NQ;
+        p.NB = (int)L.NB;
+        p.NS = (int)L.NS;
+        p.N = (int)N;
+        p.K = (int)K;
+        p.xsp = xsp + r0 * L.NB * 96;
+        p.xs = xs + r0 * L.NB;
+        p.M = (int)rows;
+        p.Y = Y + r0 * ldy;
+        p.ldy = ldy;
+        p.part = (float *)(ws + pl.ws_part_off);
+        p.S = pl.S;
+        p.qps = pl.qps;
+        e = launch_q4_dense(p, pl.mt, pl.waves, pl.grid, s, &variant);
+    }
+    return record_status(e, variant);
+}
+
+size_t qmm_q4_1_matmul_id_workspace_bytes(int64_t n_tokens, int64_t n_used, int64_t n_expert, int64_t K,
+                                          int64_t N) {
+    if (n_tokens <= 0 || n_used <= 0 || n_expert <= 0 || K <= 0 || N <= 0 || K % 32 != 0) return 0;
+    return (size_t)plan_q4_moe(n_tokens, n_used, n_expert, K, N).ws_bytes;
+}
+
+qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t ldx, const void *Wexperts,
+                          int64_t n_expert, int64_t N, size_t expert_stride, const int32_t *ids,
+                          int64_t ids_row_stride, int64_t n_used, float *Y, int64_t ldy_slot, int64_t ldy_token,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_tokens < 0 || K <= 0 || N < 0 || ldx < K || n_expert <= 0 || n_used <= 0 ||
+        ids_row_stride < n_used || ldy_slot < N || ldy_token < n_used * ldy_slot)
+        return QMM_ERR_INVALID;
+    if (K % 32 != 0) return QMM_ERR_UNSUPPORTED;
+    if (n_expert > 8192 || n_tokens * n_used > INT32_MAX / 2 || K > INT32_MAX / 2 || N > INT32_MAX / 2)
+        return QMM_ERR_UNSUPPORTED;
+    if (n_tokens == 0 || N == 0) return QMM_OK;
+    if (!X || !Wexperts || !ids || !Y || !aligned_to(Wexperts, 256) || !aligned_to(X, 4) || !aligned_to(Y, 4) ||
+        !aligned_to(ids, 4))
+        return QMM_ERR_INVALID;
+    const Q4Layout L = q4_layout(K, N);
+    if (expert_stride < (size_t)L.total || expert_stride % 256 != 0) return QMM_ERR_INVALID;
+    const MoePlan pl = plan_q4_moe(n_tokens, n_used, n_expert, K, N);
+    if (!workspace || workspace_bytes < (size_t)pl.ws_bytes || !aligned_to(workspace, 256))
+        return QMM_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *ws = (uint8_t *)workspace;
+    uint16_t *xsp = (uint16_t *)(ws + pl.ws_xsp_off);
+    float *xs = (float *)(ws + pl.ws_xs_off);
+    int32_t *sorted = (int32_t *)(ws + pl.ws_sorted_off);
+    int32_t *chunk_info = (int32_t *)(ws + pl.ws_chunk_off);
+    int32_t *misc = (int32_t *)(ws + pl.ws_misc_off);
+    hipError_t e = launch_q4_xsplit(X, ldx, n_tokens, L.NB, xsp, xs, s);
+    if (e == hipSuccess)
+        e = launch_moe_route(ids, ids_row_stride, n_tokens, n_used, n_expert, pl.rpc, sorted, chunk_info, misc,
+                             misc + 1, s);
+    const char *variant = "";
+    if (e == hipSuccess) {
+        Q4Params p{};
+        p.recs = (const uint8_t *)Wexperts;
+        p.expert_stride = (int64_t)expert_stride;
+        p.NQ = (int)L.NQ;
+        p.NB = (int)L.NB;
+        p.NS = (int)L.NS;
+        p.N = (int)N;
+        p.K = (int)K;
+        p.xsp = xsp;
+        p.xs = xs;
+        p.Y = Y;
+        p.sorted = sorted;
+        p.chunk_info = chunk_info;
+        p.nchunks = misc;
+        p.n_used = (int)n_used;
+        p.ldy_slot = ldy_slot;
+        p.ldy_token = ldy_token;
+        e = launch_q4_moe(p, pl.max_chunks, s, &variant);
+    }
+    return record_status(e, variant);
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+"""GPU parity of the q4_1 path (repack, product, MUL_MAT_ID) against the CPU
+oracle, through the C ABI.
+
+The repack is a byte permutation and must be exact.  Products must satisfy
+||Y - Y_ref||_F <= 1e-5 * ||Y_ref||_F against the oracle's fp64 result on the
+same codes.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from gpu_util import canonical_q4_parts, to_dev, to_np, torch_dev, unpack_q4_records
+
+pytestmark = pytest.mark.gpu
+
+FROB_TOL = 1e-5
+
+
+def _abs_scale(orc, X, blocks, K, N):
+    """|X| @ |W|: the magnitude of the terms each output sums."""
+    return np.abs(X.astype(np.float64)) @ np.abs(orc.q4_1_decode(blocks, K, N))
+
+
+def _check(got, ref, scale=None):
+    """The 1e-5 relative Frobenius gate.  For small edge shapes (`scale`
+    given) it is taken relative to ||(|X| @ |W|)||_F instead of ||Y||_F: with
+    one block and one column, d*sum(q*x) and m*sum(x) can cancel to an output
+    far smaller than the terms, and fp32 rounding of the terms is then large
+    relative to that output though tiny relative to the terms."""
+    err = np.linalg.norm(got.astype(np.float64) - ref)
+    denom = np.linalg.norm(ref) if scale is None else max(np.linalg.norm(ref), np.linalg.norm(scale))
+    assert err <= FROB_TOL * denom, (err / max(denom, 1e-300))
+
+
+@pytest.fixture(scope="module")
+def q():
+    import int8_bit_weight_amd as q
+    return q
+
+
+def _blocks(K, N, seed, zero_cols=(), zero_scale_blocks=False):
+    W, blocks = wl.q4_weight(K, N, seed_index=seed)
+    blocks = blocks.copy()
+    for c in zero_cols:
+        if c < N:
+            blocks[c] = 0                      # d = m = 0, codes 0: an all-zero column
+    if zero_scale_blocks and N > 1 and K >= 64:
+        blocks[1, 1, 0:2] = 0                  # d = 0 on one block: value m everywhere
+    return blocks
+
+
+def _repack(q, blocks, K, N):
+    return q.q4_1_repack(to_dev(blocks.reshape(-1)), K, N)
+
+
+@pytest.mark.parametrize("K,N", [(4096, 64), (96, 17), (32, 1), (160, 300)])
+def test_repack_is_exact_permutation(q, K, N):
+    blocks = _blocks(K, N, seed=K + N)
+    p = _repack(q, blocks, K, N)
+    assert q.last_variant() == "q4_repack"
+    codes, d, m = unpack_q4_records(to_np(p.data), K, N)
+    rc, rd, rm = canonical_q4_parts(blocks, K, N)
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(d, rd) and np.array_equal(m, rm)
+    raw = to_np(p.data)
+    NB, NS = K // 32, (N + 15) // 16
+    NQ = (NB + 3) // 4
+    assert raw.size == 64 + NS * NQ * 1280 == q.lib.qmm_q4_1_packed_bytes(K, N)
+
+
+def _matmul_case(q, orc, M, K, N, seed, small=False, **kw):
+    blocks = _blocks(K, N, seed, **kw)
+    X = wl.q4_activations(M, K, seed_index=seed)
+    p = _repack(q, blocks, K, N)
+    Y = q.q4_1_matmul(to_dev(X), p)
+    got = to_np(Y)
+    ref = orc.q4_1_matmul(X, blocks, K, N)
+    _check(got, ref, _abs_scale(orc, X, blocks, K, N) if small else None)
+    return got, ref
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 32, 1), (1, 96, 17), (2, 64, 15), (16, 4096, 64), (17, 160, 300),
+                                   (33, 256, 40), (5, 1024, 33), (16, 32 * 44, 272), (64, 128, 48)])
+def test_q4_matmul_small(q, orc, M, K, N):
+    _matmul_case(q, orc, M, K, N, seed=M * 7 + K + N, small=True, zero_cols=(3,), zero_scale_blocks=True)
+
+
+def test_q4_matmul_variants_and_determinism(q, orc):
+    import torch
+    blocks = _blocks(1024, 256, seed=5)
+    p = _repack(q, blocks, 1024, 256)
+    X = to_dev(wl.q4_activations(16, 1024, seed_index=5))
+    a = to_np(q.q4_1_matmul(X, p))
+    assert q.last_variant() == "q4_mm_m16"
+    b = to_np(q.q4_1_matmul(X, p))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    q.q4_1_matmul(to_dev(wl.q4_activations(20, 1024, seed_index=6)), p)
+    assert q.last_variant() == "q4_mm_m32"
+    # strided X and Y
+    Xw = torch.zeros((16, 1024 + 32), dtype=torch.float32, device=torch_dev())
+    Xw[:, :1024] = X
+    Yw = torch.full((16, 256 + 8), 7.0, dtype=torch.float32, device=torch_dev())
+    q.q4_1_matmul(Xw[:, :1024], p, out=Yw[:, :256])
+    out = to_np(Yw)
+    assert np.array_equal(out[:, :256].view(np.uint32), a.view(np.uint32))
+    assert (out[:, 256:] == 7.0).all()
+
+
+@pytest.mark.parametrize("shape", range(len(wl.Q4_SHAPES)))
+@pytest.mark.parametrize("M", wl.Q4_ROWS)
+def test_q4_matmul_full_size(q, orc, shape, M):
+    """8B-class shapes at M = 1 and 16: full output against the fp64 oracle."""
+    K, N = wl.Q4_SHAPES[shape]
+    got, ref = _matmul_case(q, orc, M, K, N, seed=shape)
+    assert np.isfinite(got).all()
+
+
+# ------------------------------------------------------------ MUL_MAT_ID ---
+
+def _moe_case(q, orc, E, K, N, T, n_used, stride=17, seed=0, ids=None, check="full"):
+    g = np.random.default_rng(seed)
+    experts = np.stack([wl.encode_q4_1(wl.normal_f32(g, (K, N), 0.02)) for _ in range(E)])
+    X = wl.normal_f32(g, (T, K))
+    if ids is None:
+        ids = np.stack([g.permutation(max(E, stride))[:stride] % E for _ in range(T)]).astype(np.int32)
+    buf, estride = q.q4_1_repack_experts(to_dev(experts), K, N)
+    Y = q.q4_1_matmul_id(to_dev(X), buf, E, K, N, estride, to_dev(ids), n_used)
+    assert q.last_variant() == "q4_mm_moe_m32"
+    got = to_np(Y)
+    if check == "full":
+        ref = orc.q4_1_matmul_id(X, experts, E, K, N, ids, n_used)
+        absw = [np.abs(orc.q4_1_decode(experts[e], K, N)) for e in range(E)]
+        scale = np.stack([np.stack([np.abs(X[t].astype(np.float64)) @ absw[ids[t, s]] for s in range(n_used)])
+                          for t in range(T)])
+        _check(got, ref, scale)
+        for s in range(n_used):
+            _check(got[:, s], ref[:, s], scale[:, s])
+    return got, (experts, X, ids)
+
+
+def test_moe_small_strided(q, orc):
+    got, (experts, X, ids) = _moe_case(q, orc, E=6, K=64, N=24, T=10, n_used=3)
+    # the unused tail of each id row changes nothing
+    ids2 = ids.copy()
+    ids2[:, 3:] = (ids2[:, 3:] + 1) % 6
+    buf, estride = q.q4_1_repack_experts(to_dev(experts), 64, 24)
+    got2 = to_np(q.q4_1_matmul_id(to_dev(X), buf, 6, 64, 24, estride, to_dev(ids2), 3))
+    assert np.array_equal(got.view(np.uint32), got2.view(np.uint32))
+
+
+@pytest.mark.parametrize("E,K,N,T,n_used", [(20, 96, 40, 37, 4), (3, 32, 16, 1, 1), (9, 256, 300, 70, 8),
+                                             (128, 64, 48, 64, 8)])
+def test_moe_shapes(q, orc, E, K, N, T, n_used):
+    _moe_case(q, orc, E, K, N, T, n_used, seed=E + K + N + T)
+
+
+def test_moe_single_expert_takes_all_rows(q, orc):
+    """Every pair routed to one expert (many row chunks on one expert): equal
+    to the dense product with that expert's weight."""
+    E, K, N, T, n_used = 4, 128, 64, 70, 3
+    ids = np.full((T, 17), 2, dtype=np.int32)
+    got, (experts, X, _) = _moe_case(q, orc, E, K, N, T, n_used, ids=ids, check="none")
+    ref = orc.q4_1_matmul(X, experts[2], K, N)
+    scale = _abs_scale(orc, X, experts[2], K, N)
+    for s in range(n_used):
+        _check(got[:, s], ref, scale)
+
+
+def test_moe_out_of_range_id_is_skipped(q, orc):
+    """An id outside [0, E) is caught by the routing kernel's own bound check:
+    that pair's output row is left untouched, every other pair is correct."""
+    import torch
+    E, K, N, T, n_used = 5, 64, 32, 6, 2
+    g = np.random.default_rng(3)
+    experts = np.stack([wl.encode_q4_1(wl.normal_f32(g, (K, N), 0.02)) for _ in range(E)])
+    X = wl.normal_f32(g, (T, K))
+    ids = np.stack([g.permutation(17)[:17] % E for _ in range(T)]).astype(np.int32)
+    ids[4, 1] = E + 3
+    buf, estride = q.q4_1_repack_experts(to_dev(experts), K, N)
+    Y = torch.full((T, n_used, N), -9.0, dtype=torch.float32, device=torch_dev())
+    q.q4_1_matmul_id(to_dev(X), buf, E, K, N, estride, to_dev(ids), n_used, out=Y)
+    got = to_np(Y)
+    assert (got[4, 1] == -9.0).all()
+    ok = ids.copy()
+    ok[4, 1] = 0
+    ref = orc.q4_1_matmul_id(X, experts, E, K, N, ok, n_used)
+    mask = np.ones((T, n_used), dtype=bool)
+    mask[4, 1] = False
+    absw = [np.abs(orc.q4_1_decode(experts[e], K, N)) for e in range(E)]
+    scale = np.stack([np.stack([np.abs(X[t].astype(np.float64)) @ absw[ok[t, s]] for s in range(n_used)])
+                      for t in range(T)])
+    _check(got[mask], ref[mask], scale[mask])
+
+
+def test_moe_full_config_sampled(q, orc):
+    """128 experts of 2048 x 768 q4_1, 512 tokens, top-8 ids from a stride-17
+    view: 24 whole tokens (all slots) against the fp64 oracle plus 4096
+    sampled outputs."""
+    d = wl.moe_inputs()
+    E, K, N = wl.MOE_EXPERTS, wl.MOE_K, wl.MOE_N
+    buf, estride = q.q4_1_repack_experts(to_dev(d["experts"]), K, N)
+    Y = q.q4_1_matmul_id(to_dev(d["X"]), buf, E, K, N, estride, to_dev(d["ids"]), wl.MOE_USED)
+    got = to_np(Y)
+    g = np.random.default_rng(11)
+    toks = np.sort(g.choice(wl.MOE_TOKENS, 24, replace=False))
+    ref = orc.q4_1_matmul_id(d["X"][toks], d["experts"], E, K, N, d["ids"][toks], wl.MOE_USED)
+    _check(got[toks], ref)
+    it = g.integers(0, wl.MOE_TOKENS, 4096)
+    is_ = g.integers(0, wl.MOE_USED, 4096)
+    in_ = g.integers(0, N, 4096)
+    refs = orc.q4_1_matmul_id_at(d["X"], d["experts"], E, K, N, d["ids"], it, is_, in_)
+    _check(got[it, is_, in_], refs)
