@@ -5,15 +5,18 @@ Workload (one "step"): the seven Qwen3-0.6B projections of all 28 layers
 (196 distinct weights, fp32 N(0, 0.02), packed once by pack_b_int8 before the
 timed region: ~420 MiB of int8 codes, more than the 256 MiB Infinity Cache)
 run as decode at M = 1, 16 and 32 rows of fp32 N(0, 1) activations.  Every
-call is quantize_rows_int8 (per-row amax/127) followed by int8_gemm with the
-fp32 epilogue (row scale x column scale).  Each M's 196 calls are captured in
+call is int8_gemm_dynamic: per-row amax/127 quantisation of the activations
+(inside the int8 product kernel at M <= 16, a separate kernel at M = 32) and
+the int8 product with the fp32 epilogue (row scale x column scale).  Each M's 196 calls are captured in
 one HIP graph; a step replays the three graphs.
 
 `value` is the step's algorithmic bytes (per call K*N weight bytes + 4N column
 scales + 4MK activations + 4MN outputs) over its wall time, in GB/s.
-`roofline` is the int8 decode GEMM kernel alone: its algorithmic bytes per
-launch (K*N + 4N + M*K + 4M + 4MN) over its average launch duration, timed
-with HIP events around each launch on the launch stream.  `extra` carries the
+`roofline` is the dominant kernel, the int8 decode GEMM: its algorithmic
+bytes per launch (K*N + 4N + 4MK + 4MN with the activations quantised inside
+at M <= 16; K*N + 4N + MK + 4M + 4MN on pre-quantised rows at M = 32) over
+its average launch time from graphs of its launches alone (HIP events on the
+replay stream, dispatch gaps included).  `extra` carries the
 per-M figures and the other configurations (int8 prefill at M = 2048).
 `cpu_baseline` times the CPU oracle on one whole step.
 
@@ -50,11 +53,6 @@ def parse_args():
 def call_bytes(M, K, N):
     """Algorithmic bytes of one projection call (quantize + product + epilogue)."""
     return K * N + 4 * N + 4 * M * K + 4 * M * N
-
-
-def gemm_kernel_bytes(M, K, N):
-    """Algorithmic bytes of one int8 decode GEMM launch."""
-    return K * N + 4 * N + M * K + 4 * M + 4 * M * N
 
 
 def time_launches(torch, launches):
@@ -107,30 +105,25 @@ def main() -> int:
     torch.cuda.synchronize()
     log("packed in %.1f s" % (time.perf_counter() - t0))
 
-    calls = {}     # M -> list of (l, p, K, N, X, Xq, rs, Y)
+    calls = {}     # M -> list of (l, p, K, N, X, Y)
     for M in rows:
         lst = []
         for l in range(layers):
             for p, (_, K, N) in enumerate(projs):
                 X = torch.from_numpy(wl.projection_activations(M, K, seed_index=10000 + l * 16 + p)).to(dev)
-                Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
-                rs = torch.empty((M,), dtype=torch.float32, device=dev)
                 Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-                lst.append((l, p, K, N, X, Xq, rs, Y))
+                lst.append((l, p, K, N, X, Y))
         calls[M] = lst
-    ws_need = max(q.lib.qmm_int8_gemm_workspace_bytes(M, K, N) for M in rows for (_, K, N) in projs)
-    ws = torch.zeros(max(ws_need, 256), dtype=torch.uint8, device=dev)
 
     def run_m(M):
-        for (l, p, K, N, X, Xq, rs, Y) in calls[M]:
-            q.quantize_rows_int8(X, out=(Xq, rs))
-            q.int8_gemm(Xq, 0, packed[(l, p)], 0, out_f32=Y, row_scale=rs, ws=ws)
+        for (l, p, K, N, X, Y) in calls[M]:
+            q.int8_gemm_dynamic(X, packed[(l, p)], out_f32=Y)
 
     # eager reference outputs, then one graph per M, checked bit for bit
     for M in rows:
         run_m(M)
     torch.cuda.synchronize()
-    eager = {M: [c[7].clone() for c in calls[M]] for M in rows}
+    eager = {M: [c[5].clone() for c in calls[M]] for M in rows}
     graphs = {}
     for M in rows:
         g = torch.cuda.CUDAGraph()
@@ -140,15 +133,15 @@ def main() -> int:
     for rep in range(2):
         for M in rows:
             for c in calls[M]:
-                c[7].fill_(float("nan"))
+                c[5].fill_(float("nan"))
             graphs[M].replay()
         torch.cuda.synchronize()
         for M in rows:
             for c, ref in zip(calls[M], eager[M]):
-                if not torch.equal(c[7].view(torch.int32), ref.view(torch.int32)):
+                if not torch.equal(c[5].view(torch.int32), ref.view(torch.int32)):
                     raise RuntimeError("graph replay differs from eager result (M=%d)" % M)
 
-    step_bytes = {M: sum(call_bytes(M, K, N) for (_, _, K, N, *_r) in calls[M]) for M in rows}
+    step_bytes = {M: sum(call_bytes(M, c[2], c[3]) for c in calls[M]) for M in rows}
     total_bytes = sum(step_bytes.values())
 
     # -------------------------------------------------------------- timed ---
@@ -173,37 +166,61 @@ def main() -> int:
     per_m = {}
     for M in rows:
         sec = sum(a.elapsed_time(b) for a, b in ev[M]) * 1e-3 / args.steps
-        per_m[M] = dict(ms=sec * 1e3, gbs=step_bytes[M] / sec / 1e9, calls=len(calls[M]))
+        per_m[M] = dict(sec=sec, gbs=step_bytes[M] / sec / 1e9, calls=len(calls[M]))
     log("step %.3f ms, %.1f GB/s" % (ms_per_step, value))
 
-    # ----------------------------------------- dominant kernel: int8 GEMM ---
-    def mk(M, c):
-        l, p, K, N, X, Xq, rs, Y = c
-        return lambda: q.int8_gemm(Xq, 0, packed[(l, p)], 0, out_f32=Y, row_scale=rs, ws=ws)
-
+    # Dominant kernel: the int8 decode GEMM (k_int8_decode).  At M <= 16 each
+    # call is exactly one launch of it (activations quantised inside); at
+    # M = 32 a call is the row quantiser plus it.  Its average launch time is
+    # taken from graphs holding only its launches, replayed back to back and
+    # timed with HIP events on the replay stream (so the short dispatch gaps
+    # between launches are included).
+    kern_b, kern_t, n_launch = 0, 0.0, 0
     kern = {}
-    tot_b, tot_t, n_launch = 0, 0.0, 0
     for M in rows:
-        launches = [mk(M, c) for c in calls[M]]
-        durs = []
-        for _ in range(3):
-            durs.append(time_launches(torch, launches))
-        durs = np.min(np.array(durs), axis=0)   # best of 3 per launch
-        kb = sum(gemm_kernel_bytes(M, c[2], c[3]) for c in calls[M])
-        kern[M] = dict(avg_us=float(durs.mean() * 1e6), gbs=kb / float(durs.sum()) / 1e9)
-        tot_b += kb
-        tot_t += float(durs.sum())
-        n_launch += len(launches)
-    achieved = tot_b / tot_t / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_int8_decode", "avg_launch_us": round(tot_t / n_launch * 1e6, 3),
-                "launches_per_step": n_launch}
+        if M <= 16:
+            sec = per_m[M]["sec"]
+            kb = step_bytes[M]
+        else:
+            pre = []
+            for (l, p, K, N, X, Y) in calls[M]:
+                Xq, rs = q.quantize_rows_int8(X)
+                pre.append((packed[(l, p)], Xq, rs, Y))
+            torch.cuda.synchronize()
 
-    extra = {"per_m": {str(M): {"step_ms": round(per_m[M]["ms"], 4), "GB/s": round(per_m[M]["gbs"], 2),
+            def run_gemm(pre=pre):
+                for (pk, Xq, rs, Y) in pre:
+                    q.int8_gemm(Xq, 0, pk, 0, out_f32=Y, row_scale=rs)
+            run_gemm()
+            gk = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gk):
+                run_gemm()
+            gk.replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(args.steps):
+                gk.replay()
+            b.record()
+            torch.cuda.synchronize()
+            sec = a.elapsed_time(b) * 1e-3 / args.steps
+            kb = sum(c[2] * c[3] + 4 * c[3] + M * c[2] + 4 * M + 4 * M * c[3] for c in calls[M])
+        kern[M] = dict(us=sec / len(calls[M]) * 1e6, gbs=kb / sec / 1e9)
+        kern_b += kb
+        kern_t += sec
+        n_launch += len(calls[M])
+    achieved = kern_b / kern_t / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_int8_decode",
+                "avg_launch_us": round(kern_t / n_launch * 1e6, 3), "launches_per_step": n_launch}
+
+    extra = {"per_m": {str(M): {"step_ms": round(per_m[M]["sec"] * 1e3, 4), "GB/s": round(per_m[M]["gbs"], 2),
                                 "%HBM": round(100 * per_m[M]["gbs"] / HBM_PEAK_GBS, 2),
-                                "gemm_kernel_avg_us": round(kern[M]["avg_us"], 3),
-                                "gemm_kernel_GB/s": round(kern[M]["gbs"], 2)} for M in rows}}
+                                "call_us": round(per_m[M]["sec"] / per_m[M]["calls"] * 1e6, 3),
+                                "decode_kernel_us": round(kern[M]["us"], 3),
+                                "decode_kernel_GB/s": round(kern[M]["gbs"], 2)}
+                       for M in rows}}
 
     # --------------------------------------------- int8 prefill, M = 2048 ---
     if not args.no_extra:
@@ -223,6 +240,63 @@ def main() -> int:
                                      "%MFMA": round(100 * tops / INT8_PEAK_TOPS, 2)}
             del pk, A, Y
         extra["int8_prefill_m2048"] = pre
+
+        # ------------------------------- q4_1 product, M = 1 and 16 ---
+        q4 = {}
+        for i, (K, N) in enumerate(wl.Q4_SHAPES):
+            _, blocks = wl.q4_weight(K, N, seed_index=i)
+            bd = torch.from_numpy(blocks.reshape(-1)).to(dev)
+            ring = [q.q4_1_repack(bd, K, N) for _ in range(16)]   # 16 copies: ~590 MB, past the MALL
+            torch.cuda.synchronize()
+            wbytes = ring[0].data.numel() - 64
+            for M in wl.Q4_ROWS:
+                X = torch.from_numpy(wl.q4_activations(M, K, seed_index=i)).to(dev)
+                Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+                wsq = q.workspace(q.lib.qmm_q4_1_matmul_workspace_bytes(M, K, N), dev)
+                fs = [(lambda W=W, X=X, Y=Y, wsq=wsq: q.q4_1_matmul(X, W, out=Y, ws=wsq)) for W in ring]
+                fs[0]()
+                ts = np.array(time_launches(torch, fs * 3))
+                t = float(np.median(ts))
+                b = wbytes + 4 * M * K + 4 * M * N
+                q4["%dx%d_m%d" % (K, N, M)] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                                               "%HBM": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2)}
+            del ring, bd
+        extra["q4_1_matmul"] = q4
+
+        # --------------------------------------------- MUL_MAT_ID ---
+        d = wl.moe_inputs()
+        E, K, N = wl.MOE_EXPERTS, wl.MOE_K, wl.MOE_N
+        ed = torch.from_numpy(d["experts"]).to(dev)
+        rings = [q.q4_1_repack_experts(ed, K, N) for _ in range(4)]   # 4 copies: ~500 MB
+        X = torch.from_numpy(d["X"]).to(dev)
+        ids = torch.from_numpy(d["ids"]).to(dev)
+        Y = torch.empty((wl.MOE_TOKENS, wl.MOE_USED, N), dtype=torch.float32, device=dev)
+        wsm = q.workspace(q.lib.qmm_q4_1_matmul_id_workspace_bytes(wl.MOE_TOKENS, wl.MOE_USED, E, K, N), dev)
+        fs = [(lambda buf=buf, st=st: q.q4_1_matmul_id(X, buf, E, K, N, st, ids, wl.MOE_USED, out=Y, ws=wsm))
+              for buf, st in rings]
+        fs[0]()
+        t = float(np.median(time_launches(torch, fs * 5)))
+        wb = E * (rings[0][0].numel() // E - 64)
+        b = wb + X.numel() * 4 + wl.MOE_TOKENS * wl.MOE_IDS_STRIDE * 4 + Y.numel() * 4
+        extra["q4_1_matmul_id"] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                                   "%HBM": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2),
+                                   "experts": E, "tokens": wl.MOE_TOKENS, "top_k": wl.MOE_USED}
+        del rings, ed
+
+        # -------------------------------- one-time packing (a1, a5) ---
+        K, N = 4096, 14336
+        W = torch.from_numpy(wl.normal_f32(wl.rng(4, 77), (K, N), 0.02)).to(dev)
+        f = lambda: q.pack_b_int8(W)  # noqa: E731
+        f()
+        t = float(np.median(time_launches(torch, [f] * 5)))
+        extra["pack_b_int8_4096x14336"] = {"us": round(t * 1e6, 1), "GB/s": round((4 * K * N + K * N) / t / 1e9, 1)}
+        _, blocks = wl.q4_weight(K, N, seed_index=0)
+        bd = torch.from_numpy(blocks.reshape(-1)).to(dev)
+        f = lambda: q.q4_1_repack(bd, K, N)  # noqa: E731
+        f()
+        t = float(np.median(time_launches(torch, [f] * 5)))
+        extra["q4_1_repack_4096x14336"] = {"us": round(t * 1e6, 1), "GB/s": round(2 * blocks.nbytes / t / 1e9, 1)}
+        del W, bd
 
     # ------------------------------------------------------- CPU baseline ---
     cpu = None

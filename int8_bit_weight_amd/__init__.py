@@ -63,6 +63,9 @@ _SIGS = {
     "qmm_int8_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "int8_gemm": (_INT, [_P, _INT, _I64, _I64, _I64, _I32, _P, _INT, _I64, _I32,
                          ctypes.POINTER(qmm_epilogue), _P, _SZ, _P]),
+    "qmm_int8_gemm_dynamic_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "int8_gemm_dynamic": (_INT, [_P, _I64, _I64, _I64, _P, _I64, ctypes.POINTER(qmm_epilogue), _P, _I64, _P,
+                                 _P, _SZ, _P]),
     "qmm_q4_1_packed_bytes": (_SZ, [_I64, _I64]),
     "q4_1_repack": (_INT, [_P, _I64, _I64, _P, _SZ, _P]),
     "qmm_q4_1_matmul_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -238,6 +241,51 @@ def int8_gemm(A, zA: int, packedB: PackedInt8, zB: int = 0, *, out_i32=None, out
     wsz = 0 if ws is None else ws.numel() * ws.element_size()
     _check("int8_gemm", lib.int8_gemm(_ptr(A), at, M, K, A.stride(0), int(zA), _ptr(packedB.data), packedB.bt,
                                       N, int(zB), ctypes.byref(ep), _ptr(ws), wsz, _stream(stream)))
+    return out_i32, out_f32, out_q8
+
+
+def _epilogue(out_i32, out_f32, out_q8, q8_unsigned, row_scale, col_scale, scale, bias_f32, bias_i32, zp_out):
+    ep = qmm_epilogue()
+    outs = 0
+    if out_i32 is not None:
+        outs |= QMM_OUT_I32
+        ep.y_i32, ep.ld_i32 = out_i32.data_ptr(), out_i32.stride(0)
+    if out_f32 is not None:
+        outs |= QMM_OUT_F32
+        ep.y_f32, ep.ld_f32 = out_f32.data_ptr(), out_f32.stride(0)
+    if out_q8 is not None:
+        outs |= QMM_OUT_U8 if q8_unsigned else QMM_OUT_I8
+        ep.y_q8, ep.ld_q8 = out_q8.data_ptr(), out_q8.stride(0)
+    ep.outputs = outs
+    ep.row_scale = None if row_scale is None else row_scale.data_ptr()
+    ep.col_scale = None if col_scale is None else col_scale.data_ptr()
+    ep.scale = float(scale)
+    ep.bias_f32 = None if bias_f32 is None else bias_f32.data_ptr()
+    ep.bias_i32 = None if bias_i32 is None else bias_i32.data_ptr()
+    ep.zp_out = int(zp_out)
+    return ep
+
+
+def int8_gemm_dynamic(X, packedB: PackedInt8, *, out_i32=None, out_f32=None, out_q8=None, q8_unsigned=False,
+                      col_scale=None, scale: float = 1.0, bias_f32=None, bias_i32=None, zp_out: int = 0,
+                      xq_out=None, rs_out=None, ws=None, stream=None):
+    """fp32 activations quantised per row (amax/127) inside the product with a
+    weight packed by pack_b_int8; same results as quantize_rows_int8 followed
+    by int8_gemm.  Optionally also writes the quantised rows (xq_out) and the
+    row scales (rs_out)."""
+    M, K = X.shape
+    if K != packedB.K or packedB.bt != QMM_S8:
+        raise ValueError("weight must be an int8 weight packed for K=%d" % K)
+    N = packedB.N
+    ep = _epilogue(out_i32, out_f32, out_q8, q8_unsigned, None, col_scale, scale, bias_f32, bias_i32, zp_out)
+    need = lib.qmm_int8_gemm_dynamic_workspace_bytes(M, K, N)
+    if ws is None and need > 0:
+        ws = workspace(need, X.device)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    ldq = 0 if xq_out is None else xq_out.stride(0)
+    _check("int8_gemm_dynamic", lib.int8_gemm_dynamic(_ptr(X), M, K, X.stride(0), _ptr(packedB.data), N,
+                                                      ctypes.byref(ep), _ptr(xq_out), ldq, _ptr(rs_out), _ptr(ws),
+                                                      wsz, _stream(stream)))
     return out_i32, out_f32, out_q8
 
 

@@ -151,6 +151,62 @@ size_t qmm_int8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     return (size_t)plan_int8_gemm(M, K, N).ws_bytes;
 }
 
+// Output selection, leading dimensions and zero point (no pointer checks).
+static qmm_status check_epilogue(const qmm_epilogue *ep, int64_t N) {
+    const uint32_t outs = ep->outputs;
+    if (outs == 0 || (outs & ~15u) || ((outs & QMM_OUT_I8) && (outs & QMM_OUT_U8))) return QMM_ERR_INVALID;
+    if ((outs & QMM_OUT_I32) && ep->ld_i32 < N) return QMM_ERR_INVALID;
+    if ((outs & QMM_OUT_F32) && ep->ld_f32 < N) return QMM_ERR_INVALID;
+    if ((outs & (QMM_OUT_I8 | QMM_OUT_U8))) {
+        if (ep->ld_q8 < N) return QMM_ERR_INVALID;
+        const int32_t lo = (outs & QMM_OUT_U8) ? 0 : -128;
+        if (ep->zp_out < lo || ep->zp_out > lo + 255) return QMM_ERR_INVALID;
+    }
+    return QMM_OK;
+}
+
+// Output pointers of a non-empty product.
+static qmm_status check_epilogue_ptrs(const qmm_epilogue *ep) {
+    const uint32_t outs = ep->outputs;
+    if ((outs & QMM_OUT_I32) && (!ep->y_i32 || !aligned(ep->y_i32, 4))) return QMM_ERR_INVALID;
+    if ((outs & QMM_OUT_F32) && (!ep->y_f32 || !aligned(ep->y_f32, 4))) return QMM_ERR_INVALID;
+    if ((outs & (QMM_OUT_I8 | QMM_OUT_U8)) && !ep->y_q8) return QMM_ERR_INVALID;
+    return QMM_OK;
+}
+
+static void fill_params(Int8GemmParams &p, int64_t M, int64_t K, int64_t N, const void *packedB,
+                        const qmm_epilogue *ep) {
+    const PackedBLayout L = packed_b_layout(K, N);
+    const int8_t *base = (const int8_t *)packedB;
+    p.M = (int)M;
+    p.K = (int)K;
+    p.N = (int)N;
+    p.codes = base + L.codes_off;
+    p.colsum = (const int32_t *)(base + L.colsum_off);
+    p.KT = (int)L.KT;
+    p.NS = (int)L.NS;
+    p.outputs = ep->outputs;
+    p.y_i32 = ep->y_i32;
+    p.ld_i32 = ep->ld_i32;
+    p.y_f32 = ep->y_f32;
+    p.ld_f32 = ep->ld_f32;
+    p.y_q8 = (int8_t *)ep->y_q8;
+    p.ld_q8 = ep->ld_q8;
+    p.q8_u8 = (ep->outputs & QMM_OUT_U8) != 0;
+    p.row_scale = ep->row_scale;
+    p.col_scale = ep->col_scale ? ep->col_scale : (const float *)(base + L.scale_off);
+    p.scale = ep->scale;
+    p.bias_f32 = ep->bias_f32;
+    p.bias_i32 = ep->bias_i32;
+    p.zp_out = ep->zp_out;
+}
+
+static void trace_gemm(const char *fn, const char *variant, int64_t M, int64_t K, int64_t N, const Int8Plan &plan) {
+    if (trace_on())
+        fprintf(stderr, "qmm %s variant=%s M=%lld K=%lld N=%lld grid=%lld waves=%d tpw=%d\n", fn, variant,
+                (long long)M, (long long)K, (long long)N, (long long)plan.grid, plan.waves, plan.tpw);
+}
+
 qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t lda, int32_t zA,
                      const void *packedB, qmm_i8type bt, int64_t N, int32_t zB,
                      const qmm_epilogue *ep, void *workspace, size_t workspace_bytes,
@@ -161,59 +217,93 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
     if (lda < K) return QMM_ERR_INVALID;
     const int32_t za_lo = at == QMM_U8 ? 0 : -128, zb_lo = bt == QMM_U8 ? 0 : -128;
     if (zA < za_lo || zA > za_lo + 255 || zB < zb_lo || zB > zb_lo + 255) return QMM_ERR_INVALID;
-    const uint32_t outs = ep->outputs;
-    if (outs == 0 || (outs & ~15u) || ((outs & QMM_OUT_I8) && (outs & QMM_OUT_U8))) return QMM_ERR_INVALID;
+    qmm_status st = check_epilogue(ep, N);
+    if (st != QMM_OK) return st;
     if (!k_in_bound(K) || M > INT32_MAX || N > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return QMM_OK;
-    if (!A || !packedB || !aligned(packedB, 256)) return QMM_ERR_INVALID;
-    if ((outs & QMM_OUT_I32) && (!ep->y_i32 || ep->ld_i32 < N || !aligned(ep->y_i32, 4))) return QMM_ERR_INVALID;
-    if ((outs & QMM_OUT_F32) && (!ep->y_f32 || ep->ld_f32 < N || !aligned(ep->y_f32, 4))) return QMM_ERR_INVALID;
-    if ((outs & (QMM_OUT_I8 | QMM_OUT_U8))) {
-        if (!ep->y_q8 || ep->ld_q8 < N) return QMM_ERR_INVALID;
-        const int32_t lo = (outs & QMM_OUT_U8) ? 0 : -128;
-        if (ep->zp_out < lo || ep->zp_out > lo + 255) return QMM_ERR_INVALID;
-    }
-    const PackedBLayout L = packed_b_layout(K, N);
+    if (!A || !packedB || !aligned(packedB, 256) || check_epilogue_ptrs(ep) != QMM_OK) return QMM_ERR_INVALID;
     const Int8Plan plan = plan_int8_gemm(M, K, N);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
         return QMM_ERR_WORKSPACE;
 
     Int8GemmParams p{};
+    fill_params(p, M, K, N, packedB, ep);
     p.A = (const int8_t *)A;
     p.lda = lda;
-    p.M = (int)M;
-    p.K = (int)K;
-    p.N = (int)N;
     p.a_u8 = at == QMM_U8;
     p.a_vec = aligned(A, 16) && (lda % 16 == 0);
     p.zAs = zA - (at == QMM_U8 ? 128 : 0);
     p.zBs = zB - (bt == QMM_U8 ? 128 : 0);
-    const int8_t *base = (const int8_t *)packedB;
-    p.codes = base + L.codes_off;
-    p.colsum = (const int32_t *)(base + L.colsum_off);
-    p.KT = (int)L.KT;
-    p.NS = (int)L.NS;
-    p.outputs = outs;
-    p.y_i32 = ep->y_i32;
-    p.ld_i32 = ep->ld_i32;
-    p.y_f32 = ep->y_f32;
-    p.ld_f32 = ep->ld_f32;
-    p.y_q8 = (int8_t *)ep->y_q8;
-    p.ld_q8 = ep->ld_q8;
-    p.q8_u8 = (outs & QMM_OUT_U8) != 0;
-    p.row_scale = ep->row_scale;
-    p.col_scale = ep->col_scale ? ep->col_scale : (const float *)(base + L.scale_off);
-    p.scale = ep->scale;
-    p.bias_f32 = ep->bias_f32;
-    p.bias_i32 = ep->bias_i32;
-    p.zp_out = ep->zp_out;
     const char *variant = "";
-    qmm_status st = hip_status(launch_int8_gemm(plan, p, (hipStream_t)stream, &variant));
+    st = hip_status(launch_int8_gemm(plan, p, (hipStream_t)stream, &variant));
     g_last_variant = variant;
-    if (trace_on())
-        fprintf(stderr, "qmm int8_gemm variant=%s M=%lld K=%lld N=%lld grid=%lld waves=%d tpw=%d\n",
-                variant, (long long)M, (long long)K, (long long)N, (long long)plan.grid, plan.waves,
-                plan.tpw);
+    trace_gemm("int8_gemm", variant, M, K, N, plan);
+    return st;
+}
+
+size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M <= 0 || K <= 0 || N <= 0) return 0;
+    if (M <= 16) return (size_t)plan_int8_gemm(M, K, N).ws_bytes;
+    return (size_t)(round_up(M * K, 256) + round_up(4 * M, 256));
+}
+
+qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, const void *packedB, int64_t N,
+                             const qmm_epilogue *ep, int8_t *Xq, int64_t ldq, float *row_scale,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    if (M < 0 || N < 0 || K <= 0 || !ep || ldx < K) return QMM_ERR_INVALID;
+    if (ep->row_scale) return QMM_ERR_INVALID;  // the row scales are the computed ones
+    if (Xq && ldq < K) return QMM_ERR_INVALID;
+    qmm_status st = check_epilogue(ep, N);
+    if (st != QMM_OK) return st;
+    if (!k_in_bound(K) || M > INT32_MAX / 2 || N > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return QMM_OK;
+    if (!X || !packedB || !aligned(packedB, 256) || !aligned(X, 4) || (row_scale && !aligned(row_scale, 4)) ||
+        check_epilogue_ptrs(ep) != QMM_OK)
+        return QMM_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    if (M > 16) {
+        // The row quantiser, then the product.  Inside the product kernel
+        // every 16-column workgroup would quantise all M x K activations
+        // again, which above 16 rows costs more than the second launch.
+        int8_t *q = Xq;
+        float *rs = row_scale;
+        int64_t lq = ldq;
+        const size_t need = (q && rs) ? 0 : qmm_int8_gemm_dynamic_workspace_bytes(M, K, N);
+        if (need > 0) {
+            if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return QMM_ERR_WORKSPACE;
+            if (!q) {
+                q = (int8_t *)workspace;
+                lq = K;
+            }
+            if (!rs) rs = (float *)((int8_t *)workspace + round_up(M * K, 256));
+        }
+        st = quantize_rows_int8(X, M, K, ldx, q, lq, rs, stream);
+        if (st != QMM_OK) return st;
+        qmm_epilogue e2 = *ep;
+        e2.row_scale = rs;
+        return int8_gemm(q, QMM_S8, M, K, lq, 0, packedB, QMM_S8, N, 0, &e2, nullptr, 0, stream);
+    }
+    // 16 wavefronts, and enough k tiles per wavefront that one round covers
+    // K, so the activations stay in registers between the amax pass and the
+    // quantise pass when that takes at most 2 tiles (K <= 2048).
+    Int8Plan plan = plan_int8_gemm(M, K, N);
+    plan.waves = 16;
+    plan.tpw = (int)ceil_div(packed_b_layout(K, N).KT, 16);
+    plan.tpw = plan.tpw <= 1 ? 1 : (plan.tpw <= 2 ? 2 : 4);
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
+        return QMM_ERR_WORKSPACE;
+    Int8GemmParams p{};
+    fill_params(p, M, K, N, packedB, ep);
+    p.X = X;
+    p.ldx = ldx;
+    p.x_vec = aligned(X, 16) && (ldx % 4 == 0);
+    p.xq_out = Xq;
+    p.ldq = ldq;
+    p.rs_out = row_scale;
+    const char *variant = "";
+    st = hip_status(launch_int8_gemm_dynamic(plan, p, s, &variant));
+    g_last_variant = variant;
+    trace_gemm("int8_gemm_dynamic", variant, M, K, N, plan);
     return st;
 }
 

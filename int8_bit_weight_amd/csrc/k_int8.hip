@@ -130,22 +130,35 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float *__restrict__
 //   mult = fl32(fl32(rs[m]*cs[n]) * scale)
 //   F32  = fma(fl32(Y), mult, bias_f32[n])
 //   I8/U8: v = fl32(fl32(Y + bias_i32[n]) * mult); clamp(rne(v) + zp_out)
-__device__ __forceinline__ void epilogue_store(const Int8GemmParams &p, int m, int n, uint32_t S,
-                                               int32_t rowsum, bool has_zb) {
-    uint32_t Y = S - (uint32_t)p.zAs * (uint32_t)p.colsum[n];
+// Column operands of the epilogue for one output column.
+struct ColOps {
+    int32_t colsum;
+    float cs;
+    float bias_f;
+    int32_t bias_i;
+};
+
+__device__ __forceinline__ ColOps load_colops(const Int8GemmParams &p, int n) {
+    ColOps c;
+    c.colsum = p.zAs != 0 ? p.colsum[n] : 0;
+    c.cs = p.col_scale[n];
+    c.bias_f = p.bias_f32 ? p.bias_f32[n] : 0.0f;
+    c.bias_i = p.bias_i32 ? p.bias_i32[n] : 0;
+    return c;
+}
+
+__device__ __forceinline__ void epilogue_store_c(const Int8GemmParams &p, int m, int n, uint32_t S,
+                                                 int32_t rowsum, bool has_zb, float rs, const ColOps &c) {
+    uint32_t Y = S - (uint32_t)p.zAs * (uint32_t)c.colsum;
     if (has_zb) Y -= (uint32_t)p.zBs * ((uint32_t)rowsum - (uint32_t)p.K * (uint32_t)p.zAs);
     const int32_t y = (int32_t)Y;
     if (p.outputs & QMM_OUT_I32) p.y_i32[(int64_t)m * p.ld_i32 + n] = y;
     if (p.outputs & (QMM_OUT_F32 | QMM_OUT_I8 | QMM_OUT_U8)) {
-        const float rs = p.row_scale ? p.row_scale[m] : 1.0f;
-        const float rc = rs * p.col_scale[n];
+        const float rc = rs * c.cs;
         const float mult = rc * p.scale;
-        if (p.outputs & QMM_OUT_F32) {
-            const float b = p.bias_f32 ? p.bias_f32[n] : 0.0f;
-            p.y_f32[(int64_t)m * p.ld_f32 + n] = fmaf((float)y, mult, b);
-        }
+        if (p.outputs & QMM_OUT_F32) p.y_f32[(int64_t)m * p.ld_f32 + n] = fmaf((float)y, mult, c.bias_f);
         if (p.outputs & (QMM_OUT_I8 | QMM_OUT_U8)) {
-            const uint32_t acc = Y + (uint32_t)(p.bias_i32 ? p.bias_i32[n] : 0);
+            const uint32_t acc = Y + (uint32_t)c.bias_i;
             float v = (float)(int32_t)acc * mult;
             v = fminf(fmaxf(v, -65536.0f), 65536.0f);
             int q = (int)rintf(v) + p.zp_out;
@@ -154,6 +167,11 @@ __device__ __forceinline__ void epilogue_store(const Int8GemmParams &p, int m, i
             p.y_q8[(int64_t)m * p.ld_q8 + n] = (int8_t)(uint8_t)q;
         }
     }
+}
+
+__device__ __forceinline__ void epilogue_store(const Int8GemmParams &p, int m, int n, uint32_t S,
+                                               int32_t rowsum, bool has_zb, float rs) {
+    epilogue_store_c(p, m, n, S, rowsum, has_zb, rs, load_colops(p, n));
 }
 
 // 16 bytes of A' (shifted domain) for row `row`, k = k0 .. k0+15; zero where
@@ -185,6 +203,37 @@ __device__ __forceinline__ v4i load_a16(const Int8GemmParams &p, int row, int k0
     return v;
 }
 
+// 16 fp32 activations of row `row`, k = k0 .. k0+15 (zero outside M x K).
+__device__ __forceinline__ void load_x16(const Int8GemmParams &p, int row, int k0, float (&x)[16]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = 0.0f;
+    if (row >= p.M || k0 >= p.K) return;
+    const float *src = p.X + (int64_t)row * p.ldx + k0;
+    if (p.x_vec && k0 + 16 <= p.K) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const v4f v = *(const v4f *)(src + 4 * j);
+            x[4 * j] = v[0];
+            x[4 * j + 1] = v[1];
+            x[4 * j + 2] = v[2];
+            x[4 * j + 3] = v[3];
+        }
+        return;
+    }
+    for (int j = 0; j < 16; ++j)
+        if (k0 + j < p.K) x[j] = src[j];
+}
+
+// Codes of 16 activations for row scale s (same rule as k_quantize_rows).
+__device__ __forceinline__ v4i quant16(const float (&x)[16], float s) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (s > 0.0f) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) w[j >> 2] |= (uint32_t)(quant_code(x[j], s) & 0xFF) << (8 * (j & 3));
+    }
+    return v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+}
+
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
@@ -198,14 +247,33 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 // waves' 16x16 int32 tiles are summed in LDS in wave order and the epilogue
 // runs in the same workgroup: no cross-workgroup traffic, no atomics, no
 // fences, no workspace.
-template <int MT, int WAVES, int TPW, bool HAS_ZB>
+template <int MT, int WAVES, int TPW, bool HAS_ZB, bool QUANT>
 __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
     constexpr int NE = MT * 256;  // elements of the (MT*16) x 16 output tile
     constexpr int NT = WAVES * 64;
+    constexpr int ROWS = MT * 16;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int strip = blockIdx.x;
     const int8_t *strip_codes = p.codes + (int64_t)strip * p.KT * kTileBytes + lane * 16;
+
+    __shared__ float s_amax[WAVES][ROWS];
+    __shared__ float s_scale[ROWS];
+    __shared__ ColOps s_col[16];
+    // Epilogue operands are fetched now so their latency overlaps the stream.
+    if (threadIdx.x < 16) {
+        const int n = strip * kTileN + threadIdx.x;
+        s_col[threadIdx.x] = n < p.N ? load_colops(p, n) : ColOps{0, 0.0f, 0.0f, 0};
+    } else if (!QUANT && threadIdx.x >= 64 && threadIdx.x < 64 + ROWS) {
+        const int m = threadIdx.x - 64;
+        s_scale[m] = (p.row_scale && m < p.M) ? p.row_scale[m] : 1.0f;
+    }
+    // Activations stay in registers between the two passes when TPW*MT is
+    // small and one round of the wavefronts covers all of K; otherwise the
+    // second pass reloads them (L1/L2 hits).
+    constexpr bool KEEP_T = QUANT && (TPW * MT <= 2);
+    const bool keep = KEEP_T && p.KT <= WAVES * TPW;
+    float xk[KEEP_T ? TPW : 1][KEEP_T ? MT : 1][16];
 
     v4i acc[MT];
     v4i accr[MT];
@@ -216,21 +284,93 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
     }
     const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
-    for (int base = wave; base < p.KT; base += WAVES * TPW) {
-        v4i bf[TPW];
-        v4i af[TPW][MT];
+    v4i bf[TPW];
+    auto load_b = [&](int base) {
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int kt = base + i * WAVES;
             bf[i] = kt < p.KT ? *(const v4i *)(strip_codes + (int64_t)kt * kTileBytes) : v4i{0, 0, 0, 0};
         }
+    };
+
+    if (QUANT) {
+        // The first round's weight tiles are in flight while the row maxima
+        // are found: every workgroup covers all of K for its strip, so the
+        // maxima over its wavefronts are the full-row maxima.
+        load_b(wave);
+        float lmax[MT];
+#pragma unroll
+        for (int r = 0; r < MT; ++r) lmax[r] = 0.0f;
+        for (int base = wave; base < p.KT; base += WAVES * TPW) {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int kt = base + i * WAVES;
+                if (kt < p.KT) {
+#pragma unroll
+                    for (int r = 0; r < MT; ++r) {
+                        float x[16];
+                        load_x16(p, r * 16 + (lane & 15), kt * kTileK + (lane >> 4) * 16, x);
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) lmax[r] = fmaxf(lmax[r], fabsf(x[j]));
+                        if (KEEP_T && keep) {
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) xk[KEEP_T ? i : 0][KEEP_T ? r : 0][j] = x[j];
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < MT; ++r) {
+            lmax[r] = fmaxf(lmax[r], __shfl_xor(lmax[r], 16));
+            lmax[r] = fmaxf(lmax[r], __shfl_xor(lmax[r], 32));
+            if (lane < 16) s_amax[wave][r * 16 + lane] = lmax[r];
+        }
+        __syncthreads();
+        if (threadIdx.x < ROWS) {
+            float a = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) a = fmaxf(a, s_amax[w][threadIdx.x]);
+            s_scale[threadIdx.x] = (a == 0.0f) ? 0.0f : a / 127.0f;
+            if (p.rs_out && strip == 0 && (int)threadIdx.x < p.M) p.rs_out[threadIdx.x] = s_scale[threadIdx.x];
+        }
+        __syncthreads();
+    }
+
+    for (int base = wave; base < p.KT; base += WAVES * TPW) {
+        if (!QUANT || base != wave) load_b(base);
+        v4i af[TPW][MT];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int kt = base + i * WAVES;
 #pragma unroll
-            for (int r = 0; r < MT; ++r)
-                af[i][r] = kt < p.KT ? load_a16(p, r * 16 + (lane & 15), kt * kTileK + (lane >> 4) * 16)
-                                     : v4i{0, 0, 0, 0};
+            for (int r = 0; r < MT; ++r) {
+                const int row = r * 16 + (lane & 15);
+                const int k0 = kt * kTileK + (lane >> 4) * 16;
+                if (kt >= p.KT) {
+                    af[i][r] = v4i{0, 0, 0, 0};
+                } else if (QUANT) {
+                    float x[16];
+                    if (KEEP_T && keep) {
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) x[j] = xk[KEEP_T ? i : 0][KEEP_T ? r : 0][j];
+                    } else {
+                        load_x16(p, row, k0, x);
+                    }
+                    af[i][r] = quant16(x, s_scale[row]);
+                    if (p.xq_out && strip == 0 && row < p.M && k0 < p.K) {
+                        int8_t *dst = p.xq_out + (int64_t)row * p.ldq + k0;
+                        if (k0 + 16 <= p.K && (((uintptr_t)dst) & 15) == 0) {
+                            *(v4i *)dst = af[i][r];
+                        } else {
+                            for (int j = 0; j < 16 && k0 + j < p.K; ++j)
+                                dst[j] = (int8_t)((uint32_t)af[i][r][j >> 2] >> (8 * (j & 3)));
+                        }
+                    }
+                } else {
+                    af[i][r] = load_a16(p, row, k0);
+                }
+            }
         }
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -242,9 +382,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
         }
     }
 
-    __shared__ int32_t s_red[WAVES][MT * 16][17];
-    __shared__ int32_t s_redr[WAVES][MT * 16];
-    __shared__ int32_t s_rowsum[MT * 16];
+    __shared__ int32_t s_red[WAVES][ROWS][17];
+    __shared__ int32_t s_redr[WAVES][ROWS];
+    __shared__ int32_t s_rowsum[ROWS];
 #pragma unroll
     for (int r = 0; r < MT; ++r)
 #pragma unroll
@@ -255,7 +395,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
         }
     __syncthreads();
     if (HAS_ZB) {
-        if (threadIdx.x < MT * 16) {
+        if (threadIdx.x < ROWS) {
             int32_t rsum = 0;
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) rsum += s_redr[w][threadIdx.x];
@@ -270,7 +410,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
             int32_t v = 0;
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) v += s_red[w][m][e & 15];
-            epilogue_store(p, m, n, (uint32_t)v, HAS_ZB ? s_rowsum[m] : 0, HAS_ZB);
+            epilogue_store_c(p, m, n, (uint32_t)v, HAS_ZB ? s_rowsum[m] : 0, HAS_ZB, s_scale[m], s_col[e & 15]);
         }
     }
 }
@@ -362,35 +502,38 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
                 const int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + v;
                 const int n = (strip0 + wn * 4 + j) * kTileN + (lane & 15);
                 if (m < p.M && n < p.N)
-                    epilogue_store(p, m, n, (uint32_t)acc[i][j][v], HAS_ZB ? accr[i][v] : 0, HAS_ZB);
+                    epilogue_store(p, m, n, (uint32_t)acc[i][j][v], HAS_ZB ? accr[i][v] : 0, HAS_ZB,
+                                   p.row_scale ? p.row_scale[m] : 1.0f);
             }
 }
 
-template <int MT, int WAVES, int TPW>
+template <int MT, int WAVES, int TPW, bool QUANT>
 hipError_t launch_decode(const Int8GemmParams &p, hipStream_t s) {
     if (p.zBs != 0)
-        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, true>), dim3((unsigned)p.NS), dim3(WAVES * 64), 0, s, p);
+        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, true, QUANT>), dim3((unsigned)p.NS), dim3(WAVES * 64), 0,
+                           s, p);
     else
-        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, false>), dim3((unsigned)p.NS), dim3(WAVES * 64), 0, s, p);
+        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, false, QUANT>), dim3((unsigned)p.NS), dim3(WAVES * 64),
+                           0, s, p);
     return hipGetLastError();
 }
 
-template <int MT, int WAVES>
+template <int MT, int WAVES, bool QUANT>
 hipError_t launch_decode_tpw(const Int8GemmParams &p, int tpw, hipStream_t s) {
     switch (tpw) {
-        case 1: return launch_decode<MT, WAVES, 1>(p, s);
-        case 2: return launch_decode<MT, WAVES, 2>(p, s);
-        case 4: return launch_decode<MT, WAVES, 4>(p, s);
+        case 1: return launch_decode<MT, WAVES, 1, QUANT>(p, s);
+        case 2: return launch_decode<MT, WAVES, 2, QUANT>(p, s);
+        case 4: return launch_decode<MT, WAVES, 4, QUANT>(p, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int MT>
+template <int MT, bool QUANT>
 hipError_t launch_decode_waves(const Int8GemmParams &p, int waves, int tpw, hipStream_t s) {
     switch (waves) {
-        case 4: return launch_decode_tpw<MT, 4>(p, tpw, s);
-        case 8: return launch_decode_tpw<MT, 8>(p, tpw, s);
-        case 16: return launch_decode_tpw<MT, 16>(p, tpw, s);
+        case 4: return launch_decode_tpw<MT, 4, QUANT>(p, tpw, s);
+        case 8: return launch_decode_tpw<MT, 8, QUANT>(p, tpw, s);
+        case 16: return launch_decode_tpw<MT, 16, QUANT>(p, tpw, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -430,8 +573,8 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
                             const char **variant) {
     if (plan.variant == 0) {
         *variant = plan.mt == 1 ? "int8_decode_m16" : "int8_decode_m32";
-        if (plan.mt == 1) return launch_decode_waves<1>(p, plan.waves, plan.tpw, s);
-        return launch_decode_waves<2>(p, plan.waves, plan.tpw, s);
+        if (plan.mt == 1) return launch_decode_waves<1, false>(p, plan.waves, plan.tpw, s);
+        return launch_decode_waves<2, false>(p, plan.waves, plan.tpw, s);
     }
     *variant = "int8_prefill_128x128";
     dim3 grid((unsigned)ceil_div(p.NS, PF_BN / kTileN), (unsigned)ceil_div(p.M, PF_BM));
@@ -440,6 +583,14 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
     else
         hipLaunchKernelGGL((k_int8_prefill<false>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
+                                    const char **variant) {
+    if (plan.variant != 0) return hipErrorInvalidValue;
+    *variant = plan.mt == 1 ? "int8_dynamic_m16" : "int8_dynamic_m32";
+    if (plan.mt == 1) return launch_decode_waves<1, true>(p, plan.waves, plan.tpw, s);
+    return launch_decode_waves<2, true>(p, plan.waves, plan.tpw, s);
 }
 
 }  // namespace qmm

@@ -93,6 +93,13 @@ struct Int8GemmParams {
     const float *bias_f32;
     const int32_t *bias_i32;
     int32_t zp_out;
+    // dynamic variant: fp32 activations quantised per row inside the kernel
+    const float *X;
+    int64_t ldx;
+    int x_vec;             // 1: X and ldx allow aligned 16-byte loads
+    int8_t *xq_out;        // optional copies of the quantised rows / scales
+    int64_t ldq;
+    float *rs_out;
 };
 
 struct Int8Plan {
@@ -114,6 +121,8 @@ hipError_t launch_quantize_rows(const float *X, int64_t M, int64_t K, int64_t ld
                                 int64_t ldq, float *row_scale, hipStream_t s);
 hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                             const char **variant);
+hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
+                                    const char **variant);
 
 }  // namespace qmm
 

@@ -272,3 +272,53 @@ def test_workspace_shared_across_shapes(q, orc):
         q.int8_gemm(to_dev(A), 1, p, -2, out_i32=y, ws=ws)
         assert np.array_equal(to_np(y), orc.int8_gemm_i64(A, 1, B, -2).astype(np.int32)), (M, K, N)
     assert (to_np(ws) == 0).all()
+
+
+# ------------------------------------------------- dynamic (fused) path ---
+
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 2048), (16, 1024, 1024), (32, 3072, 1024), (16, 2048, 1024),
+                                   (16, 3072, 1024), (1, 3072, 64), (3, 100, 37), (17, 1056, 17), (33, 320, 48),
+                                   (80, 256, 130), (16, 64, 16)])
+def test_dynamic_matches_two_step_and_oracle(q, orc, M, K, N):
+    """int8_gemm_dynamic == quantize_rows_int8 + int8_gemm bit for bit (fp32
+    output, quantised rows, row scales), and the oracle's int32 product."""
+    import torch
+    dev = torch_dev()
+    g = np.random.default_rng(M + K + N)
+    W = wl.normal_f32(g, (K, N), 0.02)
+    X = wl.normal_f32(g, (M, K))
+    X[0] = 0.0
+    p = q.pack_b_int8(to_dev(W))
+    Xd = to_dev(X)
+    Xq2, rs2 = q.quantize_rows_int8(Xd)
+    y2 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q.int8_gemm(Xq2, 0, p, 0, out_f32=y2, row_scale=rs2)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    y32 = torch.empty((M, N), dtype=torch.int32, device=dev)
+    xq = torch.full((M, K), 99, dtype=torch.int8, device=dev)
+    rs = torch.full((M,), -1.0, dtype=torch.float32, device=dev)
+    q.int8_gemm_dynamic(Xd, p, out_f32=y, out_i32=y32, xq_out=xq, rs_out=rs)
+    if M <= 16:
+        assert q.last_variant() == "int8_dynamic_m16"
+    elif M <= 32:
+        assert q.last_variant() == "int8_decode_m32"
+    assert np.array_equal(to_np(y).view(np.uint32), to_np(y2).view(np.uint32))
+    assert np.array_equal(to_np(xq), to_np(Xq2))
+    assert np.array_equal(to_np(rs).view(np.uint32), to_np(rs2).view(np.uint32))
+    Qa, sa = orc.quantize_rows_int8(X)
+    Qb, sb, _ = orc.pack_b_int8(W)
+    Y64 = orc.int8_gemm_i64(Qa, 0, Qb, 0)
+    assert np.array_equal(to_np(y32), Y64.astype(np.int32))
+    assert max_rel_err(to_np(y), orc.epilogue_f64(Y64, sa, sb)) <= F32_TOL
+
+
+def test_dynamic_without_side_outputs(q, orc):
+    import torch
+    W = wl.projection_weight(1, 6)
+    X = wl.projection_activations(16, W.shape[0], seed_index=3)
+    p = q.pack_b_int8(to_dev(W))
+    y = torch.empty((16, W.shape[1]), dtype=torch.float32, device=torch_dev())
+    q.int8_gemm_dynamic(to_dev(X), p, out_f32=y)
+    Qa, sa = orc.quantize_rows_int8(X)
+    Qb, sb, _ = orc.pack_b_int8(W)
+    assert max_rel_err(to_np(y), orc.epilogue_f64(orc.int8_gemm_i64(Qa, 0, Qb, 0), sa, sb)) <= F32_TOL
