@@ -13,47 +13,45 @@ namespace qmm {
 // Set by every entry point (defined in api.cpp).
 qmm_status record_status(hipError_t e, const char *variant);
 
-// Dense q4_1: rows run in launches of up to 32 (two 16-row MFMA tiles).  A
-// workgroup is 4 wavefronts x 4 strips = 256 columns and a k range of `qps`
-// records; the k range is split S ways so that about `target` workgroups are
-// in flight, and the S partial results are summed in split order by a
-// second kernel.  Fewer splits at larger M keep the partial traffic (S*M*N
-// floats) small next to the weight bytes.
+// Dense q4_1: rows run in launches of up to 32 (one or two 16-row MFMA
+// tiles).  A workgroup is 8 wavefronts x 2 strips = 256 columns and a k
+// range of `qps` records (a multiple of the chunk, 2 records at 16 rows, 1
+// at 32).  The k range is split S ways so that about `target` workgroups are
+// in flight; the S partial results are summed in split order by a second
+// kernel.  Fewer splits at larger M keep the partial traffic (S*M*N floats)
+// small next to the weight bytes.
 Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
     Q4Plan pl{};
     const Q4Layout L = q4_layout(K, N);
     pl.rows_per_launch = M < 32 ? M : 32;
     pl.mt = pl.rows_per_launch <= 16 ? 1 : 2;
-    pl.waves = 4;
-    const int64_t groups = ceil_div(L.NS, 4 * pl.waves);
+    pl.waves = 8;
+    const int64_t qc = pl.mt == 1 ? 2 : 1;
+    const int64_t groups = ceil_div(L.NS, 2 * pl.waves);
     const int64_t target = pl.rows_per_launch <= 4 ? 512 : 256;
     int64_t S = ceil_div(target, groups);
-    const int64_t max_s = ceil_div(L.NQ, 2);
+    const int64_t max_s = ceil_div(L.NQ, qc);
     if (S > max_s) S = max_s;
     if (S < 1) S = 1;
-    int64_t qps = ceil_div(L.NQ, S);
-    qps = round_up(qps, 2);
+    int64_t qps = round_up(ceil_div(L.NQ, S), qc);
     S = ceil_div(L.NQ, qps);
     pl.S = (int)S;
     pl.qps = (int)qps;
     pl.grid = groups * S;
-    pl.ws_xsp_off = 0;
-    pl.ws_xs_off = round_up(M * L.NB * 3 * 32 * 2, 256);
-    pl.ws_part_off = pl.ws_xs_off + round_up(M * L.NB * 4, 256);
-    pl.ws_bytes = pl.ws_part_off + (S > 1 ? round_up(S * pl.rows_per_launch * N * 4, 256) : 0);
+    pl.ws_part_off = 0;
+    pl.ws_bytes = S > 1 ? round_up(S * pl.rows_per_launch * N * 4, 256) : 0;
     return pl;
 }
 
 MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N) {
     MoePlan pl{};
-    const Q4Layout L = q4_layout(K, N);
     const int64_t P = T * n_used;
+    (void)K;
+    (void)N;
     pl.rpc = 32;
     pl.max_chunks = ceil_div(P, pl.rpc) + E;
-    pl.ws_xsp_off = 0;
-    pl.ws_xs_off = round_up(T * L.NB * 3 * 32 * 2, 256);
-    pl.ws_sorted_off = pl.ws_xs_off + round_up(T * L.NB * 4, 256);
-    pl.ws_chunk_off = pl.ws_sorted_off + round_up(P * 4, 256);
+    pl.ws_sorted_off = 0;
+    pl.ws_chunk_off = round_up(P * 4, 256);
     pl.ws_misc_off = pl.ws_chunk_off + round_up(pl.max_chunks * 3 * 4, 256);
     pl.ws_bytes = pl.ws_misc_off + 256;
     return pl;
@@ -98,13 +96,10 @@ qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx, const 
         return QMM_ERR_INVALID;
     const Q4Layout L = q4_layout(K, N);
     const Q4Plan pl = plan_q4_matmul(M, K, N);
-    if (!workspace || workspace_bytes < (size_t)pl.ws_bytes || !aligned_to(workspace, 256))
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)pl.ws_bytes || !aligned_to(workspace, 256)))
         return QMM_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    uint8_t *ws = (uint8_t *)workspace;
-    uint16_t *xsp = (uint16_t *)(ws + pl.ws_xsp_off);
-    float *xs = (float *)(ws + pl.ws_xs_off);
-    hipError_t e = launch_q4_xsplit(X, ldx, M, L.NB, xsp, xs, s);
+    hipError_t e = hipSuccess;
     const char *variant = "";
     for (int64_t r0 = 0; r0 < M && e == hipSuccess; r0 += pl.rows_per_launch) {
         const int64_t rows = (M - r0) < pl.rows_per_launch ? (M - r0) : pl.rows_per_launch;
@@ -115,12 +110,13 @@ qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx, const 
         p.NS = (int)L.NS;
         p.N = (int)N;
         p.K = (int)K;
-        p.xsp = xsp + r0 * L.NB * 96;
-        p.xs = xs + r0 * L.NB;
+        p.X = X + r0 * ldx;
+        p.ldx = ldx;
+        p.x_vec = aligned_to(X, 16) && (ldx % 4 == 0);
         p.M = (int)rows;
         p.Y = Y + r0 * ldy;
         p.ldy = ldy;
-        p.part = (float *)(ws + pl.ws_part_off);
+        p.part = (float *)((uint8_t *)workspace + pl.ws_part_off);
         p.S = pl.S;
         p.qps = pl.qps;
         e = launch_q4_dense(p, pl.mt, pl.waves, pl.grid, s, &variant);
@@ -155,15 +151,11 @@ qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t l
         return QMM_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = (uint8_t *)workspace;
-    uint16_t *xsp = (uint16_t *)(ws + pl.ws_xsp_off);
-    float *xs = (float *)(ws + pl.ws_xs_off);
     int32_t *sorted = (int32_t *)(ws + pl.ws_sorted_off);
     int32_t *chunk_info = (int32_t *)(ws + pl.ws_chunk_off);
     int32_t *misc = (int32_t *)(ws + pl.ws_misc_off);
-    hipError_t e = launch_q4_xsplit(X, ldx, n_tokens, L.NB, xsp, xs, s);
-    if (e == hipSuccess)
-        e = launch_moe_route(ids, ids_row_stride, n_tokens, n_used, n_expert, pl.rpc, sorted, chunk_info, misc,
-                             misc + 1, s);
+    hipError_t e = launch_moe_route(ids, ids_row_stride, n_tokens, n_used, n_expert, pl.rpc, sorted, chunk_info,
+                                    misc, misc + 1, s);
     const char *variant = "";
     if (e == hipSuccess) {
         Q4Params p{};
@@ -174,8 +166,9 @@ qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t l
         p.NS = (int)L.NS;
         p.N = (int)N;
         p.K = (int)K;
-        p.xsp = xsp;
-        p.xs = xs;
+        p.X = X;
+        p.ldx = ldx;
+        p.x_vec = aligned_to(X, 16) && (ldx % 4 == 0);
         p.Y = Y;
         p.sorted = sorted;
         p.chunk_info = chunk_info;

@@ -1,9 +1,9 @@
 // k_q4_1.hip -- q4_1 path kernels for gfx950 (CDNA4, wave64):
 //   * repack of canonical q4_1 blocks into the record layout (qmm_internal.h)
-//   * activation split: x = x0 + x1 + x2 with bf16 terms (near exact), plus
-//     fp32 block sums of x
-//   * the q4_1 product on MFMA (v_mfma_f32_16x16x32_bf16): one 32-k block is
-//     one MFMA k-step, so each block gets a fresh accumulator and
+//   * the q4_1 product on MFMA (v_mfma_f32_16x16x32_bf16) with fp32
+//     activations split in-kernel into three bf16 terms (x = x0 + x1 + x2,
+//     near exact): one 32-k block is one MFMA k-step, so each block gets a
+//     fresh accumulator and
 //       Y += d * (sum_k q*x) + m * (sum_k x)
 //     ("NPU engine: full ELFs, no xclbin", "Q4NX chunks": q4_1 blocks;
 //     "Zaya 8B Q4NX on the AMD NPU", "Round 26": W = q*scale + min with bf16
@@ -90,62 +90,34 @@ __global__ __launch_bounds__(256) void k_q4_repack(const uint8_t *__restrict__ b
     if (g == 0) *(v4i *)(dst + 1024 + c * 16) = v4i{(int)dm[0], (int)dm[1], (int)dm[2], (int)dm[3]};
 }
 
-// ---------------------------------------------------- activation split ---
-// One thread per (row, k).  x0 = bf16(x), x1 = bf16(x - x0), x2 = bf16(x - x0 - x1)
-// (both differences are exact in fp32), stored [row][block][term][32].  The
-// 32 lanes of a block also sum x in a fixed butterfly order.
-__global__ __launch_bounds__(256) void k_q4_xsplit(const float *__restrict__ X, int64_t ldx, int R, int NB,
-                                                   uint16_t *__restrict__ xsp, float *__restrict__ xs) {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t per_row = (int64_t)NB * 32;
-    const bool valid = gid < (int64_t)R * per_row;
-    const int64_t row = gid / per_row;
-    const int64_t rem = gid % per_row;
-    const int64_t b = rem >> 5;
-    const int j = (int)(rem & 31);
-    const float x = valid ? X[row * ldx + b * 32 + j] : 0.0f;
-    const uint32_t t0 = bf16_rne_bits(x);
-    const float r1 = x - bf16_bits_f32(t0);
-    const uint32_t t1 = bf16_rne_bits(r1);
-    const float r2 = r1 - bf16_bits_f32(t1);
-    const uint32_t t2 = bf16_rne_bits(r2);
-    float s = x;
-#pragma unroll
-    for (int off = 16; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (valid) {
-        uint16_t *dst = xsp + ((row * NB + b) * 3) * 32 + j;
-        dst[0] = (uint16_t)t0;
-        dst[32] = (uint16_t)t1;
-        dst[64] = (uint16_t)t2;
-        if (j == 0) xs[row * NB + b] = s;
-    }
-}
-
 // ----------------------------------------------------------- the product ---
-// Workgroup = WAVES wavefronts; each wavefront owns 4 column strips (64
-// columns) and all MT*16 rows of the workgroup's row set.  The split
-// activations of the rows are staged in LDS in chunks of KCB blocks (double
-// buffered, next chunk's global loads issued before the current chunk's
-// MFMAs) and shared by all wavefronts; each wavefront streams its strips'
-// records (16 bytes of codes + 16 bytes of (d,m) per lane per record, one
-// record prefetched ahead) and keeps its outputs in registers across the
-// whole k range.
+// Workgroup = WAVES wavefronts; each wavefront owns C column strips (16 C
+// columns) and all MT*16 rows of the workgroup's row set.  The k range is
+// walked in chunks of QC records (4 QC blocks of 32 k):
+//   * activations: the workgroup reads its rows' fp32 values for the chunk,
+//     splits each into three bf16 terms (x = x0 + x1 + x2; both differences
+//     are exact in fp32), sums each 32-k block in a fixed order, and stores
+//     the terms as MFMA A fragments in LDS (double buffered: the next chunk's
+//     global loads are issued before the current chunk's MFMAs);
+//   * weights: each wavefront streams its strips' records (16 bytes of codes
+//     and 16 bytes of (d, m) per lane per record), one chunk ahead in
+//     registers;
+//   * per block and strip: codes -> exact bf16, three MFMAs into a fresh
+//     accumulator, then y += d * acc + m * sum_k(x).
 //   dense: blockIdx -> (strip group, k split); rows 0..M-1.
 //   MoE:   blockIdx -> (strip group, row chunk); the chunk table gives the
 //          expert and the sorted (token, slot) pairs of its rows.
-template <int MT, int WAVES, bool MOE>
-__global__ __launch_bounds__(WAVES * 64) void k_q4_mm(Q4Params p) {
+template <int MT, int WAVES, int C, int QC, bool MOE, int MINW>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_mm(Q4Params p) {
     constexpr int NT = WAVES * 64;
     constexpr int ROWS = MT * 16;
-    constexpr int SPW = 4;
-    constexpr int SPG = SPW * WAVES;
-    constexpr int APIECES = KCB * 3 * ROWS * 4;
-    constexpr int APT = (APIECES + NT - 1) / NT;
-    constexpr int XPIECES = KCB * ROWS;
-    constexpr int XPT = (XPIECES + NT - 1) / NT;
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][KCB][3][MT][1024];
-    __shared__ __attribute__((aligned(16))) float sXS[2][KCB][ROWS];
-    __shared__ int sTok[ROWS];
+    constexpr int SPG = C * WAVES;
+    constexpr int BPC = 4 * QC;
+    constexpr int PIECES = BPC * ROWS * 4;  // (block, row, k-octet) pieces of a chunk
+    constexpr int PPT = (PIECES + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BPC][3][MT][1024];
+    __shared__ __attribute__((aligned(16))) float sXS[2][BPC][ROWS];
+    __shared__ int64_t sRow[ROWS];  // element offset of each row of X, -1 = zero row
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -170,147 +142,173 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm(Q4Params p) {
         q1 = min(p.NQ, q0 + p.qps);
     }
     recs += kHeaderBytes;
-    if (tid < ROWS) sTok[tid] = (tid < nrows) ? (MOE ? p.sorted[row0 + tid] / p.n_used : tid) : -1;
+    if (tid < ROWS) {
+        int64_t off = -1;
+        if (tid < nrows) off = (int64_t)(MOE ? p.sorted[row0 + tid] / p.n_used : tid) * p.ldx;
+        sRow[tid] = off;
+    }
     __syncthreads();
 
-    v4i stg[APT];
-    float stx[XPT];
-    auto gload_chunk = [&](int qc) {
-        const int b0 = qc * 4;
+    // ---- activation staging
+    float xr[PPT][8];
+    auto gload_a = [&](int qc) {
 #pragma unroll
-        for (int i = 0; i < APT; ++i) {
+        for (int i = 0; i < PPT; ++i) {
             const int idx = tid + i * NT;
-            v4i v = {0, 0, 0, 0};
-            if (idx < APIECES) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[i][e] = 0.0f;
+            if (idx < PIECES) {
                 const int g = idx & 3;
-                const int t = (idx >> 2) % 3;
-                const int rest = (idx >> 2) / 3;
-                const int row = rest % ROWS;
-                const int b = b0 + rest / ROWS;
-                const int tok = sTok[row];
-                if (tok >= 0 && b < p.NB)
-                    v = *(const v4i *)(p.xsp + (((int64_t)tok * p.NB + b) * 3 + t) * 32 + g * 8);
-            }
-            stg[i] = v;
-        }
+                const int row = (idx >> 2) % ROWS;
+                const int b = qc * 4 + (idx >> 2) / ROWS;
+                const int64_t off = sRow[row];
+                if (off >= 0 && b < p.NB) {
+                    const float *src = p.X + off + b * 32 + g * 8;
+                    if (p.x_vec) {
+                        const v4f lo = *(const v4f *)src;
+                        const v4f hi = *(const v4f *)(src + 4);
+                        xr[i][0] = lo[0]; xr[i][1] = lo[1]; xr[i][2] = lo[2]; xr[i][3] = lo[3];
+                        xr[i][4] = hi[0]; xr[i][5] = hi[1]; xr[i][6] = hi[2]; xr[i][7] = hi[3];
+                    } else {
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int idx = tid + i * NT;
-            float v = 0.0f;
-            if (idx < XPIECES) {
-                const int row = idx % ROWS;
-                const int b = b0 + idx / ROWS;
-                const int tok = sTok[row];
-                if (tok >= 0 && b < p.NB) v = p.xs[(int64_t)tok * p.NB + b];
+                        for (int e = 0; e < 8; ++e) xr[i][e] = src[e];
+                    }
+                }
             }
-            stx[i] = v;
         }
     };
-    auto sstore_chunk = [&](int buf) {
+    auto sstore_a = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < APT; ++i) {
+        for (int i = 0; i < PPT; ++i) {
             const int idx = tid + i * NT;
-            if (idx < APIECES) {
-                const int g = idx & 3;
-                const int t = (idx >> 2) % 3;
-                const int rest = (idx >> 2) / 3;
-                const int row = rest % ROWS;
-                const int bl = rest / ROWS;
-                *(v4i *)(&sA[buf][bl][t][row >> 4][(g * 16 + (row & 15)) * 16]) = stg[i];
+            float bsum = 0.0f;
+            uint32_t w[3][4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                uint32_t t[3][2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float x = xr[i][e + h];
+                    bsum += x;
+                    t[0][h] = bf16_rne_bits(x);
+                    const float r1 = x - bf16_bits_f32(t[0][h]);
+                    t[1][h] = bf16_rne_bits(r1);
+                    const float r2 = r1 - bf16_bits_f32(t[1][h]);
+                    t[2][h] = bf16_rne_bits(r2);
+                }
+#pragma unroll
+                for (int tt = 0; tt < 3; ++tt) w[tt][e >> 1] = t[tt][0] | (t[tt][1] << 16);
             }
-        }
+            // the four k-octets of one (row, block) sit in four adjacent lanes
+            bsum += __shfl_xor(bsum, 1);
+            bsum += __shfl_xor(bsum, 2);
+            if (idx < PIECES) {
+                const int g = idx & 3;
+                const int row = (idx >> 2) % ROWS;
+                const int bl = (idx >> 2) / ROWS;
+                uint8_t *dst = &sA[buf][bl][0][row >> 4][(g * 16 + (row & 15)) * 16];
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int idx = tid + i * NT;
-            if (idx < XPIECES) sXS[buf][idx / ROWS][idx % ROWS] = stx[i];
-        }
-    };
-
-    const int strip_base = sg * SPG + wave * SPW;
-    auto load_rec = [&](int quad, v4i *codes, v4i *sc) {
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-            const int strip = strip_base + j;
-            if (strip < p.NS && quad < q1) {
-                const uint8_t *rec = recs + ((int64_t)strip * p.NQ + quad) * kQ4RecBytes;
-                codes[j] = *(const v4i *)(rec + lane * 16);
-                sc[j] = *(const v4i *)(rec + 1024 + (lane & 15) * 16);
-            } else {
-                codes[j] = v4i{0, 0, 0, 0};
-                sc[j] = v4i{0, 0, 0, 0};
+                for (int tt = 0; tt < 3; ++tt)
+                    *(v4i *)(dst + tt * MT * 1024) = v4i{(int)w[tt][0], (int)w[tt][1], (int)w[tt][2], (int)w[tt][3]};
+                if (g == 0) sXS[buf][bl][row] = bsum;
             }
         }
     };
 
-    v4f acc_y[MT][SPW];
+    // ---- weight records
+    const int strip_base = sg * SPG + wave * C;
+    // current chunk's records and the next chunk's (register arrays are only
+    // ever indexed with compile-time indices)
+    v4i bc[QC][C], bs[QC][C], nbc[QC][C], nbs[QC][C];
+    auto gload_b = [&](int qc, v4i (&dc)[QC][C], v4i (&ds)[QC][C]) {
+#pragma unroll
+        for (int q = 0; q < QC; ++q)
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const int quad = qc + q;
+                const int strip = strip_base + j;
+                if (strip < p.NS && quad < q1) {
+                    const uint8_t *rec = recs + ((int64_t)strip * p.NQ + quad) * kQ4RecBytes;
+                    dc[q][j] = *(const v4i *)(rec + lane * 16);
+                    ds[q][j] = *(const v4i *)(rec + 1024 + (lane & 15) * 16);
+                } else {
+                    dc[q][j] = v4i{0, 0, 0, 0};
+                    ds[q][j] = v4i{0, 0, 0, 0};
+                }
+            }
+    };
+
+    v4f acc_y[MT][C];
 #pragma unroll
     for (int rt = 0; rt < MT; ++rt)
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) acc_y[rt][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < C; ++j) acc_y[rt][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nchunk = (q1 - q0 + 1) / 2;
+    const int nchunk = (q1 - q0 + QC - 1) / QC;
     if (nchunk > 0) {
-        gload_chunk(q0);
-        sstore_chunk(0);
+        gload_b(q0, bc, bs);
+        gload_a(q0);
+        sstore_a(0);
     }
     __syncthreads();
-    v4i codes[SPW], sc[SPW], ncodes[SPW], nsc[SPW];
-    if (nchunk > 0) load_rec(q0, codes, sc);
     for (int c = 0; c < nchunk; ++c) {
         const int buf = c & 1;
-        const int qc = q0 + 2 * c;
-        if (c + 1 < nchunk) gload_chunk(qc + 2);
+        const int qc = q0 + c * QC;
+        if (c + 1 < nchunk) {
+            gload_b(qc + QC, nbc, nbs);
+            gload_a(qc + QC);
+        }
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-            const int quad = qc + qq;
-            load_rec(quad + 1, ncodes, nsc);  // prefetch (zeros past the range)
-            if (quad < q1) {
+        for (int q = 0; q < QC; ++q) {
+#pragma unroll 2
+            for (int i = 0; i < 4; ++i) {
+                const int bl = q * 4 + i;
+                v8bf a[MT][3];
+                v4f xsv[MT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int bl = qq * 4 + i;
-                    v8bf a[MT][3];
-                    v4f xsv[MT];
+                for (int rt = 0; rt < MT; ++rt) {
+#pragma unroll
+                    for (int t = 0; t < 3; ++t) a[rt][t] = *(const v8bf *)(&sA[buf][bl][t][rt][lane * 16]);
+                    xsv[rt] = *(const v4f *)(&sXS[buf][bl][rt * 16 + 4 * (lane >> 4)]);
+                }
+#pragma unroll
+                for (int j = 0; j < C; ++j) {
+                    const v8bf bop = decode8((uint32_t)bc[q][j][i]);
+                    const uint32_t dm = (uint32_t)bs[q][j][i];
+                    const float d = bf16_bits_f32(dm & 0xFFFFu);
+                    const float mn = bf16_bits_f32(dm >> 16);
 #pragma unroll
                     for (int rt = 0; rt < MT; ++rt) {
+                        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][0], bop, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][1], bop, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][2], bop, acc, 0, 0, 0);
 #pragma unroll
-                        for (int t = 0; t < 3; ++t) a[rt][t] = *(const v8bf *)(&sA[buf][bl][t][rt][lane * 16]);
-                        xsv[rt] = *(const v4f *)(&sXS[buf][bl][rt * 16 + 4 * (lane >> 4)]);
-                    }
-#pragma unroll
-                    for (int j = 0; j < SPW; ++j) {
-                        const v8bf bop = decode8((uint32_t)codes[j][i]);
-                        const uint32_t dm = (uint32_t)sc[j][i];
-                        const float d = bf16_bits_f32(dm & 0xFFFFu);
-                        const float mn = bf16_bits_f32(dm >> 16);
-#pragma unroll
-                        for (int rt = 0; rt < MT; ++rt) {
-                            v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][0], bop, acc, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][1], bop, acc, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][2], bop, acc, 0, 0, 0);
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                acc_y[rt][j][v] = fmaf(d, acc[v], acc_y[rt][j][v]);
-                                acc_y[rt][j][v] = fmaf(mn, xsv[rt][v], acc_y[rt][j][v]);
-                            }
+                        for (int v = 0; v < 4; ++v) {
+                            acc_y[rt][j][v] = fmaf(d, acc[v], acc_y[rt][j][v]);
+                            acc_y[rt][j][v] = fmaf(mn, xsv[rt][v], acc_y[rt][j][v]);
                         }
                     }
                 }
             }
-#pragma unroll
-            for (int j = 0; j < SPW; ++j) {
-                codes[j] = ncodes[j];
-                sc[j] = nsc[j];
-            }
         }
-        if (c + 1 < nchunk) sstore_chunk(buf ^ 1);
+        if (c + 1 < nchunk) {
+            sstore_a(buf ^ 1);
+#pragma unroll
+            for (int q = 0; q < QC; ++q)
+#pragma unroll
+                for (int j = 0; j < C; ++j) {
+                    bc[q][j] = nbc[q][j];
+                    bs[q][j] = nbs[q][j];
+                }
+        }
         __syncthreads();
     }
 
 #pragma unroll
     for (int rt = 0; rt < MT; ++rt)
 #pragma unroll
-        for (int j = 0; j < SPW; ++j)
+        for (int j = 0; j < C; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int row = rt * 16 + 4 * (lane >> 4) + v;
@@ -416,22 +414,14 @@ hipError_t launch_q4_repack(const uint8_t *blocks, const Q4Layout &L, uint8_t *p
     return hipGetLastError();
 }
 
-hipError_t launch_q4_xsplit(const float *X, int64_t ldx, int64_t R, int64_t NB, uint16_t *xsp, float *xs,
-                            hipStream_t s) {
-    const int64_t threads = R * NB * 32;
-    hipLaunchKernelGGL(k_q4_xsplit, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s, X, ldx, (int)R,
-                       (int)NB, xsp, xs);
-    return hipGetLastError();
-}
-
 hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int64_t grid, hipStream_t s,
                            const char **variant) {
-    if (mt == 1 && waves == 4) {
+    if (mt == 1 && waves == 8) {
         *variant = "q4_mm_m16";
-        hipLaunchKernelGGL((k_q4_mm<1, 4, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
-    } else if (mt == 2 && waves == 4) {
+        hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4>), dim3((unsigned)grid), dim3(512), 0, s, p);
+    } else if (mt == 2 && waves == 8) {
         *variant = "q4_mm_m32";
-        hipLaunchKernelGGL((k_q4_mm<2, 4, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4>), dim3((unsigned)grid), dim3(512), 0, s, p);
     } else {
         return hipErrorInvalidValue;
     }
@@ -453,10 +443,11 @@ hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, i
 }
 
 hipError_t launch_q4_moe(const Q4Params &p, int64_t max_chunks, hipStream_t s, const char **variant) {
-    constexpr int WAVES = 6;
-    const int64_t groups = ceil_div(p.NS, 4 * WAVES);
+    constexpr int WAVES = 6, C = 4;
+    const int64_t groups = ceil_div(p.NS, C * WAVES);
     *variant = "q4_mm_moe_m32";
-    hipLaunchKernelGGL((k_q4_mm<2, WAVES, true>), dim3((unsigned)(groups * max_chunks)), dim3(WAVES * 64), 0, s, p);
+    hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 3>), dim3((unsigned)(groups * max_chunks)), dim3(WAVES * 64),
+                       0, s, p);
     return hipGetLastError();
 }
 

@@ -165,8 +165,9 @@ struct Q4Params {
     const uint8_t *recs;      // dense: the weight; MoE: expert 0
     int64_t expert_stride;    // MoE: bytes between experts
     int NQ, NB, NS, N, K;
-    const uint16_t *xsp;      // split activations [rows][NB][3][32] bf16
-    const float *xs;          // block sums [rows][NB]
+    const float *X;           // fp32 activations (row stride ldx)
+    int64_t ldx;
+    int x_vec;                // 1: X and ldx allow aligned 16-byte loads
     int M;                    // dense rows in this launch
     float *Y;
     int64_t ldy;
@@ -183,7 +184,7 @@ struct Q4Params {
 struct Q4Plan {
     int mt, waves, S, qps;
     int64_t grid, rows_per_launch;
-    int64_t ws_xsp_off, ws_xs_off, ws_part_off, ws_bytes;
+    int64_t ws_part_off, ws_bytes;
 };
 
 Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N);
@@ -191,14 +192,12 @@ Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N);
 struct MoePlan {
     int rpc;
     int64_t max_chunks;
-    int64_t ws_xsp_off, ws_xs_off, ws_sorted_off, ws_chunk_off, ws_misc_off, ws_bytes;
+    int64_t ws_sorted_off, ws_chunk_off, ws_misc_off, ws_bytes;
 };
 
 MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N);
 
 hipError_t launch_q4_repack(const uint8_t *blocks, const Q4Layout &L, uint8_t *packed, hipStream_t s);
-hipError_t launch_q4_xsplit(const float *X, int64_t ldx, int64_t R, int64_t NB, uint16_t *xsp, float *xs,
-                            hipStream_t s);
 hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int64_t grid, hipStream_t s,
                            const char **variant);
 hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, int64_t n_used, int64_t E,
