@@ -6,17 +6,18 @@ Workload (one "step"): the seven Qwen3-0.6B projections of all 28 layers
 timed region: ~420 MiB of int8 codes, more than the 256 MiB Infinity Cache)
 run as decode at M = 1, 16 and 32 rows of fp32 N(0, 1) activations.  Every
 call is int8_gemm_dynamic: per-row amax/127 quantisation of the activations
-(inside the int8 product kernel at M <= 16, a separate kernel at M = 32) and
-the int8 product with the fp32 epilogue (row scale x column scale).  Each M's 196 calls are captured in
+(inside the int8 product kernel for M <= 16 and K <= 1024, a separate kernel
+otherwise) and the int8 product with the fp32 epilogue (row scale x column
+scale).  Each M's 196 calls are captured in
 one HIP graph; a step replays the three graphs.
 
 `value` is the step's algorithmic bytes (per call K*N weight bytes + 4N column
 scales + 4MK activations + 4MN outputs) over its wall time, in GB/s.
 `roofline` is the dominant kernel, the int8 decode GEMM: its algorithmic
-bytes per launch (K*N + 4N + 4MK + 4MN with the activations quantised inside
-at M <= 16; K*N + 4N + MK + 4M + 4MN on pre-quantised rows at M = 32) over
-its average launch time from graphs of its launches alone (HIP events on the
-replay stream, dispatch gaps included).  `extra` carries the
+bytes per launch (K*N + 4N + 4MK + 4MN with the activations quantised inside,
+for M <= 16 and K <= 1024; K*N + 4N + MK + 4M + 4MN on pre-quantised rows
+otherwise) over its average launch time from graphs of its launches alone
+(HIP events on the replay stream, dispatch gaps included).  `extra` carries the
 per-M figures and the other configurations (int8 prefill at M = 2048).
 `cpu_baseline` times the CPU oracle on one whole step.
 
@@ -35,6 +36,23 @@ INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published
 METRIC = "GB/s & %HBM peak at M=1/16; int8 TOPS & %MFMA peak at M=2048"
 
 
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE) of `bench.py --probe --no-cpu-baseline`, each
+# scaled by what the counter reads for the probe's 1 GiB device copy (FETCH_SIZE
+# x 2.0, WRITE_SIZE x 1.0).  Valid only for the kernel sources it was taken on.
+MEASURED_TRAFFIC = {"sources_sha1": "d66bdf8df42cc04132f4e031501b28c1241040e8", "bytes_per_launch": 2774681}
+
+
+def decode_traffic():
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha1()
+    for f in ("k_int8.hip", "api.cpp"):
+        with open(os.path.join(here, "int8_bit_weight_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return MEASURED_TRAFFIC["bytes_per_launch"] if h.hexdigest() == MEASURED_TRAFFIC["sources_sha1"] else None
+
+
 def log(msg: str) -> None:
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
@@ -47,6 +65,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--layers", type=int, default=None, help="(debug) fewer layers")
+    ap.add_argument("--probe", action="store_true",
+                    help="counter probe: one 1 GiB device copy (the calibration kernel), then each decode "
+                         "call of one step once, eagerly; for rocprofv3 --pmc runs")
     return ap.parse_args()
 
 
@@ -119,6 +140,21 @@ def main() -> int:
         for (l, p, K, N, X, Y) in calls[M]:
             q.int8_gemm_dynamic(X, packed[(l, p)], out_f32=Y)
 
+    if args.probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        for M in rows:
+            run_m(M)
+        torch.cuda.synchronize()
+        print(json.dumps({"probe": "copy 1073741824 bytes, then %d decode calls" %
+                          sum(len(calls[M]) for M in rows),
+                          "decode_algorithmic_bytes": {str(M): sum(call_bytes(M, c[2], c[3]) for c in calls[M])
+                                                       for M in rows}}))
+        return 0
+
     # eager reference outputs, then one graph per M, checked bit for bit
     for M in rows:
         run_m(M)
@@ -169,50 +205,55 @@ def main() -> int:
         per_m[M] = dict(sec=sec, gbs=step_bytes[M] / sec / 1e9, calls=len(calls[M]))
     log("step %.3f ms, %.1f GB/s" % (ms_per_step, value))
 
-    # Dominant kernel: the int8 decode GEMM (k_int8_decode).  At M <= 16 each
-    # call is exactly one launch of it (activations quantised inside); at
-    # M = 32 a call is the row quantiser plus it.  Its average launch time is
+    # Dominant kernel: the int8 decode GEMM (k_int8_decode).  A call is one
+    # launch of it with the activations quantised inside (M <= 16, K <= 1024)
+    # or the row quantiser plus it.  Its average launch time is
     # taken from graphs holding only its launches, replayed back to back and
     # timed with HIP events on the replay stream (so the short dispatch gaps
     # between launches are included).
     kern_b, kern_t, n_launch = 0, 0.0, 0
     kern = {}
     for M in rows:
-        if M <= 16:
-            sec = per_m[M]["sec"]
-            kb = step_bytes[M]
-        else:
-            pre = []
-            for (l, p, K, N, X, Y) in calls[M]:
+        pre = []
+        kb = 0
+        for (l, p, K, N, X, Y) in calls[M]:
+            if M <= 16 and K <= 1024:
+                pre.append((packed[(l, p)], X, None, Y))
+                kb += call_bytes(M, K, N)
+            else:
                 Xq, rs = q.quantize_rows_int8(X)
                 pre.append((packed[(l, p)], Xq, rs, Y))
-            torch.cuda.synchronize()
+                kb += K * N + 4 * N + M * K + 4 * M + 4 * M * N
+        torch.cuda.synchronize()
 
-            def run_gemm(pre=pre):
-                for (pk, Xq, rs, Y) in pre:
-                    q.int8_gemm(Xq, 0, pk, 0, out_f32=Y, row_scale=rs)
-            run_gemm()
-            gk = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gk):
-                run_gemm()
+        def run_kernels(pre=pre):
+            for (pk, A, rs, Y) in pre:
+                if rs is None:
+                    q.int8_gemm_dynamic(A, pk, out_f32=Y)
+                else:
+                    q.int8_gemm(A, 0, pk, 0, out_f32=Y, row_scale=rs)
+        run_kernels()
+        gk = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gk):
+            run_kernels()
+        gk.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
             gk.replay()
-            torch.cuda.synchronize()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(args.steps):
-                gk.replay()
-            b.record()
-            torch.cuda.synchronize()
-            sec = a.elapsed_time(b) * 1e-3 / args.steps
-            kb = sum(c[2] * c[3] + 4 * c[3] + M * c[2] + 4 * M + 4 * M * c[3] for c in calls[M])
+        b.record()
+        torch.cuda.synchronize()
+        sec = a.elapsed_time(b) * 1e-3 / args.steps
         kern[M] = dict(us=sec / len(calls[M]) * 1e6, gbs=kb / sec / 1e9)
         kern_b += kb
         kern_t += sec
         n_launch += len(calls[M])
     achieved = kern_b / kern_t / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_int8_decode",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(), "kernel": "k_int8_decode",
+                "algorithmic_bytes_per_launch": round(kern_b / n_launch),
                 "avg_launch_us": round(kern_t / n_launch * 1e6, 3), "launches_per_step": n_launch}
 
     extra = {"per_m": {str(M): {"step_ms": round(per_m[M]["sec"] * 1e3, 4), "GB/s": round(per_m[M]["gbs"], 2),

@@ -243,7 +243,7 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
 
 size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     if (M <= 0 || K <= 0 || N <= 0) return 0;
-    if (M <= 16) return (size_t)plan_int8_gemm(M, K, N).ws_bytes;
+    if (M <= 16 && K <= 1024) return (size_t)plan_int8_gemm(M, K, N).ws_bytes;
     return (size_t)(round_up(M * K, 256) + round_up(4 * M, 256));
 }
 
@@ -261,10 +261,11 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
         check_epilogue_ptrs(ep) != QMM_OK)
         return QMM_ERR_INVALID;
     hipStream_t s = (hipStream_t)stream;
-    if (M > 16) {
+    if (M > 16 || K > 1024) {
         // The row quantiser, then the product.  Inside the product kernel
-        // every 16-column workgroup would quantise all M x K activations
-        // again, which above 16 rows costs more than the second launch.
+        // every 16-column workgroup quantises all M x K activations again;
+        // that only beats a second launch while each of 16 wavefronts holds
+        // one 64-k tile of them in registers (M <= 16, K <= 1024).
         int8_t *q = Xq;
         float *rs = row_scale;
         int64_t lq = ldq;
@@ -283,13 +284,11 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
         e2.row_scale = rs;
         return int8_gemm(q, QMM_S8, M, K, lq, 0, packedB, QMM_S8, N, 0, &e2, nullptr, 0, stream);
     }
-    // 16 wavefronts, and enough k tiles per wavefront that one round covers
-    // K, so the activations stay in registers between the amax pass and the
-    // quantise pass when that takes at most 2 tiles (K <= 2048).
+    // 16 wavefronts with one k tile each: one round covers K <= 1024, so the
+    // activations stay in registers between the amax and quantise passes.
     Int8Plan plan = plan_int8_gemm(M, K, N);
     plan.waves = 16;
-    plan.tpw = (int)ceil_div(packed_b_layout(K, N).KT, 16);
-    plan.tpw = plan.tpw <= 1 ? 1 : (plan.tpw <= 2 ? 2 : 4);
+    plan.tpw = 1;
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
         return QMM_ERR_WORKSPACE;
     Int8GemmParams p{};

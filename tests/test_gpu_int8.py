@@ -298,8 +298,10 @@ def test_dynamic_matches_two_step_and_oracle(q, orc, M, K, N):
     xq = torch.full((M, K), 99, dtype=torch.int8, device=dev)
     rs = torch.full((M,), -1.0, dtype=torch.float32, device=dev)
     q.int8_gemm_dynamic(Xd, p, out_f32=y, out_i32=y32, xq_out=xq, rs_out=rs)
-    if M <= 16:
+    if M <= 16 and K <= 1024:
         assert q.last_variant() == "int8_dynamic_m16"
+    elif M <= 16:
+        assert q.last_variant() == "int8_decode_m16"
     elif M <= 32:
         assert q.last_variant() == "int8_decode_m32"
     assert np.array_equal(to_np(y).view(np.uint32), to_np(y2).view(np.uint32))
