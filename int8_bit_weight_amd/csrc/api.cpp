@@ -45,7 +45,7 @@ qmm_status record_status(hipError_t e, const char *variant) {
 // Decode (M <= 32): one workgroup per 16-column strip of the weight, with
 // WAVES wavefronts (4, 8 or 16) splitting its k tiles and TPW (1, 2 or 4)
 // tiles per wavefront per round, chosen so one round covers as much of K as
-// possible.  Prefill (M > 32): 128 x 128 MFMA tiles.  QMM_DECODE_WAVES /
+// possible.  Prefill (M > 32): 256 x 128 MFMA tiles.  QMM_DECODE_WAVES /
 // QMM_DECODE_TPW override the choice (tuning only: integer results are exact
 // and the fp32 epilogue does not depend on the choice either).
 Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N) {
@@ -66,7 +66,7 @@ Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N) {
         pl.grid = L.NS;
     } else {
         pl.variant = 1;
-        pl.grid = ceil_div(L.NS, 8) * ceil_div(M, 128);
+        pl.grid = ceil_div(L.NS, 8) * ceil_div(M, 256);
     }
     return pl;
 }

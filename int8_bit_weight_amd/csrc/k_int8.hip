@@ -10,6 +10,8 @@
 // (Int8Gemm)", and "The ONNX pack: weights to Q4NX, matmuls to our kernels,
 // no VitisAI", sections "The three layers of the pack", "Why it folds
 // without a new kernel" and "What works today, and what does not".
+#include <type_traits>
+
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -416,95 +418,188 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
 }
 
 // -------------------------------------------------------- prefill GEMM ---
-// 128 x 128 output tile per workgroup, k step 64, 4 wavefronts in a 2 x 2
-// grid each owning 64 x 64 (4 x 4 MFMA tiles of 16 x 16).  A and B tiles are
-// double-buffered in LDS; the next tile's global loads are issued before the
-// current tile's MFMAs.  A rows in LDS are 64 bytes with the 16-byte chunk
-// index XOR-swizzled by (row/2)%4 so a wavefront's 16-byte reads of 16 rows
-// spread over all banks; B tiles are copied as is (already lane-ordered).
-constexpr int PF_BM = 128, PF_BN = 128;
+// 256 x 128 output tile per workgroup, k step 64, 4 wavefronts in a 2 x 2
+// grid each owning 128 x 64 (8 x 4 MFMA tiles of 16 x 16, 128 int32
+// accumulators per lane, held in AGPRs).  Both operands sit in LDS in MFMA
+// fragment order (1 KiB per 16 rows or 16 columns x 64 k, 16 bytes per lane),
+// so every fragment read is one linear ds_read_b128 per lane; the packed
+// weight tiles are already in that order and are copied as is.  Each
+// wavefront reads 12 fragments per 32 MFMAs.
+// Global loads run PF_DEPTH k steps ahead through a ring of register stages
+// (compile-time slots: the k loop is unrolled by PF_DEPTH), so the L2/MALL
+// latency of a stage is covered by PF_DEPTH - 1 steps of MFMAs; LDS holds two
+// stages.  Row and column epilogue operands are staged in LDS once.
+constexpr int PF_BM = 256, PF_BN = 128, PF_DEPTH = 4;
 
-__device__ __forceinline__ int swz_a(int row, int kc) { return row * 64 + ((kc ^ ((row >> 1) & 3)) << 4); }
+template <int N>
+using ic = std::integral_constant<int, N>;
 
-template <bool HAS_ZB>
+// FAST (A 16-byte aligned, lda % 16 == 0, K % 64 == 0): every global load is
+// unconditional, so loads issued for later stages stay in flight (a load
+// inside a branch makes the compiler wait for it at the branch's end).  Rows
+// past M read row M - 1 and strips past the last read the last strip; those
+// products land in outputs that are never stored.  uint8 A is shifted when
+// the stage is written to LDS.
+template <bool HAS_ZB, bool FAST>
 __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
-    __shared__ __attribute__((aligned(16))) int8_t sA[2][PF_BM * kTileK];
-    __shared__ __attribute__((aligned(16))) int8_t sB[2][(PF_BN / kTileN) * kTileBytes];
+    constexpr int AF = PF_BM / 16;      // A fragments per stage
+    constexpr int BF = PF_BN / 16;      // B fragments per stage
+    constexpr int ACH = AF * 64 / 256;  // 16-byte A chunks per thread per stage (4)
+    constexpr int BCH = BF * 64 / 256;  // 16-byte B chunks per thread per stage (2)
+    __shared__ __attribute__((aligned(16))) int8_t sA[2][AF * 1024];
+    __shared__ __attribute__((aligned(16))) int8_t sB[2][BF * 1024];
+    __shared__ float s_rs[PF_BM];
+    __shared__ ColOps s_col[PF_BN];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * PF_BM;
-    const int strip0 = blockIdx.x * (PF_BN / kTileN);
+    const int tiles_n = (p.NS + BF - 1) / BF;
+    const int bn = blockIdx.x % tiles_n;
+    const int bm = blockIdx.x / tiles_n;
+    const int m0 = bm * PF_BM;
+    const int strip0 = bn * BF;
+    const int KT = p.KT;
 
-    v4i ra[2], rb[2];
-    auto gload = [&](int kt) {
+    for (int r = tid; r < PF_BM; r += 256) {
+        const int m = m0 + r;
+        s_rs[r] = (m < p.M && p.row_scale) ? p.row_scale[m] : 1.0f;
+    }
+    if (tid < PF_BN) {
+        const int n = strip0 * kTileN + tid;
+        s_col[tid] = n < p.N ? load_colops(p, n) : ColOps{0, 0.0f, 0.0f, 0};
+    }
+
+    // per-thread source pointers of the FAST path (k advances by 64 bytes a step)
+    const int8_t *a_src[ACH];
+    const int8_t *b_src[BCH];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i;
-            ra[i] = load_a16(p, m0 + (c >> 2), kt * kTileK + (c & 3) * 16);
-            const int f = c >> 6;
-            const int strip = strip0 + f;
-            if (strip < p.NS)
-                rb[i] = *(const v4i *)(p.codes + ((int64_t)strip * p.KT + kt) * kTileBytes + (c & 63) * 16);
-            else
-                rb[i] = v4i{0, 0, 0, 0};
+    for (int i = 0; i < ACH; ++i) {
+        const int c = tid + 256 * i;
+        const int row = min(m0 + (c >> 2), p.M - 1);
+        a_src[i] = p.A + (int64_t)row * p.lda + (c & 3) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+        const int c = tid + 256 * i;
+        const int strip = min(strip0 + (c >> 6), p.NS - 1);
+        b_src[i] = p.codes + (int64_t)strip * KT * kTileBytes + (c & 63) * 16;
+    }
+    const uint32_t flip = p.a_u8 ? 0x80808080u : 0u;
+
+    v4i ra[PF_DEPTH][ACH], rb[PF_DEPTH][BCH];
+    auto gload = [&](auto slot, int kt) {
+        constexpr int sl = decltype(slot)::value;
+        if (FAST) {
+#pragma unroll
+            for (int i = 0; i < ACH; ++i) ra[sl][i] = *(const v4i *)(a_src[i] + (int64_t)kt * kTileK);
+#pragma unroll
+            for (int i = 0; i < BCH; ++i) rb[sl][i] = *(const v4i *)(b_src[i] + (int64_t)kt * kTileBytes);
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int c = tid + 256 * i;  // (row, k-chunk) = (c >> 2, c & 3)
+            ra[sl][i] = load_a16(p, m0 + (c >> 2), kt * kTileK + (c & 3) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < BCH; ++i) {
+            const int c = tid + 256 * i;  // (strip, lane chunk) = (c >> 6, c & 63)
+            const int strip = strip0 + (c >> 6);
+            rb[sl][i] = strip < p.NS
+                            ? *(const v4i *)(p.codes + ((int64_t)strip * KT + kt) * kTileBytes + (c & 63) * 16)
+                            : v4i{0, 0, 0, 0};
         }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](auto slot, int buf) {
+        constexpr int sl = decltype(slot)::value;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < ACH; ++i) {
             const int c = tid + 256 * i;
-            *(v4i *)(&sA[buf][swz_a(c >> 2, c & 3)]) = ra[i];
-            *(v4i *)(&sB[buf][(c >> 6) * kTileBytes + (c & 63) * 16]) = rb[i];
+            const int r = c >> 2;
+            v4i v = ra[sl][i];
+            if (FAST) {
+                v[0] ^= flip;
+                v[1] ^= flip;
+                v[2] ^= flip;
+                v[3] ^= flip;
+            }
+            *(v4i *)(&sA[buf][(r >> 4) * 1024 + ((c & 3) * 16 + (r & 15)) * 16]) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < BCH; ++i) {
+            const int c = tid + 256 * i;
+            *(v4i *)(&sB[buf][c * 16]) = rb[sl][i];
         }
     };
 
-    v4i acc[4][4];
-    v4i accr[4];
+    v4i acc[8][4];
+    v4i accr[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
         accr[i] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
     }
     const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
-    gload(0);
-    sstore(0);
+    auto compute = [&](int buf) {
+        v4i b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = *(const v4i *)(&sB[buf][(wn * 4 + j) * 1024 + lane * 16]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const v4i a = *(const v4i *)(&sA[buf][(wm * 8 + i) * 1024 + lane * 16]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_i8(a, b[j], acc[i][j]);
+            if (HAS_ZB) accr[i] = mfma_i8(a, ones, accr[i]);
+        }
+    };
+
+    // stage s lives in register slot s % PF_DEPTH and LDS buffer s % 2
+    gload(ic<0>{}, 0);
+    gload(ic<1>{}, min(1, KT - 1));
+    gload(ic<2>{}, min(2, KT - 1));
+    gload(ic<3>{}, min(3, KT - 1));
+    sstore(ic<0>{}, 0);
     __syncthreads();
-    for (int kt = 0; kt < p.KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < p.KT) gload(kt + 1);
-        v4i a[4], b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wm * 64 + i * 16 + (lane & 15);
-            a[i] = *(const v4i *)(&sA[buf][swz_a(row, lane >> 4)]);
-            b[i] = *(const v4i *)(&sB[buf][(wn * 4 + i) * kTileBytes + lane * 16]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_i8(a[i], b[j], acc[i][j]);
-            if (HAS_ZB) accr[i] = mfma_i8(a[i], ones, accr[i]);
-        }
-        if (kt + 1 < p.KT) sstore(buf ^ 1);
+    // Steady state: every step unconditionally stores the next stage and
+    // loads the stage PF_DEPTH ahead (clamped to the last k tile), so no load
+    // sits inside a branch; a store past the end only fills an LDS buffer
+    // that is never read again.
+    auto step = [&](auto J, int kt) {
+        constexpr int j = decltype(J)::value;
+        compute(kt & 1);
+        sstore(ic<(j + 1) % PF_DEPTH>{}, (kt + 1) & 1);
+        gload(ic<j>{}, min(kt + PF_DEPTH, KT - 1));
         __syncthreads();
+    };
+    const int KT4 = KT - KT % PF_DEPTH;
+    for (int base = 0; base < KT4; base += PF_DEPTH) {
+        step(ic<0>{}, base);
+        step(ic<1>{}, base + 1);
+        step(ic<2>{}, base + 2);
+        step(ic<3>{}, base + 3);
     }
+    if (KT4 < KT) step(ic<0>{}, KT4);
+    if (KT4 + 1 < KT) step(ic<1>{}, KT4 + 1);
+    if (KT4 + 2 < KT) step(ic<2>{}, KT4 + 2);
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+            const int cl = (wn * 4 + j) * 16 + (lane & 15);
+            const int n = strip0 * kTileN + cl;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + v;
-                const int n = (strip0 + wn * 4 + j) * kTileN + (lane & 15);
+                const int rl = wm * 128 + i * 16 + 4 * (lane >> 4) + v;
+                const int m = m0 + rl;
                 if (m < p.M && n < p.N)
-                    epilogue_store(p, m, n, (uint32_t)acc[i][j][v], HAS_ZB ? accr[i][v] : 0, HAS_ZB,
-                                   p.row_scale ? p.row_scale[m] : 1.0f);
+                    epilogue_store_c(p, m, n, (uint32_t)acc[i][j][v], HAS_ZB ? accr[i][v] : 0, HAS_ZB, s_rs[rl],
+                                     s_col[cl]);
             }
+        }
 }
 
 template <int MT, int WAVES, int TPW, bool QUANT>
@@ -576,12 +671,20 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
         if (plan.mt == 1) return launch_decode_waves<1, false>(p, plan.waves, plan.tpw, s);
         return launch_decode_waves<2, false>(p, plan.waves, plan.tpw, s);
     }
-    *variant = "int8_prefill_128x128";
-    dim3 grid((unsigned)ceil_div(p.NS, PF_BN / kTileN), (unsigned)ceil_div(p.M, PF_BM));
-    if (p.zBs != 0)
-        hipLaunchKernelGGL((k_int8_prefill<true>), grid, dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((k_int8_prefill<false>), grid, dim3(256), 0, s, p);
+    *variant = "int8_prefill_256x128";
+    dim3 grid((unsigned)(ceil_div(p.NS, PF_BN / kTileN) * ceil_div(p.M, PF_BM)));
+    const bool fast = p.a_vec && (p.K % kTileK) == 0;
+    if (p.zBs != 0) {
+        if (fast)
+            hipLaunchKernelGGL((k_int8_prefill<true, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_int8_prefill<true, false>), grid, dim3(256), 0, s, p);
+    } else {
+        if (fast)
+            hipLaunchKernelGGL((k_int8_prefill<false, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_int8_prefill<false, false>), grid, dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -16,6 +16,8 @@
 // Codes stay exact: bytes 0..15 read as OCP e4m3 are exactly q * 2^-9, and
 // v_cvt_scalef32_pk_bf16_fp8 with scale 2^9 turns two of them into two exact
 // bf16 integers per instruction.
+#include <type_traits>
+
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -24,8 +26,7 @@ namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-constexpr int KCB = 8;  // blocks per LDS-staged activation chunk (two records)
+template <int N> using ic = std::integral_constant<int, N>;
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
     uint32_t u = __float_as_uint(x);
@@ -36,15 +37,16 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
 __device__ __forceinline__ float bf16_bits_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // Eight 4-bit codes (record nibble order) -> eight exact bf16 values in k order.
+// Each conversion yields one packed pair; the four pairs are the four dwords
+// of the MFMA operand as they are (a bit cast, no element shuffling).
 __device__ __forceinline__ v8bf decode8(uint32_t w) {
     const uint32_t lo = w & 0x0F0F0F0Fu;
     const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false);
-    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true);
-    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false);
-    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true);
-    v8bf r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-    return r;
+    const v4i r = {__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false)),
+                   __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true)),
+                   __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false)),
+                   __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true))};
+    return __builtin_bit_cast(v8bf, r);
 }
 
 // ---------------------------------------------------------------- repack ---
@@ -94,34 +96,56 @@ __global__ __launch_bounds__(256) void k_q4_repack(const uint8_t *__restrict__ b
 // Workgroup = WAVES wavefronts; each wavefront owns C column strips (16 C
 // columns) and all MT*16 rows of the workgroup's row set.  The k range is
 // walked in chunks of QC records (4 QC blocks of 32 k):
-//   * activations: the workgroup reads its rows' fp32 values for the chunk,
-//     splits each into three bf16 terms (x = x0 + x1 + x2; both differences
-//     are exact in fp32), sums each 32-k block in a fixed order, and stores
-//     the terms as MFMA A fragments in LDS (double buffered: the next chunk's
-//     global loads are issued before the current chunk's MFMAs);
+//   * activations: the workgroup reads its rows' fp32 values for the next
+//     chunk, splits each into three bf16 terms (x = x0 + x1 + x2; both
+//     differences are exact in fp32), sums each 32-k block in a fixed order,
+//     and stores the terms as MFMA A fragments in LDS (double buffered).
+//     Only rows that exist are split; the fragments of absent rows hold
+//     whatever LDS held and only reach accumulator rows that are never
+//     stored (an MFMA output row depends on its own A row alone);
 //   * weights: each wavefront streams its strips' records (16 bytes of codes
 //     and 16 bytes of (d, m) per lane per record), one chunk ahead in
-//     registers;
+//     registers: with QC >= 2 a record's registers are refilled with the
+//     next chunk's record as soon as its last block is used; with QC == 1
+//     two register sets alternate and the chunk loop is unrolled by two;
 //   * per block and strip: codes -> exact bf16, three MFMAs into a fresh
 //     accumulator, then y += d * acc + m * sum_k(x).
 //   dense: blockIdx -> (strip group, k split); rows 0..M-1.
 //   MoE:   blockIdx -> (strip group, row chunk); the chunk table gives the
 //          expert and the sorted (token, slot) pairs of its rows.
-template <int MT, int WAVES, int C, int QC, bool MOE, int MINW>
+// Loads are never inside branches (a load in a branch makes the compiler wait
+// for it where the branch ends, which would serialise the prefetch): indices
+// past the valid range are clamped to valid memory and the values are masked
+// where they are used.  XVEC: X and ldx allow aligned 16-byte loads.
+//
+// LDS layout of one 16-row A fragment (1 KiB): the 16-byte piece of (row r,
+// k-octet g) sits at slot 16 g + (r ^ f(g)), f = {0, 6, 10, 12}.  MFMA lane
+// L reads (r, g) = (L % 16, L / 16); the staging stores write (g, r) with g
+// fastest.  With this swizzle every 8 and every 16 consecutive lanes of
+// either access touch distinct 16-byte bank groups.
+__device__ __forceinline__ int a_slot(int r, int g) {
+    return g * 16 + (r ^ ((0xCA60 >> (4 * g)) & 15));
+}
+
+template <int MT, int WAVES, int C, int QC, bool MOE, int MINW, bool XVEC>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_mm(Q4Params p) {
     constexpr int NT = WAVES * 64;
     constexpr int ROWS = MT * 16;
     constexpr int SPG = C * WAVES;
     constexpr int BPC = 4 * QC;
-    constexpr int PIECES = BPC * ROWS * 4;  // (block, row, k-octet) pieces of a chunk
+    constexpr int PIECES = BPC * ROWS * 4;  // (block, row, k-octet) pieces of a chunk at most
     constexpr int PPT = (PIECES + NT - 1) / NT;
+    constexpr bool ROLL = QC >= 2;
+    constexpr int NSET = ROLL ? 1 : 2;     // weight register sets
+    constexpr int ADB = MT == 1 ? 2 : 1;   // A fragment register sets
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][BPC][3][MT][1024];
     __shared__ __attribute__((aligned(16))) float sXS[2][BPC][ROWS];
-    __shared__ int64_t sRow[ROWS];  // element offset of each row of X, -1 = zero row
+    __shared__ int64_t sRow[ROWS];  // element offset of each row of X
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform, so record addresses are computed in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int groups = (p.NS + SPG - 1) / SPG;
     const int sg = blockIdx.x % groups;
     const int job = blockIdx.x / groups;
@@ -142,45 +166,52 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         q1 = min(p.NQ, q0 + p.qps);
     }
     recs += kHeaderBytes;
-    if (tid < ROWS) {
-        int64_t off = -1;
-        if (tid < nrows) off = (int64_t)(MOE ? p.sorted[row0 + tid] / p.n_used : tid) * p.ldx;
-        sRow[tid] = off;
-    }
+    if (tid < nrows) sRow[tid] = (int64_t)(MOE ? p.sorted[row0 + tid] / p.n_used : tid) * p.ldx;
     __syncthreads();
 
-    // ---- activation staging
+    // ---- activation staging.  Pieces of the existing rows only:
+    // piece -> (g = piece % 4, row = piece / 4 % nrows, block = piece / 4 / nrows).
+    const int active = nrows * BPC * 4;
+    int pbl[PPT], pg[PPT], prow[PPT], pdst[PPT];
+    int64_t psrc[PPT];
+    bool pok[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int idx = tid + i * NT;
+        const int pc = min(idx, active - 1);
+        const int t = pc >> 2;
+        const int row = t % nrows;
+        prow[i] = row;
+        pg[i] = pc & 3;
+        pbl[i] = t / nrows;
+        pok[i] = idx < active;
+        psrc[i] = sRow[row] + pg[i] * 8;
+        pdst[i] = (pbl[i] * 3 * MT + (row >> 4)) * 1024 + a_slot(row & 15, pg[i]) * 16;
+    }
     float xr[PPT][8];
+    bool xok[PPT];
     auto gload_a = [&](int qc) {
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
-            const int idx = tid + i * NT;
+            const int b = qc * 4 + pbl[i];
+            xok[i] = pok[i] && b < p.NB;
+            const float *src = p.X + psrc[i] + min(b, p.NB - 1) * 32;
+            if (XVEC) {
+                const v4f lo = *(const v4f *)src;
+                const v4f hi = *(const v4f *)(src + 4);
+                xr[i][0] = lo[0]; xr[i][1] = lo[1]; xr[i][2] = lo[2]; xr[i][3] = lo[3];
+                xr[i][4] = hi[0]; xr[i][5] = hi[1]; xr[i][6] = hi[2]; xr[i][7] = hi[3];
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xr[i][e] = 0.0f;
-            if (idx < PIECES) {
-                const int g = idx & 3;
-                const int row = (idx >> 2) % ROWS;
-                const int b = qc * 4 + (idx >> 2) / ROWS;
-                const int64_t off = sRow[row];
-                if (off >= 0 && b < p.NB) {
-                    const float *src = p.X + off + b * 32 + g * 8;
-                    if (p.x_vec) {
-                        const v4f lo = *(const v4f *)src;
-                        const v4f hi = *(const v4f *)(src + 4);
-                        xr[i][0] = lo[0]; xr[i][1] = lo[1]; xr[i][2] = lo[2]; xr[i][3] = lo[3];
-                        xr[i][4] = hi[0]; xr[i][5] = hi[1]; xr[i][6] = hi[2]; xr[i][7] = hi[3];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) xr[i][e] = src[e];
-                    }
-                }
+                for (int e = 0; e < 8; ++e) xr[i][e] = src[e];
             }
         }
     };
     auto sstore_a = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
-            const int idx = tid + i * NT;
+            // wave-uniform: waves whose pieces are all past the existing rows skip
+            if (i * NT + wave * 64 >= active) continue;
             float bsum = 0.0f;
             uint32_t w[3][4];
 #pragma unroll
@@ -188,7 +219,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                 uint32_t t[3][2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const float x = xr[i][e + h];
+                    const float x = xok[i] ? xr[i][e + h] : 0.0f;
                     bsum += x;
                     t[0][h] = bf16_rne_bits(x);
                     const float r1 = x - bf16_bits_f32(t[0][h]);
@@ -202,40 +233,30 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
             // the four k-octets of one (row, block) sit in four adjacent lanes
             bsum += __shfl_xor(bsum, 1);
             bsum += __shfl_xor(bsum, 2);
-            if (idx < PIECES) {
-                const int g = idx & 3;
-                const int row = (idx >> 2) % ROWS;
-                const int bl = (idx >> 2) / ROWS;
-                uint8_t *dst = &sA[buf][bl][0][row >> 4][(g * 16 + (row & 15)) * 16];
+            if (pok[i]) {
+                uint8_t *dst = &sA[buf][0][0][0][0] + pdst[i];
 #pragma unroll
                 for (int tt = 0; tt < 3; ++tt)
                     *(v4i *)(dst + tt * MT * 1024) = v4i{(int)w[tt][0], (int)w[tt][1], (int)w[tt][2], (int)w[tt][3]};
-                if (g == 0) sXS[buf][bl][row] = bsum;
+                if (pg[i] == 0) sXS[buf][pbl[i]][prow[i]] = bsum;
             }
         }
     };
 
-    // ---- weight records
+    // ---- weight records.  Strips past the last read the last strip (their
+    // columns are never stored); records past the range read the last record
+    // of the range and are given d = m = 0 where they are used.
     const int strip_base = sg * SPG + wave * C;
-    // current chunk's records and the next chunk's (register arrays are only
-    // ever indexed with compile-time indices)
-    v4i bc[QC][C], bs[QC][C], nbc[QC][C], nbs[QC][C];
-    auto gload_b = [&](int qc, v4i (&dc)[QC][C], v4i (&ds)[QC][C]) {
+    v4i bc[NSET][QC][C], bs[NSET][QC][C];
+    auto gload_rec = [&](int quad, v4i (&dc)[C], v4i (&ds)[C]) {
+        const int qq = min(quad, q1 - 1);
 #pragma unroll
-        for (int q = 0; q < QC; ++q)
-#pragma unroll
-            for (int j = 0; j < C; ++j) {
-                const int quad = qc + q;
-                const int strip = strip_base + j;
-                if (strip < p.NS && quad < q1) {
-                    const uint8_t *rec = recs + ((int64_t)strip * p.NQ + quad) * kQ4RecBytes;
-                    dc[q][j] = *(const v4i *)(rec + lane * 16);
-                    ds[q][j] = *(const v4i *)(rec + 1024 + (lane & 15) * 16);
-                } else {
-                    dc[q][j] = v4i{0, 0, 0, 0};
-                    ds[q][j] = v4i{0, 0, 0, 0};
-                }
-            }
+        for (int j = 0; j < C; ++j) {
+            const int strip = min(strip_base + j, p.NS - 1);
+            const uint8_t *rec = recs + ((int64_t)strip * p.NQ + qq) * kQ4RecBytes;
+            dc[j] = *(const v4i *)(rec + (uint32_t)lane * 16u);
+            ds[j] = *(const v4i *)(rec + 1024 + (uint32_t)(lane & 15) * 16u);
+        }
     };
 
     v4f acc_y[MT][C];
@@ -244,65 +265,91 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 #pragma unroll
         for (int j = 0; j < C; ++j) acc_y[rt][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
+    const int a_off = a_slot(lane & 15, lane >> 4) * 16;
     const int nchunk = (q1 - q0 + QC - 1) / QC;
+
+    // One chunk: c = chunk index, buf = its LDS buffer, S = its weight set.
+    // The next chunk's activations (and, with two sets, its records) are
+    // loaded first; the last chunk reloads its own (never used).
+    auto chunk = [&](int c, int buf, auto S_) {
+        constexpr int S = decltype(S_)::value;
+        const int qc = q0 + c * QC;
+        const int qn = q0 + min(c + 1, nchunk - 1) * QC;
+        if (!ROLL) {
+#pragma unroll
+            for (int q = 0; q < QC; ++q) gload_rec(qn + q, bc[S ^ (NSET - 1)][q], bs[S ^ (NSET - 1)][q]);
+        }
+        gload_a(qn);
+        v8bf a[ADB][MT][3];
+        v4f xsv[ADB][MT];
+        auto lds_a = [&](int bl, v8bf (&ad)[MT][3], v4f (&xd)[MT]) {
+#pragma unroll
+            for (int rt = 0; rt < MT; ++rt) {
+#pragma unroll
+                for (int t = 0; t < 3; ++t) ad[rt][t] = *(const v8bf *)(&sA[buf][bl][t][rt][a_off]);
+                xd[rt] = *(const v4f *)(&sXS[buf][bl][rt * 16 + 4 * (lane >> 4)]);
+            }
+        };
+        if (ADB == 2) lds_a(0, a[0], xsv[0]);
+#pragma unroll
+        for (int bl = 0; bl < BPC; ++bl) {
+            const int q = bl >> 2, i = bl & 3;
+            const int ab = ADB == 2 ? (bl & 1) : 0;
+            if (ADB == 2) {
+                if (bl + 1 < BPC) lds_a(bl + 1, a[(bl + 1) & 1], xsv[(bl + 1) & 1]);
+            } else {
+                lds_a(bl, a[0], xsv[0]);
+            }
+            const bool rec_ok = qc + q < q1;
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const v8bf bop = decode8((uint32_t)bc[S][q][j][i]);
+                const uint32_t dm = rec_ok ? (uint32_t)bs[S][q][j][i] : 0u;
+                const float d = bf16_bits_f32(dm & 0xFFFFu);
+                const float mn = bf16_bits_f32(dm >> 16);
+#pragma unroll
+                for (int rt = 0; rt < MT; ++rt) {
+                    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][0], bop, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][1], bop, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][2], bop, acc, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        acc_y[rt][j][v] = fmaf(d, acc[v], acc_y[rt][j][v]);
+                        acc_y[rt][j][v] = fmaf(mn, xsv[ab][rt][v], acc_y[rt][j][v]);
+                    }
+                }
+            }
+            // pin the accumulators here: otherwise the compiler sinks every
+            // block's d/m update to the end of the chunk and keeps all the
+            // MFMA results alive until then
+#pragma unroll
+            for (int rt = 0; rt < MT; ++rt)
+#pragma unroll
+                for (int j = 0; j < C; ++j) asm volatile("" : "+v"(acc_y[rt][j]));
+            if (ROLL && i == 3) gload_rec(qn + q, bc[0][q], bs[0][q]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        sstore_a(buf ^ 1);
+        __syncthreads();
+    };
+
     if (nchunk > 0) {
-        gload_b(q0, bc, bs);
+#pragma unroll
+        for (int q = 0; q < QC; ++q) gload_rec(q0 + q, bc[0][q], bs[0][q]);
         gload_a(q0);
         sstore_a(0);
     }
     __syncthreads();
-    for (int c = 0; c < nchunk; ++c) {
-        const int buf = c & 1;
-        const int qc = q0 + c * QC;
-        if (c + 1 < nchunk) {
-            gload_b(qc + QC, nbc, nbs);
-            gload_a(qc + QC);
+    if (ROLL) {
+        for (int c = 0; c < nchunk; ++c) chunk(c, c & 1, ic<0>{});
+    } else {
+        // pairs of chunks; an odd count ends with one chunk past the range,
+        // whose records are masked (d = m = 0) and activations are zero
+        for (int c = 0; c < nchunk; c += 2) {
+            chunk(c, 0, ic<0>{});
+            chunk(c + 1, 1, ic<NSET - 1>{});
         }
-#pragma unroll
-        for (int q = 0; q < QC; ++q) {
-#pragma unroll 2
-            for (int i = 0; i < 4; ++i) {
-                const int bl = q * 4 + i;
-                v8bf a[MT][3];
-                v4f xsv[MT];
-#pragma unroll
-                for (int rt = 0; rt < MT; ++rt) {
-#pragma unroll
-                    for (int t = 0; t < 3; ++t) a[rt][t] = *(const v8bf *)(&sA[buf][bl][t][rt][lane * 16]);
-                    xsv[rt] = *(const v4f *)(&sXS[buf][bl][rt * 16 + 4 * (lane >> 4)]);
-                }
-#pragma unroll
-                for (int j = 0; j < C; ++j) {
-                    const v8bf bop = decode8((uint32_t)bc[q][j][i]);
-                    const uint32_t dm = (uint32_t)bs[q][j][i];
-                    const float d = bf16_bits_f32(dm & 0xFFFFu);
-                    const float mn = bf16_bits_f32(dm >> 16);
-#pragma unroll
-                    for (int rt = 0; rt < MT; ++rt) {
-                        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][0], bop, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][1], bop, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt][2], bop, acc, 0, 0, 0);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            acc_y[rt][j][v] = fmaf(d, acc[v], acc_y[rt][j][v]);
-                            acc_y[rt][j][v] = fmaf(mn, xsv[rt][v], acc_y[rt][j][v]);
-                        }
-                    }
-                }
-            }
-        }
-        if (c + 1 < nchunk) {
-            sstore_a(buf ^ 1);
-#pragma unroll
-            for (int q = 0; q < QC; ++q)
-#pragma unroll
-                for (int j = 0; j < C; ++j) {
-                    bc[q][j] = nbc[q][j];
-                    bs[q][j] = nbs[q][j];
-                }
-        }
-        __syncthreads();
     }
 
 #pragma unroll
@@ -416,12 +463,19 @@ hipError_t launch_q4_repack(const uint8_t *blocks, const Q4Layout &L, uint8_t *p
 
 hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int64_t grid, hipStream_t s,
                            const char **variant) {
+    const dim3 g((unsigned)grid), b(512);
     if (mt == 1 && waves == 8) {
         *variant = "q4_mm_m16";
-        hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4>), dim3((unsigned)grid), dim3(512), 0, s, p);
+        if (p.x_vec)
+            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, true>), g, b, 0, s, p);
+        else
+            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, false>), g, b, 0, s, p);
     } else if (mt == 2 && waves == 8) {
         *variant = "q4_mm_m32";
-        hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4>), dim3((unsigned)grid), dim3(512), 0, s, p);
+        if (p.x_vec)
+            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, true>), g, b, 0, s, p);
+        else
+            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, false>), g, b, 0, s, p);
     } else {
         return hipErrorInvalidValue;
     }
@@ -443,11 +497,14 @@ hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, i
 }
 
 hipError_t launch_q4_moe(const Q4Params &p, int64_t max_chunks, hipStream_t s, const char **variant) {
-    constexpr int WAVES = 6, C = 4;
+    constexpr int WAVES = 8, C = 2;
     const int64_t groups = ceil_div(p.NS, C * WAVES);
     *variant = "q4_mm_moe_m32";
-    hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 3>), dim3((unsigned)(groups * max_chunks)), dim3(WAVES * 64),
-                       0, s, p);
+    const dim3 g((unsigned)(groups * max_chunks)), b(WAVES * 64);
+    if (p.x_vec)
+        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, true>), g, b, 0, s, p);
+    else
+        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, false>), g, b, 0, s, p);
     return hipGetLastError();
 }
 

@@ -230,7 +230,7 @@ def test_prefill_full_compare(q, orc, M, K, N, zA, zB):
     B = wl.uniform_i8(g, (K, N))
     rs = (g.uniform(0.5, 1.5, M) / 127).astype(np.float32)
     _gemm_case(q, orc, A, zA, B, zB, rs=rs, bias=wl.normal_f32(g, (N,)), scale=np.float32(0.01),
-               expect_variant="int8_prefill_128x128")
+               expect_variant="int8_prefill_256x128")
 
 
 @pytest.mark.parametrize("shape", range(len(wl.PREFILL_SHAPES)))
@@ -246,7 +246,7 @@ def test_prefill_full_size_sampled(q, orc, shape):
     y32 = torch.empty((wl.PREFILL_M, N), dtype=torch.int32, device=dev)
     yf = torch.empty((wl.PREFILL_M, N), dtype=torch.float32, device=dev)
     q.int8_gemm(to_dev(d["A"]), 0, p, 0, out_i32=y32, out_f32=yf, row_scale=to_dev(d["rs"]))
-    assert q.last_variant() == "int8_prefill_128x128"
+    assert q.last_variant() == "int8_prefill_256x128"
     g = np.random.default_rng(99 + shape)
     im = np.concatenate([g.integers(0, wl.PREFILL_M, 4096), [0, 0, wl.PREFILL_M - 1, wl.PREFILL_M - 1]])
     in_ = np.concatenate([g.integers(0, N, 4096), [0, N - 1, 0, N - 1]])
