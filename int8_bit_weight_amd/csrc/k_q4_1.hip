@@ -28,14 +28,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 template <int N> using ic = std::integral_constant<int, N>;
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
-__device__ __forceinline__ float bf16_bits_f32(uint32_t h) { return __uint_as_float(h << 16); }
-
 // Eight 4-bit codes (record nibble order) -> eight exact bf16 values in k order.
 // Each conversion yields one packed pair; the four pairs are the four dwords
 // of the MFMA operand as they are (a bit cast, no element shuffling).
@@ -95,28 +87,35 @@ __global__ __launch_bounds__(256) void k_q4_repack(const uint8_t *__restrict__ b
 // ----------------------------------------------------------- the product ---
 // Workgroup = WAVES wavefronts; each wavefront owns C column strips (16 C
 // columns) and all MT*16 rows of the workgroup's row set.  The k range is
-// walked in chunks of QC records (4 QC blocks of 32 k):
+// walked in chunks of QC records (4 QC blocks of 32 k).  Per block b and
+// column n the product needs d_bn * sum_k(q x) + m_bn * sum_k(x):
 //   * activations: the workgroup reads its rows' fp32 values for the next
-//     chunk, splits each into three bf16 terms (x = x0 + x1 + x2; both
-//     differences are exact in fp32), sums each 32-k block in a fixed order,
-//     and stores the terms as MFMA A fragments in LDS (double buffered).
-//     Only rows that exist are split; the fragments of absent rows hold
-//     whatever LDS held and only reach accumulator rows that are never
-//     stored (an MFMA output row depends on its own A row alone);
+//     chunk and splits each into three bf16 terms, x = x0 + x1 + x2 (the
+//     conversions round to nearest; both differences are exact in fp32, and
+//     x2 is exact in bf16).  The terms are stored in LDS as MFMA A fragments
+//     (double buffered).  Each block's sum of x (fixed order) is split the
+//     same way and stored as a second A operand whose k index is the block
+//     of the chunk.  Only rows that exist are staged; fragments of absent
+//     rows only reach accumulator rows that are never stored (an MFMA output
+//     row depends on its own A row alone);
 //   * weights: each wavefront streams its strips' records (16 bytes of codes
 //     and 16 bytes of (d, m) per lane per record), one chunk ahead in
 //     registers: with QC >= 2 a record's registers are refilled with the
 //     next chunk's record as soon as its last block is used; with QC == 1
 //     two register sets alternate and the chunk loop is unrolled by two;
-//   * per block and strip: codes -> exact bf16, three MFMAs into a fresh
-//     accumulator, then y += d * acc + m * sum_k(x).
+//   * d term, per block and strip: codes -> exact bf16, three MFMAs into a
+//     fresh accumulator, then y += d * acc;
+//   * m term, per chunk and strip: the chunk's m values as a bf16 B operand
+//     (k = block) against the split block sums, three MFMAs accumulating
+//     over the whole k range.
 //   dense: blockIdx -> (strip group, k split); rows 0..M-1.
 //   MoE:   blockIdx -> (strip group, row chunk); the chunk table gives the
 //          expert and the sorted (token, slot) pairs of its rows.
 // Loads are never inside branches (a load in a branch makes the compiler wait
 // for it where the branch ends, which would serialise the prefetch): indices
-// past the valid range are clamped to valid memory and the values are masked
-// where they are used.  XVEC: X and ldx allow aligned 16-byte loads.
+// past the valid range are clamped to valid memory.  A record past the range
+// takes its (d, m) from the last 16 bytes of the packed header, which are
+// zero, so it adds nothing.  XVEC: X and ldx allow aligned 16-byte loads.
 //
 // LDS layout of one 16-row A fragment (1 KiB): the 16-byte piece of (row r,
 // k-octet g) sits at slot 16 g + (r ^ f(g)), f = {0, 6, 10, 12}.  MFMA lane
@@ -127,19 +126,31 @@ __device__ __forceinline__ int a_slot(int r, int g) {
     return g * 16 + (r ^ ((0xCA60 >> (4 * g)) & 15));
 }
 
+// Two floats -> packed bf16 pair (round to nearest even), and the pair's
+// residuals x - bf16(x), exact in fp32.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    const v2bf r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
 template <int MT, int WAVES, int C, int QC, bool MOE, int MINW, bool XVEC>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_mm(Q4Params p) {
     constexpr int NT = WAVES * 64;
     constexpr int ROWS = MT * 16;
     constexpr int SPG = C * WAVES;
     constexpr int BPC = 4 * QC;
+    static_assert(BPC <= 8, "the m-term operand holds at most 8 blocks per chunk");
     constexpr int PIECES = BPC * ROWS * 4;  // (block, row, k-octet) pieces of a chunk at most
     constexpr int PPT = (PIECES + NT - 1) / NT;
     constexpr bool ROLL = QC >= 2;
     constexpr int NSET = ROLL ? 1 : 2;     // weight register sets
     constexpr int ADB = MT == 1 ? 2 : 1;   // A fragment register sets
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][BPC][3][MT][1024];
-    __shared__ __attribute__((aligned(16))) float sXS[2][BPC][ROWS];
+    // block sums as A fragments: row r, block bl at byte 16 r + 2 bl (k-octet
+    // 0); k-octets 1..3 and blocks past BPC stay zero
+    __shared__ __attribute__((aligned(16))) uint8_t sXM[2][3][MT][1024];
     __shared__ int64_t sRow[ROWS];  // element offset of each row of X
 
     const int tid = threadIdx.x;
@@ -150,14 +161,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     const int sg = blockIdx.x % groups;
     const int job = blockIdx.x / groups;
 
-    const uint8_t *recs = p.recs;
+    const uint8_t *hdr = p.recs;
     int nrows, row0 = 0, q0, q1;
     if (MOE) {
         if (job >= *p.nchunks) return;
         const int expert = p.chunk_info[job * 3 + 0];
         row0 = p.chunk_info[job * 3 + 1];
         nrows = p.chunk_info[job * 3 + 2];
-        recs += (int64_t)expert * p.expert_stride;
+        hdr += (int64_t)expert * p.expert_stride;
         q0 = 0;
         q1 = p.NQ;
     } else {
@@ -165,8 +176,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         q0 = job * p.qps;
         q1 = min(p.NQ, q0 + p.qps);
     }
-    recs += kHeaderBytes;
+    const uint8_t *recs = hdr + kHeaderBytes;
     if (tid < nrows) sRow[tid] = (int64_t)(MOE ? p.sorted[row0 + tid] / p.n_used : tid) * p.ldx;
+    for (int o = tid * 16; o < (int)sizeof(sXM); o += NT * 16) *(v4i *)(&sXM[0][0][0][0] + o) = v4i{0, 0, 0, 0};
     __syncthreads();
 
     // ---- activation staging.  Pieces of the existing rows only:
@@ -216,19 +228,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
             uint32_t w[3][4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                uint32_t t[3][2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const float x = xok[i] ? xr[i][e + h] : 0.0f;
-                    bsum += x;
-                    t[0][h] = bf16_rne_bits(x);
-                    const float r1 = x - bf16_bits_f32(t[0][h]);
-                    t[1][h] = bf16_rne_bits(r1);
-                    const float r2 = r1 - bf16_bits_f32(t[1][h]);
-                    t[2][h] = bf16_rne_bits(r2);
-                }
-#pragma unroll
-                for (int tt = 0; tt < 3; ++tt) w[tt][e >> 1] = t[tt][0] | (t[tt][1] << 16);
+                const float x0 = xok[i] ? xr[i][e] : 0.0f;
+                const float x1 = xok[i] ? xr[i][e + 1] : 0.0f;
+                bsum += x0;
+                bsum += x1;
+                const uint32_t t0 = pk_bf16(x0, x1);
+                const float r0 = x0 - bf16_lo_f32(t0), r1 = x1 - bf16_hi_f32(t0);
+                const uint32_t t1 = pk_bf16(r0, r1);
+                const uint32_t t2 = pk_bf16(r0 - bf16_lo_f32(t1), r1 - bf16_hi_f32(t1));
+                w[0][e >> 1] = t0;
+                w[1][e >> 1] = t1;
+                w[2][e >> 1] = t2;
             }
             // the four k-octets of one (row, block) sit in four adjacent lanes
             bsum += __shfl_xor(bsum, 1);
@@ -238,14 +248,23 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 #pragma unroll
                 for (int tt = 0; tt < 3; ++tt)
                     *(v4i *)(dst + tt * MT * 1024) = v4i{(int)w[tt][0], (int)w[tt][1], (int)w[tt][2], (int)w[tt][3]};
-                if (pg[i] == 0) sXS[buf][pbl[i]][prow[i]] = bsum;
+                if (pg[i] == 0) {
+                    const uint32_t s0 = pk_bf16(bsum, 0.0f);
+                    const float sr = bsum - bf16_lo_f32(s0);
+                    const uint32_t s1 = pk_bf16(sr, 0.0f);
+                    const uint32_t s2 = pk_bf16(sr - bf16_lo_f32(s1), 0.0f);
+                    uint8_t *xm = &sXM[buf][0][prow[i] >> 4][0] + (prow[i] & 15) * 16 + pbl[i] * 2;
+                    *(uint16_t *)(xm) = (uint16_t)s0;
+                    *(uint16_t *)(xm + MT * 1024) = (uint16_t)s1;
+                    *(uint16_t *)(xm + 2 * MT * 1024) = (uint16_t)s2;
+                }
             }
         }
     };
 
     // ---- weight records.  Strips past the last read the last strip (their
     // columns are never stored); records past the range read the last record
-    // of the range and are given d = m = 0 where they are used.
+    // of the range for codes and the header's zero tail for (d, m).
     const int strip_base = sg * SPG + wave * C;
     v4i bc[NSET][QC][C], bs[NSET][QC][C];
     auto gload_rec = [&](int quad, v4i (&dc)[C], v4i (&ds)[C]) {
@@ -254,59 +273,65 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         for (int j = 0; j < C; ++j) {
             const int strip = min(strip_base + j, p.NS - 1);
             const uint8_t *rec = recs + ((int64_t)strip * p.NQ + qq) * kQ4RecBytes;
+            const uint8_t *dmp = quad < q1 ? rec + 1024 + (uint32_t)(lane & 15) * 16u : hdr + kHeaderBytes - 16;
             dc[j] = *(const v4i *)(rec + (uint32_t)lane * 16u);
-            ds[j] = *(const v4i *)(rec + 1024 + (uint32_t)(lane & 15) * 16u);
+            ds[j] = *(const v4i *)dmp;
         }
     };
 
-    v4f acc_y[MT][C];
+    v4f acc_y[MT][C], acc_m[MT][C];
 #pragma unroll
     for (int rt = 0; rt < MT; ++rt)
 #pragma unroll
-        for (int j = 0; j < C; ++j) acc_y[rt][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < C; ++j) {
+            acc_y[rt][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            acc_m[rt][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 
     const int a_off = a_slot(lane & 15, lane >> 4) * 16;
     const int nchunk = (q1 - q0 + QC - 1) / QC;
 
     // One chunk: c = chunk index, buf = its LDS buffer, S = its weight set.
     // The next chunk's activations (and, with two sets, its records) are
-    // loaded first; the last chunk reloads its own (never used).
+    // loaded first; the last chunk reloads its own activations (never used).
     auto chunk = [&](int c, int buf, auto S_) {
         constexpr int S = decltype(S_)::value;
-        const int qc = q0 + c * QC;
         const int qn = q0 + min(c + 1, nchunk - 1) * QC;
         if (!ROLL) {
+            // unclamped: the chunk past the range (odd count) gets d = m = 0
+            const int qr = q0 + (c + 1) * QC;
 #pragma unroll
-            for (int q = 0; q < QC; ++q) gload_rec(qn + q, bc[S ^ (NSET - 1)][q], bs[S ^ (NSET - 1)][q]);
+            for (int q = 0; q < QC; ++q) gload_rec(qr + q, bc[S ^ (NSET - 1)][q], bs[S ^ (NSET - 1)][q]);
         }
         gload_a(qn);
         v8bf a[ADB][MT][3];
-        v4f xsv[ADB][MT];
-        auto lds_a = [&](int bl, v8bf (&ad)[MT][3], v4f (&xd)[MT]) {
+        auto lds_a = [&](int bl, v8bf (&ad)[MT][3]) {
 #pragma unroll
-            for (int rt = 0; rt < MT; ++rt) {
+            for (int rt = 0; rt < MT; ++rt)
 #pragma unroll
                 for (int t = 0; t < 3; ++t) ad[rt][t] = *(const v8bf *)(&sA[buf][bl][t][rt][a_off]);
-                xd[rt] = *(const v4f *)(&sXS[buf][bl][rt * 16 + 4 * (lane >> 4)]);
-            }
         };
-        if (ADB == 2) lds_a(0, a[0], xsv[0]);
+        // m values of the chunk's blocks as bf16 pairs (k = block), packed
+        // before the records' registers are refilled
+        uint32_t mw[C][4];
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) mw[j][t] = 0u;
+        if (ADB == 2) lds_a(0, a[0]);
 #pragma unroll
         for (int bl = 0; bl < BPC; ++bl) {
             const int q = bl >> 2, i = bl & 3;
             const int ab = ADB == 2 ? (bl & 1) : 0;
             if (ADB == 2) {
-                if (bl + 1 < BPC) lds_a(bl + 1, a[(bl + 1) & 1], xsv[(bl + 1) & 1]);
+                if (bl + 1 < BPC) lds_a(bl + 1, a[(bl + 1) & 1]);
             } else {
-                lds_a(bl, a[0], xsv[0]);
+                lds_a(bl, a[0]);
             }
-            const bool rec_ok = qc + q < q1;
 #pragma unroll
             for (int j = 0; j < C; ++j) {
                 const v8bf bop = decode8((uint32_t)bc[S][q][j][i]);
-                const uint32_t dm = rec_ok ? (uint32_t)bs[S][q][j][i] : 0u;
-                const float d = bf16_bits_f32(dm & 0xFFFFu);
-                const float mn = bf16_bits_f32(dm >> 16);
+                const float d = bf16_lo_f32((uint32_t)bs[S][q][j][i]);
 #pragma unroll
                 for (int rt = 0; rt < MT; ++rt) {
                     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -314,21 +339,39 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][1], bop, acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][2], bop, acc, 0, 0, 0);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        acc_y[rt][j][v] = fmaf(d, acc[v], acc_y[rt][j][v]);
-                        acc_y[rt][j][v] = fmaf(mn, xsv[ab][rt][v], acc_y[rt][j][v]);
-                    }
+                    for (int v = 0; v < 4; ++v) acc_y[rt][j][v] = fmaf(d, acc[v], acc_y[rt][j][v]);
                 }
             }
             // pin the accumulators here: otherwise the compiler sinks every
-            // block's d/m update to the end of the chunk and keeps all the
-            // MFMA results alive until then
+            // block's update to the end of the chunk and keeps all the MFMA
+            // results alive until then
 #pragma unroll
             for (int rt = 0; rt < MT; ++rt)
 #pragma unroll
                 for (int j = 0; j < C; ++j) asm volatile("" : "+v"(acc_y[rt][j]));
-            if (ROLL && i == 3) gload_rec(qn + q, bc[0][q], bs[0][q]);
+            if (i == 3) {
+#pragma unroll
+                for (int j = 0; j < C; ++j) {
+                    // high halves (m) of blocks (0, 1) and (2, 3) of the record
+                    mw[j][2 * q] = __builtin_amdgcn_perm((uint32_t)bs[S][q][j][1], (uint32_t)bs[S][q][j][0], 0x07060302u);
+                    mw[j][2 * q + 1] = __builtin_amdgcn_perm((uint32_t)bs[S][q][j][3], (uint32_t)bs[S][q][j][2], 0x07060302u);
+                }
+                if (ROLL) gload_rec(qn + q, bc[0][q], bs[0][q]);
+            }
             __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int rt = 0; rt < MT; ++rt) {
+            v8bf xm[3];
+#pragma unroll
+            for (int t = 0; t < 3; ++t) xm[t] = *(const v8bf *)(&sXM[buf][t][rt][lane * 16]);
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const v8bf mop = __builtin_bit_cast(v8bf, v4i{(int)mw[j][0], (int)mw[j][1], (int)mw[j][2], (int)mw[j][3]});
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+                    acc_m[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm[t], mop, acc_m[rt][j], 0, 0, 0);
+            }
         }
         sstore_a(buf ^ 1);
         __syncthreads();
@@ -345,7 +388,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         for (int c = 0; c < nchunk; ++c) chunk(c, c & 1, ic<0>{});
     } else {
         // pairs of chunks; an odd count ends with one chunk past the range,
-        // whose records are masked (d = m = 0) and activations are zero
+        // whose records have d = m = 0
         for (int c = 0; c < nchunk; c += 2) {
             chunk(c, 0, ic<0>{});
             chunk(c + 1, 1, ic<NSET - 1>{});
@@ -361,7 +404,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                 const int row = rt * 16 + 4 * (lane >> 4) + v;
                 const int n = (strip_base + j) * 16 + (lane & 15);
                 if (row < nrows && n < p.N) {
-                    const float val = acc_y[rt][j][v];
+                    const float val = acc_y[rt][j][v] + acc_m[rt][j][v];
                     if (MOE) {
                         const int pair = p.sorted[row0 + row];
                         const int t = pair / p.n_used;
@@ -376,14 +419,24 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
             }
 }
 
-// Sum of the k-split partials in split order.
+// Sum of the k-split partials in split order.  Loads go out eight at a time
+// (independent, clamped to the last split; extra ones are not added) so that
+// a thread waits for one memory latency per eight splits, not per split.
 __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ part, int S, int M, int N,
                                                      float *__restrict__ Y, int64_t ldy) {
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (gid >= (int64_t)M * N) return;
     const int64_t m = gid / N, n = gid % N;
+    const int64_t stride = (int64_t)M * N;
     float acc = 0.0f;
-    for (int s = 0; s < S; ++s) acc += part[((int64_t)s * M + m) * N + n];
+    for (int s0 = 0; s0 < S; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[min(s0 + u, S - 1) * stride + gid];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < S) acc += v[u];
+    }
     Y[m * ldy + n] = acc;
 }
 
