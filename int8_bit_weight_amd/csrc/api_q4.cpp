@@ -24,9 +24,10 @@ Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
     Q4Plan pl{};
     const Q4Layout L = q4_layout(K, N);
     pl.rows_per_launch = M < 32 ? M : 32;
-    pl.mt = pl.rows_per_launch <= 16 ? 1 : 2;
+    // mt 0: one 16-row tile holding the three bf16 terms of up to 4 rows
+    pl.mt = pl.rows_per_launch <= 4 ? 0 : pl.rows_per_launch <= 16 ? 1 : 2;
     pl.waves = 8;
-    const int64_t qc = pl.mt == 1 ? 2 : 1;
+    const int64_t qc = pl.mt <= 1 ? 2 : 1;
     const int64_t groups = ceil_div(L.NS, 2 * pl.waves);
     const int64_t target = pl.rows_per_launch <= 4 ? 512 : 256;
     int64_t S = ceil_div(target, groups);

@@ -135,22 +135,28 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 __device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-template <int MT, int WAVES, int C, int QC, bool MOE, int MINW, bool XVEC>
+template <int MT, int WAVES, int C, int QC, bool MOE, int MINW, bool XVEC, bool TIR>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_mm(Q4Params p) {
+    static_assert(!TIR || (MT == 1 && !MOE), "terms in rows: one 16-row tile, dense");
     constexpr int NT = WAVES * 64;
     constexpr int ROWS = MT * 16;
+    constexpr int XROWS = TIR ? 4 : ROWS;  // activation rows a workgroup can hold
+    constexpr int NF = TIR ? 1 : 3;        // A fragments per block and row tile
     constexpr int SPG = C * WAVES;
     constexpr int BPC = 4 * QC;
     static_assert(BPC <= 8, "the m-term operand holds at most 8 blocks per chunk");
-    constexpr int PIECES = BPC * ROWS * 4;  // (block, row, k-octet) pieces of a chunk at most
+    constexpr int PIECES = BPC * XROWS * 4;  // (block, row, k-octet) pieces of a chunk at most
     constexpr int PPT = (PIECES + NT - 1) / NT;
-    constexpr bool ROLL = QC >= 2;
-    constexpr int NSET = ROLL ? 1 : 2;     // weight register sets
+    // weight register sets.  QC >= 2: one set; each record's registers are
+    // refilled with the next chunk's record right after their last use.
+    // QC == 1: two sets; chunk c loads chunk c + 1's records into the other
+    // set when it starts.
+    constexpr int NSET = QC >= 2 ? 1 : 2;
     constexpr int ADB = MT == 1 ? 2 : 1;   // A fragment register sets
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BPC][3][MT][1024];
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BPC][NF][MT][1024];
     // block sums as A fragments: row r, block bl at byte 16 r + 2 bl (k-octet
     // 0); k-octets 1..3 and blocks past BPC stay zero
-    __shared__ __attribute__((aligned(16))) uint8_t sXM[2][3][MT][1024];
+    __shared__ __attribute__((aligned(16))) uint8_t sXM[2][NF][MT][1024];
     __shared__ int64_t sRow[ROWS];  // element offset of each row of X
 
     const int tid = threadIdx.x;
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     // ---- activation staging.  Pieces of the existing rows only:
     // piece -> (g = piece % 4, row = piece / 4 % nrows, block = piece / 4 / nrows).
     const int active = nrows * BPC * 4;
-    int pbl[PPT], pg[PPT], prow[PPT], pdst[PPT];
+    int pbl[PPT], pg[PPT], prow[PPT], pdst[PPT][TIR ? 3 : 1];
     int64_t psrc[PPT];
     bool pok[PPT];
 #pragma unroll
@@ -198,7 +204,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         pbl[i] = t / nrows;
         pok[i] = idx < active;
         psrc[i] = sRow[row] + pg[i] * 8;
-        pdst[i] = (pbl[i] * 3 * MT + (row >> 4)) * 1024 + a_slot(row & 15, pg[i]) * 16;
+        if (TIR) {
+#pragma unroll
+            for (int t = 0; t < (TIR ? 3 : 1); ++t) pdst[i][t] = pbl[i] * 1024 + a_slot(4 * row + t, pg[i]) * 16;
+        } else {
+            pdst[i][0] = (pbl[i] * 3 * MT + (row >> 4)) * 1024 + a_slot(row & 15, pg[i]) * 16;
+        }
     }
     float xr[PPT][8];
     bool xok[PPT];
@@ -244,19 +255,26 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
             bsum += __shfl_xor(bsum, 1);
             bsum += __shfl_xor(bsum, 2);
             if (pok[i]) {
-                uint8_t *dst = &sA[buf][0][0][0][0] + pdst[i];
 #pragma unroll
                 for (int tt = 0; tt < 3; ++tt)
-                    *(v4i *)(dst + tt * MT * 1024) = v4i{(int)w[tt][0], (int)w[tt][1], (int)w[tt][2], (int)w[tt][3]};
+                    *(v4i *)(&sA[buf][0][0][0][0] + (TIR ? pdst[i][TIR ? tt : 0] : pdst[i][0] + tt * MT * 1024)) =
+                        v4i{(int)w[tt][0], (int)w[tt][1], (int)w[tt][2], (int)w[tt][3]};
                 if (pg[i] == 0) {
                     const uint32_t s0 = pk_bf16(bsum, 0.0f);
                     const float sr = bsum - bf16_lo_f32(s0);
                     const uint32_t s1 = pk_bf16(sr, 0.0f);
                     const uint32_t s2 = pk_bf16(sr - bf16_lo_f32(s1), 0.0f);
-                    uint8_t *xm = &sXM[buf][0][prow[i] >> 4][0] + (prow[i] & 15) * 16 + pbl[i] * 2;
-                    *(uint16_t *)(xm) = (uint16_t)s0;
-                    *(uint16_t *)(xm + MT * 1024) = (uint16_t)s1;
-                    *(uint16_t *)(xm + 2 * MT * 1024) = (uint16_t)s2;
+                    if (TIR) {
+                        uint8_t *xm = &sXM[buf][0][0][0] + prow[i] * 64 + pbl[i] * 2;
+                        *(uint16_t *)(xm) = (uint16_t)s0;
+                        *(uint16_t *)(xm + 16) = (uint16_t)s1;
+                        *(uint16_t *)(xm + 32) = (uint16_t)s2;
+                    } else {
+                        uint8_t *xm = &sXM[buf][0][prow[i] >> 4][0] + (prow[i] & 15) * 16 + pbl[i] * 2;
+                        *(uint16_t *)(xm) = (uint16_t)s0;
+                        *(uint16_t *)(xm + MT * 1024) = (uint16_t)s1;
+                        *(uint16_t *)(xm + 2 * MT * 1024) = (uint16_t)s2;
+                    }
                 }
             }
         }
@@ -297,19 +315,19 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     auto chunk = [&](int c, int buf, auto S_) {
         constexpr int S = decltype(S_)::value;
         const int qn = q0 + min(c + 1, nchunk - 1) * QC;
-        if (!ROLL) {
+        if (NSET == 2) {
             // unclamped: the chunk past the range (odd count) gets d = m = 0
-            const int qr = q0 + (c + 1) * QC;
 #pragma unroll
-            for (int q = 0; q < QC; ++q) gload_rec(qr + q, bc[S ^ (NSET - 1)][q], bs[S ^ (NSET - 1)][q]);
+            for (int q = 0; q < QC; ++q)
+                gload_rec(q0 + (c + 1) * QC + q, bc[S ^ (NSET - 1)][q], bs[S ^ (NSET - 1)][q]);
         }
         gload_a(qn);
-        v8bf a[ADB][MT][3];
-        auto lds_a = [&](int bl, v8bf (&ad)[MT][3]) {
+        v8bf a[ADB][MT][NF];
+        auto lds_a = [&](int bl, v8bf (&ad)[MT][NF]) {
 #pragma unroll
             for (int rt = 0; rt < MT; ++rt)
 #pragma unroll
-                for (int t = 0; t < 3; ++t) ad[rt][t] = *(const v8bf *)(&sA[buf][bl][t][rt][a_off]);
+                for (int t = 0; t < NF; ++t) ad[rt][t] = *(const v8bf *)(&sA[buf][bl][t][rt][a_off]);
         };
         // m values of the chunk's blocks as bf16 pairs (k = block), packed
         // before the records' registers are refilled
@@ -335,11 +353,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 #pragma unroll
                 for (int rt = 0; rt < MT; ++rt) {
                     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][0], bop, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][1], bop, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][2], bop, acc, 0, 0, 0);
+                    if (TIR) {
+                        // rows 4m, 4m+1, 4m+2 hold the three terms of row m
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][0], bop, acc, 0, 0, 0);
+                        acc_y[rt][j][0] = fmaf(d, acc[0] + acc[1] + acc[2], acc_y[rt][j][0]);
+                    } else {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc_y[rt][j][v] = fmaf(d, acc[v], acc_y[rt][j][v]);
+                        for (int t = 0; t < NF; ++t)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][t], bop, acc, 0, 0, 0);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc_y[rt][j][v] = fmaf(d, acc[v], acc_y[rt][j][v]);
+                    }
                 }
             }
             // pin the accumulators here: otherwise the compiler sinks every
@@ -356,20 +380,20 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                     mw[j][2 * q] = __builtin_amdgcn_perm((uint32_t)bs[S][q][j][1], (uint32_t)bs[S][q][j][0], 0x07060302u);
                     mw[j][2 * q + 1] = __builtin_amdgcn_perm((uint32_t)bs[S][q][j][3], (uint32_t)bs[S][q][j][2], 0x07060302u);
                 }
-                if (ROLL) gload_rec(qn + q, bc[0][q], bs[0][q]);
+                if (NSET == 1) gload_rec(qn + q, bc[0][q], bs[0][q]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int rt = 0; rt < MT; ++rt) {
-            v8bf xm[3];
+            v8bf xm[NF];
 #pragma unroll
-            for (int t = 0; t < 3; ++t) xm[t] = *(const v8bf *)(&sXM[buf][t][rt][lane * 16]);
+            for (int t = 0; t < NF; ++t) xm[t] = *(const v8bf *)(&sXM[buf][t][rt][lane * 16]);
 #pragma unroll
             for (int j = 0; j < C; ++j) {
                 const v8bf mop = __builtin_bit_cast(v8bf, v4i{(int)mw[j][0], (int)mw[j][1], (int)mw[j][2], (int)mw[j][3]});
 #pragma unroll
-                for (int t = 0; t < 3; ++t)
+                for (int t = 0; t < NF; ++t)
                     acc_m[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm[t], mop, acc_m[rt][j], 0, 0, 0);
             }
         }
@@ -378,13 +402,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     };
 
     if (nchunk > 0) {
+        gload_a(q0);
 #pragma unroll
         for (int q = 0; q < QC; ++q) gload_rec(q0 + q, bc[0][q], bs[0][q]);
-        gload_a(q0);
         sstore_a(0);
     }
     __syncthreads();
-    if (ROLL) {
+    if (NSET == 1) {
         for (int c = 0; c < nchunk; ++c) chunk(c, c & 1, ic<0>{});
     } else {
         // pairs of chunks; an odd count ends with one chunk past the range,
@@ -400,11 +424,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 #pragma unroll
         for (int j = 0; j < C; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = rt * 16 + 4 * (lane >> 4) + v;
+            for (int v = 0; v < (TIR ? 1 : 4); ++v) {
+                const int row = TIR ? (lane >> 4) : rt * 16 + 4 * (lane >> 4) + v;
                 const int n = (strip_base + j) * 16 + (lane & 15);
                 if (row < nrows && n < p.N) {
-                    const float val = acc_y[rt][j][v] + acc_m[rt][j][v];
+                    const float val = TIR ? acc_y[rt][j][0] + ((acc_m[rt][j][0] + acc_m[rt][j][1]) + acc_m[rt][j][2])
+                                          : acc_y[rt][j][v] + acc_m[rt][j][v];
                     if (MOE) {
                         const int pair = p.sorted[row0 + row];
                         const int t = pair / p.n_used;
@@ -517,18 +542,24 @@ hipError_t launch_q4_repack(const uint8_t *blocks, const Q4Layout &L, uint8_t *p
 hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int64_t grid, hipStream_t s,
                            const char **variant) {
     const dim3 g((unsigned)grid), b(512);
-    if (mt == 1 && waves == 8) {
+    if (mt == 0 && waves == 8) {
+        *variant = "q4_mm_m4";
+        if (p.x_vec)
+            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, true, true>), g, b, 0, s, p);
+        else
+            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, false, true>), g, b, 0, s, p);
+    } else if (mt == 1 && waves == 8) {
         *variant = "q4_mm_m16";
         if (p.x_vec)
-            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, true>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, true, false>), g, b, 0, s, p);
         else
-            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, false>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, false, false>), g, b, 0, s, p);
     } else if (mt == 2 && waves == 8) {
         *variant = "q4_mm_m32";
         if (p.x_vec)
-            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, true>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, true, false>), g, b, 0, s, p);
         else
-            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, false>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, false, false>), g, b, 0, s, p);
     } else {
         return hipErrorInvalidValue;
     }
@@ -555,9 +586,9 @@ hipError_t launch_q4_moe(const Q4Params &p, int64_t max_chunks, hipStream_t s, c
     *variant = "q4_mm_moe_m32";
     const dim3 g((unsigned)(groups * max_chunks)), b(WAVES * 64);
     if (p.x_vec)
-        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, true>), g, b, 0, s, p);
+        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, true, false>), g, b, 0, s, p);
     else
-        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, false>), g, b, 0, s, p);
+        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, false, false>), g, b, 0, s, p);
     return hipGetLastError();
 }
 
