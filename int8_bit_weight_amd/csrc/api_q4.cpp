@@ -27,6 +27,24 @@ Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
     // mt 0: one 16-row tile holding the three bf16 terms of up to 4 rows
     pl.mt = pl.rows_per_launch <= 4 ? 0 : pl.rows_per_launch <= 16 ? 1 : 2;
     pl.waves = 8;
+    if (pl.mt == 0) {
+        // k_q4_gemv: workgroups of 4 wavefronts x 2 strips; each split stages
+        // its activations for at most 8 records (8 KiB of LDS per record)
+        pl.waves = 4;
+        const int64_t groups = ceil_div(L.NS, 8);
+        int64_t S = ceil_div(L.NQ, 8);
+        const int64_t want = ceil_div(448, groups);
+        if (S < want) S = want;
+        if (S > L.NQ) S = L.NQ;
+        const int64_t qps = round_up(ceil_div(L.NQ, S), 2) > 8 ? 8 : round_up(ceil_div(L.NQ, S), 2);
+        S = ceil_div(L.NQ, qps);
+        pl.S = (int)S;
+        pl.qps = (int)qps;
+        pl.grid = groups * S;
+        pl.ws_part_off = 0;
+        pl.ws_bytes = S > 1 ? round_up(S * pl.rows_per_launch * N * 4, 256) : 0;
+        return pl;
+    }
     const int64_t qc = pl.mt <= 1 ? 2 : 1;
     const int64_t groups = ceil_div(L.NS, 2 * pl.waves);
     const int64_t target = pl.rows_per_launch <= 4 ? 512 : 256;

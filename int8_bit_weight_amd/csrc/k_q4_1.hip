@@ -135,17 +135,15 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 __device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-template <int MT, int WAVES, int C, int QC, bool MOE, int MINW, bool XVEC, bool TIR>
+template <int MT, int WAVES, int C, int QC, bool MOE, int MINW, bool XVEC>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_mm(Q4Params p) {
-    static_assert(!TIR || (MT == 1 && !MOE), "terms in rows: one 16-row tile, dense");
     constexpr int NT = WAVES * 64;
     constexpr int ROWS = MT * 16;
-    constexpr int XROWS = TIR ? 4 : ROWS;  // activation rows a workgroup can hold
-    constexpr int NF = TIR ? 1 : 3;        // A fragments per block and row tile
+    constexpr int NF = 3;  // A fragments (bf16 terms) per block and row tile
     constexpr int SPG = C * WAVES;
     constexpr int BPC = 4 * QC;
     static_assert(BPC <= 8, "the m-term operand holds at most 8 blocks per chunk");
-    constexpr int PIECES = BPC * XROWS * 4;  // (block, row, k-octet) pieces of a chunk at most
+    constexpr int PIECES = BPC * ROWS * 4;  // (block, row, k-octet) pieces of a chunk at most
     constexpr int PPT = (PIECES + NT - 1) / NT;
     // weight register sets.  QC >= 2: one set; each record's registers are
     // refilled with the next chunk's record right after their last use.
@@ -190,7 +188,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     // ---- activation staging.  Pieces of the existing rows only:
     // piece -> (g = piece % 4, row = piece / 4 % nrows, block = piece / 4 / nrows).
     const int active = nrows * BPC * 4;
-    int pbl[PPT], pg[PPT], prow[PPT], pdst[PPT][TIR ? 3 : 1];
+    int pbl[PPT], pg[PPT], prow[PPT], pdst[PPT];
     int64_t psrc[PPT];
     bool pok[PPT];
 #pragma unroll
@@ -204,12 +202,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         pbl[i] = t / nrows;
         pok[i] = idx < active;
         psrc[i] = sRow[row] + pg[i] * 8;
-        if (TIR) {
-#pragma unroll
-            for (int t = 0; t < (TIR ? 3 : 1); ++t) pdst[i][t] = pbl[i] * 1024 + a_slot(4 * row + t, pg[i]) * 16;
-        } else {
-            pdst[i][0] = (pbl[i] * 3 * MT + (row >> 4)) * 1024 + a_slot(row & 15, pg[i]) * 16;
-        }
+        pdst[i] = (pbl[i] * 3 * MT + (row >> 4)) * 1024 + a_slot(row & 15, pg[i]) * 16;
     }
     float xr[PPT][8];
     bool xok[PPT];
@@ -257,24 +250,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
             if (pok[i]) {
 #pragma unroll
                 for (int tt = 0; tt < 3; ++tt)
-                    *(v4i *)(&sA[buf][0][0][0][0] + (TIR ? pdst[i][TIR ? tt : 0] : pdst[i][0] + tt * MT * 1024)) =
+                    *(v4i *)(&sA[buf][0][0][0][0] + pdst[i] + tt * MT * 1024) =
                         v4i{(int)w[tt][0], (int)w[tt][1], (int)w[tt][2], (int)w[tt][3]};
                 if (pg[i] == 0) {
                     const uint32_t s0 = pk_bf16(bsum, 0.0f);
                     const float sr = bsum - bf16_lo_f32(s0);
                     const uint32_t s1 = pk_bf16(sr, 0.0f);
                     const uint32_t s2 = pk_bf16(sr - bf16_lo_f32(s1), 0.0f);
-                    if (TIR) {
-                        uint8_t *xm = &sXM[buf][0][0][0] + prow[i] * 64 + pbl[i] * 2;
-                        *(uint16_t *)(xm) = (uint16_t)s0;
-                        *(uint16_t *)(xm + 16) = (uint16_t)s1;
-                        *(uint16_t *)(xm + 32) = (uint16_t)s2;
-                    } else {
-                        uint8_t *xm = &sXM[buf][0][prow[i] >> 4][0] + (prow[i] & 15) * 16 + pbl[i] * 2;
-                        *(uint16_t *)(xm) = (uint16_t)s0;
-                        *(uint16_t *)(xm + MT * 1024) = (uint16_t)s1;
-                        *(uint16_t *)(xm + 2 * MT * 1024) = (uint16_t)s2;
-                    }
+                    uint8_t *xm = &sXM[buf][0][prow[i] >> 4][0] + (prow[i] & 15) * 16 + pbl[i] * 2;
+                    *(uint16_t *)(xm) = (uint16_t)s0;
+                    *(uint16_t *)(xm + MT * 1024) = (uint16_t)s1;
+                    *(uint16_t *)(xm + 2 * MT * 1024) = (uint16_t)s2;
                 }
             }
         }
@@ -353,17 +339,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 #pragma unroll
                 for (int rt = 0; rt < MT; ++rt) {
                     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                    if (TIR) {
-                        // rows 4m, 4m+1, 4m+2 hold the three terms of row m
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][0], bop, acc, 0, 0, 0);
-                        acc_y[rt][j][0] = fmaf(d, acc[0] + acc[1] + acc[2], acc_y[rt][j][0]);
-                    } else {
 #pragma unroll
-                        for (int t = 0; t < NF; ++t)
-                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][t], bop, acc, 0, 0, 0);
+                    for (int t = 0; t < NF; ++t)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ab][rt][t], bop, acc, 0, 0, 0);
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) acc_y[rt][j][v] = fmaf(d, acc[v], acc_y[rt][j][v]);
-                    }
+                    for (int v = 0; v < 4; ++v) acc_y[rt][j][v] = fmaf(d, acc[v], acc_y[rt][j][v]);
                 }
             }
             // pin the accumulators here: otherwise the compiler sinks every
@@ -424,12 +404,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 #pragma unroll
         for (int j = 0; j < C; ++j)
 #pragma unroll
-            for (int v = 0; v < (TIR ? 1 : 4); ++v) {
-                const int row = TIR ? (lane >> 4) : rt * 16 + 4 * (lane >> 4) + v;
+            for (int v = 0; v < 4; ++v) {
+                const int row = rt * 16 + 4 * (lane >> 4) + v;
                 const int n = (strip_base + j) * 16 + (lane & 15);
                 if (row < nrows && n < p.N) {
-                    const float val = TIR ? acc_y[rt][j][0] + ((acc_m[rt][j][0] + acc_m[rt][j][1]) + acc_m[rt][j][2])
-                                          : acc_y[rt][j][v] + acc_m[rt][j][v];
+                    const float val = acc_y[rt][j][v] + acc_m[rt][j][v];
                     if (MOE) {
                         const int pair = p.sorted[row0 + row];
                         const int t = pair / p.n_used;
@@ -442,6 +421,208 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                     }
                 }
             }
+}
+
+// ------------------------------------------------ the product, M <= 4 ---
+// Decode-shaped product (at most 4 activation rows).  One MFMA 16-row tile
+// holds the three bf16 terms of each row (rows 4m, 4m+1, 4m+2 of the tile),
+// so a block and strip cost one MFMA.  A workgroup owns SPG = WAVES * C
+// strips and a k range of at most QMAX records: it first stages the
+// activation terms of its whole k range in LDS (one barrier), then each
+// wavefront streams its strips' records through registers with no further
+// synchronisation.  Records go two at a time (8 blocks, the k extent of one
+// m-term MFMA); NSET register sets keep the loads NSET such chunks ahead:
+// a record's registers are refilled with chunk c + NSET's record right after
+// their last use.  Records past the range read d = m = 0 (the header's zero
+// tail), so padding chunks add nothing.
+template <int WAVES, int C, int QMAX, int NSET, int MINW, bool XVEC>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_gemv(Q4Params p) {
+    constexpr int NT = WAVES * 64;
+    constexpr int SPG = C * WAVES;
+    constexpr int QC = 2;
+    static_assert(QMAX % (QC * NSET) == 0, "whole chunk sets");
+    constexpr int BMAX = 4 * QMAX;
+    constexpr int GMAX = QMAX / QC;
+    __shared__ __attribute__((aligned(16))) uint8_t sA[BMAX][1024];
+    // m-term A operand per chunk: row 4m+t, k = block of the chunk (k-octet 0)
+    __shared__ __attribute__((aligned(16))) uint8_t sXM[GMAX][1024];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int groups = (p.NS + SPG - 1) / SPG;
+    const int sg = blockIdx.x % groups;
+    const int job = blockIdx.x / groups;
+    const int nrows = p.M;
+    const int q0 = job * p.qps;
+    const int q1 = min(p.NQ, q0 + p.qps);
+    const int nchunk = (q1 - q0 + QC - 1) / QC;
+    const int nstaged = (nchunk + NSET - 1) / NSET * NSET;  // chunks run, padding included
+    const uint8_t *hdr = p.recs;
+    const uint8_t *recs = hdr + kHeaderBytes;
+
+    // ---- activation terms of the whole k range.  Pieces (row, block,
+    // k-octet), k-octet fastest; blocks past the matrix or the range are
+    // staged as zeros.  The activation loads go out first, then the first
+    // records' loads, then the split (which waits for the activations only).
+    constexpr int PPT = (4 * BMAX * 4 + NT - 1) / NT;
+    const int total = nrows * nstaged * 4 * QC * 4;
+    float xr[PPT][8];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int idx = tid + i * NT;
+        const int pc = min(idx, total - 1);
+        const int g = pc & 3;
+        const int m = (pc >> 2) % nrows;
+        const int b = (pc >> 2) / nrows;
+        const int gb = min(q0 * 4 + b, p.NB - 1);
+        const float *src = p.X + (int64_t)m * p.ldx + gb * 32 + g * 8;
+        if (XVEC) {
+            const v4f lo = *(const v4f *)src;
+            const v4f hi = *(const v4f *)(src + 4);
+            xr[i][0] = lo[0]; xr[i][1] = lo[1]; xr[i][2] = lo[2]; xr[i][3] = lo[3];
+            xr[i][4] = hi[0]; xr[i][5] = hi[1]; xr[i][6] = hi[2]; xr[i][7] = hi[3];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[i][e] = src[e];
+        }
+    }
+
+    const int strip_base = sg * SPG + wave * C;
+    v4i bc[NSET][QC][C], bs[NSET][QC][C];
+    auto gload_rec = [&](int quad, v4i (&dc)[C], v4i (&ds)[C]) {
+        const int qq = min(quad, q1 - 1);
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const int strip = min(strip_base + j, p.NS - 1);
+            const uint8_t *rec = recs + ((int64_t)strip * p.NQ + qq) * kQ4RecBytes;
+            const uint8_t *dmp = quad < q1 ? rec + 1024 + (uint32_t)(lane & 15) * 16u : hdr + kHeaderBytes - 16;
+            dc[j] = *(const v4i *)(rec + (uint32_t)lane * 16u);
+            ds[j] = *(const v4i *)dmp;
+        }
+    };
+#pragma unroll
+    for (int st = 0; st < NSET; ++st)
+#pragma unroll
+        for (int q = 0; q < QC; ++q) gload_rec(q0 + st * QC + q, bc[st][q], bs[st][q]);
+
+    for (int o = tid * 16; o < nstaged * 1024; o += NT * 16) *(v4i *)(&sXM[0][0] + o) = v4i{0, 0, 0, 0};
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        // wave-uniform: waves whose pieces are all past the last one skip
+        if (i * NT + wave * 64 >= total) continue;
+        const int idx = tid + i * NT;
+        const int pc = min(idx, total - 1);
+        const int g = pc & 3;
+        const int m = (pc >> 2) % nrows;
+        const int b = (pc >> 2) / nrows;
+        const bool ok = idx < total && q0 * 4 + b < p.NB && b < (q1 - q0) * 4;
+        float bsum = 0.0f;
+        uint32_t w[3][4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float x0 = ok ? xr[i][e] : 0.0f;
+            const float x1 = ok ? xr[i][e + 1] : 0.0f;
+            bsum += x0;
+            bsum += x1;
+            const uint32_t t0 = pk_bf16(x0, x1);
+            const float r0 = x0 - bf16_lo_f32(t0), r1 = x1 - bf16_hi_f32(t0);
+            const uint32_t t1 = pk_bf16(r0, r1);
+            const uint32_t t2 = pk_bf16(r0 - bf16_lo_f32(t1), r1 - bf16_hi_f32(t1));
+            w[0][e >> 1] = t0;
+            w[1][e >> 1] = t1;
+            w[2][e >> 1] = t2;
+        }
+        // the four k-octets of one (row, block) sit in four adjacent lanes
+        bsum += __shfl_xor(bsum, 1);
+        bsum += __shfl_xor(bsum, 2);
+        if (idx < total) {
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+                *(v4i *)(&sA[b][a_slot(4 * m + t, g) * 16]) = v4i{(int)w[t][0], (int)w[t][1], (int)w[t][2], (int)w[t][3]};
+            if (g == 0) {
+                const uint32_t s0 = pk_bf16(bsum, 0.0f);
+                const float sr = bsum - bf16_lo_f32(s0);
+                const uint32_t s1 = pk_bf16(sr, 0.0f);
+                const uint32_t s2 = pk_bf16(sr - bf16_lo_f32(s1), 0.0f);
+                uint8_t *xm = &sXM[b >> 3][m * 64 + (b & 7) * 2];
+                *(uint16_t *)(xm) = (uint16_t)s0;
+                *(uint16_t *)(xm + 16) = (uint16_t)s1;
+                *(uint16_t *)(xm + 32) = (uint16_t)s2;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- stream the records
+    float acc_y[C];
+    v4f acc_m[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        acc_y[j] = 0.0f;
+        acc_m[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int a_off = a_slot(lane & 15, lane >> 4) * 16;
+    auto chunk = [&](int c, auto S_) {
+        constexpr int S = decltype(S_)::value;
+        uint32_t mw[C][4];
+        v8bf a[2];
+        a[0] = *(const v8bf *)(&sA[c * 4 * QC][a_off]);
+#pragma unroll
+        for (int bl = 0; bl < 4 * QC; ++bl) {
+            const int q = bl >> 2, i = bl & 3;
+            if (bl + 1 < 4 * QC) a[(bl + 1) & 1] = *(const v8bf *)(&sA[c * 4 * QC + bl + 1][a_off]);
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const v8bf bop = decode8((uint32_t)bc[S][q][j][i]);
+                const float d = bf16_lo_f32((uint32_t)bs[S][q][j][i]);
+                v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[bl & 1], bop, acc, 0, 0, 0);
+                acc_y[j] = fmaf(d, acc[0] + acc[1] + acc[2], acc_y[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < C; ++j) asm volatile("" : "+v"(acc_y[j]));
+            if (i == 3) {
+#pragma unroll
+                for (int j = 0; j < C; ++j) {
+                    mw[j][2 * q] = __builtin_amdgcn_perm((uint32_t)bs[S][q][j][1], (uint32_t)bs[S][q][j][0], 0x07060302u);
+                    mw[j][2 * q + 1] = __builtin_amdgcn_perm((uint32_t)bs[S][q][j][3], (uint32_t)bs[S][q][j][2], 0x07060302u);
+                }
+                gload_rec(q0 + (c + NSET) * QC + q, bc[S][q], bs[S][q]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const v8bf xm = *(const v8bf *)(&sXM[c][lane * 16]);
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const v8bf mop = __builtin_bit_cast(v8bf, v4i{(int)mw[j][0], (int)mw[j][1], (int)mw[j][2], (int)mw[j][3]});
+            acc_m[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, mop, acc_m[j], 0, 0, 0);
+        }
+    };
+    if (NSET == 1) {
+        for (int c = 0; c < nchunk; ++c) chunk(c, ic<0>{});
+    } else {
+        // pairs of chunks; an odd count ends with a chunk past the range
+        // (d = m = 0, zero activations)
+        for (int c = 0; c < nchunk; c += 2) {
+            chunk(c, ic<0>{});
+            chunk(c + 1, ic<NSET - 1>{});
+        }
+    }
+
+    const int m = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        const int n = (strip_base + j) * 16 + (lane & 15);
+        if (m < nrows && n < p.N) {
+            const float val = acc_y[j] + ((acc_m[j][0] + acc_m[j][1]) + acc_m[j][2]);
+            if (p.S == 1)
+                p.Y[(int64_t)m * p.ldy + n] = val;
+            else
+                p.part[((int64_t)job * p.M + m) * p.N + n] = val;
+        }
+    }
 }
 
 // Sum of the k-split partials in split order.  Loads go out eight at a time
@@ -542,24 +723,27 @@ hipError_t launch_q4_repack(const uint8_t *blocks, const Q4Layout &L, uint8_t *p
 hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int64_t grid, hipStream_t s,
                            const char **variant) {
     const dim3 g((unsigned)grid), b(512);
-    if (mt == 0 && waves == 8) {
-        *variant = "q4_mm_m4";
+    if (mt == 0) {
+        // k_q4_gemv<WAVES, C, QMAX, ...>: the planner's groups, splits and
+        // qps assume 4 wavefronts x 2 strips and at most 8 records per split
+        *variant = "q4_gemv_m4";
+        const dim3 b4(256);
         if (p.x_vec)
-            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, true, true>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_gemv<4, 2, 8, 2, 4, true>), g, b4, 0, s, p);
         else
-            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, false, true>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_gemv<4, 2, 8, 2, 4, false>), g, b4, 0, s, p);
     } else if (mt == 1 && waves == 8) {
         *variant = "q4_mm_m16";
         if (p.x_vec)
-            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, true, false>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, true>), g, b, 0, s, p);
         else
-            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, false, false>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, false>), g, b, 0, s, p);
     } else if (mt == 2 && waves == 8) {
         *variant = "q4_mm_m32";
         if (p.x_vec)
-            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, true, false>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, true>), g, b, 0, s, p);
         else
-            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, false, false>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, false>), g, b, 0, s, p);
     } else {
         return hipErrorInvalidValue;
     }
@@ -586,9 +770,9 @@ hipError_t launch_q4_moe(const Q4Params &p, int64_t max_chunks, hipStream_t s, c
     *variant = "q4_mm_moe_m32";
     const dim3 g((unsigned)(groups * max_chunks)), b(WAVES * 64);
     if (p.x_vec)
-        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, true, false>), g, b, 0, s, p);
+        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, true>), g, b, 0, s, p);
     else
-        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, false, false>), g, b, 0, s, p);
+        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, false>), g, b, 0, s, p);
     return hipGetLastError();
 }
 

@@ -93,7 +93,7 @@ def test_q4_matmul_variants_and_determinism(q, orc):
     a = to_np(q.q4_1_matmul(X, p))
     assert q.last_variant() == "q4_mm_m16"
     q.q4_1_matmul(to_dev(wl.q4_activations(3, 1024, seed_index=7)), p)
-    assert q.last_variant() == "q4_mm_m4"
+    assert q.last_variant() == "q4_gemv_m4"
     b = to_np(q.q4_1_matmul(X, p))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     q.q4_1_matmul(to_dev(wl.q4_activations(20, 1024, seed_index=6)), p)
