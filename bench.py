@@ -6,18 +6,19 @@ Workload (one "step"): the seven Qwen3-0.6B projections of all 28 layers
 timed region: ~420 MiB of int8 codes, more than the 256 MiB Infinity Cache)
 run as decode at M = 1, 16 and 32 rows of fp32 N(0, 1) activations.  Every
 call is int8_gemm_dynamic: per-row amax/127 quantisation of the activations
-(inside the int8 product kernel for M <= 16 and K <= 1024, a separate kernel
-otherwise) and the int8 product with the fp32 epilogue (row scale x column
-scale).  Each M's 196 calls are captured in
-one HIP graph; a step replays the three graphs.
+(inside the int8 product kernel when M' * K <= 32768 with M' = M rounded up to
+a power of two <= 16, a separate kernel otherwise) and the int8 product with
+the fp32 epilogue (row scale x column scale).  Each M's 196 calls are
+captured in one HIP graph; a step replays the three graphs.
 
 `value` is the step's algorithmic bytes (per call K*N weight bytes + 4N column
 scales + 4MK activations + 4MN outputs) over its wall time, in GB/s.
-`roofline` is the dominant kernel, the int8 decode GEMM: its algorithmic
-bytes per launch (K*N + 4N + 4MK + 4MN with the activations quantised inside,
-for M <= 16 and K <= 1024; K*N + 4N + MK + 4M + 4MN on pre-quantised rows
-otherwise) over its average launch time from graphs of its launches alone
-(HIP events on the replay stream, dispatch gaps included).  `extra` carries the
+`roofline` is the dominant kernel, the int8 decode GEMM (k_int8_decode_q with
+the quantisation inside, k_int8_decode on pre-quantised rows): its
+algorithmic bytes per launch (K*N + 4N + 4MK + 4MN with the activations
+quantised inside; K*N + 4N + MK + 4M + 4MN on pre-quantised rows) over its
+average launch time from graphs of its launches alone (HIP events on the
+replay stream, dispatch gaps included).  `extra` carries the
 per-M figures and the other configurations (int8 prefill at M = 2048).
 `cpu_baseline` times the CPU oracle on one whole step.
 
@@ -40,7 +41,7 @@ METRIC = "GB/s & %HBM peak at M=1/16; int8 TOPS & %MFMA peak at M=2048"
 # (FETCH_SIZE, then WRITE_SIZE) of `bench.py --probe --no-cpu-baseline`, each
 # scaled by what the counter reads for the probe's 1 GiB device copy (FETCH_SIZE
 # x 2.0, WRITE_SIZE x 1.0).  Valid only for the kernel sources it was taken on.
-MEASURED_TRAFFIC = {"sources_sha1": "d66bdf8df42cc04132f4e031501b28c1241040e8", "bytes_per_launch": 2774681}
+MEASURED_TRAFFIC = {"sources_sha1": "383aca85567698abf1cf8036fc90de58eebd0507", "bytes_per_launch": 2802484}
 
 
 def decode_traffic():
@@ -69,6 +70,14 @@ def parse_args():
                     help="counter probe: one 1 GiB device copy (the calibration kernel), then each decode "
                          "call of one step once, eagerly; for rocprofv3 --pmc runs")
     return ap.parse_args()
+
+
+def fused_quant(M, K):
+    """int8_gemm_dynamic quantises inside the product kernel (one launch)."""
+    e = 1
+    while e < M:
+        e <<= 1
+    return e <= 16 and K <= 4096 and e * K <= 32768
 
 
 def call_bytes(M, K, N):
@@ -205,9 +214,9 @@ def main() -> int:
         per_m[M] = dict(sec=sec, gbs=step_bytes[M] / sec / 1e9, calls=len(calls[M]))
     log("step %.3f ms, %.1f GB/s" % (ms_per_step, value))
 
-    # Dominant kernel: the int8 decode GEMM (k_int8_decode).  A call is one
-    # launch of it with the activations quantised inside (M <= 16, K <= 1024)
-    # or the row quantiser plus it.  Its average launch time is
+    # Dominant kernel: the int8 decode GEMM.  A call is one launch of it with
+    # the activations quantised inside (fused_quant) or the row quantiser
+    # plus it.  Its average launch time is
     # taken from graphs holding only its launches, replayed back to back and
     # timed with HIP events on the replay stream (so the short dispatch gaps
     # between launches are included).
@@ -217,7 +226,7 @@ def main() -> int:
         pre = []
         kb = 0
         for (l, p, K, N, X, Y) in calls[M]:
-            if M <= 16 and K <= 1024:
+            if fused_quant(M, K):
                 pre.append((packed[(l, p)], X, None, Y))
                 kb += call_bytes(M, K, N)
             else:
@@ -252,7 +261,8 @@ def main() -> int:
         n_launch += len(calls[M])
     achieved = kern_b / kern_t / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(), "kernel": "k_int8_decode",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
+                "kernel": "int8 decode GEMM (k_int8_decode_q, k_int8_decode)",
                 "algorithmic_bytes_per_launch": round(kern_b / n_launch),
                 "avg_launch_us": round(kern_t / n_launch * 1e6, 3), "launches_per_step": n_launch}
 

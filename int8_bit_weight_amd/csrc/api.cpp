@@ -54,13 +54,11 @@ Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N) {
     if (M <= 32) {
         pl.variant = 0;
         pl.mt = M <= 16 ? 1 : 2;
-        int waves = L.KT <= 4 ? 4 : (L.KT <= 8 ? 8 : 16);
+        // one round of 16 wavefronts covers K <= 4096 (up to 4 tiles each);
+        // (waves, tiles per wave) is one of 4x1, 8x1, 16x1, 16x2, 16x4
+        const int waves = L.KT <= 4 ? 4 : (L.KT <= 8 ? 8 : 16);
         int tpw = (int)ceil_div(L.KT, waves);
         tpw = tpw <= 1 ? 1 : (tpw <= 2 ? 2 : 4);
-        waves = env_int("QMM_DECODE_WAVES", waves);
-        tpw = env_int("QMM_DECODE_TPW", tpw);
-        if (waves != 4 && waves != 8 && waves != 16) waves = 16;
-        if (tpw != 1 && tpw != 2 && tpw != 4) tpw = 4;
         pl.waves = waves;
         pl.tpw = tpw;
         pl.grid = L.NS;
@@ -241,9 +239,19 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
     return st;
 }
 
+// The fused form quantises all M x K activations in every workgroup: it
+// wins while that is small next to a second launch (measured on MI355X for
+// the Qwen3-0.6B projections: M = 1 and M = 16 with K <= 2048 gain, M = 32
+// loses).
+static bool dynamic_fused(int64_t M, int64_t K) {
+    int64_t e = 1;
+    while (e < M) e <<= 1;
+    return e <= 16 && K <= 4096 && e * K <= 32768;
+}
+
 size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     if (M <= 0 || K <= 0 || N <= 0) return 0;
-    if (M <= 16 && K <= 1024) return (size_t)plan_int8_gemm(M, K, N).ws_bytes;
+    if (dynamic_fused(M, K)) return (size_t)plan_int8_gemm(M, K, N).ws_bytes;
     return (size_t)(round_up(M * K, 256) + round_up(4 * M, 256));
 }
 
@@ -261,11 +269,8 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
         check_epilogue_ptrs(ep) != QMM_OK)
         return QMM_ERR_INVALID;
     hipStream_t s = (hipStream_t)stream;
-    if (M > 16 || K > 1024) {
-        // The row quantiser, then the product.  Inside the product kernel
-        // every 16-column workgroup quantises all M x K activations again;
-        // that only beats a second launch while each of 16 wavefronts holds
-        // one 64-k tile of them in registers (M <= 16, K <= 1024).
+    if (!dynamic_fused(M, K)) {
+        // The row quantiser, then the product.
         int8_t *q = Xq;
         float *rs = row_scale;
         int64_t lq = ldq;
@@ -284,11 +289,10 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
         e2.row_scale = rs;
         return int8_gemm(q, QMM_S8, M, K, lq, 0, packedB, QMM_S8, N, 0, &e2, nullptr, 0, stream);
     }
-    // 16 wavefronts with one k tile each: one round covers K <= 1024, so the
-    // activations stay in registers between the amax and quantise passes.
+    // 16 wavefronts with up to 4 k tiles each: one round covers K <= 4096,
+    // so the activations stay in registers between the amax and quantise
+    // passes.
     Int8Plan plan = plan_int8_gemm(M, K, N);
-    plan.waves = 16;
-    plan.tpw = 1;
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
         return QMM_ERR_WORKSPACE;
     Int8GemmParams p{};

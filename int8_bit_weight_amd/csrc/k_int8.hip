@@ -171,59 +171,74 @@ __device__ __forceinline__ void epilogue_store_c(const Int8GemmParams &p, int m,
     }
 }
 
-__device__ __forceinline__ void epilogue_store(const Int8GemmParams &p, int m, int n, uint32_t S,
-                                               int32_t rowsum, bool has_zb, float rs) {
-    epilogue_store_c(p, m, n, S, rowsum, has_zb, rs, load_colops(p, n));
-}
+// --------------------------------------------------------- decode GEMM ---
+// Loads of the decode kernels are never inside branches (a load in a branch
+// makes the compiler wait for it where the branch ends, which serialises the
+// memory round trips): rows, k and tiles past the valid range are clamped to
+// valid memory and the values are masked where they are used.  AVEC (A or X
+// 16-byte aligned, ld and K multiples of 16) selects 16-byte loads.
 
 // 16 bytes of A' (shifted domain) for row `row`, k = k0 .. k0+15; zero where
 // row >= M or k >= K.  uint8 A is shifted by flipping the top bit.
+template <bool AVEC>
 __device__ __forceinline__ v4i load_a16(const Int8GemmParams &p, int row, int k0) {
-    v4i v = {0, 0, 0, 0};
-    if (row >= p.M || k0 >= p.K) return v;
-    const int8_t *src = p.A + (int64_t)row * p.lda + k0;
+    const int r = min(row, p.M - 1);
+    const int8_t *src = p.A + (int64_t)r * p.lda;
     const uint32_t flip = p.a_u8 ? 0x80808080u : 0u;
-    if (p.a_vec && k0 + 16 <= p.K) {
-        v = *(const v4i *)src;
-        v[0] ^= flip;
-        v[1] ^= flip;
-        v[2] ^= flip;
-        v[3] ^= flip;
-        return v;
-    }
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    for (int j = 0; j < 16; ++j) {
-        if (k0 + j < p.K) {
-            const uint32_t b = (uint8_t)src[j] ^ (flip & 0xFFu);
-            w[j >> 2] |= b << (8 * (j & 3));
+    uint32_t w[4];
+    if (AVEC) {
+        const bool ok = row < p.M && k0 < p.K;
+        const v4i v = *(const v4i *)(src + min(k0, p.K - 16));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = ok ? ((uint32_t)v[i] ^ flip) : 0u;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t b = (uint8_t)src[min(k0 + j, p.K - 1)] ^ (flip & 0xFFu);
+            w[j >> 2] |= (row < p.M && k0 + j < p.K ? b : 0u) << (8 * (j & 3));
         }
     }
-    v[0] = (int)w[0];
-    v[1] = (int)w[1];
-    v[2] = (int)w[2];
-    v[3] = (int)w[3];
-    return v;
+    return v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
 }
 
 // 16 fp32 activations of row `row`, k = k0 .. k0+15 (zero outside M x K).
+template <bool AVEC>
 __device__ __forceinline__ void load_x16(const Int8GemmParams &p, int row, int k0, float (&x)[16]) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = 0.0f;
-    if (row >= p.M || k0 >= p.K) return;
-    const float *src = p.X + (int64_t)row * p.ldx + k0;
-    if (p.x_vec && k0 + 16 <= p.K) {
+    const int r = min(row, p.M - 1);
+    const float *src = p.X + (int64_t)r * p.ldx;
+    if (AVEC) {
+        const bool ok = row < p.M && k0 < p.K;
+        const float *s = src + min(k0, p.K - 16);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const v4f v = *(const v4f *)(src + 4 * j);
-            x[4 * j] = v[0];
-            x[4 * j + 1] = v[1];
-            x[4 * j + 2] = v[2];
-            x[4 * j + 3] = v[3];
+            const v4f v = *(const v4f *)(s + 4 * j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * j + e] = ok ? v[e] : 0.0f;
         }
-        return;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float v = src[min(k0 + j, p.K - 1)];
+            x[j] = (row < p.M && k0 + j < p.K) ? v : 0.0f;
+        }
     }
-    for (int j = 0; j < 16; ++j)
-        if (k0 + j < p.K) x[j] = src[j];
+}
+
+// Epilogue operands of column n (loaded for every thread; columns past N
+// read column N-1 and are never stored).  Null operands read a valid array
+// and are replaced by 0.
+__device__ __forceinline__ ColOps load_colops_c(const Int8GemmParams &p, int n) {
+    const int c = min(n, p.N - 1);
+    const float bf = (p.bias_f32 ? p.bias_f32 : p.col_scale)[c];
+    const int32_t bi = (p.bias_i32 ? p.bias_i32 : p.colsum)[c];
+    ColOps o;
+    o.colsum = p.colsum[c];
+    o.cs = p.col_scale[c];
+    o.bias_f = p.bias_f32 ? bf : 0.0f;
+    o.bias_i = p.bias_i32 ? bi : 0;
+    return o;
 }
 
 // Codes of 16 activations for row scale s (same rule as k_quantize_rows).
@@ -240,148 +255,58 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// --------------------------------------------------------- decode GEMM ---
-// M <= 16*MT.  One workgroup per 16-column strip; its WAVES wavefronts split
-// the k tiles round-robin (wave w takes tiles w, w+WAVES, ...), TPW tiles per
-// round.  Each wave issues all TPW weight-tile loads (one 16-byte load per
-// lane per tile, a contiguous 1 KiB per tile) and the matching activation
-// loads before its first MFMA, so a whole round is in flight at once.  The
+// M <= 16*MT on quantised activations.  One workgroup per 16-column strip;
+// its WAVES wavefronts split the k tiles round-robin (wave w takes tiles w,
+// w+WAVES, ...), TPW tiles per round, and every load of a round (one 16-byte
+// weight load per lane per tile, a contiguous 1 KiB per tile, and the
+// matching activation loads) is issued before its first MFMA.  The
+// epilogue's column and row operands are fetched with the first round.  The
 // waves' 16x16 int32 tiles are summed in LDS in wave order and the epilogue
-// runs in the same workgroup: no cross-workgroup traffic, no atomics, no
-// fences, no workspace.
-template <int MT, int WAVES, int TPW, bool HAS_ZB, bool QUANT>
+// runs in the same workgroup: no cross-workgroup traffic, no workspace.
+template <int MT, int WAVES, int TPW, bool HAS_ZB, bool AVEC>
 __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
     constexpr int NE = MT * 256;  // elements of the (MT*16) x 16 output tile
     constexpr int NT = WAVES * 64;
+    constexpr int EPT = (NE + NT - 1) / NT;  // epilogue elements per thread
     constexpr int ROWS = MT * 16;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int strip = blockIdx.x;
     const int8_t *strip_codes = p.codes + (int64_t)strip * p.KT * kTileBytes + lane * 16;
 
-    __shared__ float s_amax[WAVES][ROWS];
-    __shared__ float s_scale[ROWS];
-    __shared__ ColOps s_col[16];
-    // Epilogue operands are fetched now so their latency overlaps the stream.
-    if (threadIdx.x < 16) {
-        const int n = strip * kTileN + threadIdx.x;
-        s_col[threadIdx.x] = n < p.N ? load_colops(p, n) : ColOps{0, 0.0f, 0.0f, 0};
-    } else if (!QUANT && threadIdx.x >= 64 && threadIdx.x < 64 + ROWS) {
-        const int m = threadIdx.x - 64;
-        s_scale[m] = (p.row_scale && m < p.M) ? p.row_scale[m] : 1.0f;
-    }
-    // Activations stay in registers between the two passes when TPW*MT is
-    // small and one round of the wavefronts covers all of K; otherwise the
-    // second pass reloads them (L1/L2 hits).
-    constexpr bool KEEP_T = QUANT && (TPW * MT <= 2);
-    const bool keep = KEEP_T && p.KT <= WAVES * TPW;
-    float xk[KEEP_T ? TPW : 1][KEEP_T ? MT : 1][16];
-
-    v4i acc[MT];
-    v4i accr[MT];
+    v4i acc[MT], accr[MT];
 #pragma unroll
     for (int r = 0; r < MT; ++r) {
         acc[r] = v4i{0, 0, 0, 0};
         accr[r] = v4i{0, 0, 0, 0};
     }
     const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-
-    v4i bf[TPW];
-    auto load_b = [&](int base) {
+    const ColOps col = load_colops_c(p, strip * kTileN + (threadIdx.x & 15));
+    float rs[EPT];
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int kt = base + i * WAVES;
-            bf[i] = kt < p.KT ? *(const v4i *)(strip_codes + (int64_t)kt * kTileBytes) : v4i{0, 0, 0, 0};
-        }
-    };
-
-    if (QUANT) {
-        // The first round's weight tiles are in flight while the row maxima
-        // are found: every workgroup covers all of K for its strip, so the
-        // maxima over its wavefronts are the full-row maxima.
-        load_b(wave);
-        float lmax[MT];
-#pragma unroll
-        for (int r = 0; r < MT; ++r) lmax[r] = 0.0f;
-        for (int base = wave; base < p.KT; base += WAVES * TPW) {
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int kt = base + i * WAVES;
-                if (kt < p.KT) {
-#pragma unroll
-                    for (int r = 0; r < MT; ++r) {
-                        float x[16];
-                        load_x16(p, r * 16 + (lane & 15), kt * kTileK + (lane >> 4) * 16, x);
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) lmax[r] = fmaxf(lmax[r], fabsf(x[j]));
-                        if (KEEP_T && keep) {
-#pragma unroll
-                            for (int j = 0; j < 16; ++j) xk[KEEP_T ? i : 0][KEEP_T ? r : 0][j] = x[j];
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < MT; ++r) {
-            lmax[r] = fmaxf(lmax[r], __shfl_xor(lmax[r], 16));
-            lmax[r] = fmaxf(lmax[r], __shfl_xor(lmax[r], 32));
-            if (lane < 16) s_amax[wave][r * 16 + lane] = lmax[r];
-        }
-        __syncthreads();
-        if (threadIdx.x < ROWS) {
-            float a = 0.0f;
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w) a = fmaxf(a, s_amax[w][threadIdx.x]);
-            s_scale[threadIdx.x] = (a == 0.0f) ? 0.0f : a / 127.0f;
-            if (p.rs_out && strip == 0 && (int)threadIdx.x < p.M) p.rs_out[threadIdx.x] = s_scale[threadIdx.x];
-        }
-        __syncthreads();
+    for (int i = 0; i < EPT; ++i) {
+        const int m = min((int)(threadIdx.x + i * NT) >> 4, p.M - 1);
+        const float v = (p.row_scale ? p.row_scale : p.col_scale)[m];
+        rs[i] = p.row_scale ? v : 1.0f;
     }
 
     for (int base = wave; base < p.KT; base += WAVES * TPW) {
-        if (!QUANT || base != wave) load_b(base);
-        v4i af[TPW][MT];
+        v4i bf[TPW], af[TPW][MT];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int kt = base + i * WAVES;
+            bf[i] = *(const v4i *)(strip_codes + (int64_t)min(kt, p.KT - 1) * kTileBytes);
 #pragma unroll
-            for (int r = 0; r < MT; ++r) {
-                const int row = r * 16 + (lane & 15);
-                const int k0 = kt * kTileK + (lane >> 4) * 16;
-                if (kt >= p.KT) {
-                    af[i][r] = v4i{0, 0, 0, 0};
-                } else if (QUANT) {
-                    float x[16];
-                    if (KEEP_T && keep) {
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) x[j] = xk[KEEP_T ? i : 0][KEEP_T ? r : 0][j];
-                    } else {
-                        load_x16(p, row, k0, x);
-                    }
-                    af[i][r] = quant16(x, s_scale[row]);
-                    if (p.xq_out && strip == 0 && row < p.M && k0 < p.K) {
-                        int8_t *dst = p.xq_out + (int64_t)row * p.ldq + k0;
-                        if (k0 + 16 <= p.K && (((uintptr_t)dst) & 15) == 0) {
-                            *(v4i *)dst = af[i][r];
-                        } else {
-                            for (int j = 0; j < 16 && k0 + j < p.K; ++j)
-                                dst[j] = (int8_t)((uint32_t)af[i][r][j >> 2] >> (8 * (j & 3)));
-                        }
-                    }
-                } else {
-                    af[i][r] = load_a16(p, row, k0);
-                }
-            }
+            for (int r = 0; r < MT; ++r)
+                af[i][r] = load_a16<AVEC>(p, r * 16 + (lane & 15), kt * kTileK + (lane >> 4) * 16);
         }
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
+        for (int i = 0; i < TPW; ++i)
 #pragma unroll
             for (int r = 0; r < MT; ++r) {
                 acc[r] = mfma_i8(af[i][r], bf[i], acc[r]);
                 if (HAS_ZB) accr[r] = mfma_i8(af[i][r], ones, accr[r]);
             }
-        }
     }
 
     __shared__ int32_t s_red[WAVES][ROWS][17];
@@ -405,14 +330,187 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
         }
         __syncthreads();
     }
-    for (int e = threadIdx.x; e < NE; e += NT) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + i * NT;
         const int m = e >> 4;
         const int n = strip * kTileN + (e & 15);
-        if (m < p.M && n < p.N) {
+        if (e < NE && m < p.M && n < p.N) {
             int32_t v = 0;
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) v += s_red[w][m][e & 15];
-            epilogue_store_c(p, m, n, (uint32_t)v, HAS_ZB ? s_rowsum[m] : 0, HAS_ZB, s_scale[m], s_col[e & 15]);
+            epilogue_store_c(p, m, n, (uint32_t)v, HAS_ZB ? s_rowsum[m] : 0, HAS_ZB, rs[i], col);
+        }
+    }
+}
+
+// x / s rounded to nearest, bit-identical to the IEEE quotient: y = 1/s is
+// correctly rounded (one IEEE division per lane), two residual corrections
+// with fma bring x*y to within one ulp and then, by Markstein's theorem
+// (a faithful quotient plus RN(residual) times a correctly rounded
+// reciprocal rounds to the correctly rounded quotient), to RN(x/s).  The
+// theorem needs no underflow or overflow: callers use it for normal s and
+// take the IEEE division otherwise.
+__device__ __forceinline__ float div_by(float x, float s, float y) {
+    const float q0 = x * y;
+    const float q1 = fmaf(fmaf(-q0, s, x), y, q0);
+    return fmaf(fmaf(-q1, s, x), y, q1);
+}
+
+// Fused dynamic quantisation for small M x K (the planner takes it when
+// M' * K <= 32768, M' = M rounded up to a power of two <= 16, and K <= 4096):
+// 16 wavefronts, TPW k tiles each
+// (wave w takes tiles w, w+16, ...).  Activations are held compactly: E = M
+// rounded up to a power of two values per lane (at most 32), 64/E lanes per
+// row, so every lane does real work (at M = 1 each lane holds one value per
+// tile).  All loads go out first.  Row maxima combine across the lanes of a
+// row (shuffles) and the waves (LDS, one barrier); each lane forms its row's
+// scale amax/127 and quantises its values with the k_quantize_rows rule;
+// per tile the codes go through a wave-private LDS area into MFMA A-operand
+// order (one 16-row tile per 16 rows); then the LDS sum over the waves and
+// the epilogue.  Every workgroup quantises all M x K activations again,
+// which is why the planner keeps M*K small here.
+template <int E, int TPW, bool AVEC>
+__global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p) {
+    constexpr int WAVES = 16;
+    constexpr int L = 64 / E;              // lanes per row
+    constexpr int MT = E > 16 ? 2 : 1;     // 16-row MFMA tiles
+    constexpr int ROWS = MT * 16;
+    constexpr int NE = ROWS * 16;          // outputs of the workgroup
+    static_assert(E == 1 || E == 2 || E == 4 || E == 8 || E == 16 || E == 32, "E is a power of two <= 32");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int strip = blockIdx.x;
+    const int m = lane / L;                    // row of this lane's values
+    const int kl = (lane % L) * E;             // their first k within a tile
+    const bool row_ok = m < p.M;
+
+    // loads: activations, weight tiles, the epilogue's column operands
+    float x[TPW][E];
+    v4i bf[TPW];
+    {
+        const float *src = p.X + (int64_t)min(m, p.M - 1) * p.ldx;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int k0 = (wave + t * WAVES) * kTileK + kl;
+            const bool ok = row_ok && k0 < p.K;
+            if (AVEC && E >= 4) {
+                const float *s = src + min(k0, p.K - E);
+#pragma unroll
+                for (int j = 0; j < E; j += 4) {
+                    const v4f v = *(const v4f *)(s + j);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[t][j + e] = ok ? v[e] : 0.0f;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < E; ++j) {
+                    const float v = src[min(k0 + j, p.K - 1)];
+                    x[t][j] = (ok && k0 + j < p.K) ? v : 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+            bf[t] = *(const v4i *)(p.codes + ((int64_t)strip * p.KT + min(wave + t * WAVES, p.KT - 1)) * kTileBytes +
+                                   lane * 16);
+    }
+    const ColOps col = load_colops_c(p, strip * kTileN + (threadIdx.x & 15));
+
+    __shared__ __attribute__((aligned(16))) float s_amax[ROWS][WAVES];  // [row][wave]
+    __shared__ float s_scale[ROWS];
+    __shared__ __attribute__((aligned(16))) int8_t s_q[WAVES][ROWS][64];  // [wave][row][k]
+    __shared__ int32_t s_red[WAVES][ROWS][17];
+
+    float a = 0.0f;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int j = 0; j < E; ++j) a = fmaxf(a, fabsf(x[t][j]));
+#pragma unroll
+    for (int o = 1; o < L; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+    if (lane % L == 0) s_amax[m][wave] = a;
+    __syncthreads();
+    a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; w += 4) {
+        const v4f v = *(const v4f *)(&s_amax[m][w]);
+        a = fmaxf(fmaxf(a, fmaxf(v[0], v[1])), fmaxf(v[2], v[3]));
+    }
+    const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
+    if (wave == 0 && lane % L == 0) {
+        s_scale[m] = s;
+        if (p.rs_out && strip == 0 && row_ok) p.rs_out[m] = s;
+    }
+    const float y = 1.0f / s;
+    const bool fast_s = s >= 0x1p-100f && s <= 0x1p100f;
+
+    v4i acc[MT];
+#pragma unroll
+    for (int r = 0; r < MT; ++r) acc[r] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        // codes: clamp(rne(x / s), -127, 127), 0 for an all-zero row
+        float qv[E];
+        bool fast = fast_s;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            qv[j] = div_by(x[t][j], s, y);
+            fast = fast && fabsf(qv[j]) <= 256.0f;
+        }
+        if (!fast) {
+#pragma unroll
+            for (int j = 0; j < E; ++j) qv[j] = x[t][j] / s;
+        }
+        uint32_t w[(E + 3) / 4];
+#pragma unroll
+        for (int i = 0; i < (E + 3) / 4; ++i) w[i] = 0u;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            float r = rintf(qv[j]);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            const uint32_t c = s > 0.0f ? (uint32_t)((int)r & 0xFF) : 0u;
+            w[j >> 2] |= c << (8 * (j & 3));
+        }
+        int8_t *qdst = &s_q[wave][m][kl];
+        if constexpr (E == 1) *(uint8_t *)qdst = (uint8_t)w[0];
+        else if constexpr (E == 2) *(uint16_t *)qdst = (uint16_t)w[0];
+        else if constexpr (E == 4) *(uint32_t *)qdst = w[0];
+        else if constexpr (E == 8) *(uint64_t *)qdst = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+        else {
+#pragma unroll
+            for (int i = 0; i < E / 16; ++i)
+                *(v4i *)(qdst + 16 * i) = v4i{(int)w[4 * i], (int)w[4 * i + 1], (int)w[4 * i + 2], (int)w[4 * i + 3]};
+        }
+        const int k0 = (wave + t * WAVES) * kTileK + kl;
+        if (p.xq_out && strip == 0 && row_ok && k0 < p.K) {
+            int8_t *dst = p.xq_out + (int64_t)m * p.ldq + k0;
+            for (int j = 0; j < E && k0 + j < p.K; ++j) dst[j] = (int8_t)(w[j >> 2] >> (8 * (j & 3)));
+        }
+        __builtin_amdgcn_wave_barrier();
+        // A operands: lane (row lane % 16, k-group lane / 16); rows >= M are zero
+#pragma unroll
+        for (int r = 0; r < MT; ++r) {
+            const int ar = r * 16 + (lane & 15);
+            v4i af = *(const v4i *)(&s_q[wave][ar][(lane >> 4) * 16]);
+            if (ar >= p.M) af = v4i{0, 0, 0, 0};
+            acc[r] = mfma_i8(af, bf[t], acc[r]);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_red[wave][r * 16 + 4 * (lane >> 4) + i][lane & 15] = acc[r][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < NE; e += WAVES * 64) {
+        const int mo = e >> 4;
+        const int n = strip * kTileN + (e & 15);
+        if (mo < p.M && n < p.N) {
+            int32_t v = 0;
+#pragma unroll
+            for (int ww = 0; ww < WAVES; ++ww) v += s_red[ww][mo][e & 15];
+            epilogue_store_c(p, mo, n, (uint32_t)v, 0, false, s_scale[mo], col);
         }
     }
 }
@@ -500,7 +598,7 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
 #pragma unroll
         for (int i = 0; i < ACH; ++i) {
             const int c = tid + 256 * i;  // (row, k-chunk) = (c >> 2, c & 3)
-            ra[sl][i] = load_a16(p, m0 + (c >> 2), kt * kTileK + (c & 3) * 16);
+            ra[sl][i] = load_a16<false>(p, m0 + (c >> 2), kt * kTileK + (c & 3) * 16);
         }
 #pragma unroll
         for (int i = 0; i < BCH; ++i) {
@@ -602,35 +700,26 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         }
 }
 
-template <int MT, int WAVES, int TPW, bool QUANT>
+template <int MT, int WAVES, int TPW, bool AVEC>
 hipError_t launch_decode(const Int8GemmParams &p, hipStream_t s) {
     if (p.zBs != 0)
-        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, true, QUANT>), dim3((unsigned)p.NS), dim3(WAVES * 64), 0,
+        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, true, AVEC>), dim3((unsigned)p.NS), dim3(WAVES * 64), 0,
                            s, p);
     else
-        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, false, QUANT>), dim3((unsigned)p.NS), dim3(WAVES * 64),
+        hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, false, AVEC>), dim3((unsigned)p.NS), dim3(WAVES * 64),
                            0, s, p);
     return hipGetLastError();
 }
 
-template <int MT, int WAVES, bool QUANT>
-hipError_t launch_decode_tpw(const Int8GemmParams &p, int tpw, hipStream_t s) {
-    switch (tpw) {
-        case 1: return launch_decode<MT, WAVES, 1, QUANT>(p, s);
-        case 2: return launch_decode<MT, WAVES, 2, QUANT>(p, s);
-        case 4: return launch_decode<MT, WAVES, 4, QUANT>(p, s);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <int MT, bool QUANT>
-hipError_t launch_decode_waves(const Int8GemmParams &p, int waves, int tpw, hipStream_t s) {
-    switch (waves) {
-        case 4: return launch_decode_tpw<MT, 4, QUANT>(p, tpw, s);
-        case 8: return launch_decode_tpw<MT, 8, QUANT>(p, tpw, s);
-        case 16: return launch_decode_tpw<MT, 16, QUANT>(p, tpw, s);
-        default: return hipErrorInvalidValue;
-    }
+// (waves, tiles per wave) pairs the planner uses: 4x1, 8x1, 16x1, 16x2, 16x4.
+template <int MT, bool AVEC>
+hipError_t launch_decode_shape(const Int8GemmParams &p, int waves, int tpw, hipStream_t s) {
+    if (waves == 4 && tpw == 1) return launch_decode<MT, 4, 1, AVEC>(p, s);
+    if (waves == 8 && tpw == 1) return launch_decode<MT, 8, 1, AVEC>(p, s);
+    if (waves == 16 && tpw == 1) return launch_decode<MT, 16, 1, AVEC>(p, s);
+    if (waves == 16 && tpw == 2) return launch_decode<MT, 16, 2, AVEC>(p, s);
+    if (waves == 16 && tpw == 4) return launch_decode<MT, 16, 4, AVEC>(p, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -668,8 +757,12 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
                             const char **variant) {
     if (plan.variant == 0) {
         *variant = plan.mt == 1 ? "int8_decode_m16" : "int8_decode_m32";
-        if (plan.mt == 1) return launch_decode_waves<1, false>(p, plan.waves, plan.tpw, s);
-        return launch_decode_waves<2, false>(p, plan.waves, plan.tpw, s);
+        const bool avec = p.a_vec && (p.K % 16) == 0;
+        if (plan.mt == 1)
+            return avec ? launch_decode_shape<1, true>(p, plan.waves, plan.tpw, s)
+                        : launch_decode_shape<1, false>(p, plan.waves, plan.tpw, s);
+        return avec ? launch_decode_shape<2, true>(p, plan.waves, plan.tpw, s)
+                    : launch_decode_shape<2, false>(p, plan.waves, plan.tpw, s);
     }
     *variant = "int8_prefill_256x128";
     dim3 grid((unsigned)(ceil_div(p.NS, PF_BN / kTileN) * ceil_div(p.M, PF_BM)));
@@ -688,12 +781,40 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
     return hipGetLastError();
 }
 
+template <int E, int TPW>
+hipError_t launch_dyn(const Int8GemmParams &p, bool avec, hipStream_t s) {
+    const dim3 g((unsigned)p.NS), b(1024);
+    if (E >= 4 && avec)
+        hipLaunchKernelGGL((k_int8_decode_q<E, TPW, true>), g, b, 0, s, p);
+    else
+        hipLaunchKernelGGL((k_int8_decode_q<E, TPW, false>), g, b, 0, s, p);
+    return hipGetLastError();
+}
+
+// E * K <= 32768 (the planner's bound) keeps E * TPW <= 32.
+template <int E>
+hipError_t launch_dyn_tpw(const Int8GemmParams &p, bool avec, hipStream_t s) {
+    if (p.KT <= 16) return launch_dyn<E, 1>(p, avec, s);
+    if constexpr (E <= 16) {
+        if (p.KT <= 32) return launch_dyn<E, 2>(p, avec, s);
+    }
+    if constexpr (E <= 8) {
+        if (p.KT <= 64) return launch_dyn<E, 4>(p, avec, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                                     const char **variant) {
-    if (plan.variant != 0) return hipErrorInvalidValue;
-    *variant = plan.mt == 1 ? "int8_dynamic_m16" : "int8_dynamic_m32";
-    if (plan.mt == 1) return launch_decode_waves<1, true>(p, plan.waves, plan.tpw, s);
-    return launch_decode_waves<2, true>(p, plan.waves, plan.tpw, s);
+    if (plan.variant != 0 || p.M > 16 || p.KT > 64 || p.zBs != 0) return hipErrorInvalidValue;
+    *variant = "int8_dynamic_m16";
+    const bool v = p.x_vec && (p.K % 16) == 0;
+    // E: values per lane, M rounded up to a power of two
+    if (p.M <= 1) return launch_dyn_tpw<1>(p, v, s);
+    if (p.M <= 2) return launch_dyn_tpw<2>(p, v, s);
+    if (p.M <= 4) return launch_dyn_tpw<4>(p, v, s);
+    if (p.M <= 8) return launch_dyn_tpw<8>(p, v, s);
+    return launch_dyn_tpw<16>(p, v, s);
 }
 
 }  // namespace qmm

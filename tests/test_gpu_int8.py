@@ -278,7 +278,8 @@ def test_workspace_shared_across_shapes(q, orc):
 
 @pytest.mark.parametrize("M,K,N", [(1, 1024, 2048), (16, 1024, 1024), (32, 3072, 1024), (16, 2048, 1024),
                                    (16, 3072, 1024), (1, 3072, 64), (3, 100, 37), (17, 1056, 17), (33, 320, 48),
-                                   (80, 256, 130), (16, 64, 16)])
+                                   (80, 256, 130), (16, 64, 16), (32, 1024, 64), (20, 512, 40), (5, 4096, 48),
+                                   (2, 2048, 33), (1, 4000, 20), (9, 3000, 16)])
 def test_dynamic_matches_two_step_and_oracle(q, orc, M, K, N):
     """int8_gemm_dynamic == quantize_rows_int8 + int8_gemm bit for bit (fp32
     output, quantised rows, row scales), and the oracle's int32 product."""
@@ -298,7 +299,8 @@ def test_dynamic_matches_two_step_and_oracle(q, orc, M, K, N):
     xq = torch.full((M, K), 99, dtype=torch.int8, device=dev)
     rs = torch.full((M,), -1.0, dtype=torch.float32, device=dev)
     q.int8_gemm_dynamic(Xd, p, out_f32=y, out_i32=y32, xq_out=xq, rs_out=rs)
-    if M <= 16 and K <= 1024:
+    mp = 1 << max(0, (M - 1).bit_length())
+    if mp <= 16 and K <= 4096 and mp * K <= 32768:
         assert q.last_variant() == "int8_dynamic_m16"
     elif M <= 16:
         assert q.last_variant() == "int8_decode_m16"
@@ -312,6 +314,49 @@ def test_dynamic_matches_two_step_and_oracle(q, orc, M, K, N):
     Y64 = orc.int8_gemm_i64(Qa, 0, Qb, 0)
     assert np.array_equal(to_np(y32), Y64.astype(np.int32))
     assert max_rel_err(to_np(y), orc.epilogue_f64(Y64, sa, sb)) <= F32_TOL
+
+
+def _near_tie_rows(M, K, seed):
+    """Activation rows whose quotients x/s sit within a few ulps of a
+    half-integer (the rounding decisions of rne(x/s)), plus rows with scales
+    near the ends of the fp32 range."""
+    g = np.random.default_rng(seed)
+    X = np.zeros((M, K), dtype=np.float32)
+    for m in range(M):
+        amax = np.float32([1.0, 3.7e-3, 123.456, 2.5e-38, 1.5e38, 7.0][m % 6] * g.uniform(0.5, 2.0))
+        s = np.float32(amax / np.float32(127.0))
+        j = g.integers(-127, 127, K).astype(np.float32) + np.float32(0.5)
+        x = (j * s).astype(np.float32)
+        steps = g.integers(-3, 4, K)
+        for k in range(K):
+            for _ in range(abs(int(steps[k]))):
+                x[k] = np.nextafter(x[k], np.float32(np.inf) if steps[k] > 0 else np.float32(-np.inf))
+        x = np.clip(x, -amax, amax)
+        x[g.integers(0, K)] = amax if m % 2 == 0 else -amax
+        X[m] = x
+    return X
+
+
+@pytest.mark.parametrize("M,K", [(1, 1024), (2, 1024), (3, 960), (4, 1024), (7, 96), (8, 1024), (16, 1024)])
+def test_dynamic_rounding_near_ties(q, orc, M, K):
+    """The fused quantiser's codes equal the oracle's rne(x/s) (IEEE fp32
+    division) bit for bit on quotients within ulps of a rounding boundary and
+    on scales near both ends of the fp32 range."""
+    import torch
+    X = _near_tie_rows(M, K, seed=M * 31 + K)
+    W = wl.normal_f32(np.random.default_rng(5), (K, 32), 0.02)
+    p = q.pack_b_int8(to_dev(W))
+    y = torch.empty((M, 32), dtype=torch.float32, device=torch_dev())
+    xq = torch.full((M, K), 99, dtype=torch.int8, device=torch_dev())
+    rs = torch.full((M,), -1.0, dtype=torch.float32, device=torch_dev())
+    q.int8_gemm_dynamic(to_dev(X), p, out_f32=y, xq_out=xq, rs_out=rs)
+    assert q.last_variant() == "int8_dynamic_m16"
+    Qa, sa = orc.quantize_rows_int8(X)
+    assert np.array_equal(to_np(rs).view(np.uint32), sa.view(np.uint32))
+    got = to_np(xq)
+    assert np.array_equal(got, Qa), np.argwhere(got != Qa)[:5]
+    Xq2, _ = q.quantize_rows_int8(to_dev(X))
+    assert np.array_equal(to_np(Xq2), Qa)
 
 
 def test_dynamic_without_side_outputs(q, orc):
