@@ -6,7 +6,7 @@ Workload (one "step"): the seven Qwen3-0.6B projections of all 28 layers
 timed region: ~420 MiB of int8 codes, more than the 256 MiB Infinity Cache)
 run as decode at M = 1, 16 and 32 rows of fp32 N(0, 1) activations.  Every
 call is int8_gemm_dynamic: per-row amax/127 quantisation of the activations
-(inside the int8 product kernel when M' * K <= 32768 with M' = M rounded up to
+(inside the int8 product kernel when M' * K <= 16384 with M' = M rounded up to
 a power of two <= 16, a separate kernel otherwise) and the int8 product with
 the fp32 epilogue (row scale x column scale).  Each M's 196 calls are
 captured in one HIP graph; a step replays the three graphs.
@@ -77,7 +77,7 @@ def fused_quant(M, K):
     e = 1
     while e < M:
         e <<= 1
-    return e <= 16 and K <= 4096 and e * K <= 32768
+    return e <= 16 and K <= 4096 and e * K <= 16384
 
 
 def call_bytes(M, K, N):

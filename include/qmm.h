@@ -173,7 +173,7 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
                      void *stream);
 
 /* Workspace bytes int8_gemm_dynamic needs (0 when the quantisation is fused:
- * M <= 16, K <= 4096 and M' * K <= 32768, M' = M rounded up to a power of 2). */
+ * M <= 16, K <= 4096 and M' * K <= 16384, M' = M rounded up to a power of 2). */
 size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 /*
@@ -183,7 +183,7 @@ size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * weight packed by pack_b_int8 (zA = zB = 0); the epilogue uses the computed
  * row scales (ep->row_scale must be NULL).  Results are bit-identical to
  * quantize_rows_int8 followed by int8_gemm.  For M <= 16, K <= 4096 and
- * M' * K <= 32768 (M' = M rounded up to a power of 2) the quantisation runs
+ * M' * K <= 16384 (M' = M rounded up to a power of 2) the quantisation runs
  * inside the product kernel (one launch); otherwise the two kernels run in
  * turn.  Xq (M x K int8, ldq >= K) and row_scale ([M] fp32)
  * optionally receive the quantised rows and their scales; pass NULL to skip

@@ -246,7 +246,7 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
 static bool dynamic_fused(int64_t M, int64_t K) {
     int64_t e = 1;
     while (e < M) e <<= 1;
-    return e <= 16 && K <= 4096 && e * K <= 32768;
+    return e <= 16 && K <= 4096 && e * K <= 16384;
 }
 
 size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N) {

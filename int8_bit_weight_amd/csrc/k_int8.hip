@@ -105,24 +105,82 @@ __global__ __launch_bounds__(256) void k_pack_b(const void *__restrict__ Bsrc, i
     }
 }
 
+// x / s rounded to nearest, bit-identical to the IEEE quotient: y = 1/s is
+// correctly rounded (one IEEE division per lane), two residual corrections
+// with fma bring x*y to within one ulp and then, by Markstein's theorem
+// (a faithful quotient plus RN(residual) times a correctly rounded
+// reciprocal rounds to the correctly rounded quotient), to RN(x/s).  The
+// theorem needs no underflow or overflow: callers use it for normal s and
+// take the IEEE division otherwise.
+__device__ __forceinline__ float div_by(float x, float s, float y) {
+    const float q0 = x * y;
+    const float q1 = fmaf(fmaf(-q0, s, x), y, q0);
+    return fmaf(fmaf(-q1, s, x), y, q1);
+}
+
+// Codes of 4 values for scale s > 0 with y = 1/s (k_quantize_rows rule:
+// clamp(rne(x / s), -127, 127)), packed little-endian; `fast` selects the
+// division above, else the IEEE division.
+__device__ __forceinline__ uint32_t quant4(const float (&x)[4], float s, float y, bool fast) {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float q = div_by(x[j], s, y);
+        if (!fast || !(fabsf(q) <= 256.0f)) q = x[j] / s;
+        float r = rintf(q);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        w |= (uint32_t)((int)r & 0xFF) << (8 * j);
+    }
+    return w;
+}
+
 // ------------------------------------------------------- row quantiser ---
-// One workgroup (256 threads) per row.
+// One workgroup (256 threads) per row.  VEC (X and Xq rows 16- and 4-byte
+// aligned, K a multiple of 4, K <= 4096): every thread loads its up to 16
+// values with 16-byte loads at once, keeps them in registers through the
+// row maximum and writes 4 codes per 4-byte store.  Otherwise two strided
+// passes over the row.
+template <bool VEC>
 __global__ __launch_bounds__(256) void k_quantize_rows(const float *__restrict__ X, int64_t ldx,
                                                        int K, int8_t *__restrict__ Xq, int64_t ldq,
                                                        float *__restrict__ row_scale) {
     const int64_t m = blockIdx.x;
     const int t = threadIdx.x;
     const float *x = X + m * ldx;
+    int8_t *q = Xq + m * ldq;
     __shared__ float s_red[4];
     float amax = 0.0f;
-    for (int k = t; k < K; k += 256) amax = fmaxf(amax, fabsf(x[k]));
+    float v[4][4];
+    if (VEC) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = (t + 256 * i) * 4;
+            const v4f l = *(const v4f *)(x + min(k, K - 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[i][e] = k < K ? l[e] : 0.0f;
+                amax = fmaxf(amax, fabsf(v[i][e]));
+            }
+        }
+    } else {
+        for (int k = t; k < K; k += 256) amax = fmaxf(amax, fabsf(x[k]));
+    }
     amax = wave_max_f(amax);
     if ((t & 63) == 0) s_red[t >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
     const float s = (amax == 0.0f) ? 0.0f : amax / 127.0f;
-    int8_t *q = Xq + m * ldq;
-    for (int k = t; k < K; k += 256) q[k] = (s > 0.0f) ? (int8_t)quant_code(x[k], s) : (int8_t)0;
+    const float y = 1.0f / s;
+    const bool fast = s >= 0x1p-100f && s <= 0x1p100f;
+    if (VEC) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = (t + 256 * i) * 4;
+            if (k < K) *(uint32_t *)(q + k) = s > 0.0f ? quant4(v[i], s, y, fast) : 0u;
+        }
+    } else {
+        for (int k = t; k < K; k += 256) q[k] = (s > 0.0f) ? (int8_t)quant_code(x[k], s) : (int8_t)0;
+    }
     if (t == 0) row_scale[m] = s;
 }
 
@@ -344,21 +402,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
     }
 }
 
-// x / s rounded to nearest, bit-identical to the IEEE quotient: y = 1/s is
-// correctly rounded (one IEEE division per lane), two residual corrections
-// with fma bring x*y to within one ulp and then, by Markstein's theorem
-// (a faithful quotient plus RN(residual) times a correctly rounded
-// reciprocal rounds to the correctly rounded quotient), to RN(x/s).  The
-// theorem needs no underflow or overflow: callers use it for normal s and
-// take the IEEE division otherwise.
-__device__ __forceinline__ float div_by(float x, float s, float y) {
-    const float q0 = x * y;
-    const float q1 = fmaf(fmaf(-q0, s, x), y, q0);
-    return fmaf(fmaf(-q1, s, x), y, q1);
-}
-
 // Fused dynamic quantisation for small M x K (the planner takes it when
-// M' * K <= 32768, M' = M rounded up to a power of two <= 16, and K <= 4096):
+// M' * K <= 16384, M' = M rounded up to a power of two <= 16, and K <= 4096):
 // 16 wavefronts, TPW k tiles each
 // (wave w takes tiles w, w+16, ...).  Activations are held compactly: E = M
 // rounded up to a power of two values per lane (at most 32), 64/E lanes per
@@ -749,7 +794,14 @@ hipError_t launch_pack_b_raw(const void *B, int u8, int64_t ldb, const PackedBLa
 
 hipError_t launch_quantize_rows(const float *X, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
                                 int64_t ldq, float *row_scale, hipStream_t s) {
-    hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)M), dim3(256), 0, s, X, ldx, (int)K, Xq, ldq, row_scale);
+    const bool vec = K <= 4096 && K % 4 == 0 && ldx % 4 == 0 && ldq % 4 == 0 && ((uintptr_t)X % 16) == 0 &&
+                     ((uintptr_t)Xq % 4) == 0;
+    if (vec)
+        hipLaunchKernelGGL(k_quantize_rows<true>, dim3((unsigned)M), dim3(256), 0, s, X, ldx, (int)K, Xq, ldq,
+                           row_scale);
+    else
+        hipLaunchKernelGGL(k_quantize_rows<false>, dim3((unsigned)M), dim3(256), 0, s, X, ldx, (int)K, Xq, ldq,
+                           row_scale);
     return hipGetLastError();
 }
 
@@ -791,14 +843,14 @@ hipError_t launch_dyn(const Int8GemmParams &p, bool avec, hipStream_t s) {
     return hipGetLastError();
 }
 
-// E * K <= 32768 (the planner's bound) keeps E * TPW <= 32.
+// E * K <= 16384 (the planner's bound) keeps E * TPW <= 16.
 template <int E>
 hipError_t launch_dyn_tpw(const Int8GemmParams &p, bool avec, hipStream_t s) {
     if (p.KT <= 16) return launch_dyn<E, 1>(p, avec, s);
-    if constexpr (E <= 16) {
+    if constexpr (E <= 8) {
         if (p.KT <= 32) return launch_dyn<E, 2>(p, avec, s);
     }
-    if constexpr (E <= 8) {
+    if constexpr (E <= 4) {
         if (p.KT <= 64) return launch_dyn<E, 4>(p, avec, s);
     }
     return hipErrorInvalidValue;
