@@ -11,6 +11,7 @@
 // no VitisAI", sections "The three layers of the pack", "Why it folds
 // without a new kernel" and "What works today, and what does not".
 #include <type_traits>
+#include <utility>
 
 #include "qmm_internal.h"
 
@@ -198,14 +199,6 @@ struct ColOps {
     int32_t bias_i;
 };
 
-__device__ __forceinline__ ColOps load_colops(const Int8GemmParams &p, int n) {
-    ColOps c;
-    c.colsum = p.zAs != 0 ? p.colsum[n] : 0;
-    c.cs = p.col_scale[n];
-    c.bias_f = p.bias_f32 ? p.bias_f32[n] : 0.0f;
-    c.bias_i = p.bias_i32 ? p.bias_i32[n] : 0;
-    return c;
-}
 
 __device__ __forceinline__ void epilogue_store_c(const Int8GemmParams &p, int m, int n, uint32_t S,
                                                  int32_t rowsum, bool has_zb, float rs, const ColOps &c) {
@@ -565,33 +558,53 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p) {
 // grid each owning 128 x 64 (8 x 4 MFMA tiles of 16 x 16, 128 int32
 // accumulators per lane, held in AGPRs).  Both operands sit in LDS in MFMA
 // fragment order (1 KiB per 16 rows or 16 columns x 64 k, 16 bytes per lane),
-// so every fragment read is one linear ds_read_b128 per lane; the packed
-// weight tiles are already in that order and are copied as is.  Each
-// wavefront reads 12 fragments per 32 MFMAs.
+// so every fragment read is one ds_read_b128 per lane; the packed weight
+// tiles are already in that order and are copied as is.  In an A fragment
+// the 16-byte piece of (row r, k-chunk g) sits at slot 16 g + (r ^ f(g)),
+// f = {0, 6, 10, 12}: the staging stores (four consecutive lanes hold one
+// row's four chunks, so the global loads stay 64 bytes contiguous) and the
+// MFMA reads (lane L: row L % 16, chunk L / 16) both touch distinct 16-byte
+// bank groups in every 8 and every 16 consecutive lanes.  Each wavefront
+// reads 12 fragments per 32 MFMAs.
 // Global loads run PF_DEPTH k steps ahead through a ring of register stages
 // (compile-time slots: the k loop is unrolled by PF_DEPTH), so the L2/MALL
 // latency of a stage is covered by PF_DEPTH - 1 steps of MFMAs; LDS holds two
 // stages.  Row and column epilogue operands are staged in LDS once.
 constexpr int PF_BM = 256, PF_BN = 128, PF_DEPTH = 4;
 
+__device__ __forceinline__ int pf_slot(int r, int g) {
+    return g * 16 + (r ^ ((0xCA60 >> (4 * g)) & 15));
+}
+
 template <int N>
 using ic = std::integral_constant<int, N>;
+
+// f(ic<0>{}), f(ic<1>{}), ..., f(ic<N-1>{})
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(ic<I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // FAST (A 16-byte aligned, lda % 16 == 0, K % 64 == 0): every global load is
 // unconditional, so loads issued for later stages stay in flight (a load
 // inside a branch makes the compiler wait for it at the branch's end).  Rows
 // past M read row M - 1 and strips past the last read the last strip; those
-// products land in outputs that are never stored.  uint8 A is shifted when
-// the stage is written to LDS.
-template <bool HAS_ZB, bool FAST>
+// products land in outputs that are never stored.  FLIP (uint8 A on the FAST
+// path): A is shifted when the stage is written to LDS.
+template <bool HAS_ZB, bool FAST, bool FLIP>
 __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     constexpr int AF = PF_BM / 16;      // A fragments per stage
     constexpr int BF = PF_BN / 16;      // B fragments per stage
     constexpr int ACH = AF * 64 / 256;  // 16-byte A chunks per thread per stage (4)
     constexpr int BCH = BF * 64 / 256;  // 16-byte B chunks per thread per stage (2)
-    __shared__ __attribute__((aligned(16))) int8_t sA[2][AF * 1024];
-    __shared__ __attribute__((aligned(16))) int8_t sB[2][BF * 1024];
-    __shared__ float s_rs[PF_BM];
+    constexpr int SA = AF * 1024, SB = BF * 1024;  // bytes of one stage
+    __shared__ __attribute__((aligned(16))) int8_t sA[3][SA];
+    __shared__ __attribute__((aligned(16))) int8_t sB[3][SB];
+    __shared__ __attribute__((aligned(16))) float s_rs[PF_BM];
     __shared__ ColOps s_col[PF_BN];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -603,15 +616,6 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     const int m0 = bm * PF_BM;
     const int strip0 = bn * BF;
     const int KT = p.KT;
-
-    for (int r = tid; r < PF_BM; r += 256) {
-        const int m = m0 + r;
-        s_rs[r] = (m < p.M && p.row_scale) ? p.row_scale[m] : 1.0f;
-    }
-    if (tid < PF_BN) {
-        const int n = strip0 * kTileN + tid;
-        s_col[tid] = n < p.N ? load_colops(p, n) : ColOps{0, 0.0f, 0.0f, 0};
-    }
 
     // per-thread source pointers of the FAST path (k advances by 64 bytes a step)
     const int8_t *a_src[ACH];
@@ -628,9 +632,15 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         const int strip = min(strip0 + (c >> 6), p.NS - 1);
         b_src[i] = p.codes + (int64_t)strip * KT * kTileBytes + (c & 63) * 16;
     }
-    const uint32_t flip = p.a_u8 ? 0x80808080u : 0u;
-
     v4i ra[PF_DEPTH][ACH], rb[PF_DEPTH][BCH];
+    int a_dst[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int c = tid + 256 * i;
+        const int r = c >> 2;
+        a_dst[i] = (r >> 4) * 1024 + pf_slot(r & 15, c & 3) * 16;
+    }
+    const int a_rd = pf_slot(lane & 15, lane >> 4) * 16;
     auto gload = [&](auto slot, int kt) {
         constexpr int sl = decltype(slot)::value;
         if (FAST) {
@@ -649,25 +659,23 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         for (int i = 0; i < BCH; ++i) {
             const int c = tid + 256 * i;  // (strip, lane chunk) = (c >> 6, c & 63)
             const int strip = strip0 + (c >> 6);
-            rb[sl][i] = strip < p.NS
-                            ? *(const v4i *)(p.codes + ((int64_t)strip * KT + kt) * kTileBytes + (c & 63) * 16)
-                            : v4i{0, 0, 0, 0};
+            const v4i v = *(const v4i *)(p.codes + ((int64_t)min(strip, p.NS - 1) * KT + kt) * kTileBytes +
+                                         (c & 63) * 16);
+            rb[sl][i] = strip < p.NS ? v : v4i{0, 0, 0, 0};
         }
     };
     auto sstore = [&](auto slot, int buf) {
         constexpr int sl = decltype(slot)::value;
 #pragma unroll
         for (int i = 0; i < ACH; ++i) {
-            const int c = tid + 256 * i;
-            const int r = c >> 2;
             v4i v = ra[sl][i];
-            if (FAST) {
-                v[0] ^= flip;
-                v[1] ^= flip;
-                v[2] ^= flip;
-                v[3] ^= flip;
+            if (FLIP) {
+                v[0] ^= 0x80808080;
+                v[1] ^= 0x80808080;
+                v[2] ^= 0x80808080;
+                v[3] ^= 0x80808080;
             }
-            *(v4i *)(&sA[buf][(r >> 4) * 1024 + ((c & 3) * 16 + (r & 15)) * 16]) = v;
+            *(v4i *)(&sA[buf][a_dst[i]]) = v;
         }
 #pragma unroll
         for (int i = 0; i < BCH; ++i) {
@@ -686,48 +694,89 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     }
     const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
-    auto compute = [&](int buf) {
-        v4i b[4];
+    // MFMA fragments, double-buffered in registers: a step's fragments are
+    // read from LDS during the previous step's MFMAs.
+    v4i fa[2][8], fb[2][4];
+    auto lds_frags = [&](auto F, int buf) {
+        constexpr int f = decltype(F)::value;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = *(const v4i *)(&sB[buf][(wn * 4 + j) * 1024 + lane * 16]);
+        for (int j = 0; j < 4; ++j) fb[f][j] = *(const v4i *)(&sB[buf][(wn * 4 + j) * 1024 + lane * 16]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fa[f][i] = *(const v4i *)(&sA[buf][(wm * 8 + i) * 1024 + a_rd]);
+    };
+    auto mfmas = [&](auto F) {
+        constexpr int f = decltype(F)::value;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const v4i a = *(const v4i *)(&sA[buf][(wm * 8 + i) * 1024 + lane * 16]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_i8(a, b[j], acc[i][j]);
-            if (HAS_ZB) accr[i] = mfma_i8(a, ones, accr[i]);
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_i8(fa[f][i], fb[f][j], acc[i][j]);
+            if (HAS_ZB) accr[i] = mfma_i8(fa[f][i], ones, accr[i]);
         }
     };
 
-    // stage s lives in register slot s % PF_DEPTH and LDS buffer s % 2
-    gload(ic<0>{}, 0);
-    gload(ic<1>{}, min(1, KT - 1));
-    gload(ic<2>{}, min(2, KT - 1));
-    gload(ic<3>{}, min(3, KT - 1));
+    // Stage s: register slot s % PF_DEPTH, LDS buffer s % 3, fragment set
+    // s % 2.  Step k: read step k+1's fragments (LDS buffer written in step
+    // k-1, published by its barrier), MFMAs of step k, store stage k+2 (its
+    // buffer was last read for step k-1, whose reads completed before the
+    // MFMAs of step k-1), load stage k+PF_DEPTH, barrier.
+    static_for<PF_DEPTH>([&](auto S) { gload(S, min(decltype(S)::value, KT - 1)); });
     sstore(ic<0>{}, 0);
+    sstore(ic<1 % PF_DEPTH>{}, 1);
     __syncthreads();
-    // Steady state: every step unconditionally stores the next stage and
-    // loads the stage PF_DEPTH ahead (clamped to the last k tile), so no load
-    // sits inside a branch; a store past the end only fills an LDS buffer
-    // that is never read again.
+    lds_frags(ic<0>{}, 0);
     auto step = [&](auto J, int kt) {
         constexpr int j = decltype(J)::value;
-        compute(kt & 1);
-        sstore(ic<(j + 1) % PF_DEPTH>{}, (kt + 1) & 1);
+        lds_frags(ic<(j + 1) & 1>{}, (kt + 1) % 3);
+        mfmas(ic<j & 1>{});
+        sstore(ic<(j + 2) % PF_DEPTH>{}, (kt + 2) % 3);
         gload(ic<j>{}, min(kt + PF_DEPTH, KT - 1));
         __syncthreads();
     };
-    const int KT4 = KT - KT % PF_DEPTH;
-    for (int base = 0; base < KT4; base += PF_DEPTH) {
-        step(ic<0>{}, base);
-        step(ic<1>{}, base + 1);
-        step(ic<2>{}, base + 2);
-        step(ic<3>{}, base + 3);
-    }
-    if (KT4 < KT) step(ic<0>{}, KT4);
-    if (KT4 + 1 < KT) step(ic<1>{}, KT4 + 1);
-    if (KT4 + 2 < KT) step(ic<2>{}, KT4 + 2);
+    static_assert(PF_DEPTH % 2 == 0, "fragment sets alternate with the unrolled steps");
+    const int KTD = KT - KT % PF_DEPTH;
+    for (int base = 0; base < KTD; base += PF_DEPTH)
+        static_for<PF_DEPTH>([&](auto J) { step(J, base + decltype(J)::value); });
+    static_for<PF_DEPTH - 1>([&](auto J) {
+        if (KTD + decltype(J)::value < KT) step(J, KTD + decltype(J)::value);
+    });
 
+    // ---- epilogue.  Row scales and column operands are staged in LDS (the
+    // A/B buffers are no longer needed); the common case (fp32 output, no
+    // zero points, a whole tile inside M x N) runs without per-element
+    // branches.
+    for (int r = tid; r < PF_BM; r += 256) {
+        const int m = min(m0 + r, p.M - 1);
+        const float v = (p.row_scale ? p.row_scale : p.col_scale)[m];
+        s_rs[r] = p.row_scale ? v : 1.0f;
+    }
+    if (tid < PF_BN) s_col[tid] = load_colops_c(p, strip0 * kTileN + tid);
+    __syncthreads();
+    const bool whole = m0 + PF_BM <= p.M && (strip0 + BF) * kTileN <= p.N;
+    if (!HAS_ZB && p.outputs == QMM_OUT_F32 && p.zAs == 0 && whole) {
+        float cm[4], cb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const ColOps c = s_col[(wn * 4 + j) * 16 + (lane & 15)];
+            cm[j] = c.cs;
+            cb[j] = c.bias_f;
+        }
+        float *ybase = p.y_f32 + (int64_t)(m0 + wm * 128 + 4 * (lane >> 4)) * p.ld_f32 + strip0 * kTileN +
+                       wn * 64 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const v4f rs = *(const v4f *)(&s_rs[wm * 128 + i * 16 + 4 * (lane >> 4)]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float *yrow = ybase + (int64_t)(i * 16 + v) * p.ld_f32;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float mult = (rs[v] * cm[j]) * p.scale;
+                    yrow[j * 16] = fmaf((float)acc[i][j][v], mult, cb[j]);
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -819,16 +868,21 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
     *variant = "int8_prefill_256x128";
     dim3 grid((unsigned)(ceil_div(p.NS, PF_BN / kTileN) * ceil_div(p.M, PF_BM)));
     const bool fast = p.a_vec && (p.K % kTileK) == 0;
+    const dim3 b(256);
     if (p.zBs != 0) {
-        if (fast)
-            hipLaunchKernelGGL((k_int8_prefill<true, true>), grid, dim3(256), 0, s, p);
+        if (fast && p.a_u8)
+            hipLaunchKernelGGL((k_int8_prefill<true, true, true>), grid, b, 0, s, p);
+        else if (fast)
+            hipLaunchKernelGGL((k_int8_prefill<true, true, false>), grid, b, 0, s, p);
         else
-            hipLaunchKernelGGL((k_int8_prefill<true, false>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((k_int8_prefill<true, false, false>), grid, b, 0, s, p);
     } else {
-        if (fast)
-            hipLaunchKernelGGL((k_int8_prefill<false, true>), grid, dim3(256), 0, s, p);
+        if (fast && p.a_u8)
+            hipLaunchKernelGGL((k_int8_prefill<false, true, true>), grid, b, 0, s, p);
+        else if (fast)
+            hipLaunchKernelGGL((k_int8_prefill<false, true, false>), grid, b, 0, s, p);
         else
-            hipLaunchKernelGGL((k_int8_prefill<false, false>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((k_int8_prefill<false, false, false>), grid, b, 0, s, p);
     }
     return hipGetLastError();
 }
