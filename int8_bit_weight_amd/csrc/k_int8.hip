@@ -306,6 +306,10 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
 // M <= 16*MT on quantised activations.  One workgroup per 16-column strip;
 // its WAVES wavefronts split the k tiles round-robin (wave w takes tiles w,
 // w+WAVES, ...), TPW tiles per round, and every load of a round (one 16-byte
@@ -555,26 +559,32 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p) {
 
 // -------------------------------------------------------- prefill GEMM ---
 // 256 x 128 output tile per workgroup, k step 64, 4 wavefronts in a 2 x 2
-// grid each owning 128 x 64 (8 x 4 MFMA tiles of 16 x 16, 128 int32
-// accumulators per lane, held in AGPRs).  Both operands sit in LDS in MFMA
-// fragment order (1 KiB per 16 rows or 16 columns x 64 k, 16 bytes per lane),
-// so every fragment read is one ds_read_b128 per lane; the packed weight
-// tiles are already in that order and are copied as is.  In an A fragment
-// the 16-byte piece of (row r, k-chunk g) sits at slot 16 g + (r ^ f(g)),
-// f = {0, 6, 10, 12}: the staging stores (four consecutive lanes hold one
-// row's four chunks, so the global loads stay 64 bytes contiguous) and the
-// MFMA reads (lane L: row L % 16, chunk L / 16) both touch distinct 16-byte
-// bank groups in every 8 and every 16 consecutive lanes.  Each wavefront
-// reads 12 fragments per 32 MFMAs.
+// grid each owning 128 x 64: 4 x 2 tiles of v_mfma_i32_32x32x32_i8 (two per
+// tile and k step, 128 int32 accumulators per lane).  The 32 x 32 form
+// sustained 4.1-4.3 POP/s in an issue-rate probe even at one wavefront per
+// SIMD, the 16 x 16 x 64 form 2.5 (one wave) to 3.3 (four waves).  A
+// 32 x 32 x 32 operand takes, for lane L, row (or column) L % 32 and the
+// 16-k chunk 2 h + L / 32 of k half h.  The activations are staged through
+// LDS in 16-row fragments of 64 k (1 KiB, 16 bytes per lane chunk; every
+// operand read is one ds_read_b128 per lane).  The weight operands come
+// straight from the packed tiles in global memory (already 16-byte lane
+// chunks of 16 k for one column) into registers: LDS throughput, not the
+// MFMA rate, bounded the version that staged both operands (a run with
+// the MFMAs removed took 80 % of the time of the full kernel).  In an A fragment
+// the 16-byte piece of (row r, k-chunk g) sits at slot 4 r + (g ^ t(r)),
+// t(r) = ((r >> 1) ^ (r >> 3)) & 3: a row's four chunks fill four
+// consecutive slots, so the lanes that fill consecutive slots (a global-to-LDS
+// copy puts lane L's piece in slot L) read 64 contiguous bytes of one row,
+// and the MFMA reads (lane L: row L % 16, one chunk) touch distinct 16-byte
+// bank groups in every 8 and every 16 consecutive lanes.
 // Global loads run PF_DEPTH k steps ahead through a ring of register stages
 // (compile-time slots: the k loop is unrolled by PF_DEPTH), so the L2/MALL
 // latency of a stage is covered by PF_DEPTH - 1 steps of MFMAs; LDS holds two
 // stages.  Row and column epilogue operands are staged in LDS once.
 constexpr int PF_BM = 256, PF_BN = 128, PF_DEPTH = 4;
 
-__device__ __forceinline__ int pf_slot(int r, int g) {
-    return g * 16 + (r ^ ((0xCA60 >> (4 * g)) & 15));
-}
+__device__ __forceinline__ int pf_chunk_perm(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int pf_slot(int r, int g) { return 4 * r + (g ^ pf_chunk_perm(r)); }
 
 template <int N>
 using ic = std::integral_constant<int, N>;
@@ -589,6 +599,120 @@ __device__ __forceinline__ void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+#ifndef PF_SCHED
+#define PF_SCHED 2
+#endif
+// Instruction order of one k step.  With one wavefront per SIMD nothing
+// else hides a wait, and left to itself the scheduler moves the LDS operand
+// reads for the next step down next to their first use (each pair of MFMAs
+// then waits for an LDS round trip).  The order pinned here puts one memory
+// instruction between consecutive MFMAs: the next step's 8 operand reads,
+// then the 8 global loads, then the 4 activation stores, so that the LDS
+// stores have drained by the barrier that ends the step.
+template <bool HAS_ZB>
+__device__ __forceinline__ void pf_schedule() {
+    constexpr int MFMA = 0x008, VMEM_RD = 0x020, DS_RD = 0x100, DS_WR = 0x200;
+    if constexpr (PF_SCHED == 1) {
+        static_for<8>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+        });
+        static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
+        });
+        static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DS_WR, 1, 0);
+        });
+        if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
+    } else if constexpr (PF_SCHED == 4) {
+        __builtin_amdgcn_sched_group_barrier(DS_WR, 4, 0);
+        static_for<8>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+        });
+        static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(MFMA, HAS_ZB ? 8 : 4, 0);
+    } else if constexpr (PF_SCHED == 5) {
+        static_for<8>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+        });
+        static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(MFMA, HAS_ZB ? 7 : 3, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_WR, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+    } else if constexpr (PF_SCHED == 6) {
+        static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DS_RD, 2, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_WR, 4, 0);
+        static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(MFMA, HAS_ZB ? 11 : 7, 0);
+    } else if constexpr (PF_SCHED == 2) {
+        static_for<8>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+        });
+        static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DS_WR, 1, 0);
+        });
+        static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
+        });
+        if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
+    }
+}
+
+// Step order of the direct-load path: the 8 operand reads for the next step
+// and the 8 global loads (4 straight into LDS, 4 weight operands) each sit
+// between two MFMAs.
+template <bool HAS_ZB>
+__device__ __forceinline__ void pf_schedule_direct() {
+    constexpr int MFMA = 0x008, VMEM = 0x060, DS_RD = 0x100;
+    static_for<8>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+    });
+    static_for<8>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(VMEM, 1, 0);
+    });
+    if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
+}
+
+// s_waitcnt that waits for the vector memory counter only (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// Workgroup barrier for LDS written by this workgroup's own LDS stores and
+// by global-to-LDS copies whose completion the caller has already waited for
+// (vmcnt).  __syncthreads' release fence would also wait for every
+// outstanding global load, including the weight operands and the copies of
+// later stages that are meant to stay in flight across the barrier.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // FAST (A 16-byte aligned, lda % 16 == 0, K % 64 == 0): every global load is
 // unconditional, so loads issued for later stages stay in flight (a load
 // inside a branch makes the compiler wait for it at the branch's end).  Rows
@@ -600,15 +724,32 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     constexpr int AF = PF_BM / 16;      // A fragments per stage
     constexpr int BF = PF_BN / 16;      // B fragments per stage
     constexpr int ACH = AF * 64 / 256;  // 16-byte A chunks per thread per stage (4)
-    constexpr int BCH = BF * 64 / 256;  // 16-byte B chunks per thread per stage (2)
-    constexpr int SA = AF * 1024, SB = BF * 1024;  // bytes of one stage
-    __shared__ __attribute__((aligned(16))) int8_t sA[3][SA];
-    __shared__ __attribute__((aligned(16))) int8_t sB[3][SB];
+    constexpr int SA = AF * 1024;  // bytes of one activation stage
+    constexpr bool DIRECT = FAST && !FLIP;  // activations copied straight into LDS
+    // activation stages in LDS: three for the register-staged path; for the
+    // direct path one array per stage, so that the compiler can tell a read
+    // of one stage from a copy still landing in another (it waits for every
+    // outstanding global-to-LDS copy before a read it cannot separate from
+    // them)
+    __shared__ __attribute__((aligned(16))) int8_t sA[DIRECT ? 1 : 3][DIRECT ? 16 : SA];
+    static_assert(PF_DEPTH <= 6, "direct-path stage arrays");
+    __shared__ __attribute__((aligned(16))) int8_t sD0[DIRECT ? SA : 16], sD1[DIRECT ? SA : 16],
+        sD2[DIRECT ? SA : 16], sD3[DIRECT ? SA : 16], sD4[DIRECT && PF_DEPTH > 4 ? SA : 16],
+        sD5[DIRECT && PF_DEPTH > 5 ? SA : 16];
+    auto stage_buf = [&](auto B) -> int8_t * {
+        constexpr int b = decltype(B)::value;
+        if constexpr (b == 0) return sD0;
+        else if constexpr (b == 1) return sD1;
+        else if constexpr (b == 2) return sD2;
+        else if constexpr (b == 3) return sD3;
+        else if constexpr (b == 4) return sD4;
+        else return sD5;
+    };
     __shared__ __attribute__((aligned(16))) float s_rs[PF_BM];
     __shared__ ColOps s_col[PF_BN];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int tiles_n = (p.NS + BF - 1) / BF;
     const int bn = blockIdx.x % tiles_n;
@@ -617,37 +758,53 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     const int strip0 = bn * BF;
     const int KT = p.KT;
 
-    // per-thread source pointers of the FAST path (k advances by 64 bytes a step)
+    // FAST: wave w moves A fragments 4 w .. 4 w + 3 of each stage, one
+    // 16-byte piece per lane, into slot L of the fragment (straight into LDS,
+    // or through registers when the bytes are flipped on the way); lane L
+    // fetches the (row, k-chunk) that the swizzle puts in slot L.  k advances
+    // by 64 bytes a step.
     const int8_t *a_src[ACH];
-    const int8_t *b_src[BCH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-        const int c = tid + 256 * i;
-        const int row = min(m0 + (c >> 2), p.M - 1);
-        a_src[i] = p.A + (int64_t)row * p.lda + (c & 3) * 16;
+        const int r = lane >> 2;
+        const int g = (lane & 3) ^ pf_chunk_perm(r);
+        const int row = min(m0 + (4 * wave + i) * 16 + r, p.M - 1);
+        a_src[i] = p.A + (int64_t)row * p.lda + g * 16;
     }
+    // weight operands of this wave: column tile t (32 columns, strips
+    // 2t and 2t+1 of the wave's 4), k half h; strips past the last read the
+    // last one (their columns are never stored)
+    const int8_t *b_src[2];
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-        const int c = tid + 256 * i;
-        const int strip = min(strip0 + (c >> 6), p.NS - 1);
-        b_src[i] = p.codes + (int64_t)strip * KT * kTileBytes + (c & 63) * 16;
+    for (int t = 0; t < 2; ++t) {
+        const int strip = min(strip0 + wn * 4 + t * 2 + ((lane & 31) >> 4), p.NS - 1);
+        b_src[t] = p.codes + (int64_t)strip * KT * kTileBytes;
     }
-    v4i ra[PF_DEPTH][ACH], rb[PF_DEPTH][BCH];
+    v4i ra[PF_DEPTH][ACH], rb[PF_DEPTH][2][2];
     int a_dst[ACH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
         const int c = tid + 256 * i;
         const int r = c >> 2;
-        a_dst[i] = (r >> 4) * 1024 + pf_slot(r & 15, c & 3) * 16;
+        a_dst[i] = FAST ? (4 * wave + i) * 1024 + lane * 16 : (r >> 4) * 1024 + pf_slot(r & 15, c & 3) * 16;
     }
-    const int a_rd = pf_slot(lane & 15, lane >> 4) * 16;
+    // operand read offsets inside a 1 KiB fragment, per k half: chunk 2 h + L / 32
+    int a_rd[2], b_rd[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        a_rd[h] = pf_slot(lane & 15, 2 * h + (lane >> 5)) * 16;
+        b_rd[h] = ((2 * h + (lane >> 5)) * 16 + (lane & 15)) * 16;  // inside a packed 1 KiB tile
+    }
     auto gload = [&](auto slot, int kt) {
         constexpr int sl = decltype(slot)::value;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) rb[sl][t][h] = *(const v4i *)(b_src[t] + (int64_t)kt * kTileBytes + b_rd[h]);
+        if (DIRECT) return;
         if (FAST) {
 #pragma unroll
             for (int i = 0; i < ACH; ++i) ra[sl][i] = *(const v4i *)(a_src[i] + (int64_t)kt * kTileK);
-#pragma unroll
-            for (int i = 0; i < BCH; ++i) rb[sl][i] = *(const v4i *)(b_src[i] + (int64_t)kt * kTileBytes);
             return;
         }
 #pragma unroll
@@ -655,14 +812,15 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
             const int c = tid + 256 * i;  // (row, k-chunk) = (c >> 2, c & 3)
             ra[sl][i] = load_a16<false>(p, m0 + (c >> 2), kt * kTileK + (c & 3) * 16);
         }
+    };
+    // FAST: A stage kt into LDS buffer BUF, without passing through registers
+    auto dload = [&](auto BUF, int kt) {
+        constexpr int b = decltype(BUF)::value;
 #pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int c = tid + 256 * i;  // (strip, lane chunk) = (c >> 6, c & 63)
-            const int strip = strip0 + (c >> 6);
-            const v4i v = *(const v4i *)(p.codes + ((int64_t)min(strip, p.NS - 1) * KT + kt) * kTileBytes +
-                                         (c & 63) * 16);
-            rb[sl][i] = strip < p.NS ? v : v4i{0, 0, 0, 0};
-        }
+        for (int i = 0; i < ACH; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(a_src[i] + (int64_t)kt * kTileK),
+                                             (__attribute__((address_space(3))) void *)(stage_buf(ic<b>{}) + (4 * wave + i) * 1024),
+                                             16, 0, 0);
     };
     auto sstore = [&](auto slot, int buf) {
         constexpr int sl = decltype(slot)::value;
@@ -677,48 +835,90 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
             }
             *(v4i *)(&sA[buf][a_dst[i]]) = v;
         }
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int c = tid + 256 * i;
-            *(v4i *)(&sB[buf][c * 16]) = rb[sl][i];
-        }
     };
 
-    v4i acc[8][4];
-    v4i accr[8];
+    v16i acc[4][2];
+    v16i accr[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        accr[i] = v4i{0, 0, 0, 0};
+    for (int i = 0; i < 4; ++i) {
+        accr[i] = v16i{};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < 2; ++j) acc[i][j] = v16i{};
     }
     const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
-    // MFMA fragments, double-buffered in registers: a step's fragments are
-    // read from LDS during the previous step's MFMAs.
-    v4i fa[2][8], fb[2][4];
-    auto lds_frags = [&](auto F, int buf) {
+    // activation operands, double-buffered in registers: a step's operands
+    // are read from LDS during the previous step's MFMAs.  [tile][k half]
+    v4i fa[2][4][2];
+    auto lds_frags_at = [&](auto F, const int8_t *base) {
         constexpr int f = decltype(F)::value;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[f][j] = *(const v4i *)(&sB[buf][(wn * 4 + j) * 1024 + lane * 16]);
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) fa[f][i] = *(const v4i *)(&sA[buf][(wm * 8 + i) * 1024 + a_rd]);
+            for (int t = 0; t < 4; ++t)
+                fa[f][t][h] = *(const v4i *)(base + (wm * 8 + t * 2 + ((lane & 31) >> 4)) * 1024 + a_rd[h]);
     };
-    auto mfmas = [&](auto F) {
-        constexpr int f = decltype(F)::value;
+    auto lds_frags = [&](auto F, int buf) { lds_frags_at(F, &sA[buf][0]); };
+    // step k: activation set F, weight operands from register slot S
+    auto mfmas = [&](auto F, auto S) {
+        constexpr int f = decltype(F)::value, sl = decltype(S)::value;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_i8(fa[f][i], fb[f][j], acc[i][j]);
-            if (HAS_ZB) accr[i] = mfma_i8(fa[f][i], ones, accr[i]);
-        }
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_i8(fa[f][i][h], rb[sl][j][h], acc[i][j]);
+                if (HAS_ZB) accr[i] = mfma32_i8(fa[f][i][h], ones, accr[i]);
+            }
     };
 
-    // Stage s: register slot s % PF_DEPTH, LDS buffer s % 3, fragment set
-    // s % 2.  Step k: read step k+1's fragments (LDS buffer written in step
-    // k-1, published by its barrier), MFMAs of step k, store stage k+2 (its
-    // buffer was last read for step k-1, whose reads completed before the
-    // MFMAs of step k-1), load stage k+PF_DEPTH, barrier.
+    // Stage s: register slot s % PF_DEPTH, LDS buffer s % 3, activation
+    // operand set s % 2.  Step k: read step k+1's activation operands (LDS
+    // buffer written in step k-1, published by its barrier), MFMAs of step k
+    // (weight operands in slot k % PF_DEPTH, loaded PF_DEPTH steps ago),
+    // store stage k+2's activations (its buffer was last read for step k-1,
+    // whose reads completed before the MFMAs of step k-1), load stage
+    // k+PF_DEPTH into slot k % PF_DEPTH, barrier.
+    const int KTD = KT - KT % PF_DEPTH;
+    if constexpr (DIRECT) {
+        // Stage s: LDS buffer and weight register slot s % PF_DEPTH,
+        // activation operand set s % 2.  Step k: read step k+1's activation
+        // operands (published by the barrier of step k-1), MFMAs of step k,
+        // load stage k+PF_DEPTH (its buffer held stage k, read in step k-1;
+        // its register slot was just read by the MFMAs), then wait until
+        // stage k+2 has landed in LDS and barrier.  Every step issues 8
+        // vector memory operations (4 to LDS, 4 to registers; stages past
+        // the last repeat the last one), so stage k+2's are complete once at
+        // most 8 (PF_DEPTH - 2) remain outstanding.
+        static_for<PF_DEPTH>([&](auto S) {
+            const int kt = min(decltype(S)::value, KT - 1);
+            dload(S, kt);
+            gload(S, kt);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<8 * (PF_DEPTH - 2)>();
+        lds_barrier();
+        lds_frags_at(ic<0>{}, stage_buf(ic<0>{}));
+        wait_lgkmcnt0();
+        auto dstep = [&](auto J, int kt) {
+            constexpr int j = decltype(J)::value;
+            lds_frags_at(ic<(j + 1) & 1>{}, stage_buf(ic<(j + 1) % PF_DEPTH>{}));
+            mfmas(ic<j & 1>{}, J);
+            const int kn = min(kt + PF_DEPTH, KT - 1);
+            dload(J, kn);
+            gload(J, kn);
+            pf_schedule_direct<HAS_ZB>();
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<8 * (PF_DEPTH - 2)>();
+            lds_barrier();
+        };
+        for (int base = 0; base < KTD; base += PF_DEPTH)
+            static_for<PF_DEPTH>([&](auto J) { dstep(J, base + decltype(J)::value); });
+        static_for<PF_DEPTH - 1>([&](auto J) {
+            if (KTD + decltype(J)::value < KT) dstep(J, KTD + decltype(J)::value);
+        });
+        wait_vmcnt<0>();
+    } else {
     static_for<PF_DEPTH>([&](auto S) { gload(S, min(decltype(S)::value, KT - 1)); });
     sstore(ic<0>{}, 0);
     sstore(ic<1 % PF_DEPTH>{}, 1);
@@ -727,18 +927,20 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     auto step = [&](auto J, int kt) {
         constexpr int j = decltype(J)::value;
         lds_frags(ic<(j + 1) & 1>{}, (kt + 1) % 3);
-        mfmas(ic<j & 1>{});
+        mfmas(ic<j & 1>{}, J);
         sstore(ic<(j + 2) % PF_DEPTH>{}, (kt + 2) % 3);
         gload(ic<j>{}, min(kt + PF_DEPTH, KT - 1));
+        pf_schedule<HAS_ZB>();
         __syncthreads();
     };
     static_assert(PF_DEPTH % 2 == 0, "fragment sets alternate with the unrolled steps");
-    const int KTD = KT - KT % PF_DEPTH;
+    static_assert(PF_DEPTH >= 3, "stage k+2 is stored in step k: it must have been loaded in an earlier step");
     for (int base = 0; base < KTD; base += PF_DEPTH)
         static_for<PF_DEPTH>([&](auto J) { step(J, base + decltype(J)::value); });
     static_for<PF_DEPTH - 1>([&](auto J) {
         if (KTD + decltype(J)::value < KT) step(J, KTD + decltype(J)::value);
     });
+    }
 
     // ---- epilogue.  Row scales and column operands are staged in LDS (the
     // A/B buffers are no longer needed); the common case (fp32 output, no
@@ -752,43 +954,48 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     if (tid < PF_BN) s_col[tid] = load_colops_c(p, strip0 * kTileN + tid);
     __syncthreads();
     const bool whole = m0 + PF_BM <= p.M && (strip0 + BF) * kTileN <= p.N;
+    // accumulator element e of tile (i, j): row i*32 + 8 (e / 4) + 4 (L / 32) + e % 4,
+    // column j*32 + L % 32 of the wavefront's 128 x 64 block
     if (!HAS_ZB && p.outputs == QMM_OUT_F32 && p.zAs == 0 && whole) {
-        float cm[4], cb[4];
+        float cm[2], cb[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const ColOps c = s_col[(wn * 4 + j) * 16 + (lane & 15)];
+        for (int j = 0; j < 2; ++j) {
+            const ColOps c = s_col[wn * 64 + j * 32 + (lane & 31)];
             cm[j] = c.cs;
             cb[j] = c.bias_f;
         }
-        float *ybase = p.y_f32 + (int64_t)(m0 + wm * 128 + 4 * (lane >> 4)) * p.ld_f32 + strip0 * kTileN +
-                       wn * 64 + (lane & 15);
+        float *ybase = p.y_f32 + (int64_t)(m0 + wm * 128 + 4 * (lane >> 5)) * p.ld_f32 + strip0 * kTileN +
+                       wn * 64 + (lane & 31);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const v4f rs = *(const v4f *)(&s_rs[wm * 128 + i * 16 + 4 * (lane >> 4)]);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float *yrow = ybase + (int64_t)(i * 16 + v) * p.ld_f32;
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = i * 32 + 8 * g;
+                const v4f rs = *(const v4f *)(&s_rs[wm * 128 + r0 + 4 * (lane >> 5)]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float mult = (rs[v] * cm[j]) * p.scale;
-                    yrow[j * 16] = fmaf((float)acc[i][j][v], mult, cb[j]);
+                for (int v = 0; v < 4; ++v) {
+                    float *yrow = ybase + (int64_t)(r0 + v) * p.ld_f32;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const float mult = (rs[v] * cm[j]) * p.scale;
+                        yrow[j * 32] = fmaf((float)acc[i][j][4 * g + v], mult, cb[j]);
+                    }
                 }
             }
-        }
         return;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int cl = (wn * 4 + j) * 16 + (lane & 15);
+        for (int j = 0; j < 2; ++j) {
+            const int cl = wn * 64 + j * 32 + (lane & 31);
             const int n = strip0 * kTileN + cl;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int rl = wm * 128 + i * 16 + 4 * (lane >> 4) + v;
+            for (int e = 0; e < 16; ++e) {
+                const int rl = wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 const int m = m0 + rl;
                 if (m < p.M && n < p.N)
-                    epilogue_store_c(p, m, n, (uint32_t)acc[i][j][v], HAS_ZB ? accr[i][v] : 0, HAS_ZB, s_rs[rl],
+                    epilogue_store_c(p, m, n, (uint32_t)acc[i][j][e], HAS_ZB ? accr[i][e] : 0, HAS_ZB, s_rs[rl],
                                      s_col[cl]);
             }
         }
