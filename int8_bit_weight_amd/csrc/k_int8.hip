@@ -561,26 +561,31 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p) {
 // 256 x 128 output tile per workgroup, k step 64, 4 wavefronts in a 2 x 2
 // grid each owning 128 x 64: 4 x 2 tiles of v_mfma_i32_32x32x32_i8 (two per
 // tile and k step, 128 int32 accumulators per lane).  The 32 x 32 form
-// sustained 4.1-4.3 POP/s in an issue-rate probe even at one wavefront per
-// SIMD, the 16 x 16 x 64 form 2.5 (one wave) to 3.3 (four waves).  A
-// 32 x 32 x 32 operand takes, for lane L, row (or column) L % 32 and the
-// 16-k chunk 2 h + L / 32 of k half h.  The activations are staged through
-// LDS in 16-row fragments of 64 k (1 KiB, 16 bytes per lane chunk; every
-// operand read is one ds_read_b128 per lane).  The weight operands come
-// straight from the packed tiles in global memory (already 16-byte lane
-// chunks of 16 k for one column) into registers: LDS throughput, not the
-// MFMA rate, bounded the version that staged both operands (a run with
-// the MFMAs removed took 80 % of the time of the full kernel).  In an A fragment
-// the 16-byte piece of (row r, k-chunk g) sits at slot 4 r + (g ^ t(r)),
-// t(r) = ((r >> 1) ^ (r >> 3)) & 3: a row's four chunks fill four
-// consecutive slots, so the lanes that fill consecutive slots (a global-to-LDS
-// copy puts lane L's piece in slot L) read 64 contiguous bytes of one row,
-// and the MFMA reads (lane L: row L % 16, one chunk) touch distinct 16-byte
-// bank groups in every 8 and every 16 consecutive lanes.
-// Global loads run PF_DEPTH k steps ahead through a ring of register stages
-// (compile-time slots: the k loop is unrolled by PF_DEPTH), so the L2/MALL
-// latency of a stage is covered by PF_DEPTH - 1 steps of MFMAs; LDS holds two
-// stages.  Row and column epilogue operands are staged in LDS once.
+// issues one MFMA per 32 cycles even at one wavefront per SIMD (the 16 x 16
+// x 64 form reached 2.5 POP/s there, 3.3 at four waves).  With random int8
+// operands on every SIMD the chip clock drops to about 1.5 GHz (2.1 GHz with
+// constant operands), so about 3.0 POP/s, not the nominal 5.0, is the
+// ceiling for this data.  A 32 x 32 x 32 operand takes, for lane L, row (or
+// column) L % 32 and the 16-k chunk 2 h + L / 32 of k half h.
+//
+// Activations: 16-row fragments of 64 k in LDS (1 KiB, one ds_read_b128 per
+// lane per operand).  On the aligned path every stage is copied global-to-LDS
+// (global_load_lds_dwordx4: no register round trip and no LDS store
+// instructions, which measured about 140 cycles a step when interleaved with
+// the MFMAs) into a ring of PF_DEPTH LDS stages.  Weights: the packed tiles
+// are already 16-byte lane chunks of 16 k for one column, so every wavefront
+// loads its operands straight into a ring of PF_DEPTH register stages.
+// Loads run PF_DEPTH k steps ahead (compile-time slots: the k loop is
+// unrolled by PF_DEPTH).
+//
+// In an A fragment the 16-byte piece of (row r, k-chunk g) sits at slot
+// 4 r + (g ^ t(r)), t(r) = ((r >> 1) ^ (r >> 3)) & 3: a row's four chunks
+// fill four consecutive slots, so the lanes that fill consecutive slots (a
+// global-to-LDS copy puts lane L's piece in slot L) read 64 contiguous bytes
+// of one row (a layout with 16 rows per 16 lanes made the copies 25 % slower
+// overall), and the MFMA reads (lane L: row L % 16, one chunk) touch distinct
+// 16-byte bank groups in every 8 and every 16 consecutive lanes.  Row and
+// column epilogue operands are staged in LDS once.
 constexpr int PF_BM = 256, PF_BN = 128, PF_DEPTH = 4;
 
 __device__ __forceinline__ int pf_chunk_perm(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -599,83 +604,30 @@ __device__ __forceinline__ void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-#ifndef PF_SCHED
-#define PF_SCHED 2
-#endif
-// Instruction order of one k step.  With one wavefront per SIMD nothing
-// else hides a wait, and left to itself the scheduler moves the LDS operand
-// reads for the next step down next to their first use (each pair of MFMAs
-// then waits for an LDS round trip).  The order pinned here puts one memory
-// instruction between consecutive MFMAs: the next step's 8 operand reads,
-// then the 8 global loads, then the 4 activation stores, so that the LDS
-// stores have drained by the barrier that ends the step.
+// Instruction order of one k step of the register-staged path.  With one
+// wavefront per SIMD nothing else hides a wait, and left to itself the
+// scheduler moves the LDS operand reads for the next step down next to their
+// first use (each pair of MFMAs then waits for an LDS round trip).  The order
+// pinned here puts one memory instruction between consecutive MFMAs: the
+// next step's 8 operand reads, the 4 activation stores, then the 8 global
+// loads (two per MFMA).  Of the placements tried (stores grouped at the
+// start or the end of the step, loads before the stores) this was fastest.
 template <bool HAS_ZB>
-__device__ __forceinline__ void pf_schedule() {
+__device__ __forceinline__ void pf_schedule_staged() {
     constexpr int MFMA = 0x008, VMEM_RD = 0x020, DS_RD = 0x100, DS_WR = 0x200;
-    if constexpr (PF_SCHED == 1) {
-        static_for<8>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
-        });
-        static_for<4>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
-        });
-        static_for<4>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(DS_WR, 1, 0);
-        });
-        if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
-    } else if constexpr (PF_SCHED == 4) {
-        __builtin_amdgcn_sched_group_barrier(DS_WR, 4, 0);
-        static_for<8>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
-        });
-        static_for<4>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
-        });
-        __builtin_amdgcn_sched_group_barrier(MFMA, HAS_ZB ? 8 : 4, 0);
-    } else if constexpr (PF_SCHED == 5) {
-        static_for<8>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
-        });
-        static_for<4>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
-        });
-        __builtin_amdgcn_sched_group_barrier(MFMA, HAS_ZB ? 7 : 3, 0);
-        __builtin_amdgcn_sched_group_barrier(DS_WR, 4, 0);
+    static_for<8>([&](auto) {
         __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-    } else if constexpr (PF_SCHED == 6) {
-        static_for<4>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(DS_RD, 2, 0);
-        });
+        __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+    });
+    static_for<4>([&](auto) {
         __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(DS_WR, 4, 0);
-        static_for<4>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
-        });
-        __builtin_amdgcn_sched_group_barrier(MFMA, HAS_ZB ? 11 : 7, 0);
-    } else if constexpr (PF_SCHED == 2) {
-        static_for<8>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
-        });
-        static_for<4>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(DS_WR, 1, 0);
-        });
-        static_for<4>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
-        });
-        if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
-    }
+        __builtin_amdgcn_sched_group_barrier(DS_WR, 1, 0);
+    });
+    static_for<4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
+    });
+    if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
 }
 
 // Step order of the direct-load path: the 8 operand reads for the next step
@@ -717,25 +669,27 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // unconditional, so loads issued for later stages stay in flight (a load
 // inside a branch makes the compiler wait for it at the branch's end).  Rows
 // past M read row M - 1 and strips past the last read the last strip; those
-// products land in outputs that are never stored.  FLIP (uint8 A on the FAST
-// path): A is shifted when the stage is written to LDS.
+// products land in outputs that are never stored.  The FAST path copies the
+// activations global-to-LDS; the general path stages them through registers
+// (masked, shifted for uint8 A, stored to LDS).  FLIP (uint8 A on the FAST
+// path): the copies land unshifted and each step flips its own operand
+// registers before its MFMAs.
 template <bool HAS_ZB, bool FAST, bool FLIP>
 __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     constexpr int AF = PF_BM / 16;      // A fragments per stage
     constexpr int BF = PF_BN / 16;      // B fragments per stage
     constexpr int ACH = AF * 64 / 256;  // 16-byte A chunks per thread per stage (4)
     constexpr int SA = AF * 1024;  // bytes of one activation stage
-    constexpr bool DIRECT = FAST && !FLIP;  // activations copied straight into LDS
     // activation stages in LDS: three for the register-staged path; for the
-    // direct path one array per stage, so that the compiler can tell a read
+    // FAST path one array per stage, so that the compiler can tell a read
     // of one stage from a copy still landing in another (it waits for every
     // outstanding global-to-LDS copy before a read it cannot separate from
     // them)
-    __shared__ __attribute__((aligned(16))) int8_t sA[DIRECT ? 1 : 3][DIRECT ? 16 : SA];
+    __shared__ __attribute__((aligned(16))) int8_t sA[FAST ? 1 : 3][FAST ? 16 : SA];
     static_assert(PF_DEPTH <= 6, "direct-path stage arrays");
-    __shared__ __attribute__((aligned(16))) int8_t sD0[DIRECT ? SA : 16], sD1[DIRECT ? SA : 16],
-        sD2[DIRECT ? SA : 16], sD3[DIRECT ? SA : 16], sD4[DIRECT && PF_DEPTH > 4 ? SA : 16],
-        sD5[DIRECT && PF_DEPTH > 5 ? SA : 16];
+    __shared__ __attribute__((aligned(16))) int8_t sD0[FAST ? SA : 16], sD1[FAST ? SA : 16],
+        sD2[FAST ? SA : 16], sD3[FAST ? SA : 16], sD4[FAST && PF_DEPTH > 4 ? SA : 16],
+        sD5[FAST && PF_DEPTH > 5 ? SA : 16];
     auto stage_buf = [&](auto B) -> int8_t * {
         constexpr int b = decltype(B)::value;
         if constexpr (b == 0) return sD0;
@@ -758,11 +712,10 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     const int strip0 = bn * BF;
     const int KT = p.KT;
 
-    // FAST: wave w moves A fragments 4 w .. 4 w + 3 of each stage, one
-    // 16-byte piece per lane, into slot L of the fragment (straight into LDS,
-    // or through registers when the bytes are flipped on the way); lane L
-    // fetches the (row, k-chunk) that the swizzle puts in slot L.  k advances
-    // by 64 bytes a step.
+    // FAST: wave w copies A fragments 4 w .. 4 w + 3 of each stage straight
+    // into LDS, one 16-byte piece per lane landing in slot L of the fragment;
+    // lane L fetches the (row, k-chunk) that the swizzle puts in slot L.  k
+    // advances by 64 bytes a step.
     const int8_t *a_src[ACH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
@@ -781,12 +734,12 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         b_src[t] = p.codes + (int64_t)strip * KT * kTileBytes;
     }
     v4i ra[PF_DEPTH][ACH], rb[PF_DEPTH][2][2];
-    int a_dst[ACH];
+    int a_dst[ACH];  // general path: LDS byte offset of thread's piece i of a stage
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
         const int c = tid + 256 * i;
         const int r = c >> 2;
-        a_dst[i] = FAST ? (4 * wave + i) * 1024 + lane * 16 : (r >> 4) * 1024 + pf_slot(r & 15, c & 3) * 16;
+        a_dst[i] = (r >> 4) * 1024 + pf_slot(r & 15, c & 3) * 16;
     }
     // operand read offsets inside a 1 KiB fragment, per k half: chunk 2 h + L / 32
     int a_rd[2], b_rd[2];
@@ -801,12 +754,7 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int h = 0; h < 2; ++h) rb[sl][t][h] = *(const v4i *)(b_src[t] + (int64_t)kt * kTileBytes + b_rd[h]);
-        if (DIRECT) return;
-        if (FAST) {
-#pragma unroll
-            for (int i = 0; i < ACH; ++i) ra[sl][i] = *(const v4i *)(a_src[i] + (int64_t)kt * kTileK);
-            return;
-        }
+        if (FAST) return;
 #pragma unroll
         for (int i = 0; i < ACH; ++i) {
             const int c = tid + 256 * i;  // (row, k-chunk) = (c >> 2, c & 3)
@@ -825,16 +773,7 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     auto sstore = [&](auto slot, int buf) {
         constexpr int sl = decltype(slot)::value;
 #pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            v4i v = ra[sl][i];
-            if (FLIP) {
-                v[0] ^= 0x80808080;
-                v[1] ^= 0x80808080;
-                v[2] ^= 0x80808080;
-                v[3] ^= 0x80808080;
-            }
-            *(v4i *)(&sA[buf][a_dst[i]]) = v;
-        }
+        for (int i = 0; i < ACH; ++i) *(v4i *)(&sA[buf][a_dst[i]]) = ra[sl][i];
     };
 
     v16i acc[4][2];
@@ -880,7 +819,7 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     // whose reads completed before the MFMAs of step k-1), load stage
     // k+PF_DEPTH into slot k % PF_DEPTH, barrier.
     const int KTD = KT - KT % PF_DEPTH;
-    if constexpr (DIRECT) {
+    if constexpr (FAST) {
         // Stage s: LDS buffer and weight register slot s % PF_DEPTH,
         // activation operand set s % 2.  Step k: read step k+1's activation
         // operands (published by the barrier of step k-1), MFMAs of step k,
@@ -903,6 +842,14 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         auto dstep = [&](auto J, int kt) {
             constexpr int j = decltype(J)::value;
             lds_frags_at(ic<(j + 1) & 1>{}, stage_buf(ic<(j + 1) % PF_DEPTH>{}));
+            if constexpr (FLIP) {
+                // uint8 activations: the flip happens on this step's operands,
+                // read (and waited for) before the previous barrier
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) fa[j & 1][t][h] ^= 0x80808080;
+            }
             mfmas(ic<j & 1>{}, J);
             const int kn = min(kt + PF_DEPTH, KT - 1);
             dload(J, kn);
@@ -930,7 +877,7 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         mfmas(ic<j & 1>{}, J);
         sstore(ic<(j + 2) % PF_DEPTH>{}, (kt + 2) % 3);
         gload(ic<j>{}, min(kt + PF_DEPTH, KT - 1));
-        pf_schedule<HAS_ZB>();
+        pf_schedule_staged<HAS_ZB>();
         __syncthreads();
     };
     static_assert(PF_DEPTH % 2 == 0, "fragment sets alternate with the unrolled steps");
