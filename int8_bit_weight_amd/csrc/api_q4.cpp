@@ -28,21 +28,28 @@ Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
     pl.mt = pl.rows_per_launch <= 4 ? 0 : pl.rows_per_launch <= 16 ? 1 : 2;
     pl.waves = 8;
     if (pl.mt == 0) {
-        // k_q4_gemv: workgroups of 4 wavefronts x 2 strips; each split stages
-        // its activations for at most 8 records (8 KiB of LDS per record)
-        pl.waves = 4;
-        const int64_t groups = ceil_div(L.NS, 8);
-        int64_t S = ceil_div(L.NQ, 8);
-        const int64_t want = ceil_div(448, groups);
-        if (S < want) S = want;
-        if (S > L.NQ) S = L.NQ;
-        const int64_t qps = round_up(ceil_div(L.NQ, S), 2) > 8 ? 8 : round_up(ceil_div(L.NQ, S), 2);
-        S = ceil_div(L.NQ, qps);
-        pl.S = (int)S;
-        pl.qps = (int)qps;
-        pl.grid = groups * S;
+        // k_q4_gemv: a workgroup owns one strip and its 4, 8 or 16
+        // wavefronts split the k range, so one launch covers the whole
+        // product.  The fewest wavefronts that leave at most 8 records each
+        // (the kernel keeps them all in flight) and give about 2048
+        // wavefronts in all; 16 when none does.
+        // At one row the kernel keeps all of a wavefront's records in flight
+        // and the tail after the last data arrives is one wavefront's records,
+        // so at most 4 records each where the workgroup size allows.
+        pl.cs = 1;
+        pl.waves = 16;
+        const int64_t rmax = M == 1 && ceil_div(L.NQ, 16) <= 4 ? 4 : 8;
+        for (int w : {4, 8, 16}) {
+            if (ceil_div(L.NQ, w) <= rmax && L.NS * w >= 2048) {
+                pl.waves = w;
+                break;
+            }
+        }
+        pl.S = 1;
+        pl.qps = (int)ceil_div(L.NQ, pl.waves);
+        pl.grid = ceil_div(L.NS, pl.cs);
         pl.ws_part_off = 0;
-        pl.ws_bytes = S > 1 ? round_up(S * pl.rows_per_launch * N * 4, 256) : 0;
+        pl.ws_bytes = 0;
         return pl;
     }
     const int64_t qc = pl.mt <= 1 ? 2 : 1;
@@ -138,7 +145,7 @@ qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx, const 
         p.part = (float *)((uint8_t *)workspace + pl.ws_part_off);
         p.S = pl.S;
         p.qps = pl.qps;
-        e = launch_q4_dense(p, pl.mt, pl.waves, pl.grid, s, &variant);
+        e = launch_q4_dense(p, pl.mt, pl.waves, pl.cs, pl.grid, s, &variant);
     }
     return record_status(e, variant);
 }

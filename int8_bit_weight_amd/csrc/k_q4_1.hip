@@ -17,6 +17,7 @@
 // v_cvt_scalef32_pk_bf16_fp8 with scale 2^9 turns two of them into two exact
 // bf16 integers per instruction.
 #include <type_traits>
+#include <utility>
 
 #include "qmm_internal.h"
 
@@ -26,7 +27,19 @@ namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 template <int N> using ic = std::integral_constant<int, N>;
+
+// f(ic<0>{}), ..., f(ic<N-1>{})
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(ic<I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Eight 4-bit codes (record nibble order) -> eight exact bf16 values in k order.
 // Each conversion yields one packed pair; the four pairs are the four dwords
@@ -426,202 +439,296 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 // ------------------------------------------------ the product, M <= 4 ---
 // Decode-shaped product (at most 4 activation rows).  One MFMA 16-row tile
 // holds the three bf16 terms of each row (rows 4m, 4m+1, 4m+2 of the tile),
-// so a block and strip cost one MFMA.  A workgroup owns SPG = WAVES * C
-// strips and a k range of at most QMAX records: it first stages the
-// activation terms of its whole k range in LDS (one barrier), then each
-// wavefront streams its strips' records through registers with no further
-// synchronisation.  Records go two at a time (8 blocks, the k extent of one
-// m-term MFMA); NSET register sets keep the loads NSET such chunks ahead:
-// a record's registers are refilled with chunk c + NSET's record right after
-// their last use.  Records past the range read d = m = 0 (the header's zero
-// tail), so padding chunks add nothing.
-template <int WAVES, int C, int QMAX, int NSET, int MINW, bool XVEC>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_gemv(Q4Params p) {
-    constexpr int NT = WAVES * 64;
-    constexpr int SPG = C * WAVES;
-    constexpr int QC = 2;
-    static_assert(QMAX % (QC * NSET) == 0, "whole chunk sets");
-    constexpr int BMAX = 4 * QMAX;
-    constexpr int GMAX = QMAX / QC;
-    __shared__ __attribute__((aligned(16))) uint8_t sA[BMAX][1024];
-    // m-term A operand per chunk: row 4m+t, k = block of the chunk (k-octet 0)
-    __shared__ __attribute__((aligned(16))) uint8_t sXM[GMAX][1024];
+// so a block and strip cost one MFMA.  A workgroup owns C strips and the
+// whole k range, which its W wavefronts split: wavefront w takes records
+// [w qpw, (w+1) qpw).  Each wavefront streams its records through a ring of
+// D register slots (codes, (d, m) words and the record's 128 activations per
+// row), so D records per strip are in flight; nothing waits on another
+// wavefront until the end, where the W partial sums are added in wavefront
+// order through LDS.  No second launch and no workspace.
+//   * activations: each lane loads 16 bytes (4 values of one row) of the
+//     record, splits them into the three bf16 terms and writes the terms to
+//     the wavefront's own LDS area; a lane of the A operand (row 4m+t,
+//     k-octet g) then reads its 8 terms of each block with one ds_read_b128.
+//     LDS operations of one wavefront complete in order, so no barrier.
+//   * m term: the lanes that split the activations also add them up per
+//     block (own values, then a DPP reduction inside 8 or 16 lanes); one
+//     lane per (row, block) writes the sum to the wavefront's LDS area and
+//     every output lane (row m, column c) reads its row's four sums with one
+//     ds_read_b128, so y += d (sum of the three d-term outputs) + m (sum).
+//   * records past the wavefront's range read its last record for codes and
+//     activations and the header's zero tail for (d, m): they add nothing.
+//     Blocks past K in the last record have d = m = 0 in the packed layout;
+//     their activation reads are clamped inside the row.
+template <int W, int C, int D, int MR, bool XVEC>
+__global__ __launch_bounds__(W * 64) void k_q4_gemv(Q4Params p) {
+    static_assert(MR == 1 || MR == 2 || MR == 4, "activation rows per launch");
+    // per wavefront: terms of the current record, [row][term][k] bf16, a
+    // term plane padded to 160 elements (320 bytes) so that the (term,
+    // k-octet) pieces one operand read touches sit in distinct bank groups.
+    // A-operand lanes of absent rows read row M - 1 and those of the unused
+    // fourth term read term 2: an MFMA output row depends on its own A row
+    // only, and outputs of absent rows and of the fourth term are never used.
+    constexpr int TP = 160;
+    __shared__ __attribute__((aligned(16))) uint16_t sT[W][4][3][TP];
+    __shared__ __attribute__((aligned(16))) float sXS[W][4][4];  // block sums [row][block] of the record
+    __shared__ float sRed[W][C][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int strip0 = blockIdx.x * C;
+    const int q0 = min(wave * p.qps, p.NQ);
+    const int q1 = min(q0 + p.qps, p.NQ);
+    const uint8_t *hdr = p.recs;
+    const uint8_t *recs = hdr + kHeaderBytes;
+    const int M = p.M;  // 1 .. MR
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int groups = (p.NS + SPG - 1) / SPG;
-    const int sg = blockIdx.x % groups;
-    const int job = blockIdx.x / groups;
-    const int nrows = p.M;
-    const int q0 = job * p.qps;
-    const int q1 = min(p.NQ, q0 + p.qps);
-    const int nchunk = (q1 - q0 + QC - 1) / QC;
-    const int nstaged = (nchunk + NSET - 1) / NSET * NSET;  // chunks run, padding included
+    // A operand lane: row 4 am + at of the tile, k-octet ag
+    const int am = (lane & 15) >> 2, at = lane & 3, ag = lane >> 4;
+    const int a_rd = ((am < M ? am : M - 1) * 3 + (at < 3 ? at : 2)) * TP + 8 * ag;  // element offset in sT[wave]
+    // activation loads: XL values of row xrow at k = xk of the record
+    constexpr int XL = MR == 1 ? 2 : 4;         // values per lane per load
+    constexpr int XH = MR == 4 ? 2 : 1;         // loads per lane per record
+    const int xk = MR == 1 ? 2 * lane : 4 * (lane & 31);
+
+    v4i wc[D][C], wd[D][C];
+    float xv[D][XH][XL];
+    auto gload = [&](auto S, int q) {
+        constexpr int s = decltype(S)::value;
+        const bool pad = q >= q1;
+        const int qq = min(q, q1 - 1);
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const int strip = min(strip0 + j, p.NS - 1);
+            const uint8_t *rec = recs + ((int64_t)strip * p.NQ + qq) * kQ4RecBytes;
+            wc[s][j] = *(const v4i *)(rec + (uint32_t)lane * 16u);
+            wd[s][j] = *(const v4i *)(pad ? hdr + kHeaderBytes - 16 : rec + 1024 + (uint32_t)(lane & 15) * 16u);
+        }
+        const int k = min(qq * 128 + xk, p.K - XL);
+#pragma unroll
+        for (int h = 0; h < XH; ++h) {
+            const int row = MR == 1 ? 0 : min(2 * h + (lane >> 5), M - 1);
+            const float *src = p.X + (int64_t)row * p.ldx + k;
+            if (XVEC && XL == 4) {
+                const v4f v = *(const v4f *)src;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xv[s][h][e] = v[e];
+            } else if (XVEC) {
+                const v2f v = *(const v2f *)src;
+                xv[s][h][0] = v[0];
+                xv[s][h][1] = v[1];
+            } else {
+#pragma unroll
+                for (int e = 0; e < XL; ++e) xv[s][h][e] = src[e];
+            }
+        }
+    };
+
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    // lanes of one (row, block) of the activation loads: 16 at one row (2
+    // values each), 8 otherwise (4 values each); the last of them holds the sum
+    constexpr int XG = MR == 1 ? 16 : 8;
+    float y[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) y[j] = 0.0f;
+
+    // record in slot S: stage its activation terms, then 4 blocks x (C + 1) MFMAs
+    auto record = [&](auto S) {
+        constexpr int s = decltype(S)::value;
+#pragma unroll
+        for (int h = 0; h < XH; ++h) {
+            uint32_t t[3][XL / 2];
+#pragma unroll
+            for (int e = 0; e < XL; e += 2) {
+                const float x0 = xv[s][h][e], x1 = xv[s][h][e + 1];
+                const uint32_t t0 = pk_bf16(x0, x1);
+                const float r0 = x0 - bf16_lo_f32(t0), r1 = x1 - bf16_hi_f32(t0);
+                const uint32_t t1 = pk_bf16(r0, r1);
+                t[0][e >> 1] = t0;
+                t[1][e >> 1] = t1;
+                t[2][e >> 1] = pk_bf16(r0 - bf16_lo_f32(t1), r1 - bf16_hi_f32(t1));
+            }
+            const int row = MR == 1 ? 0 : 2 * h + (lane >> 5);
+#pragma unroll
+            for (int tt = 0; tt < 3; ++tt) {
+                if (XL == 4)
+                    *(v2i *)(&sT[wave][row][tt][xk]) = v2i{(int)t[tt][0], (int)t[tt][1]};
+                else
+                    *(uint32_t *)(&sT[wave][row][tt][xk]) = t[tt][0];
+            }
+            float bs = xv[s][h][0];
+#pragma unroll
+            for (int e = 1; e < XL; ++e) bs += xv[s][h][e];
+            // inclusive prefix sums inside each row of 16 lanes (row_shr 1, 2, 4, 8)
+            bs += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bs), 0x111, 0xF, 0xF, true));
+            bs += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bs), 0x112, 0xF, 0xF, true));
+            bs += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bs), 0x114, 0xF, 0xF, true));
+            if (XG == 16)
+                bs += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bs), 0x118, 0xF, 0xF, true));
+            if ((lane & (XG - 1)) == XG - 1) sXS[wave][row][(xk >> 5) & 3] = bs;
+        }
+        const v4f xs4 = *(const v4f *)(&sXS[wave][lane >> 4][0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v8bf a = *(const v8bf *)(&sT[wave][0][0][0] + a_rd + 32 * i);
+            const float xs = xs4[i];
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, decode8((uint32_t)wc[s][j][i]), zero, 0, 0, 0);
+                const uint32_t dm = (uint32_t)wd[s][j][i];
+                y[j] = fmaf(bf16_lo_f32(dm), (acc[0] + acc[1]) + acc[2], y[j]);
+                y[j] = fmaf(bf16_hi_f32(dm), xs, y[j]);
+            }
+            // pin the sums here: otherwise the compiler sinks every block's
+            // update to the end of the loop and keeps all MFMA results alive
+#pragma unroll
+            for (int j = 0; j < C; ++j) asm volatile("" : "+v"(y[j]));
+        }
+    };
+
+    // steps of D records; the last step's records past the range are the
+    // zero-weight padding described above (no load sits in a branch, so the
+    // ring stays in flight)
+    if (q0 < q1) {
+        static_for<D>([&](auto S) { gload(S, q0 + decltype(S)::value); });
+        for (int q = q0; q < q1; q += D) {
+            static_for<D>([&](auto S) {
+                record(S);
+                gload(S, q + decltype(S)::value + D);
+                // keep each record's work in its own step (hoisting the next
+                // records' activation work ahead costs registers)
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+    }
+
+    // y of lane (row lane >> 4, column lane & 15) of each strip; rows past M hold zeros
+#pragma unroll
+    for (int j = 0; j < C; ++j) sRed[wave][j][lane] = y[j];
+    __syncthreads();
+    for (int o = threadIdx.x; o < C * 64; o += W * 64) {
+        const int j = o >> 6, l = o & 63;
+        const int m = l >> 4;
+        const int n = (strip0 + j) * 16 + (l & 15);
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) v += sRed[w][j][l];
+        if (m < M && n < p.N && strip0 + j < p.NS) p.Y[(int64_t)m * p.ldy + n] = v;
+    }
+}
+
+// M = 1 with at most QMAX records per wavefront: the same split of the k
+// range as k_q4_gemv, but each wavefront stages the activation terms and
+// block sums of its whole k range (at most 128 QMAX values) once; their loads
+// go out first (they come from L2, ahead of the records' HBM traffic).  A
+// record's remaining work is per block one LDS operand read, the code decode,
+// one MFMA and two fma.  Every record of the wavefront is loaded at the start,
+// so a wavefront whose data comes late has little left to do; the fewer
+// records per wavefront, the shorter that tail (4 where the planner can).
+template <int W, int QMAX, bool XVEC>
+__global__ __launch_bounds__(W * 64) void k_q4_gemv1(Q4Params p) {
+    static_assert(QMAX == 4 || QMAX == 8, "records per wavefront");
+    constexpr int D = QMAX;
+    constexpr int XPL = QMAX * 128 / 64;  // activation values per lane
+    // term planes of the range padded by 64 bytes (a plane is 256 QMAX bytes,
+    // so the stride is 64 mod 256): the (term, k-octet) pieces of one operand
+    // read sit in distinct bank groups.  Lanes of the unused fourth term read
+    // term 2 and rows 1..3 of the tile repeat row 0 (outputs never used).
+    constexpr int TPL = QMAX * 128 + 32;
+    __shared__ __attribute__((aligned(16))) uint16_t sT[W][3][TPL];
+    __shared__ __attribute__((aligned(16))) float sXS[W][QMAX * 4];  // block sums of the range
+    __shared__ float sRed[W][16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int strip = min((int)blockIdx.x, p.NS - 1);
+    const int q0 = min(wave * p.qps, p.NQ);
+    const int q1 = min(q0 + p.qps, p.NQ);
     const uint8_t *hdr = p.recs;
     const uint8_t *recs = hdr + kHeaderBytes;
 
-    // ---- activation terms of the whole k range.  Pieces (row, block,
-    // k-octet), k-octet fastest; blocks past the matrix or the range are
-    // staged as zeros.  The activation loads go out first, then the first
-    // records' loads, then the split (which waits for the activations only).
-    constexpr int PPT = (4 * BMAX * 4 + NT - 1) / NT;
-    const int total = nrows * nstaged * 4 * QC * 4;
-    float xr[PPT][8];
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-        const int idx = tid + i * NT;
-        const int pc = min(idx, total - 1);
-        const int g = pc & 3;
-        const int m = (pc >> 2) % nrows;
-        const int b = (pc >> 2) / nrows;
-        const int gb = min(q0 * 4 + b, p.NB - 1);
-        const float *src = p.X + (int64_t)m * p.ldx + gb * 32 + g * 8;
+    v4i wc[D], wd[D];
+    auto gload = [&](auto S, int q) {
+        constexpr int s = decltype(S)::value;
+        const bool pad = q >= q1;
+        const int qq = min(q, q1 - 1);
+        const uint8_t *rec = recs + ((int64_t)strip * p.NQ + qq) * kQ4RecBytes;
+        wc[s] = *(const v4i *)(rec + (uint32_t)lane * 16u);
+        wd[s] = *(const v4i *)(pad ? hdr + kHeaderBytes - 16 : rec + 1024 + (uint32_t)(lane & 15) * 16u);
+    };
+    float y = 0.0f;
+    if (q0 < q1) {
+        // activations k0 + XPL L .. + XPL - 1 of the range (clamped inside the
+        // row: values past the range or past K meet zero-weight records or blocks)
+        const int k = min(q0 * 128 + XPL * lane, p.K - XPL);
+        float x[XPL];
         if (XVEC) {
-            const v4f lo = *(const v4f *)src;
-            const v4f hi = *(const v4f *)(src + 4);
-            xr[i][0] = lo[0]; xr[i][1] = lo[1]; xr[i][2] = lo[2]; xr[i][3] = lo[3];
-            xr[i][4] = hi[0]; xr[i][5] = hi[1]; xr[i][6] = hi[2]; xr[i][7] = hi[3];
+#pragma unroll
+            for (int u = 0; u < XPL / 4; ++u) {
+                const v4f v = *(const v4f *)(p.X + k + 4 * u);
+                x[4 * u] = v[0]; x[4 * u + 1] = v[1]; x[4 * u + 2] = v[2]; x[4 * u + 3] = v[3];
+            }
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xr[i][e] = src[e];
+            for (int e = 0; e < XPL; ++e) x[e] = p.X[k + e];
         }
-    }
-
-    const int strip_base = sg * SPG + wave * C;
-    v4i bc[NSET][QC][C], bs[NSET][QC][C];
-    auto gload_rec = [&](int quad, v4i (&dc)[C], v4i (&ds)[C]) {
-        const int qq = min(quad, q1 - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<D>([&](auto S) { gload(S, q0 + decltype(S)::value); });
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t t[3][XPL / 2];
+        float bs = 0.0f;
 #pragma unroll
-        for (int j = 0; j < C; ++j) {
-            const int strip = min(strip_base + j, p.NS - 1);
-            const uint8_t *rec = recs + ((int64_t)strip * p.NQ + qq) * kQ4RecBytes;
-            const uint8_t *dmp = quad < q1 ? rec + 1024 + (uint32_t)(lane & 15) * 16u : hdr + kHeaderBytes - 16;
-            dc[j] = *(const v4i *)(rec + (uint32_t)lane * 16u);
-            ds[j] = *(const v4i *)dmp;
-        }
-    };
-#pragma unroll
-    for (int st = 0; st < NSET; ++st)
-#pragma unroll
-        for (int q = 0; q < QC; ++q) gload_rec(q0 + st * QC + q, bc[st][q], bs[st][q]);
-
-    for (int o = tid * 16; o < nstaged * 1024; o += NT * 16) *(v4i *)(&sXM[0][0] + o) = v4i{0, 0, 0, 0};
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-        // wave-uniform: waves whose pieces are all past the last one skip
-        if (i * NT + wave * 64 >= total) continue;
-        const int idx = tid + i * NT;
-        const int pc = min(idx, total - 1);
-        const int g = pc & 3;
-        const int m = (pc >> 2) % nrows;
-        const int b = (pc >> 2) / nrows;
-        const bool ok = idx < total && q0 * 4 + b < p.NB && b < (q1 - q0) * 4;
-        float bsum = 0.0f;
-        uint32_t w[3][4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            const float x0 = ok ? xr[i][e] : 0.0f;
-            const float x1 = ok ? xr[i][e + 1] : 0.0f;
-            bsum += x0;
-            bsum += x1;
+        for (int e = 0; e < XPL; e += 2) {
+            const float x0 = x[e], x1 = x[e + 1];
+            bs += x0;
+            bs += x1;
             const uint32_t t0 = pk_bf16(x0, x1);
             const float r0 = x0 - bf16_lo_f32(t0), r1 = x1 - bf16_hi_f32(t0);
             const uint32_t t1 = pk_bf16(r0, r1);
-            const uint32_t t2 = pk_bf16(r0 - bf16_lo_f32(t1), r1 - bf16_hi_f32(t1));
-            w[0][e >> 1] = t0;
-            w[1][e >> 1] = t1;
-            w[2][e >> 1] = t2;
+            t[0][e >> 1] = t0;
+            t[1][e >> 1] = t1;
+            t[2][e >> 1] = pk_bf16(r0 - bf16_lo_f32(t1), r1 - bf16_hi_f32(t1));
         }
-        // the four k-octets of one (row, block) sit in four adjacent lanes
-        bsum += __shfl_xor(bsum, 1);
-        bsum += __shfl_xor(bsum, 2);
-        if (idx < total) {
 #pragma unroll
-            for (int t = 0; t < 3; ++t)
-                *(v4i *)(&sA[b][a_slot(4 * m + t, g) * 16]) = v4i{(int)w[t][0], (int)w[t][1], (int)w[t][2], (int)w[t][3]};
-            if (g == 0) {
-                const uint32_t s0 = pk_bf16(bsum, 0.0f);
-                const float sr = bsum - bf16_lo_f32(s0);
-                const uint32_t s1 = pk_bf16(sr, 0.0f);
-                const uint32_t s2 = pk_bf16(sr - bf16_lo_f32(s1), 0.0f);
-                uint8_t *xm = &sXM[b >> 3][m * 64 + (b & 7) * 2];
-                *(uint16_t *)(xm) = (uint16_t)s0;
-                *(uint16_t *)(xm + 16) = (uint16_t)s1;
-                *(uint16_t *)(xm + 32) = (uint16_t)s2;
+        for (int tt = 0; tt < 3; ++tt)
+#pragma unroll
+            for (int u = 0; u < XPL / 8; ++u)
+                *(v4i *)(&sT[wave][tt][XPL * lane + 8 * u]) =
+                    v4i{(int)t[tt][4 * u], (int)t[tt][4 * u + 1], (int)t[tt][4 * u + 2], (int)t[tt][4 * u + 3]};
+        // a block (32 values) is 32 / XPL lanes: the last of them holds the sum
+        bs += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bs), 0x111, 0xF, 0xF, true));
+        if (XPL == 8)
+            bs += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bs), 0x112, 0xF, 0xF, true));
+        constexpr int LPB = 32 / XPL;
+        if ((lane & (LPB - 1)) == LPB - 1) sXS[wave][lane / LPB] = bs;
+
+        // A operand lane: term at (<= 2) of row 0, k-octet ag
+        const int at = lane & 3, ag = lane >> 4;
+        const int a_rd = (at < 3 ? at : 2) * TPL + 8 * ag;
+        auto record = [&](auto S, int qi) {
+            constexpr int s = decltype(S)::value;
+            const v4f xs4 = *(const v4f *)(&sXS[wave][4 * qi]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const v8bf a = *(const v8bf *)(&sT[wave][0][0] + a_rd + qi * 128 + 32 * i);
+                const v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, decode8((uint32_t)wc[s][i]),
+                                                                       v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                const uint32_t dm = (uint32_t)wd[s][i];
+                y = fmaf(bf16_lo_f32(dm), (acc[0] + acc[1]) + acc[2], y);
+                y = fmaf(bf16_hi_f32(dm), xs4[i], y);
+                asm volatile("" : "+v"(y));
             }
-        }
+        };
+        static_for<D>([&](auto S) { record(S, decltype(S)::value); });
     }
+
+    // lanes 0..15 hold the columns (row 0 of the tile's output rows 0..3)
+    if (lane < 16) sRed[wave][lane] = y;
     __syncthreads();
-
-    // ---- stream the records
-    float acc_y[C];
-    v4f acc_m[C];
+    if (threadIdx.x < 16) {
+        float v = 0.0f;
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-        acc_y[j] = 0.0f;
-        acc_m[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    const int a_off = a_slot(lane & 15, lane >> 4) * 16;
-    auto chunk = [&](int c, auto S_) {
-        constexpr int S = decltype(S_)::value;
-        uint32_t mw[C][4];
-        v8bf a[2];
-        a[0] = *(const v8bf *)(&sA[c * 4 * QC][a_off]);
-#pragma unroll
-        for (int bl = 0; bl < 4 * QC; ++bl) {
-            const int q = bl >> 2, i = bl & 3;
-            if (bl + 1 < 4 * QC) a[(bl + 1) & 1] = *(const v8bf *)(&sA[c * 4 * QC + bl + 1][a_off]);
-#pragma unroll
-            for (int j = 0; j < C; ++j) {
-                const v8bf bop = decode8((uint32_t)bc[S][q][j][i]);
-                const float d = bf16_lo_f32((uint32_t)bs[S][q][j][i]);
-                v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[bl & 1], bop, acc, 0, 0, 0);
-                acc_y[j] = fmaf(d, acc[0] + acc[1] + acc[2], acc_y[j]);
-            }
-#pragma unroll
-            for (int j = 0; j < C; ++j) asm volatile("" : "+v"(acc_y[j]));
-            if (i == 3) {
-#pragma unroll
-                for (int j = 0; j < C; ++j) {
-                    mw[j][2 * q] = __builtin_amdgcn_perm((uint32_t)bs[S][q][j][1], (uint32_t)bs[S][q][j][0], 0x07060302u);
-                    mw[j][2 * q + 1] = __builtin_amdgcn_perm((uint32_t)bs[S][q][j][3], (uint32_t)bs[S][q][j][2], 0x07060302u);
-                }
-                gload_rec(q0 + (c + NSET) * QC + q, bc[S][q], bs[S][q]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const v8bf xm = *(const v8bf *)(&sXM[c][lane * 16]);
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-            const v8bf mop = __builtin_bit_cast(v8bf, v4i{(int)mw[j][0], (int)mw[j][1], (int)mw[j][2], (int)mw[j][3]});
-            acc_m[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, mop, acc_m[j], 0, 0, 0);
-        }
-    };
-    if (NSET == 1) {
-        for (int c = 0; c < nchunk; ++c) chunk(c, ic<0>{});
-    } else {
-        // pairs of chunks; an odd count ends with a chunk past the range
-        // (d = m = 0, zero activations)
-        for (int c = 0; c < nchunk; c += 2) {
-            chunk(c, ic<0>{});
-            chunk(c + 1, ic<NSET - 1>{});
-        }
-    }
-
-    const int m = lane >> 4;
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-        const int n = (strip_base + j) * 16 + (lane & 15);
-        if (m < nrows && n < p.N) {
-            const float val = acc_y[j] + ((acc_m[j][0] + acc_m[j][1]) + acc_m[j][2]);
-            if (p.S == 1)
-                p.Y[(int64_t)m * p.ldy + n] = val;
-            else
-                p.part[((int64_t)job * p.M + m) * p.N + n] = val;
-        }
+        for (int w = 0; w < W; ++w) v += sRed[w][threadIdx.x];
+        const int n = strip * 16 + (int)threadIdx.x;
+        if ((int)blockIdx.x < p.NS && n < p.N) p.Y[n] = v;
     }
 }
 
@@ -720,18 +827,57 @@ hipError_t launch_q4_repack(const uint8_t *blocks, const Q4Layout &L, uint8_t *p
     return hipGetLastError();
 }
 
-hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int64_t grid, hipStream_t s,
+hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t grid, hipStream_t s,
                            const char **variant) {
     const dim3 g((unsigned)grid), b(512);
     if (mt == 0) {
-        // k_q4_gemv<WAVES, C, QMAX, ...>: the planner's groups, splits and
-        // qps assume 4 wavefronts x 2 strips and at most 8 records per split
+        // k_q4_gemv<W, 1, D, MR, XVEC>: one strip per workgroup, p.qps records per wavefront
         *variant = "q4_gemv_m4";
-        const dim3 b4(256);
-        if (p.x_vec)
-            hipLaunchKernelGGL((k_q4_gemv<4, 2, 8, 2, 4, true>), g, b4, 0, s, p);
-        else
-            hipLaunchKernelGGL((k_q4_gemv<4, 2, 8, 2, 4, false>), g, b4, 0, s, p);
+        const dim3 bw(waves * 64);
+        const int mr = p.M == 1 ? 1 : p.M == 2 ? 2 : 4;
+        bool ok = true;
+        auto go = [&](auto W_, auto MR_) {
+            constexpr int Wv = decltype(W_)::value, MRv = decltype(MR_)::value;
+            // all of a wavefront's records in flight at once (8 slots; 4 at
+            // four rows, where each slot also holds 8 activation values)
+            constexpr int Dv = MRv == 4 ? 4 : 8;
+            if (p.x_vec)
+                hipLaunchKernelGGL((k_q4_gemv<Wv, 1, Dv, MRv, true>), g, bw, 0, s, p);
+            else
+                hipLaunchKernelGGL((k_q4_gemv<Wv, 1, Dv, MRv, false>), g, bw, 0, s, p);
+        };
+        auto by_m = [&](auto W_) {
+            if (mr == 1) go(W_, ic<1>{});
+            else if (mr == 2) go(W_, ic<2>{});
+            else go(W_, ic<4>{});
+        };
+        // one row and at most 8 records per wavefront: activations staged once
+        auto go1 = [&](auto W_) {
+            constexpr int Wv = decltype(W_)::value;
+            *variant = "q4_gemv_m1";
+            if (p.qps <= 4) {
+                if (p.x_vec)
+                    hipLaunchKernelGGL((k_q4_gemv1<Wv, 4, true>), g, bw, 0, s, p);
+                else
+                    hipLaunchKernelGGL((k_q4_gemv1<Wv, 4, false>), g, bw, 0, s, p);
+            } else {
+                if (p.x_vec)
+                    hipLaunchKernelGGL((k_q4_gemv1<Wv, 8, true>), g, bw, 0, s, p);
+                else
+                    hipLaunchKernelGGL((k_q4_gemv1<Wv, 8, false>), g, bw, 0, s, p);
+            }
+        };
+        const bool one = p.M == 1 && p.qps <= 8;
+        if (cs != 1) ok = false;
+        else if (one && waves == 4) go1(ic<4>{});
+        else if (one && waves == 8) go1(ic<8>{});
+        else if (one && waves == 16) go1(ic<16>{});
+        else if (waves == 4) by_m(ic<4>{});
+        else if (waves == 8) by_m(ic<8>{});
+        else if (waves == 16) by_m(ic<16>{});
+        else ok = false;
+        if (!ok) return hipErrorInvalidValue;
+        return hipGetLastError();
     } else if (mt == 1 && waves == 8) {
         *variant = "q4_mm_m16";
         if (p.x_vec)

@@ -182,7 +182,7 @@ struct Q4Params {
 };
 
 struct Q4Plan {
-    int mt, waves, S, qps;
+    int mt, waves, cs, S, qps;  // cs: strips per workgroup of the M <= 4 kernel
     int64_t grid, rows_per_launch;
     int64_t ws_part_off, ws_bytes;
 };
@@ -198,7 +198,7 @@ struct MoePlan {
 MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N);
 
 hipError_t launch_q4_repack(const uint8_t *blocks, const Q4Layout &L, uint8_t *packed, hipStream_t s);
-hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int64_t grid, hipStream_t s,
+hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t grid, hipStream_t s,
                            const char **variant);
 hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, int64_t n_used, int64_t E,
                             int rpc, int32_t *sorted, int32_t *chunk_info, int32_t *nchunks, int32_t *err,
