@@ -755,23 +755,28 @@ __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ p
 
 // ------------------------------------------------------ MoE routing sort ---
 // One workgroup.  Counts the used (token, slot) pairs per expert (ids read
-// through the row stride), scans the counts, scatters pair ids into
-// per-expert runs and writes the chunk table (expert, first row, rows) with
-// at most `rpc` rows per chunk.  Pairs whose id lies outside [0, E) are left
-// out (their outputs are not written) and flagged in *err.  Rows inside an
-// expert's run may come in any order: each output row depends on its own
-// activation row only.
+// once, through the row stride, and kept in registers), scans the counts,
+// scatters pair ids into per-expert runs and writes the chunk table (expert,
+// first row, rows) with at most `rpc` rows per chunk.  Pairs whose id lies
+// outside [0, E) are left out (their outputs are not written) and flagged in
+// *err.  Rows inside an expert's run may come in any order: each output row
+// depends on its own activation row only.  The scan is parallel: each thread
+// sums a run of consecutive experts, a wavefront scan and a scan of the
+// wavefront totals give every run its offsets.
+constexpr int kRoutePairsPerThread = 8;  // pairs held in registers per pass
 __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ ids, int64_t ids_stride, int T,
                                                     int n_used, int E, int rpc, int32_t *__restrict__ sorted,
                                                     int32_t *__restrict__ chunk_info, int32_t *__restrict__ nchunks,
                                                     int32_t *__restrict__ err) {
     extern __shared__ int32_t sh[];
-    int32_t *cnt = sh;
-    int32_t *off = sh + E;
-    int32_t *coff = sh + 2 * E;
-    int32_t *fill = sh + 3 * E;
+    int32_t *cnt = sh;           // [E] pairs per expert
+    int32_t *off = sh + E;       // [E] first sorted row of the expert
+    int32_t *coff = sh + 2 * E;  // [E] first chunk of the expert
+    int32_t *fill = sh + 3 * E;  // [E] rows scattered so far
     __shared__ int s_bad;
+    __shared__ int s_wsum[16][2];
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int P = T * n_used;
     for (int e = tid; e < E; e += 1024) {
         cnt[e] = 0;
@@ -779,31 +784,79 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
     }
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    for (int pr = tid; pr < P; pr += 1024) {
+    // ---- ids of the first pass in registers; larger P loops (re-reading)
+    int ev[kRoutePairsPerThread];
+#pragma unroll
+    for (int u = 0; u < kRoutePairsPerThread; ++u) {
+        const int pr = tid + 1024 * u;
+        ev[u] = pr < P ? ids[(int64_t)(pr / n_used) * ids_stride + pr % n_used] : -1;
+    }
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < kRoutePairsPerThread; ++u) {
+        const int pr = tid + 1024 * u;
+        if (pr < P) {
+            if (ev[u] >= 0 && ev[u] < E) atomicAdd(&cnt[ev[u]], 1);
+            else bad = true;
+        }
+    }
+    for (int pr = tid + 1024 * kRoutePairsPerThread; pr < P; pr += 1024) {
         const int e = ids[(int64_t)(pr / n_used) * ids_stride + pr % n_used];
-        if (e >= 0 && e < E)
-            atomicAdd(&cnt[e], 1);
-        else
-            s_bad = 1;
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+        else bad = true;
+    }
+    if (bad) s_bad = 1;
+    __syncthreads();
+    // ---- scan: thread t owns experts [t EPT, (t+1) EPT)
+    const int EPT = (E + 1023) / 1024;
+    const int e0 = min(tid * EPT, E), e1 = min(e0 + EPT, E);
+    int lc = 0, lch = 0;
+    for (int e = e0; e < e1; ++e) {
+        lc += cnt[e];
+        lch += (cnt[e] + rpc - 1) / rpc;
+    }
+    int ic = lc, ich = lch;  // inclusive wavefront scan
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int a = __shfl_up(ic, d), b = __shfl_up(ich, d);
+        if (lane >= d) {
+            ic += a;
+            ich += b;
+        }
+    }
+    if (lane == 63) {
+        s_wsum[wave][0] = ic;
+        s_wsum[wave][1] = ich;
     }
     __syncthreads();
-    if (tid == 0) {
-        int o = 0, co = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = o;
-            coff[e] = co;
-            o += cnt[e];
-            co += (cnt[e] + rpc - 1) / rpc;
-        }
-        *nchunks = co;
+    int bc = 0, bch = 0;  // totals of the earlier wavefronts
+    for (int w = 0; w < wave; ++w) {
+        bc += s_wsum[w][0];
+        bch += s_wsum[w][1];
+    }
+    int o = bc + ic - lc, co = bch + ich - lch;
+    for (int e = e0; e < e1; ++e) {
+        off[e] = o;
+        coff[e] = co;
+        o += cnt[e];
+        co += (cnt[e] + rpc - 1) / rpc;
+    }
+    if (tid == 1023) {
+        *nchunks = bch + ich;
         *err = s_bad;
     }
     __syncthreads();
-    for (int pr = tid; pr < P; pr += 1024) {
+    // ---- scatter and chunk table
+#pragma unroll
+    for (int u = 0; u < kRoutePairsPerThread; ++u) {
+        const int pr = tid + 1024 * u;
+        if (pr < P && ev[u] >= 0 && ev[u] < E) sorted[off[ev[u]] + atomicAdd(&fill[ev[u]], 1)] = pr;
+    }
+    for (int pr = tid + 1024 * kRoutePairsPerThread; pr < P; pr += 1024) {
         const int e = ids[(int64_t)(pr / n_used) * ids_stride + pr % n_used];
         if (e >= 0 && e < E) sorted[off[e] + atomicAdd(&fill[e], 1)] = pr;
     }
-    for (int e = tid; e < E; e += 1024) {
+    for (int e = e0; e < e1; ++e) {
         const int nc = (cnt[e] + rpc - 1) / rpc;
         for (int c = 0; c < nc; ++c) {
             const int idx = coff[e] + c;
