@@ -227,7 +227,8 @@ size_t qmm_q4_1_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * ldy >= N).  Codes are decoded inside the kernel and kept exact; the
  * relative Frobenius error against exact arithmetic is below 1e-5.
  * workspace: device, >= qmm_q4_1_matmul_workspace_bytes(M,K,N), zero-filled
- * before its first use (same counter-region rule as int8_gemm).
+ * before its first use (same counter-region rule as int8_gemm).  That size is
+ * 0 for M <= 4 (one launch, no partial sums), where workspace may be NULL.
  */
 qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx,
                        const void *Wpacked, int64_t N, float *Y, int64_t ldy,
