@@ -130,14 +130,12 @@ __global__ __launch_bounds__(256) void k_q4_repack(const uint8_t *__restrict__ b
 // takes its (d, m) from the last 16 bytes of the packed header, which are
 // zero, so it adds nothing.  XVEC: X and ldx allow aligned 16-byte loads.
 //
-// LDS layout of one 16-row A fragment (1 KiB): the 16-byte piece of (row r,
-// k-octet g) sits at slot 16 g + (r ^ f(g)), f = {0, 6, 10, 12}.  MFMA lane
-// L reads (r, g) = (L % 16, L / 16); the staging stores write (g, r) with g
-// fastest.  With this swizzle every 8 and every 16 consecutive lanes of
-// either access touch distinct 16-byte bank groups.
-__device__ __forceinline__ int a_slot(int r, int g) {
-    return g * 16 + (r ^ ((0xCA60 >> (4 * g)) & 15));
-}
+// LDS layout of one 16-row A fragment (1 KiB): in MFMA lane order, the
+// 16-byte piece of (row r, k-octet g) at slot 16 g + r, the slot lane 16 g + r
+// reads, and the staging stores fill consecutive slots from consecutive
+// threads.  Contiguous 16-byte-per-lane accesses measured free of LDS bank
+// conflicts; an XOR swizzle of the rows by k-octet (16 g + (r ^ f(g)),
+// f = {0, 6, 10, 12}) measured 2-way conflicted on every operand read.
 
 // Two floats -> packed bf16 pair (round to nearest even), and the pair's
 // residuals x - bf16(x), exact in fp32.
@@ -148,7 +146,7 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 __device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-template <int MT, int WAVES, int C, int QC, bool MOE, int MINW, bool XVEC>
+template <int MT, int WAVES, int C, int QC, bool MOE, int MINW, bool XVEC, int RS = 2, int XD = 1>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_mm(Q4Params p) {
     constexpr int NT = WAVES * 64;
     constexpr int ROWS = MT * 16;
@@ -160,9 +158,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     constexpr int PPT = (PIECES + NT - 1) / NT;
     // weight register sets.  QC >= 2: one set; each record's registers are
     // refilled with the next chunk's record right after their last use.
-    // QC == 1: two sets; chunk c loads chunk c + 1's records into the other
-    // set when it starts.
-    constexpr int NSET = QC >= 2 ? 1 : 2;
+    // QC == 1: RS sets; chunk c loads chunk c + RS - 1's records into the set
+    // chunk c - 1 used when it starts (RS - 1 chunks in flight).
+    constexpr int NSET = QC >= 2 ? 1 : RS;
+    static_assert(NSET == 1 || NSET == 2 || NSET == 4, "record sets");
+    // activation register sets: chunk c loads chunk c + XD's activations
+    // (XD > 1 needs the chunk loop unrolled by XD: one set per unrolled chunk)
+    static_assert(XD == 1 || XD == NSET, "activation sets follow the record sets");
     constexpr int ADB = MT == 1 ? 2 : 1;   // A fragment register sets
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][BPC][NF][MT][1024];
     // block sums as A fragments: row r, block bl at byte 16 r + 2 bl (k-octet
@@ -194,59 +196,64 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         q1 = min(p.NQ, q0 + p.qps);
     }
     const uint8_t *recs = hdr + kHeaderBytes;
+    const int ntile = (nrows + 15) >> 4;  // 16-row tiles holding rows (MFMAs of the others are skipped)
     if (tid < nrows) sRow[tid] = (int64_t)(MOE ? p.sorted[row0 + tid] / p.n_used : tid) * p.ldx;
     for (int o = tid * 16; o < (int)sizeof(sXM); o += NT * 16) *(v4i *)(&sXM[0][0][0][0] + o) = v4i{0, 0, 0, 0};
     __syncthreads();
 
-    // ---- activation staging.  Pieces of the existing rows only:
-    // piece -> (g = piece % 4, row = piece / 4 % nrows, block = piece / 4 / nrows).
-    const int active = nrows * BPC * 4;
+    // ---- activation staging.  piece -> (r = piece % 16, g = piece / 16 % 4,
+    // tile = piece / 64 % MT, block = piece / 64 / MT): a wavefront's 64
+    // pieces are one fragment, lane order.  Rows past nrows read row
+    // nrows - 1 and stage zeros (their MFMA output rows are never stored);
+    // wavefronts whose tile holds no rows skip the staging (wave-uniform).
     int pbl[PPT], pg[PPT], prow[PPT], pdst[PPT];
     int64_t psrc[PPT];
-    bool pok[PPT];
+    bool pok[PPT], pon[PPT];
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
         const int idx = tid + i * NT;
-        const int pc = min(idx, active - 1);
-        const int t = pc >> 2;
-        const int row = t % nrows;
+        const int pc = min(idx, PIECES - 1);
+        const int r = pc & 15, g = (pc >> 4) & 3, tile = (pc >> 6) % MT, blk = (pc >> 6) / MT;
+        const int row = tile * 16 + r;
         prow[i] = row;
-        pg[i] = pc & 3;
-        pbl[i] = t / nrows;
-        pok[i] = idx < active;
-        psrc[i] = sRow[row] + pg[i] * 8;
-        pdst[i] = (pbl[i] * 3 * MT + (row >> 4)) * 1024 + a_slot(row & 15, pg[i]) * 16;
+        pg[i] = g;
+        pbl[i] = blk;
+        pok[i] = idx < PIECES && row < nrows;
+        pon[i] = idx < PIECES && tile < ntile;
+        psrc[i] = sRow[min(row, nrows - 1)] + g * 8;
+        pdst[i] = (blk * 3 * MT + tile) * 1024 + (g * 16 + r) * 16;
     }
-    float xr[PPT][8];
-    bool xok[PPT];
-    auto gload_a = [&](int qc) {
+    float xr[XD][PPT][8];
+    bool xok[XD][PPT];
+    auto gload_a = [&](int qc, auto X_) {
+        constexpr int xs = decltype(X_)::value;
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const int b = qc * 4 + pbl[i];
-            xok[i] = pok[i] && b < p.NB;
+            xok[xs][i] = pok[i] && b < p.NB;
             const float *src = p.X + psrc[i] + min(b, p.NB - 1) * 32;
             if (XVEC) {
                 const v4f lo = *(const v4f *)src;
                 const v4f hi = *(const v4f *)(src + 4);
-                xr[i][0] = lo[0]; xr[i][1] = lo[1]; xr[i][2] = lo[2]; xr[i][3] = lo[3];
-                xr[i][4] = hi[0]; xr[i][5] = hi[1]; xr[i][6] = hi[2]; xr[i][7] = hi[3];
+                xr[xs][i][0] = lo[0]; xr[xs][i][1] = lo[1]; xr[xs][i][2] = lo[2]; xr[xs][i][3] = lo[3];
+                xr[xs][i][4] = hi[0]; xr[xs][i][5] = hi[1]; xr[xs][i][6] = hi[2]; xr[xs][i][7] = hi[3];
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) xr[i][e] = src[e];
+                for (int e = 0; e < 8; ++e) xr[xs][i][e] = src[e];
             }
         }
     };
-    auto sstore_a = [&](int buf) {
+    auto sstore_a = [&](int buf, auto X_) {
+        constexpr int xs = decltype(X_)::value;
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
-            // wave-uniform: waves whose pieces are all past the existing rows skip
-            if (i * NT + wave * 64 >= active) continue;
+            if (!pon[i]) continue;  // wave-uniform
             float bsum = 0.0f;
             uint32_t w[3][4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float x0 = xok[i] ? xr[i][e] : 0.0f;
-                const float x1 = xok[i] ? xr[i][e + 1] : 0.0f;
+                const float x0 = xok[xs][i] ? xr[xs][i][e] : 0.0f;
+                const float x1 = xok[xs][i] ? xr[xs][i][e + 1] : 0.0f;
                 bsum += x0;
                 bsum += x1;
                 const uint32_t t0 = pk_bf16(x0, x1);
@@ -257,10 +264,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                 w[1][e >> 1] = t1;
                 w[2][e >> 1] = t2;
             }
-            // the four k-octets of one (row, block) sit in four adjacent lanes
-            bsum += __shfl_xor(bsum, 1);
-            bsum += __shfl_xor(bsum, 2);
-            if (pok[i]) {
+            // the four k-octets of one (row, block) sit in lanes r, r+16, r+32, r+48
+            bsum += __shfl_xor(bsum, 16);
+            bsum += __shfl_xor(bsum, 32);
+            {
 #pragma unroll
                 for (int tt = 0; tt < 3; ++tt)
                     *(v4i *)(&sA[buf][0][0][0][0] + pdst[i] + tt * MT * 1024) =
@@ -305,22 +312,26 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
             acc_m[rt][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         }
 
-    const int a_off = a_slot(lane & 15, lane >> 4) * 16;
+    const int a_off = lane * 16;
     const int nchunk = (q1 - q0 + QC - 1) / QC;
 
-    // One chunk: c = chunk index, buf = its LDS buffer, S = its weight set.
-    // The next chunk's activations (and, with two sets, its records) are
-    // loaded first; the last chunk reloads its own activations (never used).
+    // One chunk: c = chunk index, buf = its LDS buffer, S = its weight set
+    // (and activation set when XD > 1).  Chunk c + XD's activations (clamped
+    // to the last chunk) and chunk c + NSET - 1's records are loaded first;
+    // chunk c + 1's activations are split into LDS at the end.
     auto chunk = [&](int c, int buf, auto S_) {
         constexpr int S = decltype(S_)::value;
-        const int qn = q0 + min(c + 1, nchunk - 1) * QC;
-        if (NSET == 2) {
-            // unclamped: the chunk past the range (odd count) gets d = m = 0
+        constexpr int XS = XD == 1 ? 0 : S;
+        const int qn = q0 + min(c + XD, nchunk - 1) * QC;
+        if (NSET >= 2) {
+            // unclamped: chunks past the range (the padding of the last
+            // unrolled step) get d = m = 0
+            constexpr int SN = (S + NSET - 1) % NSET;
 #pragma unroll
             for (int q = 0; q < QC; ++q)
-                gload_rec(q0 + (c + 1) * QC + q, bc[S ^ (NSET - 1)][q], bs[S ^ (NSET - 1)][q]);
+                gload_rec(q0 + (c + NSET - 1) * QC + q, bc[SN][q], bs[SN][q]);
         }
-        gload_a(qn);
+        gload_a(qn, ic<XS>{});
         v8bf a[ADB][MT][NF];
         auto lds_a = [&](int bl, v8bf (&ad)[MT][NF]) {
 #pragma unroll
@@ -351,6 +362,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                 const float d = bf16_lo_f32((uint32_t)bs[S][q][j][i]);
 #pragma unroll
                 for (int rt = 0; rt < MT; ++rt) {
+                    if (rt > 0 && ntile <= rt) continue;  // row tile without rows (wave-uniform)
                     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int t = 0; t < NF; ++t)
@@ -379,6 +391,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         }
 #pragma unroll
         for (int rt = 0; rt < MT; ++rt) {
+            if (rt > 0 && ntile <= rt) continue;
             v8bf xm[NF];
 #pragma unroll
             for (int t = 0; t < NF; ++t) xm[t] = *(const v8bf *)(&sXM[buf][t][rt][lane * 16]);
@@ -390,26 +403,30 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                     acc_m[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm[t], mop, acc_m[rt][j], 0, 0, 0);
             }
         }
-        sstore_a(buf ^ 1);
+        sstore_a(buf ^ 1, ic<(XS + 1) % XD>{});
         __syncthreads();
     };
 
     if (nchunk > 0) {
-        gload_a(q0);
+        static_for<XD>([&](auto X_) { gload_a(q0 + min(decltype(X_)::value, nchunk - 1) * QC, X_); });
+        static_for<(NSET > 1 ? NSET - 1 : 1)>([&](auto S_) {
+            constexpr int st = decltype(S_)::value;
 #pragma unroll
-        for (int q = 0; q < QC; ++q) gload_rec(q0 + q, bc[0][q], bs[0][q]);
-        sstore_a(0);
+            for (int q = 0; q < QC; ++q) gload_rec(q0 + st * QC + q, bc[st][q], bs[st][q]);
+        });
+        sstore_a(0, ic<0>{});
     }
     __syncthreads();
     if (NSET == 1) {
         for (int c = 0; c < nchunk; ++c) chunk(c, c & 1, ic<0>{});
     } else {
-        // pairs of chunks; an odd count ends with one chunk past the range,
-        // whose records have d = m = 0
-        for (int c = 0; c < nchunk; c += 2) {
-            chunk(c, 0, ic<0>{});
-            chunk(c + 1, 1, ic<NSET - 1>{});
-        }
+        // steps of NSET chunks; the last step's chunks past the range have
+        // records with d = m = 0
+        for (int c = 0; c < nchunk; c += NSET)
+            static_for<NSET>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                chunk(c + j, j & 1, J);
+            });
     }
 
 #pragma unroll
@@ -762,7 +779,9 @@ __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ p
 // *err.  Rows inside an expert's run may come in any order: each output row
 // depends on its own activation row only.  The scan is parallel: each thread
 // sums a run of consecutive experts, a wavefront scan and a scan of the
-// wavefront totals give every run its offsets.
+// wavefront totals give every run its offsets.  The chunk table lists the
+// full chunks (rpc rows) of every expert first and the partial ones after
+// them, so that workgroups dispatched last get the smaller jobs.
 constexpr int kRoutePairsPerThread = 8;  // pairs held in registers per pass
 __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ ids, int64_t ids_stride, int T,
                                                     int n_used, int E, int rpc, int32_t *__restrict__ sorted,
@@ -771,10 +790,9 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
     extern __shared__ int32_t sh[];
     int32_t *cnt = sh;           // [E] pairs per expert
     int32_t *off = sh + E;       // [E] first sorted row of the expert
-    int32_t *coff = sh + 2 * E;  // [E] first chunk of the expert
-    int32_t *fill = sh + 3 * E;  // [E] rows scattered so far
+    int32_t *fill = sh + 2 * E;  // [E] rows scattered so far
     __shared__ int s_bad;
-    __shared__ int s_wsum[16][2];
+    __shared__ int s_wsum[16][3];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int P = T * n_used;
@@ -807,46 +825,66 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
     }
     if (bad) s_bad = 1;
     __syncthreads();
-    // ---- scan: thread t owns experts [t EPT, (t+1) EPT)
+    // ---- scan: thread t owns experts [t EPT, (t+1) EPT); pairs, full chunks
+    // and partial chunks
     const int EPT = (E + 1023) / 1024;
     const int e0 = min(tid * EPT, E), e1 = min(e0 + EPT, E);
-    int lc = 0, lch = 0;
+    int lc = 0, lf = 0, lp = 0;
     for (int e = e0; e < e1; ++e) {
         lc += cnt[e];
-        lch += (cnt[e] + rpc - 1) / rpc;
+        lf += cnt[e] / rpc;
+        lp += cnt[e] % rpc != 0;
     }
-    int ic = lc, ich = lch;  // inclusive wavefront scan
+    int ic = lc, iF = lf, ip = lp;  // inclusive wavefront scans
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        const int a = __shfl_up(ic, d), b = __shfl_up(ich, d);
+        const int a = __shfl_up(ic, d), b = __shfl_up(iF, d), c = __shfl_up(ip, d);
         if (lane >= d) {
             ic += a;
-            ich += b;
+            iF += b;
+            ip += c;
         }
     }
     if (lane == 63) {
         s_wsum[wave][0] = ic;
-        s_wsum[wave][1] = ich;
+        s_wsum[wave][1] = iF;
+        s_wsum[wave][2] = ip;
     }
     __syncthreads();
-    int bc = 0, bch = 0;  // totals of the earlier wavefronts
-    for (int w = 0; w < wave; ++w) {
-        bc += s_wsum[w][0];
-        bch += s_wsum[w][1];
+    int bc = 0, bf = 0, bp = 0, nfull = 0, npart = 0;  // earlier wavefronts; all wavefronts
+    for (int w = 0; w < 16; ++w) {
+        if (w < wave) {
+            bc += s_wsum[w][0];
+            bf += s_wsum[w][1];
+            bp += s_wsum[w][2];
+        }
+        nfull += s_wsum[w][1];
+        npart += s_wsum[w][2];
     }
-    int o = bc + ic - lc, co = bch + ich - lch;
+    int o = bc + ic - lc, fo = bf + iF - lf, po = nfull + bp + ip - lp;
     for (int e = e0; e < e1; ++e) {
         off[e] = o;
-        coff[e] = co;
-        o += cnt[e];
-        co += (cnt[e] + rpc - 1) / rpc;
+        const int c = cnt[e], nf = c / rpc;
+        for (int k = 0; k < nf; ++k) {
+            chunk_info[(fo + k) * 3 + 0] = e;
+            chunk_info[(fo + k) * 3 + 1] = o + k * rpc;
+            chunk_info[(fo + k) * 3 + 2] = rpc;
+        }
+        fo += nf;
+        if (c % rpc != 0) {
+            chunk_info[po * 3 + 0] = e;
+            chunk_info[po * 3 + 1] = o + nf * rpc;
+            chunk_info[po * 3 + 2] = c % rpc;
+            ++po;
+        }
+        o += c;
     }
-    if (tid == 1023) {
-        *nchunks = bch + ich;
+    if (tid == 0) {
+        *nchunks = nfull + npart;
         *err = s_bad;
     }
     __syncthreads();
-    // ---- scatter and chunk table
+    // ---- scatter
 #pragma unroll
     for (int u = 0; u < kRoutePairsPerThread; ++u) {
         const int pr = tid + 1024 * u;
@@ -855,15 +893,6 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
     for (int pr = tid + 1024 * kRoutePairsPerThread; pr < P; pr += 1024) {
         const int e = ids[(int64_t)(pr / n_used) * ids_stride + pr % n_used];
         if (e >= 0 && e < E) sorted[off[e] + atomicAdd(&fill[e], 1)] = pr;
-    }
-    for (int e = e0; e < e1; ++e) {
-        const int nc = (cnt[e] + rpc - 1) / rpc;
-        for (int c = 0; c < nc; ++c) {
-            const int idx = coff[e] + c;
-            chunk_info[idx * 3 + 0] = e;
-            chunk_info[idx * 3 + 1] = off[e] + c * rpc;
-            chunk_info[idx * 3 + 2] = min(rpc, cnt[e] - c * rpc);
-        }
     }
 }
 
@@ -957,7 +986,7 @@ hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t
 hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, int64_t n_used, int64_t E,
                             int rpc, int32_t *sorted, int32_t *chunk_info, int32_t *nchunks, int32_t *err,
                             hipStream_t s) {
-    const size_t shmem = (size_t)E * 4 * sizeof(int32_t);
+    const size_t shmem = (size_t)E * 3 * sizeof(int32_t);
     hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), shmem, s, ids, ids_stride, (int)T, (int)n_used, (int)E,
                        rpc, sorted, chunk_info, nchunks, err);
     return hipGetLastError();
