@@ -85,6 +85,45 @@ def test_q4_matmul_small(q, orc, M, K, N):
     _matmul_case(q, orc, M, K, N, seed=M * 7 + K + N, small=True, zero_cols=(3,), zero_scale_blocks=True)
 
 
+def test_q4_matmul_one_row_paths(q, orc):
+    """M = 1: the one-launch kernel (aligned and unaligned activations, bitwise
+    repeatable), its fallback when a wavefront would hold more than 8 records,
+    and M = 4 at a ragged shape."""
+    import torch
+    K, N = 4096, 96
+    blocks = _blocks(K, N, seed=11)
+    p = _repack(q, blocks, K, N)
+    X = wl.q4_activations(1, K, seed_index=11)
+    ref = orc.q4_1_matmul(X, blocks, K, N)
+    a = to_np(q.q4_1_matmul(to_dev(X), p))
+    assert q.last_variant() == "q4_gemv_m1"
+    _check(a, ref)
+    b = to_np(q.q4_1_matmul(to_dev(X), p))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # activations one float past a 16-byte boundary: scalar loads
+    Xw = torch.zeros((1, K + 1), dtype=torch.float32, device=torch_dev())
+    Xw[:, 1:] = to_dev(X)
+    c = to_np(q.q4_1_matmul(Xw[:, 1:], p))
+    assert q.last_variant() == "q4_gemv_m1"
+    _check(c, ref)
+    # 160 records over 16 wavefronts: more than 8 each
+    K2, N2 = 20480, 40
+    blocks2 = _blocks(K2, N2, seed=12)
+    p2 = _repack(q, blocks2, K2, N2)
+    X2 = wl.q4_activations(1, K2, seed_index=12)
+    got2 = to_np(q.q4_1_matmul(to_dev(X2), p2))
+    assert q.last_variant() == "q4_gemv_m4"
+    _check(got2, orc.q4_1_matmul(X2, blocks2, K2, N2))
+    # four rows, K not a multiple of 128, N not a multiple of 16
+    K3, N3 = 160, 33
+    blocks3 = _blocks(K3, N3, seed=13, zero_cols=(3,), zero_scale_blocks=True)
+    p3 = _repack(q, blocks3, K3, N3)
+    X3 = wl.q4_activations(4, K3, seed_index=13)
+    got3 = to_np(q.q4_1_matmul(to_dev(X3), p3))
+    assert q.last_variant() == "q4_gemv_m4"
+    _check(got3, orc.q4_1_matmul(X3, blocks3, K3, N3), _abs_scale(orc, X3, blocks3, K3, N3))
+
+
 def test_q4_matmul_variants_and_determinism(q, orc):
     import torch
     blocks = _blocks(1024, 256, seed=5)
