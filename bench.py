@@ -6,9 +6,10 @@ Workload (one "step"): the seven Qwen3-0.6B projections of all 28 layers
 timed region: ~420 MiB of int8 codes, more than the 256 MiB Infinity Cache)
 run as decode at M = 1, 16 and 32 rows of fp32 N(0, 1) activations.  Every
 call is int8_gemm_dynamic: per-row amax/127 quantisation of the activations
-(inside the int8 product kernel when M' * K <= 16384 with M' = M rounded up to
-a power of two <= 16, a separate kernel otherwise) and the int8 product with
-the fp32 epilogue (row scale x column scale).  Each M's 196 calls are
+(inside the int8 product kernel when the rows cut into 1, 2 or 4 groups give
+M' * K <= 16384 with M' = rows per group rounded up to a power of two <= 16, a
+separate kernel otherwise) and the int8 product with the fp32 epilogue (row
+scale x column scale).  Each M's 196 calls are
 captured in one HIP graph; a step replays the three graphs.
 
 `value` is the step's algorithmic bytes (per call K*N weight bytes + 4N column
@@ -73,11 +74,18 @@ def parse_args():
 
 
 def fused_quant(M, K):
-    """int8_gemm_dynamic quantises inside the product kernel (one launch)."""
-    e = 1
-    while e < M:
-        e <<= 1
-    return e <= 16 and K <= 4096 and e * K <= 16384
+    """int8_gemm_dynamic quantises inside the product kernel (one launch; the
+    rows in 1, 2 or 4 groups of M' <= 16 rows with M' * K <= 16384)."""
+    if K > 4096:
+        return False
+    for g in (1, 2, 4):
+        r = -(-M // g)
+        e = 1
+        while e < r:
+            e <<= 1
+        if e <= 16 and e * K <= 16384:
+            return True
+    return False
 
 
 def call_bytes(M, K, N):

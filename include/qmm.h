@@ -172,8 +172,8 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
                      const qmm_epilogue *ep, void *workspace, size_t workspace_bytes,
                      void *stream);
 
-/* Workspace bytes int8_gemm_dynamic needs (0 when the quantisation is fused:
- * M <= 16, K <= 4096 and M' * K <= 16384, M' = M rounded up to a power of 2). */
+/* Workspace bytes int8_gemm_dynamic needs (0 when the quantisation is fused,
+ * see int8_gemm_dynamic). */
 size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 /*
@@ -182,10 +182,12 @@ size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * row with amax/127 (the quantize_rows_int8 rule) and multiplied with a
  * weight packed by pack_b_int8 (zA = zB = 0); the epilogue uses the computed
  * row scales (ep->row_scale must be NULL).  Results are bit-identical to
- * quantize_rows_int8 followed by int8_gemm.  For M <= 16, K <= 4096 and
- * M' * K <= 16384 (M' = M rounded up to a power of 2) the quantisation runs
- * inside the product kernel (one launch); otherwise the two kernels run in
- * turn.  Xq (M x K int8, ldq >= K) and row_scale ([M] fp32)
+ * quantize_rows_int8 followed by int8_gemm.  The quantisation runs inside
+ * the product kernel (one launch) when K <= 4096 and the rows, cut into
+ * G = 1, 2 or 4 groups of R = ceil(M / G) (the smallest such G), give
+ * R' <= 16 and R' * K <= 16384, R' = R rounded up to a power of 2; each group
+ * is then a grid row that reads the weight once.  Otherwise the two kernels
+ * run in turn.  Xq (M x K int8, ldq >= K) and row_scale ([M] fp32)
  * optionally receive the quantised rows and their scales; pass NULL to skip
  * them (the two-kernel form then keeps them in the workspace).
  */

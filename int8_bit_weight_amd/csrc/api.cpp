@@ -243,15 +243,31 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
 // wins while that is small next to a second launch (measured on MI355X for
 // the Qwen3-0.6B projections: M = 1 and M = 16 with K <= 2048 gain, M = 32
 // loses).
-static bool dynamic_fused(int64_t M, int64_t K) {
-    int64_t e = 1;
-    while (e < M) e <<= 1;
-    return e <= 16 && K <= 4096 && e * K <= 16384;
+// The quantisation inside the product: every workgroup quantises the rows it
+// multiplies, which beats a second launch while M' * K <= 16384 (M' = rows
+// rounded up to a power of two <= 16).  Larger M is cut into row groups of
+// that size (a second grid dimension, the weights read once per group): 0
+// groups = not fused, else 1, 2 or 4.
+static int dynamic_groups(int64_t M, int64_t K) {
+    if (K > 4096) return 0;
+    for (int g : {1, 2, 4}) {
+        const int64_t r = (M + g - 1) / g;
+        int64_t e = 1;
+        while (e < r) e <<= 1;
+        if (e <= 16 && e * K <= 16384) return g;
+    }
+    return 0;
+}
+static bool dynamic_fused(int64_t M, int64_t K) { return dynamic_groups(M, K) > 0; }
+// rows one workgroup of the fused path quantises and multiplies
+static int64_t dynamic_rows(int64_t M, int64_t K) {
+    const int g = dynamic_groups(M, K);
+    return g > 1 ? (M + g - 1) / g : M;
 }
 
 size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     if (M <= 0 || K <= 0 || N <= 0) return 0;
-    if (dynamic_fused(M, K)) return (size_t)plan_int8_gemm(M, K, N).ws_bytes;
+    if (dynamic_fused(M, K)) return (size_t)plan_int8_gemm(dynamic_rows(M, K), K, N).ws_bytes;
     return (size_t)(round_up(M * K, 256) + round_up(4 * M, 256));
 }
 
@@ -292,7 +308,8 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
     // 16 wavefronts with up to 4 k tiles each: one round covers K <= 4096,
     // so the activations stay in registers between the amax and quantise
     // passes.
-    Int8Plan plan = plan_int8_gemm(M, K, N);
+    const int64_t rows = dynamic_rows(M, K);
+    Int8Plan plan = plan_int8_gemm(rows, K, N);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
         return QMM_ERR_WORKSPACE;
     Int8GemmParams p{};
@@ -303,6 +320,7 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
     p.xq_out = Xq;
     p.ldq = ldq;
     p.rs_out = row_scale;
+    p.rpg = rows < M ? (int)rows : 0;
     const char *variant = "";
     st = hip_status(launch_int8_gemm_dynamic(plan, p, s, &variant));
     g_last_variant = variant;

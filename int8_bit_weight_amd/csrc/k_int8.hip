@@ -400,7 +400,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
 }
 
 // Fused dynamic quantisation for small M x K (the planner takes it when
-// M' * K <= 16384, M' = M rounded up to a power of two <= 16, and K <= 4096):
+// M' * K <= 16384, M' = rows per group rounded up to a power of two <= 16,
+// and K <= 4096; up to 4 row groups run as the grid's second dimension):
 // 16 wavefronts, TPW k tiles each
 // (wave w takes tiles w, w+16, ...).  Activations are held compactly: E = M
 // rounded up to a power of two values per lane (at most 32), 64/E lanes per
@@ -414,6 +415,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
 // which is why the planner keeps M*K small here.
 template <int E, int TPW, bool AVEC>
 __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p) {
+    if (p.rpg > 0) {
+        // row group blockIdx.y: rows [y rpg, y rpg + rpg) of the call, quantised
+        // and multiplied on their own (the weights are read once per group)
+        const int r0 = (int)blockIdx.y * p.rpg;
+        p.M = min(p.rpg, p.M - r0);
+        p.X += (int64_t)r0 * p.ldx;
+        if (p.y_i32) p.y_i32 += (int64_t)r0 * p.ld_i32;
+        if (p.y_f32) p.y_f32 += (int64_t)r0 * p.ld_f32;
+        if (p.y_q8) p.y_q8 += (int64_t)r0 * p.ld_q8;
+        if (p.xq_out) p.xq_out += (int64_t)r0 * p.ldq;
+        if (p.rs_out) p.rs_out += r0;
+    }
     constexpr int WAVES = 16;
     constexpr int L = 64 / E;              // lanes per row
     constexpr int MT = E > 16 ? 2 : 1;     // 16-row MFMA tiles
@@ -1043,7 +1056,8 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
 
 template <int E, int TPW>
 hipError_t launch_dyn(const Int8GemmParams &p, bool avec, hipStream_t s) {
-    const dim3 g((unsigned)p.NS), b(1024);
+    const unsigned groups = p.rpg > 0 ? (unsigned)((p.M + p.rpg - 1) / p.rpg) : 1u;
+    const dim3 g((unsigned)p.NS, groups), b(1024);
     if (E >= 4 && avec)
         hipLaunchKernelGGL((k_int8_decode_q<E, TPW, true>), g, b, 0, s, p);
     else
@@ -1066,14 +1080,15 @@ hipError_t launch_dyn_tpw(const Int8GemmParams &p, bool avec, hipStream_t s) {
 
 hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                                     const char **variant) {
-    if (plan.variant != 0 || p.M > 16 || p.KT > 64 || p.zBs != 0) return hipErrorInvalidValue;
-    *variant = "int8_dynamic_m16";
+    const int rows = p.rpg > 0 ? p.rpg : p.M;  // rows one workgroup quantises
+    if (plan.variant != 0 || rows > 16 || p.KT > 64 || p.zBs != 0) return hipErrorInvalidValue;
+    *variant = p.rpg > 0 ? "int8_dynamic_groups" : "int8_dynamic_m16";
     const bool v = p.x_vec && (p.K % 16) == 0;
-    // E: values per lane, M rounded up to a power of two
-    if (p.M <= 1) return launch_dyn_tpw<1>(p, v, s);
-    if (p.M <= 2) return launch_dyn_tpw<2>(p, v, s);
-    if (p.M <= 4) return launch_dyn_tpw<4>(p, v, s);
-    if (p.M <= 8) return launch_dyn_tpw<8>(p, v, s);
+    // E: values per lane, the rows rounded up to a power of two
+    if (rows <= 1) return launch_dyn_tpw<1>(p, v, s);
+    if (rows <= 2) return launch_dyn_tpw<2>(p, v, s);
+    if (rows <= 4) return launch_dyn_tpw<4>(p, v, s);
+    if (rows <= 8) return launch_dyn_tpw<8>(p, v, s);
     return launch_dyn_tpw<16>(p, v, s);
 }
 

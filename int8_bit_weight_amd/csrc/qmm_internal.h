@@ -100,6 +100,7 @@ struct Int8GemmParams {
     int8_t *xq_out;        // optional copies of the quantised rows / scales
     int64_t ldq;
     float *rs_out;
+    int rpg;               // > 0: rows per row group (blockIdx.y), each group an independent call
 };
 
 struct Int8Plan {

@@ -276,10 +276,25 @@ def test_workspace_shared_across_shapes(q, orc):
 
 # ------------------------------------------------- dynamic (fused) path ---
 
+def _dynamic_groups(M, K):
+    """Row groups of the fused dynamic path: the fewest of 1, 2, 4 whose rows
+    (rounded up to a power of two <= 16) times K stay <= 16384; 0 = two launches."""
+    if K > 4096:
+        return 0
+    for g in (1, 2, 4):
+        r = -(-M // g)
+        e = 1 << max(0, (r - 1).bit_length())
+        if e <= 16 and e * K <= 16384:
+            return g
+    return 0
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 1024, 2048), (16, 1024, 1024), (32, 3072, 1024), (16, 2048, 1024),
                                    (16, 3072, 1024), (1, 3072, 64), (3, 100, 37), (17, 1056, 17), (33, 320, 48),
                                    (80, 256, 130), (16, 64, 16), (32, 1024, 64), (20, 512, 40), (5, 4096, 48),
-                                   (2, 2048, 33), (1, 4000, 20), (9, 3000, 16), (4, 4096, 40), (6, 2048, 24)])
+                                   (2, 2048, 33), (1, 4000, 20), (9, 3000, 16), (4, 4096, 40), (6, 2048, 24),
+                                   (32, 1024, 2048), (32, 2048, 1024), (31, 1024, 96), (25, 2048, 40),
+                                   (18, 3000, 64), (12, 3072, 48)])
 def test_dynamic_matches_two_step_and_oracle(q, orc, M, K, N):
     """int8_gemm_dynamic == quantize_rows_int8 + int8_gemm bit for bit (fp32
     output, quantised rows, row scales), and the oracle's int32 product."""
@@ -299,9 +314,11 @@ def test_dynamic_matches_two_step_and_oracle(q, orc, M, K, N):
     xq = torch.full((M, K), 99, dtype=torch.int8, device=dev)
     rs = torch.full((M,), -1.0, dtype=torch.float32, device=dev)
     q.int8_gemm_dynamic(Xd, p, out_f32=y, out_i32=y32, xq_out=xq, rs_out=rs)
-    mp = 1 << max(0, (M - 1).bit_length())
-    if mp <= 16 and K <= 4096 and mp * K <= 16384:
+    groups = _dynamic_groups(M, K)
+    if groups == 1:
         assert q.last_variant() == "int8_dynamic_m16"
+    elif groups > 1:
+        assert q.last_variant() == "int8_dynamic_groups"
     elif M <= 16:
         assert q.last_variant() == "int8_decode_m16"
     elif M <= 32:
@@ -337,7 +354,8 @@ def _near_tie_rows(M, K, seed):
     return X
 
 
-@pytest.mark.parametrize("M,K", [(1, 1024), (2, 1024), (3, 960), (4, 1024), (7, 96), (8, 1024), (16, 1024)])
+@pytest.mark.parametrize("M,K", [(1, 1024), (2, 1024), (3, 960), (4, 1024), (7, 96), (8, 1024), (16, 1024),
+                                 (32, 1024), (27, 2048)])
 def test_dynamic_rounding_near_ties(q, orc, M, K):
     """The fused quantiser's codes equal the oracle's rne(x/s) (IEEE fp32
     division) bit for bit on quotients within ulps of a rounding boundary and
@@ -350,7 +368,7 @@ def test_dynamic_rounding_near_ties(q, orc, M, K):
     xq = torch.full((M, K), 99, dtype=torch.int8, device=torch_dev())
     rs = torch.full((M,), -1.0, dtype=torch.float32, device=torch_dev())
     q.int8_gemm_dynamic(to_dev(X), p, out_f32=y, xq_out=xq, rs_out=rs)
-    assert q.last_variant() == "int8_dynamic_m16"
+    assert q.last_variant() == ("int8_dynamic_m16" if _dynamic_groups(M, K) == 1 else "int8_dynamic_groups")
     Qa, sa = orc.quantize_rows_int8(X)
     assert np.array_equal(to_np(rs).view(np.uint32), sa.view(np.uint32))
     got = to_np(xq)
