@@ -42,7 +42,7 @@ METRIC = "GB/s & %HBM peak at M=1/16; int8 TOPS & %MFMA peak at M=2048"
 # (FETCH_SIZE, then WRITE_SIZE) of `bench.py --probe --no-cpu-baseline`, each
 # scaled by what the counter reads for the probe's 1 GiB device copy (FETCH_SIZE
 # x 2.0, WRITE_SIZE x 1.0).  Valid only for the kernel sources it was taken on.
-MEASURED_TRAFFIC = {"sources_sha1": "d13eba195deac7e491423f5f11159578067b4022", "bytes_per_launch": 2758600}
+MEASURED_TRAFFIC = {"sources_sha1": "aaba2921b7fc14d9e3645fbf8f0941807f7679c6", "bytes_per_launch": 3134357}
 
 
 def decode_traffic():
