@@ -52,6 +52,19 @@ Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
         pl.ws_bytes = 0;
         return pl;
     }
+    if (pl.mt == 1) {
+        // k_q4_mm16: 8 wavefronts x 2 strips per workgroup and at most 8
+        // records (its whole k range is staged in LDS at once); the k range
+        // is split as evenly as that allows
+        const int64_t groups = ceil_div(L.NS, 16);
+        const int64_t S = ceil_div(L.NQ, 8);
+        pl.qps = (int)ceil_div(L.NQ, S);
+        pl.S = (int)ceil_div(L.NQ, pl.qps);
+        pl.grid = groups * pl.S;
+        pl.ws_part_off = 0;
+        pl.ws_bytes = pl.S > 1 ? round_up((int64_t)pl.S * pl.rows_per_launch * N * 4, 256) : 0;
+        return pl;
+    }
     const int64_t qc = pl.mt <= 1 ? 2 : 1;
     const int64_t groups = ceil_div(L.NS, 2 * pl.waves);
     const int64_t target = pl.rows_per_launch <= 4 ? 512 : 256;

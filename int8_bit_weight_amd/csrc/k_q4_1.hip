@@ -749,6 +749,216 @@ __global__ __launch_bounds__(W * 64) void k_q4_gemv1(Q4Params p) {
     }
 }
 
+// ----------------------------------------- the product, 5 <= M <= 16 ---
+// One 16-row MFMA tile of activation rows, three MFMAs (one per bf16 term)
+// per block and strip, as in k_q4_mm.  A workgroup of WAVES wavefronts owns
+// WAVES * C strips and a k range of at most QMAX records; the grid splits
+// the k range S ways and k_q4_finalize adds the S partial sums.  What
+// differs from k_q4_mm is the order of the work: the workgroup splits the
+// activations of its whole k range into LDS once, right at the start (every
+// wavefront's activation loads are issued before any record load), and the
+// records then stream through a ring of R register slots per wavefront with
+// no barrier after the staging one.  (Chunk by chunk, each chunk's
+// activation loads, split and barrier sat between the weight loads and the
+// MFMAs.)
+//   * staging: piece (block bl, k-octet g, row r) = 8 activations, loaded
+//     with two 16-byte loads ahead of the record loads, split into the
+//     three bf16 terms and stored at sA[bl][term] in MFMA lane order (lane
+//     16 g + r).  Rows past M and blocks past K stage zeros.  The block
+//     sums (the four k-octets of a (row, block) lie in lanes r, r+16, r+32,
+//     r+48 of one wavefront) are split the same way into the m-term A
+//     operand: row r, block bl at byte 16 r + 2 (bl % 8) of sXM[bl / 8].
+//   * records past the workgroup's range take the last record's codes and
+//     the header's zero tail for (d, m): they add nothing.
+template <int WAVES, int C, int QMAX, int R, bool XVEC>
+__global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
+    constexpr int NT = WAVES * 64;
+    constexpr int NBLK = 4 * QMAX;
+    constexpr int NG = (NBLK + 7) / 8;  // m-term operands of 8 blocks
+    constexpr int PIECES = NBLK * 64;
+    static_assert(PIECES % NT == 0 && NBLK % 8 == 0, "pieces per thread");
+    static_assert(R >= 1 && R <= QMAX, "record ring");
+    constexpr int PPT = PIECES / NT;
+    constexpr int SPG = WAVES * C;
+    __shared__ __attribute__((aligned(16))) uint8_t sA[NBLK][3][1024];
+    __shared__ __attribute__((aligned(16))) uint8_t sXM[NG][3][1024];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int groups = (p.NS + SPG - 1) / SPG;
+    const int sg = blockIdx.x % groups;
+    const int job = blockIdx.x / groups;
+    const int q0 = job * p.qps;
+    const int q1 = min(p.NQ, q0 + p.qps);
+    const int M = p.M;
+    const uint8_t *hdr = p.recs;
+    const uint8_t *recs = hdr + kHeaderBytes;
+
+    // ---- activation loads (first: the staging waits for them alone)
+    float xr[PPT][8];
+    bool xok[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + i * NT;
+        const int r = pc & 15, g = (pc >> 4) & 3, bl = pc >> 6;
+        const int b = q0 * 4 + bl;
+        xok[i] = r < M && b < p.NB;
+        const float *src = p.X + (int64_t)min(r, M - 1) * p.ldx + min(b, p.NB - 1) * 32 + g * 8;
+        if (XVEC) {
+            const v4f lo = *(const v4f *)src;
+            const v4f hi = *(const v4f *)(src + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xr[i][e] = lo[e];
+                xr[i][4 + e] = hi[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[i][e] = src[e];
+        }
+    }
+
+    // every wavefront's activation loads go out before any record load: the
+    // memory pipeline returns them in order, and the staging needs them first
+    __builtin_amdgcn_s_barrier();
+    // ---- the wavefront's records in k order, through a ring of R slots:
+    // the first R now, record q + R as soon as record q is used
+    const int strip_base = sg * SPG + wave * C;
+    v4i wc[R][C], wd[R][C];
+    auto gload_rec = [&](int q, v4i (&dc)[C], v4i (&dd)[C]) {
+        const int qq = min(q0 + q, q1 - 1);
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const int strip = min(strip_base + j, p.NS - 1);
+            const uint8_t *rec = recs + ((int64_t)strip * p.NQ + qq) * kQ4RecBytes;
+            dc[j] = *(const v4i *)(rec + (uint32_t)lane * 16u);
+            dd[j] = *(const v4i *)(q0 + q < q1 ? rec + 1024 + (uint32_t)(lane & 15) * 16u : hdr + kHeaderBytes - 16);
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < R; ++q) gload_rec(q, wc[q], wd[q]);
+
+    // ---- staging.  k-octets 1..3 of the m-term operands stay zero (bytes
+    // 256.. of each fragment; the block sums fill bytes 0..255)
+    for (int o = tid * 16; o < NG * 3 * 768; o += NT * 16) {
+        const int f = o / 768;
+        *(v4i *)(&sXM[0][0][0] + f * 1024 + 256 + o % 768) = v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + i * NT;
+        const int r = pc & 15, g = (pc >> 4) & 3, bl = pc >> 6;
+        float bsum = 0.0f;
+        uint32_t w[3][4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float x0 = xok[i] ? xr[i][e] : 0.0f;
+            const float x1 = xok[i] ? xr[i][e + 1] : 0.0f;
+            bsum += x0;
+            bsum += x1;
+            const uint32_t t0 = pk_bf16(x0, x1);
+            const float r0 = x0 - bf16_lo_f32(t0), r1 = x1 - bf16_hi_f32(t0);
+            const uint32_t t1 = pk_bf16(r0, r1);
+            const uint32_t t2 = pk_bf16(r0 - bf16_lo_f32(t1), r1 - bf16_hi_f32(t1));
+            w[0][e >> 1] = t0;
+            w[1][e >> 1] = t1;
+            w[2][e >> 1] = t2;
+        }
+        bsum += __shfl_xor(bsum, 16);
+        bsum += __shfl_xor(bsum, 32);
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+            *(v4i *)(&sA[bl][t][(g * 16 + r) * 16]) = v4i{(int)w[t][0], (int)w[t][1], (int)w[t][2], (int)w[t][3]};
+        if (g == 0) {
+            const uint32_t s0 = pk_bf16(bsum, 0.0f);
+            const float sr = bsum - bf16_lo_f32(s0);
+            const uint32_t s1 = pk_bf16(sr, 0.0f);
+            const uint32_t s2 = pk_bf16(sr - bf16_lo_f32(s1), 0.0f);
+            uint8_t *xm = &sXM[bl >> 3][0][r * 16 + (bl & 7) * 2];
+            *(uint16_t *)(xm) = (uint16_t)s0;
+            *(uint16_t *)(xm + 1024) = (uint16_t)s1;
+            *(uint16_t *)(xm + 2048) = (uint16_t)s2;
+        }
+    }
+    // LDS barrier without a memory fence: a fence would wait for the record
+    // loads still in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // ---- the product
+    v4f acc_y[C], acc_m[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        acc_y[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        acc_m[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int a_off = lane * 16;
+    uint32_t mw[2][C][2];  // m values of the last two records, bf16 pairs (k = block)
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+        const int sl = q % R;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int bl = 4 * q + i;
+            v8bf a[3];
+#pragma unroll
+            for (int t = 0; t < 3; ++t) a[t] = *(const v8bf *)(&sA[bl][t][a_off]);
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const v8bf bop = decode8((uint32_t)wc[sl][j][i]);
+                const float d = bf16_lo_f32((uint32_t)wd[sl][j][i]);
+                v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t = 0; t < 3; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], bop, acc, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc_y[j][v] = fmaf(d, acc[v], acc_y[j][v]);
+            }
+            // keep each block's update here (else the compiler sinks them all
+            // to the end and keeps every MFMA result alive)
+#pragma unroll
+            for (int j = 0; j < C; ++j) asm volatile("" : "+v"(acc_y[j]));
+        }
+        // the record's m values (high halves of its four (d, m) words), then
+        // its slot takes record q + R
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            mw[q & 1][j][0] = __builtin_amdgcn_perm((uint32_t)wd[sl][j][1], (uint32_t)wd[sl][j][0], 0x07060302u);
+            mw[q & 1][j][1] = __builtin_amdgcn_perm((uint32_t)wd[sl][j][3], (uint32_t)wd[sl][j][2], 0x07060302u);
+        }
+        if (q + R < QMAX) gload_rec(q + R, wc[sl], wd[sl]);
+        if (q & 1) {
+            // m term of records q-1 and q: their 8 m values (k = block) against
+            // the split block sums
+            v8bf xm[3];
+#pragma unroll
+            for (int t = 0; t < 3; ++t) xm[t] = *(const v8bf *)(&sXM[q >> 1][t][a_off]);
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const v4i mv = {(int)mw[0][j][0], (int)mw[0][j][1], (int)mw[1][j][0], (int)mw[1][j][1]};
+                const v8bf mop = __builtin_bit_cast(v8bf, mv);
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+                    acc_m[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm[t], mop, acc_m[j], 0, 0, 0);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int row = 4 * (lane >> 4) + v;
+            const int n = (strip_base + j) * 16 + (lane & 15);
+            if (row < M && n < p.N) {
+                const float val = acc_y[j][v] + acc_m[j][v];
+                if (p.S == 1)
+                    p.Y[(int64_t)row * p.ldy + n] = val;
+                else
+                    p.part[((int64_t)job * M + row) * p.N + n] = val;
+            }
+        }
+}
+
 // Sum of the k-split partials in split order.  Loads go out eight at a time
 // (independent, clamped to the last split; extra ones are not added) so that
 // a thread waits for one memory latency per eight splits, not per split.
@@ -961,11 +1171,14 @@ hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t
         if (!ok) return hipErrorInvalidValue;
         return hipGetLastError();
     } else if (mt == 1 && waves == 8) {
-        *variant = "q4_mm_m16";
+        // k_q4_mm16<8, 2, 8, 2, XVEC>: at most 8 records per workgroup, 2 in flight
+        // per wavefront (measured: 4, 6 and 8 in flight were 2-12 % slower)
+        *variant = "q4_mm16";
+        if (p.qps > 8 || p.M > 16) return hipErrorInvalidValue;
         if (p.x_vec)
-            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, true>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm16<8, 2, 8, 2, true>), g, b, 0, s, p);
         else
-            hipLaunchKernelGGL((k_q4_mm<1, 8, 2, 2, false, 4, false>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm16<8, 2, 8, 2, false>), g, b, 0, s, p);
     } else if (mt == 2 && waves == 8) {
         *variant = "q4_mm_m32";
         if (p.x_vec)

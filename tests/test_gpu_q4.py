@@ -124,13 +124,35 @@ def test_q4_matmul_one_row_paths(q, orc):
     _check(got3, orc.q4_1_matmul(X3, blocks3, K3, N3), _abs_scale(orc, X3, blocks3, K3, N3))
 
 
+@pytest.mark.parametrize("M,K,N,aligned", [(16, 1440, 300, True), (9, 1440, 300, False), (16, 256, 40, False),
+                                           (5, 32 * 37, 17, True), (12, 8192, 48, True)])
+def test_q4_matmul_m16_paths(q, orc, M, K, N, aligned):
+    """5 <= M <= 16: whole k range staged at once.  K = 1440 (45 blocks):
+    two k splits of 6 records, the second with a partial last record and two
+    padding records; K = 256: one split, no second kernel; K = 8192: eight
+    splits; N not a multiple of the workgroup's 256 columns; activations one
+    float past a 16-byte boundary (scalar loads)."""
+    import torch
+    blocks = _blocks(K, N, seed=M + K + N, zero_cols=(1,), zero_scale_blocks=True)
+    p = _repack(q, blocks, K, N)
+    X = wl.q4_activations(M, K, seed_index=M + K)
+    Xd = to_dev(X)
+    if not aligned:
+        Xw = torch.zeros((M, K + 1), dtype=torch.float32, device=torch_dev())
+        Xw[:, 1:] = Xd
+        Xd = Xw[:, 1:]
+    got = to_np(q.q4_1_matmul(Xd, p))
+    assert q.last_variant() == "q4_mm16"
+    _check(got, orc.q4_1_matmul(X, blocks, K, N), _abs_scale(orc, X, blocks, K, N))
+
+
 def test_q4_matmul_variants_and_determinism(q, orc):
     import torch
     blocks = _blocks(1024, 256, seed=5)
     p = _repack(q, blocks, 1024, 256)
     X = to_dev(wl.q4_activations(16, 1024, seed_index=5))
     a = to_np(q.q4_1_matmul(X, p))
-    assert q.last_variant() == "q4_mm_m16"
+    assert q.last_variant() == "q4_mm16"
     q.q4_1_matmul(to_dev(wl.q4_activations(3, 1024, seed_index=7)), p)
     assert q.last_variant() == "q4_gemv_m4"
     b = to_np(q.q4_1_matmul(X, p))
