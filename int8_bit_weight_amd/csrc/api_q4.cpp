@@ -85,14 +85,18 @@ Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
 MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N) {
     MoePlan pl{};
     const int64_t P = T * n_used;
-    (void)K;
-    (void)N;
     pl.rpc = 32;
     pl.max_chunks = ceil_div(P, pl.rpc) + E;
     pl.ws_sorted_off = 0;
     pl.ws_chunk_off = round_up(P * 4, 256);
     pl.ws_misc_off = pl.ws_chunk_off + round_up(pl.max_chunks * 3 * 4, 256);
-    pl.ws_bytes = pl.ws_misc_off + 256;
+    // the activation split: fp16 terms (4 bytes per activation), block sums,
+    // scale exponents
+    const Q4Layout L = q4_layout(K, N);
+    pl.ws_xs_off = pl.ws_misc_off + 256;
+    pl.ws_xsum_off = pl.ws_xs_off + round_up(T * L.NB * 128, 256);
+    pl.ws_xsc_off = pl.ws_xsum_off + round_up(T * L.NQ * 48, 256);
+    pl.ws_bytes = pl.ws_xsc_off + round_up(T * 4, 256);
     return pl;
 }
 
@@ -193,8 +197,20 @@ qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t l
     int32_t *sorted = (int32_t *)(ws + pl.ws_sorted_off);
     int32_t *chunk_info = (int32_t *)(ws + pl.ws_chunk_off);
     int32_t *misc = (int32_t *)(ws + pl.ws_misc_off);
+    MoeSplit sp{};
+    sp.X = X;
+    sp.ldx = ldx;
+    sp.T = (int)n_tokens;
+    sp.K = (int)K;
+    sp.NB = (int)L.NB;
+    sp.NQ = (int)L.NQ;
+    sp.x_vec = aligned_to(X, 16) && (ldx % 4 == 0);
+    sp.xs = ws + pl.ws_xs_off;
+    sp.xsum = ws + pl.ws_xsum_off;
+    sp.xsc = (int32_t *)(ws + pl.ws_xsc_off);
+    sp.zero16 = ws + pl.ws_misc_off + 64;
     hipError_t e = launch_moe_route(ids, ids_row_stride, n_tokens, n_used, n_expert, pl.rpc, sorted, chunk_info,
-                                    misc, misc + 1, s);
+                                    misc, misc + 1, sp, s);
     const char *variant = "";
     if (e == hipSuccess) {
         Q4Params p{};
@@ -215,6 +231,10 @@ qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t l
         p.n_used = (int)n_used;
         p.ldy_slot = ldy_slot;
         p.ldy_token = ldy_token;
+        p.xs = sp.xs;
+        p.xsum = sp.xsum;
+        p.xsc = sp.xsc;
+        p.zero16 = sp.zero16;
         e = launch_q4_moe(p, pl.max_chunks, s, &variant);
     }
     return record_status(e, variant);

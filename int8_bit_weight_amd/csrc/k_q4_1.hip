@@ -29,6 +29,8 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 template <int N> using ic = std::integral_constant<int, N>;
 
 // f(ic<0>{}), ..., f(ic<N-1>{})
@@ -144,6 +146,13 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, r);
 }
 __device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+// s_waitcnt on the vector memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_q4() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 __device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 template <int MT, int WAVES, int C, int QC, bool MOE, int MINW, bool XVEC, int RS = 2, int XD = 1>
@@ -980,6 +989,210 @@ __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ p
     Y[m * ldy + n] = acc;
 }
 
+// -------------------------------------------------- grouped MoE product ---
+// One workgroup per (chunk of <= 32 rows of one expert, group of WAVES * C
+// strips); chunks come from the routing table, past-the-end workgroups exit.
+// The activations arrive split (k_moe_route's other workgroups): per chunk
+// (one record, four blocks) the workgroup gathers its rows' 16-byte pieces
+// of the split buffers (each lane its own row's address) into registers,
+// three fragments per wavefront, together with the next record, and stores
+// them into the other stage of a two-stage LDS ring at the end of the
+// chunk; one barrier per chunk.  (A global_load_lds copy made the compiler
+// wait for every load in flight before the stage's reads.)
+//   * d term, per block, strip and 16-row tile: two MFMAs
+//     (v_mfma_f32_16x16x32_f16: the fp16 terms against the exact fp16
+//     codes) into a fresh accumulator, then y += d * acc;
+//   * m term, per record, strip and tile: three bf16 MFMAs of the split
+//     block sums (k = block, k-octet 0; the other k-octets are copied from a
+//     zero piece) against the record's m values, accumulated into y;
+//   * the epilogue undoes the token's scale: Y = y * 2^-sc[t].
+// Rows past the chunk repeat its last row (their outputs are not stored);
+// blocks past K read the last block (their d = m = 0).
+template <int WAVES, int C, int MINW>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_moe(Q4Params p) {
+    constexpr int MT = 2, ROWS = MT * 16, SPG = WAVES * C;
+    constexpr int NFD = 4 * 2 * MT;  // d-term fragments per chunk: block x term x tile
+    constexpr int NFM = 3 * MT;      // m-term fragments: term x tile
+    constexpr int FPW = (NFD + NFM + WAVES - 1) / WAVES;  // fragments copied per wavefront
+    // stage = the chunk's fragments: d term [block][term][tile], then m term [term][tile]
+    __shared__ __attribute__((aligned(16))) uint8_t sS0[NFD + NFM][1024], sS1[NFD + NFM][1024];
+    __shared__ int sTok[ROWS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int groups = (p.NS + SPG - 1) / SPG;
+    const int sg = blockIdx.x % groups;
+    const int job = blockIdx.x / groups;
+    if (job >= *p.nchunks) return;
+    const int expert = p.chunk_info[job * 3 + 0];
+    const int row0 = p.chunk_info[job * 3 + 1];
+    const int nrows = p.chunk_info[job * 3 + 2];
+    const uint8_t *hdr = p.recs + (int64_t)expert * p.expert_stride;
+    const uint8_t *recs = hdr + kHeaderBytes;
+    const int ntile = (nrows + 15) >> 4;
+    const int NQ = p.NQ;
+    if (tid < ROWS) sTok[tid] = p.sorted[row0 + min(tid, nrows - 1)] / p.n_used;
+    __syncthreads();
+
+    // ---- gather sources: fragment f = wave + WAVES i of the stage (clamped:
+    // the wavefronts with fewer fragments store the last one again, the same
+    // bytes to the same place); d term
+    // (block f >> 2, term (f >> 1) & 1, tile f & 1), m term f - NFD = (term
+    // >> 1, tile & 1).  Lane (row r, k-octet g) of a tile.
+    const int r = lane & 15, g = lane >> 4;
+    const int a_off = lane * 16;
+    const uint8_t *fsrc[FPW];
+    int fblk[FPW], fbm[FPW], fstep[FPW], foff[FPW];
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) {
+        const int f = min(wave + WAVES * i, NFD + NFM - 1);
+        foff[i] = f * 1024;
+        const bool isd = f < NFD;
+        const int u = isd ? (f >> 1) & 1 : (f - NFD) >> 1;
+        const int tile = isd ? f & 1 : (f - NFD) & 1;
+        const int tok = sTok[tile * 16 + r];
+        const uint8_t *dsrc = p.xs + ((int64_t)tok * p.NB * 2 + u) * 64 + g * 16;
+        const uint8_t *msrc = g == 0 ? p.xsum + ((int64_t)tok * NQ * 3 + u) * 16 : p.zero16;
+        fsrc[i] = isd ? dsrc : msrc;
+        // byte offset of record q: d term min(4 q + block, NB - 1) * 128,
+        // m term q * 48 (0 for the zero piece); arithmetic, no branch
+        fblk[i] = isd ? f >> 2 : 0;
+        fbm[i] = isd ? 128 : 0;
+        fstep[i] = isd ? 0 : (g == 0 ? 48 : 0);
+    }
+    // gathers of record q (clamped to the last record) into registers, and
+    // their stores into stage ST
+    v4i fr[FPW];
+    auto fload = [&](int q) {
+        const int qq = min(q, NQ - 1);
+#pragma unroll
+        for (int i = 0; i < FPW; ++i) {
+            const int64_t o = (int64_t)(min(qq * 4 + fblk[i], p.NB - 1) * fbm[i] + qq * fstep[i]);
+            fr[i] = *(const v4i *)(fsrc[i] + o);
+        }
+    };
+    auto fstore = [&](auto ST) {
+        constexpr int st = decltype(ST)::value;
+        uint8_t *base = st == 0 ? &sS0[0][0] : &sS1[0][0];
+#pragma unroll
+        for (int i = 0; i < FPW; ++i) *(v4i *)(base + foff[i] + a_off) = fr[i];
+    };
+
+    // ---- weight records: two register sets, record q + 1 loaded while q computes
+    const int strip_base = sg * SPG + wave * C;
+    v4i bc[2][C], bd[2][C];
+    auto gload_rec = [&](int q, v4i (&dc)[C], v4i (&dd)[C]) {
+        const int qq = min(q, NQ - 1);
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const int strip = min(strip_base + j, p.NS - 1);
+            const uint8_t *rec = recs + ((int64_t)strip * NQ + qq) * kQ4RecBytes;
+            dc[j] = *(const v4i *)(rec + (uint32_t)lane * 16u);
+            dd[j] = *(const v4i *)(q < NQ ? rec + 1024 + (uint32_t)(lane & 15) * 16u : hdr + kHeaderBytes - 16);
+        }
+    };
+
+    v4f y[MT][C];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < C; ++j) y[t][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // chunk q in stage ST with record set ST
+    auto chunk = [&](auto ST, int q) {
+        constexpr int st = decltype(ST)::value;
+        // stage st was stored at the end of the previous chunk (LDS only: no
+        // memory fence, which would wait for the loads in flight)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        fload(q + 1);
+        gload_rec(q + 1, bc[st ^ 1], bd[st ^ 1]);
+        const uint8_t *A = st == 0 ? &sS0[0][0] : &sS1[0][0];
+        const uint8_t *Mf = A + NFD * 1024;
+#pragma unroll
+        for (int bl = 0; bl < 4; ++bl) {
+            v8h a[MT][2];
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) a[t][u] = *(const v8h *)(A + ((bl * 2 + u) * MT + t) * 1024 + a_off);
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const uint32_t cw = (uint32_t)bc[st][j][bl];
+                const uint32_t lo = cw & 0x0F0F0F0Fu, hi = (cw >> 4) & 0x0F0F0F0Fu;
+                const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);
+                const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);
+                const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);
+                const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);
+                const v8h bop = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                const float d = bf16_lo_f32((uint32_t)bd[st][j][bl]);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    if (t > 0 && ntile <= t) continue;  // row tile without rows (wave-uniform)
+                    v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t][0], bop, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t][1], bop, acc, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) y[t][j][v] = fmaf(d, acc[v], y[t][j][v]);
+                }
+            }
+            // keep each block's update here (else the compiler sinks them to
+            // the end of the chunk and keeps every MFMA result alive)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int j = 0; j < C; ++j) asm volatile("" : "+v"(y[t][j]));
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (t > 0 && ntile <= t) continue;
+            v8bf xm[3];
+#pragma unroll
+            for (int u = 0; u < 3; ++u) xm[u] = *(const v8bf *)(Mf + (u * MT + t) * 1024 + a_off);
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const v4i mv = {(int)__builtin_amdgcn_perm((uint32_t)bd[st][j][1], (uint32_t)bd[st][j][0], 0x07060302u),
+                                (int)__builtin_amdgcn_perm((uint32_t)bd[st][j][3], (uint32_t)bd[st][j][2], 0x07060302u), 0, 0};
+                const v8bf mop = __builtin_bit_cast(v8bf, mv);
+#pragma unroll
+                for (int u = 0; u < 3; ++u) y[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm[u], mop, y[t][j], 0, 0, 0);
+            }
+        }
+        // chunk q + 1's pieces into the other stage (read after the next barrier)
+        fstore(ic<st ^ 1>{});
+    };
+
+    fload(0);
+    gload_rec(0, bc[0], bd[0]);
+    fstore(ic<0>{});
+    // pairs of chunks (NQ >= 1: a do-while keeps the first record loads
+    // ahead of the first stores); at odd NQ the last pair's second chunk is
+    // record NQ, whose (d, m) come from the header's zero tail: it adds
+    // exactly zero
+    int q = 0;
+    do {
+        chunk(ic<0>{}, q);
+        chunk(ic<1>{}, q + 1);
+        q += 2;
+    } while (q < NQ);
+
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = t * 16 + 4 * (lane >> 4) + v;
+                const int n = (strip_base + j) * 16 + (lane & 15);
+                if (row < nrows && n < p.N) {
+                    const int pair = p.sorted[row0 + row];
+                    const int tk = pair / p.n_used;
+                    const int sl = pair - tk * p.n_used;
+                    p.Y[(int64_t)tk * p.ldy_token + (int64_t)sl * p.ldy_slot + n] =
+                        __builtin_ldexpf(y[t][j][v], -p.xsc[tk]);
+                }
+            }
+}
+
 // ------------------------------------------------------ MoE routing sort ---
 // One workgroup.  Counts the used (token, slot) pairs per expert (ids read
 // once, through the row stride, and kept in registers), scans the counts,
@@ -992,11 +1205,115 @@ __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ p
 // wavefront totals give every run its offsets.  The chunk table lists the
 // full chunks (rpc rows) of every expert first and the partial ones after
 // them, so that workgroups dispatched last get the smaller jobs.
+//
+// The launch's other workgroups split the activations for the grouped
+// product, four tokens per workgroup (256 threads each): the token's max |x|
+// fixes a power-of-two scale 2^sc with sc = 15 - e (max |x| = f 2^e, f in
+// [0.5, 1)), so that every scaled value lies below 2^15 and the two fp16
+// terms h0 = fp16(x 2^sc), h1 = fp16(x 2^sc - h0) hold it to about 2^-22
+// relative (the scaling is exact; the subtraction is exact in fp32).  The
+// block sums of the scaled values (32 k, fixed order: 8 values per thread,
+// then the four k-octets) are split into three bf16 terms, as the m term's
+// A operand; four blocks (one record) per 16 bytes, the upper 8 zero.
+constexpr int kSplitTokensPerGroup = 4;
+__device__ void moe_split_token(const MoeSplit &sp, int t, int ltid, float *s_max) {
+    const int lane = ltid & 63, wl = ltid >> 6;  // wavefront of the token (0..3)
+    const float *xr = sp.X + (int64_t)t * sp.ldx;
+    const int npc = sp.NQ * 16;  // pieces (block, k-octet), whole records
+    auto load8 = [&](int pc, float (&v)[8]) {
+        const int b = pc >> 2, g = pc & 3;
+        const bool ok = b < sp.NB;
+        const float *src = xr + (int64_t)min(b, sp.NB - 1) * 32 + g * 8;
+        if (sp.x_vec) {
+            const v4f lo = *(const v4f *)src, hi = *(const v4f *)(src + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = ok ? lo[e] : 0.0f;
+                v[4 + e] = ok ? hi[e] : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = ok ? src[e] : 0.0f;
+        }
+    };
+    float am = 0.0f;
+    for (int pc = ltid; pc < npc; pc += 256) {
+        float v[8];
+        load8(pc, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) am = fmaxf(am, __shfl_xor(am, d));
+    if (lane == 0) s_max[wl] = am;
+    __syncthreads();
+    const float tm = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    const int sc = 15 - __builtin_amdgcn_frexp_expf(tm);
+    if (ltid == 0) sp.xsc[t] = sc;
+    for (int pc0 = 0; pc0 < npc; pc0 += 256) {  // uniform trip count: the shuffles below
+        const int pc = pc0 + ltid;
+        const int b = pc >> 2, g = pc & 3;
+        float v[8];
+        load8(min(pc, npc - 1), v);
+        float bs = 0.0f;
+        uint32_t h[2][4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float x0 = __builtin_ldexpf(v[e], sc), x1 = __builtin_ldexpf(v[e + 1], sc);
+            bs += x0;
+            bs += x1;
+            const v2h a0 = {(_Float16)x0, (_Float16)x1};
+            const v2h a1 = {(_Float16)(x0 - (float)a0[0]), (_Float16)(x1 - (float)a0[1])};
+            h[0][e >> 1] = __builtin_bit_cast(uint32_t, a0);
+            h[1][e >> 1] = __builtin_bit_cast(uint32_t, a1);
+        }
+        if (pc < npc && b < sp.NB) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                *(v4i *)(sp.xs + (((int64_t)t * sp.NB + b) * 2 + u) * 64 + g * 16) =
+                    v4i{(int)h[u][0], (int)h[u][1], (int)h[u][2], (int)h[u][3]};
+        }
+        // block sum over the four k-octets (lanes 4b'..4b'+3), then the four
+        // blocks of the record (lanes 16q'..16q'+15) into its first lane
+        bs += __shfl_xor(bs, 1);
+        bs += __shfl_xor(bs, 2);
+        float s4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s4[k] = __shfl(bs, (lane & ~15) + 4 * k);
+        if (pc < npc && (pc & 15) == 0) {
+            uint32_t w[3][2];
+#pragma unroll
+            for (int k = 0; k < 4; k += 2) {
+                const uint32_t t0 = pk_bf16(s4[k], s4[k + 1]);
+                const float r0 = s4[k] - bf16_lo_f32(t0), r1 = s4[k + 1] - bf16_hi_f32(t0);
+                const uint32_t t1 = pk_bf16(r0, r1);
+                const uint32_t t2 = pk_bf16(r0 - bf16_lo_f32(t1), r1 - bf16_hi_f32(t1));
+                w[0][k >> 1] = t0;
+                w[1][k >> 1] = t1;
+                w[2][k >> 1] = t2;
+            }
+            const int q = pc >> 4;
+#pragma unroll
+            for (int u = 0; u < 3; ++u)
+                *(v4i *)(sp.xsum + (((int64_t)t * sp.NQ + q) * 3 + u) * 16) = v4i{(int)w[u][0], (int)w[u][1], 0, 0};
+        }
+    }
+}
+
 constexpr int kRoutePairsPerThread = 8;  // pairs held in registers per pass
 __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ ids, int64_t ids_stride, int T,
                                                     int n_used, int E, int rpc, int32_t *__restrict__ sorted,
                                                     int32_t *__restrict__ chunk_info, int32_t *__restrict__ nchunks,
-                                                    int32_t *__restrict__ err) {
+                                                    int32_t *__restrict__ err, MoeSplit sp) {
+    if (blockIdx.x > 0) {
+        __shared__ float s_max[kSplitTokensPerGroup][4];
+        const int grp = threadIdx.x >> 8;
+        const int t = ((int)blockIdx.x - 1) * kSplitTokensPerGroup + grp;
+        if (blockIdx.x == 1 && threadIdx.x == 0) *(v4i *)sp.zero16 = v4i{0, 0, 0, 0};
+        // tokens past T repeat token T - 1 (the same values, written again)
+        moe_split_token(sp, min(t, T - 1), threadIdx.x & 255, s_max[grp]);
+        return;
+    }
     extern __shared__ int32_t sh[];
     int32_t *cnt = sh;           // [E] pairs per expert
     int32_t *off = sh + E;       // [E] first sorted row of the expert
@@ -1198,22 +1515,21 @@ hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t
 
 hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, int64_t n_used, int64_t E,
                             int rpc, int32_t *sorted, int32_t *chunk_info, int32_t *nchunks, int32_t *err,
-                            hipStream_t s) {
+                            const MoeSplit &sp, hipStream_t s) {
     const size_t shmem = (size_t)E * 3 * sizeof(int32_t);
-    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), shmem, s, ids, ids_stride, (int)T, (int)n_used, (int)E,
-                       rpc, sorted, chunk_info, nchunks, err);
+    // workgroup 0 routes; workgroups 1.. split four tokens each
+    const unsigned grid = 1u + (unsigned)ceil_div(T, kSplitTokensPerGroup);
+    hipLaunchKernelGGL(k_moe_route, dim3(grid), dim3(1024), shmem, s, ids, ids_stride, (int)T, (int)n_used, (int)E,
+                       rpc, sorted, chunk_info, nchunks, err, sp);
     return hipGetLastError();
 }
 
 hipError_t launch_q4_moe(const Q4Params &p, int64_t max_chunks, hipStream_t s, const char **variant) {
     constexpr int WAVES = 8, C = 2;
     const int64_t groups = ceil_div(p.NS, C * WAVES);
-    *variant = "q4_mm_moe_m32";
+    *variant = "q4_moe_m32";
     const dim3 g((unsigned)(groups * max_chunks)), b(WAVES * 64);
-    if (p.x_vec)
-        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, true>), g, b, 0, s, p);
-    else
-        hipLaunchKernelGGL((k_q4_mm<2, WAVES, C, 1, true, 4, false>), g, b, 0, s, p);
+    hipLaunchKernelGGL((k_q4_moe<WAVES, C, 4>), g, b, 0, s, p);
     return hipGetLastError();
 }
 

@@ -188,7 +188,7 @@ def _moe_case(q, orc, E, K, N, T, n_used, stride=17, seed=0, ids=None, check="fu
         ids = np.stack([g.permutation(max(E, stride))[:stride] % E for _ in range(T)]).astype(np.int32)
     buf, estride = q.q4_1_repack_experts(to_dev(experts), K, N)
     Y = q.q4_1_matmul_id(to_dev(X), buf, E, K, N, estride, to_dev(ids), n_used)
-    assert q.last_variant() == "q4_mm_moe_m32"
+    assert q.last_variant() == "q4_moe_m32"
     got = to_np(Y)
     if check == "full":
         ref = orc.q4_1_matmul_id(X, experts, E, K, N, ids, n_used)
