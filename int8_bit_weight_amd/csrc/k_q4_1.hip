@@ -11,11 +11,14 @@
 //   * MUL_MAT_ID routing: a counting sort of the (token, slot) pairs by
 //     expert into chunks of rows, read through the strided id view ("Zaya
 //     8B", "The bugs that were the work"), and one grouped launch over all
-//     chunks (the grouped-dispatch cost lesson of "Round 25p").
+//     chunks (the grouped-dispatch cost lesson of "Round 25p"); the routing
+//     launch also splits every token once into two fp16 terms under a
+//     power-of-two scale, which the grouped product multiplies with
+//     v_mfma_f32_16x16x32_f16 (two MFMAs per block instead of three).
 //
 // Codes stay exact: bytes 0..15 read as OCP e4m3 are exactly q * 2^-9, and
-// v_cvt_scalef32_pk_bf16_fp8 with scale 2^9 turns two of them into two exact
-// bf16 integers per instruction.
+// v_cvt_scalef32_pk_bf16_fp8 (or _f16_fp8) with scale 2^9 turns two of them
+// into two exact bf16 (fp16) integers per instruction.
 #include <type_traits>
 #include <utility>
 
@@ -123,9 +126,8 @@ __global__ __launch_bounds__(256) void k_q4_repack(const uint8_t *__restrict__ b
 //   * m term, per chunk and strip: the chunk's m values as a bf16 B operand
 //     (k = block) against the split block sums, three MFMAs accumulating
 //     over the whole k range.
-//   dense: blockIdx -> (strip group, k split); rows 0..M-1.
-//   MoE:   blockIdx -> (strip group, row chunk); the chunk table gives the
-//          expert and the sorted (token, slot) pairs of its rows.
+//   blockIdx -> (strip group, k split); rows 0..M-1 (17 <= M <= 32 per
+//   launch; k_q4_mm16 takes 5 <= M <= 16 and k_q4_moe the grouped product).
 // Loads are never inside branches (a load in a branch makes the compiler wait
 // for it where the branch ends, which would serialise the prefetch): indices
 // past the valid range are clamped to valid memory.  A record past the range
@@ -155,7 +157,7 @@ __device__ __forceinline__ void wait_vmcnt_q4() {
 }
 __device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-template <int MT, int WAVES, int C, int QC, bool MOE, int MINW, bool XVEC, int RS = 2, int XD = 1>
+template <int MT, int WAVES, int C, int QC, int MINW, bool XVEC, int RS = 2, int XD = 1>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_mm(Q4Params p) {
     constexpr int NT = WAVES * 64;
     constexpr int ROWS = MT * 16;
@@ -190,23 +192,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     const int job = blockIdx.x / groups;
 
     const uint8_t *hdr = p.recs;
-    int nrows, row0 = 0, q0, q1;
-    if (MOE) {
-        if (job >= *p.nchunks) return;
-        const int expert = p.chunk_info[job * 3 + 0];
-        row0 = p.chunk_info[job * 3 + 1];
-        nrows = p.chunk_info[job * 3 + 2];
-        hdr += (int64_t)expert * p.expert_stride;
-        q0 = 0;
-        q1 = p.NQ;
-    } else {
-        nrows = p.M;
-        q0 = job * p.qps;
-        q1 = min(p.NQ, q0 + p.qps);
-    }
+    const int nrows = p.M;
+    const int q0 = job * p.qps;
+    const int q1 = min(p.NQ, q0 + p.qps);
     const uint8_t *recs = hdr + kHeaderBytes;
     const int ntile = (nrows + 15) >> 4;  // 16-row tiles holding rows (MFMAs of the others are skipped)
-    if (tid < nrows) sRow[tid] = (int64_t)(MOE ? p.sorted[row0 + tid] / p.n_used : tid) * p.ldx;
+    if (tid < nrows) sRow[tid] = (int64_t)tid * p.ldx;
     for (int o = tid * 16; o < (int)sizeof(sXM); o += NT * 16) *(v4i *)(&sXM[0][0][0][0] + o) = v4i{0, 0, 0, 0};
     __syncthreads();
 
@@ -448,12 +439,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                 const int n = (strip_base + j) * 16 + (lane & 15);
                 if (row < nrows && n < p.N) {
                     const float val = acc_y[rt][j][v] + acc_m[rt][j][v];
-                    if (MOE) {
-                        const int pair = p.sorted[row0 + row];
-                        const int t = pair / p.n_used;
-                        const int s = pair - t * p.n_used;
-                        p.Y[(int64_t)t * p.ldy_token + (int64_t)s * p.ldy_slot + n] = val;
-                    } else if (p.S == 1) {
+                    if (p.S == 1) {
                         p.Y[(int64_t)row * p.ldy + n] = val;
                     } else {
                         p.part[((int64_t)job * p.M + row) * p.N + n] = val;
@@ -1499,9 +1485,9 @@ hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t
     } else if (mt == 2 && waves == 8) {
         *variant = "q4_mm_m32";
         if (p.x_vec)
-            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, true>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, 4, true>), g, b, 0, s, p);
         else
-            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, false, 4, false>), g, b, 0, s, p);
+            hipLaunchKernelGGL((k_q4_mm<2, 8, 2, 1, 4, false>), g, b, 0, s, p);
     } else {
         return hipErrorInvalidValue;
     }
