@@ -994,9 +994,9 @@ __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ p
 //   * the epilogue undoes the token's scale: Y = y * 2^-sc[t].
 // Rows past the chunk repeat its last row (their outputs are not stored);
 // blocks past K read the last block (their d = m = 0).
-template <int WAVES, int C, int MINW>
+template <int MT, int WAVES, int C, int MINW>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_moe(Q4Params p) {
-    constexpr int MT = 2, ROWS = MT * 16, SPG = WAVES * C;
+    constexpr int ROWS = MT * 16, SPG = WAVES * C;
     constexpr int NFD = 4 * 2 * MT;  // d-term fragments per chunk: block x term x tile
     constexpr int NFM = 3 * MT;      // m-term fragments: term x tile
     constexpr int FPW = (NFD + NFM + WAVES - 1) / WAVES;  // fragments copied per wavefront
@@ -1023,9 +1023,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 
     // ---- gather sources: fragment f = wave + WAVES i of the stage (clamped:
     // the wavefronts with fewer fragments store the last one again, the same
-    // bytes to the same place); d term
-    // (block f >> 2, term (f >> 1) & 1, tile f & 1), m term f - NFD = (term
-    // >> 1, tile & 1).  Lane (row r, k-octet g) of a tile.
+    // bytes to the same place); d term f = (block * 2 + term) * MT + tile,
+    // m term f - NFD = term * MT + tile.  Lane (row r, k-octet g) of a tile.
     const int r = lane & 15, g = lane >> 4;
     const int a_off = lane * 16;
     const uint8_t *fsrc[FPW];
@@ -1035,15 +1034,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         const int f = min(wave + WAVES * i, NFD + NFM - 1);
         foff[i] = f * 1024;
         const bool isd = f < NFD;
-        const int u = isd ? (f >> 1) & 1 : (f - NFD) >> 1;
-        const int tile = isd ? f & 1 : (f - NFD) & 1;
+        const int u = isd ? (f / MT) & 1 : (f - NFD) / MT;
+        const int tile = isd ? f % MT : (f - NFD) % MT;
         const int tok = sTok[tile * 16 + r];
         const uint8_t *dsrc = p.xs + ((int64_t)tok * p.NB * 2 + u) * 64 + g * 16;
         const uint8_t *msrc = g == 0 ? p.xsum + ((int64_t)tok * NQ * 3 + u) * 16 : p.zero16;
         fsrc[i] = isd ? dsrc : msrc;
         // byte offset of record q: d term min(4 q + block, NB - 1) * 128,
         // m term q * 48 (0 for the zero piece); arithmetic, no branch
-        fblk[i] = isd ? f >> 2 : 0;
+        fblk[i] = isd ? f / (2 * MT) : 0;
         fbm[i] = isd ? 128 : 0;
         fstep[i] = isd ? 0 : (g == 0 ? 48 : 0);
     }
@@ -1515,7 +1514,7 @@ hipError_t launch_q4_moe(const Q4Params &p, int64_t max_chunks, hipStream_t s, c
     const int64_t groups = ceil_div(p.NS, C * WAVES);
     *variant = "q4_moe_m32";
     const dim3 g((unsigned)(groups * max_chunks)), b(WAVES * 64);
-    hipLaunchKernelGGL((k_q4_moe<WAVES, C, 4>), g, b, 0, s, p);
+    hipLaunchKernelGGL((k_q4_moe<2, WAVES, C, 4>), g, b, 0, s, p);
     return hipGetLastError();
 }
 

@@ -217,6 +217,27 @@ def test_moe_shapes(q, orc, E, K, N, T, n_used):
     _moe_case(q, orc, E, K, N, T, n_used, seed=E + K + N + T)
 
 
+def test_moe_token_magnitudes(q, orc):
+    """Tokens whose magnitudes lie far outside fp16's range (1e-30 .. 1e30,
+    mixed in one call): the grouped product's per-token power-of-two scale
+    keeps every token, checked token by token, within the 1e-5 gate.  K = 160
+    leaves a partial last record."""
+    E, K, N, T, n_used = 6, 160, 40, 9, 3
+    g = np.random.default_rng(21)
+    experts = np.stack([wl.encode_q4_1(wl.normal_f32(g, (K, N), 0.02)) for _ in range(E)])
+    factors = np.array([1.0, 1e30, 1e-30, 1e-20, 1e20, 3.0e4, 7.5e-6, 1.0, 65504.0], dtype=np.float32)
+    X = (wl.normal_f32(g, (T, K)) * factors[:, None]).astype(np.float32)
+    ids = np.stack([g.permutation(17)[:17] % E for _ in range(T)]).astype(np.int32)
+    buf, estride = q.q4_1_repack_experts(to_dev(experts), K, N)
+    got = to_np(q.q4_1_matmul_id(to_dev(X), buf, E, K, N, estride, to_dev(ids), n_used))
+    assert np.isfinite(got).all()
+    ref = orc.q4_1_matmul_id(X, experts, E, K, N, ids, n_used)
+    absw = [np.abs(orc.q4_1_decode(experts[e], K, N)) for e in range(E)]
+    for t in range(T):
+        scale = np.stack([np.abs(X[t].astype(np.float64)) @ absw[ids[t, s]] for s in range(n_used)])
+        _check(got[t], ref[t], scale)
+
+
 def test_moe_single_expert_takes_all_rows(q, orc):
     """Every pair routed to one expert (many row chunks on one expert): equal
     to the dense product with that expert's weight."""
