@@ -6,7 +6,7 @@ Workload (one "step"): the seven Qwen3-0.6B projections of all 28 layers
 timed region: ~420 MiB of int8 codes, more than the 256 MiB Infinity Cache)
 run as decode at M = 1, 16 and 32 rows of fp32 N(0, 1) activations.  Every
 call is int8_gemm_dynamic: per-row amax/127 quantisation of the activations
-(inside the int8 product kernel when the rows cut into 1, 2 or 4 groups give
+(inside the int8 product kernel when the rows cut into 1, 2, 4 or 8 groups give
 M' * K <= 16384 with M' = rows per group rounded up to a power of two <= 16, a
 separate kernel otherwise) and the int8 product with the fp32 epilogue (row
 scale x column scale).  Each M's 196 calls are
@@ -42,7 +42,7 @@ METRIC = "GB/s & %HBM peak at M=1/16; int8 TOPS & %MFMA peak at M=2048"
 # (FETCH_SIZE, then WRITE_SIZE) of `bench.py --probe --no-cpu-baseline`, each
 # scaled by what the counter reads for the probe's 1 GiB device copy (FETCH_SIZE
 # x 2.0, WRITE_SIZE x 1.0).  Valid only for the kernel sources it was taken on.
-MEASURED_TRAFFIC = {"sources_sha1": "aaba2921b7fc14d9e3645fbf8f0941807f7679c6", "bytes_per_launch": 3134357}
+MEASURED_TRAFFIC = {"sources_sha1": "17432852cff03b64edb33e48c24eafe4790ebfde", "bytes_per_launch": 3249238}
 
 
 def decode_traffic():
@@ -75,10 +75,10 @@ def parse_args():
 
 def fused_quant(M, K):
     """int8_gemm_dynamic quantises inside the product kernel (one launch; the
-    rows in 1, 2 or 4 groups of M' <= 16 rows with M' * K <= 16384)."""
+    rows in 1, 2, 4 or 8 groups of M' <= 16 rows with M' * K <= 16384)."""
     if K > 4096:
         return False
-    for g in (1, 2, 4):
+    for g in (1, 2, 4, 8):
         r = -(-M // g)
         e = 1
         while e < r:

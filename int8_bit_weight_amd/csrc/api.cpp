@@ -247,10 +247,10 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
 // multiplies, which beats a second launch while M' * K <= 16384 (M' = rows
 // rounded up to a power of two <= 16).  Larger M is cut into row groups of
 // that size (a second grid dimension, the weights read once per group): 0
-// groups = not fused, else 1, 2 or 4.
+// groups = not fused, else 1, 2, 4 or 8.
 static int dynamic_groups(int64_t M, int64_t K) {
     if (K > 4096) return 0;
-    for (int g : {1, 2, 4}) {
+    for (int g : {1, 2, 4, 8}) {
         const int64_t r = (M + g - 1) / g;
         int64_t e = 1;
         while (e < r) e <<= 1;

@@ -401,7 +401,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
 
 // Fused dynamic quantisation for small M x K (the planner takes it when
 // M' * K <= 16384, M' = rows per group rounded up to a power of two <= 16,
-// and K <= 4096; up to 4 row groups run as the grid's second dimension):
+// and K <= 4096; up to 8 row groups run as the grid's second dimension):
 // 16 wavefronts, TPW k tiles each
 // (wave w takes tiles w, w+16, ...).  Activations are held compactly: E = M
 // rounded up to a power of two values per lane (at most 32), 64/E lanes per
