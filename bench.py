@@ -42,7 +42,7 @@ METRIC = "GB/s & %HBM peak at M=1/16; int8 TOPS & %MFMA peak at M=2048"
 # (FETCH_SIZE, then WRITE_SIZE) of `bench.py --probe --no-cpu-baseline`, each
 # scaled by what the counter reads for the probe's 1 GiB device copy (FETCH_SIZE
 # x 2.0, WRITE_SIZE x 1.0).  Valid only for the kernel sources it was taken on.
-MEASURED_TRAFFIC = {"sources_sha1": "17432852cff03b64edb33e48c24eafe4790ebfde", "bytes_per_launch": 3249238}
+MEASURED_TRAFFIC = {"sources_sha1": "16eaf38b47611a986a5875923eb5a3991899af1b", "bytes_per_launch": 3246316}
 
 
 def decode_traffic():

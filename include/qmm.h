@@ -184,10 +184,11 @@ size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * row scales (ep->row_scale must be NULL).  Results are bit-identical to
  * quantize_rows_int8 followed by int8_gemm.  The quantisation runs inside
  * the product kernel (one launch) when K <= 4096 and the rows, cut into
- * G = 1, 2, 4 or 8 groups of R = ceil(M / G) (the smallest such G), give
- * R' <= 16 and R' * K <= 16384, R' = R rounded up to a power of 2; each group
- * is then a grid row that reads the weight once.  Otherwise the two kernels
- * run in turn.  Xq (M x K int8, ldq >= K) and row_scale ([M] fp32)
+ * G = 1, 2, 4 or 8 groups of R = ceil(M / G), give R' <= 16 and
+ * R' * K <= 16384, R' = R rounded up to a power of 2 (G is the smallest one
+ * with R' <= 8 if there is one, else the smallest one with R' <= 16); each
+ * group is then a grid row that reads the weight once.  Otherwise the two
+ * kernels run in turn.  Xq (M x K int8, ldq >= K) and row_scale ([M] fp32)
  * optionally receive the quantised rows and their scales; pass NULL to skip
  * them (the two-kernel form then keeps them in the workspace).
  */

@@ -246,16 +246,19 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
 // The quantisation inside the product: every workgroup quantises the rows it
 // multiplies, which beats a second launch while M' * K <= 16384 (M' = rows
 // rounded up to a power of two <= 16).  Larger M is cut into row groups of
-// that size (a second grid dimension, the weights read once per group): 0
-// groups = not fused, else 1, 2, 4 or 8.
+// that size (a second grid dimension, the weights read once per group, mostly
+// from L2), preferring groups of at most 8 rows: a workgroup's quantisation
+// of 16 rows cost more than the extra weight reads (measured; groups of 4
+// rows cost more again).  0 groups = not fused, else 1, 2, 4 or 8.
 static int dynamic_groups(int64_t M, int64_t K) {
     if (K > 4096) return 0;
-    for (int g : {1, 2, 4, 8}) {
-        const int64_t r = (M + g - 1) / g;
-        int64_t e = 1;
-        while (e < r) e <<= 1;
-        if (e <= 16 && e * K <= 16384) return g;
-    }
+    for (int rmax : {8, 16})
+        for (int g : {1, 2, 4, 8}) {
+            const int64_t r = (M + g - 1) / g;
+            int64_t e = 1;
+            while (e < r) e <<= 1;
+            if (e <= rmax && e * K <= 16384) return g;
+        }
     return 0;
 }
 static bool dynamic_fused(int64_t M, int64_t K) { return dynamic_groups(M, K) > 0; }

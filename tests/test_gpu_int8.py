@@ -278,14 +278,16 @@ def test_workspace_shared_across_shapes(q, orc):
 
 def _dynamic_groups(M, K):
     """Row groups of the fused dynamic path: the fewest of 1, 2, 4, 8 whose rows
-    (rounded up to a power of two <= 16) times K stay <= 16384; 0 = two launches."""
+    (rounded up to a power of two, <= 8 if possible, else <= 16) times K stay
+    <= 16384; 0 = two launches."""
     if K > 4096:
         return 0
-    for g in (1, 2, 4, 8):
-        r = -(-M // g)
-        e = 1 << max(0, (r - 1).bit_length())
-        if e <= 16 and e * K <= 16384:
-            return g
+    for rmax in (8, 16):
+        for g in (1, 2, 4, 8):
+            r = -(-M // g)
+            e = 1 << max(0, (r - 1).bit_length())
+            if e <= rmax and e * K <= 16384:
+                return g
     return 0
 
 
