@@ -238,6 +238,28 @@ def test_moe_token_magnitudes(q, orc):
         _check(got[t], ref[t], scale)
 
 
+def test_moe_unaligned_activations(q, orc):
+    """Activation rows one float past a 16-byte boundary (ldx = K + 1): the
+    split's scalar-load path gives the same bits as the aligned call."""
+    import torch
+    E, K, N, T, n_used = 7, 96, 40, 13, 4
+    g = np.random.default_rng(8)
+    experts = np.stack([wl.encode_q4_1(wl.normal_f32(g, (K, N), 0.02)) for _ in range(E)])
+    X = wl.normal_f32(g, (T, K))
+    ids = np.stack([g.permutation(17)[:17] % E for _ in range(T)]).astype(np.int32)
+    buf, estride = q.q4_1_repack_experts(to_dev(experts), K, N)
+    a = to_np(q.q4_1_matmul_id(to_dev(X), buf, E, K, N, estride, to_dev(ids), n_used))
+    Xw = torch.zeros((T, K + 1), dtype=torch.float32, device=torch_dev())
+    Xw[:, 1:] = to_dev(X)
+    b = to_np(q.q4_1_matmul_id(Xw[:, 1:], buf, E, K, N, estride, to_dev(ids), n_used))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    ref = orc.q4_1_matmul_id(X, experts, E, K, N, ids, n_used)
+    absw = [np.abs(orc.q4_1_decode(experts[e], K, N)) for e in range(E)]
+    scale = np.stack([np.stack([np.abs(X[t].astype(np.float64)) @ absw[ids[t, s]] for s in range(n_used)])
+                      for t in range(T)])
+    _check(b, ref, scale)
+
+
 def test_moe_single_expert_takes_all_rows(q, orc):
     """Every pair routed to one expert (many row chunks on one expert): equal
     to the dense product with that expert's weight."""
