@@ -643,20 +643,20 @@ __device__ __forceinline__ void pf_schedule_staged() {
     if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
 }
 
-// Step order of the direct-load path: the 8 operand reads for the next step
-// and the 8 global loads (4 straight into LDS, 4 weight operands) each sit
-// between two MFMAs.
+// Step order of the direct-load path: the 12 operand reads for the next
+// step (8 activation, 4 weight) and the 6 global-to-LDS copies (4 activation
+// fragments, 2 weight tiles) spread between the 16 MFMAs.
 template <bool HAS_ZB>
 __device__ __forceinline__ void pf_schedule_direct() {
     constexpr int MFMA = 0x008, VMEM = 0x060, DS_RD = 0x100;
-    static_for<8>([&](auto) {
+    static_for<6>([&](auto) {
         __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
-    });
-    static_for<8>([&](auto) {
         __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
         __builtin_amdgcn_sched_group_barrier(VMEM, 1, 0);
     });
+    __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
     if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
 }
 
@@ -693,6 +693,8 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     constexpr int BF = PF_BN / 16;      // B fragments per stage
     constexpr int ACH = AF * 64 / 256;  // 16-byte A chunks per thread per stage (4)
     constexpr int SA = AF * 1024;  // bytes of one activation stage
+    constexpr int SB = BF * 1024;  // bytes of one weight stage (FAST: in LDS after the activations)
+    constexpr int SD = FAST ? SA + SB : 16;
     // activation stages in LDS: three for the register-staged path; for the
     // FAST path one array per stage, so that the compiler can tell a read
     // of one stage from a copy still landing in another (it waits for every
@@ -700,9 +702,8 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     // them)
     __shared__ __attribute__((aligned(16))) int8_t sA[FAST ? 1 : 3][FAST ? 16 : SA];
     static_assert(PF_DEPTH <= 6, "direct-path stage arrays");
-    __shared__ __attribute__((aligned(16))) int8_t sD0[FAST ? SA : 16], sD1[FAST ? SA : 16],
-        sD2[FAST ? SA : 16], sD3[FAST ? SA : 16], sD4[FAST && PF_DEPTH > 4 ? SA : 16],
-        sD5[FAST && PF_DEPTH > 5 ? SA : 16];
+    __shared__ __attribute__((aligned(16))) int8_t sD0[SD], sD1[SD], sD2[SD], sD3[SD],
+        sD4[FAST && PF_DEPTH > 4 ? SD : 16], sD5[FAST && PF_DEPTH > 5 ? SD : 16];
     auto stage_buf = [&](auto B) -> int8_t * {
         constexpr int b = decltype(B)::value;
         if constexpr (b == 0) return sD0;
@@ -774,13 +775,28 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
             ra[sl][i] = load_a16<false>(p, m0 + (c >> 2), kt * kTileK + (c & 3) * 16);
         }
     };
-    // FAST: A stage kt into LDS buffer BUF, without passing through registers
+    // FAST: weight tiles of the workgroup's 8 strips: wave w copies strips
+    // 2 w and 2 w + 1 (lane L copies 16-byte chunk L of the packed tile, so
+    // the LDS image is the tile as stored)
+    const int8_t *bt_src[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int strip = min(strip0 + 2 * wave + u, p.NS - 1);
+        bt_src[u] = p.codes + (int64_t)strip * KT * kTileBytes + lane * 16;
+    }
+    // FAST: stage kt (activation fragments and weight tiles) into LDS buffer
+    // BUF, without passing through registers
     auto dload = [&](auto BUF, int kt) {
         constexpr int b = decltype(BUF)::value;
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
             __builtin_amdgcn_global_load_lds((const void *)(a_src[i] + (int64_t)kt * kTileK),
                                              (__attribute__((address_space(3))) void *)(stage_buf(ic<b>{}) + (4 * wave + i) * 1024),
+                                             16, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            __builtin_amdgcn_global_load_lds((const void *)(bt_src[u] + (int64_t)kt * kTileBytes),
+                                             (__attribute__((address_space(3))) void *)(stage_buf(ic<b>{}) + SA + (2 * wave + u) * 1024),
                                              16, 0, 0);
     };
     auto sstore = [&](auto slot, int buf) {
@@ -802,6 +818,8 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     // activation operands, double-buffered in registers: a step's operands
     // are read from LDS during the previous step's MFMAs.  [tile][k half]
     v4i fa[2][4][2];
+    // FAST: weight operands from LDS as well, double-buffered like fa: [tile][k half]
+    v4i fb[2][2][2];
     auto lds_frags_at = [&](auto F, const int8_t *base) {
         constexpr int f = decltype(F)::value;
 #pragma unroll
@@ -809,9 +827,17 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
 #pragma unroll
             for (int t = 0; t < 4; ++t)
                 fa[f][t][h] = *(const v4i *)(base + (wm * 8 + t * 2 + ((lane & 31) >> 4)) * 1024 + a_rd[h]);
+        if constexpr (FAST) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    fb[f][t][h] = *(const v4i *)(base + SA + (wn * 4 + t * 2 + ((lane & 31) >> 4)) * 1024 + b_rd[h]);
+        }
     };
     auto lds_frags = [&](auto F, int buf) { lds_frags_at(F, &sA[buf][0]); };
-    // step k: activation set F, weight operands from register slot S
+    // step k: activation set F, weight operands from register slot S (FAST:
+    // from operand set F)
     auto mfmas = [&](auto F, auto S) {
         constexpr int f = decltype(F)::value, sl = decltype(S)::value;
 #pragma unroll
@@ -819,7 +845,8 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_i8(fa[f][i][h], rb[sl][j][h], acc[i][j]);
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = mfma32_i8(fa[f][i][h], FAST ? fb[f][j][h] : rb[sl][j][h], acc[i][j]);
                 if (HAS_ZB) accr[i] = mfma32_i8(fa[f][i][h], ones, accr[i]);
             }
     };
@@ -833,22 +860,17 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     // k+PF_DEPTH into slot k % PF_DEPTH, barrier.
     const int KTD = KT - KT % PF_DEPTH;
     if constexpr (FAST) {
-        // Stage s: LDS buffer and weight register slot s % PF_DEPTH,
-        // activation operand set s % 2.  Step k: read step k+1's activation
+        // Stage s: LDS buffer s % PF_DEPTH (activation fragments, then the
+        // weight tiles), operand sets s % 2.  Step k: read step k+1's
         // operands (published by the barrier of step k-1), MFMAs of step k,
-        // load stage k+PF_DEPTH (its buffer held stage k, read in step k-1;
-        // its register slot was just read by the MFMAs), then wait until
-        // stage k+2 has landed in LDS and barrier.  Every step issues 8
-        // vector memory operations (4 to LDS, 4 to registers; stages past
-        // the last repeat the last one), so stage k+2's are complete once at
-        // most 8 (PF_DEPTH - 2) remain outstanding.
-        static_for<PF_DEPTH>([&](auto S) {
-            const int kt = min(decltype(S)::value, KT - 1);
-            dload(S, kt);
-            gload(S, kt);
-        });
+        // copy stage k+PF_DEPTH (its buffer held stage k, read in step
+        // k-1), then wait until stage k+2 has landed in LDS and barrier.
+        // Every step issues 6 copies per wavefront (stages past the last
+        // repeat the last one), so stage k+2's are complete once at most
+        // 6 (PF_DEPTH - 2) remain outstanding.
+        static_for<PF_DEPTH>([&](auto S) { dload(S, min(decltype(S)::value, KT - 1)); });
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<8 * (PF_DEPTH - 2)>();
+        wait_vmcnt<6 * (PF_DEPTH - 2)>();
         lds_barrier();
         lds_frags_at(ic<0>{}, stage_buf(ic<0>{}));
         wait_lgkmcnt0();
@@ -866,10 +888,9 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
             mfmas(ic<j & 1>{}, J);
             const int kn = min(kt + PF_DEPTH, KT - 1);
             dload(J, kn);
-            gload(J, kn);
             pf_schedule_direct<HAS_ZB>();
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<8 * (PF_DEPTH - 2)>();
+            wait_vmcnt<6 * (PF_DEPTH - 2)>();
             lds_barrier();
         };
         for (int base = 0; base < KTD; base += PF_DEPTH)
