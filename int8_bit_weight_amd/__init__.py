@@ -3,7 +3,7 @@
 Only argument marshalling lives here: every step of the computation runs in
 the library's HIP kernels.  PyTorch supplies device memory and the current
 HIP stream.  The binding raises ``ImportError`` if the library has not been
-built (``python -m int8_bit_weight_amd.build``); there is no CPU fallback.
+built (``python int8_bit_weight_amd/build.py``); there is no CPU fallback.
 
 Functions carry the names of the C entry points declared in include/qmm.h:
 ``pack_b_int8``, ``pack_b_int8_raw``, ``quantize_rows_int8``, ``int8_gemm``,
@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libqmm.so")
 import torch  # noqa: E402,F401
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libqmm.so is not built; run `python -m int8_bit_weight_amd.build` "
+    raise ImportError("libqmm.so is not built; run `python int8_bit_weight_amd/build.py` "
                       "(hipcc, gfx950) first")
 
 lib = ctypes.CDLL(LIB_PATH)

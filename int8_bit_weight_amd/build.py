@@ -1,6 +1,6 @@
 """Build libqmm.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m int8_bit_weight_amd.build
+    python int8_bit_weight_amd/build.py
 
 Every source under csrc/ is compiled for gfx950 only, with packed fp32
 instructions disabled and MFMA accumulators in VGPRs, then linked into
