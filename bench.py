@@ -281,6 +281,66 @@ def main() -> int:
                                 "decode_kernel_GB/s": round(kern[M]["gbs"], 2)}
                        for M in rows}}
 
+    # ---------------- the same projections with shared inputs fused ---
+    # q, k and v read the same activations, and so do gate and up: packing
+    # their weights side by side (per-column packing makes the codes, scales
+    # and column sums those of the separate packs) gives 4 calls per layer
+    # instead of 7, with the same output columns bit for bit.
+    if not args.no_extra:
+        groups = ((0, 1, 2), (3,), (4, 5), (6,))
+        fpk = {}
+        for l in range(layers):
+            for gi, grp in enumerate(groups):
+                W = np.concatenate([wl.projection_weight(l, p) for p in grp], axis=1)
+                fpk[(l, gi)] = q.pack_b_int8(torch.from_numpy(W).to(dev))
+        fused = {}
+        for M in rows:
+            lst, fb = [], 0
+            for l in range(layers):
+                for gi, grp in enumerate(groups):
+                    K = projs[grp[0]][1]
+                    N = sum(projs[p][2] for p in grp)
+                    X = next(c[4] for c in calls[M] if c[0] == l and c[1] == grp[0])
+                    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+                    lst.append((fpk[(l, gi)], X, Y))
+                    fb += call_bytes(M, K, N)
+
+            def run_fused(lst=lst):
+                for (pk, X, Y) in lst:
+                    q.int8_gemm_dynamic(X, pk, out_f32=Y)
+            run_fused()
+            torch.cuda.synchronize()
+            # bit-identical to separate calls on the same activations
+            for l in range(layers):
+                for gi, grp in enumerate(groups):
+                    _, X, Yf = lst[l * len(groups) + gi]
+                    c0 = 0
+                    for p in grp:
+                        n = projs[p][2]
+                        Ys = torch.empty((M, n), dtype=torch.float32, device=dev)
+                        q.int8_gemm_dynamic(X, packed[(l, p)], out_f32=Ys)
+                        if not torch.equal(Yf[:, c0:c0 + n].contiguous().view(torch.int32), Ys.view(torch.int32)):
+                            raise RuntimeError("fused projection differs from the separate call (M=%d)" % M)
+                        c0 += n
+            gf = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gf):
+                run_fused()
+            gf.replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(args.steps):
+                gf.replay()
+            b.record()
+            torch.cuda.synchronize()
+            sec = a.elapsed_time(b) * 1e-3 / args.steps
+            fused[str(M)] = {"step_ms": round(sec * 1e3, 4), "GB/s": round(fb / sec / 1e9, 2),
+                             "%HBM": round(100 * fb / sec / 1e9 / HBM_PEAK_GBS, 2),
+                             "calls": len(lst), "call_us": round(sec / len(lst) * 1e6, 3)}
+        extra["fused_qkv_gate_up"] = fused
+        del fpk
+
     # --------------------------------------------- int8 prefill, M = 2048 ---
     if not args.no_extra:
         pre = {}
@@ -341,6 +401,41 @@ def main() -> int:
                                    "%HBM": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2),
                                    "experts": E, "tokens": wl.MOE_TOKENS, "top_k": wl.MOE_USED}
         del rings, ed
+
+        # ------------ lm_head-shaped projection: K = 1024, N = 151936 ---
+        K, N = wl.LM_HEAD_K, wl.LM_HEAD_N
+        Wh = wl.lm_head_weight()
+        Wl = torch.from_numpy(Wh).to(dev)
+        ring = [q.pack_b_int8(Wl) for _ in range(4)]          # 4 copies: ~623 MB, past the MALL
+        del Wl
+        lm = {}
+        for M in wl.LM_HEAD_ROWS:
+            X = torch.from_numpy(wl.lm_head_activations(M, seed_index=M)).to(dev)
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            fs = [(lambda pk=pk, X=X, Y=Y: q.int8_gemm_dynamic(X, pk, out_f32=Y)) for pk in ring]
+            fs[0]()
+            t = float(np.median(time_launches(torch, fs * 3)))
+            b = call_bytes(M, K, N)
+            lm["int8_m%d" % M] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                                  "%HBM": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2)}
+        del ring
+        bd = torch.from_numpy(wl.encode_q4_1(Wh).reshape(-1)).to(dev)
+        del Wh
+        ring = [q.q4_1_repack(bd, K, N) for _ in range(6)]    # 6 copies: ~583 MB
+        del bd
+        wbytes = ring[0].data.numel() - 64
+        for M in wl.LM_HEAD_ROWS:
+            X = torch.from_numpy(wl.lm_head_activations(M, seed_index=100 + M)).to(dev)
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            wsq = q.workspace(q.lib.qmm_q4_1_matmul_workspace_bytes(M, K, N), dev)
+            fs = [(lambda W=W, X=X, Y=Y, wsq=wsq: q.q4_1_matmul(X, W, out=Y, ws=wsq)) for W in ring]
+            fs[0]()
+            t = float(np.median(time_launches(torch, fs * 3)))
+            b = wbytes + 4 * M * K + 4 * M * N
+            lm["q4_1_m%d" % M] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                                  "%HBM": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2)}
+        del ring
+        extra["lm_head_1024x151936"] = lm
 
         # -------------------------------- one-time packing (a1, a5) ---
         K, N = 4096, 14336

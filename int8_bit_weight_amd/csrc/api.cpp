@@ -45,13 +45,32 @@ qmm_status record_status(hipError_t e, const char *variant) {
 // Decode (M <= 32): one workgroup per 16-column strip of the weight, with
 // WAVES wavefronts (4, 8 or 16) splitting its k tiles and TPW (1, 2 or 4)
 // tiles per wavefront per round, chosen so one round covers as much of K as
-// possible.  Prefill (M > 32): 256 x 128 MFMA tiles.  QMM_DECODE_WAVES /
-// QMM_DECODE_TPW override the choice (tuning only: integer results are exact
-// and the fp32 epilogue does not depend on the choice either).
-Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N) {
+// possible.  With many strips (an output projection onto a vocabulary) and
+// A small enough to sit in LDS, one wavefront per strip over the whole k
+// range instead (the wide decode).  Prefill (M > 32): 256 x 128 MFMA tiles.
+// Integer results are exact whatever the choice, and the fp32 epilogue is
+// one per-element formula, so no output bit depends on it.  The wide decode
+// starts at 1024 strips (measured: on the 0.6B projections, 64-384 strips,
+// it was 1.2-2.4x slower per call; on 9496 strips 1.7x faster at M = 1 and
+// 3.8x at M = 16).  QMM_WIDE_MIN_STRIPS overrides the threshold (tuning).
+static int64_t wide_min_strips() {
+    static int64_t v = env_int("QMM_WIDE_MIN_STRIPS", (int)kWideMinStrips);
+    return v;
+}
+static bool use_wide(int64_t M, int64_t K, int64_t N) {
+    const PackedBLayout L = packed_b_layout(K, N);
+    const int mt = M <= 16 ? 1 : 2;
+    return M <= 32 && L.NS >= wide_min_strips() && L.KT * mt <= kWideMaxTiles;
+}
+
+Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N, bool allow_wide) {
     Int8Plan pl{};
     const PackedBLayout L = packed_b_layout(K, N);
-    if (M <= 32) {
+    if (allow_wide && use_wide(M, K, N)) {
+        pl.variant = 2;
+        pl.mt = M <= 16 ? 1 : 2;
+        pl.grid = ceil_div(L.NS, kWideWaves);
+    } else if (M <= 32) {
         pl.variant = 0;
         pl.mt = M <= 16 ? 1 : 2;
         // one round of 16 wavefronts covers K <= 4096 (up to 4 tiles each);
@@ -261,7 +280,12 @@ static int dynamic_groups(int64_t M, int64_t K) {
         }
     return 0;
 }
-static bool dynamic_fused(int64_t M, int64_t K) { return dynamic_groups(M, K) > 0; }
+// Calls the wide decode takes (many columns) quantise in a launch of their
+// own: there the weight bytes per workgroup are few next to a quantisation in
+// every workgroup.
+static bool dynamic_fused(int64_t M, int64_t K, int64_t N) {
+    return dynamic_groups(M, K) > 0 && !use_wide(M, K, N);
+}
 // rows one workgroup of the fused path quantises and multiplies
 static int64_t dynamic_rows(int64_t M, int64_t K) {
     const int g = dynamic_groups(M, K);
@@ -270,7 +294,7 @@ static int64_t dynamic_rows(int64_t M, int64_t K) {
 
 size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     if (M <= 0 || K <= 0 || N <= 0) return 0;
-    if (dynamic_fused(M, K)) return (size_t)plan_int8_gemm(dynamic_rows(M, K), K, N).ws_bytes;
+    if (dynamic_fused(M, K, N)) return (size_t)plan_int8_gemm(dynamic_rows(M, K), K, N, false).ws_bytes;
     return (size_t)(round_up(M * K, 256) + round_up(4 * M, 256));
 }
 
@@ -288,7 +312,7 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
         check_epilogue_ptrs(ep) != QMM_OK)
         return QMM_ERR_INVALID;
     hipStream_t s = (hipStream_t)stream;
-    if (!dynamic_fused(M, K)) {
+    if (!dynamic_fused(M, K, N)) {
         // The row quantiser, then the product.
         int8_t *q = Xq;
         float *rs = row_scale;
@@ -312,7 +336,7 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
     // so the activations stay in registers between the amax and quantise
     // passes.
     const int64_t rows = dynamic_rows(M, K);
-    Int8Plan plan = plan_int8_gemm(rows, K, N);
+    Int8Plan plan = plan_int8_gemm(rows, K, N, false);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
         return QMM_ERR_WORKSPACE;
     Int8GemmParams p{};

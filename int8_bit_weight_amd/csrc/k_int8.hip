@@ -399,6 +399,86 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
     }
 }
 
+// Decode over many columns (M <= 16*MT, N of tens of thousands, such as an
+// output projection onto a vocabulary): one wavefront per 16-column strip
+// over its whole k range, kWideWaves strips per workgroup.  The workgroup
+// copies A' (shifted domain) into LDS once, in MFMA operand order (tile kt,
+// row tile r: lane l's 16 bytes are row 16 r + l % 16, k = 64 kt + 16 (l / 16)
+// .. +15), so each wavefront streams only its own strip's weight tiles,
+// through a ring of D register stages issued before the A copy, and no
+// wavefront waits for another after that copy: the epilogue runs straight
+// from the MFMA accumulators (lane l holds rows 4 (l / 16) + i, column
+// l % 16).  The per-strip workgroups of k_int8_decode instead split one
+// strip's k range over their wavefronts and sum the pieces in LDS, which
+// costs a reduction and a barrier per 16 columns.  Loads past the last tile
+// re-read the last tile (clamped), never out of range.
+template <int MT, int D, bool HAS_ZB, bool AVEC>
+__global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide(Int8GemmParams p) {
+    extern __shared__ v4i s_a[];  // [KT][MT][64]
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int strip_raw = (int)blockIdx.x * kWideWaves + wave;
+    const bool strip_ok = strip_raw < p.NS;
+    const int strip = min(strip_raw, p.NS - 1);
+    const int8_t *codes = p.codes + (int64_t)strip * p.KT * kTileBytes + lane * 16;
+    const int last = p.KT - 1;
+
+    v4i bf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) bf[i] = *(const v4i *)(codes + (int64_t)min(i, last) * kTileBytes);
+    const ColOps col = load_colops_c(p, strip * kTileN + (lane & 15));
+    float rs[MT][4];
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = min(r * 16 + 4 * (lane >> 4) + i, p.M - 1);
+            const float v = (p.row_scale ? p.row_scale : p.col_scale)[m];
+            rs[r][i] = p.row_scale ? v : 1.0f;
+        }
+    const int na = p.KT * MT * 64;
+    for (int u = threadIdx.x; u < na; u += kWideWaves * 64) {
+        const int l = u & 63;
+        const int rt = (u >> 6) % MT;
+        const int kt = (u >> 6) / MT;
+        s_a[u] = load_a16<AVEC>(p, rt * 16 + (l & 15), kt * kTileK + (l >> 4) * 16);
+    }
+    __syncthreads();
+
+    v4i acc[MT], accr[MT];
+#pragma unroll
+    for (int r = 0; r < MT; ++r) {
+        acc[r] = v4i{0, 0, 0, 0};
+        accr[r] = v4i{0, 0, 0, 0};
+    }
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    for (int kt0 = 0; kt0 < p.KT; kt0 += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            const int kt = kt0 + i;
+            if (kt < p.KT) {
+#pragma unroll
+                for (int r = 0; r < MT; ++r) {
+                    const v4i a = s_a[(kt * MT + r) * 64 + lane];
+                    acc[r] = mfma_i8(a, bf[i], acc[r]);
+                    if (HAS_ZB) accr[r] = mfma_i8(a, ones, accr[r]);
+                }
+            }
+            bf[i] = *(const v4i *)(codes + (int64_t)min(kt + D, last) * kTileBytes);
+        }
+    }
+
+    const int n = strip * kTileN + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < MT; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = r * 16 + 4 * (lane >> 4) + i;
+            if (strip_ok && m < p.M && n < p.N)
+                epilogue_store_c(p, m, n, (uint32_t)acc[r][i], HAS_ZB ? accr[r][i] : 0, HAS_ZB, rs[r][i], col);
+        }
+}
+
 // Fused dynamic quantisation for small M x K (the planner takes it when
 // M' * K <= 16384, M' = rows per group rounded up to a power of two <= 16,
 // and K <= 4096; up to 8 row groups run as the grid's second dimension):
@@ -993,6 +1073,24 @@ hipError_t launch_decode(const Int8GemmParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int MT, int D, bool AVEC>
+hipError_t launch_wide_d(const Int8GemmParams &p, hipStream_t s) {
+    const dim3 grid((unsigned)ceil_div(p.NS, kWideWaves));
+    const size_t lds = (size_t)p.KT * MT * 64 * sizeof(v4i);
+    if (p.zBs != 0)
+        hipLaunchKernelGGL((k_int8_decode_wide<MT, D, true, AVEC>), grid, dim3(kWideWaves * 64), lds, s, p);
+    else
+        hipLaunchKernelGGL((k_int8_decode_wide<MT, D, false, AVEC>), grid, dim3(kWideWaves * 64), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int MT, bool AVEC>
+hipError_t launch_wide(const Int8GemmParams &p, hipStream_t s) {
+    if (p.KT * MT > kWideMaxTiles) return hipErrorInvalidValue;
+    if (p.KT <= 8) return launch_wide_d<MT, 8, AVEC>(p, s);
+    return launch_wide_d<MT, 16, AVEC>(p, s);
+}
+
 // (waves, tiles per wave) pairs the planner uses: 4x1, 8x1, 16x1, 16x2, 16x4.
 template <int MT, bool AVEC>
 hipError_t launch_decode_shape(const Int8GemmParams &p, int waves, int tpw, hipStream_t s) {
@@ -1044,6 +1142,12 @@ hipError_t launch_quantize_rows(const float *X, int64_t M, int64_t K, int64_t ld
 
 hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                             const char **variant) {
+    if (plan.variant == 2) {
+        *variant = plan.mt == 1 ? "int8_decode_wide_m16" : "int8_decode_wide_m32";
+        const bool avec = p.a_vec && (p.K % 16) == 0;
+        if (plan.mt == 1) return avec ? launch_wide<1, true>(p, s) : launch_wide<1, false>(p, s);
+        return avec ? launch_wide<2, true>(p, s) : launch_wide<2, false>(p, s);
+    }
     if (plan.variant == 0) {
         *variant = plan.mt == 1 ? "int8_decode_m16" : "int8_decode_m32";
         const bool avec = p.a_vec && (p.K % 16) == 0;

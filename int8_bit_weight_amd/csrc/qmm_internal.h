@@ -103,8 +103,15 @@ struct Int8GemmParams {
     int rpg;               // > 0: rows per row group (blockIdx.y), each group an independent call
 };
 
+// The wide decode (one wavefront per strip over the whole k range) stages
+// all of A' in LDS: at most this many 1 KiB operand tiles (k tiles x 16-row
+// tiles), 64 KiB.  It is planned from this many 16-column strips on.
+constexpr int kWideWaves = 8;        // strips (wavefronts) per workgroup
+constexpr int kWideMaxTiles = 64;
+constexpr int64_t kWideMinStrips = 1024;
+
 struct Int8Plan {
-    int variant;      // 0 = decode (M <= 32), 1 = prefill
+    int variant;      // 0 = decode (M <= 32), 1 = prefill, 2 = wide decode (M <= 32, many columns)
     int mt;           // 16-row tiles (decode)
     int waves;        // waves per workgroup (decode)
     int tpw;          // k tiles per wave per round (decode)
@@ -112,7 +119,9 @@ struct Int8Plan {
     int64_t ws_bytes; // workspace the plan needs (0 for every current variant)
 };
 
-Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N);
+// allow_wide = false: the per-strip decode for M <= 32 whatever N (the fused
+// quantising launch has no wide form)
+Int8Plan plan_int8_gemm(int64_t M, int64_t K, int64_t N, bool allow_wide = true);
 
 hipError_t launch_pack_b_f32(const float *W, int64_t ldw, const PackedBLayout &L, void *packed,
                              hipStream_t s);

@@ -168,6 +168,69 @@ def test_int8_unaligned_lda_and_strided_outputs(q, orc):
     assert (out[:, N:] == 0).all()
 
 
+# ------------------------------------------ wide decode (many columns) ---
+
+@pytest.mark.parametrize("M,K,N,a_u8,zA,zB", [(1, 1024, 16390, False, 0, 0), (16, 100, 16400, True, 131, -5),
+                                              (7, 4096, 16384, False, 0, 7), (32, 2048, 16385, False, -4, 0),
+                                              (20, 64, 20000, True, 0, 0), (3, 1056, 16500, True, 255, 127)])
+def test_wide_decode_full_compare(q, orc, M, K, N, a_u8, zA, zB):
+    """M <= 32 over at least 1024 16-column strips: one wavefront per strip
+    over the whole k range.  Ragged N (a partial last strip and a partial last
+    workgroup of strips), ragged K, uint8 A, zero points (row sums on the
+    MFMA), int32, fp32 and requantised int8 outputs, against the oracle."""
+    g = np.random.default_rng(M * 7 + K + N)
+    A = wl.uniform_u8(g, (M, K)) if a_u8 else wl.uniform_i8(g, (M, K))
+    B = wl.uniform_i8(g, (K, N))
+    rs = g.uniform(0.5, 1.5, M).astype(np.float32)
+    bias_i32 = g.integers(-5000, 5000, N).astype(np.int32)
+    _gemm_case(q, orc, A, zA, B, zB, rs=rs, bias=wl.normal_f32(g, (N,)), scale=np.float32(3e-5),
+               requant=dict(u8=False, bias_i32=bias_i32, zp_out=3),
+               expect_variant="int8_decode_wide_m16" if M <= 16 else "int8_decode_wide_m32")
+
+
+def test_wide_decode_unaligned_a(q, orc):
+    """A with lda = K + 3 (byte loads into the LDS copy)."""
+    import torch
+    g = np.random.default_rng(78)
+    M, K, N = 5, 300, 16400
+    Afull = wl.uniform_i8(g, (M, K + 3))
+    B = wl.uniform_i8(g, (K, N))
+    p = q.pack_b_int8_raw(to_dev(B))
+    y = torch.zeros((M, N), dtype=torch.int32, device=torch_dev())
+    q.int8_gemm(to_dev(Afull)[:, :K], -3, p, 11, out_i32=y)
+    assert q.last_variant() == "int8_decode_wide_m16"
+    ref = orc.int8_gemm_i64(np.ascontiguousarray(Afull[:, :K]), -3, B, 11)
+    assert np.array_equal(to_np(y), ref.astype(np.int32))
+
+
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_wide_decode_dynamic(q, orc, M):
+    """int8_gemm_dynamic over many columns quantises in a launch of its own,
+    then the wide product: the same bits as quantize_rows_int8 + int8_gemm,
+    and the oracle's int32 product."""
+    import torch
+    dev = torch_dev()
+    K, N = 1024, 16500
+    g = np.random.default_rng(M + 5)
+    W = wl.normal_f32(g, (K, N), 0.02)
+    X = wl.normal_f32(g, (M, K))
+    p = q.pack_b_int8(to_dev(W))
+    Xd = to_dev(X)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    y32 = torch.empty((M, N), dtype=torch.int32, device=dev)
+    q.int8_gemm_dynamic(Xd, p, out_f32=y, out_i32=y32)
+    assert q.last_variant() == ("int8_decode_wide_m16" if M <= 16 else "int8_decode_wide_m32")
+    Xq2, rs2 = q.quantize_rows_int8(Xd)
+    y2 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q.int8_gemm(Xq2, 0, p, 0, out_f32=y2, row_scale=rs2)
+    assert np.array_equal(to_np(y).view(np.uint32), to_np(y2).view(np.uint32))
+    Qa, sa = orc.quantize_rows_int8(X)
+    Qb, sb, _ = orc.pack_b_int8(W)
+    Y64 = orc.int8_gemm_i64(Qa, 0, Qb, 0)
+    assert np.array_equal(to_np(y32), Y64.astype(np.int32))
+    assert max_rel_err(to_np(y), orc.epilogue_f64(Y64, sa, sb)) <= F32_TOL
+
+
 def test_int8_empty_is_noop(q):
     import torch
     dev = torch_dev()

@@ -14,7 +14,10 @@ Shapes follow the pages' workloads:
     Q4NX on the AMD NPU");
   * a 2048-token int8 prefill over the same 8B-class shapes;
   * a 128-expert MUL_MAT_ID with top-8 ids read from a stride-17 view
-    ("Zaya 8B Q4NX on the AMD NPU", "The bugs that were the work").
+    ("Zaya 8B Q4NX on the AMD NPU", "The bugs that were the work");
+  * the Qwen3-0.6B output projection (lm_head: hidden 1024 onto a 151936-word
+    vocabulary), one large streaming matmul per decoded token ("The ONNX
+    pack", "What works today": the per-token step it is part of).
 The pages measure on real checkpoints and text; none are available, so these
 seeded draws stand in for them with the stated shapes and distributions.
 """
@@ -48,6 +51,10 @@ MOE_N = 768
 MOE_TOKENS = 512
 MOE_USED = 8
 MOE_IDS_STRIDE = 17
+
+LM_HEAD_K = 1024
+LM_HEAD_N = 151936
+LM_HEAD_ROWS = (1, 16)
 
 Q4_BLOCK = 32
 Q4_BLOCK_BYTES = 20
@@ -195,6 +202,15 @@ def prefill_inputs(K: int, N: int, M: int = PREFILL_M, seed_index: int = 0):
     W = normal_f32(g, (K, N), 0.02)
     rs = (g.uniform(0.5, 1.5, size=M) / 127.0).astype(np.float32)
     return dict(A=A, W=W, rs=rs)
+
+
+def lm_head_weight() -> np.ndarray:
+    """fp32 N(0, 0.02) output-projection weight [1024, 151936] (622 MB)."""
+    return normal_f32(rng(6, 0), (LM_HEAD_K, LM_HEAD_N), 0.02)
+
+
+def lm_head_activations(M: int, seed_index: int = 0) -> np.ndarray:
+    return normal_f32(rng(6, 10 + seed_index), (M, LM_HEAD_K))
 
 
 def moe_ids(T: int = MOE_TOKENS, n_expert: int = MOE_EXPERTS, stride: int = MOE_IDS_STRIDE,
