@@ -57,8 +57,9 @@ def _load():
         "oracle_q4_1_decode": (None, [_P, _I64, _I64, _P]),
         "oracle_q4_1_matmul": (None, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64]),
         "oracle_q4_1_matmul_at": (None, [_P, _I64, _I64, _P, _P, _P, _I64, _P]),
-        "oracle_q4_1_matmul_id": (_INT, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64]),
-        "oracle_q4_1_matmul_id_at": (_INT, [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _P, _I64, _P]),
+        "oracle_q4_1_matmul_id": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _I64,
+                                         _I64]),
+        "oracle_q4_1_matmul_id_at": (_INT, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _P, _I64, _P]),
         "oracle_num_threads": (_INT, []),
     }
     for name, (res, args) in sig.items():
@@ -204,33 +205,48 @@ def q4_1_matmul_at(X: np.ndarray, blocks: np.ndarray, K: int, N: int, im, in_) -
     return out
 
 
+def _moe_x(X: np.ndarray, n_used: int):
+    """Activations [T, K] (shared by the slots) or [T, n_used, K] (one row per
+    slot): contiguous fp32 array, K, token stride and slot stride."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if X.ndim == 2:
+        return X, X.shape[1], X.shape[1], 0
+    assert X.ndim == 3 and X.shape[1] == n_used
+    return X, X.shape[2], X.shape[1] * X.shape[2], X.shape[2]
+
+
 def q4_1_matmul_id(X: np.ndarray, experts: np.ndarray, n_expert: int, K: int, N: int,
                    ids: np.ndarray, n_used: int) -> np.ndarray:
-    """ids: int32 [T, ids_row_stride]; returns Y [T, n_used, N] fp64."""
-    X = np.ascontiguousarray(X, dtype=np.float32)
+    """X: fp32 [T, K] (shared form) or [T, n_used, K] (per-slot form); ids:
+    int32 [T, ids_row_stride]; returns Y [T, n_used, N] fp64."""
+    X, kx, ldx, ldx_slot = _moe_x(X, n_used)
+    assert kx == K
     experts = np.ascontiguousarray(experts, dtype=np.uint8)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     T = X.shape[0]
     assert ids.shape[0] == T and ids.shape[1] >= n_used
     assert experts.size == n_expert * (K // 32) * N * 20
     Y = np.empty((T, n_used, N), dtype=np.float64)
-    rc = _load().oracle_q4_1_matmul_id(_ptr(X), T, K, K, _ptr(experts), n_expert, N, _ptr(ids),
+    rc = _load().oracle_q4_1_matmul_id(_ptr(X), T, K, ldx, ldx_slot, _ptr(experts), n_expert, N, _ptr(ids),
                                         ids.shape[1], n_used, _ptr(Y), N, n_used * N)
     if rc != 0:
         raise ValueError("expert id out of range")
     return Y
 
 
-def q4_1_matmul_id_at(X, experts, n_expert, K, N, ids, it, is_, in_) -> np.ndarray:
-    X = np.ascontiguousarray(X, dtype=np.float32)
+def q4_1_matmul_id_at(X, experts, n_expert, K, N, ids, it, is_, in_, n_used=None) -> np.ndarray:
+    """Outputs (it[i], is_[i], in_[i]); X as in q4_1_matmul_id (the per-slot
+    form needs n_used)."""
+    X, kx, ldx, ldx_slot = _moe_x(X, n_used if X.ndim == 3 else 0)
+    assert kx == K
     experts = np.ascontiguousarray(experts, dtype=np.uint8)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     it = np.ascontiguousarray(it, dtype=np.int64)
     is_ = np.ascontiguousarray(is_, dtype=np.int64)
     in_ = np.ascontiguousarray(in_, dtype=np.int64)
     out = np.empty(it.shape, dtype=np.float64)
-    rc = _load().oracle_q4_1_matmul_id_at(_ptr(X), K, K, _ptr(experts), n_expert, N, _ptr(ids), ids.shape[1],
-                                           _ptr(it), _ptr(is_), _ptr(in_), it.size, _ptr(out))
+    rc = _load().oracle_q4_1_matmul_id_at(_ptr(X), K, ldx, ldx_slot, _ptr(experts), n_expert, N, _ptr(ids),
+                                           ids.shape[1], _ptr(it), _ptr(is_), _ptr(in_), it.size, _ptr(out))
     if rc != 0:
         raise ValueError("expert id out of range")
     return out

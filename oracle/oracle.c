@@ -267,8 +267,10 @@ void oracle_q4_1_matmul_at(const float *X, int64_t K, int64_t ldx, const uint8_t
  * view (17 sorted experts per token, row stride 17 int32); only the first
  * n_expert_used of each row are used and they must be read through the
  * stride.  [P5] "What's next": gate/up experts read the shared activation
- * form [k, ntokens], i.e. token t's row for every slot. */
-int oracle_q4_1_matmul_id(const float *X, int64_t T, int64_t K, int64_t ldx,
+ * form [k, ntokens], i.e. token t's row for every slot (ldx_slot = 0); down
+ * experts read a row of their own per (token, slot), the per-expert form
+ * [k, n_expert_used, ntokens] (row at t*ldx + s*ldx_slot). */
+int oracle_q4_1_matmul_id(const float *X, int64_t T, int64_t K, int64_t ldx, int64_t ldx_slot,
                           const uint8_t *experts, int64_t n_expert, int64_t N,
                           const int32_t *ids, int64_t ids_row_stride, int64_t n_used,
                           double *Y, int64_t ldy_slot, int64_t ldy_token) {
@@ -287,7 +289,7 @@ int oracle_q4_1_matmul_id(const float *X, int64_t T, int64_t K, int64_t ldx,
             for (int64_t n = 0; n < N; ++n) {
                 double acc = 0.0;
                 for (int64_t k = 0; k < K; ++k)
-                    acc += (double)X[t * ldx + k] * q4_1_value(W, K, k, n);
+                    acc += (double)X[t * ldx + s * ldx_slot + k] * q4_1_value(W, K, k, n);
                 Y[t * ldy_token + s * ldy_slot + n] = acc;
             }
         }
@@ -295,7 +297,7 @@ int oracle_q4_1_matmul_id(const float *X, int64_t T, int64_t K, int64_t ldx,
     return 0;
 }
 
-int oracle_q4_1_matmul_id_at(const float *X, int64_t K, int64_t ldx,
+int oracle_q4_1_matmul_id_at(const float *X, int64_t K, int64_t ldx, int64_t ldx_slot,
                              const uint8_t *experts, int64_t n_expert, int64_t N,
                              const int32_t *ids, int64_t ids_row_stride,
                              const int64_t *it, const int64_t *is, const int64_t *in,
@@ -312,7 +314,7 @@ int oracle_q4_1_matmul_id_at(const float *X, int64_t K, int64_t ldx,
         const uint8_t *W = experts + (int64_t)e * expert_bytes;
         double acc = 0.0;
         for (int64_t k = 0; k < K; ++k)
-            acc += (double)X[it[i] * ldx + k] * q4_1_value(W, K, k, in[i]);
+            acc += (double)X[it[i] * ldx + is[i] * ldx_slot + k] * q4_1_value(W, K, k, in[i]);
         out[i] = acc;
     }
     return 0;

@@ -80,17 +80,19 @@ void oracle_q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx,
 void oracle_q4_1_matmul_at(const float *X, int64_t K, int64_t ldx, const uint8_t *blocks,
                            const int64_t *im, const int64_t *in, int64_t count, double *out);
 
-/* MUL_MAT_ID with the shared activation form: for t < T, s < n_used,
- * e = ids[t*ids_row_stride + s], Y[t][s][:] = X[t] * W_e.  Experts are
- * canonical q4_1 matrices stored one after another (K/32*N blocks each).
- * Y element (t,s,n) lives at t*ldy_token + s*ldy_slot + n.
+/* MUL_MAT_ID: for t < T, s < n_used, e = ids[t*ids_row_stride + s],
+ * Y[t][s][:] = x(t,s) * W_e, where the activation row x(t,s) starts at
+ * X + t*ldx + s*ldx_slot: ldx_slot = 0 is the shared form (token t's row for
+ * every slot), ldx_slot >= K the per-slot form.  Experts are canonical q4_1
+ * matrices stored one after another (K/32*N blocks each).  Y element (t,s,n)
+ * lives at t*ldy_token + s*ldy_slot + n.
  * Returns 0, or -1 if an id lies outside [0, n_expert). */
-int oracle_q4_1_matmul_id(const float *X, int64_t T, int64_t K, int64_t ldx,
+int oracle_q4_1_matmul_id(const float *X, int64_t T, int64_t K, int64_t ldx, int64_t ldx_slot,
                           const uint8_t *experts, int64_t n_expert, int64_t N,
                           const int32_t *ids, int64_t ids_row_stride, int64_t n_used,
                           double *Y, int64_t ldy_slot, int64_t ldy_token);
 /* Sampled form: output (t[i], s[i], n[i]). */
-int oracle_q4_1_matmul_id_at(const float *X, int64_t K, int64_t ldx,
+int oracle_q4_1_matmul_id_at(const float *X, int64_t K, int64_t ldx, int64_t ldx_slot,
                              const uint8_t *experts, int64_t n_expert, int64_t N,
                              const int32_t *ids, int64_t ids_row_stride,
                              const int64_t *it, const int64_t *is, const int64_t *in,

@@ -214,3 +214,57 @@ def test_moe_sampled(orc):
     in_ = np.array([15, 3, 0])
     got = orc.q4_1_matmul_id_at(X, experts, E, K, N, ids, it, is_, in_)
     assert np.array_equal(got, Y[it, is_, in_])
+
+
+# ------------------------------------- MUL_MAT_ID, per-slot activations ---
+# Down experts read an activation row of their own per (token, slot), the
+# per-expert form [k, n_expert_used, ntokens] ("Zaya 8B Q4NX on the AMD NPU",
+# "What's next": reading token t's shared row for every slot was the bug).
+
+def test_moe_per_slot_reduces_to_shared(orc):
+    """Every slot row equal to the token's row: the shared form's result."""
+    g = np.random.default_rng(41)
+    E, K, N, T, n_used = 7, 64, 24, 9, 3
+    experts, X, ids = _small_moe(g, E, K, N, T, n_used=n_used)
+    X3 = np.repeat(X[:, None, :], n_used, axis=1)
+    assert np.array_equal(orc.q4_1_matmul_id(X3, experts, E, K, N, ids, n_used),
+                          orc.q4_1_matmul_id(X, experts, E, K, N, ids, n_used))
+
+
+def test_moe_per_slot_against_numpy(orc):
+    """Each (t, s) output is numpy's fp64 product of that slot's row with the
+    decoded expert (decode pinned by its closed form); reading slot 0's row for
+    every slot (the pages' bug) gives a different result."""
+    g = np.random.default_rng(42)
+    E, K, N, T, n_used = 6, 96, 20, 7, 4
+    experts, _, ids = _small_moe(g, E, K, N, T, n_used=n_used)
+    X3 = wl.normal_f32(g, (T, n_used, K))
+    Y = orc.q4_1_matmul_id(X3, experts, E, K, N, ids, n_used)
+    W = [orc.q4_1_decode(experts[e], K, N) for e in range(E)]
+    for t in range(T):
+        for s in range(n_used):
+            ref = X3[t, s].astype(np.float64) @ W[ids[t, s]]
+            assert np.allclose(Y[t, s], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    bug = orc.q4_1_matmul_id(np.ascontiguousarray(X3[:, 0]), experts, E, K, N, ids, n_used)
+    assert np.array_equal(bug[:, 0], Y[:, 0])
+    assert not np.allclose(bug[:, 1:], Y[:, 1:])
+
+
+def test_moe_per_slot_permutation_and_sampled(orc):
+    """Permuting the slots (ids and rows together) permutes the outputs; the
+    sampled form reads the same rows."""
+    g = np.random.default_rng(43)
+    E, K, N, T, n_used = 8, 64, 16, 6, 5
+    experts, _, ids = _small_moe(g, E, K, N, T, n_used=n_used)
+    X3 = wl.normal_f32(g, (T, n_used, K))
+    Y = orc.q4_1_matmul_id(X3, experts, E, K, N, ids, n_used)
+    perm = g.permutation(n_used)
+    ids_p = ids.copy()
+    ids_p[:, :n_used] = ids[:, perm]
+    Yp = orc.q4_1_matmul_id(np.ascontiguousarray(X3[:, perm]), experts, E, K, N, ids_p, n_used)
+    assert np.array_equal(Yp, Y[:, perm])
+    it = np.array([0, 5, 3, 2])
+    is_ = np.array([4, 0, 2, 1])
+    in_ = np.array([15, 3, 0, 7])
+    got = orc.q4_1_matmul_id_at(X3, experts, E, K, N, ids, it, is_, in_, n_used=n_used)
+    assert np.array_equal(got, Y[it, is_, in_])
