@@ -395,11 +395,34 @@ def main() -> int:
               for buf, st in rings]
         fs[0]()
         t = float(np.median(time_launches(torch, fs * 5)))
-        wb = E * (rings[0][0].numel() // E - 64)
+        wb = E * (K * N // 2 + (K // 32) * N * 4)     # codes + bf16 (d, m) per block
         b = wb + X.numel() * 4 + wl.MOE_TOKENS * wl.MOE_IDS_STRIDE * 4 + Y.numel() * 4
         extra["q4_1_matmul_id"] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
                                    "%HBM": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2),
                                    "experts": E, "tokens": wl.MOE_TOKENS, "top_k": wl.MOE_USED}
+        del rings, ed
+
+        # MUL_MAT_ID of the down experts: a row per (token, slot)
+        d = wl.moe_down_inputs()
+        K, N = wl.MOE_DOWN_K, wl.MOE_DOWN_N
+        ed = torch.from_numpy(d["experts"]).to(dev)
+        rings = [q.q4_1_repack_experts(ed, K, N) for _ in range(4)]   # 4 copies: ~500 MB
+        X = torch.from_numpy(d["X"]).to(dev)
+        ids = torch.from_numpy(d["ids"]).to(dev)
+        Y = torch.empty((wl.MOE_TOKENS, wl.MOE_USED, N), dtype=torch.float32, device=dev)
+        wsm = q.workspace(q.lib.qmm_q4_1_matmul_id_per_slot_workspace_bytes(wl.MOE_TOKENS, wl.MOE_USED, E, K, N),
+                          dev)
+        fs = [(lambda buf=buf, st=st: q.q4_1_matmul_id_per_slot(X, buf, E, K, N, st, ids, wl.MOE_USED, out=Y,
+                                                               ws=wsm))
+              for buf, st in rings]
+        fs[0]()
+        t = float(np.median(time_launches(torch, fs * 5)))
+        wb = E * (K * N // 2 + (K // 32) * N * 4)     # codes + bf16 (d, m) per block
+        b = wb + X.numel() * 4 + wl.MOE_TOKENS * wl.MOE_IDS_STRIDE * 4 + Y.numel() * 4
+        extra["q4_1_matmul_id_per_slot"] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                                            "%HBM": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2),
+                                            "experts": E, "K": K, "N": N, "tokens": wl.MOE_TOKENS,
+                                            "top_k": wl.MOE_USED}
         del rings, ed
 
         # ------------ lm_head-shaped projection: K = 1024, N = 151936 ---

@@ -262,6 +262,29 @@ qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t l
                           float *Y, int64_t ldy_slot, int64_t ldy_token,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace bytes q4_1_matmul_id_per_slot needs. */
+size_t qmm_q4_1_matmul_id_per_slot_workspace_bytes(int64_t n_tokens, int64_t n_used, int64_t n_expert,
+                                                   int64_t K, int64_t N);
+
+/*
+ * q4_1_matmul_id_per_slot: MUL_MAT_ID whose activations hold a row of their
+ * own per (token, slot), the per-expert form [k, n_expert_used, ntokens] the
+ * down experts read ([P5] "What's next": reading token t's shared row for
+ * every slot made every expert compute with the first slot's activation).
+ * For t < n_tokens and s < n_used:
+ *   e = ids[t*ids_row_stride + s];
+ *   Y[t*ldy_token + s*ldy_slot + n] = X[t*ldx_token + s*ldx_slot + :] . W_e[:, n]
+ *   X         device fp32, ldx_slot >= K, ldx_token >= n_used*ldx_slot
+ * Every other argument, the error codes and the workspace rule are those of
+ * q4_1_matmul_id; the workspace grows with n_tokens*n_used activation rows
+ * instead of n_tokens.
+ */
+qmm_status q4_1_matmul_id_per_slot(const float *X, int64_t n_tokens, int64_t K, int64_t ldx_slot,
+                                   int64_t ldx_token, const void *Wexperts, int64_t n_expert, int64_t N,
+                                   size_t expert_stride, const int32_t *ids, int64_t ids_row_stride,
+                                   int64_t n_used, float *Y, int64_t ldy_slot, int64_t ldy_token,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------- helpers --- */
 
 const char *qmm_status_string(qmm_status s);

@@ -7,7 +7,7 @@ built (``python int8_bit_weight_amd/build.py``); there is no CPU fallback.
 
 Functions carry the names of the C entry points declared in include/qmm.h:
 ``pack_b_int8``, ``pack_b_int8_raw``, ``quantize_rows_int8``, ``int8_gemm``,
-``q4_1_repack``, ``q4_1_matmul``, ``q4_1_matmul_id``.
+``q4_1_repack``, ``q4_1_matmul``, ``q4_1_matmul_id``, ``q4_1_matmul_id_per_slot``.
 """
 from __future__ import annotations
 
@@ -73,6 +73,9 @@ _SIGS = {
     "qmm_q4_1_matmul_id_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
     "q4_1_matmul_id": (_INT, [_P, _I64, _I64, _I64, _P, _I64, _I64, _SZ, _P, _I64, _I64,
                               _P, _I64, _I64, _P, _SZ, _P]),
+    "qmm_q4_1_matmul_id_per_slot_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
+    "q4_1_matmul_id_per_slot": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _I64, _I64, _SZ, _P, _I64, _I64,
+                                       _P, _I64, _I64, _P, _SZ, _P]),
     "qmm_status_string": (ctypes.c_char_p, [_INT]),
     "qmm_last_hip_error": (_INT, []),
     "qmm_last_variant": (ctypes.c_char_p, []),
@@ -350,4 +353,23 @@ def q4_1_matmul_id(X, experts, n_expert: int, K: int, N: int, expert_stride: int
     _check("q4_1_matmul_id", lib.q4_1_matmul_id(_ptr(X), T, K, X.stride(0), _ptr(experts), n_expert, N,
                                                 expert_stride, _ptr(ids), ids.stride(0), n_used, _ptr(Y),
                                                 Y.stride(1), Y.stride(0), _ptr(ws), wsz, _stream(stream)))
+    return Y
+
+
+def q4_1_matmul_id_per_slot(X, experts, n_expert: int, K: int, N: int, expert_stride: int, ids, n_used: int,
+                            out=None, ws=None, stream=None):
+    """MUL_MAT_ID with a row per (token, slot): Y[t, s] = X[t, s] @ W_{ids[t, s]}
+    for fp32 X [T, n_used, K] (unit stride along K)."""
+    torch = _torch()
+    T = X.shape[0]
+    assert X.dim() == 3 and X.shape[1] == n_used and X.shape[2] == K and X.stride(2) == 1
+    Y = torch.empty((T, n_used, N), dtype=torch.float32, device=X.device) if out is None else out
+    need = lib.qmm_q4_1_matmul_id_per_slot_workspace_bytes(T, n_used, n_expert, K, N)
+    if ws is None and need > 0:
+        ws = workspace(need, X.device)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("q4_1_matmul_id_per_slot",
+           lib.q4_1_matmul_id_per_slot(_ptr(X), T, K, X.stride(1), X.stride(0), _ptr(experts), n_expert, N,
+                                       expert_stride, _ptr(ids), ids.stride(0), n_used, _ptr(Y), Y.stride(1),
+                                       Y.stride(0), _ptr(ws), wsz, _stream(stream)))
     return Y

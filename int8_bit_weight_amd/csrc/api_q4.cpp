@@ -82,9 +82,10 @@ Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
     return pl;
 }
 
-MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N) {
+MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N, bool per_slot) {
     MoePlan pl{};
     const int64_t P = T * n_used;
+    const int64_t R = per_slot ? P : T;  // activation rows split
     pl.rpc = 32;
     pl.max_chunks = ceil_div(P, pl.rpc) + E;
     pl.ws_sorted_off = 0;
@@ -94,9 +95,9 @@ MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N) 
     // scale exponents
     const Q4Layout L = q4_layout(K, N);
     pl.ws_xs_off = pl.ws_misc_off + 256;
-    pl.ws_xsum_off = pl.ws_xs_off + round_up(T * L.NB * 128, 256);
-    pl.ws_xsc_off = pl.ws_xsum_off + round_up(T * L.NQ * 48, 256);
-    pl.ws_bytes = pl.ws_xsc_off + round_up(T * 4, 256);
+    pl.ws_xsum_off = pl.ws_xs_off + round_up(R * L.NB * 128, 256);
+    pl.ws_xsc_off = pl.ws_xsum_off + round_up(R * L.NQ * 48, 256);
+    pl.ws_bytes = pl.ws_xsc_off + round_up(R * 4, 256);
     return pl;
 }
 
@@ -170,16 +171,27 @@ qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx, const 
 size_t qmm_q4_1_matmul_id_workspace_bytes(int64_t n_tokens, int64_t n_used, int64_t n_expert, int64_t K,
                                           int64_t N) {
     if (n_tokens <= 0 || n_used <= 0 || n_expert <= 0 || K <= 0 || N <= 0 || K % 32 != 0) return 0;
-    return (size_t)plan_q4_moe(n_tokens, n_used, n_expert, K, N).ws_bytes;
+    return (size_t)plan_q4_moe(n_tokens, n_used, n_expert, K, N, false).ws_bytes;
 }
 
-qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t ldx, const void *Wexperts,
-                          int64_t n_expert, int64_t N, size_t expert_stride, const int32_t *ids,
-                          int64_t ids_row_stride, int64_t n_used, float *Y, int64_t ldy_slot, int64_t ldy_token,
-                          void *workspace, size_t workspace_bytes, void *stream) {
-    if (n_tokens < 0 || K <= 0 || N < 0 || ldx < K || n_expert <= 0 || n_used <= 0 ||
-        ids_row_stride < n_used || ldy_slot < N || ldy_token < n_used * ldy_slot)
+size_t qmm_q4_1_matmul_id_per_slot_workspace_bytes(int64_t n_tokens, int64_t n_used, int64_t n_expert, int64_t K,
+                                                   int64_t N) {
+    if (n_tokens <= 0 || n_used <= 0 || n_expert <= 0 || K <= 0 || N <= 0 || K % 32 != 0) return 0;
+    return (size_t)plan_q4_moe(n_tokens, n_used, n_expert, K, N, true).ws_bytes;
+}
+
+}  // extern "C"
+
+// Both MUL_MAT_ID forms: the shared one (ldx_slot = 0: token t's row for
+// every slot) and the per-slot one (a row per (token, slot) pair).
+static qmm_status moe_call(const float *X, int64_t n_tokens, int64_t K, int64_t ldx, int64_t ldx_slot,
+                           bool per_slot, const void *Wexperts, int64_t n_expert, int64_t N, size_t expert_stride,
+                           const int32_t *ids, int64_t ids_row_stride, int64_t n_used, float *Y, int64_t ldy_slot,
+                           int64_t ldy_token, void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_tokens < 0 || K <= 0 || N < 0 || n_expert <= 0 || n_used <= 0 || ids_row_stride < n_used ||
+        ldy_slot < N || ldy_token < n_used * ldy_slot)
         return QMM_ERR_INVALID;
+    if (per_slot ? (ldx_slot < K || ldx < n_used * ldx_slot) : ldx < K) return QMM_ERR_INVALID;
     if (K % 32 != 0) return QMM_ERR_UNSUPPORTED;
     if (n_expert > 8192 || n_tokens * n_used > INT32_MAX / 2 || K > INT32_MAX / 2 || N > INT32_MAX / 2)
         return QMM_ERR_UNSUPPORTED;
@@ -189,7 +201,7 @@ qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t l
         return QMM_ERR_INVALID;
     const Q4Layout L = q4_layout(K, N);
     if (expert_stride < (size_t)L.total || expert_stride % 256 != 0) return QMM_ERR_INVALID;
-    const MoePlan pl = plan_q4_moe(n_tokens, n_used, n_expert, K, N);
+    const MoePlan pl = plan_q4_moe(n_tokens, n_used, n_expert, K, N, per_slot);
     if (!workspace || workspace_bytes < (size_t)pl.ws_bytes || !aligned_to(workspace, 256))
         return QMM_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
@@ -197,14 +209,18 @@ qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t l
     int32_t *sorted = (int32_t *)(ws + pl.ws_sorted_off);
     int32_t *chunk_info = (int32_t *)(ws + pl.ws_chunk_off);
     int32_t *misc = (int32_t *)(ws + pl.ws_misc_off);
+    const bool xvec = aligned_to(X, 16) && (ldx % 4 == 0) && (ldx_slot % 4 == 0);
     MoeSplit sp{};
     sp.X = X;
     sp.ldx = ldx;
+    sp.ldx_slot = per_slot ? ldx_slot : 0;
     sp.T = (int)n_tokens;
+    sp.per = per_slot ? (int)n_used : 1;
+    sp.R = (int)(per_slot ? n_tokens * n_used : n_tokens);
     sp.K = (int)K;
     sp.NB = (int)L.NB;
     sp.NQ = (int)L.NQ;
-    sp.x_vec = aligned_to(X, 16) && (ldx % 4 == 0);
+    sp.x_vec = xvec;
     sp.xs = ws + pl.ws_xs_off;
     sp.xsum = ws + pl.ws_xsum_off;
     sp.xsc = (int32_t *)(ws + pl.ws_xsc_off);
@@ -223,7 +239,7 @@ qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t l
         p.K = (int)K;
         p.X = X;
         p.ldx = ldx;
-        p.x_vec = aligned_to(X, 16) && (ldx % 4 == 0);
+        p.x_vec = xvec;
         p.Y = Y;
         p.sorted = sorted;
         p.chunk_info = chunk_info;
@@ -235,9 +251,28 @@ qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t l
         p.xsum = sp.xsum;
         p.xsc = sp.xsc;
         p.zero16 = sp.zero16;
-        e = launch_q4_moe(p, pl.max_chunks, s, &variant);
+        e = launch_q4_moe(p, per_slot, pl.max_chunks, s, &variant);
     }
     return record_status(e, variant);
+}
+
+extern "C" {
+
+qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t ldx, const void *Wexperts,
+                          int64_t n_expert, int64_t N, size_t expert_stride, const int32_t *ids,
+                          int64_t ids_row_stride, int64_t n_used, float *Y, int64_t ldy_slot, int64_t ldy_token,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    return moe_call(X, n_tokens, K, ldx, 0, false, Wexperts, n_expert, N, expert_stride, ids, ids_row_stride,
+                    n_used, Y, ldy_slot, ldy_token, workspace, workspace_bytes, stream);
+}
+
+qmm_status q4_1_matmul_id_per_slot(const float *X, int64_t n_tokens, int64_t K, int64_t ldx_slot,
+                                   int64_t ldx_token, const void *Wexperts, int64_t n_expert, int64_t N,
+                                   size_t expert_stride, const int32_t *ids, int64_t ids_row_stride, int64_t n_used,
+                                   float *Y, int64_t ldy_slot, int64_t ldy_token, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    return moe_call(X, n_tokens, K, ldx_token, ldx_slot, true, Wexperts, n_expert, N, expert_stride, ids,
+                    ids_row_stride, n_used, Y, ldy_slot, ldy_token, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

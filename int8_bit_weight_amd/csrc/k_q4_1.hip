@@ -993,8 +993,14 @@ __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ p
 //     zero piece) against the record's m values, accumulated into y;
 //   * the epilogue undoes the token's scale: Y = y * 2^-sc[t].
 // Rows past the chunk repeat its last row (their outputs are not stored);
-// blocks past K read the last block (their d = m = 0).
-template <int MT, int WAVES, int C, int MINW>
+// blocks past K read the last block (their d = m = 0).  Both row tiles are
+// multiplied even when the chunk has at most 16 rows.  With a wave-uniform
+// branch skipping the second tile's MFMAs, every chunk of <= 16 rows came out
+// wrong in the per-slot build of this kernel (measured over chunk sizes 1 to
+// 40) while the shared build of the same source was right; without the
+// branch the k loop has no branch between an MFMA and the instructions that
+// read its result, and both builds are right at every chunk size.
+template <int MT, int WAVES, int C, int MINW, bool PER_SLOT>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_moe(Q4Params p) {
     constexpr int ROWS = MT * 16, SPG = WAVES * C;
     constexpr int NFD = 4 * 2 * MT;  // d-term fragments per chunk: block x term x tile
@@ -1016,9 +1022,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     const int nrows = p.chunk_info[job * 3 + 2];
     const uint8_t *hdr = p.recs + (int64_t)expert * p.expert_stride;
     const uint8_t *recs = hdr + kHeaderBytes;
-    const int ntile = (nrows + 15) >> 4;
     const int NQ = p.NQ;
-    if (tid < ROWS) sTok[tid] = p.sorted[row0 + min(tid, nrows - 1)] / p.n_used;
+    // activation row of each row of the chunk: the token (shared form) or the
+    // (token, slot) pair itself (per-slot form)
+    if (tid < ROWS) {
+        const int pair = p.sorted[row0 + min(tid, nrows - 1)];
+        sTok[tid] = PER_SLOT ? pair : pair / p.n_used;
+    }
     __syncthreads();
 
     // ---- gather sources: fragment f = wave + WAVES i of the stage (clamped:
@@ -1113,7 +1123,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                 const float d = bf16_lo_f32((uint32_t)bd[st][j][bl]);
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
-                    if (t > 0 && ntile <= t) continue;  // row tile without rows (wave-uniform)
                     v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t][0], bop, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t][1], bop, acc, 0, 0, 0);
 #pragma unroll
@@ -1129,7 +1138,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            if (t > 0 && ntile <= t) continue;
             v8bf xm[3];
 #pragma unroll
             for (int u = 0; u < 3; ++u) xm[u] = *(const v8bf *)(Mf + (u * MT + t) * 1024 + a_off);
@@ -1173,7 +1181,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                     const int tk = pair / p.n_used;
                     const int sl = pair - tk * p.n_used;
                     p.Y[(int64_t)tk * p.ldy_token + (int64_t)sl * p.ldy_slot + n] =
-                        __builtin_ldexpf(y[t][j][v], -p.xsc[tk]);
+                        __builtin_ldexpf(y[t][j][v], -p.xsc[PER_SLOT ? pair : tk]);
                 }
             }
 }
@@ -1203,7 +1211,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 constexpr int kSplitTokensPerGroup = 4;
 __device__ void moe_split_token(const MoeSplit &sp, int t, int ltid, float *s_max) {
     const int lane = ltid & 63, wl = ltid >> 6;  // wavefront of the token (0..3)
-    const float *xr = sp.X + (int64_t)t * sp.ldx;
+    // activation row t: token t (shared form), or pair t = token * per + slot
+    const float *xr = sp.X + (int64_t)(t / sp.per) * sp.ldx + (int64_t)(t % sp.per) * sp.ldx_slot;
     const int npc = sp.NQ * 16;  // pieces (block, k-octet), whole records
     auto load8 = [&](int pc, float (&v)[8]) {
         const int b = pc >> 2, g = pc & 3;
@@ -1295,8 +1304,8 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
         const int grp = threadIdx.x >> 8;
         const int t = ((int)blockIdx.x - 1) * kSplitTokensPerGroup + grp;
         if (blockIdx.x == 1 && threadIdx.x == 0) *(v4i *)sp.zero16 = v4i{0, 0, 0, 0};
-        // tokens past T repeat token T - 1 (the same values, written again)
-        moe_split_token(sp, min(t, T - 1), threadIdx.x & 255, s_max[grp]);
+        // rows past R repeat row R - 1 (the same values, written again)
+        moe_split_token(sp, min(t, sp.R - 1), threadIdx.x & 255, s_max[grp]);
         return;
     }
     extern __shared__ int32_t sh[];
@@ -1502,19 +1511,23 @@ hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, i
                             int rpc, int32_t *sorted, int32_t *chunk_info, int32_t *nchunks, int32_t *err,
                             const MoeSplit &sp, hipStream_t s) {
     const size_t shmem = (size_t)E * 3 * sizeof(int32_t);
-    // workgroup 0 routes; workgroups 1.. split four tokens each
-    const unsigned grid = 1u + (unsigned)ceil_div(T, kSplitTokensPerGroup);
+    // workgroup 0 routes; workgroups 1.. split four activation rows each
+    const unsigned grid = 1u + (unsigned)ceil_div(sp.R, kSplitTokensPerGroup);
     hipLaunchKernelGGL(k_moe_route, dim3(grid), dim3(1024), shmem, s, ids, ids_stride, (int)T, (int)n_used, (int)E,
                        rpc, sorted, chunk_info, nchunks, err, sp);
     return hipGetLastError();
 }
 
-hipError_t launch_q4_moe(const Q4Params &p, int64_t max_chunks, hipStream_t s, const char **variant) {
+hipError_t launch_q4_moe(const Q4Params &p, bool per_slot, int64_t max_chunks, hipStream_t s,
+                         const char **variant) {
     constexpr int WAVES = 8, C = 2;
     const int64_t groups = ceil_div(p.NS, C * WAVES);
     *variant = "q4_moe_m32";
     const dim3 g((unsigned)(groups * max_chunks)), b(WAVES * 64);
-    hipLaunchKernelGGL((k_q4_moe<2, WAVES, C, 4>), g, b, 0, s, p);
+    if (per_slot)
+        hipLaunchKernelGGL((k_q4_moe<2, WAVES, C, 4, true>), g, b, 0, s, p);
+    else
+        hipLaunchKernelGGL((k_q4_moe<2, WAVES, C, 4, false>), g, b, 0, s, p);
     return hipGetLastError();
 }
 

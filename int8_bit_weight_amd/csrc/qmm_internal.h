@@ -190,9 +190,9 @@ struct Q4Params {
     int n_used;
     int64_t ldy_slot, ldy_token;
     // MoE activations split once per call by the routing launch
-    const uint8_t *xs;        // [T][NB][2][4] 16-byte pieces: two fp16 terms of x * 2^sc[t]
-    const uint8_t *xsum;      // [T][NQ][3] 16 bytes: the record's four block sums (bf16 terms)
-    const int32_t *xsc;       // [T] scale exponents sc[t]
+    const uint8_t *xs;        // [R][NB][2][4] 16-byte pieces: two fp16 terms of x * 2^sc[a]
+    const uint8_t *xsum;      // [R][NQ][3] 16 bytes: the record's four block sums (bf16 terms)
+    const int32_t *xsc;       // [R] scale exponents sc[a] (R activation rows, see MoeSplit)
     const uint8_t *zero16;    // 16 zero bytes
 };
 
@@ -200,10 +200,13 @@ struct Q4Params {
 // sc[t] = 15 - e with the token's max |x| = f 2^e, f in [0.5, 1); each piece
 // (block b, k-octet g) of x * 2^sc as two fp16 terms, and each block's sum
 // of x * 2^sc as three bf16 terms, four blocks (a record) per 16 bytes.
+// The MoE activation split works on activation rows: R = T tokens (shared
+// form, per = 1) or R = T * n_used (token, slot) pairs (per-slot form,
+// per = n_used); row a starts at X + (a / per) * ldx + (a % per) * ldx_slot.
 struct MoeSplit {
     const float *X;
-    int64_t ldx;
-    int T, K, NB, NQ, x_vec;
+    int64_t ldx, ldx_slot;
+    int T, R, per, K, NB, NQ, x_vec;
     uint8_t *xs, *xsum, *zero16;
     int32_t *xsc;
 };
@@ -222,7 +225,7 @@ struct MoePlan {
     int64_t ws_sorted_off, ws_chunk_off, ws_misc_off, ws_xs_off, ws_xsum_off, ws_xsc_off, ws_bytes;
 };
 
-MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N);
+MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N, bool per_slot);
 
 hipError_t launch_q4_repack(const uint8_t *blocks, const Q4Layout &L, uint8_t *packed, hipStream_t s);
 hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t grid, hipStream_t s,
@@ -230,6 +233,7 @@ hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t
 hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, int64_t n_used, int64_t E,
                             int rpc, int32_t *sorted, int32_t *chunk_info, int32_t *nchunks, int32_t *err,
                             const MoeSplit &sp, hipStream_t s);
-hipError_t launch_q4_moe(const Q4Params &p, int64_t max_chunks, hipStream_t s, const char **variant);
+// per_slot: the activation row of pair (t, s) is the pair itself, not token t
+hipError_t launch_q4_moe(const Q4Params &p, bool per_slot, int64_t max_chunks, hipStream_t s, const char **variant);
 
 }  // namespace qmm

@@ -98,3 +98,33 @@ def test_pack_and_quantize_rejections(q):
     assert q.lib.pack_b_int8_raw(FAKE, 3, 64, 16, 16, FAKE, 1 << 20, None) == INV
     assert q.lib.quantize_rows_int8(FAKE, 4, 64, 63, FAKE, 64, FAKE, None) == INV
     assert q.lib.quantize_rows_int8(FAKE, 0, 64, 64, FAKE, 64, FAKE, None) == q.QMM_OK
+
+
+def _moe(q, per_slot, T=4, K=64, ldx_slot=64, ldx=64, N=32, n_used=2, ids_stride=17, E=4, ws_bytes=1 << 24,
+         ldy_slot=32, ldy_token=64, stride=None):
+    stride = stride if stride is not None else q.lib.qmm_q4_1_packed_bytes(K, N) if K % 32 == 0 else 1 << 16
+    stride = (stride + 255) // 256 * 256
+    if per_slot:
+        return q.lib.q4_1_matmul_id_per_slot(FAKE, T, K, ldx_slot, ldx, FAKE, E, N, stride, FAKE, ids_stride,
+                                             n_used, FAKE, ldy_slot, ldy_token, FAKE, ws_bytes, None)
+    return q.lib.q4_1_matmul_id(FAKE, T, K, ldx, FAKE, E, N, stride, FAKE, ids_stride, n_used, FAKE, ldy_slot,
+                                ldy_token, FAKE, ws_bytes, None)
+
+
+def test_moe_rejections(q):
+    INV, UNS = q.QMM_ERR_INVALID, q.QMM_ERR_UNSUPPORTED
+    assert _moe(q, False, ldx=63) == INV
+    assert _moe(q, False, ids_stride=1) == INV
+    assert _moe(q, False, ldy_token=63) == INV
+    assert _moe(q, False, K=48, ldx=48) == UNS
+    assert _moe(q, False, ws_bytes=16) == q.QMM_ERR_WORKSPACE
+    assert _moe(q, False, T=0) == q.QMM_OK
+    # per-slot rows: ldx_slot >= K and the token stride covers n_used rows
+    assert _moe(q, True, ldx_slot=63, ldx=128) == INV
+    assert _moe(q, True, ldx_slot=64, ldx=127) == INV
+    assert _moe(q, True, K=48, ldx_slot=48, ldx=96) == UNS
+    assert _moe(q, True, ldx=128, ws_bytes=16) == q.QMM_ERR_WORKSPACE
+    assert _moe(q, True, ldx=128, T=0) == q.QMM_OK
+    # the per-slot workspace holds a split row per (token, slot)
+    assert (q.lib.qmm_q4_1_matmul_id_per_slot_workspace_bytes(512, 8, 128, 768, 2048) >
+            q.lib.qmm_q4_1_matmul_id_workspace_bytes(512, 8, 128, 768, 2048))

@@ -316,3 +316,108 @@ def test_moe_full_config_sampled(q, orc):
     in_ = g.integers(0, N, 4096)
     refs = orc.q4_1_matmul_id_at(d["X"], d["experts"], E, K, N, d["ids"], it, is_, in_)
     _check(got[it, is_, in_], refs)
+
+
+# ------------------------------------- MUL_MAT_ID, per-slot activations ---
+
+def _moe_slot_case(q, orc, E, K, N, T, n_used, seed=0, pad=0):
+    """Per-slot rows X[t, s] (ldx_slot = K + pad) against the fp64 oracle,
+    slot by slot."""
+    import torch
+    g = np.random.default_rng(seed)
+    experts = np.stack([wl.encode_q4_1(wl.normal_f32(g, (K, N), 0.02)) for _ in range(E)])
+    X = wl.normal_f32(g, (T, n_used, K))
+    ids = np.stack([g.permutation(max(E, 17))[:17] % E for _ in range(T)]).astype(np.int32)
+    buf, estride = q.q4_1_repack_experts(to_dev(experts), K, N)
+    Xd = to_dev(X)
+    if pad:
+        Xw = torch.zeros((T, n_used, K + pad), dtype=torch.float32, device=torch_dev())
+        Xw[:, :, :K] = Xd
+        Xd = Xw[:, :, :K]
+    got = to_np(q.q4_1_matmul_id_per_slot(Xd, buf, E, K, N, estride, to_dev(ids), n_used))
+    assert q.last_variant() == "q4_moe_m32"
+    ref = orc.q4_1_matmul_id(X, experts, E, K, N, ids, n_used)
+    absw = [np.abs(orc.q4_1_decode(experts[e], K, N)) for e in range(E)]
+    scale = np.stack([np.stack([np.abs(X[t, s].astype(np.float64)) @ absw[ids[t, s]] for s in range(n_used)])
+                      for t in range(T)])
+    _check(got, ref, scale)
+    for s in range(n_used):
+        _check(got[:, s], ref[:, s], scale[:, s])
+    return got, (experts, X, ids, buf, estride)
+
+
+@pytest.mark.parametrize("E,K,N,T,n_used,pad", [(6, 64, 24, 10, 3, 0), (20, 96, 40, 37, 4, 1), (3, 32, 16, 1, 1, 0),
+                                                 (9, 768, 300, 70, 8, 4), (128, 64, 48, 64, 8, 0)])
+def test_moe_per_slot_shapes(q, orc, E, K, N, T, n_used, pad):
+    """A row per (token, slot): ragged N, a partial last record (K = 96),
+    unaligned rows (ldx_slot = K + 1), padded rows (K + 4), one token."""
+    _moe_slot_case(q, orc, E, K, N, T, n_used, seed=E + K + N + T, pad=pad)
+
+
+def test_moe_per_slot_equal_rows_match_shared(q, orc):
+    """Every slot row equal to its token's row: the same bits as the shared
+    form (each output row depends on its own activation row only)."""
+    import torch
+    E, K, N, T, n_used = 11, 128, 72, 23, 5
+    g = np.random.default_rng(9)
+    experts = np.stack([wl.encode_q4_1(wl.normal_f32(g, (K, N), 0.02)) for _ in range(E)])
+    X = wl.normal_f32(g, (T, K))
+    ids = np.stack([g.permutation(17)[:17] % E for _ in range(T)]).astype(np.int32)
+    buf, estride = q.q4_1_repack_experts(to_dev(experts), K, N)
+    a = to_np(q.q4_1_matmul_id(to_dev(X), buf, E, K, N, estride, to_dev(ids), n_used))
+    X3 = to_dev(np.repeat(X[:, None, :], n_used, axis=1))
+    b = to_np(q.q4_1_matmul_id_per_slot(X3, buf, E, K, N, estride, to_dev(ids), n_used))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # a broadcast view (slot stride 0) is rejected: rows must not overlap
+    with pytest.raises(RuntimeError):
+        q.q4_1_matmul_id_per_slot(to_dev(X)[:, None, :].expand(T, n_used, K), buf, E, K, N, estride,
+                                  to_dev(ids), n_used)
+
+
+def test_moe_down_config_sampled(q, orc):
+    """The down experts: 128 experts of 768 x 2048 q4_1, 512 tokens x top-8
+    per-slot rows, ids from a stride-17 view: 16 whole tokens (all slots)
+    against the fp64 oracle plus 4096 sampled outputs."""
+    d = wl.moe_down_inputs()
+    E, K, N = wl.MOE_EXPERTS, wl.MOE_DOWN_K, wl.MOE_DOWN_N
+    buf, estride = q.q4_1_repack_experts(to_dev(d["experts"]), K, N)
+    Y = q.q4_1_matmul_id_per_slot(to_dev(d["X"]), buf, E, K, N, estride, to_dev(d["ids"]), wl.MOE_USED)
+    got = to_np(Y)
+    assert np.isfinite(got).all()
+    g = np.random.default_rng(12)
+    toks = np.sort(g.choice(wl.MOE_TOKENS, 16, replace=False))
+    ref = orc.q4_1_matmul_id(d["X"][toks], d["experts"], E, K, N, d["ids"][toks], wl.MOE_USED)
+    _check(got[toks], ref)
+    it = g.integers(0, wl.MOE_TOKENS, 4096)
+    is_ = g.integers(0, wl.MOE_USED, 4096)
+    in_ = g.integers(0, N, 4096)
+    refs = orc.q4_1_matmul_id_at(d["X"], d["experts"], E, K, N, d["ids"], it, is_, in_, n_used=wl.MOE_USED)
+    _check(got[it, is_, in_], refs)
+
+
+@pytest.mark.parametrize("per_slot", [False, True])
+def test_moe_every_chunk_size(q, orc, per_slot):
+    """Regression: expert e receives exactly e + 1 (token, slot) pairs, e < 40,
+    so the routing table holds full chunks and partial chunks of every size
+    from 1 to 32 rows (one or two 16-row tiles); every output row is checked
+    against the oracle, in both activation forms."""
+    E, K, N, n_used = 40, 256, 300, 4
+    T = E * (E + 1) // 2 // n_used
+    g = np.random.default_rng(5)
+    experts = np.stack([wl.encode_q4_1(wl.normal_f32(g, (K, N), 0.02)) for _ in range(E)])
+    lst = np.concatenate([np.full(e + 1, e) for e in range(E)])
+    g.shuffle(lst)
+    ids = np.zeros((T, 17), dtype=np.int32)
+    ids[:, :n_used] = lst.reshape(T, n_used)
+    ids[:, n_used:] = g.integers(0, E, (T, 17 - n_used))
+    buf, estride = q.q4_1_repack_experts(to_dev(experts), K, N)
+    if per_slot:
+        X = wl.normal_f32(g, (T, n_used, K))
+        got = to_np(q.q4_1_matmul_id_per_slot(to_dev(X), buf, E, K, N, estride, to_dev(ids), n_used))
+    else:
+        X = wl.normal_f32(g, (T, K))
+        got = to_np(q.q4_1_matmul_id(to_dev(X), buf, E, K, N, estride, to_dev(ids), n_used))
+    ref = orc.q4_1_matmul_id(X, experts, E, K, N, ids, n_used)
+    for e in range(E):
+        sel = ids[:, :n_used] == e
+        _check(got[sel], ref[sel])

@@ -14,7 +14,9 @@ Shapes follow the pages' workloads:
     Q4NX on the AMD NPU");
   * a 2048-token int8 prefill over the same 8B-class shapes;
   * a 128-expert MUL_MAT_ID with top-8 ids read from a stride-17 view
-    ("Zaya 8B Q4NX on the AMD NPU", "The bugs that were the work");
+    ("Zaya 8B Q4NX on the AMD NPU", "The bugs that were the work"), and its
+    down experts (768 x 2048), which read a row per (token, slot) ("What's
+    next": the per-expert activation form);
   * the Qwen3-0.6B output projection (lm_head: hidden 1024 onto a 151936-word
     vocabulary), one large streaming matmul per decoded token ("The ONNX
     pack", "What works today": the per-token step it is part of).
@@ -44,6 +46,10 @@ Q4_ROWS = (1, 16)
 
 PREFILL_M = 2048
 PREFILL_SHAPES = ((4096, 4096), (4096, 14336), (14336, 4096))
+
+# the down experts of the same MoE: K x N = 768 x 2048, a row per (token, slot)
+MOE_DOWN_K = 768
+MOE_DOWN_N = 2048
 
 MOE_EXPERTS = 128
 MOE_K = 2048
@@ -234,4 +240,17 @@ def moe_inputs(n_expert: int = MOE_EXPERTS, K: int = MOE_K, N: int = MOE_N, T: i
         experts[e] = encode_q4_1(normal_f32(g, (K, N), 0.02))
     X = normal_f32(g, (T, K))
     ids = moe_ids(T, n_expert, MOE_IDS_STRIDE, seed_index)
+    return dict(experts=experts, X=X, ids=ids)
+
+
+def moe_down_inputs(n_expert: int = MOE_EXPERTS, K: int = MOE_DOWN_K, N: int = MOE_DOWN_N, T: int = MOE_TOKENS,
+                    n_used: int = MOE_USED, seed_index: int = 0):
+    """Down experts [n_expert, N, K/32, 20], per-slot activations
+    [T, n_used, K] (each (token, slot) row its own N(0,1) draw), ids [T, 17]."""
+    g = rng(7, seed_index)
+    experts = np.empty((n_expert, N, K // Q4_BLOCK, Q4_BLOCK_BYTES), dtype=np.uint8)
+    for e in range(n_expert):
+        experts[e] = encode_q4_1(normal_f32(g, (K, N), 0.02))
+    X = normal_f32(g, (T, n_used, K))
+    ids = moe_ids(T, n_expert, MOE_IDS_STRIDE, 100 + seed_index)
     return dict(experts=experts, X=X, ids=ids)
