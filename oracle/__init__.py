@@ -48,6 +48,7 @@ def _load():
     sig = {
         "oracle_int8_bound_ok": (_INT, [_I64]),
         "oracle_int8_gemm_i64": (None, [_P, _INT, _I64, _I64, _I64, _I32, _P, _INT, _I64, _I64, _I32, _P, _I64]),
+        "oracle_int8_gemm_axis_i64": (None, [_P, _INT, _I64, _I64, _I64, _P, _P, _INT, _I64, _I64, _P, _P, _I64]),
         "oracle_int8_gemm_at": (None, [_P, _INT, _I64, _I64, _I32, _P, _INT, _I64, _I32, _P, _P, _I64, _P]),
         "oracle_epilogue_f64": (None, [_P, _I64, _I64, _I64, _P, _P, _F32, _P, _P]),
         "oracle_requant": (_INT, [_P, _I64, _I64, _I64, _P, _P, _F32, _P, _I32, _INT, _P]),
@@ -102,6 +103,23 @@ def int8_gemm_i64(A: np.ndarray, zA: int, B: np.ndarray, zB: int) -> np.ndarray:
     assert K == K2
     Y = np.empty((M, N), dtype=np.int64)
     _load().oracle_int8_gemm_i64(_ptr(A), _i8kind(A), M, K, K, zA, _ptr(B), _i8kind(B), N, N, zB, _ptr(Y), N)
+    return Y
+
+
+def int8_gemm_axis_i64(A: np.ndarray, zA, B: np.ndarray, zB) -> np.ndarray:
+    """Per-axis zero points: Y[m,n] = sum_k (A[m,k]-zA[m])(B[k,n]-zB[n]) as
+    int64 (naive); zA [M] and zB [N] int32."""
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    M, K = A.shape
+    K2, N = B.shape
+    assert K == K2
+    zA = np.ascontiguousarray(zA, dtype=np.int32)
+    zB = np.ascontiguousarray(zB, dtype=np.int32)
+    assert zA.shape == (M,) and zB.shape == (N,)
+    Y = np.empty((M, N), dtype=np.int64)
+    _load().oracle_int8_gemm_axis_i64(_ptr(A), _i8kind(A), M, K, K, _ptr(zA), _ptr(B), _i8kind(B), N, N, _ptr(zB),
+                                      _ptr(Y), N)
     return Y
 
 

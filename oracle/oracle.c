@@ -70,6 +70,28 @@ void oracle_int8_gemm_i64(const void *A, int a_u8, int64_t M, int64_t K, int64_t
     }
 }
 
+/* [P1] "What works today": zero points per axis, one per activation row
+ * (zA[m]) and one per weight column (zB[n]), the same axes as the per-axis
+ * scales.  The plain definition, written out: Y[m,n] = sum_k (A[m,k] - zA[m])
+ * (B[k,n] - zB[n]) in int64. */
+void oracle_int8_gemm_axis_i64(const void *A, int a_u8, int64_t M, int64_t K, int64_t lda, const int32_t *zA,
+                               const void *B, int b_u8, int64_t N, int64_t ldb, const int32_t *zB,
+                               int64_t *Y, int64_t ldy) {
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t a = load_i8(A, a_u8, m * lda + k) - zA[m];
+                int64_t b = load_i8(B, b_u8, k * ldb + n) - zB[n];
+                acc += a * b;
+            }
+            Y[m * ldy + n] = acc;
+        }
+    }
+}
+
 void oracle_int8_gemm_at(const void *A, int a_u8, int64_t K, int64_t lda, int32_t zA,
                          const void *B, int b_u8, int64_t ldb, int32_t zB,
                          const int64_t *im, const int64_t *in, int64_t count, int64_t *out) {

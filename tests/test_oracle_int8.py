@@ -185,3 +185,52 @@ def test_requant_scales_fold_in_fp32_order(orc):
             v = np.float32(np.float32(Y[m, n]) * mult)
             exp = int(np.clip(np.rint(v) - 7, -128, 127))
             assert out[m, n] == exp
+
+
+# ---------------------------------------------- per-axis zero points ---
+# "The ONNX pack", "What works today": a zero point per activation row and
+# one per weight column, on the same axes as the per-axis scales.
+
+@pytest.mark.parametrize("a_u8,b_u8", [(False, False), (True, False), (False, True), (True, True)])
+def test_axis_zero_points_against_numpy(orc, a_u8, b_u8):
+    """numpy int64 product of the explicitly shifted matrices."""
+    g = np.random.default_rng(61 + 2 * a_u8 + b_u8)
+    M, K, N = 9, 70, 13
+    A = wl.uniform_u8(g, (M, K)) if a_u8 else wl.uniform_i8(g, (M, K))
+    B = wl.uniform_u8(g, (K, N)) if b_u8 else wl.uniform_i8(g, (K, N))
+    lo_a, lo_b = (0 if a_u8 else -128), (0 if b_u8 else -128)
+    zA = g.integers(lo_a, lo_a + 256, M).astype(np.int32)
+    zB = g.integers(lo_b, lo_b + 256, N).astype(np.int32)
+    zA[0], zB[0] = lo_a, lo_b + 255            # range ends
+    ref = (A.astype(np.int64) - zA[:, None]) @ (B.astype(np.int64) - zB[None, :])
+    assert np.array_equal(orc.int8_gemm_axis_i64(A, zA, B, zB), ref)
+
+
+def test_axis_zero_points_reduce_to_scalar(orc):
+    """Constant vectors give the per-tensor product (pinned above)."""
+    g = np.random.default_rng(62)
+    A = wl.uniform_u8(g, (5, 33))
+    B = wl.uniform_i8(g, (33, 7))
+    Y = orc.int8_gemm_axis_i64(A, np.full(5, 200, np.int32), B, np.full(7, -25, np.int32))
+    assert np.array_equal(Y, orc.int8_gemm_i64(A, 200, B, -25))
+
+
+def test_axis_zero_points_expanded_identity_brute_force(orc):
+    """The page's expansion sum a*w - zx*sum w - zw*sum a + K*zx*zw, evaluated
+    with Python integers over every entry of tiny shapes with extreme
+    values; each row and column its own zero point."""
+    vals = [-128, -1, 0, 1, 127]
+    for M, K, N in [(1, 1, 1), (2, 3, 2), (3, 2, 3)]:
+        g = np.random.default_rng(M * 100 + K * 10 + N)
+        A = g.choice(vals, (M, K)).astype(np.int8)
+        B = g.choice(vals, (K, N)).astype(np.int8)
+        zA = g.choice(vals, M).astype(np.int32)
+        zB = g.choice(vals, N).astype(np.int32)
+        Y = orc.int8_gemm_axis_i64(A, zA, B, zB)
+        for m in range(M):
+            for n in range(N):
+                a = [int(v) for v in A[m]]
+                w = [int(B[k, n]) for k in range(K)]
+                zx, zw = int(zA[m]), int(zB[n])
+                want = sum(x * y for x, y in zip(a, w)) - zx * sum(w) - zw * sum(a) + K * zx * zw
+                assert Y[m, n] == want
