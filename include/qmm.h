@@ -172,6 +172,25 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
                      const qmm_epilogue *ep, void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/*
+ * int8_gemm_per_axis: int8_gemm with a zero point per activation row and one
+ * per weight column ([P1] "What works today": asymmetric zero points per
+ * axis, on the same axes as the per-axis scales, folded into the epilogue):
+ *   Y[m,n] = sum_k (A[m,k] - zA_row[m]) * (B[k,n] - zB_col[n])
+ *          = S - zA'[m]*colSum[n] - zB'[n]*(rowSum[m] - K*zA'[m])  (int32)
+ * then the same epilogue: per-axis scales come through ep->row_scale (s_x[m])
+ * and ep->col_scale (s_w[n]), and the QDQ group "int8 in, int8 out" is the
+ * I8/U8 output with ep->scale = 1/s_y and ep->zp_out = zp_y.
+ *   zA_row   device int32 [M], each in at's range, or NULL (all 0)
+ *   zB_col   device int32 [N], each in bt's range, or NULL (all 0)
+ * The ranges are a precondition (device data, not checked on the host).
+ * Every other argument, the bound on K and the error codes are int8_gemm's.
+ */
+qmm_status int8_gemm_per_axis(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t lda,
+                              const int32_t *zA_row, const void *packedB, qmm_i8type bt, int64_t N,
+                              const int32_t *zB_col, const qmm_epilogue *ep, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* Workspace bytes int8_gemm_dynamic needs (0 when the quantisation is fused,
  * see int8_gemm_dynamic). */
 size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N);

@@ -63,6 +63,7 @@ _SIGS = {
     "qmm_int8_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "int8_gemm": (_INT, [_P, _INT, _I64, _I64, _I64, _I32, _P, _INT, _I64, _I32,
                          ctypes.POINTER(qmm_epilogue), _P, _SZ, _P]),
+    "int8_gemm_per_axis": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _INT, _I64, _P, _P, _P, _SZ, _P]),
     "qmm_int8_gemm_dynamic_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "int8_gemm_dynamic": (_INT, [_P, _I64, _I64, _I64, _P, _I64, ctypes.POINTER(qmm_epilogue), _P, _I64, _P,
                                  _P, _SZ, _P]),
@@ -211,6 +212,8 @@ def int8_gemm(A, zA: int, packedB: PackedInt8, zB: int = 0, *, out_i32=None, out
               q8_unsigned: bool = False, row_scale=None, col_scale=None, scale: float = 1.0, bias_f32=None,
               bias_i32=None, zp_out: int = 0, ws=None, stream=None):
     """int8 x int8 -> int32 product with the zero-point correction epilogue.
+    zA / zB: scalars, or int32 device vectors (one per row of A / column of the
+    weight) for per-axis zero points (int8_gemm_per_axis).
 
     Writes whichever of out_i32 (int32 [M,N]), out_f32 (fp32 [M,N]) and out_q8
     (int8 or uint8 [M,N]) are given; returns them as a tuple in that order."""
@@ -242,6 +245,19 @@ def int8_gemm(A, zA: int, packedB: PackedInt8, zB: int = 0, *, out_i32=None, out
     if ws is None and need > 0:
         ws = workspace(need, A.device)
     wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    if torch.is_tensor(zA) or torch.is_tensor(zB):
+        # per-axis zero points: int32 [M] per activation row, int32 [N] per
+        # weight column (a scalar given with a vector becomes a vector)
+        def vec(z, n):
+            if torch.is_tensor(z):
+                assert z.dtype == torch.int32 and z.shape == (n,) and z.is_contiguous()
+                return z
+            return None if int(z) == 0 else torch.full((n,), int(z), dtype=torch.int32, device=A.device)
+        za, zb = vec(zA, M), vec(zB, N)
+        _check("int8_gemm_per_axis",
+               lib.int8_gemm_per_axis(_ptr(A), at, M, K, A.stride(0), _ptr(za), _ptr(packedB.data), packedB.bt, N,
+                                      _ptr(zb), ctypes.byref(ep), _ptr(ws), wsz, _stream(stream)))
+        return out_i32, out_f32, out_q8
     _check("int8_gemm", lib.int8_gemm(_ptr(A), at, M, K, A.stride(0), int(zA), _ptr(packedB.data), packedB.bt,
                                       N, int(zB), ctypes.byref(ep), _ptr(ws), wsz, _stream(stream)))
     return out_i32, out_f32, out_q8

@@ -224,10 +224,13 @@ static void trace_gemm(const char *fn, const char *variant, int64_t M, int64_t K
                 (long long)M, (long long)K, (long long)N, (long long)plan.grid, plan.waves, plan.tpw);
 }
 
-qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t lda, int32_t zA,
-                     const void *packedB, qmm_i8type bt, int64_t N, int32_t zB,
-                     const qmm_epilogue *ep, void *workspace, size_t workspace_bytes,
-                     void *stream) {
+// int8_gemm and int8_gemm_per_axis: scalar zero points zA, zB, or one per
+// row of A (za_row) and one per column of B (zb_col), device vectors in the
+// caller's domain (a precondition, like the MoE ids: in the type's range).
+static qmm_status gemm_call(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t lda, int32_t zA,
+                            const int32_t *za_row, const void *packedB, qmm_i8type bt, int64_t N, int32_t zB,
+                            const int32_t *zb_col, const qmm_epilogue *ep, void *workspace, size_t workspace_bytes,
+                            void *stream, const char *fn) {
     if (M < 0 || N < 0 || K <= 0 || !ep || (at != QMM_S8 && at != QMM_U8) ||
         (bt != QMM_S8 && bt != QMM_U8))
         return QMM_ERR_INVALID;
@@ -239,6 +242,7 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
     if (!k_in_bound(K) || M > INT32_MAX || N > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return QMM_OK;
     if (!A || !packedB || !aligned(packedB, 256) || check_epilogue_ptrs(ep) != QMM_OK) return QMM_ERR_INVALID;
+    if ((za_row && !aligned(za_row, 4)) || (zb_col && !aligned(zb_col, 4))) return QMM_ERR_INVALID;
     const Int8Plan plan = plan_int8_gemm(M, K, N);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
         return QMM_ERR_WORKSPACE;
@@ -251,11 +255,32 @@ qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t
     p.a_vec = aligned(A, 16) && (lda % 16 == 0);
     p.zAs = zA - (at == QMM_U8 ? 128 : 0);
     p.zBs = zB - (bt == QMM_U8 ? 128 : 0);
+    p.za_row = za_row;
+    p.zb_col = zb_col;
+    p.za_off = at == QMM_U8 ? 128 : 0;
+    p.zb_off = bt == QMM_U8 ? 128 : 0;
     const char *variant = "";
     st = hip_status(launch_int8_gemm(plan, p, (hipStream_t)stream, &variant));
     g_last_variant = variant;
-    trace_gemm("int8_gemm", variant, M, K, N, plan);
+    trace_gemm(fn, variant, M, K, N, plan);
     return st;
+}
+
+qmm_status int8_gemm(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t lda, int32_t zA,
+                     const void *packedB, qmm_i8type bt, int64_t N, int32_t zB,
+                     const qmm_epilogue *ep, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    return gemm_call(A, at, M, K, lda, zA, nullptr, packedB, bt, N, zB, nullptr, ep, workspace, workspace_bytes,
+                     stream, "int8_gemm");
+}
+
+qmm_status int8_gemm_per_axis(const void *A, qmm_i8type at, int64_t M, int64_t K, int64_t lda,
+                              const int32_t *zA_row, const void *packedB, qmm_i8type bt, int64_t N,
+                              const int32_t *zB_col, const qmm_epilogue *ep, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    const int32_t za = at == QMM_U8 ? 128 : 0, zb = bt == QMM_U8 ? 128 : 0;  // in range; unused with vectors
+    return gemm_call(A, at, M, K, lda, za, zA_row, packedB, bt, N, zb, zB_col, ep, workspace, workspace_bytes,
+                     stream, "int8_gemm_per_axis");
 }
 
 // The fused form quantises all M x K activations in every workgroup: it

@@ -188,6 +188,8 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float *__restrict__
 // ------------------------------------------------------------- epilogue ---
 // Zero-point correction in wrapping int32, then the requested outputs.
 //   Y    = S - zA'*colsum[n] - zB'*(rowsum[m] - K*zA')
+// (zA' per row and zB' per column with per-axis zero points: the same
+// expansion of sum_k (a - zA')(b - zB'), each product with its own pair)
 //   mult = fl32(fl32(rs[m]*cs[n]) * scale)
 //   F32  = fma(fl32(Y), mult, bias_f32[n])
 //   I8/U8: v = fl32(fl32(Y + bias_i32[n]) * mult); clamp(rne(v) + zp_out)
@@ -197,13 +199,21 @@ struct ColOps {
     float cs;
     float bias_f;
     int32_t bias_i;
+    int32_t zb;  // zB' of the column (shifted domain)
 };
+
+// zA' of row m (shifted domain).  Called in the epilogues, after the main
+// loads: the load sits in a branch only on the per-axis path.
+__device__ __forceinline__ int32_t row_za(const Int8GemmParams &p, int m) {
+    return p.za_row ? p.za_row[m] - p.za_off : p.zAs;
+}
 
 
 __device__ __forceinline__ void epilogue_store_c(const Int8GemmParams &p, int m, int n, uint32_t S,
-                                                 int32_t rowsum, bool has_zb, float rs, const ColOps &c) {
-    uint32_t Y = S - (uint32_t)p.zAs * (uint32_t)c.colsum;
-    if (has_zb) Y -= (uint32_t)p.zBs * ((uint32_t)rowsum - (uint32_t)p.K * (uint32_t)p.zAs);
+                                                 int32_t rowsum, bool has_zb, float rs, int32_t za,
+                                                 const ColOps &c) {
+    uint32_t Y = S - (uint32_t)za * (uint32_t)c.colsum;
+    if (has_zb) Y -= (uint32_t)c.zb * ((uint32_t)rowsum - (uint32_t)p.K * (uint32_t)za);
     const int32_t y = (int32_t)Y;
     if (p.outputs & QMM_OUT_I32) p.y_i32[(int64_t)m * p.ld_i32 + n] = y;
     if (p.outputs & (QMM_OUT_F32 | QMM_OUT_I8 | QMM_OUT_U8)) {
@@ -284,11 +294,13 @@ __device__ __forceinline__ ColOps load_colops_c(const Int8GemmParams &p, int n) 
     const int c = min(n, p.N - 1);
     const float bf = (p.bias_f32 ? p.bias_f32 : p.col_scale)[c];
     const int32_t bi = (p.bias_i32 ? p.bias_i32 : p.colsum)[c];
+    const int32_t zb = (p.zb_col ? p.zb_col : p.colsum)[c];
     ColOps o;
     o.colsum = p.colsum[c];
     o.cs = p.col_scale[c];
     o.bias_f = p.bias_f32 ? bf : 0.0f;
     o.bias_i = p.bias_i32 ? bi : 0;
+    o.zb = p.zb_col ? zb - p.zb_off : p.zBs;
     return o;
 }
 
@@ -394,7 +406,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
             int32_t v = 0;
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) v += s_red[w][m][e & 15];
-            epilogue_store_c(p, m, n, (uint32_t)v, HAS_ZB ? s_rowsum[m] : 0, HAS_ZB, rs[i], col);
+            epilogue_store_c(p, m, n, (uint32_t)v, HAS_ZB ? s_rowsum[m] : 0, HAS_ZB, rs[i], row_za(p, m), col);
         }
     }
 }
@@ -475,7 +487,8 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide(Int8GemmPa
         for (int i = 0; i < 4; ++i) {
             const int m = r * 16 + 4 * (lane >> 4) + i;
             if (strip_ok && m < p.M && n < p.N)
-                epilogue_store_c(p, m, n, (uint32_t)acc[r][i], HAS_ZB ? accr[r][i] : 0, HAS_ZB, rs[r][i], col);
+                epilogue_store_c(p, m, n, (uint32_t)acc[r][i], HAS_ZB ? accr[r][i] : 0, HAS_ZB, rs[r][i],
+                                 row_za(p, m), col);
         }
 }
 
@@ -645,7 +658,7 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p) {
             int32_t v = 0;
 #pragma unroll
             for (int ww = 0; ww < WAVES; ++ww) v += s_red[ww][mo][e & 15];
-            epilogue_store_c(p, mo, n, (uint32_t)v, 0, false, s_scale[mo], col);
+            epilogue_store_c(p, mo, n, (uint32_t)v, 0, false, s_scale[mo], 0, col);
         }
     }
 }
@@ -794,6 +807,7 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         else return sD5;
     };
     __shared__ __attribute__((aligned(16))) float s_rs[PF_BM];
+    __shared__ int32_t s_za[PF_BM];
     __shared__ ColOps s_col[PF_BN];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1011,13 +1025,14 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         const int m = min(m0 + r, p.M - 1);
         const float v = (p.row_scale ? p.row_scale : p.col_scale)[m];
         s_rs[r] = p.row_scale ? v : 1.0f;
+        s_za[r] = row_za(p, m);
     }
     if (tid < PF_BN) s_col[tid] = load_colops_c(p, strip0 * kTileN + tid);
     __syncthreads();
     const bool whole = m0 + PF_BM <= p.M && (strip0 + BF) * kTileN <= p.N;
     // accumulator element e of tile (i, j): row i*32 + 8 (e / 4) + 4 (L / 32) + e % 4,
     // column j*32 + L % 32 of the wavefront's 128 x 64 block
-    if (!HAS_ZB && p.outputs == QMM_OUT_F32 && p.zAs == 0 && whole) {
+    if (!HAS_ZB && p.outputs == QMM_OUT_F32 && p.zAs == 0 && !p.za_row && whole) {
         float cm[2], cb[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -1057,14 +1072,14 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
                 const int m = m0 + rl;
                 if (m < p.M && n < p.N)
                     epilogue_store_c(p, m, n, (uint32_t)acc[i][j][e], HAS_ZB ? accr[i][e] : 0, HAS_ZB, s_rs[rl],
-                                     s_col[cl]);
+                                     s_za[rl], s_col[cl]);
             }
         }
 }
 
 template <int MT, int WAVES, int TPW, bool AVEC>
 hipError_t launch_decode(const Int8GemmParams &p, hipStream_t s) {
-    if (p.zBs != 0)
+    if (p.zBs != 0 || p.zb_col)
         hipLaunchKernelGGL((k_int8_decode<MT, WAVES, TPW, true, AVEC>), dim3((unsigned)p.NS), dim3(WAVES * 64), 0,
                            s, p);
     else
@@ -1077,7 +1092,7 @@ template <int MT, int D, bool AVEC>
 hipError_t launch_wide_d(const Int8GemmParams &p, hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(p.NS, kWideWaves));
     const size_t lds = (size_t)p.KT * MT * 64 * sizeof(v4i);
-    if (p.zBs != 0)
+    if (p.zBs != 0 || p.zb_col)
         hipLaunchKernelGGL((k_int8_decode_wide<MT, D, true, AVEC>), grid, dim3(kWideWaves * 64), lds, s, p);
     else
         hipLaunchKernelGGL((k_int8_decode_wide<MT, D, false, AVEC>), grid, dim3(kWideWaves * 64), lds, s, p);
@@ -1161,7 +1176,7 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
     dim3 grid((unsigned)(ceil_div(p.NS, PF_BN / kTileN) * ceil_div(p.M, PF_BM)));
     const bool fast = p.a_vec && (p.K % kTileK) == 0;
     const dim3 b(256);
-    if (p.zBs != 0) {
+    if (p.zBs != 0 || p.zb_col) {
         if (fast && p.a_u8)
             hipLaunchKernelGGL((k_int8_prefill<true, true, true>), grid, b, 0, s, p);
         else if (fast)
@@ -1206,7 +1221,8 @@ hipError_t launch_dyn_tpw(const Int8GemmParams &p, bool avec, hipStream_t s) {
 hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                                     const char **variant) {
     const int rows = p.rpg > 0 ? p.rpg : p.M;  // rows one workgroup quantises
-    if (plan.variant != 0 || rows > 16 || p.KT > 64 || p.zBs != 0) return hipErrorInvalidValue;
+    if (plan.variant != 0 || rows > 16 || p.KT > 64 || p.zBs != 0 || p.zb_col || p.za_row)
+        return hipErrorInvalidValue;
     *variant = p.rpg > 0 ? "int8_dynamic_groups" : "int8_dynamic_m16";
     const bool v = p.x_vec && (p.K % 16) == 0;
     // E: values per lane, the rows rounded up to a power of two

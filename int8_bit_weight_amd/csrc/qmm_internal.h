@@ -75,6 +75,11 @@ struct Int8GemmParams {
     int a_u8;             // 1: A is uint8 (flip the top bit to shift by 128)
     int a_vec;            // 1: A and lda allow aligned 16-byte loads
     int32_t zAs, zBs;     // zero points in the shifted (int8) domain
+    // per-axis zero points (NULL: the scalars above): one per row of A, one per
+    // column of B, in the caller's domain; za_off / zb_off (128 for uint8, else
+    // 0) take them to the shifted domain
+    const int32_t *za_row, *zb_col;
+    int32_t za_off, zb_off;
     const int8_t *codes;  // packed tiles
     const int32_t *colsum;
     int KT, NS;           // k tiles, n strips

@@ -128,3 +128,14 @@ def test_moe_rejections(q):
     # the per-slot workspace holds a split row per (token, slot)
     assert (q.lib.qmm_q4_1_matmul_id_per_slot_workspace_bytes(512, 8, 128, 768, 2048) >
             q.lib.qmm_q4_1_matmul_id_workspace_bytes(512, 8, 128, 768, 2048))
+
+
+def test_int8_gemm_per_axis_rejections(q):
+    INV = q.QMM_ERR_INVALID
+    ep = _ep(q)
+    f = q.lib.int8_gemm_per_axis
+    assert f(FAKE, 0, 4, 64, 64, ctypes.c_void_p(4098), FAKE, 0, 64, None, ctypes.byref(ep), None, 0, None) == INV
+    assert f(FAKE, 0, 4, 64, 64, None, FAKE, 0, 64, ctypes.c_void_p(4098), ctypes.byref(ep), None, 0, None) == INV
+    assert f(FAKE, 0, 4, 64, 63, None, FAKE, 0, 64, None, ctypes.byref(ep), None, 0, None) == INV
+    assert f(FAKE, 2, 4, 64, 64, None, FAKE, 0, 64, None, ctypes.byref(ep), None, 0, None) == INV
+    assert f(FAKE, 0, 0, 64, 64, FAKE, FAKE, 0, 64, FAKE, ctypes.byref(ep), None, 0, None) == q.QMM_OK

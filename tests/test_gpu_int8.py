@@ -231,6 +231,71 @@ def test_wide_decode_dynamic(q, orc, M):
     assert max_rel_err(to_np(y), orc.epilogue_f64(Y64, sa, sb)) <= F32_TOL
 
 
+# ------------------------------------------------ per-axis zero points ---
+
+def _axis_case(q, orc, M, K, N, a_u8, b_u8, seed, expect_variant, zx=None, zw=None, zy=None):
+    """The fused QDQ group with per-axis parameters: int8/uint8 activations
+    and weights as given, a zero point and a scale per activation row and per
+    weight column, int32 + fp32 + requantised int8 outputs (ep.scale = 1/s_y,
+    zp_out = zp_y), against the oracle (integers bit-exact)."""
+    import torch
+    dev = torch_dev()
+    g = np.random.default_rng(seed)
+    A = wl.uniform_u8(g, (M, K)) if a_u8 else wl.uniform_i8(g, (M, K))
+    B = wl.uniform_u8(g, (K, N)) if b_u8 else wl.uniform_i8(g, (K, N))
+    lo_a, lo_b = (0 if a_u8 else -128), (0 if b_u8 else -128)
+    zA = (g.integers(lo_a, lo_a + 256, M) if zx is None else np.full(M, zx)).astype(np.int32)
+    zB = (g.integers(lo_b, lo_b + 256, N) if zw is None else np.full(N, zw)).astype(np.int32)
+    zA[0] = lo_a + 255
+    zB[-1] = lo_b
+    sx = g.uniform(0.5, 2.0, M).astype(np.float32) / np.float32(127.0)
+    sw = g.uniform(0.5, 2.0, N).astype(np.float32) / np.float32(127.0)
+    Y64 = orc.int8_gemm_axis_i64(A, zA, B, zB)
+    assert np.abs(Y64).max() < 2 ** 31
+    sy = np.float32(np.abs(Y64 * sx[:, None].astype(np.float64) * sw[None, :]).max() / 100.0)
+    scale = np.float32(1.0) / sy
+    zp = int(g.integers(-20, 20)) if zy is None else zy
+    p = q.pack_b_int8_raw(to_dev(B))
+    y32 = torch.full((M, N), -7, dtype=torch.int32, device=dev)
+    yf = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    yq = torch.zeros((M, N), dtype=torch.int8, device=dev)
+    q.int8_gemm(to_dev(A), to_dev(zA), p, to_dev(zB), out_i32=y32, out_f32=yf, out_q8=yq, row_scale=to_dev(sx),
+                col_scale=to_dev(sw), scale=float(scale), zp_out=zp)
+    assert q.last_variant() == expect_variant
+    assert np.array_equal(to_np(y32), Y64.astype(np.int32))
+    assert max_rel_err(to_np(yf), orc.epilogue_f64(Y64, sx, sw, scale)) <= F32_TOL
+    assert np.array_equal(to_np(yq), orc.requant(Y64, sx, sw, scale, None, zp, False))
+    return A, zA, B, zB, p
+
+
+@pytest.mark.parametrize("M,K,N,a_u8,b_u8,variant", [
+    (8, 16, 6, False, False, "int8_decode_m16"),          # the pages' proof-graph shape
+    (1, 1024, 1024, True, False, "int8_decode_m16"), (16, 1056, 272, False, True, "int8_decode_m16"),
+    (32, 3072, 1024, True, True, "int8_decode_m32"), (3, 100, 16400, True, False, "int8_decode_wide_m16"),
+    (29, 1024, 16500, False, True, "int8_decode_wide_m32"), (256, 1024, 1024, False, False, "int8_prefill_256x128"),
+    (300, 200, 130, True, True, "int8_prefill_256x128")])
+def test_per_axis_zero_points(q, orc, M, K, N, a_u8, b_u8, variant):
+    _axis_case(q, orc, M, K, N, a_u8, b_u8, seed=M * 3 + K + N, expect_variant=variant)
+
+
+def test_per_axis_pages_values_and_constant_vectors(q, orc):
+    """The pages' per-tensor values zp_x = -40, zp_w = -25, zp_y = -7 on the
+    8 x 16 x 6 proof shape, given as constant vectors: the same bits as the
+    scalar-zero-point call, and the oracle."""
+    import torch
+    A, zA, B, zB, p = _axis_case(q, orc, 8, 16, 6, False, False, seed=7, expect_variant="int8_decode_m16",
+                                 zx=-40, zw=-25, zy=-7)
+    zA[:] = -40
+    zB[:] = -25
+    dev = torch_dev()
+    a = torch.empty((8, 6), dtype=torch.int32, device=dev)
+    b = torch.empty((8, 6), dtype=torch.int32, device=dev)
+    q.int8_gemm(to_dev(A), to_dev(zA), p, to_dev(zB), out_i32=a)
+    q.int8_gemm(to_dev(A), -40, p, -25, out_i32=b)
+    assert np.array_equal(to_np(a), to_np(b))
+    assert np.array_equal(to_np(a), orc.int8_gemm_i64(A, -40, B, -25).astype(np.int32))
+
+
 def test_int8_empty_is_noop(q):
     import torch
     dev = torch_dev()
