@@ -1,0 +1,454 @@
+// k_int8_prefill.hip -- the int8 x int8 -> int32 prefill GEMM for gfx950
+// (M > 32): LDS-staged tiles, v_mfma_i32_32x32x32_i8, the zero-point
+// correction epilogue of "int8 inference" (onemodel docs), "Product kernel
+// (Int8Gemm)", and "The ONNX pack", "What works today, and what does not".
+#include <type_traits>
+#include <utility>
+
+#include "qmm_internal.h"
+
+namespace qmm {
+
+namespace {
+
+#include "int8_common.h"
+
+// -------------------------------------------------------- prefill GEMM ---
+// 256 x 128 output tile per workgroup, k step 64, 4 wavefronts in a 2 x 2
+// grid each owning 128 x 64: 4 x 2 tiles of v_mfma_i32_32x32x32_i8 (two per
+// tile and k step, 128 int32 accumulators per lane).  The 32 x 32 form
+// issues one MFMA per 32 cycles even at one wavefront per SIMD (the 16 x 16
+// x 64 form reached 2.5 POP/s there, 3.3 at four waves).  With random int8
+// operands on every SIMD the chip clock drops to about 1.5 GHz (2.1 GHz with
+// constant operands), so about 3.0 POP/s, not the nominal 5.0, is the
+// ceiling for this data.  A 32 x 32 x 32 operand takes, for lane L, row (or
+// column) L % 32 and the 16-k chunk 2 h + L / 32 of k half h.
+//
+// Activations: 16-row fragments of 64 k in LDS (1 KiB, one ds_read_b128 per
+// lane per operand).  On the aligned path every stage is copied global-to-LDS
+// (global_load_lds_dwordx4: no register round trip and no LDS store
+// instructions, which measured about 140 cycles a step when interleaved with
+// the MFMAs) into a ring of PF_DEPTH LDS stages.  Weights: the packed tiles
+// are already 16-byte lane chunks of 16 k for one column, so every wavefront
+// loads its operands straight into a ring of PF_DEPTH register stages.
+// Loads run PF_DEPTH k steps ahead (compile-time slots: the k loop is
+// unrolled by PF_DEPTH).
+//
+// In an A fragment the 16-byte piece of (row r, k-chunk g) sits at slot
+// 4 r + (g ^ t(r)), t(r) = ((r >> 1) ^ (r >> 3)) & 3: a row's four chunks
+// fill four consecutive slots, so the lanes that fill consecutive slots (a
+// global-to-LDS copy puts lane L's piece in slot L) read 64 contiguous bytes
+// of one row (a layout with 16 rows per 16 lanes made the copies 25 % slower
+// overall), and the MFMA reads (lane L: row L % 16, one chunk) touch distinct
+// 16-byte bank groups in every 8 and every 16 consecutive lanes.  Row and
+// column epilogue operands are staged in LDS once.
+constexpr int PF_BM = 256, PF_BN = 128, PF_DEPTH = 4;
+
+__device__ __forceinline__ int pf_chunk_perm(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int pf_slot(int r, int g) { return 4 * r + (g ^ pf_chunk_perm(r)); }
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+// f(ic<0>{}), f(ic<1>{}), ..., f(ic<N-1>{})
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(ic<I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Instruction order of one k step of the register-staged path.  With one
+// wavefront per SIMD nothing else hides a wait, and left to itself the
+// scheduler moves the LDS operand reads for the next step down next to their
+// first use (each pair of MFMAs then waits for an LDS round trip).  The order
+// pinned here puts one memory instruction between consecutive MFMAs: the
+// next step's 8 operand reads, the 4 activation stores, then the 8 global
+// loads (two per MFMA).  Of the placements tried (stores grouped at the
+// start or the end of the step, loads before the stores) this was fastest.
+template <bool HAS_ZB>
+__device__ __forceinline__ void pf_schedule_staged() {
+    constexpr int MFMA = 0x008, VMEM_RD = 0x020, DS_RD = 0x100, DS_WR = 0x200;
+    static_for<8>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+    });
+    static_for<4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_WR, 1, 0);
+    });
+    static_for<4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(VMEM_RD, 2, 0);
+    });
+    if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
+}
+
+// Step order of the direct-load path: the 12 operand reads for the next
+// step (8 activation, 4 weight) and the 6 global-to-LDS copies (4 activation
+// fragments, 2 weight tiles) spread between the 16 MFMAs.
+template <bool HAS_ZB>
+__device__ __forceinline__ void pf_schedule_direct() {
+    constexpr int MFMA = 0x008, VMEM = 0x060, DS_RD = 0x100;
+    static_for<6>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(VMEM, 1, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
+    if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
+}
+
+// s_waitcnt that waits for the vector memory counter only (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// Workgroup barrier for LDS written by this workgroup's own LDS stores and
+// by global-to-LDS copies whose completion the caller has already waited for
+// (vmcnt).  __syncthreads' release fence would also wait for every
+// outstanding global load, including the weight operands and the copies of
+// later stages that are meant to stay in flight across the barrier.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// FAST (A 16-byte aligned, lda % 16 == 0, K % 64 == 0): every global load is
+// unconditional, so loads issued for later stages stay in flight (a load
+// inside a branch makes the compiler wait for it at the branch's end).  Rows
+// past M read row M - 1 and strips past the last read the last strip; those
+// products land in outputs that are never stored.  The FAST path copies the
+// activations global-to-LDS; the general path stages them through registers
+// (masked, shifted for uint8 A, stored to LDS).  FLIP (uint8 A on the FAST
+// path): the copies land unshifted and each step flips its own operand
+// registers before its MFMAs.
+template <bool HAS_ZB, bool FAST, bool FLIP>
+__global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
+    constexpr int AF = PF_BM / 16;      // A fragments per stage
+    constexpr int BF = PF_BN / 16;      // B fragments per stage
+    constexpr int ACH = AF * 64 / 256;  // 16-byte A chunks per thread per stage (4)
+    constexpr int SA = AF * 1024;  // bytes of one activation stage
+    constexpr int SB = BF * 1024;  // bytes of one weight stage (FAST: in LDS after the activations)
+    constexpr int SD = FAST ? SA + SB : 16;
+    // activation stages in LDS: three for the register-staged path; for the
+    // FAST path one array per stage, so that the compiler can tell a read
+    // of one stage from a copy still landing in another (it waits for every
+    // outstanding global-to-LDS copy before a read it cannot separate from
+    // them)
+    __shared__ __attribute__((aligned(16))) int8_t sA[FAST ? 1 : 3][FAST ? 16 : SA];
+    static_assert(PF_DEPTH <= 6, "direct-path stage arrays");
+    __shared__ __attribute__((aligned(16))) int8_t sD0[SD], sD1[SD], sD2[SD], sD3[SD],
+        sD4[FAST && PF_DEPTH > 4 ? SD : 16], sD5[FAST && PF_DEPTH > 5 ? SD : 16];
+    auto stage_buf = [&](auto B) -> int8_t * {
+        constexpr int b = decltype(B)::value;
+        if constexpr (b == 0) return sD0;
+        else if constexpr (b == 1) return sD1;
+        else if constexpr (b == 2) return sD2;
+        else if constexpr (b == 3) return sD3;
+        else if constexpr (b == 4) return sD4;
+        else return sD5;
+    };
+    __shared__ __attribute__((aligned(16))) float s_rs[PF_BM];
+    __shared__ int32_t s_za[PF_BM];
+    __shared__ ColOps s_col[PF_BN];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_n = (p.NS + BF - 1) / BF;
+    const int bn = blockIdx.x % tiles_n;
+    const int bm = blockIdx.x / tiles_n;
+    const int m0 = bm * PF_BM;
+    const int strip0 = bn * BF;
+    const int KT = p.KT;
+
+    // FAST: wave w copies A fragments 4 w .. 4 w + 3 of each stage straight
+    // into LDS, one 16-byte piece per lane landing in slot L of the fragment;
+    // lane L fetches the (row, k-chunk) that the swizzle puts in slot L.  k
+    // advances by 64 bytes a step.
+    const int8_t *a_src[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int r = lane >> 2;
+        const int g = (lane & 3) ^ pf_chunk_perm(r);
+        const int row = min(m0 + (4 * wave + i) * 16 + r, p.M - 1);
+        a_src[i] = p.A + (int64_t)row * p.lda + g * 16;
+    }
+    // weight operands of this wave: column tile t (32 columns, strips
+    // 2t and 2t+1 of the wave's 4), k half h; strips past the last read the
+    // last one (their columns are never stored)
+    const int8_t *b_src[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int strip = min(strip0 + wn * 4 + t * 2 + ((lane & 31) >> 4), p.NS - 1);
+        b_src[t] = p.codes + (int64_t)strip * KT * kTileBytes;
+    }
+    v4i ra[PF_DEPTH][ACH], rb[PF_DEPTH][2][2];
+    int a_dst[ACH];  // general path: LDS byte offset of thread's piece i of a stage
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int c = tid + 256 * i;
+        const int r = c >> 2;
+        a_dst[i] = (r >> 4) * 1024 + pf_slot(r & 15, c & 3) * 16;
+    }
+    // operand read offsets inside a 1 KiB fragment, per k half: chunk 2 h + L / 32
+    int a_rd[2], b_rd[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        a_rd[h] = pf_slot(lane & 15, 2 * h + (lane >> 5)) * 16;
+        b_rd[h] = ((2 * h + (lane >> 5)) * 16 + (lane & 15)) * 16;  // inside a packed 1 KiB tile
+    }
+    auto gload = [&](auto slot, int kt) {
+        constexpr int sl = decltype(slot)::value;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) rb[sl][t][h] = *(const v4i *)(b_src[t] + (int64_t)kt * kTileBytes + b_rd[h]);
+        if (FAST) return;
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int c = tid + 256 * i;  // (row, k-chunk) = (c >> 2, c & 3)
+            ra[sl][i] = load_a16<false>(p, m0 + (c >> 2), kt * kTileK + (c & 3) * 16);
+        }
+    };
+    // FAST: weight tiles of the workgroup's 8 strips: wave w copies strips
+    // 2 w and 2 w + 1 (lane L copies 16-byte chunk L of the packed tile, so
+    // the LDS image is the tile as stored)
+    const int8_t *bt_src[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int strip = min(strip0 + 2 * wave + u, p.NS - 1);
+        bt_src[u] = p.codes + (int64_t)strip * KT * kTileBytes + lane * 16;
+    }
+    // FAST: stage kt (activation fragments and weight tiles) into LDS buffer
+    // BUF, without passing through registers
+    auto dload = [&](auto BUF, int kt) {
+        constexpr int b = decltype(BUF)::value;
+#pragma unroll
+        for (int i = 0; i < ACH; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(a_src[i] + (int64_t)kt * kTileK),
+                                             (__attribute__((address_space(3))) void *)(stage_buf(ic<b>{}) + (4 * wave + i) * 1024),
+                                             16, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            __builtin_amdgcn_global_load_lds((const void *)(bt_src[u] + (int64_t)kt * kTileBytes),
+                                             (__attribute__((address_space(3))) void *)(stage_buf(ic<b>{}) + SA + (2 * wave + u) * 1024),
+                                             16, 0, 0);
+    };
+    auto sstore = [&](auto slot, int buf) {
+        constexpr int sl = decltype(slot)::value;
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) *(v4i *)(&sA[buf][a_dst[i]]) = ra[sl][i];
+    };
+
+    v16i acc[4][2];
+    v16i accr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        accr[i] = v16i{};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v16i{};
+    }
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+
+    // activation operands, double-buffered in registers: a step's operands
+    // are read from LDS during the previous step's MFMAs.  [tile][k half]
+    v4i fa[2][4][2];
+    // FAST: weight operands from LDS as well, double-buffered like fa: [tile][k half]
+    v4i fb[2][2][2];
+    auto lds_frags_at = [&](auto F, const int8_t *base) {
+        constexpr int f = decltype(F)::value;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                fa[f][t][h] = *(const v4i *)(base + (wm * 8 + t * 2 + ((lane & 31) >> 4)) * 1024 + a_rd[h]);
+        if constexpr (FAST) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    fb[f][t][h] = *(const v4i *)(base + SA + (wn * 4 + t * 2 + ((lane & 31) >> 4)) * 1024 + b_rd[h]);
+        }
+    };
+    auto lds_frags = [&](auto F, int buf) { lds_frags_at(F, &sA[buf][0]); };
+    // step k: activation set F, weight operands from register slot S (FAST:
+    // from operand set F)
+    auto mfmas = [&](auto F, auto S) {
+        constexpr int f = decltype(F)::value, sl = decltype(S)::value;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = mfma32_i8(fa[f][i][h], FAST ? fb[f][j][h] : rb[sl][j][h], acc[i][j]);
+                if (HAS_ZB) accr[i] = mfma32_i8(fa[f][i][h], ones, accr[i]);
+            }
+    };
+
+    // Stage s: register slot s % PF_DEPTH, LDS buffer s % 3, activation
+    // operand set s % 2.  Step k: read step k+1's activation operands (LDS
+    // buffer written in step k-1, published by its barrier), MFMAs of step k
+    // (weight operands in slot k % PF_DEPTH, loaded PF_DEPTH steps ago),
+    // store stage k+2's activations (its buffer was last read for step k-1,
+    // whose reads completed before the MFMAs of step k-1), load stage
+    // k+PF_DEPTH into slot k % PF_DEPTH, barrier.
+    const int KTD = KT - KT % PF_DEPTH;
+    if constexpr (FAST) {
+        // Stage s: LDS buffer s % PF_DEPTH (activation fragments, then the
+        // weight tiles), operand sets s % 2.  Step k: read step k+1's
+        // operands (published by the barrier of step k-1), MFMAs of step k,
+        // copy stage k+PF_DEPTH (its buffer held stage k, read in step
+        // k-1), then wait until stage k+2 has landed in LDS and barrier.
+        // Every step issues 6 copies per wavefront (stages past the last
+        // repeat the last one), so stage k+2's are complete once at most
+        // 6 (PF_DEPTH - 2) remain outstanding.
+        static_for<PF_DEPTH>([&](auto S) { dload(S, min(decltype(S)::value, KT - 1)); });
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<6 * (PF_DEPTH - 2)>();
+        lds_barrier();
+        lds_frags_at(ic<0>{}, stage_buf(ic<0>{}));
+        wait_lgkmcnt0();
+        auto dstep = [&](auto J, int kt) {
+            constexpr int j = decltype(J)::value;
+            lds_frags_at(ic<(j + 1) & 1>{}, stage_buf(ic<(j + 1) % PF_DEPTH>{}));
+            if constexpr (FLIP) {
+                // uint8 activations: the flip happens on this step's operands,
+                // read (and waited for) before the previous barrier
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) fa[j & 1][t][h] ^= 0x80808080;
+            }
+            mfmas(ic<j & 1>{}, J);
+            const int kn = min(kt + PF_DEPTH, KT - 1);
+            dload(J, kn);
+            pf_schedule_direct<HAS_ZB>();
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<6 * (PF_DEPTH - 2)>();
+            lds_barrier();
+        };
+        for (int base = 0; base < KTD; base += PF_DEPTH)
+            static_for<PF_DEPTH>([&](auto J) { dstep(J, base + decltype(J)::value); });
+        static_for<PF_DEPTH - 1>([&](auto J) {
+            if (KTD + decltype(J)::value < KT) dstep(J, KTD + decltype(J)::value);
+        });
+        wait_vmcnt<0>();
+    } else {
+    static_for<PF_DEPTH>([&](auto S) { gload(S, min(decltype(S)::value, KT - 1)); });
+    sstore(ic<0>{}, 0);
+    sstore(ic<1 % PF_DEPTH>{}, 1);
+    __syncthreads();
+    lds_frags(ic<0>{}, 0);
+    auto step = [&](auto J, int kt) {
+        constexpr int j = decltype(J)::value;
+        lds_frags(ic<(j + 1) & 1>{}, (kt + 1) % 3);
+        mfmas(ic<j & 1>{}, J);
+        sstore(ic<(j + 2) % PF_DEPTH>{}, (kt + 2) % 3);
+        gload(ic<j>{}, min(kt + PF_DEPTH, KT - 1));
+        pf_schedule_staged<HAS_ZB>();
+        __syncthreads();
+    };
+    static_assert(PF_DEPTH % 2 == 0, "fragment sets alternate with the unrolled steps");
+    static_assert(PF_DEPTH >= 3, "stage k+2 is stored in step k: it must have been loaded in an earlier step");
+    for (int base = 0; base < KTD; base += PF_DEPTH)
+        static_for<PF_DEPTH>([&](auto J) { step(J, base + decltype(J)::value); });
+    static_for<PF_DEPTH - 1>([&](auto J) {
+        if (KTD + decltype(J)::value < KT) step(J, KTD + decltype(J)::value);
+    });
+    }
+
+    // ---- epilogue.  Row scales and column operands are staged in LDS (the
+    // A/B buffers are no longer needed); the common case (fp32 output, no
+    // zero points, a whole tile inside M x N) runs without per-element
+    // branches.
+    for (int r = tid; r < PF_BM; r += 256) {
+        const int m = min(m0 + r, p.M - 1);
+        const float v = (p.row_scale ? p.row_scale : p.col_scale)[m];
+        s_rs[r] = p.row_scale ? v : 1.0f;
+        s_za[r] = row_za(p, m);
+    }
+    if (tid < PF_BN) s_col[tid] = load_colops_c(p, strip0 * kTileN + tid);
+    __syncthreads();
+    const bool whole = m0 + PF_BM <= p.M && (strip0 + BF) * kTileN <= p.N;
+    // accumulator element e of tile (i, j): row i*32 + 8 (e / 4) + 4 (L / 32) + e % 4,
+    // column j*32 + L % 32 of the wavefront's 128 x 64 block
+    if (!HAS_ZB && p.outputs == QMM_OUT_F32 && p.zAs == 0 && !p.za_row && whole) {
+        float cm[2], cb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const ColOps c = s_col[wn * 64 + j * 32 + (lane & 31)];
+            cm[j] = c.cs;
+            cb[j] = c.bias_f;
+        }
+        float *ybase = p.y_f32 + (int64_t)(m0 + wm * 128 + 4 * (lane >> 5)) * p.ld_f32 + strip0 * kTileN +
+                       wn * 64 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = i * 32 + 8 * g;
+                const v4f rs = *(const v4f *)(&s_rs[wm * 128 + r0 + 4 * (lane >> 5)]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float *yrow = ybase + (int64_t)(r0 + v) * p.ld_f32;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const float mult = (rs[v] * cm[j]) * p.scale;
+                        yrow[j * 32] = fmaf((float)acc[i][j][4 * g + v], mult, cb[j]);
+                    }
+                }
+            }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int cl = wn * 64 + j * 32 + (lane & 31);
+            const int n = strip0 * kTileN + cl;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int rl = wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int m = m0 + rl;
+                if (m < p.M && n < p.N)
+                    epilogue_store_c(p, m, n, (uint32_t)acc[i][j][e], HAS_ZB ? accr[i][e] : 0, HAS_ZB, s_rs[rl],
+                                     s_za[rl], s_col[cl]);
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_int8_prefill(const Int8GemmParams &p, hipStream_t s) {
+    dim3 grid((unsigned)(ceil_div(p.NS, PF_BN / kTileN) * ceil_div(p.M, PF_BM)));
+    const bool fast = p.a_vec && (p.K % kTileK) == 0;
+    const dim3 b(256);
+    if (p.zBs != 0 || p.zb_col) {
+        if (fast && p.a_u8)
+            hipLaunchKernelGGL((k_int8_prefill<true, true, true>), grid, b, 0, s, p);
+        else if (fast)
+            hipLaunchKernelGGL((k_int8_prefill<true, true, false>), grid, b, 0, s, p);
+        else
+            hipLaunchKernelGGL((k_int8_prefill<true, false, false>), grid, b, 0, s, p);
+    } else {
+        if (fast && p.a_u8)
+            hipLaunchKernelGGL((k_int8_prefill<false, true, true>), grid, b, 0, s, p);
+        else if (fast)
+            hipLaunchKernelGGL((k_int8_prefill<false, true, false>), grid, b, 0, s, p);
+        else
+            hipLaunchKernelGGL((k_int8_prefill<false, false, false>), grid, b, 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qmm

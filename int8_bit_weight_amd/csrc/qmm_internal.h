@@ -69,42 +69,45 @@ inline PackedBLayout packed_b_layout(int64_t K, int64_t N) {
 // int8 GEMM launch parameters (passed by value as the kernel argument).
 // ------------------------------------------------------------------------
 struct Int8GemmParams {
+    // 8-byte fields first, then the 4-byte ones: no padding, 240 bytes (the
+    // decode calls measured 0.2 us slower per launch with this struct at 264
+    // bytes, padded between its int and pointer fields)
     const int8_t *A;      // raw bytes of A (int8 or uint8)
     int64_t lda;
-    int M, K, N;
-    int a_u8;             // 1: A is uint8 (flip the top bit to shift by 128)
-    int a_vec;            // 1: A and lda allow aligned 16-byte loads
-    int32_t zAs, zBs;     // zero points in the shifted (int8) domain
-    // per-axis zero points (NULL: the scalars above): one per row of A, one per
-    // column of B, in the caller's domain; za_off / zb_off (128 for uint8, else
-    // 0) take them to the shifted domain
+    // per-axis zero points (NULL: the scalars zAs, zBs): one per row of A, one
+    // per column of B, in the caller's domain; za_off / zb_off (128 for uint8,
+    // else 0) take them to the shifted domain
     const int32_t *za_row, *zb_col;
-    int32_t za_off, zb_off;
     const int8_t *codes;  // packed tiles
     const int32_t *colsum;
-    int KT, NS;           // k tiles, n strips
     // epilogue
-    uint32_t outputs;
     int32_t *y_i32;
     int64_t ld_i32;
     float *y_f32;
     int64_t ld_f32;
     int8_t *y_q8;
     int64_t ld_q8;
-    int q8_u8;
     const float *row_scale;  // NULL = 1
     const float *col_scale;  // never NULL (defaults to the packed scales)
-    float scale;
     const float *bias_f32;
     const int32_t *bias_i32;
-    int32_t zp_out;
     // dynamic variant: fp32 activations quantised per row inside the kernel
     const float *X;
     int64_t ldx;
-    int x_vec;             // 1: X and ldx allow aligned 16-byte loads
     int8_t *xq_out;        // optional copies of the quantised rows / scales
     int64_t ldq;
     float *rs_out;
+    int M, K, N;
+    int a_u8;             // 1: A is uint8 (flip the top bit to shift by 128)
+    int a_vec;            // 1: A and lda allow aligned 16-byte loads
+    int32_t zAs, zBs;     // zero points in the shifted (int8) domain
+    int32_t za_off, zb_off;
+    int KT, NS;           // k tiles, n strips
+    uint32_t outputs;
+    int q8_u8;
+    float scale;
+    int32_t zp_out;
+    int x_vec;             // 1: X and ldx allow aligned 16-byte loads
     int rpg;               // > 0: rows per row group (blockIdx.y), each group an independent call
 };
 
@@ -134,6 +137,8 @@ hipError_t launch_pack_b_raw(const void *B, int u8, int64_t ldb, const PackedBLa
                              void *packed, hipStream_t s);
 hipError_t launch_quantize_rows(const float *X, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
                                 int64_t ldq, float *row_scale, hipStream_t s);
+// the prefill kernel (M > 32), launched by launch_int8_gemm
+hipError_t launch_int8_prefill(const Int8GemmParams &p, hipStream_t s);
 hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                             const char **variant);
 hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
