@@ -58,6 +58,7 @@ def _load():
         "oracle_q4_1_decode": (None, [_P, _I64, _I64, _P]),
         "oracle_q4_1_matmul": (None, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64]),
         "oracle_q4_1_matmul_at": (None, [_P, _I64, _I64, _P, _P, _P, _I64, _P]),
+        "oracle_q4_1_matmul_q8": (None, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _I64]),
         "oracle_q4_1_matmul_id": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _I64,
                                          _I64]),
         "oracle_q4_1_matmul_id_at": (_INT, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _P, _I64, _P]),
@@ -209,6 +210,19 @@ def q4_1_matmul(X: np.ndarray, blocks: np.ndarray, K: int, N: int) -> np.ndarray
     assert X.shape[1] == K and blocks.size == (K // 32) * N * 20
     Y = np.empty((M, N), dtype=np.float64)
     _load().oracle_q4_1_matmul(_ptr(X), M, K, K, _ptr(blocks), N, _ptr(Y), N)
+    return Y
+
+
+def q4_1_matmul_q8(Xq: np.ndarray, sa: np.ndarray, blocks: np.ndarray, K: int, N: int) -> np.ndarray:
+    """q4_1 weights x per-row int8 activations: Xq int8 [M, K], row scales sa
+    fp32 [M]; returns Y [M, N] fp64."""
+    Xq = np.ascontiguousarray(Xq, dtype=np.int8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    M = Xq.shape[0]
+    assert Xq.shape[1] == K and sa.shape == (M,) and blocks.size == (K // 32) * N * 20
+    Y = np.empty((M, N), dtype=np.float64)
+    _load().oracle_q4_1_matmul_q8(_ptr(Xq), _ptr(sa), M, K, K, _ptr(blocks), N, _ptr(Y), N)
     return Y
 
 

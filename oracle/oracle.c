@@ -285,6 +285,38 @@ void oracle_q4_1_matmul_at(const float *X, int64_t K, int64_t ldx, const uint8_t
     }
 }
 
+/* q4_1 weights against per-row int8 activations ([P1] "The three layers of
+ * the pack", item 2: every matmul input quantised per row with amax/127;
+ * [P4] "Q4NX chunks": W = q*d + m per block of 32 k).  The block form: per
+ * block b of column n the integer dot D = sum_k q*xq and the integer row sum
+ * S = sum_k xq are exact; then Y[m,n] = sa[m] * sum_b (d*D + mn*S), in fp64
+ * with the blocks in k order. */
+void oracle_q4_1_matmul_q8(const int8_t *Xq, const float *sa, int64_t M, int64_t K, int64_t ldq,
+                           const uint8_t *blocks, int64_t N, double *Y, int64_t ldy) {
+    const int64_t NB = K / 32;
+    int64_t n;
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < NB; ++b) {
+                const uint8_t *blk = blocks + (n * NB + b) * 20;
+                const double d = bf16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+                const double mn = bf16_to_f64((uint16_t)(blk[2] | (blk[3] << 8)));
+                int64_t D = 0, S = 0;
+                for (int j = 0; j < 32; ++j) {
+                    const int64_t q = (j < 16) ? (blk[4 + j] & 0x0F) : (blk[4 + j - 16] >> 4);
+                    const int64_t x = Xq[m * ldq + b * 32 + j];
+                    D += q * x;
+                    S += x;
+                }
+                acc += d * (double)D + mn * (double)S;
+            }
+            Y[m * ldy + n] = (double)sa[m] * acc;
+        }
+    }
+}
+
 /* [P5] "The bugs that were the work": the per-token expert ids are a strided
  * view (17 sorted experts per token, row stride 17 int32); only the first
  * n_expert_used of each row are used and they must be read through the

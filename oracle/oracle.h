@@ -85,6 +85,12 @@ void oracle_q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx,
 void oracle_q4_1_matmul_at(const float *X, int64_t K, int64_t ldx, const uint8_t *blocks,
                            const int64_t *im, const int64_t *in, int64_t count, double *out);
 
+/* q4_1 weights x per-row int8 activations (codes Xq, scales sa):
+ * Y[m,n] = sa[m] * sum_b (d[n,b] * sum_{k in b} q*xq + m[n,b] * sum_{k in b} xq),
+ * integer block sums exact, the rest fp64. */
+void oracle_q4_1_matmul_q8(const int8_t *Xq, const float *sa, int64_t M, int64_t K, int64_t ldq,
+                           const uint8_t *blocks, int64_t N, double *Y, int64_t ldy);
+
 /* MUL_MAT_ID: for t < T, s < n_used, e = ids[t*ids_row_stride + s],
  * Y[t][s][:] = x(t,s) * W_e, where the activation row x(t,s) starts at
  * X + t*ldx + s*ldx_slot: ldx_slot = 0 is the shared form (token t's row for

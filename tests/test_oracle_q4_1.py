@@ -268,3 +268,57 @@ def test_moe_per_slot_permutation_and_sampled(orc):
     in_ = np.array([15, 3, 0, 7])
     got = orc.q4_1_matmul_id_at(X3, experts, E, K, N, ids, it, is_, in_, n_used=n_used)
     assert np.array_equal(got, Y[it, is_, in_])
+
+
+# ------------------------- q4_1 weights x per-row int8 activations ---
+
+def test_q4_q8_against_numpy(orc):
+    """Y = diag(sa) (Xq @ W) with W decoded by its closed form (pinned above):
+    numpy fp64 on the decoded weight, including codes 0/15, d = 0 blocks and
+    activation codes +-127."""
+    g = np.random.default_rng(71)
+    M, K, N = 5, 160, 19
+    W = wl.normal_f32(g, (K, N), 0.02)
+    blocks = wl.encode_q4_1(W)
+    blocks[3, 1, :2] = 0                         # d = 0 block
+    Xq = g.integers(-127, 128, (M, K)).astype(np.int8)
+    Xq[0, :7] = 127
+    Xq[1, 40:50] = -127
+    sa = g.uniform(0.001, 0.05, M).astype(np.float32)
+    Y = orc.q4_1_matmul_q8(Xq, sa, blocks, K, N)
+    ref = (Xq.astype(np.float64) @ orc.q4_1_decode(blocks, K, N)) * sa.astype(np.float64)[:, None]
+    assert np.allclose(Y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_q4_q8_integer_block_form(orc):
+    """The block form with Python integers for the dots and row sums on one
+    block per column, from explicit (d, m, codes): exact to fp64 rounding."""
+    g = np.random.default_rng(72)
+    N, nb = 3, 2
+    d_bits, m_bits, codes, blocks = _explicit_blocks(N, nb, g)
+    K = 32 * nb
+    Xq = g.integers(-127, 128, (2, K)).astype(np.int8)
+    sa = np.array([0.5, 0.25], dtype=np.float32)
+    Y = orc.q4_1_matmul_q8(Xq, sa, blocks, K, N)
+    for m in range(2):
+        for n in range(N):
+            tot = 0.0
+            for b in range(nb):
+                xs = [int(v) for v in Xq[m, 32 * b:32 * b + 32]]
+                D = sum(int(c) * x for c, x in zip(codes[n, b], xs))
+                S = sum(xs)
+                tot += float(wl.bf16_bits_to_f32(d_bits[n, b])) * D + float(wl.bf16_bits_to_f32(m_bits[n, b])) * S
+            assert Y[m, n] == pytest.approx(float(sa[m]) * tot, rel=1e-15, abs=1e-300)
+
+
+def test_q4_q8_matches_fp32_activation_path(orc):
+    """With activations that are exactly their int8 codes times the row scale,
+    the fp32-activation product (pinned above) gives the same result."""
+    g = np.random.default_rng(73)
+    M, K, N = 3, 96, 11
+    blocks = wl.encode_q4_1(wl.normal_f32(g, (K, N), 0.02))
+    Xq = g.integers(-127, 128, (M, K)).astype(np.int8)
+    sa = np.array([1.0, 0.5, 2.0 ** -7], dtype=np.float32)
+    X = (Xq.astype(np.float32) * sa[:, None]).astype(np.float32)     # exact: power-of-two scales
+    assert np.allclose(orc.q4_1_matmul_q8(Xq, sa, blocks, K, N), orc.q4_1_matmul(X, blocks, K, N),
+                       rtol=1e-12, atol=1e-15)
