@@ -361,7 +361,7 @@ def main() -> int:
         extra["int8_prefill_m2048"] = pre
 
         # ------------------------------- q4_1 product, M = 1 and 16 ---
-        q4 = {}
+        q4, q4q8 = {}, {}
         for i, (K, N) in enumerate(wl.Q4_SHAPES):
             _, blocks = wl.q4_weight(K, N, seed_index=i)
             bd = torch.from_numpy(blocks.reshape(-1)).to(dev)
@@ -379,8 +379,17 @@ def main() -> int:
                 b = wbytes + 4 * M * K + 4 * M * N
                 q4["%dx%d_m%d" % (K, N, M)] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
                                                "%HBM": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2)}
+                # the same weights against per-row int8 activations
+                Xq, sa = q.quantize_rows_int8(X)
+                fs = [(lambda W=W, Xq=Xq, sa=sa, Y=Y: q.q4_1_matmul_q8(Xq, sa, W, out=Y)) for W in ring]
+                fs[0]()
+                t = float(np.median(np.array(time_launches(torch, fs * 3))))
+                b = wbytes + M * K + 4 * M + 4 * M * N
+                q4q8["%dx%d_m%d" % (K, N, M)] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                                                 "%HBM": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2)}
             del ring, bd
         extra["q4_1_matmul"] = q4
+        extra["q4_1_matmul_q8"] = q4q8
 
         # --------------------------------------------- MUL_MAT_ID ---
         d = wl.moe_inputs()

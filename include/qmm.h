@@ -256,6 +256,21 @@ qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx,
                        const void *Wpacked, int64_t N, float *Y, int64_t ldy,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * q4_1_matmul_q8: q4_1 weights against per-row int8 activations (the codes
+ * and scales quantize_rows_int8 writes: [P1] "The three layers of the pack",
+ * item 2; [P4] "Q4NX chunks" for W = q*d + m):
+ *   Y[m,n] = row_scale[m] * sum_b ( d[n,b] * sum_{k in b} q[n,k]*Xq[m,k]
+ *                                 + m[n,b] * sum_{k in b} Xq[m,k] )
+ * Each block dot and row sum is exact (int32 MFMA); the combination is fp32.
+ * It trades the fp32 activations of q4_1_matmul for int8 ones.
+ *   Xq         device int8 M x K (ldq >= K); row_scale device fp32 [M]
+ *   Wpacked    written by q4_1_repack for this K, N;  Y device fp32 M x N
+ * K % 32 != 0 is QMM_ERR_UNSUPPORTED.  Rows run 16 per launch; no workspace.
+ */
+qmm_status q4_1_matmul_q8(const int8_t *Xq, const float *row_scale, int64_t M, int64_t K, int64_t ldq,
+                          const void *Wpacked, int64_t N, float *Y, int64_t ldy, void *stream);
+
 /* Workspace bytes q4_1_matmul_id needs. */
 size_t qmm_q4_1_matmul_id_workspace_bytes(int64_t n_tokens, int64_t n_used, int64_t n_expert,
                                           int64_t K, int64_t N);

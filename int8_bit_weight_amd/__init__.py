@@ -7,7 +7,8 @@ built (``python int8_bit_weight_amd/build.py``); there is no CPU fallback.
 
 Functions carry the names of the C entry points declared in include/qmm.h:
 ``pack_b_int8``, ``pack_b_int8_raw``, ``quantize_rows_int8``, ``int8_gemm``,
-``q4_1_repack``, ``q4_1_matmul``, ``q4_1_matmul_id``, ``q4_1_matmul_id_per_slot``.
+``q4_1_repack``, ``q4_1_matmul``, ``q4_1_matmul_q8``, ``q4_1_matmul_id``,
+``q4_1_matmul_id_per_slot``.
 """
 from __future__ import annotations
 
@@ -77,6 +78,7 @@ _SIGS = {
     "qmm_q4_1_matmul_id_per_slot_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64]),
     "q4_1_matmul_id_per_slot": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _I64, _I64, _SZ, _P, _I64, _I64,
                                        _P, _I64, _I64, _P, _SZ, _P]),
+    "q4_1_matmul_q8": (_INT, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "qmm_status_string": (ctypes.c_char_p, [_INT]),
     "qmm_last_hip_error": (_INT, []),
     "qmm_last_variant": (ctypes.c_char_p, []),
@@ -353,6 +355,20 @@ def q4_1_repack_experts(blocks, K: int, N: int, stream=None):
         _check("q4_1_repack", lib.q4_1_repack(_ptr(blocks[e]), K, N, ctypes.c_void_p(out.data_ptr() + e * stride),
                                               stride, _stream(stream)))
     return out, stride
+
+
+def q4_1_matmul_q8(Xq, row_scale, W: PackedQ4, out=None, stream=None):
+    """Y = diag(row_scale) (Xq @ dequant(W)) for int8 Xq [M, K] (the codes and
+    scales of quantize_rows_int8); returns fp32 Y [M, N]."""
+    torch = _torch()
+    M, K = Xq.shape
+    if K != W.K:
+        raise ValueError("Xq has K=%d, packed weight has K=%d" % (K, W.K))
+    assert Xq.dtype == torch.int8 and Xq.stride(1) == 1
+    Y = torch.empty((M, W.N), dtype=torch.float32, device=Xq.device) if out is None else out
+    _check("q4_1_matmul_q8", lib.q4_1_matmul_q8(_ptr(Xq), _ptr(row_scale), M, K, Xq.stride(0), _ptr(W.data), W.N,
+                                                _ptr(Y), Y.stride(0), _stream(stream)))
+    return Y
 
 
 def q4_1_matmul_id(X, experts, n_expert: int, K: int, N: int, expert_stride: int, ids, n_used: int, out=None,

@@ -168,6 +168,37 @@ qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx, const 
     return record_status(e, variant);
 }
 
+qmm_status q4_1_matmul_q8(const int8_t *Xq, const float *row_scale, int64_t M, int64_t K, int64_t ldq,
+                          const void *Wpacked, int64_t N, float *Y, int64_t ldy, void *stream) {
+    if (M < 0 || K <= 0 || N < 0 || ldq < K || ldy < N) return QMM_ERR_INVALID;
+    if (K % 32 != 0) return QMM_ERR_UNSUPPORTED;
+    if (M > INT32_MAX / 2 || K > INT32_MAX / 2 || N > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return QMM_OK;
+    if (!Xq || !row_scale || !Wpacked || !Y || !aligned_to(Wpacked, 256) || !aligned_to(row_scale, 4) ||
+        !aligned_to(Y, 4))
+        return QMM_ERR_INVALID;
+    const Q4Layout L = q4_layout(K, N);
+    hipError_t e = hipSuccess;
+    const char *variant = "";
+    // one launch per 16 rows (each reads the whole weight)
+    for (int64_t r0 = 0; r0 < M && e == hipSuccess; r0 += 16) {
+        Q4Q8Params p{};
+        p.recs = (const uint8_t *)Wpacked;
+        p.Xq = Xq + r0 * ldq;
+        p.row_scale = row_scale + r0;
+        p.Y = Y + r0 * ldy;
+        p.ldq = ldq;
+        p.ldy = ldy;
+        p.NQ = (int)L.NQ;
+        p.NS = (int)L.NS;
+        p.N = (int)N;
+        p.K = (int)K;
+        p.M = (int)((M - r0) < 16 ? (M - r0) : 16);
+        e = launch_q4_q8(p, (hipStream_t)stream, &variant);
+    }
+    return record_status(e, variant);
+}
+
 size_t qmm_q4_1_matmul_id_workspace_bytes(int64_t n_tokens, int64_t n_used, int64_t n_expert, int64_t K,
                                           int64_t N) {
     if (n_tokens <= 0 || n_used <= 0 || n_expert <= 0 || K <= 0 || N <= 0 || K % 32 != 0) return 0;

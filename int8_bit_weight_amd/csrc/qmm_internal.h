@@ -210,6 +210,18 @@ struct Q4Params {
 // sc[t] = 15 - e with the token's max |x| = f 2^e, f in [0.5, 1); each piece
 // (block b, k-octet g) of x * 2^sc as two fp16 terms, and each block's sum
 // of x * 2^sc as three bf16 terms, four blocks (a record) per 16 bytes.
+// q4_1 weights x per-row int8 activations (k_q4_q8): one launch per 16 rows.
+struct Q4Q8Params {
+    const uint8_t *recs;      // the weight (q4_1 device layout, with its header)
+    const int8_t *Xq;         // int8 activation codes, row stride ldq
+    const float *row_scale;   // [M] per-row scales
+    float *Y;
+    int64_t ldq, ldy;
+    int NQ, NS, N, K, M;      // M <= 16 rows in this launch
+};
+
+hipError_t launch_q4_q8(const Q4Q8Params &p, hipStream_t s, const char **variant);
+
 // The MoE activation split works on activation rows: R = T tokens (shared
 // form, per = 1) or R = T * n_used (token, slot) pairs (per-slot form,
 // per = n_used); row a starts at X + (a / per) * ldx + (a % per) * ldx_slot.

@@ -139,3 +139,14 @@ def test_int8_gemm_per_axis_rejections(q):
     assert f(FAKE, 0, 4, 64, 63, None, FAKE, 0, 64, None, ctypes.byref(ep), None, 0, None) == INV
     assert f(FAKE, 2, 4, 64, 64, None, FAKE, 0, 64, None, ctypes.byref(ep), None, 0, None) == INV
     assert f(FAKE, 0, 0, 64, 64, FAKE, FAKE, 0, 64, FAKE, ctypes.byref(ep), None, 0, None) == q.QMM_OK
+
+
+def test_q4_1_matmul_q8_rejections(q):
+    INV, UNS = q.QMM_ERR_INVALID, q.QMM_ERR_UNSUPPORTED
+    f = q.lib.q4_1_matmul_q8
+    assert f(FAKE, FAKE, 4, 64, 63, FAKE, 16, FAKE, 16, None) == INV       # ldq < K
+    assert f(FAKE, FAKE, 4, 64, 64, FAKE, 16, FAKE, 15, None) == INV       # ldy < N
+    assert f(FAKE, FAKE, 4, 48, 48, FAKE, 16, FAKE, 16, None) == UNS       # K % 32
+    assert f(FAKE, None, 4, 64, 64, FAKE, 16, FAKE, 16, None) == INV       # no row scales
+    assert f(FAKE, FAKE, 4, 64, 64, ctypes.c_void_p(4096 + 16), 16, FAKE, 16, None) == INV
+    assert f(FAKE, FAKE, 0, 64, 64, FAKE, 16, FAKE, 16, None) == q.QMM_OK

@@ -421,3 +421,49 @@ def test_moe_every_chunk_size(q, orc, per_slot):
     for e in range(E):
         sel = ids[:, :n_used] == e
         _check(got[sel], ref[sel])
+
+
+# --------------------------- q4_1 weights x per-row int8 activations ---
+
+def _q8_case(q, orc, M, K, N, seed, small=True, pad=0, **kw):
+    """Activations quantised per row on the GPU (bit-exact to the oracle's
+    quantiser), then q4_1_matmul_q8 against the oracle's block form."""
+    import torch
+    blocks = _blocks(K, N, seed, **kw)
+    X = wl.q4_activations(M, K, seed_index=seed)
+    X[0, :5] = 0.0
+    p = _repack(q, blocks, K, N)
+    Xq, sa = q.quantize_rows_int8(to_dev(X))
+    Qa, so = orc.quantize_rows_int8(X)
+    assert np.array_equal(to_np(Xq), Qa)
+    if pad:
+        Xw = torch.zeros((M, K + pad), dtype=torch.int8, device=torch_dev())
+        Xw[:, :K] = Xq
+        Xq = Xw[:, :K]
+    got = to_np(q.q4_1_matmul_q8(Xq, sa, p))
+    assert q.last_variant() == "q4_q8_m16"
+    ref = orc.q4_1_matmul_q8(Qa, so, blocks, K, N)
+    scale = _abs_scale(orc, Qa.astype(np.float32) * so[:, None], blocks, K, N) if small else None
+    _check(got, ref, scale)
+    return got, ref, (Xq, sa, p)
+
+
+@pytest.mark.parametrize("M,K,N,pad", [(1, 32, 1, 0), (1, 96, 17, 0), (5, 160, 33, 1), (16, 4096, 64, 0),
+                                       (16, 1440, 300, 8), (17, 256, 40, 0), (33, 128, 48, 3), (3, 32 * 45, 20, 0),
+                                       (2, 8192, 272, 0)])
+def test_q4_q8_shapes(q, orc, M, K, N, pad):
+    """Ragged N, a partial last record (K = 96, 160, 1440), one to three
+    16-row launches, unaligned activation rows (byte loads), 4, 8 and 16
+    wavefronts per strip (2 to 64 records)."""
+    _q8_case(q, orc, M, K, N, seed=M + K + N, pad=pad, zero_cols=(3,), zero_scale_blocks=True)
+
+
+@pytest.mark.parametrize("shape", range(len(wl.Q4_SHAPES)))
+@pytest.mark.parametrize("M", wl.Q4_ROWS)
+def test_q4_q8_full_size(q, orc, shape, M):
+    """8B-class shapes at M = 1 and 16: the full output against the oracle,
+    and bitwise equal on a second call."""
+    K, N = wl.Q4_SHAPES[shape]
+    got, _, (Xq, sa, p) = _q8_case(q, orc, M, K, N, seed=shape, small=False)
+    again = to_np(q.q4_1_matmul_q8(Xq, sa, p))
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
