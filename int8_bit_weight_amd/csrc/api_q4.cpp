@@ -6,7 +6,7 @@
 #include <cstdlib>
 
 #include "qmm.h"
-#include "qmm_internal.h"
+#include "q4_internal.h"
 
 namespace qmm {
 

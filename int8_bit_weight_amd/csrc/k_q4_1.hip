@@ -22,7 +22,7 @@
 #include <type_traits>
 #include <utility>
 
-#include "qmm_internal.h"
+#include "q4_internal.h"
 
 namespace qmm {
 

@@ -14,7 +14,7 @@
 // rounding.
 #include <cstdlib>
 
-#include "qmm_internal.h"
+#include "q4_internal.h"
 
 namespace qmm {
 
