@@ -296,6 +296,25 @@ def test_per_axis_pages_values_and_constant_vectors(q, orc):
     assert np.array_equal(to_np(a), orc.int8_gemm_i64(A, -40, B, -25).astype(np.int32))
 
 
+@pytest.mark.parametrize("M", [3, 40])
+def test_int8_max_k(q, orc, M):
+    """The largest K the bound K*255*128 < 2^31 admits that is a multiple of
+    64 (65792; 65794 is refused on the host): decode (several rounds of k
+    tiles per wavefront) and prefill.  One row of A and one column of B at
+    -128 make that output K * 16384 = 1,077,936,128, the largest product sum
+    of the bound; the rest is random with zero points."""
+    K = 65792
+    assert K * 255 * 128 < 2 ** 31 <= (K + 64) * 255 * 128
+    g = np.random.default_rng(M)
+    A = wl.uniform_i8(g, (M, K))
+    B = wl.uniform_i8(g, (K, 40))
+    A[1, :] = -128
+    B[:, 7] = -128
+    y32, _ = _gemm_case(q, orc, A, 0, B, 0, expect_variant="int8_decode_m16" if M <= 16 else "int8_prefill_256x128")
+    assert to_np(y32)[1, 7] == K * 16384
+    _gemm_case(q, orc, A, 3, B, -5)
+
+
 def test_int8_empty_is_noop(q):
     import torch
     dev = torch_dev()
