@@ -285,7 +285,8 @@ size_t qmm_q4_1_matmul_id_workspace_bytes(int64_t n_tokens, int64_t n_used, int6
  *   Wexperts  device, n_expert weights in the q4_1_repack layout, expert e
  *             at byte offset e*expert_stride (>= qmm_q4_1_packed_bytes(K,N))
  *   ids       device int32, row stride ids_row_stride >= n_used; every used
- *             id must lie in [0, n_expert) (a precondition: not checked)
+ *             id must lie in [0, n_expert) (a precondition: pairs with other
+ *             ids are skipped, and reported in check mode, qmm_set_check)
  * Tokens routed to each expert are grouped on the device (counting sort) and
  * run in one grouped launch.  workspace: zero-filled before its first use
  * (same counter-region rule as int8_gemm).
@@ -327,6 +328,19 @@ int qmm_last_hip_error(void);
 /* Name of the kernel variant the last call on this thread launched
  * (diagnostics; "" before the first call). */
 const char *qmm_last_variant(void);
+
+/*
+ * Check mode, a debug aid (off by default; QMM_CHECK=1 in the environment
+ * turns it on when the library loads).  While on, calls that can verify
+ * device data do so and synchronise the stream: int8_gemm and
+ * int8_gemm_per_axis read the packed weight's header (qmm_packed_b_check)
+ * and return QMM_ERR_INVALID before launching if it does not match K and N;
+ * q4_1_matmul_id and q4_1_matmul_id_per_slot return QMM_ERR_INVALID after the
+ * call if an expert id lay outside [0, n_expert) (those pairs' outputs are
+ * left unwritten, every other output is written).  The flag is process-wide.
+ */
+void qmm_set_check(int on);
+int qmm_check_enabled(void);
 
 #ifdef __cplusplus
 }

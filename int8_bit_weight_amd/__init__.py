@@ -79,6 +79,8 @@ _SIGS = {
     "q4_1_matmul_id_per_slot": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _I64, _I64, _SZ, _P, _I64, _I64,
                                        _P, _I64, _I64, _P, _SZ, _P]),
     "q4_1_matmul_q8": (_INT, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
+    "qmm_set_check": (None, [_INT]),
+    "qmm_check_enabled": (_INT, []),
     "qmm_status_string": (ctypes.c_char_p, [_INT]),
     "qmm_last_hip_error": (_INT, []),
     "qmm_last_variant": (ctypes.c_char_p, []),

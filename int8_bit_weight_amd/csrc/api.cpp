@@ -36,6 +36,10 @@ bool trace_on() {
 
 namespace qmm {
 
+// Check mode (QMM_CHECK=1 at load, or qmm_set_check): calls that can verify
+// device data do so synchronously.
+int g_check = env_int("QMM_CHECK", 0);
+
 qmm_status record_status(hipError_t e, const char *variant) {
     g_last_variant = variant;
     if (trace_on()) fprintf(stderr, "qmm %s\n", variant);
@@ -107,6 +111,9 @@ const char *qmm_status_string(qmm_status s) {
 
 int qmm_last_hip_error(void) { return g_last_hip_error; }
 const char *qmm_last_variant(void) { return g_last_variant; }
+
+void qmm_set_check(int on) { qmm::g_check = on ? 1 : 0; }
+int qmm_check_enabled(void) { return qmm::g_check; }
 
 size_t qmm_pack_b_int8_bytes(int64_t K, int64_t N) {
     if (K < 0 || N < 0) return 0;
@@ -243,6 +250,7 @@ static qmm_status gemm_call(const void *A, qmm_i8type at, int64_t M, int64_t K, 
     if (M == 0 || N == 0) return QMM_OK;
     if (!A || !packedB || !aligned(packedB, 256) || check_epilogue_ptrs(ep) != QMM_OK) return QMM_ERR_INVALID;
     if ((za_row && !aligned(za_row, 4)) || (zb_col && !aligned(zb_col, 4))) return QMM_ERR_INVALID;
+    if (g_check && qmm_packed_b_check(packedB, K, N, stream) != QMM_OK) return QMM_ERR_INVALID;
     const Int8Plan plan = plan_int8_gemm(M, K, N);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
         return QMM_ERR_WORKSPACE;

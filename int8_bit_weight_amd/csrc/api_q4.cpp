@@ -284,6 +284,17 @@ static qmm_status moe_call(const float *X, int64_t n_tokens, int64_t K, int64_t 
         p.zero16 = sp.zero16;
         e = launch_q4_moe(p, per_slot, pl.max_chunks, s, &variant);
     }
+    if (e == hipSuccess && g_check) {
+        // the routing kernel flags ids outside [0, n_expert) (their pairs are
+        // skipped, every other output is written)
+        int32_t bad = 0;
+        e = hipMemcpyAsync(&bad, misc + 1, sizeof(bad), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e == hipSuccess && bad) {
+            record_status(e, variant);
+            return QMM_ERR_INVALID;
+        }
+    }
     return record_status(e, variant);
 }
 

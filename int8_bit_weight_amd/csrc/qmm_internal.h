@@ -17,6 +17,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
 
+// check mode (qmm_set_check / QMM_CHECK=1): synchronous checks of device data
+extern int g_check;
+
 // ------------------------------------------------------------------------
 // Packed int8 weight.  The codes of a K x N weight are stored as 1 KiB tiles
 // of 64 k x 16 n.  Inside a tile, 16-byte chunk `lane` (0..63) holds the 16

@@ -150,3 +150,10 @@ def test_q4_1_matmul_q8_rejections(q):
     assert f(FAKE, None, 4, 64, 64, FAKE, 16, FAKE, 16, None) == INV       # no row scales
     assert f(FAKE, FAKE, 4, 64, 64, ctypes.c_void_p(4096 + 16), 16, FAKE, 16, None) == INV
     assert f(FAKE, FAKE, 0, 64, 64, FAKE, 16, FAKE, 16, None) == q.QMM_OK
+
+
+def test_check_mode_toggle(q):
+    q.lib.qmm_set_check(1)
+    assert q.lib.qmm_check_enabled() == 1
+    q.lib.qmm_set_check(0)
+    assert q.lib.qmm_check_enabled() == 0

@@ -536,3 +536,36 @@ def test_dynamic_without_side_outputs(q, orc):
     Qa, sa = orc.quantize_rows_int8(X)
     Qb, sb, _ = orc.pack_b_int8(W)
     assert max_rel_err(to_np(y), orc.epilogue_f64(orc.int8_gemm_i64(Qa, 0, Qb, 0), sa, sb)) <= F32_TOL
+
+
+def test_packed_header_check_and_check_mode(q):
+    """qmm_packed_b_check reads the header back (the layout-version stamp);
+    in check mode int8_gemm refuses a buffer whose header does not match
+    before launching anything."""
+    import ctypes
+    import torch
+    g = np.random.default_rng(4)
+    B = wl.uniform_i8(g, (64, 32))
+    p = q.pack_b_int8_raw(to_dev(B))
+    ptr = ctypes.c_void_p(p.data.data_ptr())
+    assert q.lib.qmm_packed_b_check(ptr, 64, 32, None) == q.QMM_OK
+    assert q.lib.qmm_packed_b_check(ptr, 64, 48, None) == q.QMM_ERR_INVALID
+    assert q.lib.qmm_packed_b_check(ptr, 128, 32, None) == q.QMM_ERR_INVALID
+    A = to_dev(wl.uniform_i8(g, (4, 64)))
+    y = torch.zeros((4, 32), dtype=torch.int32, device=torch_dev())
+    bad = q.PackedInt8(p.data.clone(), 64, 32, p.bt)
+    bad.data[0] ^= 0xFF                     # magic byte
+    q.lib.qmm_set_check(1)
+    try:
+        assert q.lib.qmm_check_enabled() == 1
+        q.int8_gemm(A, 0, p, 0, out_i32=y)   # a good buffer passes
+        with pytest.raises(RuntimeError):
+            q.int8_gemm(A, 0, bad, 0, out_i32=y)
+    finally:
+        q.lib.qmm_set_check(0)
+    assert np.array_equal(to_np(y), _np_product(A, B))
+
+
+def _np_product(A, B):
+    """numpy int64 product of a device int8 A and a host int8 B (zero points 0)."""
+    return (to_np(A).astype(np.int64) @ B.astype(np.int64)).astype(np.int32)

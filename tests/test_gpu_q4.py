@@ -467,3 +467,34 @@ def test_q4_q8_full_size(q, orc, shape, M):
     got, _, (Xq, sa, p) = _q8_case(q, orc, M, K, N, seed=shape, small=False)
     again = to_np(q.q4_1_matmul_q8(Xq, sa, p))
     assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+
+
+def test_moe_check_mode_reports_bad_id(q, orc):
+    """Check mode: an expert id outside [0, E) makes the call return
+    QMM_ERR_INVALID after it ran (that pair's output untouched, the others
+    written); the same ids in range pass."""
+    import torch
+    E, K, N, T, n_used = 5, 64, 32, 6, 2
+    g = np.random.default_rng(30)
+    experts = np.stack([wl.encode_q4_1(wl.normal_f32(g, (K, N), 0.02)) for _ in range(E)])
+    X = wl.normal_f32(g, (T, K))
+    ids = np.stack([g.permutation(17)[:17] % E for _ in range(T)]).astype(np.int32)
+    buf, estride = q.q4_1_repack_experts(to_dev(experts), K, N)
+    q.lib.qmm_set_check(1)
+    try:
+        q.q4_1_matmul_id(to_dev(X), buf, E, K, N, estride, to_dev(ids), n_used)
+        bad = ids.copy()
+        bad[3, 0] = -1
+        Y = torch.full((T, n_used, N), -9.0, dtype=torch.float32, device=torch_dev())
+        with pytest.raises(RuntimeError):
+            q.q4_1_matmul_id(to_dev(X), buf, E, K, N, estride, to_dev(bad), n_used, out=Y)
+        got = to_np(Y)
+        assert (got[3, 0] == -9.0).all()
+        ok = ids.copy()
+        ok[3, 0] = 0
+        ref = orc.q4_1_matmul_id(X, experts, E, K, N, ok, n_used)
+        mask = np.ones((T, n_used), dtype=bool)
+        mask[3, 0] = False
+        _check(got[mask], ref[mask])
+    finally:
+        q.lib.qmm_set_check(0)
