@@ -42,7 +42,7 @@ METRIC = "GB/s & %HBM peak at M=1/16; int8 TOPS & %MFMA peak at M=2048"
 # (FETCH_SIZE, then WRITE_SIZE) of `bench.py --probe --no-cpu-baseline`, each
 # scaled by what the counter reads for the probe's 1 GiB device copy (FETCH_SIZE
 # x 2.0, WRITE_SIZE x 1.0).  Valid only for the kernel sources it was taken on.
-MEASURED_TRAFFIC = {"sources_sha1": "a4e4b165eaf11bbab8d80ecaf21db3d863e8d731", "bytes_per_launch": 3244648}
+MEASURED_TRAFFIC = {"sources_sha1": "6ab42b7448f671a4659fdb238afb51f26ce78a39", "bytes_per_launch": 3244656}
 
 
 def decode_traffic():
