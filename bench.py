@@ -469,6 +469,40 @@ def main() -> int:
         del ring
         extra["lm_head_1024x151936"] = lm
 
+        # ------------- streaming-read floor: the same sizes, read cold ---
+        floor = {}
+        for nbytes in (2301952, 36700160, 155582464):
+            nb = (nbytes + 15) // 16 * 16
+            copies = max(4, -(-640 * 2 ** 20 // nb))                 # > 2 x (MALL + L2) in all
+            bufs = [torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1) for _ in range(copies)]
+            for wg in (1024, 4096, -(-nb // 4096)):                   # the last: one load per thread
+                sink = torch.empty(wg, dtype=torch.int32, device=dev)
+                fs = [(lambda b_=b_, sink=sink, wg=wg: q.read_probe(b_, sink, wg)) for b_ in bufs]
+                fs[0]()
+                # per launch through the (event, launch, event) timer, and back to
+                # back (one graph of all copies, as the decode calls are timed)
+                t = float(np.median(time_launches(torch, fs * max(1, 48 // copies))))
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    for f in fs:
+                        f()
+                gr.replay()
+                torch.cuda.synchronize()
+                a_ = torch.cuda.Event(enable_timing=True)
+                b2 = torch.cuda.Event(enable_timing=True)
+                a_.record()
+                for _ in range(3):
+                    gr.replay()
+                b2.record()
+                torch.cuda.synchronize()
+                tb = a_.elapsed_time(b2) * 1e-3 / (3 * len(fs))
+                floor["%d_B_wg%d" % (nbytes, wg)] = {"us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1),
+                                                     "back_to_back_us": round(tb * 1e6, 2),
+                                                     "back_to_back_GB/s": round(nbytes / tb / 1e9, 1)}
+                del gr
+            del bufs
+        extra["read_floor"] = floor
+
         # -------------------------------- one-time packing (a1, a5) ---
         K, N = 4096, 14336
         W = torch.from_numpy(wl.normal_f32(wl.rng(4, 77), (K, N), 0.02)).to(dev)

@@ -320,6 +320,17 @@ qmm_status q4_1_matmul_id_per_slot(const float *X, int64_t n_tokens, int64_t K, 
                                    int64_t n_used, float *Y, int64_t ldy_slot, int64_t ldy_token,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------- measurement --- */
+
+/*
+ * qmm_read_probe: a plain streaming read of `bytes` (a multiple of 16, buf
+ * 16-byte aligned) with 16-byte loads over `workgroups` workgroups of 256
+ * threads, each writing one int32 to sink[workgroup] so the loads stay.  It
+ * computes nothing: the floor a bandwidth-bound call of the same size is
+ * compared against (timing only; not part of any product path).
+ */
+qmm_status qmm_read_probe(const void *buf, size_t bytes, int32_t *sink, int64_t workgroups, void *stream);
+
 /* ------------------------------------------------------------- helpers --- */
 
 const char *qmm_status_string(qmm_status s);

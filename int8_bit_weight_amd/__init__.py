@@ -79,6 +79,7 @@ _SIGS = {
     "q4_1_matmul_id_per_slot": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _I64, _I64, _SZ, _P, _I64, _I64,
                                        _P, _I64, _I64, _P, _SZ, _P]),
     "q4_1_matmul_q8": (_INT, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
+    "qmm_read_probe": (_INT, [_P, _SZ, _P, _I64, _P]),
     "qmm_set_check": (None, [_INT]),
     "qmm_check_enabled": (_INT, []),
     "qmm_status_string": (ctypes.c_char_p, [_INT]),
@@ -371,6 +372,12 @@ def q4_1_matmul_q8(Xq, row_scale, W: PackedQ4, out=None, stream=None):
     _check("q4_1_matmul_q8", lib.q4_1_matmul_q8(_ptr(Xq), _ptr(row_scale), M, K, Xq.stride(0), _ptr(W.data), W.N,
                                                 _ptr(Y), Y.stride(0), _stream(stream)))
     return Y
+
+
+def read_probe(buf, sink, workgroups: int, stream=None):
+    """Streaming read of a device byte buffer (measurement floor; see qmm_read_probe)."""
+    _check("qmm_read_probe", lib.qmm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                int(workgroups), _stream(stream)))
 
 
 def q4_1_matmul_id(X, experts, n_expert: int, K: int, N: int, expert_stride: int, ids, n_used: int, out=None,
