@@ -360,6 +360,25 @@ def main() -> int:
             del pk, A, Y
         extra["int8_prefill_m2048"] = pre
 
+        # context, not this library: the vendor BLAS int8 product (torch._int_mm,
+        # int32 out, no epilogue) on the same shapes
+        blas = {}
+        for i, (K, N) in enumerate(wl.PREFILL_SHAPES):
+            try:
+                g_ = wl.rng(4, 50 + i)
+                A = torch.from_numpy(wl.uniform_i8(g_, (wl.PREFILL_M, K))).to(dev)
+                B = torch.from_numpy(wl.uniform_i8(g_, (N, K))).to(dev).t()     # column-major K x N
+                f = (lambda A=A, B=B: torch._int_mm(A, B))
+                f()
+                t = float(np.median(time_launches(torch, [f] * 10)))
+                tops = 2.0 * wl.PREFILL_M * K * N / t / 1e12
+                blas["%dx%d" % (K, N)] = {"us": round(t * 1e6, 2), "TOPS": round(tops, 1),
+                                          "%MFMA": round(100 * tops / INT8_PEAK_TOPS, 2)}
+                del A, B
+            except Exception as exc:  # the vendor routine may not take this layout
+                blas["%dx%d" % (K, N)] = {"error": str(exc)[:120]}
+        extra["vendor_int8_mm_m2048"] = blas
+
         # ------------------------------- q4_1 product, M = 1 and 16 ---
         q4, q4q8 = {}, {}
         for i, (K, N) in enumerate(wl.Q4_SHAPES):
