@@ -105,6 +105,19 @@ MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N, 
 
 using namespace qmm;
 
+// Rows run in launches of 32; a last launch of fewer rows is planned for its
+// own row count (the M <= 4 or 5..16 kernels), so every k_q4_mm launch has
+// 17..32 rows.  The workspace serves the larger of the two plans (launches
+// run in turn on one stream and reuse it).
+static int64_t q4_matmul_ws_bytes(int64_t M, int64_t K, int64_t N) {
+    int64_t w = plan_q4_matmul(M < 32 ? M : 32, K, N).ws_bytes;
+    if (M > 32 && M % 32 != 0) {
+        const int64_t t = plan_q4_matmul(M % 32, K, N).ws_bytes;
+        if (t > w) w = t;
+    }
+    return w;
+}
+
 static bool aligned_to(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 extern "C" {
@@ -127,7 +140,7 @@ qmm_status q4_1_repack(const void *blocks, int64_t K, int64_t N, void *packed, s
 
 size_t qmm_q4_1_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     if (M <= 0 || K <= 0 || N <= 0 || K % 32 != 0) return 0;
-    return (size_t)plan_q4_matmul(M, K, N).ws_bytes;
+    return (size_t)q4_matmul_ws_bytes(M, K, N);
 }
 
 qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx, const void *Wpacked, int64_t N,
@@ -139,14 +152,15 @@ qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx, const 
     if (!X || !Wpacked || !Y || !aligned_to(Wpacked, 256) || !aligned_to(X, 4) || !aligned_to(Y, 4))
         return QMM_ERR_INVALID;
     const Q4Layout L = q4_layout(K, N);
-    const Q4Plan pl = plan_q4_matmul(M, K, N);
-    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)pl.ws_bytes || !aligned_to(workspace, 256)))
+    const int64_t ws_need = q4_matmul_ws_bytes(M, K, N);
+    if (ws_need > 0 && (!workspace || workspace_bytes < (size_t)ws_need || !aligned_to(workspace, 256)))
         return QMM_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     const char *variant = "";
-    for (int64_t r0 = 0; r0 < M && e == hipSuccess; r0 += pl.rows_per_launch) {
-        const int64_t rows = (M - r0) < pl.rows_per_launch ? (M - r0) : pl.rows_per_launch;
+    for (int64_t r0 = 0; r0 < M && e == hipSuccess; r0 += 32) {
+        const int64_t rows = (M - r0) < 32 ? (M - r0) : 32;
+        const Q4Plan pl = plan_q4_matmul(rows, K, N);
         Q4Params p{};
         p.recs = (const uint8_t *)Wpacked;
         p.NQ = (int)L.NQ;

@@ -127,7 +127,8 @@ __global__ __launch_bounds__(256) void k_q4_repack(const uint8_t *__restrict__ b
 //     (k = block) against the split block sums, three MFMAs accumulating
 //     over the whole k range.
 //   blockIdx -> (strip group, k split); rows 0..M-1 (17 <= M <= 32 per
-//   launch; k_q4_mm16 takes 5 <= M <= 16 and k_q4_moe the grouped product).
+//   launch: the host plans a last launch of fewer rows for k_q4_gemv or
+//   k_q4_mm16; k_q4_moe is the grouped product).
 // Loads are never inside branches (a load in a branch makes the compiler wait
 // for it where the branch ends, which would serialise the prefetch): indices
 // past the valid range are clamped to valid memory.  A record past the range
@@ -196,7 +197,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     const int q0 = job * p.qps;
     const int q1 = min(p.NQ, q0 + p.qps);
     const uint8_t *recs = hdr + kHeaderBytes;
-    const int ntile = (nrows + 15) >> 4;  // 16-row tiles holding rows (MFMAs of the others are skipped)
     if (tid < nrows) sRow[tid] = (int64_t)tid * p.ldx;
     for (int o = tid * 16; o < (int)sizeof(sXM); o += NT * 16) *(v4i *)(&sXM[0][0][0][0] + o) = v4i{0, 0, 0, 0};
     __syncthreads();
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     // tile = piece / 64 % MT, block = piece / 64 / MT): a wavefront's 64
     // pieces are one fragment, lane order.  Rows past nrows read row
     // nrows - 1 and stage zeros (their MFMA output rows are never stored);
-    // wavefronts whose tile holds no rows skip the staging (wave-uniform).
+    // both row tiles are always multiplied (see the note on k_q4_moe).
     int pbl[PPT], pg[PPT], prow[PPT], pdst[PPT];
     int64_t psrc[PPT];
     bool pok[PPT], pon[PPT];
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         pg[i] = g;
         pbl[i] = blk;
         pok[i] = idx < PIECES && row < nrows;
-        pon[i] = idx < PIECES && tile < ntile;
+        pon[i] = idx < PIECES;
         psrc[i] = sRow[min(row, nrows - 1)] + g * 8;
         pdst[i] = (blk * 3 * MT + tile) * 1024 + (g * 16 + r) * 16;
     }
@@ -362,7 +362,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
                 const float d = bf16_lo_f32((uint32_t)bs[S][q][j][i]);
 #pragma unroll
                 for (int rt = 0; rt < MT; ++rt) {
-                    if (rt > 0 && ntile <= rt) continue;  // row tile without rows (wave-uniform)
                     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int t = 0; t < NF; ++t)
@@ -391,7 +390,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         }
 #pragma unroll
         for (int rt = 0; rt < MT; ++rt) {
-            if (rt > 0 && ntile <= rt) continue;
             v8bf xm[NF];
 #pragma unroll
             for (int t = 0; t < NF; ++t) xm[t] = *(const v8bf *)(&sXM[buf][t][rt][lane * 16]);
@@ -994,12 +992,14 @@ __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ p
 //   * the epilogue undoes the token's scale: Y = y * 2^-sc[t].
 // Rows past the chunk repeat its last row (their outputs are not stored);
 // blocks past K read the last block (their d = m = 0).  Both row tiles are
-// multiplied even when the chunk has at most 16 rows.  With a wave-uniform
-// branch skipping the second tile's MFMAs, every chunk of <= 16 rows came out
-// wrong in the per-slot build of this kernel (measured over chunk sizes 1 to
-// 40) while the shared build of the same source was right; without the
-// branch the k loop has no branch between an MFMA and the instructions that
-// read its result, and both builds are right at every chunk size.
+// multiplied even when the chunk has at most 16 rows: no branch may sit
+// between an MFMA and the VALU instructions that read its result.  A VALU
+// read of an MFMA destination needs wait states the hardware does not
+// enforce (the compiler emits 8 for v_mfma_f32_16x16x32_f16 on straight-line
+// code), and with a wave-uniform branch skipping the second tile, the built
+// code read the first tile's accumulator one instruction after its MFMA on
+// the branch-taken path (the wait was only on the fall-through path), so
+// every chunk of <= 16 rows summed stale accumulator registers.
 template <int MT, int WAVES, int C, int MINW, bool PER_SLOT>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_moe(Q4Params p) {
     constexpr int ROWS = MT * 16, SPG = WAVES * C;
