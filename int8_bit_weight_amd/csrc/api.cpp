@@ -286,8 +286,10 @@ qmm_status int8_gemm_per_axis(const void *A, qmm_i8type at, int64_t M, int64_t K
                               const int32_t *zA_row, const void *packedB, qmm_i8type bt, int64_t N,
                               const int32_t *zB_col, const qmm_epilogue *ep, void *workspace,
                               size_t workspace_bytes, void *stream) {
-    const int32_t za = at == QMM_U8 ? 128 : 0, zb = bt == QMM_U8 ? 128 : 0;  // in range; unused with vectors
-    return gemm_call(A, at, M, K, lda, za, zA_row, packedB, bt, N, zb, zB_col, ep, workspace, workspace_bytes,
+    // a NULL vector means zero points of 0 in the caller's domain: the scalar
+    // 0 stands in for it (in range for both types; for a uint8 operand it is
+    // -128 in the shifted domain, so the correction still runs)
+    return gemm_call(A, at, M, K, lda, 0, zA_row, packedB, bt, N, 0, zB_col, ep, workspace, workspace_bytes,
                      stream, "int8_gemm_per_axis");
 }
 

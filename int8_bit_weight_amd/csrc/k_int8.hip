@@ -261,7 +261,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode(Int8GemmParams p) {
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int m = min((int)(threadIdx.x + i * NT) >> 4, p.M - 1);
-        const float v = (p.row_scale ? p.row_scale : p.col_scale)[m];
+        // without row scales the (discarded) load reads col_scale[0], which
+        // exists for any N >= 1; col_scale[m] could lie past a caller's N
+        const float v = *(p.row_scale ? p.row_scale + m : p.col_scale);
         rs[i] = p.row_scale ? v : 1.0f;
     }
 
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide(Int8GemmPa
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = min(r * 16 + 4 * (lane >> 4) + i, p.M - 1);
-            const float v = (p.row_scale ? p.row_scale : p.col_scale)[m];
+            const float v = *(p.row_scale ? p.row_scale + m : p.col_scale);
             rs[r][i] = p.row_scale ? v : 1.0f;
         }
     const int na = p.KT * MT * 64;

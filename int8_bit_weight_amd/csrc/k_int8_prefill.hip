@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     // branches.
     for (int r = tid; r < PF_BM; r += 256) {
         const int m = min(m0 + r, p.M - 1);
-        const float v = (p.row_scale ? p.row_scale : p.col_scale)[m];
+        const float v = *(p.row_scale ? p.row_scale + m : p.col_scale);
         s_rs[r] = p.row_scale ? v : 1.0f;
         s_za[r] = row_za(p, m);
     }

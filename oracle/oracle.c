@@ -130,8 +130,9 @@ void oracle_epilogue_f64(const int64_t *Y, int64_t M, int64_t N, int64_t ldy,
 
 /* [P1] "What works today": the readback folds both scales and the output
  * scale into one multiply per element, rounds half to even (ONNX), and adds
- * the output zero point after rounding, "because rounding after an integer
- * shift would move exact ties to the wrong neighbour".  [P1] "A real Quark
+ * the output zero point after rounding, so that a tie resolves on the
+ * unshifted value (adding an odd zero point first would flip which
+ * neighbour is even).  [P1] "A real Quark
  * export": an exact int32 accumulator times an fp32 multiplier can land on
  * either side of a tie from a float-accumulating reference, so this chain is
  * fixed as the definition: every step below is one fp32 operation. */

@@ -39,12 +39,13 @@ void oracle_int8_gemm_i64(const void *A, int a_u8, int64_t M, int64_t K, int64_t
                           const void *B, int b_u8, int64_t N, int64_t ldb, int32_t zB,
                           int64_t *Y, int64_t ldy);
 
-/* The same definition at `count` sampled positions (im[i], in[i]). */
 /* Per-axis zero points: zA[M] per activation row, zB[N] per weight column;
  * Y[m,n] = sum_k (A[m,k]-zA[m])(B[k,n]-zB[n]) in int64. */
 void oracle_int8_gemm_axis_i64(const void *A, int a_u8, int64_t M, int64_t K, int64_t lda, const int32_t *zA,
                                const void *B, int b_u8, int64_t N, int64_t ldb, const int32_t *zB,
                                int64_t *Y, int64_t ldy);
+
+/* The scalar-zero-point definition at `count` sampled positions (im[i], in[i]). */
 void oracle_int8_gemm_at(const void *A, int a_u8, int64_t K, int64_t lda, int32_t zA,
                          const void *B, int b_u8, int64_t ldb, int32_t zB,
                          const int64_t *im, const int64_t *in, int64_t count, int64_t *out);

@@ -296,6 +296,60 @@ def test_per_axis_pages_values_and_constant_vectors(q, orc):
     assert np.array_equal(to_np(a), orc.int8_gemm_i64(A, -40, B, -25).astype(np.int32))
 
 
+@pytest.mark.parametrize("M,K,N,variant", [(16, 1024, 1024, "int8_decode_m16"), (3, 100, 16400, "int8_decode_wide_m16"),
+                                             (300, 200, 130, "int8_prefill_256x128")])
+@pytest.mark.parametrize("null_side", ["a", "b"])
+def test_per_axis_one_null_vector_uint8(q, orc, M, K, N, variant, null_side):
+    """int8_gemm_per_axis with uint8 activations and uint8 weights where one
+    zero-point vector is NULL: NULL means zero points of 0 (not the uint8
+    midpoint 128), so the result is sum_k A (B - zB[n]) or sum_k (A - zA[m]) B,
+    checked bit for bit against the oracle with an all-zero vector."""
+    import ctypes
+    import torch
+    dev = torch_dev()
+    g = np.random.default_rng(M + K + N + (null_side == "a"))
+    A = wl.uniform_u8(g, (M, K))
+    B = wl.uniform_u8(g, (K, N))
+    zA = g.integers(0, 256, M).astype(np.int32)
+    zB = g.integers(0, 256, N).astype(np.int32)
+    if null_side == "a":
+        zA[:] = 0
+    else:
+        zB[:] = 0
+    p = q.pack_b_int8_raw(to_dev(B))
+    y32 = torch.full((M, N), -7, dtype=torch.int32, device=dev)
+    ep = q.qmm_epilogue()
+    ep.outputs = q.QMM_OUT_I32
+    ep.y_i32, ep.ld_i32 = y32.data_ptr(), y32.stride(0)
+    Ad = to_dev(A)
+    za = None if null_side == "a" else to_dev(zA)
+    zb = None if null_side == "b" else to_dev(zB)
+    st = q.lib.int8_gemm_per_axis(Ad.data_ptr(), q.QMM_U8, M, K, K, None if za is None else za.data_ptr(),
+                                  p.data.data_ptr(), q.QMM_U8, N, None if zb is None else zb.data_ptr(),
+                                  ctypes.byref(ep), None, 0, None)
+    assert st == q.QMM_OK
+    assert q.last_variant() == variant
+    assert np.array_equal(to_np(y32), orc.int8_gemm_axis_i64(A, zA, B, zB).astype(np.int32))
+
+
+@pytest.mark.parametrize("M,K,N,variant", [(20, 256, 3, "int8_decode_m32"), (300, 128, 5, "int8_prefill_256x128")])
+def test_caller_col_scale_with_more_rows_than_columns(q, orc, M, K, N, variant):
+    """M > N with a caller's col_scale of exactly N floats and no row scales:
+    the kernels read no scale past N (the row-scale fallback load stays on
+    element 0), and the fp32 output matches the oracle."""
+    import torch
+    g = np.random.default_rng(M + N)
+    A = wl.uniform_i8(g, (M, K))
+    B = wl.uniform_i8(g, (K, N))
+    cs = g.uniform(0.5, 2.0, N).astype(np.float32)
+    p = q.pack_b_int8_raw(to_dev(B))
+    yf = torch.empty((M, N), dtype=torch.float32, device=torch_dev())
+    q.int8_gemm(to_dev(A), 0, p, 0, out_f32=yf, col_scale=to_dev(cs), scale=0.01)
+    assert q.last_variant() == variant
+    Y64 = orc.int8_gemm_i64(A, 0, B, 0)
+    assert max_rel_err(to_np(yf), orc.epilogue_f64(Y64, None, cs, 0.01)) <= F32_TOL
+
+
 @pytest.mark.parametrize("M", [3, 40])
 def test_int8_max_k(q, orc, M):
     """The largest K the bound K*255*128 < 2^31 admits that is a multiple of
