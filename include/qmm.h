@@ -320,6 +320,32 @@ qmm_status q4_1_matmul_id_per_slot(const float *X, int64_t n_tokens, int64_t K, 
                                    int64_t n_used, float *Y, int64_t ldy_slot, int64_t ldy_token,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * q4_1_matmul_id_noalloc: q4_1_matmul_id for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, serving
+ * loops, harnesses that forbid allocation).  Same arguments, results (the
+ * same kernels, bit for bit), error codes and check mode as q4_1_matmul_id,
+ * without the workspace: the routing tables and split activations live in
+ * a library-owned device array of QMM_NOALLOC_SCRATCH_BYTES per GPU, created
+ * with the library's code object on each GPU it runs on and held until the
+ * process ends.  The call itself allocates nothing and never synchronises
+ * (outside check mode).
+ *   - A call whose workspace (qmm_q4_1_matmul_id_workspace_bytes) exceeds
+ *     QMM_NOALLOC_SCRATCH_BYTES returns QMM_ERR_WORKSPACE before anything
+ *     is enqueued (16 MiB covers e.g. 512 tokens x top-8 over 128 experts
+ *     at K = 2048, which needs about 4.4 MiB).
+ *   - Every call on one GPU shares that GPU's array, and nothing in it needs
+ *     to start at any value (each call writes everything it reads): calls
+ *     that overlap in time on one GPU (different streams, or different host
+ *     threads) race and may return wrong results; serialise them.
+ *   - The GPU is the one `stream` belongs to (the current device for NULL).
+ */
+#define QMM_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+qmm_status q4_1_matmul_id_noalloc(const float *X, int64_t n_tokens, int64_t K, int64_t ldx,
+                                  const void *Wexperts, int64_t n_expert, int64_t N, size_t expert_stride,
+                                  const int32_t *ids, int64_t ids_row_stride, int64_t n_used,
+                                  float *Y, int64_t ldy_slot, int64_t ldy_token, void *stream);
+
 /* ---------------------------------------------------------- measurement --- */
 
 /*

@@ -79,6 +79,8 @@ _SIGS = {
     "q4_1_matmul_id_per_slot": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _I64, _I64, _SZ, _P, _I64, _I64,
                                        _P, _I64, _I64, _P, _SZ, _P]),
     "q4_1_matmul_q8": (_INT, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
+    "q4_1_matmul_id_noalloc": (_INT, [_P, _I64, _I64, _I64, _P, _I64, _I64, _SZ, _P, _I64, _I64,
+                                      _P, _I64, _I64, _P]),
     "qmm_read_probe": (_INT, [_P, _SZ, _P, _I64, _P]),
     "qmm_set_check": (None, [_INT]),
     "qmm_check_enabled": (_INT, []),
@@ -394,6 +396,21 @@ def q4_1_matmul_id(X, experts, n_expert: int, K: int, N: int, expert_stride: int
     _check("q4_1_matmul_id", lib.q4_1_matmul_id(_ptr(X), T, K, X.stride(0), _ptr(experts), n_expert, N,
                                                 expert_stride, _ptr(ids), ids.stride(0), n_used, _ptr(Y),
                                                 Y.stride(1), Y.stride(0), _ptr(ws), wsz, _stream(stream)))
+    return Y
+
+
+def q4_1_matmul_id_noalloc(X, experts, n_expert: int, K: int, N: int, expert_stride: int, ids, n_used: int,
+                           out=None, stream=None):
+    """q4_1_matmul_id without a workspace: the library's own per-GPU scratch
+    array holds the routing tables and split activations (calls that overlap
+    on one GPU race)."""
+    torch = _torch()
+    T = X.shape[0]
+    Y = torch.empty((T, n_used, N), dtype=torch.float32, device=X.device) if out is None else out
+    _check("q4_1_matmul_id_noalloc",
+           lib.q4_1_matmul_id_noalloc(_ptr(X), T, K, X.stride(0), _ptr(experts), n_expert, N, expert_stride,
+                                      _ptr(ids), ids.stride(0), n_used, _ptr(Y), Y.stride(1), Y.stride(0),
+                                      _stream(stream)))
     return Y
 
 

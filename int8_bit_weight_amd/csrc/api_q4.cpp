@@ -4,6 +4,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "qmm.h"
 #include "q4_internal.h"
@@ -227,12 +228,54 @@ size_t qmm_q4_1_matmul_id_per_slot_workspace_bytes(int64_t n_tokens, int64_t n_u
 
 }  // extern "C"
 
+// ------------------------------------------------ allocation-free MUL_MAT_ID ---
+// q4_1_matmul_id_noalloc keeps its routing tables and split activations in
+// this library-owned array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not the device array: the device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is handed to the kernels.
+static __device__ __align__(256) uint8_t scratch[QMM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null until looked up)
+
+// The scratch array's address on the device that runs `stream`.
+hipError_t scratch_on(hipStream_t stream, void **out) {
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
 // Both MUL_MAT_ID forms: the shared one (ldx_slot = 0: token t's row for
 // every slot) and the per-slot one (a row per (token, slot) pair).
 static qmm_status moe_call(const float *X, int64_t n_tokens, int64_t K, int64_t ldx, int64_t ldx_slot,
                            bool per_slot, const void *Wexperts, int64_t n_expert, int64_t N, size_t expert_stride,
                            const int32_t *ids, int64_t ids_row_stride, int64_t n_used, float *Y, int64_t ldy_slot,
-                           int64_t ldy_token, void *workspace, size_t workspace_bytes, void *stream) {
+                           int64_t ldy_token, void *workspace, size_t workspace_bytes, void *stream,
+                           bool use_scratch = false) {
     if (n_tokens < 0 || K <= 0 || N < 0 || n_expert <= 0 || n_used <= 0 || ids_row_stride < n_used ||
         ldy_slot < N || ldy_token < n_used * ldy_slot)
         return QMM_ERR_INVALID;
@@ -247,6 +290,13 @@ static qmm_status moe_call(const float *X, int64_t n_tokens, int64_t K, int64_t 
     const Q4Layout L = q4_layout(K, N);
     if (expert_stride < (size_t)L.total || expert_stride % 256 != 0) return QMM_ERR_INVALID;
     const MoePlan pl = plan_q4_moe(n_tokens, n_used, n_expert, K, N, per_slot);
+    if (use_scratch) {
+        // the library-owned array (allocation-free entry point)
+        if (pl.ws_bytes > (int64_t)QMM_NOALLOC_SCRATCH_BYTES) return QMM_ERR_WORKSPACE;
+        const hipError_t e = scratch_on((hipStream_t)stream, &workspace);
+        if (e != hipSuccess) return record_status(e, "q4_moe_m32");
+        workspace_bytes = QMM_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < (size_t)pl.ws_bytes || !aligned_to(workspace, 256))
         return QMM_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
@@ -332,3 +382,12 @@ qmm_status q4_1_matmul_id_per_slot(const float *X, int64_t n_tokens, int64_t K, 
 }
 
 }  // extern "C"
+
+extern "C" qmm_status q4_1_matmul_id_noalloc(const float *X, int64_t n_tokens, int64_t K, int64_t ldx,
+                                             const void *Wexperts, int64_t n_expert, int64_t N,
+                                             size_t expert_stride, const int32_t *ids, int64_t ids_row_stride,
+                                             int64_t n_used, float *Y, int64_t ldy_slot, int64_t ldy_token,
+                                             void *stream) {
+    return moe_call(X, n_tokens, K, ldx, 0, false, Wexperts, n_expert, N, expert_stride, ids, ids_row_stride,
+                    n_used, Y, ldy_slot, ldy_token, nullptr, 0, stream, true);
+}

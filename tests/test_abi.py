@@ -157,3 +157,19 @@ def test_check_mode_toggle(q):
     assert q.lib.qmm_check_enabled() == 1
     q.lib.qmm_set_check(0)
     assert q.lib.qmm_check_enabled() == 0
+
+
+def test_moe_noalloc_rejections(q):
+    """The allocation-free MUL_MAT_ID checks its arguments like the workspace
+    form and refuses, before any HIP call, a problem whose scratch would not
+    fit the library's array."""
+    INV, WS = q.QMM_ERR_INVALID, q.QMM_ERR_WORKSPACE
+    f = q.lib.q4_1_matmul_id_noalloc
+    stride = (q.lib.qmm_q4_1_packed_bytes(4096, 768) + 255) // 256 * 256
+    assert q.lib.qmm_q4_1_matmul_id_workspace_bytes(512, 8, 128, 2048, 768) <= 16 << 20
+    need = q.lib.qmm_q4_1_matmul_id_workspace_bytes(8192, 8, 128, 4096, 768)
+    assert need > 16 << 20
+    assert f(FAKE, 8192, 4096, 4096, FAKE, 128, 768, stride, FAKE, 17, 8, FAKE, 768, 8 * 768, None) == WS
+    assert f(FAKE, 4, 64, 63, FAKE, 4, 32, 1 << 16, FAKE, 17, 2, FAKE, 32, 64, None) == INV     # ldx < K
+    assert f(None, 4, 64, 64, FAKE, 4, 32, 1 << 16, FAKE, 17, 2, FAKE, 32, 64, None) == INV      # no X
+    assert f(FAKE, 0, 64, 64, FAKE, 4, 32, 1 << 16, FAKE, 17, 2, FAKE, 32, 64, None) == q.QMM_OK
