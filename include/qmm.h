@@ -216,6 +216,42 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx,
                              int8_t *Xq, int64_t ldq, float *row_scale,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * int8_gemm_dynamic_grouped: int8_gemm_dynamic over several weights that
+ * read the same activations (a decoder layer's q, k and v projections, or
+ * its gate and up projections), in one launch: [P1] "What works today, and
+ * what does not": a decode-side win needs fewer, longer launches.  X (fp32
+ * M x K, ldx >= K) is quantised per row with amax/127 once per row group
+ * and multiplied with every item's weight; item i writes
+ *   items[i].y_f32[m*ld_f32 + n] = fl32(Y_i) * fl32(fl32(rs[m]*cs_i[n])*scale)
+ *                                  + bias_f32[n]          (bias 0 if NULL)
+ * with Y_i the int32 product with weight i, rs the computed row scales and
+ * cs_i the weight's packed column scales: bit for bit what int8_gemm_dynamic
+ * with an F32-only epilogue (row_scale NULL, col_scale NULL, that scale and
+ * bias) gives for each weight alone.
+ *   items     host array of n_items (1..QMM_MAX_GROUP_ITEMS) descriptors; each
+ *             packedB was written by pack_b_int8 for this K and its N; items
+ *             with N = 0 are skipped.
+ *   workspace device scratch of qmm_int8_gemm_dynamic_grouped_workspace_bytes
+ *             (M, K) bytes (0, workspace may be NULL, whenever the rows cut
+ *             into the row groups of int8_gemm_dynamic's one-launch form;
+ *             otherwise the quantised rows and their scales, the rows
+ *             quantised once and each item multiplied in a launch of its own).
+ * Errors as int8_gemm_dynamic.
+ */
+#define QMM_MAX_GROUP_ITEMS 4
+typedef struct {
+    const void *packedB;     /* device, pack_b_int8 buffer for K x N           */
+    int64_t N;
+    float *y_f32;            /* device, M x N fp32 output                      */
+    int64_t ld_f32;
+    const float *bias_f32;   /* device [N] or NULL                             */
+} qmm_dynamic_item;
+size_t qmm_int8_gemm_dynamic_grouped_workspace_bytes(int64_t M, int64_t K);
+qmm_status int8_gemm_dynamic_grouped(const float *X, int64_t M, int64_t K, int64_t ldx,
+                                     const qmm_dynamic_item *items, int64_t n_items, float scale,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------- q4_1 --- */
 
 /*
@@ -345,17 +381,6 @@ qmm_status q4_1_matmul_id_noalloc(const float *X, int64_t n_tokens, int64_t K, i
                                   const void *Wexperts, int64_t n_expert, int64_t N, size_t expert_stride,
                                   const int32_t *ids, int64_t ids_row_stride, int64_t n_used,
                                   float *Y, int64_t ldy_slot, int64_t ldy_token, void *stream);
-
-/* ---------------------------------------------------------- measurement --- */
-
-/*
- * qmm_read_probe: a plain streaming read of `bytes` (a multiple of 16, buf
- * 16-byte aligned) with 16-byte loads over `workgroups` workgroups of 256
- * threads, each writing one int32 to sink[workgroup] so the loads stay.  It
- * computes nothing: the floor a bandwidth-bound call of the same size is
- * compared against (timing only; not part of any product path).
- */
-qmm_status qmm_read_probe(const void *buf, size_t bytes, int32_t *sink, int64_t workgroups, void *stream);
 
 /* ------------------------------------------------------------- helpers --- */
 

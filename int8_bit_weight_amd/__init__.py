@@ -55,6 +55,10 @@ class qmm_epilogue(ctypes.Structure):
     ]
 
 
+class qmm_dynamic_item(ctypes.Structure):
+    _fields_ = [("packedB", _P), ("N", _I64), ("y_f32", _P), ("ld_f32", _I64), ("bias_f32", _P)]
+
+
 _SIGS = {
     "qmm_pack_b_int8_bytes": (_SZ, [_I64, _I64]),
     "pack_b_int8": (_INT, [_P, _I64, _I64, _I64, _P, _SZ, _P]),
@@ -68,6 +72,9 @@ _SIGS = {
     "qmm_int8_gemm_dynamic_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "int8_gemm_dynamic": (_INT, [_P, _I64, _I64, _I64, _P, _I64, ctypes.POINTER(qmm_epilogue), _P, _I64, _P,
                                  _P, _SZ, _P]),
+    "qmm_int8_gemm_dynamic_grouped_workspace_bytes": (_SZ, [_I64, _I64]),
+    "int8_gemm_dynamic_grouped": (_INT, [_P, _I64, _I64, _I64, ctypes.POINTER(qmm_dynamic_item), _I64,
+                                         ctypes.c_float, _P, _SZ, _P]),
     "qmm_q4_1_packed_bytes": (_SZ, [_I64, _I64]),
     "q4_1_repack": (_INT, [_P, _I64, _I64, _P, _SZ, _P]),
     "qmm_q4_1_matmul_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -81,7 +88,6 @@ _SIGS = {
     "q4_1_matmul_q8": (_INT, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "q4_1_matmul_id_noalloc": (_INT, [_P, _I64, _I64, _I64, _P, _I64, _I64, _SZ, _P, _I64, _I64,
                                       _P, _I64, _I64, _P]),
-    "qmm_read_probe": (_INT, [_P, _SZ, _P, _I64, _P]),
     "qmm_set_check": (None, [_INT]),
     "qmm_check_enabled": (_INT, []),
     "qmm_status_string": (ctypes.c_char_p, [_INT]),
@@ -270,6 +276,35 @@ def int8_gemm(A, zA: int, packedB: PackedInt8, zB: int = 0, *, out_i32=None, out
     return out_i32, out_f32, out_q8
 
 
+def int8_gemm_dynamic_grouped(X, packed, outs=None, biases=None, scale: float = 1.0, ws=None, stream=None):
+    """int8_gemm_dynamic over several packed weights that share the fp32
+    activations X [M, K] (q/k/v, gate/up), in one launch; fp32 outputs with
+    optional per-item biases.  Returns the list of outputs."""
+    torch = _torch()
+    M, K = X.shape
+    n = len(packed)
+    if outs is None:
+        outs = [torch.empty((M, pk.N), dtype=torch.float32, device=X.device) for pk in packed]
+    biases = biases or [None] * n
+    items = (qmm_dynamic_item * n)()
+    for i, (pk, Y, b) in enumerate(zip(packed, outs, biases)):
+        if pk.K != K:
+            raise ValueError("item %d has K=%d, X has K=%d" % (i, pk.K, K))
+        items[i].packedB = pk.data.data_ptr()
+        items[i].N = pk.N
+        items[i].y_f32 = Y.data_ptr()
+        items[i].ld_f32 = Y.stride(0)
+        items[i].bias_f32 = None if b is None else b.data_ptr()
+    need = lib.qmm_int8_gemm_dynamic_grouped_workspace_bytes(M, K)
+    if ws is None and need > 0:
+        ws = workspace(need, X.device)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("int8_gemm_dynamic_grouped",
+           lib.int8_gemm_dynamic_grouped(_ptr(X), M, K, X.stride(0), items, n, float(scale), _ptr(ws), wsz,
+                                         _stream(stream)))
+    return outs
+
+
 def _epilogue(out_i32, out_f32, out_q8, q8_unsigned, row_scale, col_scale, scale, bias_f32, bias_i32, zp_out):
     ep = qmm_epilogue()
     outs = 0
@@ -374,12 +409,6 @@ def q4_1_matmul_q8(Xq, row_scale, W: PackedQ4, out=None, stream=None):
     _check("q4_1_matmul_q8", lib.q4_1_matmul_q8(_ptr(Xq), _ptr(row_scale), M, K, Xq.stride(0), _ptr(W.data), W.N,
                                                 _ptr(Y), Y.stride(0), _stream(stream)))
     return Y
-
-
-def read_probe(buf, sink, workgroups: int, stream=None):
-    """Streaming read of a device byte buffer (measurement floor; see qmm_read_probe)."""
-    _check("qmm_read_probe", lib.qmm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
-                                                int(workgroups), _stream(stream)))
 
 
 def q4_1_matmul_id(X, experts, n_expert: int, K: int, N: int, expert_stride: int, ids, n_used: int, out=None,

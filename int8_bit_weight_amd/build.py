@@ -1,10 +1,12 @@
-"""Build libqmm.so (HIP, gfx950) in-tree with hipcc.
+"""Build libqmm.so and libqmm_probe.so (HIP, gfx950) in-tree with hipcc.
 
     python int8_bit_weight_amd/build.py
 
 Every source under csrc/ is compiled for gfx950 only, with packed fp32
 instructions disabled and MFMA accumulators in VGPRs, then linked into
-int8_bit_weight_amd/libqmm.so.
+int8_bit_weight_amd/libqmm.so (the product library, include/qmm.h).  The
+streaming-read probe under probe/ becomes int8_bit_weight_amd/libqmm_probe.so
+(a measurement tool, include/qmm_probe.h).
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqmm.so")
+PROBE_SRC = os.path.join(HERE, "probe")
+PROBE_LIB = os.path.join(HERE, "libqmm_probe.so")
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -44,20 +48,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = ["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("link failed")
-    os.replace(tmp, LIB)
+        raise RuntimeError("link failed: %s" % lib)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    psrcs = sorted(glob.glob(os.path.join(PROBE_SRC, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
+        objs = list(ex.map(_compile, srcs + psrcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
         print(LIB)
+        print(PROBE_LIB)
     return LIB
 
 

@@ -390,4 +390,97 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
     return st;
 }
 
+static_assert(QMM_MAX_GROUP_ITEMS == kMaxGroups, "one grouped launch holds every item");
+
+size_t qmm_int8_gemm_dynamic_grouped_workspace_bytes(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0 || dynamic_groups(M, K) > 0) return 0;
+    return (size_t)(round_up(M * K, 256) + round_up(4 * M, 256));
+}
+
+qmm_status int8_gemm_dynamic_grouped(const float *X, int64_t M, int64_t K, int64_t ldx,
+                                     const qmm_dynamic_item *items, int64_t n_items, float scale,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+    if (M < 0 || K <= 0 || ldx < K || !items || n_items < 1 || n_items > QMM_MAX_GROUP_ITEMS)
+        return QMM_ERR_INVALID;
+    for (int64_t i = 0; i < n_items; ++i)
+        if (items[i].N < 0 || items[i].ld_f32 < items[i].N) return QMM_ERR_INVALID;
+    if (!k_in_bound(K) || M > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+    int64_t total_ns = 0;
+    for (int64_t i = 0; i < n_items; ++i) {
+        if (items[i].N > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+        total_ns += packed_b_layout(K, items[i].N).NS;
+    }
+    if (total_ns > INT32_MAX / 2) return QMM_ERR_UNSUPPORTED;
+    if (M == 0) return QMM_OK;
+    if (!X || !aligned(X, 4)) return QMM_ERR_INVALID;
+    for (int64_t i = 0; i < n_items; ++i) {
+        if (items[i].N == 0) continue;
+        const qmm_dynamic_item &it = items[i];
+        if (!it.packedB || !aligned(it.packedB, 256) || !it.y_f32 || !aligned(it.y_f32, 4) ||
+            (it.bias_f32 && !aligned(it.bias_f32, 4)))
+            return QMM_ERR_INVALID;
+        if (g_check && qmm_packed_b_check(it.packedB, K, it.N, stream) != QMM_OK) return QMM_ERR_INVALID;
+    }
+    const int G = dynamic_groups(M, K);
+    if (G == 0) {
+        // not fusable: quantise once, then one product per item
+        const size_t need = qmm_int8_gemm_dynamic_grouped_workspace_bytes(M, K);
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return QMM_ERR_WORKSPACE;
+        int8_t *q = (int8_t *)workspace;
+        float *rs = (float *)((int8_t *)workspace + round_up(M * K, 256));
+        qmm_status st = quantize_rows_int8(X, M, K, ldx, q, K, rs, stream);
+        for (int64_t i = 0; i < n_items && st == QMM_OK; ++i) {
+            if (items[i].N == 0) continue;
+            qmm_epilogue e{};
+            e.outputs = QMM_OUT_F32;
+            e.y_f32 = items[i].y_f32;
+            e.ld_f32 = items[i].ld_f32;
+            e.row_scale = rs;
+            e.scale = scale;
+            e.bias_f32 = items[i].bias_f32;
+            st = int8_gemm(q, QMM_S8, M, K, K, 0, items[i].packedB, QMM_S8, items[i].N, 0, &e, nullptr, 0, stream);
+        }
+        return st;
+    }
+    // one fused launch over the items' strips, row groups as in int8_gemm_dynamic
+    DecodeGroups dg{};
+    for (int i = 0; i < kMaxGroups; ++i) dg.strip_begin[i] = INT32_MAX;
+    int n = 0, sb = 0;
+    for (int64_t i = 0; i < n_items; ++i) {
+        if (items[i].N == 0) continue;
+        const PackedBLayout L = packed_b_layout(K, items[i].N);
+        const int8_t *base = (const int8_t *)items[i].packedB;
+        dg.codes[n] = base + L.codes_off;
+        dg.colsum[n] = (const int32_t *)(base + L.colsum_off);
+        dg.col_scale[n] = (const float *)(base + L.scale_off);
+        dg.y_f32[n] = items[i].y_f32;
+        dg.ld_f32[n] = items[i].ld_f32;
+        dg.bias_f32[n] = items[i].bias_f32;
+        dg.N[n] = (int)items[i].N;
+        dg.strip_begin[n] = sb;
+        sb += (int)L.NS;
+        ++n;
+    }
+    if (n == 0) return QMM_OK;
+    const int64_t rows = dynamic_rows(M, K);
+    const Int8Plan plan = plan_int8_gemm(rows, K, 16, false);
+    Int8GemmParams p{};
+    qmm_epilogue e0{};
+    e0.outputs = QMM_OUT_F32;
+    e0.y_f32 = dg.y_f32[0];
+    e0.ld_f32 = dg.ld_f32[0];
+    e0.scale = scale;
+    fill_params(p, M, K, dg.N[0], (const int8_t *)dg.codes[0] - kHeaderBytes, &e0);
+    p.NS = sb;  // the grid: every item's strips
+    p.X = X;
+    p.ldx = ldx;
+    p.x_vec = aligned(X, 16) && (ldx % 4 == 0);
+    p.rpg = rows < M ? (int)rows : 0;
+    const char *variant = "";
+    const qmm_status st = hip_status(launch_int8_gemm_dynamic_grouped(plan, p, dg, (hipStream_t)stream, &variant));
+    g_last_variant = variant;
+    trace_gemm("int8_gemm_dynamic_grouped", variant, M, K, sb * 16, plan);
+    return st;
+}
+
 }  // extern "C"

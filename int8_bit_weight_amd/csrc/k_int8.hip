@@ -416,8 +416,31 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide(Int8GemmPa
 // order (one 16-row tile per 16 rows); then the LDS sum over the waves and
 // the epilogue.  Every workgroup quantises all M x K activations again,
 // which is why the planner keeps M*K small here.
-template <int E, int TPW, bool AVEC>
-__global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p) {
+// GROUPED: the grid's strips are those of up to kMaxGroups weights that
+// share the activations, back to back; each workgroup takes its item's
+// weight, width and epilogue operands from `g` and works on the item's own
+// strip index (every item is the same computation as a call of its own).
+struct NoGroups {};
+template <bool GROUPED>
+using GroupArg = std::conditional_t<GROUPED, DecodeGroups, NoGroups>;
+
+template <int E, int TPW, bool AVEC, bool GROUPED>
+__global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupArg<GROUPED> g) {
+    int strip = blockIdx.x;
+    bool first_item = true;  // writes the optional quantised rows and scales
+    if constexpr (GROUPED) {
+        const int it = (strip >= g.strip_begin[1]) + (strip >= g.strip_begin[2]) + (strip >= g.strip_begin[3]);
+        strip -= g.strip_begin[it];
+        first_item = it == 0;
+        p.codes = g.codes[it];
+        p.colsum = g.colsum[it];
+        p.col_scale = g.col_scale[it];
+        p.y_f32 = g.y_f32[it];
+        p.ld_f32 = g.ld_f32[it];
+        p.bias_f32 = g.bias_f32[it];
+        p.N = g.N[it];
+        p.NS = (p.N + kTileN - 1) / kTileN;
+    }
     if (p.rpg > 0) {
         // row group blockIdx.y: rows [y rpg, y rpg + rpg) of the call, quantised
         // and multiplied on their own (the weights are read once per group)
@@ -438,7 +461,6 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p) {
     static_assert(E == 1 || E == 2 || E == 4 || E == 8 || E == 16 || E == 32, "E is a power of two <= 32");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int strip = blockIdx.x;
     const int m = lane / L;                    // row of this lane's values
     const int kl = (lane % L) * E;             // their first k within a tile
     const bool row_ok = m < p.M;
@@ -498,7 +520,7 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p) {
     const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
     if (wave == 0 && lane % L == 0) {
         s_scale[m] = s;
-        if (p.rs_out && strip == 0 && row_ok) p.rs_out[m] = s;
+        if (p.rs_out && strip == 0 && first_item && row_ok) p.rs_out[m] = s;
     }
     const float y = 1.0f / s;
     const bool fast_s = s >= 0x1p-100f && s <= 0x1p100f;
@@ -541,7 +563,7 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p) {
                 *(v4i *)(qdst + 16 * i) = v4i{(int)w[4 * i], (int)w[4 * i + 1], (int)w[4 * i + 2], (int)w[4 * i + 3]};
         }
         const int k0 = (wave + t * WAVES) * kTileK + kl;
-        if (p.xq_out && strip == 0 && row_ok && k0 < p.K) {
+        if (p.xq_out && strip == 0 && first_item && row_ok && k0 < p.K) {
             int8_t *dst = p.xq_out + (int64_t)m * p.ldq + k0;
             for (int j = 0; j < E && k0 + j < p.K; ++j) dst[j] = (int8_t)(w[j >> 2] >> (8 * (j & 3)));
         }
@@ -672,43 +694,56 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
     return launch_int8_prefill(p, s);
 }
 
-template <int E, int TPW>
-hipError_t launch_dyn(const Int8GemmParams &p, bool avec, hipStream_t s) {
+template <int E, int TPW, bool GROUPED>
+hipError_t launch_dyn(const Int8GemmParams &p, const DecodeGroups &dg, bool avec, hipStream_t s) {
     const unsigned groups = p.rpg > 0 ? (unsigned)((p.M + p.rpg - 1) / p.rpg) : 1u;
     const dim3 g((unsigned)p.NS, groups), b(1024);
+    GroupArg<GROUPED> ga{};
+    if constexpr (GROUPED) ga = dg;
     if (E >= 4 && avec)
-        hipLaunchKernelGGL((k_int8_decode_q<E, TPW, true>), g, b, 0, s, p);
+        hipLaunchKernelGGL((k_int8_decode_q<E, TPW, true, GROUPED>), g, b, 0, s, p, ga);
     else
-        hipLaunchKernelGGL((k_int8_decode_q<E, TPW, false>), g, b, 0, s, p);
+        hipLaunchKernelGGL((k_int8_decode_q<E, TPW, false, GROUPED>), g, b, 0, s, p, ga);
     return hipGetLastError();
 }
 
 // E * K <= 16384 (the planner's bound) keeps E * TPW <= 16.
-template <int E>
-hipError_t launch_dyn_tpw(const Int8GemmParams &p, bool avec, hipStream_t s) {
-    if (p.KT <= 16) return launch_dyn<E, 1>(p, avec, s);
+template <int E, bool GROUPED>
+hipError_t launch_dyn_tpw(const Int8GemmParams &p, const DecodeGroups &dg, bool avec, hipStream_t s) {
+    if (p.KT <= 16) return launch_dyn<E, 1, GROUPED>(p, dg, avec, s);
     if constexpr (E <= 8) {
-        if (p.KT <= 32) return launch_dyn<E, 2>(p, avec, s);
+        if (p.KT <= 32) return launch_dyn<E, 2, GROUPED>(p, dg, avec, s);
     }
     if constexpr (E <= 4) {
-        if (p.KT <= 64) return launch_dyn<E, 4>(p, avec, s);
+        if (p.KT <= 64) return launch_dyn<E, 4, GROUPED>(p, dg, avec, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
-                                    const char **variant) {
+template <bool GROUPED>
+hipError_t launch_dyn_rows(const Int8Plan &plan, const Int8GemmParams &p, const DecodeGroups &dg, hipStream_t s) {
     const int rows = p.rpg > 0 ? p.rpg : p.M;  // rows one workgroup quantises
     if (plan.variant != 0 || rows > 16 || p.KT > 64 || p.zBs != 0 || p.zb_col || p.za_row)
         return hipErrorInvalidValue;
-    *variant = p.rpg > 0 ? "int8_dynamic_groups" : "int8_dynamic_m16";
     const bool v = p.x_vec && (p.K % 16) == 0;
     // E: values per lane, the rows rounded up to a power of two
-    if (rows <= 1) return launch_dyn_tpw<1>(p, v, s);
-    if (rows <= 2) return launch_dyn_tpw<2>(p, v, s);
-    if (rows <= 4) return launch_dyn_tpw<4>(p, v, s);
-    if (rows <= 8) return launch_dyn_tpw<8>(p, v, s);
-    return launch_dyn_tpw<16>(p, v, s);
+    if (rows <= 1) return launch_dyn_tpw<1, GROUPED>(p, dg, v, s);
+    if (rows <= 2) return launch_dyn_tpw<2, GROUPED>(p, dg, v, s);
+    if (rows <= 4) return launch_dyn_tpw<4, GROUPED>(p, dg, v, s);
+    if (rows <= 8) return launch_dyn_tpw<8, GROUPED>(p, dg, v, s);
+    return launch_dyn_tpw<16, GROUPED>(p, dg, v, s);
+}
+
+hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
+                                    const char **variant) {
+    *variant = p.rpg > 0 ? "int8_dynamic_groups" : "int8_dynamic_m16";
+    return launch_dyn_rows<false>(plan, p, DecodeGroups{}, s);
+}
+
+hipError_t launch_int8_gemm_dynamic_grouped(const Int8Plan &plan, Int8GemmParams p, const DecodeGroups &g,
+                                            hipStream_t s, const char **variant) {
+    *variant = "int8_dynamic_grouped";
+    return launch_dyn_rows<true>(plan, p, g, s);
 }
 
 }  // namespace qmm

@@ -115,6 +115,22 @@ struct Int8GemmParams {
     int rpg;               // > 0: rows per row group (blockIdx.y), each group an independent call
 };
 
+// Grouped fused decode: up to kMaxGroups weights that share the activations
+// (one launch; the grid's strips are the items' strips back to back).  A
+// second kernel argument, so the single-weight launches keep their
+// argument size.
+constexpr int kMaxGroups = 4;
+struct DecodeGroups {
+    const int8_t *codes[kMaxGroups];
+    const int32_t *colsum[kMaxGroups];
+    const float *col_scale[kMaxGroups];
+    float *y_f32[kMaxGroups];
+    const float *bias_f32[kMaxGroups];
+    int64_t ld_f32[kMaxGroups];
+    int strip_begin[kMaxGroups];  // first grid strip of each item; unused items: INT32_MAX
+    int N[kMaxGroups];
+};
+
 // The wide decode (one wavefront per strip over the whole k range) stages
 // all of A' in LDS: at most this many 1 KiB operand tiles (k tiles x 16-row
 // tiles), 64 KiB.  It is planned from this many 16-column strips on.
@@ -147,5 +163,9 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
                             const char **variant);
 hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                                     const char **variant);
+// grouped form: p.NS is the total strip count of the items; p's per-weight
+// fields are ignored (taken from g)
+hipError_t launch_int8_gemm_dynamic_grouped(const Int8Plan &plan, Int8GemmParams p, const DecodeGroups &g,
+                                            hipStream_t s, const char **variant);
 
 }  // namespace qmm

@@ -63,6 +63,7 @@ def _load():
                                          _I64]),
         "oracle_q4_1_matmul_id_at": (_INT, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _P, _I64, _P]),
         "oracle_num_threads": (_INT, []),
+        "oracle_set_num_threads": (None, [_INT]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -89,6 +90,11 @@ def _i8kind(a: np.ndarray) -> int:
 
 def num_threads() -> int:
     return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's OpenMP loops use (timing only)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def int8_bound_ok(K: int) -> bool:

@@ -30,6 +30,16 @@
 #include <omp.h>
 #endif
 
+/* Threads the OpenMP loops use from now on (timing only; results do not
+ * depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

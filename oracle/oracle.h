@@ -112,6 +112,7 @@ int oracle_q4_1_matmul_id_at(const float *X, int64_t K, int64_t ldx, int64_t ldx
 
 /* Number of OpenMP threads the oracle runs with. */
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

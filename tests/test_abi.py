@@ -11,8 +11,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "qmm.h")).read()
+def _declared_functions(header="qmm.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, re.M)
     return sorted(set(n for n in names if n not in ("if", "while")))
@@ -34,6 +34,19 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(q):
     for n in _declared_functions():
         assert hasattr(q.lib, n), n
+
+
+def test_probe_library_is_separate(q):
+    """The measurement probe lives in libqmm_probe.so (include/qmm_probe.h),
+    not in the product library."""
+    from int8_bit_weight_amd import probe
+    assert _declared_functions("qmm_probe.h") == ["qmm_read_probe"]
+    assert hasattr(probe.lib, "qmm_read_probe")
+    assert not hasattr(q.lib, "qmm_read_probe")
+    # rejected before any HIP call: misaligned size, bad unroll
+    assert probe.lib.qmm_read_probe(FAKE, 17, FAKE, 1, 4, None) == 1
+    assert probe.lib.qmm_read_probe(FAKE, 16, FAKE, 1, 3, None) == 1
+    assert probe.lib.qmm_read_probe(FAKE, 0, FAKE, 1, 4, None) == 0
 
 
 def test_status_strings(q):
@@ -173,3 +186,29 @@ def test_moe_noalloc_rejections(q):
     assert f(FAKE, 4, 64, 63, FAKE, 4, 32, 1 << 16, FAKE, 17, 2, FAKE, 32, 64, None) == INV     # ldx < K
     assert f(None, 4, 64, 64, FAKE, 4, 32, 1 << 16, FAKE, 17, 2, FAKE, 32, 64, None) == INV      # no X
     assert f(FAKE, 0, 64, 64, FAKE, 4, 32, 1 << 16, FAKE, 17, 2, FAKE, 32, 64, None) == q.QMM_OK
+
+
+def test_dynamic_grouped_rejections(q):
+    """The grouped dynamic call checks every item before anything runs."""
+    INV = q.QMM_ERR_INVALID
+    f = q.lib.int8_gemm_dynamic_grouped
+
+    def items(*spec):
+        arr = (q.qmm_dynamic_item * len(spec))()
+        for i, (pk, n, y, ld) in enumerate(spec):
+            arr[i].packedB, arr[i].N, arr[i].y_f32, arr[i].ld_f32, arr[i].bias_f32 = pk, n, y, ld, None
+        return arr
+    ok = items((4096, 64, 4096, 64), (4096, 32, 4096, 32))
+    assert f(FAKE, 4, 64, 63, ok, 2, 1.0, None, 0, None) == INV                    # ldx < K
+    assert f(FAKE, 4, 64, 64, ok, 0, 1.0, None, 0, None) == INV                    # no items
+    assert f(FAKE, 4, 64, 64, items(*[(4096, 16, 4096, 16)] * 5), 5, 1.0, None, 0, None) == INV  # > 4 items
+    assert f(FAKE, 4, 64, 64, items((4096, 64, 4096, 63)), 1, 1.0, None, 0, None) == INV     # ld < N
+    assert f(FAKE, 4, 64, 64, items((4096 + 16, 64, 4096, 64)), 1, 1.0, None, 0, None) == INV  # alignment
+    assert f(FAKE, 4, 64, 64, items((4096, 64, None, 64)), 1, 1.0, None, 0, None) == INV     # no output
+    assert f(None, 4, 64, 64, ok, 2, 1.0, None, 0, None) == INV
+    assert f(FAKE, 0, 64, 64, ok, 2, 1.0, None, 0, None) == q.QMM_OK
+    assert f(FAKE, 4, 65794, 65794, ok, 2, 1.0, None, 0, None) == q.QMM_ERR_UNSUPPORTED   # the K bound
+    assert q.lib.qmm_int8_gemm_dynamic_grouped_workspace_bytes(16, 1024) == 0
+    assert q.lib.qmm_int8_gemm_dynamic_grouped_workspace_bytes(40, 1024) == 0    # eight row groups
+    assert q.lib.qmm_int8_gemm_dynamic_grouped_workspace_bytes(200, 256) > 0
+    assert q.lib.qmm_int8_gemm_dynamic_grouped_workspace_bytes(4, 5120) > 0

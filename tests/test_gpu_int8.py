@@ -623,3 +623,42 @@ def test_packed_header_check_and_check_mode(q):
 def _np_product(A, B):
     """numpy int64 product of a device int8 A and a host int8 B (zero points 0)."""
     return (to_np(A).astype(np.int64) @ B.astype(np.int64)).astype(np.int32)
+
+
+# ------------------------------------------------ grouped dynamic decode ---
+
+@pytest.mark.parametrize("M,K,Ns,variant", [
+    (1, 1024, (2048, 1024, 1024), "int8_dynamic_grouped"),     # q, k, v
+    (16, 1024, (3072, 3072), "int8_dynamic_grouped"),          # gate, up (two row groups)
+    (32, 1024, (2048, 1024, 1024), "int8_dynamic_grouped"),    # four row groups
+    (5, 96, (17, 300, 1, 40), "int8_dynamic_grouped"),         # ragged K and N, four items
+    (32, 3072, (1024, 16), "int8_dynamic_grouped"),            # eight row groups
+    (40, 1024, (2048, 1024), "int8_dynamic_grouped"),          # eight row groups of 5 rows
+    (4, 5120, (1024, 48), "int8_decode_m16"),                  # K > 4096: quantise once, then a product each
+    (200, 256, (2048, 1024), "int8_prefill_256x128"),          # too many rows: the same two-step form
+])
+def test_dynamic_grouped_matches_separate_calls(q, orc, M, K, Ns, variant):
+    """One grouped launch over weights that share the activations gives, bit
+    for bit, the fp32 output of one int8_gemm_dynamic call per weight (with
+    and without bias, strided outputs), and the oracle's product of the
+    quantised rows and weights."""
+    import torch
+    dev = torch_dev()
+    g = np.random.default_rng(M * 7 + K + sum(Ns))
+    X = wl.normal_f32(g, (M, K))
+    Ws = [wl.normal_f32(g, (K, n), 0.02) for n in Ns]
+    pks = [q.pack_b_int8(to_dev(W)) for W in Ws]
+    biases = [to_dev(wl.normal_f32(g, (n,))) if i % 2 == 1 else None for i, n in enumerate(Ns)]
+    Xd = to_dev(X)
+    outs = [torch.full((M, n + 3), float("nan"), dtype=torch.float32, device=dev)[:, :n] for n in Ns]
+    q.int8_gemm_dynamic_grouped(Xd, pks, outs=outs, biases=biases, scale=0.5)
+    assert q.last_variant() == variant
+    Qa, sa = orc.quantize_rows_int8(X)
+    for W, pk, b, Y in zip(Ws, pks, biases, outs):
+        n = pk.N
+        ref = torch.empty((M, n), dtype=torch.float32, device=dev)
+        q.int8_gemm_dynamic(Xd, pk, out_f32=ref, bias_f32=b, scale=0.5)
+        assert np.array_equal(to_np(Y).view(np.uint32), to_np(ref).view(np.uint32))
+        Qb, sb, _ = orc.pack_b_int8(W)
+        want = orc.epilogue_f64(orc.int8_gemm_i64(Qa, 0, Qb, 0), sa, sb, 0.5, None if b is None else to_np(b))
+        assert max_rel_err(to_np(Y), want) <= F32_TOL

@@ -1,6 +1,7 @@
 """The streaming-read probe the bandwidth floors are measured with: every
 16-byte chunk is read exactly once (each workgroup's XOR of its chunks
-matches the host's), including a ragged last pass of the grid-stride loop."""
+matches the host's), for 1 to 8 loads in flight per lane, including ragged
+last blocks and workgroups without a block."""
 import numpy as np
 import pytest
 
@@ -9,17 +10,18 @@ from gpu_util import to_dev, to_np, torch_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("nbytes,wg", [(16, 1), (4096 * 16 + 48, 7), (2301952, 1024)])
-def test_read_probe_reads_every_chunk_once(nbytes, wg):
+@pytest.mark.parametrize("nbytes,wg", [(16, 1), (4096 * 16 + 48, 7), (2301952, 1024), (131072, 300)])
+@pytest.mark.parametrize("u", [1, 2, 4, 8])
+def test_read_probe_reads_every_chunk_once(nbytes, wg, u):
     import torch
-    import int8_bit_weight_amd as q
-    g = np.random.default_rng(nbytes + wg)
+    from int8_bit_weight_amd.probe import read_probe
+    g = np.random.default_rng(nbytes + wg + u)
     host = g.integers(0, 256, nbytes, dtype=np.int64).astype(np.uint8)
     sink = torch.full((wg,), 7, dtype=torch.int32, device=torch_dev())
-    q.read_probe(to_dev(host), sink, wg)
+    read_probe(to_dev(host), sink, wg, loads_per_lane=u)
     c = host.view(np.int32).reshape(-1, 4)
     c = c[:, 0] ^ c[:, 1] ^ c[:, 2] ^ c[:, 3]
-    w = (np.arange(c.size) % (wg * 256)) // 256
+    w = (np.arange(c.size) // (256 * u)) % wg        # block -> workgroup
     want = np.zeros(wg, dtype=np.int32)
     for i in range(wg):
         want[i] = np.bitwise_xor.reduce(c[w == i]) if (w == i).any() else 0
