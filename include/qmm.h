@@ -31,9 +31,19 @@
  *     shape it has no kernel for: [P1] "What the graph gives us").
  *   - Results do not depend on the launch configuration: integer outputs are
  *     exact, and floating-point outputs are bitwise reproducible run to run.
- *   - The library keeps no state between calls and allocates no device
- *     memory; calls on different streams may run concurrently as long as they
- *     do not share an output or a workspace.
+ *   - No call allocates device memory (the one device array the library
+ *     owns, q4_1_matmul_id_noalloc's scratch, is part of its code object and
+ *     placed by the HIP runtime when it loads the kernels on a GPU).  Results depend
+ *     only on the arguments: the only state kept between calls is the
+ *     process-wide check-mode flag (qmm_set_check), the per-thread
+ *     diagnostics (qmm_last_hip_error, qmm_last_variant) and, for
+ *     q4_1_matmul_id_noalloc, one library-owned scratch array per GPU.
+ *   - Calls on different streams may run concurrently as long as they do not
+ *     share an output or a workspace (and, for q4_1_matmul_id_noalloc, not
+ *     on the same GPU).
+ *   - Workspaces are scratch: no initial contents are needed, every call
+ *     writes what it reads, and a workspace may be reused by any later call
+ *     on the same stream.
  */
 #ifndef QMM_H
 #define QMM_H
@@ -162,7 +172,7 @@ size_t qmm_int8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
  *   bt       element type the packed weight was given in (QMM_S8 for
  *            pack_b_int8); zB is in that type's range.
  *   workspace  device scratch of qmm_int8_gemm_workspace_bytes(M,K,N) bytes
- *            (256-byte aligned, zero-filled before its first use); NULL when
+ *            (256-byte aligned, any contents); NULL when
  *            that size is 0, which it is for every current kernel variant.
  * K must satisfy K*255*128 < 2^31 ([P2]: the sums cannot overflow below that
  * bound), else QMM_ERR_UNSUPPORTED.  M = 0 or N = 0 is a no-op.
@@ -284,8 +294,8 @@ size_t qmm_q4_1_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * ldx >= K), the weight in the layout written by q4_1_repack, Y fp32 (M x N,
  * ldy >= N).  Codes are decoded inside the kernel and kept exact; the
  * relative Frobenius error against exact arithmetic is below 1e-5.
- * workspace: device, >= qmm_q4_1_matmul_workspace_bytes(M,K,N), zero-filled
- * before its first use (same counter-region rule as int8_gemm).  That size is
+ * workspace: device, >= qmm_q4_1_matmul_workspace_bytes(M,K,N), 256-byte
+ * aligned, any contents (the k-split partial sums).  That size is
  * 0 for M <= 4 (one launch, no partial sums), where workspace may be NULL.
  */
 qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx,
@@ -324,8 +334,8 @@ size_t qmm_q4_1_matmul_id_workspace_bytes(int64_t n_tokens, int64_t n_used, int6
  *             id must lie in [0, n_expert) (a precondition: pairs with other
  *             ids are skipped, and reported in check mode, qmm_set_check)
  * Tokens routed to each expert are grouped on the device (counting sort) and
- * run in one grouped launch.  workspace: zero-filled before its first use
- * (same counter-region rule as int8_gemm).
+ * run in one grouped launch.  workspace: >= qmm_q4_1_matmul_id_workspace_bytes,
+ * 256-byte aligned, any contents (routing tables and split activations).
  */
 qmm_status q4_1_matmul_id(const float *X, int64_t n_tokens, int64_t K, int64_t ldx,
                           const void *Wexperts, int64_t n_expert, int64_t N, size_t expert_stride,
