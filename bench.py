@@ -44,10 +44,13 @@ DECODE_KERNEL = "k_int8_decode_q"
 PROBE_BYTES = 1 << 30
 
 # HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
-# (FETCH_SIZE, then WRITE_SIZE) of `bench.py --probe --no-cpu-baseline`, each
-# scaled by what the counter reads for the probe's plain read of 1 GiB in the
-# same run.  Valid only for the kernel sources it was taken on.
-MEASURED_TRAFFIC = {"sources_sha1": None, "bytes_per_launch": None}
+# of `bench.py --probe` (FETCH_SIZE, then WRITE_SIZE; mean over the step's 336
+# decode launches): FETCH_SIZE x 2.0, the factor the probe's plain read of
+# 1 GiB gives in the same run (524306 KiB), plus WRITE_SIZE x 1.0, the factor
+# the 1 GiB fill of the probe buffer gives (1048576 KiB).  Valid only for the
+# kernel sources it was taken on.
+MEASURED_TRAFFIC = {"sources_sha1": "3233edc8bf65b59f20cad6c4e60ed15091d1e6a5",
+                    "bytes_per_launch": round((2454.5 * 2.0 + 196.0) * 1024)}
 
 
 def decode_sources_sha1():
@@ -81,9 +84,14 @@ def parse_args():
                     help="counter probe: one plain read of 1 GiB (the calibration read), then one eager step")
     ap.add_argument("--profile", action="store_true",
                     help="the timed leg alone (setup, graph capture, warm-up and timed replays)")
+    ap.add_argument("--profile-leg", choices=("decode", "prefill"), default="decode",
+                    help="--profile: the decode step (default) or the M = 2048 prefill shapes, each warmed up "
+                         "and then launched --steps times in a row")
     ap.add_argument("--summarize", metavar="DB", help="summarize a rocprofv3 database (no GPU needed)")
     ap.add_argument("--kernel", default="", help="--summarize: kernel name substring")
     ap.add_argument("--last", type=int, default=0, help="--summarize: only the last N matching dispatches")
+    ap.add_argument("--skip", type=int, default=0, help="--summarize: leave out the first N matching dispatches")
+    ap.add_argument("--count", type=int, default=0, help="--summarize: then keep only the next N")
     return ap.parse_args()
 
 
@@ -175,20 +183,24 @@ def cpu_model():
 
 # ------------------------------------------------------------ summarize ---
 
-def summarize(path, pattern, last):
+def summarize(path, pattern, last, skip=0, count=0):
     """Per-kernel duration statistics (and per-dispatch counter means) from a
     rocprofv3 SQLite database, restricted to kernels whose name contains
-    `pattern` and to the last `last` such dispatches when given."""
+    `pattern`, past the first `skip` of them, and to the last `last` of those
+    when given."""
     import sqlite3
     import numpy as np
     db = sqlite3.connect(path)
     rows = list(db.execute("select dispatch_id, name, start, duration from kernels order by start"))
-    sel = [r for r in rows if pattern in r[1]]
+    sel = [r for r in rows if pattern in r[1]][skip:]
+    if count:
+        sel = sel[:count]
     if last:
         sel = sel[-last:]
     print("database: %s" % os.path.basename(path))
-    print("dispatches: %d in all, %d selected (kernel name contains %r%s)"
-          % (len(rows), len(sel), pattern, ", last %d" % last if last else ""))
+    print("dispatches: %d in all, %d selected (kernel name contains %r%s%s%s)"
+          % (len(rows), len(sel), pattern, ", first %d left out" % skip if skip else "",
+             ", the next %d" % count if count else "", ", last %d" % last if last else ""))
     by = {}
     for did, name, _, dur in sel:
         by.setdefault(name, []).append(dur)
@@ -223,7 +235,7 @@ def summarize(path, pattern, last):
 def main() -> int:
     args = parse_args()
     if args.summarize:
-        return summarize(args.summarize, args.kernel, args.last)
+        return summarize(args.summarize, args.kernel, args.last, args.skip, args.count)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)." % args.gpus, file=sys.stderr)
@@ -236,6 +248,8 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile and args.profile_leg == "prefill":
+        return profile_prefill(args, q, wl, torch, np, dev)
     layers = args.layers or wl.QWEN3_0_6B_LAYERS
     projs = wl.QWEN3_0_6B_PROJECTIONS
     rows = wl.DECODE_ROWS
@@ -393,6 +407,38 @@ def main() -> int:
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def profile_prefill(args, q, wl, torch, np, dev):
+    """The M = 2048 prefill shapes alone, in order: per shape 2 eager
+    launches, one untimed and one timed replay of a graph of --steps
+    launches (for rocprofv3: shape i's timed dispatches are the
+    (2 + 2 steps) i + 2 + steps .. + steps ones, --skip / --count)."""
+    res = {}
+    for i, (K, N) in enumerate(wl.PREFILL_SHAPES):
+        dp = wl.prefill_inputs(K, N, seed_index=i)
+        pk = q.pack_b_int8(torch.from_numpy(dp["W"]).to(dev))
+        A = torch.from_numpy(dp["A"]).to(dev)
+        rs = torch.from_numpy(dp["rs"]).to(dev)
+        Y = torch.empty((wl.PREFILL_M, N), dtype=torch.float32, device=dev)
+
+        def f(A=A, pk=pk, Y=Y, rs=rs):
+            q.int8_gemm(A, 0, pk, 0, out_f32=Y, row_scale=rs)
+        f()
+        f()
+        torch.cuda.synchronize()
+
+        def run(f=f):
+            for _ in range(args.steps):
+                f()
+        t = time_graph(torch, run, 1) / args.steps
+        tops = 2.0 * wl.PREFILL_M * K * N / t / 1e12
+        res["%dx%d" % (K, N)] = {"us": round(t * 1e6, 2), "TOPS": round(tops, 1),
+                                 "%MFMA": round(100 * tops / INT8_PEAK_TOPS, 2)}
+        del pk, A, Y
+    print(json.dumps({"profile": "prefill", "steps": args.steps, "shapes": res,
+                      "dispatches_per_shape": 2 + 2 * args.steps}), flush=True)
     return 0
 
 
