@@ -18,33 +18,38 @@ namespace {
 // grid each owning 128 x 64: 4 x 2 tiles of v_mfma_i32_32x32x32_i8 (two per
 // tile and k step, 128 int32 accumulators per lane).  The 32 x 32 form
 // issues one MFMA per 32 cycles even at one wavefront per SIMD (the 16 x 16
-// x 64 form reached 2.5 POP/s there, 3.3 at four waves).  With random int8
-// operands on every SIMD the chip clock drops to about 1.5 GHz (2.1 GHz with
-// constant operands), so about 3.0 POP/s, not the nominal 5.0, is the
-// ceiling for this data.  A 32 x 32 x 32 operand takes, for lane L, row (or
-// column) L % 32 and the 16-k chunk 2 h + L / 32 of k half h.
+// x 64 form reached 2.5 POP/s there, 3.3 at four waves).  A 32 x 32 x 32
+// operand takes, for lane L, row (or column) L % 32 and the 16-k chunk
+// 2 h + L / 32 of k half h.
 //
-// Activations: 16-row fragments of 64 k in LDS (1 KiB, one ds_read_b128 per
-// lane per operand).  On the aligned path every stage is copied global-to-LDS
-// (global_load_lds_dwordx4: no register round trip and no LDS store
-// instructions, which measured about 140 cycles a step when interleaved with
-// the MFMAs) into a ring of PF_DEPTH LDS stages.  Weights: the packed tiles
-// are already 16-byte lane chunks of 16 k for one column, so every wavefront
-// loads its operands straight into a ring of PF_DEPTH register stages.
-// Loads run PF_DEPTH k steps ahead (compile-time slots: the k loop is
-// unrolled by PF_DEPTH).
+// Power, not issue, bounds this kernel on random int8 data: the shader
+// clock (s_memtime against the 100 MHz s_memrealtime, per workgroup over the
+// k loop) runs at 1.83 GHz for the MFMAs alone (554 cycles a k step: the 16
+// MFMAs' 512 and the barrier), 1.70 GHz once the operand reads from LDS are
+// added and 1.40 GHz with the global-to-LDS copies as well, where the loop
+// takes 614 cycles a step.  Fewer cycles a step are bought partly back by
+// the clock.
 //
-// In an A fragment the 16-byte piece of (row r, k-chunk g) sits at slot
-// 4 r + (g ^ t(r)), t(r) = ((r >> 1) ^ (r >> 3)) & 3: a row's four chunks
-// fill four consecutive slots, so the lanes that fill consecutive slots (a
-// global-to-LDS copy puts lane L's piece in slot L) read 64 contiguous bytes
-// of one row (a layout with 16 rows per 16 lanes made the copies 25 % slower
-// overall), and the MFMA reads (lane L: row L % 16, one chunk) touch distinct
-// 16-byte bank groups in every 8 and every 16 consecutive lanes.  Row and
-// column epilogue operands are staged in LDS once.
+// Aligned path (FAST): activations and weight tiles are copied global-to-LDS
+// (global_load_lds_dwordx4: no register round trip, no LDS store
+// instructions) two k steps at a time into a ring of three pair buffers (see
+// the loop); a pair's activations are whole 128-byte rows (copies of 64
+// bytes per row, half a cache line, kept the copy path a third slower), laid
+// out so that the MFMA operand reads are free of bank conflicts.  General
+// path (unaligned A or ragged K): activations are staged through registers
+// into 16-row fragments of 64 k in LDS, weights are loaded straight into a
+// ring of PF_DEPTH register stages.
+//
+// In a general-path A fragment the 16-byte piece of (row r, k-chunk g) sits
+// at slot 4 r + (g ^ t(r)), t(r) = ((r >> 1) ^ (r >> 3)) & 3: the MFMA reads
+// (lane L: row L % 16, one chunk) touch distinct 16-byte bank groups in
+// every 8 and every 16 consecutive lanes.  Row and column epilogue operands
+// are staged in LDS once.
 constexpr int PF_BM = 256, PF_BN = 128, PF_DEPTH = 4;
 
 __device__ __forceinline__ int pf_chunk_perm(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// pair layout: chunk swizzle of row r8 (0..7) of a block of parity bp
+__device__ __forceinline__ int pf_pair_swz(int r8, int bp) { return (r8 >> 1) | (bp << 2); }
 __device__ __forceinline__ int pf_slot(int r, int g) { return 4 * r + (g ^ pf_chunk_perm(r)); }
 
 template <int N>
@@ -86,11 +91,10 @@ __device__ __forceinline__ void pf_schedule_staged() {
     if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
 }
 
-// Step order of the direct-load path: the 12 operand reads for the next
-// step (8 activation, 4 weight) and the 6 global-to-LDS copies (4 activation
-// fragments, 2 weight tiles) spread between the 16 MFMAs.
+// Step order of the pair path: the 12 operand reads for the next step and
+// the step's 6 copies spread between the 16 MFMAs.
 template <bool HAS_ZB>
-__device__ __forceinline__ void pf_schedule_direct() {
+__device__ __forceinline__ void pf_schedule_pair() {
     constexpr int MFMA = 0x008, VMEM = 0x060, DS_RD = 0x100;
     static_for<6>([&](auto) {
         __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
@@ -137,24 +141,21 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     constexpr int ACH = AF * 64 / 256;  // 16-byte A chunks per thread per stage (4)
     constexpr int SA = AF * 1024;  // bytes of one activation stage
     constexpr int SB = BF * 1024;  // bytes of one weight stage (FAST: in LDS after the activations)
-    constexpr int SD = FAST ? SA + SB : 16;
-    // activation stages in LDS: three for the register-staged path; for the
-    // FAST path one array per stage, so that the compiler can tell a read
-    // of one stage from a copy still landing in another (it waits for every
-    // outstanding global-to-LDS copy before a read it cannot separate from
-    // them)
+    // activation stages in LDS: three for the register-staged path
     __shared__ __attribute__((aligned(16))) int8_t sA[FAST ? 1 : 3][FAST ? 16 : SA];
-    static_assert(PF_DEPTH <= 6, "direct-path stage arrays");
-    __shared__ __attribute__((aligned(16))) int8_t sD0[SD], sD1[SD], sD2[SD], sD3[SD],
-        sD4[FAST && PF_DEPTH > 4 ? SD : 16], sD5[FAST && PF_DEPTH > 5 ? SD : 16];
-    auto stage_buf = [&](auto B) -> int8_t * {
+    // FAST: three pair buffers, each two k steps (128 k) of activations
+    // (32 KiB) and weight tiles (16 KiB); one array per buffer, so that the
+    // compiler can tell a read of one buffer from copies still landing in
+    // another (it waits for every outstanding global-to-LDS copy before a
+    // read it cannot separate from them)
+    constexpr int SPA = 2 * SA, SPB = 2 * SB;
+    constexpr int SP = FAST ? SPA + SPB : 16;
+    __shared__ __attribute__((aligned(16))) int8_t sP0[SP], sP1[SP], sP2[SP];
+    auto pair_buf = [&](auto B) -> int8_t * {
         constexpr int b = decltype(B)::value;
-        if constexpr (b == 0) return sD0;
-        else if constexpr (b == 1) return sD1;
-        else if constexpr (b == 2) return sD2;
-        else if constexpr (b == 3) return sD3;
-        else if constexpr (b == 4) return sD4;
-        else return sD5;
+        if constexpr (b == 0) return sP0;
+        else if constexpr (b == 1) return sP1;
+        else return sP2;
     };
     __shared__ __attribute__((aligned(16))) float s_rs[PF_BM];
     __shared__ int32_t s_za[PF_BM];
@@ -170,18 +171,17 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     const int strip0 = bn * BF;
     const int KT = p.KT;
 
-    // FAST: wave w copies A fragments 4 w .. 4 w + 3 of each stage straight
-    // into LDS, one 16-byte piece per lane landing in slot L of the fragment;
-    // lane L fetches the (row, k-chunk) that the swizzle puts in slot L.  k
-    // advances by 64 bytes a step.
-    const int8_t *a_src[ACH];
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-        const int r = lane >> 2;
-        const int g = (lane & 3) ^ pf_chunk_perm(r);
-        const int row = min(m0 + (4 * wave + i) * 16 + r, p.M - 1);
-        a_src[i] = p.A + (int64_t)row * p.lda + g * 16;
-    }
+    // FAST: a pair buffer holds 128 k of the workgroup's 256 rows as 1 KiB
+    // blocks of 8 rows x 128 bytes (whole 128-byte lines of A: copies of 64
+    // bytes per row measured a third slower).  Block b holds rows 8 b .. 8 b + 7;
+    // the 16-byte chunk c (0..7: k 16 c .. 16 c + 15 of the pair) of row
+    // 8 b + r8 sits at slot 8 r8 + (c ^ pf_pair_swz(r8, b)), so a copy's lane L
+    // (landing in slot L) reads chunk (L % 8) ^ swz of row 8 b + L / 8, and the
+    // MFMA operand reads of 16 consecutive lanes (16 rows, one chunk) touch
+    // 16 distinct 16-byte bank groups.  Wave w copies blocks 8 w .. 8 w + 7.
+    const int a_r8 = lane >> 3;
+    const int a_c0 = (lane & 7) ^ pf_pair_swz(a_r8, 0), a_c1 = (lane & 7) ^ pf_pair_swz(a_r8, 1);
+    const int a_row0 = m0 + 64 * wave + a_r8;
     // weight operands of this wave: column tile t (32 columns, strips
     // 2t and 2t+1 of the wave's 4), k half h; strips past the last read the
     // last one (their columns are never stored)
@@ -206,6 +206,20 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         a_rd[h] = pf_slot(lane & 15, 2 * h + (lane >> 5)) * 16;
         b_rd[h] = ((2 * h + (lane >> 5)) * 16 + (lane & 15)) * 16;  // inside a packed 1 KiB tile
     }
+    // FAST: A operand of row R = 32 t + L % 32 of the wave's 128 rows, chunk
+    // 4 hs + 2 h + L / 32 of the pair (hs: which k step of the pair): block
+    // R / 8, slot 8 (R % 8) + (chunk ^ swz); the tile adds 4 KiB, the wave's
+    // row half 16 KiB
+    int ap_rd[2][2];
+    {
+        const int r8 = lane & 7, blk = (lane & 31) >> 3;
+        const int swz = pf_pair_swz(r8, blk & 1);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                ap_rd[hs][h] = wm * 16384 + blk * 1024 + (8 * r8 + ((4 * hs + 2 * h + (lane >> 5)) ^ swz)) * 16;
+    }
     auto gload = [&](auto slot, int kt) {
         constexpr int sl = decltype(slot)::value;
 #pragma unroll
@@ -228,20 +242,33 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         const int strip = min(strip0 + 2 * wave + u, p.NS - 1);
         bt_src[u] = p.codes + (int64_t)strip * KT * kTileBytes + lane * 16;
     }
-    // FAST: stage kt (activation fragments and weight tiles) into LDS buffer
-    // BUF, without passing through registers
-    auto dload = [&](auto BUF, int kt) {
+    // FAST: the activations of pair q (k steps 2 q and 2 q + 1) into pair
+    // buffer BUF: 8 copies per wave, each 8 whole rows of 128 bytes; bytes
+    // past K (an odd step count's last pair, pairs past the end) read the
+    // row's last 16 bytes, which no MFMA of a real step reads
+    auto dload_a = [&](auto BUF, int q, auto U0, auto U1) {
+        constexpr int b = decltype(BUF)::value;
+        const int kb0 = min(q * 2 * kTileK + a_c0 * 16, p.K - 16);
+        const int kb1 = min(q * 2 * kTileK + a_c1 * 16, p.K - 16);
+#pragma unroll
+        for (int u = decltype(U0)::value; u < decltype(U1)::value; ++u) {
+            const int row = min(a_row0 + 8 * u, p.M - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(p.A + (int64_t)row * p.lda + ((u & 1) ? kb1 : kb0)),
+                                             (__attribute__((address_space(3))) void *)(pair_buf(ic<b>{}) + (8 * wave + u) * 1024),
+                                             16, 0, 0);
+        }
+    };
+    // FAST: the weight tiles of pair q into pair buffer BUF: 4 copies per
+    // wave (strips 2 w, 2 w + 1 for both k steps; tiles past K read the last)
+    auto dload_b = [&](auto BUF, int q) {
         constexpr int b = decltype(BUF)::value;
 #pragma unroll
-        for (int i = 0; i < ACH; ++i)
-            __builtin_amdgcn_global_load_lds((const void *)(a_src[i] + (int64_t)kt * kTileK),
-                                             (__attribute__((address_space(3))) void *)(stage_buf(ic<b>{}) + (4 * wave + i) * 1024),
+        for (int u = 0; u < 4; ++u) {
+            const int kt = min(2 * q + (u >> 1), KT - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(bt_src[u & 1] + (int64_t)kt * kTileBytes),
+                                             (__attribute__((address_space(3))) void *)(pair_buf(ic<b>{}) + SPA + (u >> 1) * SB + (2 * wave + (u & 1)) * 1024),
                                              16, 0, 0);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            __builtin_amdgcn_global_load_lds((const void *)(bt_src[u] + (int64_t)kt * kTileBytes),
-                                             (__attribute__((address_space(3))) void *)(stage_buf(ic<b>{}) + SA + (2 * wave + u) * 1024),
-                                             16, 0, 0);
+        }
     };
     auto sstore = [&](auto slot, int buf) {
         constexpr int sl = decltype(slot)::value;
@@ -271,15 +298,21 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
 #pragma unroll
             for (int t = 0; t < 4; ++t)
                 fa[f][t][h] = *(const v4i *)(base + (wm * 8 + t * 2 + ((lane & 31) >> 4)) * 1024 + a_rd[h]);
-        if constexpr (FAST) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    fb[f][t][h] = *(const v4i *)(base + SA + (wn * 4 + t * 2 + ((lane & 31) >> 4)) * 1024 + b_rd[h]);
-        }
     };
     auto lds_frags = [&](auto F, int buf) { lds_frags_at(F, &sA[buf][0]); };
+    // FAST: step operands from pair buffer base, k step HS of the pair
+    auto lds_frags_pair = [&](auto F, auto HS, const int8_t *base) {
+        constexpr int f = decltype(F)::value, hs = decltype(HS)::value;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) fa[f][t][h] = *(const v4i *)(base + t * 4096 + ap_rd[hs][h]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                fb[f][t][h] = *(const v4i *)(base + SPA + hs * SB + (wn * 4 + t * 2 + ((lane & 31) >> 4)) * 1024 + b_rd[h]);
+    };
     // step k: activation set F, weight operands from register slot S (FAST:
     // from operand set F)
     auto mfmas = [&](auto F, auto S) {
@@ -295,32 +328,32 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
             }
     };
 
-    // Stage s: register slot s % PF_DEPTH, LDS buffer s % 3, activation
-    // operand set s % 2.  Step k: read step k+1's activation operands (LDS
-    // buffer written in step k-1, published by its barrier), MFMAs of step k
-    // (weight operands in slot k % PF_DEPTH, loaded PF_DEPTH steps ago),
-    // store stage k+2's activations (its buffer was last read for step k-1,
-    // whose reads completed before the MFMAs of step k-1), load stage
-    // k+PF_DEPTH into slot k % PF_DEPTH, barrier.
-    const int KTD = KT - KT % PF_DEPTH;
     if constexpr (FAST) {
-        // Stage s: LDS buffer s % PF_DEPTH (activation fragments, then the
-        // weight tiles), operand sets s % 2.  Step k: read step k+1's
-        // operands (published by the barrier of step k-1), MFMAs of step k,
-        // copy stage k+PF_DEPTH (its buffer held stage k, read in step
-        // k-1), then wait until stage k+2 has landed in LDS and barrier.
-        // Every step issues 6 copies per wavefront (stages past the last
-        // repeat the last one), so stage k+2's are complete once at most
-        // 6 (PF_DEPTH - 2) remain outstanding.
-        static_for<PF_DEPTH>([&](auto S) { dload(S, min(decltype(S)::value, KT - 1)); });
+        // Pair q (k steps 2 q, 2 q + 1) lives in pair buffer q % 3.  Step k
+        // reads step k+1's operands, runs the MFMAs of step k and issues 6 of
+        // the 12 copies of pair k / 2 + 2 per wavefront (even k: activation
+        // copies 0-5; odd k: activation copies 6-7 and the 4 weight copies).
+        // That pair's buffer held pair k / 2 - 1, last read in step k - 2
+        // (for step k - 1); the barrier after step k - 2 (even) follows each
+        // wavefront's wait for its LDS reads, so no copy overwrites data a
+        // wavefront still reads.  Only even steps end with a wait and a
+        // barrier: step k + 1 (odd) reads step k + 2, the first of pair
+        // k / 2 + 1, whose copies were all issued in steps k - 2 and k - 1,
+        // so at most the 6 copies of step k may remain outstanding; an odd
+        // step's next step reads its own pair, already published.
+        dload_a(ic<0>{}, 0, ic<0>{}, ic<8>{});
+        dload_b(ic<0>{}, 0);
+        dload_a(ic<1>{}, 1, ic<0>{}, ic<8>{});
+        dload_b(ic<1>{}, 1);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<6 * (PF_DEPTH - 2)>();
+        wait_vmcnt<12>();
         lds_barrier();
-        lds_frags_at(ic<0>{}, stage_buf(ic<0>{}));
+        lds_frags_pair(ic<0>{}, ic<0>{}, pair_buf(ic<0>{}));
         wait_lgkmcnt0();
-        auto dstep = [&](auto J, int kt) {
+        // step base + j, base a multiple of 6 (j fixes the buffers)
+        auto pstep = [&](auto J, int kt) {
             constexpr int j = decltype(J)::value;
-            lds_frags_at(ic<(j + 1) & 1>{}, stage_buf(ic<(j + 1) % PF_DEPTH>{}));
+            lds_frags_pair(ic<(j + 1) & 1>{}, ic<(j + 1) & 1>{}, pair_buf(ic<((j + 1) / 2) % 3>{}));
             if constexpr (FLIP) {
                 // uint8 activations: the flip happens on this step's operands,
                 // read (and waited for) before the previous barrier
@@ -329,21 +362,36 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h) fa[j & 1][t][h] ^= 0x80808080;
             }
-            mfmas(ic<j & 1>{}, J);
-            const int kn = min(kt + PF_DEPTH, KT - 1);
-            dload(J, kn);
-            pf_schedule_direct<HAS_ZB>();
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<6 * (PF_DEPTH - 2)>();
-            lds_barrier();
+            mfmas(ic<j & 1>{}, ic<0>{});
+            if constexpr ((j & 1) == 0) {
+                dload_a(ic<(j / 2 + 2) % 3>{}, kt / 2 + 2, ic<0>{}, ic<6>{});
+                pf_schedule_pair<HAS_ZB>();
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<6>();
+                lds_barrier();
+            } else {
+                dload_a(ic<((j - 1) / 2 + 2) % 3>{}, (kt - 1) / 2 + 2, ic<6>{}, ic<8>{});
+                dload_b(ic<((j - 1) / 2 + 2) % 3>{}, (kt - 1) / 2 + 2);
+                pf_schedule_pair<HAS_ZB>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
         };
-        for (int base = 0; base < KTD; base += PF_DEPTH)
-            static_for<PF_DEPTH>([&](auto J) { dstep(J, base + decltype(J)::value); });
-        static_for<PF_DEPTH - 1>([&](auto J) {
-            if (KTD + decltype(J)::value < KT) dstep(J, KTD + decltype(J)::value);
+        const int KT6 = KT - KT % 6;
+        for (int base = 0; base < KT6; base += 6)
+            static_for<6>([&](auto J) { pstep(J, base + decltype(J)::value); });
+        static_for<5>([&](auto J) {
+            if (KT6 + decltype(J)::value < KT) pstep(J, KT6 + decltype(J)::value);
         });
         wait_vmcnt<0>();
     } else {
+    // General path.  Stage s: register slot s % PF_DEPTH, LDS buffer s % 3,
+    // activation operand set s % 2.  Step k: read step k+1's activation
+    // operands (LDS buffer written in step k-1, published by its barrier),
+    // MFMAs of step k (weight operands in slot k % PF_DEPTH, loaded PF_DEPTH
+    // steps ago), store stage k+2's activations (its buffer was last read for
+    // step k-1, whose reads completed before the MFMAs of step k-1), load
+    // stage k+PF_DEPTH into slot k % PF_DEPTH, barrier.
+    const int KTD = KT - KT % PF_DEPTH;
     static_for<PF_DEPTH>([&](auto S) { gload(S, min(decltype(S)::value, KT - 1)); });
     sstore(ic<0>{}, 0);
     sstore(ic<1 % PF_DEPTH>{}, 1);
