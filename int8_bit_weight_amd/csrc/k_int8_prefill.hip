@@ -164,9 +164,21 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
+    // Tile order: workgroup ids go round-robin over the 8 XCDs, so id w is
+    // first renumbered XCD-major (each XCD's workgroups get consecutive
+    // numbers), then numbers run through groups of 4 row tiles column by
+    // column: an XCD's resident workgroups share 4 row tiles and a run of
+    // column tiles, about a fifth less data through its L2 than a row of
+    // tiles (measured 1-3 % faster on the M = 2048 shapes).
     const int tiles_n = (p.NS + BF - 1) / BF;
-    const int bn = blockIdx.x % tiles_n;
-    const int bm = blockIdx.x / tiles_n;
+    const int tiles_m = (p.M + PF_BM - 1) / PF_BM;
+    int w = blockIdx.x;
+    if (gridDim.x % 8 == 0) w = (w % 8) * (gridDim.x / 8) + w / 8;
+    constexpr int GM = 4;
+    const int gq = w / (GM * tiles_n), gr = w % (GM * tiles_n);
+    const int gm = min(GM, tiles_m - gq * GM);
+    const int bm = gq * GM + gr % gm;
+    const int bn = gr / gm;
     const int m0 = bm * PF_BM;
     const int strip0 = bn * BF;
     const int KT = p.KT;
