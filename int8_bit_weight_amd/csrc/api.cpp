@@ -227,8 +227,8 @@ static void fill_params(Int8GemmParams &p, int64_t M, int64_t K, int64_t N, cons
 
 static void trace_gemm(const char *fn, const char *variant, int64_t M, int64_t K, int64_t N, const Int8Plan &plan) {
     if (trace_on())
-        fprintf(stderr, "qmm %s variant=%s M=%lld K=%lld N=%lld grid=%lld waves=%d tpw=%d\n", fn, variant,
-                (long long)M, (long long)K, (long long)N, (long long)plan.grid, plan.waves, plan.tpw);
+        fprintf(stderr, "qmm %s variant=%s M=%lld K=%lld N=%lld grid=%lld waves=%d tpw=%d spw=%d\n", fn, variant,
+                (long long)M, (long long)K, (long long)N, (long long)plan.grid, plan.waves, plan.tpw, plan.spw);
 }
 
 // int8_gemm and int8_gemm_per_axis: scalar zero points zA, zB, or one per
@@ -293,43 +293,71 @@ qmm_status int8_gemm_per_axis(const void *A, qmm_i8type at, int64_t M, int64_t K
                      stream, "int8_gemm_per_axis");
 }
 
-// The fused form quantises all M x K activations in every workgroup: it
-// wins while that is small next to a second launch (measured on MI355X for
-// the Qwen3-0.6B projections: M = 1 and M = 16 with K <= 2048 gain, M = 32
-// loses).
-// The quantisation inside the product: every workgroup quantises the rows it
-// multiplies, which beats a second launch while M' * K <= 16384 (M' = rows
-// rounded up to a power of two <= 16).  Larger M is cut into row groups of
-// that size (a second grid dimension, the weights read once per group, mostly
-// from L2), preferring groups of at most 8 rows: a workgroup's quantisation
-// of 16 rows cost more than the extra weight reads (measured; groups of 4
-// rows cost more again).  0 groups = not fused, else 1, 2, 4 or 8.
-static int dynamic_groups(int64_t M, int64_t K) {
-    if (K > 4096) return 0;
-    for (int rmax : {8, 16})
-        for (int g : {1, 2, 4, 8}) {
-            const int64_t r = (M + g - 1) / g;
-            int64_t e = 1;
-            while (e < r) e <<= 1;
-            if (e <= rmax && e * K <= 16384) return g;
-        }
-    return 0;
+// The fused form quantises the activations inside the product: every
+// workgroup quantises the rows it multiplies.  It is taken while
+// E * K <= 16384 and K <= 4096 for some split of the rows into 1, 2, 4 or 8
+// row groups (E = rows per group rounded up to a power of two, at most 16):
+// then one workgroup keeps its rows' values in registers from the row
+// maximum to the codes.  Beyond that the rows are quantised by a launch of
+// their own.
+static bool dynamic_fusable(int64_t M, int64_t K) {
+    if (K > 4096) return false;
+    for (int g : {1, 2, 4, 8}) {
+        const int64_t r = (M + g - 1) / g;
+        int64_t e = 1;
+        while (e < r) e <<= 1;
+        if (e <= 16 && e * K <= 16384) return true;
+    }
+    return false;
 }
 // Calls the wide decode takes (many columns) quantise in a launch of their
 // own: there the weight bytes per workgroup are few next to a quantisation in
 // every workgroup.
 static bool dynamic_fused(int64_t M, int64_t K, int64_t N) {
-    return dynamic_groups(M, K) > 0 && !use_wide(M, K, N);
+    return dynamic_fusable(M, K) && !use_wide(M, K, N);
 }
-// rows one workgroup of the fused path quantises and multiplies
-static int64_t dynamic_rows(int64_t M, int64_t K) {
-    const int g = dynamic_groups(M, K);
-    return g > 1 ? (M + g - 1) / g : M;
+
+// Shape of the fused launch: rows per row group and 16-column strips per
+// workgroup (S = 1, 2, 4; the S strips share one quantisation of the rows).
+// A workgroup reads rows * K * 4 bytes of activations (from L2) and
+// S * K * 16 bytes of weights; with one workgroup per CU resident at a time
+// (16 wavefronts), the call costs about rounds * (those bytes), rounds =
+// ceil(workgroups / 256 CUs).  The split with the fewest such bytes is
+// taken, fewer rows per group on a tie (less quantisation per workgroup).
+// On MI355X this picked the fastest of all splits for every Qwen3-0.6B
+// projection group at M = 1, 16 and 32 (the grouped q/k/v call at M = 32:
+// 4 groups of 8 rows, 4 strips per workgroup, 5.9 us against 9.7 us for one
+// strip per workgroup).
+struct DynShape {
+    int64_t rows;  // rows per group (= M: one group)
+    int spw;       // strips per workgroup
+};
+static DynShape dynamic_shape(int64_t M, int64_t K, int64_t NS) {
+    constexpr int64_t kCUs = 256;
+    DynShape best{M, 1};
+    int64_t best_cost = INT64_MAX, best_e = INT64_MAX;
+    for (int g : {1, 2, 4, 8}) {
+        const int64_t r = (M + g - 1) / g;
+        int64_t e = 1;
+        while (e < r) e <<= 1;
+        if (e > 16 || e * K > 16384) continue;
+        const int64_t groups = (M + r - 1) / r;
+        for (int spw : {1, 2, 4}) {
+            const int64_t wgs = ceil_div(NS, spw) * groups;
+            const int64_t cost = ceil_div(wgs, kCUs) * (r * K * 4 + spw * K * 16);
+            if (cost < best_cost || (cost == best_cost && e < best_e)) {
+                best_cost = cost;
+                best_e = e;
+                best = DynShape{r, spw};
+            }
+        }
+    }
+    return best;
 }
 
 size_t qmm_int8_gemm_dynamic_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     if (M <= 0 || K <= 0 || N <= 0) return 0;
-    if (dynamic_fused(M, K, N)) return (size_t)plan_int8_gemm(dynamic_rows(M, K), K, N, false).ws_bytes;
+    if (dynamic_fused(M, K, N)) return (size_t)plan_int8_gemm(dynamic_shape(M, K, packed_b_layout(K, N).NS).rows, K, N, false).ws_bytes;
     return (size_t)(round_up(M * K, 256) + round_up(4 * M, 256));
 }
 
@@ -370,8 +398,10 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
     // 16 wavefronts with up to 4 k tiles each: one round covers K <= 4096,
     // so the activations stay in registers between the amax and quantise
     // passes.
-    const int64_t rows = dynamic_rows(M, K);
+    const DynShape ds = dynamic_shape(M, K, packed_b_layout(K, N).NS);
+    const int64_t rows = ds.rows;
     Int8Plan plan = plan_int8_gemm(rows, K, N, false);
+    plan.spw = ds.spw;
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
         return QMM_ERR_WORKSPACE;
     Int8GemmParams p{};
@@ -393,7 +423,7 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
 static_assert(QMM_MAX_GROUP_ITEMS == kMaxGroups, "one grouped launch holds every item");
 
 size_t qmm_int8_gemm_dynamic_grouped_workspace_bytes(int64_t M, int64_t K) {
-    if (M <= 0 || K <= 0 || dynamic_groups(M, K) > 0) return 0;
+    if (M <= 0 || K <= 0 || dynamic_fusable(M, K)) return 0;
     return (size_t)(round_up(M * K, 256) + round_up(4 * M, 256));
 }
 
@@ -421,8 +451,7 @@ qmm_status int8_gemm_dynamic_grouped(const float *X, int64_t M, int64_t K, int64
             return QMM_ERR_INVALID;
         if (g_check && qmm_packed_b_check(it.packedB, K, it.N, stream) != QMM_OK) return QMM_ERR_INVALID;
     }
-    const int G = dynamic_groups(M, K);
-    if (G == 0) {
+    if (!dynamic_fusable(M, K)) {
         // not fusable: quantise once, then one product per item
         const size_t need = qmm_int8_gemm_dynamic_grouped_workspace_bytes(M, K);
         if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return QMM_ERR_WORKSPACE;
@@ -462,8 +491,10 @@ qmm_status int8_gemm_dynamic_grouped(const float *X, int64_t M, int64_t K, int64
         ++n;
     }
     if (n == 0) return QMM_OK;
-    const int64_t rows = dynamic_rows(M, K);
-    const Int8Plan plan = plan_int8_gemm(rows, K, 16, false);
+    const DynShape ds = dynamic_shape(M, K, sb);
+    const int64_t rows = ds.rows;
+    Int8Plan plan = plan_int8_gemm(rows, K, 16, false);
+    plan.spw = ds.spw;
     Int8GemmParams p{};
     qmm_epilogue e0{};
     e0.outputs = QMM_OUT_F32;

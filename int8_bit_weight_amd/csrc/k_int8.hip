@@ -402,36 +402,54 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide(Int8GemmPa
         }
 }
 
-// Fused dynamic quantisation for small M x K (the planner takes it when
-// M' * K <= 16384, M' = rows per group rounded up to a power of two <= 16,
-// and K <= 4096; up to 8 row groups run as the grid's second dimension):
-// 16 wavefronts, TPW k tiles each
-// (wave w takes tiles w, w+16, ...).  Activations are held compactly: E = M
-// rounded up to a power of two values per lane (at most 32), 64/E lanes per
-// row, so every lane does real work (at M = 1 each lane holds one value per
-// tile).  All loads go out first.  Row maxima combine across the lanes of a
-// row (shuffles) and the waves (LDS, one barrier); each lane forms its row's
-// scale amax/127 and quantises its values with the k_quantize_rows rule;
-// per tile the codes go through a wave-private LDS area into MFMA A-operand
-// order (one 16-row tile per 16 rows); then the LDS sum over the waves and
-// the epilogue.  Every workgroup quantises all M x K activations again,
-// which is why the planner keeps M*K small here.
+// Fused dynamic quantisation for small M x K (the planner takes it while
+// E * K <= 16384, E = rows of a row group rounded up to a power of two <= 16,
+// and K <= 4096; row groups run as the grid's second dimension).  A
+// workgroup of 16 wavefronts covers S consecutive 16-column strips:
+//   1. every wavefront loads the activations of its k tiles (tile t belongs
+//      to wave t % 16; E / 64 lanes per row, E values per lane and tile, so
+//      every lane does real work even at M = 1), then its weight tiles;
+//   2. row maxima combine across the lanes of a row (shuffles) and the
+//      waves (LDS, one barrier); each lane forms its row's scale amax/127 and
+//      quantises its values with the k_quantize_rows rule into an LDS copy of
+//      the rows' codes, laid out as MFMA A operands (E rows of 64 bytes per
+//      k tile);
+//   3. the 16 / S wavefronts of a strip take its k tiles round-robin, one
+//      16x16x64 MFMA per tile with A from LDS (rows >= E read as zero);
+//   4. the strip's wavefronts' int32 tiles are summed in LDS and the
+//      epilogue runs in the same workgroup.
+// All S strips share the one quantisation, so the activations are read
+// from L2 once per S strips: S > 1 pays where M * K is large next to a
+// strip's weights.  At S = 1 every wave only multiplies the tiles it
+// quantised itself and no barrier separates phases 2 and 3.
 // GROUPED: the grid's strips are those of up to kMaxGroups weights that
-// share the activations, back to back; each workgroup takes its item's
-// weight, width and epilogue operands from `g` and works on the item's own
-// strip index (every item is the same computation as a call of its own).
+// share the activations, back to back; each wavefront takes its strip's
+// item (weight, width, epilogue operands) from `g` and works on the item's
+// own strip index (every item is the same computation as a call of its
+// own).
 struct NoGroups {};
 template <bool GROUPED>
 using GroupArg = std::conditional_t<GROUPED, DecodeGroups, NoGroups>;
 
-template <int E, int TPW, bool AVEC, bool GROUPED>
+template <int E, int TPQ, int S, bool AVEC, bool GROUPED>
 __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupArg<GROUPED> g) {
-    int strip = blockIdx.x;
-    bool first_item = true;  // writes the optional quantised rows and scales
+    constexpr int WAVES = 16;
+    constexpr int WPS = WAVES / S;         // wavefronts per strip
+    constexpr int TPB = TPQ * S;           // weight tiles per wavefront (bound)
+    constexpr int L = 64 / E;              // lanes per row
+    static_assert(E == 1 || E == 2 || E == 4 || E == 8 || E == 16, "E is a power of two <= 16");
+    static_assert(S == 1 || S == 2 || S == 4, "S divides the 16 wavefronts");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slot = wave / WPS, kg = wave % WPS;
+    // the quantised rows and scales are written once, by workgroup x = 0
+    const bool writer = blockIdx.x == 0;
+    const int gstrip = (int)blockIdx.x * S + slot;
+    const bool strip_ok = gstrip < p.NS;
+    int strip = min(gstrip, p.NS - 1);
     if constexpr (GROUPED) {
         const int it = (strip >= g.strip_begin[1]) + (strip >= g.strip_begin[2]) + (strip >= g.strip_begin[3]);
         strip -= g.strip_begin[it];
-        first_item = it == 0;
         p.codes = g.codes[it];
         p.colsum = g.colsum[it];
         p.col_scale = g.col_scale[it];
@@ -439,8 +457,8 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupA
         p.ld_f32 = g.ld_f32[it];
         p.bias_f32 = g.bias_f32[it];
         p.N = g.N[it];
-        p.NS = (p.N + kTileN - 1) / kTileN;
     }
+    // (after the item's operands: the row offsets apply to its output)
     if (p.rpg > 0) {
         // row group blockIdx.y: rows [y rpg, y rpg + rpg) of the call, quantised
         // and multiplied on their own (the weights are read once per group)
@@ -453,25 +471,18 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupA
         if (p.xq_out) p.xq_out += (int64_t)r0 * p.ldq;
         if (p.rs_out) p.rs_out += r0;
     }
-    constexpr int WAVES = 16;
-    constexpr int L = 64 / E;              // lanes per row
-    constexpr int MT = E > 16 ? 2 : 1;     // 16-row MFMA tiles
-    constexpr int ROWS = MT * 16;
-    constexpr int NE = ROWS * 16;          // outputs of the workgroup
-    static_assert(E == 1 || E == 2 || E == 4 || E == 8 || E == 16 || E == 32, "E is a power of two <= 32");
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const int m = lane / L;                    // row of this lane's values
     const int kl = (lane % L) * E;             // their first k within a tile
     const bool row_ok = m < p.M;
+    const int KT = p.KT;
 
     // loads: activations, weight tiles, the epilogue's column operands
-    float x[TPW][E];
-    v4i bf[TPW];
+    float x[TPQ][E];
+    v4i bf[TPB];
     {
         const float *src = p.X + (int64_t)min(m, p.M - 1) * p.ldx;
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
+        for (int t = 0; t < TPQ; ++t) {
             const int k0 = (wave + t * WAVES) * kTileK + kl;
             const bool ok = row_ok && k0 < p.K;
             if (AVEC && E >= 4) {
@@ -490,21 +501,20 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupA
                 }
             }
         }
+        const int8_t *cs = p.codes + (int64_t)strip * KT * kTileBytes + lane * 16;
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
-            bf[t] = *(const v4i *)(p.codes + ((int64_t)strip * p.KT + min(wave + t * WAVES, p.KT - 1)) * kTileBytes +
-                                   lane * 16);
+        for (int j = 0; j < TPB; ++j) bf[j] = *(const v4i *)(cs + (int64_t)min(kg + j * WPS, KT - 1) * kTileBytes);
     }
-    const ColOps col = load_colops_c(p, strip * kTileN + (threadIdx.x & 15));
+    const ColOps col = load_colops_c(p, strip * kTileN + (lane & 15));
 
-    __shared__ __attribute__((aligned(16))) float s_amax[ROWS][WAVES];  // [row][wave]
-    __shared__ float s_scale[ROWS];
-    __shared__ __attribute__((aligned(16))) int8_t s_q[WAVES][ROWS][64];  // [wave][row][k]
-    __shared__ int32_t s_red[WAVES][ROWS][17];
+    __shared__ __attribute__((aligned(16))) float s_amax[E][WAVES];  // [row][wave]
+    __shared__ float s_scale[E];
+    __shared__ __attribute__((aligned(16))) int8_t s_q[TPQ * WAVES][E][64];  // [k tile][row][k]
+    __shared__ int32_t s_red[WAVES][E][17];
 
     float a = 0.0f;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int t = 0; t < TPQ; ++t)
 #pragma unroll
         for (int j = 0; j < E; ++j) a = fmaxf(a, fabsf(x[t][j]));
 #pragma unroll
@@ -520,16 +530,13 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupA
     const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
     if (wave == 0 && lane % L == 0) {
         s_scale[m] = s;
-        if (p.rs_out && strip == 0 && first_item && row_ok) p.rs_out[m] = s;
+        if (p.rs_out && writer && row_ok) p.rs_out[m] = s;
     }
     const float y = 1.0f / s;
     const bool fast_s = s >= 0x1p-100f && s <= 0x1p100f;
 
-    v4i acc[MT];
 #pragma unroll
-    for (int r = 0; r < MT; ++r) acc[r] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
+    for (int t = 0; t < TPQ; ++t) {
         // codes: clamp(rne(x / s), -127, 127), 0 for an all-zero row
         float qv[E];
         bool fast = fast_s;
@@ -552,44 +559,49 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupA
             const uint32_t c = s > 0.0f ? (uint32_t)((int)r & 0xFF) : 0u;
             w[j >> 2] |= c << (8 * (j & 3));
         }
-        int8_t *qdst = &s_q[wave][m][kl];
+        // tiles past KT (only in the last round of a wave) are never read
+        int8_t *qdst = &s_q[wave + t * WAVES][m][kl];
         if constexpr (E == 1) *(uint8_t *)qdst = (uint8_t)w[0];
         else if constexpr (E == 2) *(uint16_t *)qdst = (uint16_t)w[0];
         else if constexpr (E == 4) *(uint32_t *)qdst = w[0];
         else if constexpr (E == 8) *(uint64_t *)qdst = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
-        else {
-#pragma unroll
-            for (int i = 0; i < E / 16; ++i)
-                *(v4i *)(qdst + 16 * i) = v4i{(int)w[4 * i], (int)w[4 * i + 1], (int)w[4 * i + 2], (int)w[4 * i + 3]};
-        }
+        else *(v4i *)qdst = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
         const int k0 = (wave + t * WAVES) * kTileK + kl;
-        if (p.xq_out && strip == 0 && first_item && row_ok && k0 < p.K) {
+        if (p.xq_out && writer && row_ok && k0 < p.K) {
             int8_t *dst = p.xq_out + (int64_t)m * p.ldq + k0;
             for (int j = 0; j < E && k0 + j < p.K; ++j) dst[j] = (int8_t)(w[j >> 2] >> (8 * (j & 3)));
         }
-        __builtin_amdgcn_wave_barrier();
-        // A operands: lane (row lane % 16, k-group lane / 16); rows >= M are zero
-#pragma unroll
-        for (int r = 0; r < MT; ++r) {
-            const int ar = r * 16 + (lane & 15);
-            v4i af = *(const v4i *)(&s_q[wave][ar][(lane >> 4) * 16]);
-            if (ar >= p.M) af = v4i{0, 0, 0, 0};
-            acc[r] = mfma_i8(af, bf[t], acc[r]);
-        }
-        __builtin_amdgcn_wave_barrier();
     }
+    if constexpr (S == 1) __builtin_amdgcn_wave_barrier();
+    else __syncthreads();
+
+    // A operands: lane (row lane % 16, k-group lane / 16); rows >= E are zero.
+    // Tiles past KT multiply zero weights (no branch around the MFMA).
+    v4i acc = v4i{0, 0, 0, 0};
+    const int ar = lane & 15;
 #pragma unroll
-    for (int r = 0; r < MT; ++r)
+    for (int j = 0; j < TPB; ++j) {
+        const int kt = kg + j * WPS;
+        const int ktc = min(kt, TPQ * WAVES - 1);
+        v4i af = *(const v4i *)(&s_q[ktc][ar < E ? ar : 0][(lane >> 4) * 16]);
+        if (ar >= E || kt >= KT) af = v4i{0, 0, 0, 0};
+        acc = mfma_i8(af, bf[j], acc);
+    }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_red[wave][r * 16 + 4 * (lane >> 4) + i][lane & 15] = acc[r][i];
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * (lane >> 4) + i;
+        if (r < E) s_red[wave][r][lane & 15] = acc[i];
+    }
     __syncthreads();
-    for (int e = threadIdx.x; e < NE; e += WAVES * 64) {
+    // the strip's outputs: E rows x 16 columns over its WPS wavefronts
+    const int n = strip * kTileN + (lane & 15);
+    for (int e = kg * 64 + lane; e < E * 16; e += WPS * 64) {
         const int mo = e >> 4;
-        const int n = strip * kTileN + (e & 15);
-        if (mo < p.M && n < p.N) {
+        if (strip_ok && mo < p.M && n < p.N) {
             int32_t v = 0;
 #pragma unroll
-            for (int ww = 0; ww < WAVES; ++ww) v += s_red[ww][mo][e & 15];
+            for (int ww = 0; ww < WPS; ++ww) v += s_red[slot * WPS + ww][mo][e & 15];
             epilogue_store_c(p, mo, n, (uint32_t)v, 0, false, s_scale[mo], 0, col);
         }
     }
@@ -694,28 +706,36 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
     return launch_int8_prefill(p, s);
 }
 
-template <int E, int TPW, bool GROUPED>
+template <int E, int TPQ, int S, bool GROUPED>
 hipError_t launch_dyn(const Int8GemmParams &p, const DecodeGroups &dg, bool avec, hipStream_t s) {
     const unsigned groups = p.rpg > 0 ? (unsigned)((p.M + p.rpg - 1) / p.rpg) : 1u;
-    const dim3 g((unsigned)p.NS, groups), b(1024);
+    const dim3 g((unsigned)((p.NS + S - 1) / S), groups), b(1024);
     GroupArg<GROUPED> ga{};
     if constexpr (GROUPED) ga = dg;
     if (E >= 4 && avec)
-        hipLaunchKernelGGL((k_int8_decode_q<E, TPW, true, GROUPED>), g, b, 0, s, p, ga);
+        hipLaunchKernelGGL((k_int8_decode_q<E, TPQ, S, true, GROUPED>), g, b, 0, s, p, ga);
     else
-        hipLaunchKernelGGL((k_int8_decode_q<E, TPW, false, GROUPED>), g, b, 0, s, p, ga);
+        hipLaunchKernelGGL((k_int8_decode_q<E, TPQ, S, false, GROUPED>), g, b, 0, s, p, ga);
     return hipGetLastError();
 }
 
-// E * K <= 16384 (the planner's bound) keeps E * TPW <= 16.
+template <int E, int TPQ, bool GROUPED>
+hipError_t launch_dyn_s(const Int8GemmParams &p, const DecodeGroups &dg, int spw, bool avec, hipStream_t s) {
+    if (spw == 1) return launch_dyn<E, TPQ, 1, GROUPED>(p, dg, avec, s);
+    if (spw == 2) return launch_dyn<E, TPQ, 2, GROUPED>(p, dg, avec, s);
+    if (spw == 4) return launch_dyn<E, TPQ, 4, GROUPED>(p, dg, avec, s);
+    return hipErrorInvalidValue;
+}
+
+// E * K <= 16384 (the planner's bound) keeps E * TPQ <= 16.
 template <int E, bool GROUPED>
-hipError_t launch_dyn_tpw(const Int8GemmParams &p, const DecodeGroups &dg, bool avec, hipStream_t s) {
-    if (p.KT <= 16) return launch_dyn<E, 1, GROUPED>(p, dg, avec, s);
+hipError_t launch_dyn_tpq(const Int8GemmParams &p, const DecodeGroups &dg, int spw, bool avec, hipStream_t s) {
+    if (p.KT <= 16) return launch_dyn_s<E, 1, GROUPED>(p, dg, spw, avec, s);
     if constexpr (E <= 8) {
-        if (p.KT <= 32) return launch_dyn<E, 2, GROUPED>(p, dg, avec, s);
+        if (p.KT <= 32) return launch_dyn_s<E, 2, GROUPED>(p, dg, spw, avec, s);
     }
     if constexpr (E <= 4) {
-        if (p.KT <= 64) return launch_dyn<E, 4, GROUPED>(p, dg, avec, s);
+        if (p.KT <= 64) return launch_dyn_s<E, 4, GROUPED>(p, dg, spw, avec, s);
     }
     return hipErrorInvalidValue;
 }
@@ -726,23 +746,28 @@ hipError_t launch_dyn_rows(const Int8Plan &plan, const Int8GemmParams &p, const 
     if (plan.variant != 0 || rows > 16 || p.KT > 64 || p.zBs != 0 || p.zb_col || p.za_row)
         return hipErrorInvalidValue;
     const bool v = p.x_vec && (p.K % 16) == 0;
+    const int spw = plan.spw > 0 ? plan.spw : 1;
     // E: values per lane, the rows rounded up to a power of two
-    if (rows <= 1) return launch_dyn_tpw<1, GROUPED>(p, dg, v, s);
-    if (rows <= 2) return launch_dyn_tpw<2, GROUPED>(p, dg, v, s);
-    if (rows <= 4) return launch_dyn_tpw<4, GROUPED>(p, dg, v, s);
-    if (rows <= 8) return launch_dyn_tpw<8, GROUPED>(p, dg, v, s);
-    return launch_dyn_tpw<16, GROUPED>(p, dg, v, s);
+    if (rows <= 1) return launch_dyn_tpq<1, GROUPED>(p, dg, spw, v, s);
+    if (rows <= 2) return launch_dyn_tpq<2, GROUPED>(p, dg, spw, v, s);
+    if (rows <= 4) return launch_dyn_tpq<4, GROUPED>(p, dg, spw, v, s);
+    if (rows <= 8) return launch_dyn_tpq<8, GROUPED>(p, dg, spw, v, s);
+    return launch_dyn_tpq<16, GROUPED>(p, dg, spw, v, s);
 }
 
 hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                                     const char **variant) {
-    *variant = p.rpg > 0 ? "int8_dynamic_groups" : "int8_dynamic_m16";
+    // names carry the strips per workgroup
+    static const char *const names[2][3] = {{"int8_dynamic_m16", "int8_dynamic_m16_s2", "int8_dynamic_m16_s4"},
+                                            {"int8_dynamic_groups", "int8_dynamic_groups_s2",
+                                             "int8_dynamic_groups_s4"}};
+    *variant = names[p.rpg > 0][plan.spw == 4 ? 2 : (plan.spw == 2 ? 1 : 0)];
     return launch_dyn_rows<false>(plan, p, DecodeGroups{}, s);
 }
 
 hipError_t launch_int8_gemm_dynamic_grouped(const Int8Plan &plan, Int8GemmParams p, const DecodeGroups &g,
                                             hipStream_t s, const char **variant) {
-    *variant = "int8_dynamic_grouped";
+    *variant = plan.spw == 4 ? "int8_dynamic_grouped_s4" : (plan.spw == 2 ? "int8_dynamic_grouped_s2" : "int8_dynamic_grouped");
     return launch_dyn_rows<true>(plan, p, g, s);
 }
 

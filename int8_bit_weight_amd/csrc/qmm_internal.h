@@ -143,6 +143,7 @@ struct Int8Plan {
     int mt;           // 16-row tiles (decode)
     int waves;        // waves per workgroup (decode)
     int tpw;          // k tiles per wave per round (decode)
+    int spw;          // 16-column strips per workgroup (fused quantising decode; 0 = 1)
     int64_t grid;
     int64_t ws_bytes; // workspace the plan needs (0 for every current variant)
 };

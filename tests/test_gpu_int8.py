@@ -477,19 +477,39 @@ def test_workspace_shared_across_shapes(q, orc):
 
 # ------------------------------------------------- dynamic (fused) path ---
 
-def _dynamic_groups(M, K):
-    """Row groups of the fused dynamic path: the fewest of 1, 2, 4, 8 whose rows
-    (rounded up to a power of two, <= 8 if possible, else <= 16) times K stay
-    <= 16384; 0 = two launches."""
+def _dynamic_shape(M, K, NS):
+    """(row groups, strips per workgroup) of the fused dynamic path, or None
+    for two launches.  Fused while some split into 1, 2, 4 or 8 row groups
+    keeps E <= 16 and E * K <= 16384 (E = rows per group rounded up to a
+    power of two; K <= 4096).  Among those splits and 1, 2 or 4 strips per
+    workgroup: the fewest rounds * (rows * K * 4 + S * K * 16) bytes, rounds
+    = ceil(workgroups / 256), fewer rows per group on a tie."""
     if K > 4096:
-        return 0
-    for rmax in (8, 16):
-        for g in (1, 2, 4, 8):
-            r = -(-M // g)
-            e = 1 << max(0, (r - 1).bit_length())
-            if e <= rmax and e * K <= 16384:
-                return g
-    return 0
+        return None
+    best = None
+    for g in (1, 2, 4, 8):
+        r = -(-M // g)
+        e = 1 << max(0, (r - 1).bit_length())
+        if e > 16 or e * K > 16384:
+            continue
+        groups = -(-M // r)
+        for s in (1, 2, 4):
+            wgs = -(-NS // s) * groups
+            key = (-(-wgs // 256) * (r * K * 4 + s * K * 16), e)
+            if best is None or key < best[0]:
+                best = (key, groups, s)
+    return None if best is None else best[1:]
+
+
+def _dynamic_variant(M, K, NS, grouped=False):
+    shape = _dynamic_shape(M, K, NS)
+    if shape is None:
+        return None
+    groups, s = shape
+    suffix = "" if s == 1 else "_s%d" % s
+    if grouped:
+        return "int8_dynamic_grouped" + suffix
+    return ("int8_dynamic_m16" if groups == 1 else "int8_dynamic_groups") + suffix
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 1024, 2048), (16, 1024, 1024), (32, 3072, 1024), (16, 2048, 1024),
@@ -497,7 +517,9 @@ def _dynamic_groups(M, K):
                                    (80, 256, 130), (16, 64, 16), (32, 1024, 64), (20, 512, 40), (5, 4096, 48),
                                    (2, 2048, 33), (1, 4000, 20), (9, 3000, 16), (4, 4096, 40), (6, 2048, 24),
                                    (32, 1024, 2048), (32, 2048, 1024), (31, 1024, 96), (25, 2048, 40),
-                                   (18, 3000, 64), (12, 3072, 48)])
+                                   (18, 3000, 64), (12, 3072, 48),
+                                   # several strips per workgroup, ragged last workgroups
+                                   (1, 1024, 6000), (8, 1024, 6144), (24, 1024, 3000), (32, 1024, 4000)])
 def test_dynamic_matches_two_step_and_oracle(q, orc, M, K, N):
     """int8_gemm_dynamic == quantize_rows_int8 + int8_gemm bit for bit (fp32
     output, quantised rows, row scales), and the oracle's int32 product."""
@@ -517,11 +539,9 @@ def test_dynamic_matches_two_step_and_oracle(q, orc, M, K, N):
     xq = torch.full((M, K), 99, dtype=torch.int8, device=dev)
     rs = torch.full((M,), -1.0, dtype=torch.float32, device=dev)
     q.int8_gemm_dynamic(Xd, p, out_f32=y, out_i32=y32, xq_out=xq, rs_out=rs)
-    groups = _dynamic_groups(M, K)
-    if groups == 1:
-        assert q.last_variant() == "int8_dynamic_m16"
-    elif groups > 1:
-        assert q.last_variant() == "int8_dynamic_groups"
+    want = _dynamic_variant(M, K, -(-N // 16))
+    if want is not None:
+        assert q.last_variant() == want
     elif M <= 16:
         assert q.last_variant() == "int8_decode_m16"
     elif M <= 32:
@@ -571,7 +591,7 @@ def test_dynamic_rounding_near_ties(q, orc, M, K):
     xq = torch.full((M, K), 99, dtype=torch.int8, device=torch_dev())
     rs = torch.full((M,), -1.0, dtype=torch.float32, device=torch_dev())
     q.int8_gemm_dynamic(to_dev(X), p, out_f32=y, xq_out=xq, rs_out=rs)
-    assert q.last_variant() == ("int8_dynamic_m16" if _dynamic_groups(M, K) == 1 else "int8_dynamic_groups")
+    assert q.last_variant() == _dynamic_variant(M, K, 2)
     Qa, sa = orc.quantize_rows_int8(X)
     assert np.array_equal(to_np(rs).view(np.uint32), sa.view(np.uint32))
     got = to_np(xq)
@@ -628,12 +648,16 @@ def _np_product(A, B):
 # ------------------------------------------------ grouped dynamic decode ---
 
 @pytest.mark.parametrize("M,K,Ns,variant", [
-    (1, 1024, (2048, 1024, 1024), "int8_dynamic_grouped"),     # q, k, v
-    (16, 1024, (3072, 3072), "int8_dynamic_grouped"),          # gate, up (two row groups)
-    (32, 1024, (2048, 1024, 1024), "int8_dynamic_grouped"),    # four row groups
-    (5, 96, (17, 300, 1, 40), "int8_dynamic_grouped"),         # ragged K and N, four items
-    (32, 3072, (1024, 16), "int8_dynamic_grouped"),            # eight row groups
-    (40, 1024, (2048, 1024), "int8_dynamic_grouped"),          # eight row groups of 5 rows
+    (1, 1024, (2048, 1024, 1024), None),     # q, k, v
+    (16, 1024, (3072, 3072), None),          # gate, up: two row groups, 4 strips per workgroup
+    (32, 1024, (2048, 1024, 1024), None),    # four row groups, 4 strips per workgroup
+    (1, 1024, (3072, 3072), None),           # 2 strips per workgroup
+    (5, 96, (17, 300, 1, 40), None),         # ragged K and N, four items
+    (32, 3072, (1024, 16), None),            # eight row groups, a last workgroup of one strip
+    (40, 1024, (2048, 1024), None),          # eight row groups of 5 rows
+    (32, 1024, (1040, 48, 1008, 17), None),  # items' strips straddle workgroups of 4 strips
+    (3, 2048, (4096, 1000), None),           # odd strip count, 2 strips per workgroup
+    (32, 2048, (1024,), None),               # one item, 2 strips per workgroup
     (4, 5120, (1024, 48), "int8_decode_m16"),                  # K > 4096: quantise once, then a product each
     (200, 256, (2048, 1024), "int8_prefill_256x128"),          # too many rows: the same two-step form
 ])
@@ -652,7 +676,7 @@ def test_dynamic_grouped_matches_separate_calls(q, orc, M, K, Ns, variant):
     Xd = to_dev(X)
     outs = [torch.full((M, n + 3), float("nan"), dtype=torch.float32, device=dev)[:, :n] for n in Ns]
     q.int8_gemm_dynamic_grouped(Xd, pks, outs=outs, biases=biases, scale=0.5)
-    assert q.last_variant() == variant
+    assert q.last_variant() == (variant or _dynamic_variant(M, K, sum(-(-n // 16) for n in Ns), grouped=True))
     Qa, sa = orc.quantize_rows_int8(X)
     for W, pk, b, Y in zip(Ws, pks, biases, outs):
         n = pk.N
