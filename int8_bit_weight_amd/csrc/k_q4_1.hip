@@ -991,45 +991,30 @@ __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ p
 //     zero piece) against the record's m values, accumulated into y;
 //   * the epilogue undoes the token's scale: Y = y * 2^-sc[t].
 // Rows past the chunk repeat its last row (their outputs are not stored);
-// blocks past K read the last block (their d = m = 0).  Both row tiles are
-// multiplied even when the chunk has at most 16 rows: no branch may sit
-// between an MFMA and the VALU instructions that read its result.  A VALU
-// read of an MFMA destination needs wait states the hardware does not
-// enforce (the compiler emits 8 for v_mfma_f32_16x16x32_f16 on straight-line
-// code), and with a wave-uniform branch skipping the second tile, the built
-// code read the first tile's accumulator one instruction after its MFMA on
-// the branch-taken path (the wait was only on the fall-through path), so
-// every chunk of <= 16 rows summed stale accumulator registers.
-template <int MT, int WAVES, int C, int MINW, bool PER_SLOT>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_moe(Q4Params p) {
-    constexpr int ROWS = MT * 16, SPG = WAVES * C;
+// blocks past K read the last block (their d = m = 0).  A chunk of <= 16
+// rows runs a one-tile copy of the whole job, chosen at kernel entry; inside
+// a copy every tile is multiplied: no branch may sit between an MFMA and the
+// VALU instructions that read its result.  A VALU read of an MFMA
+// destination needs wait states the hardware does not enforce (the compiler
+// emits 8 for v_mfma_f32_16x16x32_f16 on straight-line code), and with a
+// wave-uniform branch skipping the second tile's MFMAs, the built code read
+// the first tile's accumulator one instruction after its MFMA on the
+// branch-taken path (the wait was only on the fall-through path), so every
+// chunk of <= 16 rows summed stale accumulator registers.
+// One job's product with MT 16-row tiles.
+template <int MT, int WAVES, int C, bool PER_SLOT>
+__device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t *sS1, const int *sTok,
+                                        const int64_t *sYoff, const int *sYexp, int sg, int expert, int nrows) {
+    constexpr int SPG = WAVES * C;
     constexpr int NFD = 4 * 2 * MT;  // d-term fragments per chunk: block x term x tile
     constexpr int NFM = 3 * MT;      // m-term fragments: term x tile
     constexpr int FPW = (NFD + NFM + WAVES - 1) / WAVES;  // fragments copied per wavefront
-    // stage = the chunk's fragments: d term [block][term][tile], then m term [term][tile]
-    __shared__ __attribute__((aligned(16))) uint8_t sS0[NFD + NFM][1024], sS1[NFD + NFM][1024];
-    __shared__ int sTok[ROWS];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int groups = (p.NS + SPG - 1) / SPG;
-    const int sg = blockIdx.x % groups;
-    const int job = blockIdx.x / groups;
-    if (job >= *p.nchunks) return;
-    const int expert = p.chunk_info[job * 3 + 0];
-    const int row0 = p.chunk_info[job * 3 + 1];
-    const int nrows = p.chunk_info[job * 3 + 2];
     const uint8_t *hdr = p.recs + (int64_t)expert * p.expert_stride;
     const uint8_t *recs = hdr + kHeaderBytes;
     const int NQ = p.NQ;
-    // activation row of each row of the chunk: the token (shared form) or the
-    // (token, slot) pair itself (per-slot form)
-    if (tid < ROWS) {
-        const int pair = p.sorted[row0 + min(tid, nrows - 1)];
-        sTok[tid] = PER_SLOT ? pair : pair / p.n_used;
-    }
-    __syncthreads();
 
     // ---- gather sources: fragment f = wave + WAVES i of the stage (clamped:
     // the wavefronts with fewer fragments store the last one again, the same
@@ -1069,7 +1054,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
     };
     auto fstore = [&](auto ST) {
         constexpr int st = decltype(ST)::value;
-        uint8_t *base = st == 0 ? &sS0[0][0] : &sS1[0][0];
+        uint8_t *base = st == 0 ? sS0 : sS1;
 #pragma unroll
         for (int i = 0; i < FPW; ++i) *(v4i *)(base + foff[i] + a_off) = fr[i];
     };
@@ -1102,7 +1087,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         fload(q + 1);
         gload_rec(q + 1, bc[st ^ 1], bd[st ^ 1]);
-        const uint8_t *A = st == 0 ? &sS0[0][0] : &sS1[0][0];
+        const uint8_t *A = st == 0 ? sS0 : sS1;
         const uint8_t *Mf = A + NFD * 1024;
 #pragma unroll
         for (int bl = 0; bl < 4; ++bl) {
@@ -1171,19 +1156,66 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int j = 0; j < C; ++j)
+        for (int v = 0; v < 4; ++v) {
+            const int row = t * 16 + 4 * (lane >> 4) + v;
+            float *yrow = p.Y + sYoff[row];
+            const int ex = sYexp[row];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = t * 16 + 4 * (lane >> 4) + v;
+            for (int j = 0; j < C; ++j) {
                 const int n = (strip_base + j) * 16 + (lane & 15);
-                if (row < nrows && n < p.N) {
-                    const int pair = p.sorted[row0 + row];
-                    const int tk = pair / p.n_used;
-                    const int sl = pair - tk * p.n_used;
-                    p.Y[(int64_t)tk * p.ldy_token + (int64_t)sl * p.ldy_slot + n] =
-                        __builtin_ldexpf(y[t][j][v], -p.xsc[PER_SLOT ? pair : tk]);
-                }
+                if (row < nrows && n < p.N) yrow[n] = __builtin_ldexpf(y[t][j][v], ex);
             }
+        }
+}
+
+
+// The kernel: a job's chunk of <= 16 rows runs the one-tile copy of the
+// product (half the MFMA and VALU work of the two-tile copy), so that the
+// partial chunks, listed last by the routing, fill the tail of the grid.  The
+// copy is chosen at entry, before any MFMA: inside each copy no branch sits
+// between an MFMA and the instructions that read its result.
+template <int WAVES, int C, int MINW, bool PER_SLOT>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_moe(Q4Params p) {
+    constexpr int ROWS = 32, SPG = WAVES * C;
+    constexpr int STAGE = (4 * 2 * 2 + 3 * 2) * 1024;  // the two-tile copy's fragments
+    // stage = the chunk's fragments: d term [block][term][tile], then m term [term][tile]
+    __shared__ __attribute__((aligned(16))) uint8_t sS0[STAGE], sS1[STAGE];
+    __shared__ int sTok[ROWS];
+    __shared__ int64_t sYoff[ROWS];  // output row of each chunk row (token, slot)
+    __shared__ int sYexp[ROWS];      // -sc of its activation row
+
+    const int tid = threadIdx.x;
+    const int groups = (p.NS + SPG - 1) / SPG;
+    // Workgroup ids go round-robin over the 8 XCDs (each with its own L2):
+    // workgroup b runs on XCD b % 8, which takes chunks x, x + 8, x + 16, ...
+    // and all strip groups of each of them, one after another, so that a
+    // chunk's activation pieces are fetched into one L2 and read there by
+    // every strip group.  Chunks keep the routing table's order (full chunks
+    // first) across the XCDs.
+    const int x = blockIdx.x % 8, l = blockIdx.x / 8;
+    const int sg = l % groups;
+    const int job = (l / groups) * 8 + x;
+    if (job >= *p.nchunks) return;
+    const int expert = __builtin_amdgcn_readfirstlane(p.chunk_info[job * 3 + 0]);
+    const int row0 = __builtin_amdgcn_readfirstlane(p.chunk_info[job * 3 + 1]);
+    const int nrows = __builtin_amdgcn_readfirstlane(p.chunk_info[job * 3 + 2]);
+    // activation row of each row of the chunk: the token (shared form) or the
+    // (token, slot) pair itself (per-slot form); for the epilogue its output
+    // row and scale exponent (one division per row here rather than per
+    // output element)
+    if (tid < ROWS) {
+        const int pair = p.sorted[row0 + min(tid, nrows - 1)];
+        const int tk = pair / p.n_used;
+        const int sl = pair - tk * p.n_used;
+        sTok[tid] = PER_SLOT ? pair : tk;
+        sYoff[tid] = (int64_t)tk * p.ldy_token + (int64_t)sl * p.ldy_slot;
+        sYexp[tid] = -p.xsc[PER_SLOT ? pair : tk];
+    }
+    __syncthreads();
+    if (nrows <= 16)
+        moe_job<1, WAVES, C, PER_SLOT>(p, sS0, sS1, sTok, sYoff, sYexp, sg, expert, nrows);
+    else
+        moe_job<2, WAVES, C, PER_SLOT>(p, sS0, sS1, sTok, sYoff, sYexp, sg, expert, nrows);
 }
 
 // ------------------------------------------------------ MoE routing sort ---
@@ -1523,11 +1555,12 @@ hipError_t launch_q4_moe(const Q4Params &p, bool per_slot, int64_t max_chunks, h
     constexpr int WAVES = 8, C = 2;
     const int64_t groups = ceil_div(p.NS, C * WAVES);
     *variant = "q4_moe_m32";
-    const dim3 g((unsigned)(groups * max_chunks)), b(WAVES * 64);
+    // 8 XCDs x groups x (chunk slots per XCD)
+    const dim3 g((unsigned)(8 * groups * ceil_div(max_chunks, 8))), b(WAVES * 64);
     if (per_slot)
-        hipLaunchKernelGGL((k_q4_moe<2, WAVES, C, 4, true>), g, b, 0, s, p);
+        hipLaunchKernelGGL((k_q4_moe<WAVES, C, 4, true>), g, b, 0, s, p);
     else
-        hipLaunchKernelGGL((k_q4_moe<2, WAVES, C, 4, false>), g, b, 0, s, p);
+        hipLaunchKernelGGL((k_q4_moe<WAVES, C, 4, false>), g, b, 0, s, p);
     return hipGetLastError();
 }
 
