@@ -46,11 +46,11 @@ PROBE_BYTES = 1 << 30
 # HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
 # of `bench.py --probe` (FETCH_SIZE, then WRITE_SIZE; mean over the step's 336
 # decode launches): FETCH_SIZE x 2.0, the factor the probe's plain read of
-# 1 GiB gives in the same run (524306 KiB), plus WRITE_SIZE x 1.0, the factor
+# 1 GiB gives in the same run (524311 KiB), plus WRITE_SIZE x 1.0, the factor
 # the 1 GiB fill of the probe buffer gives (1048576 KiB).  Valid only for the
 # kernel sources it was taken on.
-MEASURED_TRAFFIC = {"sources_sha1": "3233edc8bf65b59f20cad6c4e60ed15091d1e6a5",
-                    "bytes_per_launch": round((2454.5 * 2.0 + 196.0) * 1024)}
+MEASURED_TRAFFIC = {"sources_sha1": "bd18d8f325717ee97c3fa68a2054b141f5403d9c",
+                    "bytes_per_launch": round((2445.3 * 2.0 + 196.0) * 1024)}
 
 
 def decode_sources_sha1():
@@ -84,14 +84,18 @@ def parse_args():
                     help="counter probe: one plain read of 1 GiB (the calibration read), then one eager step")
     ap.add_argument("--profile", action="store_true",
                     help="the timed leg alone (setup, graph capture, warm-up and timed replays)")
-    ap.add_argument("--profile-leg", choices=("decode", "prefill"), default="decode",
-                    help="--profile: the decode step (default) or the M = 2048 prefill shapes, each warmed up "
-                         "and then launched --steps times in a row")
+    ap.add_argument("--profile-leg", choices=("decode", "prefill", "q4"), default="decode",
+                    help="--profile: the decode step (default), the M = 2048 prefill shapes (each warmed up "
+                         "and then launched --steps times in a row), or the q4_1 calls (M = 1 and 16 on both "
+                         "shapes, then MUL_MAT_ID in both forms) over rings of weight copies")
     ap.add_argument("--summarize", metavar="DB", help="summarize a rocprofv3 database (no GPU needed)")
     ap.add_argument("--kernel", default="", help="--summarize: kernel name substring")
     ap.add_argument("--last", type=int, default=0, help="--summarize: only the last N matching dispatches")
     ap.add_argument("--skip", type=int, default=0, help="--summarize: leave out the first N matching dispatches")
     ap.add_argument("--count", type=int, default=0, help="--summarize: then keep only the next N")
+    ap.add_argument("--cycle", default="",
+                    help="--summarize: LABEL:N,LABEL:N,... the selected dispatches come in repeating runs of "
+                         "these lengths (e.g. 1:112,16:112,32:112 for the decode step's rows); one table per label")
     return ap.parse_args()
 
 
@@ -183,11 +187,12 @@ def cpu_model():
 
 # ------------------------------------------------------------ summarize ---
 
-def summarize(path, pattern, last, skip=0, count=0):
+def summarize(path, pattern, last, skip=0, count=0, cycle=""):
     """Per-kernel duration statistics (and per-dispatch counter means) from a
     rocprofv3 SQLite database, restricted to kernels whose name contains
     `pattern`, past the first `skip` of them, and to the last `last` of those
-    when given."""
+    when given.  `cycle` ("LABEL:N,..."): the selection repeats runs of those
+    lengths; a table per label as well."""
     import sqlite3
     import numpy as np
     db = sqlite3.connect(path)
@@ -201,17 +206,38 @@ def summarize(path, pattern, last, skip=0, count=0):
     print("dispatches: %d in all, %d selected (kernel name contains %r%s%s%s)"
           % (len(rows), len(sel), pattern, ", first %d left out" % skip if skip else "",
              ", the next %d" % count if count else "", ", last %d" % last if last else ""))
-    by = {}
-    for did, name, _, dur in sel:
-        by.setdefault(name, []).append(dur)
-    print("| kernel | launches | mean us | median us | p10 us | p90 us | min us | max us | total ms |")
-    print("|---|---|---|---|---|---|---|---|---|")
-    for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
-        a = np.array(d, dtype=np.float64) * 1e-3
-        short = name.split("(")[0] if not name.startswith("void ") else name[5:].split("(Int8")[0].split("(qmm")[0]
-        print("| %s | %d | %.3f | %.3f | %.3f | %.3f | %.3f | %.3f | %.3f |"
-              % (short[-70:], a.size, a.mean(), np.median(a), np.percentile(a, 10), np.percentile(a, 90), a.min(),
-                 a.max(), a.sum() * 1e-3))
+    def table(rows_):
+        by = {}
+        for did, name, _, dur in rows_:
+            by.setdefault(name, []).append(dur)
+        print("| kernel | launches | mean us | median us | p10 us | p90 us | min us | max us | total ms |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+            a = np.array(d, dtype=np.float64) * 1e-3
+            short = name.split("(")[0] if not name.startswith("void ") else name[5:].split("(Int8")[0].split("(qmm")[0]
+            print("| %s | %d | %.3f | %.3f | %.3f | %.3f | %.3f | %.3f | %.3f |"
+                  % (short[-70:], a.size, a.mean(), np.median(a), np.percentile(a, 10), np.percentile(a, 90),
+                     a.min(), a.max(), a.sum() * 1e-3))
+        if rows_:
+            a = np.array([r[3] for r in rows_], dtype=np.float64) * 1e-3
+            print("| (all selected) | %d | %.3f | %.3f | %.3f | %.3f | %.3f | %.3f | %.3f |"
+                  % (a.size, a.mean(), np.median(a), np.percentile(a, 10), np.percentile(a, 90), a.min(), a.max(),
+                     a.sum() * 1e-3))
+    table(sel)
+    if cycle:
+        runs = [(lab, int(n)) for lab, n in (c.split(":") for c in cycle.split(","))]
+        period = sum(n for _, n in runs)
+        groups = {lab: [] for lab, _ in runs}
+        for i, r in enumerate(sel):
+            pos = i % period
+            for lab, n in runs:
+                if pos < n:
+                    groups[lab].append(r)
+                    break
+                pos -= n
+        for lab, _ in runs:
+            print("\n%s (%d dispatches):" % (lab, len(groups[lab])))
+            table(groups[lab])
     ids = {r[0] for r in sel}
     try:
         crows = list(db.execute("select dispatch_id, counter_name, sum(value) from counters_collection "
@@ -235,7 +261,7 @@ def summarize(path, pattern, last, skip=0, count=0):
 def main() -> int:
     args = parse_args()
     if args.summarize:
-        return summarize(args.summarize, args.kernel, args.last, args.skip, args.count)
+        return summarize(args.summarize, args.kernel, args.last, args.skip, args.count, args.cycle)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)." % args.gpus, file=sys.stderr)
@@ -250,6 +276,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.profile and args.profile_leg == "prefill":
         return profile_prefill(args, q, wl, torch, np, dev)
+    if args.profile and args.profile_leg == "q4":
+        return profile_q4(args, q, wl, torch, np, dev)
     layers = args.layers or wl.QWEN3_0_6B_LAYERS
     projs = wl.QWEN3_0_6B_PROJECTIONS
     rows = wl.DECODE_ROWS
@@ -442,6 +470,58 @@ def profile_prefill(args, q, wl, torch, np, dev):
     return 0
 
 
+def q4_moe_bytes(wl, E, K, N, X, Y):
+    """Algorithmic bytes of one MUL_MAT_ID call: every expert's codes and
+    bf16 (d, m) per block, the activations, the id rows and the outputs."""
+    wb = E * (K * N // 2 + (K // 32) * N * 4)
+    return wb + X.numel() * 4 + wl.MOE_TOKENS * wl.MOE_IDS_STRIDE * 4 + Y.numel() * 4
+
+
+def profile_q4(args, q, wl, torch, np, dev):
+    """The q4_1 calls alone, eager, in order (for rocprofv3 counters and
+    traces): per shape of the q4_1 product and per M in (1, 16), one call on
+    each of 16 weight copies (~590 MB, past the 256 MB Infinity Cache); then
+    MUL_MAT_ID in the shared and the per-slot form, 2 x 4 calls over 4
+    copies of the experts."""
+    res = {}
+    for i, (K, N) in enumerate(wl.Q4_SHAPES):
+        _, blocks = wl.q4_weight(K, N, seed_index=i)
+        bd = torch.from_numpy(blocks.reshape(-1)).to(dev)
+        ring = [q.q4_1_repack(bd, K, N) for _ in range(16)]
+        wbytes = ring[0].data.numel() - 64
+        for M in wl.Q4_ROWS:
+            X = torch.from_numpy(wl.q4_activations(M, K, seed_index=i)).to(dev)
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            wsq = q.workspace(q.lib.qmm_q4_1_matmul_workspace_bytes(M, K, N), dev)
+            torch.cuda.synchronize()
+            for W in ring:
+                q.q4_1_matmul(X, W, out=Y, ws=wsq)
+            torch.cuda.synchronize()
+            res["q4_1_%dx%d_m%d" % (K, N, M)] = {"calls": len(ring), "variant": q.last_variant(),
+                                                 "algorithmic_bytes_per_call": wbytes + 4 * M * K + 4 * M * N}
+        del ring, bd
+    for name, inputs, per_slot in (("q4_1_matmul_id", wl.moe_inputs, False),
+                                   ("q4_1_matmul_id_per_slot", wl.moe_down_inputs, True)):
+        dm = inputs()
+        E = wl.MOE_EXPERTS
+        K, N = (wl.MOE_DOWN_K, wl.MOE_DOWN_N) if per_slot else (wl.MOE_K, wl.MOE_N)
+        ed = torch.from_numpy(dm["experts"]).to(dev)
+        rings = [q.q4_1_repack_experts(ed, K, N) for _ in range(4)]
+        X = torch.from_numpy(dm["X"]).to(dev)
+        ids = torch.from_numpy(dm["ids"]).to(dev)
+        Y = torch.empty((wl.MOE_TOKENS, wl.MOE_USED, N), dtype=torch.float32, device=dev)
+        fn = q.q4_1_matmul_id_per_slot if per_slot else q.q4_1_matmul_id
+        torch.cuda.synchronize()
+        for _ in range(2):
+            for buf, st in rings:
+                fn(X, buf, E, K, N, st, ids, wl.MOE_USED, out=Y)
+        torch.cuda.synchronize()
+        res[name] = {"calls": 2 * len(rings), "algorithmic_bytes_per_call": q4_moe_bytes(wl, E, K, N, X, Y)}
+        del rings, ed
+    print(json.dumps({"profile": "q4", "calls": res}), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------- extras ---
 
 def extras(args, q, wl, torch, np, dev, packed, projs, layers, rows):
@@ -590,8 +670,7 @@ def extras(args, q, wl, torch, np, dev, packed, projs, layers, rows):
                   for buf, st in rings]
         fs[0]()
         t = time_ring(torch, fs * 2)
-        wb = E * (K * N // 2 + (K // 32) * N * 4)     # codes + bf16 (d, m) per block
-        b = wb + X.numel() * 4 + wl.MOE_TOKENS * wl.MOE_IDS_STRIDE * 4 + Y.numel() * 4
+        b = q4_moe_bytes(wl, E, K, N, X, Y)
         extra[name] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
                        "%HBM": round(100 * b / t / 1e9 / HBM_PEAK_GBS, 2), "algorithmic_bytes": b,
                        "experts": E, "K": K, "N": N, "tokens": wl.MOE_TOKENS, "top_k": wl.MOE_USED}

@@ -49,3 +49,23 @@ def test_summarize_restricts_to_the_last_dispatches(tmp_path):
     assert "2 selected" in r.stdout
     assert "| 2 | 9.000 | 9.000 |" in r.stdout
     assert "FETCH_SIZE = 80.0 (2 dispatches)" in r.stdout
+
+
+def test_summarize_cycle_splits_repeating_runs(tmp_path):
+    db = tmp_path / "c.db"
+    c = sqlite3.connect(db)
+    c.execute("create table kernels (dispatch_id int, name text, start int, duration int)")
+    # two steps of (3 launches of label a at 1 us, 2 of label b at 5 us)
+    durs = [1000, 1000, 1000, 5000, 5000] * 2
+    c.executemany("insert into kernels values (?,?,?,?)",
+                  [(i, "void qmm::k_int8_decode_q<1>(x)", i * 100, d) for i, d in enumerate(durs)])
+    c.commit()
+    c.close()
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize", str(db), "--kernel",
+                        "k_int8_decode_q", "--cycle", "a:3,b:2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    out = r.stdout
+    assert "a (6 dispatches):" in out and "b (4 dispatches):" in out
+    a_part = out.split("a (6 dispatches):")[1].split("b (4 dispatches):")[0]
+    assert "| (all selected) | 6 | 1.000 |" in a_part
+    assert "| (all selected) | 4 | 5.000 |" in out.split("b (4 dispatches):")[1]
