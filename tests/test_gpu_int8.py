@@ -233,6 +233,38 @@ def test_wide_decode_dynamic(q, orc, M):
 
 # ------------------------------------------------ per-axis zero points ---
 
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_wide_and_per_strip_forms_agree_bit_for_bit(q, M):
+    """One int8_gemm_dynamic call over 1040 strips (the wide form: the row
+    quantiser, then one wavefront per strip) gives, bit for bit, the fp32
+    outputs of per-strip calls on column slices of the same weight (the fused
+    quantising form at 128 and 96 strips, and the grouped form over the
+    slices): per-column packing makes a slice's codes, scales and column sums
+    those of the whole, and every form rounds the same epilogue chain."""
+    import torch
+    dev = torch_dev()
+    K, N = 1024, 16640
+    g = np.random.default_rng(900 + M)
+    W = wl.normal_f32(g, (K, N), 0.02)
+    X = wl.normal_f32(g, (M, K))
+    Xd = to_dev(X)
+    whole = q.pack_b_int8(to_dev(W))
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q.int8_gemm_dynamic(Xd, whole, out_f32=y)
+    assert q.last_variant().startswith("int8_decode_wide")
+    cuts = [0, 2048, 3584]
+    parts = [q.pack_b_int8(to_dev(np.ascontiguousarray(W[:, a:b]))) for a, b in zip(cuts[:-1], cuts[1:])]
+    for (a, b), pk in zip(zip(cuts[:-1], cuts[1:]), parts):
+        ys = torch.empty((M, b - a), dtype=torch.float32, device=dev)
+        q.int8_gemm_dynamic(Xd, pk, out_f32=ys)
+        assert q.last_variant().startswith("int8_dynamic"), q.last_variant()
+        assert np.array_equal(to_np(ys).view(np.uint32), to_np(y[:, a:b]).view(np.uint32)), (a, b)
+    outs = q.int8_gemm_dynamic_grouped(Xd, parts)
+    assert q.last_variant().startswith("int8_dynamic_grouped")
+    for (a, b), ys in zip(zip(cuts[:-1], cuts[1:]), outs):
+        assert np.array_equal(to_np(ys).view(np.uint32), to_np(y[:, a:b]).view(np.uint32)), (a, b)
+
+
 def _axis_case(q, orc, M, K, N, a_u8, b_u8, seed, expect_variant, zx=None, zw=None, zy=None):
     """The fused QDQ group with per-axis parameters: int8/uint8 activations
     and weights as given, a zero point and a scale per activation row and per
