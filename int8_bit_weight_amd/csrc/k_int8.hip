@@ -29,6 +29,45 @@ __device__ __forceinline__ float wave_max_f(float v) {
     return v;
 }
 
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float x) {
+    // rows outside ROWS keep x
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                                                 CTRL, ROWS, 0xF, false));
+}
+
+// Maximum over each group of L consecutive lanes (L a power of two <= 64),
+// in every lane of the group, with DPP lane moves (VALU; no LDS round trip,
+// as __shfl_xor's ds_bpermute takes): quad permutations [1,0,3,2] and
+// [2,3,0,1] and the half-row and row mirrors leave every lane of a group of
+// 2, 4, 8, 16 with its maximum; the row broadcasts of lanes 15 and 31 carry
+// it into lanes 31 and 63, read back with readlane.  (The permlane16/32
+// swap builtins were not usable here: with both operands the same value the
+// compiler took the swap's first result for both.)
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "L is a power of two <= 64");
+    if constexpr (L >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
+    if constexpr (L >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
+    if constexpr (L >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+    if constexpr (L >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+    if constexpr (L >= 32) {
+        // rows 1 and 3 take the maximum with lane 15 of the row before: lanes
+        // 31 and 63 then hold their 32-lane half's maximum
+        v = fmaxf(v, dpp_f<0x142, 0xA>(v));
+        if constexpr (L == 32) {
+            const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+            const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+            v = (threadIdx.x & 63) < 32 ? lo : hi;
+        } else {
+            // rows 2 and 3 take the maximum with lane 31: lane 63 holds the wave's
+            v = fmaxf(v, dpp_f<0x143, 0xC>(v));
+            v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+        }
+    }
+    return v;
+}
+
 // Symmetric int8 code of x for scale s (s > 0): clamp(rne(x / s), -127, 127).
 // The division is IEEE correctly rounded (hipcc's default for fp32 '/').
 __device__ __forceinline__ int quant_code(float x, float s) {
@@ -510,15 +549,17 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupA
     __shared__ __attribute__((aligned(16))) float s_amax[E][WAVES];  // [row][wave]
     __shared__ float s_scale[E];
     __shared__ __attribute__((aligned(16))) int8_t s_q[TPQ * WAVES][E][64];  // [k tile][row][k]
-    __shared__ int32_t s_red[WAVES][E][17];
+    // partial tiles, [row][column][wave]: a strip's waves are contiguous, so
+    // an output's sum reads them with 16-byte loads (the row pitch of 20
+    // keeps those loads aligned)
+    __shared__ __attribute__((aligned(16))) int32_t s_red[E][16][WAVES + 4];
 
     float a = 0.0f;
 #pragma unroll
     for (int t = 0; t < TPQ; ++t)
 #pragma unroll
         for (int j = 0; j < E; ++j) a = fmaxf(a, fabsf(x[t][j]));
-#pragma unroll
-    for (int o = 1; o < L; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+    a = group_max<L>(a);
     if (lane % L == 0) s_amax[m][wave] = a;
     __syncthreads();
     a = 0.0f;
@@ -591,18 +632,23 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupA
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * (lane >> 4) + i;
-        if (r < E) s_red[wave][r][lane & 15] = acc[i];
+        if (r < E) s_red[r][lane & 15][wave] = acc[i];
     }
     __syncthreads();
     // the strip's outputs: E rows x 16 columns over its WPS wavefronts
+    // (summed in wave order: int32, so the order changes no bit)
     const int n = strip * kTileN + (lane & 15);
     for (int e = kg * 64 + lane; e < E * 16; e += WPS * 64) {
         const int mo = e >> 4;
         if (strip_ok && mo < p.M && n < p.N) {
-            int32_t v = 0;
+            const int32_t *src = &s_red[mo][e & 15][slot * WPS];
+            uint32_t v = 0u;  // wrapping int32 sum
 #pragma unroll
-            for (int ww = 0; ww < WPS; ++ww) v += s_red[slot * WPS + ww][mo][e & 15];
-            epilogue_store_c(p, mo, n, (uint32_t)v, 0, false, s_scale[mo], 0, col);
+            for (int ww = 0; ww < WPS; ww += 4) {
+                const v4i t = *(const v4i *)(src + ww);
+                v += ((uint32_t)t[0] + (uint32_t)t[1]) + ((uint32_t)t[2] + (uint32_t)t[3]);
+            }
+            epilogue_store_c(p, mo, n, v, 0, false, s_scale[mo], 0, col);
         }
     }
 }

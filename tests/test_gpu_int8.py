@@ -632,6 +632,38 @@ def test_dynamic_rounding_near_ties(q, orc, M, K):
     assert np.array_equal(to_np(Xq2), Qa)
 
 
+@pytest.mark.parametrize("M,N,E", [(1, 64, 1), (4, 2048, 2), (16, 1024, 4), (16, 4096, 8), (32, 4096, 8)])
+def test_dynamic_row_max_at_every_lane_position(q, orc, M, N, E):
+    """The fused quantiser's row maximum combines every lane and wavefront.
+    Row groups of E rows (rounded up to a power of two) keep 64 / E lanes per
+    row; each row's largest |x| is placed, over 64 calls, at every offset of a
+    64-k tile (so at every lane of its row and every one of the E values a
+    lane holds) and in every one of the 16 wavefronts' tiles (values
+    elsewhere at most a quarter of it).  The row scales and codes must equal
+    the oracle's bit for bit."""
+    import torch
+    dev = torch_dev()
+    K = 1024
+    groups, _ = _dynamic_shape(M, K, N // 16)
+    rows = -(-M // groups)
+    assert 1 << max(0, (rows - 1).bit_length()) == E
+    g = np.random.default_rng(300 + M + N)
+    p = q.pack_b_int8(to_dev(wl.normal_f32(g, (K, N), 0.02)))
+    for trial in range(64):
+        X = (g.uniform(-0.25, 0.25, (M, K))).astype(np.float32)
+        for m in range(M):
+            k = (trial + 11 * m) % 64 + 64 * ((trial + 3 * m) % 16)
+            X[m, k] = np.float32(1.0 if (trial + m) % 2 == 0 else -1.0) * np.float32(1.0 + 0.125 * m)
+        xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        rs = torch.empty((M,), dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        q.int8_gemm_dynamic(to_dev(X), p, out_f32=y, xq_out=xq, rs_out=rs)
+        assert q.last_variant() == _dynamic_variant(M, K, N // 16)
+        Qa, sa = orc.quantize_rows_int8(X)
+        assert np.array_equal(to_np(rs).view(np.uint32), sa.view(np.uint32)), trial
+        assert np.array_equal(to_np(xq), Qa), trial
+
+
 def test_dynamic_without_side_outputs(q, orc):
     import torch
     W = wl.projection_weight(1, 6)
