@@ -825,8 +825,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
         for (int j = 0; j < C; ++j) {
             const int strip = min(strip_base + j, p.NS - 1);
             const uint8_t *rec = recs + ((int64_t)strip * p.NQ + qq) * kQ4RecBytes;
-            dc[j] = *(const v4i *)(rec + (uint32_t)lane * 16u);
-            dd[j] = *(const v4i *)(q0 + q < q1 ? rec + 1024 + (uint32_t)(lane & 15) * 16u : hdr + kHeaderBytes - 16);
+            // non-temporal: each record is read once (measured 4 % faster
+            // at M = 16; the hint made the M = 1 kernels no faster)
+            dc[j] = __builtin_nontemporal_load((const v4i *)(rec + (uint32_t)lane * 16u));
+            dd[j] = __builtin_nontemporal_load((const v4i *)(q0 + q < q1 ? rec + 1024 + (uint32_t)(lane & 15) * 16u : hdr + kHeaderBytes - 16));
         }
     };
 #pragma unroll
@@ -1068,6 +1070,8 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
         for (int j = 0; j < C; ++j) {
             const int strip = min(strip_base + j, p.NS - 1);
             const uint8_t *rec = recs + ((int64_t)strip * NQ + qq) * kQ4RecBytes;
+            // plain loads (no non-temporal hint): an expert split into two
+            // chunks reads its records twice, the second time from cache
             dc[j] = *(const v4i *)(rec + (uint32_t)lane * 16u);
             dd[j] = *(const v4i *)(q < NQ ? rec + 1024 + (uint32_t)(lane & 15) * 16u : hdr + kHeaderBytes - 16);
         }
