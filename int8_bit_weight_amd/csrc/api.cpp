@@ -320,14 +320,16 @@ static bool dynamic_fused(int64_t M, int64_t K, int64_t N) {
 // Shape of the fused launch: rows per row group and 16-column strips per
 // workgroup (S = 1, 2, 4; the S strips share one quantisation of the rows).
 // A workgroup reads rows * K * 4 bytes of activations (from L2) and
-// S * K * 16 bytes of weights; with one workgroup per CU resident at a time
-// (16 wavefronts), the call costs about rounds * (those bytes), rounds =
-// ceil(workgroups / 256 CUs).  The split with the fewest such bytes is
-// taken, fewer rows per group on a tie (less quantisation per workgroup).
-// On MI355X this picked the fastest of all splits for every Qwen3-0.6B
-// projection group at M = 1, 16 and 32 (the grouped q/k/v call at M = 32:
-// 4 groups of 8 rows, 4 strips per workgroup, 5.9 us against 9.7 us for one
-// strip per workgroup).
+// S * K * 16 bytes of weights; the call costs about rounds * (those bytes),
+// rounds = ceil(workgroups / 256 CUs).  The split with the fewest such bytes
+// is taken, fewer rows per group on a tie (less quantisation per
+// workgroup).  On MI355X this picked the fastest of all splits for every
+// Qwen3-0.6B projection group at M = 1, 16 and 32, with workgroups of 16
+// wavefronts and of 8 (the grouped q/k/v call at M = 32: 4 groups of 8 rows,
+// 4 strips per workgroup, 5.3 us with 8 wavefronts against 9.7 us for one
+// strip per 16-wavefront workgroup; counting 512 workgroups per round, as
+// two 8-wavefront workgroups fit a CU, picked slower splits in 8 of 12
+// cases).
 struct DynShape {
     int64_t rows;  // rows per group (= M: one group)
     int spw;       // strips per workgroup
@@ -395,9 +397,8 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
         e2.row_scale = rs;
         return int8_gemm(q, QMM_S8, M, K, lq, 0, packedB, QMM_S8, N, 0, &e2, nullptr, 0, stream);
     }
-    // 16 wavefronts with up to 4 k tiles each: one round covers K <= 4096,
-    // so the activations stay in registers between the amax and quantise
-    // passes.
+    // one round of the workgroup's wavefronts covers K <= 4096, so the
+    // activations stay in registers between the amax and quantise passes
     const DynShape ds = dynamic_shape(M, K, packed_b_layout(K, N).NS);
     const int64_t rows = ds.rows;
     Int8Plan plan = plan_int8_gemm(rows, K, N, false);

@@ -444,16 +444,18 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide(Int8GemmPa
 // Fused dynamic quantisation for small M x K (the planner takes it while
 // E * K <= 16384, E = rows of a row group rounded up to a power of two <= 16,
 // and K <= 4096; row groups run as the grid's second dimension).  A
-// workgroup of 16 wavefronts covers S consecutive 16-column strips:
-//   1. every wavefront loads the activations of its k tiles (tile t belongs
-//      to wave t % 16; E / 64 lanes per row, E values per lane and tile, so
-//      every lane does real work even at M = 1), then its weight tiles;
-//   2. row maxima combine across the lanes of a row (shuffles) and the
+// workgroup of kDynWaves (8) wavefronts covers S consecutive 16-column
+// strips:
+//   1. every wavefront loads the activations of its TPQ k tiles (tile t
+//      belongs to wave t % 8; 64 / E lanes per row, E values per lane and
+//      tile, so every lane does real work even at M = 1; at most 32 values
+//      per lane), then its weight tiles;
+//   2. row maxima combine across the lanes of a row (DPP lane moves) and the
 //      waves (LDS, one barrier); each lane forms its row's scale amax/127 and
 //      quantises its values with the k_quantize_rows rule into an LDS copy of
 //      the rows' codes, laid out as MFMA A operands (E rows of 64 bytes per
 //      k tile);
-//   3. the 16 / S wavefronts of a strip take its k tiles round-robin, one
+//   3. the 8 / S wavefronts of a strip take its k tiles round-robin, one
 //      16x16x64 MFMA per tile with A from LDS (rows >= E read as zero);
 //   4. the strip's wavefronts' int32 tiles are summed in LDS and the
 //      epilogue runs in the same workgroup.
@@ -471,13 +473,14 @@ template <bool GROUPED>
 using GroupArg = std::conditional_t<GROUPED, DecodeGroups, NoGroups>;
 
 template <int E, int TPQ, int S, bool AVEC, bool GROUPED>
-__global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupArg<GROUPED> g) {
-    constexpr int WAVES = 16;
+__global__ __launch_bounds__(kDynWaves * 64) void k_int8_decode_q(Int8GemmParams p, GroupArg<GROUPED> g) {
+    constexpr int WAVES = kDynWaves;
     constexpr int WPS = WAVES / S;         // wavefronts per strip
     constexpr int TPB = TPQ * S;           // weight tiles per wavefront (bound)
     constexpr int L = 64 / E;              // lanes per row
     static_assert(E == 1 || E == 2 || E == 4 || E == 8 || E == 16, "E is a power of two <= 16");
-    static_assert(S == 1 || S == 2 || S == 4, "S divides the 16 wavefronts");
+    static_assert(S == 1 || S == 2 || S == 4, "S divides the wavefronts");
+    static_assert(E * TPQ <= 32, "at most 32 activations per lane");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slot = wave / WPS, kg = wave % WPS;
@@ -647,10 +650,15 @@ __global__ __launch_bounds__(1024) void k_int8_decode_q(Int8GemmParams p, GroupA
         if (strip_ok && mo < p.M && n < p.N) {
             const int32_t *src = &s_red[mo][e & 15][slot * WPS];
             uint32_t v = 0u;  // wrapping int32 sum
+            if constexpr (WPS % 4 == 0) {
 #pragma unroll
-            for (int ww = 0; ww < WPS; ww += 4) {
-                const v4i t = *(const v4i *)(src + ww);
-                v += ((uint32_t)t[0] + (uint32_t)t[1]) + ((uint32_t)t[2] + (uint32_t)t[3]);
+                for (int ww = 0; ww < WPS; ww += 4) {
+                    const v4i t = *(const v4i *)(src + ww);
+                    v += ((uint32_t)t[0] + (uint32_t)t[1]) + ((uint32_t)t[2] + (uint32_t)t[3]);
+                }
+            } else {
+#pragma unroll
+                for (int ww = 0; ww < WPS; ++ww) v += (uint32_t)src[ww];
             }
             epilogue_store_c(p, mo, n, v, 0, false, s_scale[mo], 0, col);
         }
@@ -759,7 +767,7 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
 template <int E, int TPQ, int S, bool GROUPED>
 hipError_t launch_dyn(const Int8GemmParams &p, const DecodeGroups &dg, bool avec, hipStream_t s) {
     const unsigned groups = p.rpg > 0 ? (unsigned)((p.M + p.rpg - 1) / p.rpg) : 1u;
-    const dim3 g((unsigned)((p.NS + S - 1) / S), groups), b(1024);
+    const dim3 g((unsigned)((p.NS + S - 1) / S), groups), b(kDynWaves * 64);
     GroupArg<GROUPED> ga{};
     if constexpr (GROUPED) ga = dg;
     if (E >= 4 && avec)
@@ -777,15 +785,21 @@ hipError_t launch_dyn_s(const Int8GemmParams &p, const DecodeGroups &dg, int spw
     return hipErrorInvalidValue;
 }
 
-// E * K <= 16384 (the planner's bound) keeps E * TPQ <= 16.
+// k tiles per wavefront: the power of two >= KT / 8.  The planner's bound
+// E * K <= 16384 keeps E * TPQ <= 32 (for KT in (2^a, 2^(a+1)]: E <= 2^(7-a),
+// TPQ <= 2^(a-2)).
 template <int E, bool GROUPED>
 hipError_t launch_dyn_tpq(const Int8GemmParams &p, const DecodeGroups &dg, int spw, bool avec, hipStream_t s) {
-    if (p.KT <= 16) return launch_dyn_s<E, 1, GROUPED>(p, dg, spw, avec, s);
-    if constexpr (E <= 8) {
-        if (p.KT <= 32) return launch_dyn_s<E, 2, GROUPED>(p, dg, spw, avec, s);
+    constexpr int W = kDynWaves;
+    if (p.KT <= W) return launch_dyn_s<E, 1, GROUPED>(p, dg, spw, avec, s);
+    if constexpr (E * 2 <= 32) {
+        if (p.KT <= 2 * W) return launch_dyn_s<E, 2, GROUPED>(p, dg, spw, avec, s);
     }
-    if constexpr (E <= 4) {
-        if (p.KT <= 64) return launch_dyn_s<E, 4, GROUPED>(p, dg, spw, avec, s);
+    if constexpr (E * 4 <= 32) {
+        if (p.KT <= 4 * W) return launch_dyn_s<E, 4, GROUPED>(p, dg, spw, avec, s);
+    }
+    if constexpr (E * 8 <= 32) {
+        if (p.KT <= 8 * W) return launch_dyn_s<E, 8, GROUPED>(p, dg, spw, avec, s);
     }
     return hipErrorInvalidValue;
 }

@@ -131,6 +131,12 @@ struct DecodeGroups {
     int N[kMaxGroups];
 };
 
+// Wavefronts per workgroup of the fused quantising decode (k_int8_decode_q):
+// measured faster than 16 for every Qwen3-0.6B projection group at M = 1,
+// 16 and 32 (fewer partial tiles to combine and less launch skew before the
+// row-maximum barrier).
+constexpr int kDynWaves = 8;
+
 // The wide decode (one wavefront per strip over the whole k range) stages
 // all of A' in LDS: at most this many 1 KiB operand tiles (k tiles x 16-row
 // tiles), 64 KiB.  It is planned from this many 16-column strips on.
