@@ -333,10 +333,11 @@ static bool dynamic_fused(int64_t M, int64_t K, int64_t N) {
 struct DynShape {
     int64_t rows;  // rows per group (= M: one group)
     int spw;       // strips per workgroup
+    int waves;     // wavefronts per workgroup
 };
 static DynShape dynamic_shape(int64_t M, int64_t K, int64_t NS) {
     constexpr int64_t kCUs = 256;
-    DynShape best{M, 1};
+    DynShape best{M, 1, 8};
     int64_t best_cost = INT64_MAX, best_e = INT64_MAX;
     for (int g : {1, 2, 4, 8}) {
         const int64_t r = (M + g - 1) / g;
@@ -350,10 +351,20 @@ static DynShape dynamic_shape(int64_t M, int64_t K, int64_t NS) {
             if (cost < best_cost || (cost == best_cost && e < best_e)) {
                 best_cost = cost;
                 best_e = e;
-                best = DynShape{r, spw};
+                best = DynShape{r, spw, 8};
             }
         }
     }
+    // 8 wavefronts per workgroup, 4 where K <= 1024, S <= 2 and at least 192
+    // workgroups run (a sweep of 2, 4, 8 and 16 over the Qwen3-0.6B groups:
+    // 4 won exactly those cases, by 0.2-0.5 us, and lost the others) and a
+    // lane's E * TPQ activations (TPQ = k tiles per wavefront, a power of
+    // two >= KT / 4) stay within 32
+    const int64_t wgs = ceil_div(NS, best.spw) * ceil_div(M, best.rows);
+    int64_t e = 1, tpq = 1;
+    while (e < best.rows) e <<= 1;
+    while (tpq * 4 < ceil_div(K, 64)) tpq <<= 1;
+    if (K <= 1024 && best.spw <= 2 && wgs >= 192 && e * tpq <= 32) best.waves = 4;
     return best;
 }
 
@@ -403,6 +414,7 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
     const int64_t rows = ds.rows;
     Int8Plan plan = plan_int8_gemm(rows, K, N, false);
     plan.spw = ds.spw;
+    plan.waves = ds.waves;
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes || !aligned(workspace, 256)))
         return QMM_ERR_WORKSPACE;
     Int8GemmParams p{};
@@ -496,6 +508,7 @@ qmm_status int8_gemm_dynamic_grouped(const float *X, int64_t M, int64_t K, int64
     const int64_t rows = ds.rows;
     Int8Plan plan = plan_int8_gemm(rows, K, 16, false);
     plan.spw = ds.spw;
+    plan.waves = ds.waves;
     Int8GemmParams p{};
     qmm_epilogue e0{};
     e0.outputs = QMM_OUT_F32;

@@ -444,10 +444,10 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide(Int8GemmPa
 // Fused dynamic quantisation for small M x K (the planner takes it while
 // E * K <= 16384, E = rows of a row group rounded up to a power of two <= 16,
 // and K <= 4096; row groups run as the grid's second dimension).  A
-// workgroup of kDynWaves (8) wavefronts covers S consecutive 16-column
-// strips:
+// workgroup of WAVES (8, or 4 where planned) wavefronts covers S consecutive
+// 16-column strips:
 //   1. every wavefront loads the activations of its TPQ k tiles (tile t
-//      belongs to wave t % 8; 64 / E lanes per row, E values per lane and
+//      belongs to wave t % WAVES; 64 / E lanes per row, E values per lane and
 //      tile, so every lane does real work even at M = 1; at most 32 values
 //      per lane), then its weight tiles;
 //   2. row maxima combine across the lanes of a row (DPP lane moves) and the
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide(Int8GemmPa
 //      quantises its values with the k_quantize_rows rule into an LDS copy of
 //      the rows' codes, laid out as MFMA A operands (E rows of 64 bytes per
 //      k tile);
-//   3. the 8 / S wavefronts of a strip take its k tiles round-robin, one
+//   3. the WAVES / S wavefronts of a strip take its k tiles round-robin, one
 //      16x16x64 MFMA per tile with A from LDS (rows >= E read as zero);
 //   4. the strip's wavefronts' int32 tiles are summed in LDS and the
 //      epilogue runs in the same workgroup.
@@ -472,14 +472,14 @@ struct NoGroups {};
 template <bool GROUPED>
 using GroupArg = std::conditional_t<GROUPED, DecodeGroups, NoGroups>;
 
-template <int E, int TPQ, int S, bool AVEC, bool GROUPED>
-__global__ __launch_bounds__(kDynWaves * 64) void k_int8_decode_q(Int8GemmParams p, GroupArg<GROUPED> g) {
-    constexpr int WAVES = kDynWaves;
+template <int WAVES, int E, int TPQ, int S, bool AVEC, bool GROUPED>
+__global__ __launch_bounds__(WAVES * 64) void k_int8_decode_q(Int8GemmParams p, GroupArg<GROUPED> g) {
     constexpr int WPS = WAVES / S;         // wavefronts per strip
     constexpr int TPB = TPQ * S;           // weight tiles per wavefront (bound)
     constexpr int L = 64 / E;              // lanes per row
+    static_assert(WAVES == 4 || WAVES == 8, "4 or 8 wavefronts");
     static_assert(E == 1 || E == 2 || E == 4 || E == 8 || E == 16, "E is a power of two <= 16");
-    static_assert(S == 1 || S == 2 || S == 4, "S divides the wavefronts");
+    static_assert((S == 1 || S == 2 || S == 4) && WAVES % S == 0, "S divides the wavefronts");
     static_assert(E * TPQ <= 32, "at most 32 activations per lane");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -764,43 +764,55 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
     return launch_int8_prefill(p, s);
 }
 
-template <int E, int TPQ, int S, bool GROUPED>
+template <int WAVES, int E, int TPQ, int S, bool GROUPED>
 hipError_t launch_dyn(const Int8GemmParams &p, const DecodeGroups &dg, bool avec, hipStream_t s) {
     const unsigned groups = p.rpg > 0 ? (unsigned)((p.M + p.rpg - 1) / p.rpg) : 1u;
-    const dim3 g((unsigned)((p.NS + S - 1) / S), groups), b(kDynWaves * 64);
+    const dim3 g((unsigned)((p.NS + S - 1) / S), groups), b(WAVES * 64);
     GroupArg<GROUPED> ga{};
     if constexpr (GROUPED) ga = dg;
     if (E >= 4 && avec)
-        hipLaunchKernelGGL((k_int8_decode_q<E, TPQ, S, true, GROUPED>), g, b, 0, s, p, ga);
+        hipLaunchKernelGGL((k_int8_decode_q<WAVES, E, TPQ, S, true, GROUPED>), g, b, 0, s, p, ga);
     else
-        hipLaunchKernelGGL((k_int8_decode_q<E, TPQ, S, false, GROUPED>), g, b, 0, s, p, ga);
+        hipLaunchKernelGGL((k_int8_decode_q<WAVES, E, TPQ, S, false, GROUPED>), g, b, 0, s, p, ga);
     return hipGetLastError();
 }
 
-template <int E, int TPQ, bool GROUPED>
+// strips per workgroup: 1, 2 or 4 (4 only with 8 wavefronts)
+template <int WAVES, int E, int TPQ, bool GROUPED>
 hipError_t launch_dyn_s(const Int8GemmParams &p, const DecodeGroups &dg, int spw, bool avec, hipStream_t s) {
-    if (spw == 1) return launch_dyn<E, TPQ, 1, GROUPED>(p, dg, avec, s);
-    if (spw == 2) return launch_dyn<E, TPQ, 2, GROUPED>(p, dg, avec, s);
-    if (spw == 4) return launch_dyn<E, TPQ, 4, GROUPED>(p, dg, avec, s);
+    if (spw == 1) return launch_dyn<WAVES, E, TPQ, 1, GROUPED>(p, dg, avec, s);
+    if (spw == 2) return launch_dyn<WAVES, E, TPQ, 2, GROUPED>(p, dg, avec, s);
+    if constexpr (WAVES == 8) {
+        if (spw == 4) return launch_dyn<WAVES, E, TPQ, 4, GROUPED>(p, dg, avec, s);
+    }
     return hipErrorInvalidValue;
 }
 
-// k tiles per wavefront: the power of two >= KT / 8.  The planner's bound
-// E * K <= 16384 keeps E * TPQ <= 32 (for KT in (2^a, 2^(a+1)]: E <= 2^(7-a),
-// TPQ <= 2^(a-2)).
-template <int E, bool GROUPED>
+// k tiles per wavefront: the power of two >= KT / WAVES.  With 8 wavefronts
+// the planner's bound E * K <= 16384 keeps E * TPQ <= 32 (for KT in
+// (2^a, 2^(a+1)]: E <= 2^(7-a), TPQ <= 2^(a-2)); 4 wavefronts are planned
+// only for KT <= 16 (TPQ <= 4).
+template <int WAVES, int E, bool GROUPED>
 hipError_t launch_dyn_tpq(const Int8GemmParams &p, const DecodeGroups &dg, int spw, bool avec, hipStream_t s) {
-    constexpr int W = kDynWaves;
-    if (p.KT <= W) return launch_dyn_s<E, 1, GROUPED>(p, dg, spw, avec, s);
+    constexpr int W = WAVES;
+    if (p.KT <= W) return launch_dyn_s<WAVES, E, 1, GROUPED>(p, dg, spw, avec, s);
     if constexpr (E * 2 <= 32) {
-        if (p.KT <= 2 * W) return launch_dyn_s<E, 2, GROUPED>(p, dg, spw, avec, s);
+        if (p.KT <= 2 * W) return launch_dyn_s<WAVES, E, 2, GROUPED>(p, dg, spw, avec, s);
     }
     if constexpr (E * 4 <= 32) {
-        if (p.KT <= 4 * W) return launch_dyn_s<E, 4, GROUPED>(p, dg, spw, avec, s);
+        if (p.KT <= 4 * W) return launch_dyn_s<WAVES, E, 4, GROUPED>(p, dg, spw, avec, s);
     }
-    if constexpr (E * 8 <= 32) {
-        if (p.KT <= 8 * W) return launch_dyn_s<E, 8, GROUPED>(p, dg, spw, avec, s);
+    if constexpr (E * 8 <= 32 && WAVES == 8) {
+        if (p.KT <= 8 * W) return launch_dyn_s<WAVES, E, 8, GROUPED>(p, dg, spw, avec, s);
     }
+    return hipErrorInvalidValue;
+}
+
+template <int E, bool GROUPED>
+hipError_t launch_dyn_w(const Int8GemmParams &p, const DecodeGroups &dg, int waves, int spw, bool avec,
+                        hipStream_t s) {
+    if (waves == 4) return launch_dyn_tpq<4, E, GROUPED>(p, dg, spw, avec, s);
+    if (waves == 8) return launch_dyn_tpq<8, E, GROUPED>(p, dg, spw, avec, s);
     return hipErrorInvalidValue;
 }
 
@@ -811,12 +823,13 @@ hipError_t launch_dyn_rows(const Int8Plan &plan, const Int8GemmParams &p, const 
         return hipErrorInvalidValue;
     const bool v = p.x_vec && (p.K % 16) == 0;
     const int spw = plan.spw > 0 ? plan.spw : 1;
+    const int w = plan.waves > 0 ? plan.waves : 8;
     // E: values per lane, the rows rounded up to a power of two
-    if (rows <= 1) return launch_dyn_tpq<1, GROUPED>(p, dg, spw, v, s);
-    if (rows <= 2) return launch_dyn_tpq<2, GROUPED>(p, dg, spw, v, s);
-    if (rows <= 4) return launch_dyn_tpq<4, GROUPED>(p, dg, spw, v, s);
-    if (rows <= 8) return launch_dyn_tpq<8, GROUPED>(p, dg, spw, v, s);
-    return launch_dyn_tpq<16, GROUPED>(p, dg, spw, v, s);
+    if (rows <= 1) return launch_dyn_w<1, GROUPED>(p, dg, w, spw, v, s);
+    if (rows <= 2) return launch_dyn_w<2, GROUPED>(p, dg, w, spw, v, s);
+    if (rows <= 4) return launch_dyn_w<4, GROUPED>(p, dg, w, spw, v, s);
+    if (rows <= 8) return launch_dyn_w<8, GROUPED>(p, dg, w, spw, v, s);
+    return launch_dyn_w<16, GROUPED>(p, dg, w, spw, v, s);
 }
 
 hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,

@@ -132,10 +132,10 @@ struct DecodeGroups {
 };
 
 // Wavefronts per workgroup of the fused quantising decode (k_int8_decode_q):
-// measured faster than 16 for every Qwen3-0.6B projection group at M = 1,
-// 16 and 32 (fewer partial tiles to combine and less launch skew before the
-// row-maximum barrier).
-constexpr int kDynWaves = 8;
+// 8, measured faster than 16 for every Qwen3-0.6B projection group at M = 1,
+// 16 and 32 (fewer partial tiles to combine and less skew before the
+// row-maximum barrier); 4 where K <= 1024, S <= 2 and >= 192 workgroups
+// (faster there, slower everywhere else).  Int8Plan::waves carries it.
 
 // The wide decode (one wavefront per strip over the whole k range) stages
 // all of A' in LDS: at most this many 1 KiB operand tiles (k tiles x 16-row
@@ -147,7 +147,7 @@ constexpr int64_t kWideMinStrips = 1024;
 struct Int8Plan {
     int variant;      // 0 = decode (M <= 32), 1 = prefill, 2 = wide decode (M <= 32, many columns)
     int mt;           // 16-row tiles (decode)
-    int waves;        // waves per workgroup (decode)
+    int waves;        // waves per workgroup (decode; fused quantising decode: 4 or 8)
     int tpw;          // k tiles per wave per round (decode)
     int spw;          // 16-column strips per workgroup (fused quantising decode; 0 = 1)
     int64_t grid;

@@ -551,7 +551,9 @@ def _dynamic_variant(M, K, NS, grouped=False):
                                    (32, 1024, 2048), (32, 2048, 1024), (31, 1024, 96), (25, 2048, 40),
                                    (18, 3000, 64), (12, 3072, 48),
                                    # several strips per workgroup, ragged last workgroups
-                                   (1, 1024, 6000), (8, 1024, 6144), (24, 1024, 3000), (32, 1024, 4000)])
+                                   (1, 1024, 6000), (8, 1024, 6144), (24, 1024, 3000), (32, 1024, 4000),
+                                   # 4-wavefront workgroups (K <= 1024, S <= 2, >= 192 workgroups), ragged K
+                                   (2, 1000, 6144), (1, 1000, 4000), (16, 1000, 4096)])
 def test_dynamic_matches_two_step_and_oracle(q, orc, M, K, N):
     """int8_gemm_dynamic == quantize_rows_int8 + int8_gemm bit for bit (fp32
     output, quantised rows, row scales), and the oracle's int32 product."""
