@@ -166,12 +166,23 @@ __device__ __forceinline__ float div_by(float x, float s, float y) {
 // clamp(rne(x / s), -127, 127)), packed little-endian; `fast` selects the
 // division above, else the IEEE division.
 __device__ __forceinline__ uint32_t quant4(const float (&x)[4], float s, float y, bool fast) {
+    float q[4];
+    bool ok = fast;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        q[j] = div_by(x[j], s, y);
+        ok = ok && fabsf(q[j]) <= 256.0f;
+    }
+    // the IEEE division only where the fast quotient may be off, decided per
+    // wavefront (both quotients are the correctly rounded one where ok)
+    if (!__all(ok)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = ok ? q[j] : x[j] / s;
+    }
     uint32_t w = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        float q = div_by(x[j], s, y);
-        if (!fast || !(fabsf(q) <= 256.0f)) q = x[j] / s;
-        float r = rintf(q);
+        float r = rintf(q[j]);
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         w |= (uint32_t)((int)r & 0xFF) << (8 * j);
     }
@@ -593,9 +604,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_int8_decode_q(Int8GemmParams p, 
             qv[j] = div_by(x[t][j], s, y);
             fast = fast && fabsf(qv[j]) <= 256.0f;
         }
-        if (!fast) {
+        // the IEEE division where the fast quotient may be off (a scale
+        // outside [2^-100, 2^100], a quotient past 256), decided per
+        // wavefront: as a per-lane select the compiler computed the division
+        // for every value (half the quantisation phase)
+        if (!__all(fast)) {
 #pragma unroll
-            for (int j = 0; j < E; ++j) qv[j] = x[t][j] / s;
+            for (int j = 0; j < E; ++j) qv[j] = fast ? qv[j] : x[t][j] / s;
         }
         uint32_t w[(E + 3) / 4];
 #pragma unroll
