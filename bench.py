@@ -46,11 +46,11 @@ PROBE_BYTES = 1 << 30
 # HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
 # of `bench.py --probe` (FETCH_SIZE, then WRITE_SIZE; mean over the step's 336
 # decode launches): FETCH_SIZE x 2.0, the factor the probe's plain read of
-# 1 GiB gives in the same run (524311 KiB), plus WRITE_SIZE x 1.0, the factor
+# 1 GiB gives in the same run (524306 KiB), plus WRITE_SIZE x 1.0, the factor
 # the 1 GiB fill of the probe buffer gives (1048576 KiB).  Valid only for the
 # kernel sources it was taken on.
-MEASURED_TRAFFIC = {"sources_sha1": "bd18d8f325717ee97c3fa68a2054b141f5403d9c",
-                    "bytes_per_launch": round((2445.3 * 2.0 + 196.0) * 1024)}
+MEASURED_TRAFFIC = {"sources_sha1": "a726b452c198da70873e42eef02181828ce7a1a7",
+                    "bytes_per_launch": round((2465.0 * 2.0 + 196.0) * 1024)}
 
 
 def decode_sources_sha1():
