@@ -95,9 +95,9 @@ MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N, 
     // the activation split: fp16 terms (4 bytes per activation), block sums,
     // scale exponents
     const Q4Layout L = q4_layout(K, N);
-    pl.ws_xs_off = pl.ws_misc_off + 256;
+    pl.ws_xs_off = pl.ws_misc_off + 512;
     pl.ws_xsum_off = pl.ws_xs_off + round_up(R * L.NB * 128, 256);
-    pl.ws_xsc_off = pl.ws_xsum_off + round_up(R * L.NQ * 48, 256);
+    pl.ws_xsc_off = pl.ws_xsum_off + round_up(R * L.NQ * 192, 256);
     pl.ws_bytes = pl.ws_xsc_off + round_up(R * 4, 256);
     return pl;
 }
@@ -289,6 +289,9 @@ static qmm_status moe_call(const float *X, int64_t n_tokens, int64_t K, int64_t 
         return QMM_ERR_INVALID;
     const Q4Layout L = q4_layout(K, N);
     if (expert_stride < (size_t)L.total || expert_stride % 256 != 0) return QMM_ERR_INVALID;
+    // the product kernel addresses the split activations with 32-bit offsets
+    const int64_t R = per_slot ? n_tokens * n_used : n_tokens;
+    if (R * L.NB * 128 > (int64_t)UINT32_MAX || R * L.NQ * 192 > (int64_t)UINT32_MAX) return QMM_ERR_UNSUPPORTED;
     const MoePlan pl = plan_q4_moe(n_tokens, n_used, n_expert, K, N, per_slot);
     if (use_scratch) {
         // the library-owned array (allocation-free entry point)
@@ -319,7 +322,7 @@ static qmm_status moe_call(const float *X, int64_t n_tokens, int64_t K, int64_t 
     sp.xs = ws + pl.ws_xs_off;
     sp.xsum = ws + pl.ws_xsum_off;
     sp.xsc = (int32_t *)(ws + pl.ws_xsc_off);
-    sp.zero16 = ws + pl.ws_misc_off + 64;
+    sp.zeros = ws + pl.ws_misc_off + 256;
     hipError_t e = launch_moe_route(ids, ids_row_stride, n_tokens, n_used, n_expert, pl.rpc, sorted, chunk_info,
                                     misc, misc + 1, sp, s);
     const char *variant = "";
@@ -345,7 +348,7 @@ static qmm_status moe_call(const float *X, int64_t n_tokens, int64_t K, int64_t 
         p.xs = sp.xs;
         p.xsum = sp.xsum;
         p.xsc = sp.xsc;
-        p.zero16 = sp.zero16;
+        p.zeros = sp.zeros;
         e = launch_q4_moe(p, per_slot, pl.max_chunks, s, &variant);
     }
     if (e == hipSuccess && g_check) {

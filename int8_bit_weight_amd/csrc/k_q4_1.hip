@@ -1022,10 +1022,16 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
     // the wavefronts with fewer fragments store the last one again, the same
     // bytes to the same place); d term f = (block * 2 + term) * MT + tile,
     // m term f - NFD = term * MT + tile.  Lane (row r, k-octet g) of a tile.
+    // Every load of the loop is a uniform base (the buffer and the record's
+    // offset, scalar registers) plus a per-lane 32-bit offset fixed for the
+    // job (the lane's row and k-octet): no vector address arithmetic per
+    // record.  The block sums' 64-byte entries hold zeros past their first 16
+    // bytes, so the k-octets 1..3 of the m-term operand read zeros.
     const int r = lane & 15, g = lane >> 4;
     const int a_off = lane * 16;
-    const uint8_t *fsrc[FPW];
-    int fblk[FPW], fbm[FPW], fstep[FPW], foff[FPW];
+    uint32_t fvoff[FPW];
+    int foff[FPW], fblk[FPW];
+    bool fisd[FPW];
 #pragma unroll
     for (int i = 0; i < FPW; ++i) {
         const int f = min(wave + WAVES * i, NFD + NFM - 1);
@@ -1033,15 +1039,11 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
         const bool isd = f < NFD;
         const int u = isd ? (f / MT) & 1 : (f - NFD) / MT;
         const int tile = isd ? f % MT : (f - NFD) % MT;
-        const int tok = sTok[tile * 16 + r];
-        const uint8_t *dsrc = p.xs + ((int64_t)tok * p.NB * 2 + u) * 64 + g * 16;
-        const uint8_t *msrc = g == 0 ? p.xsum + ((int64_t)tok * NQ * 3 + u) * 16 : p.zero16;
-        fsrc[i] = isd ? dsrc : msrc;
-        // byte offset of record q: d term min(4 q + block, NB - 1) * 128,
-        // m term q * 48 (0 for the zero piece); arithmetic, no branch
+        const uint32_t tok = (uint32_t)sTok[tile * 16 + r];
+        fvoff[i] = isd ? tok * (uint32_t)(p.NB * 128) + (uint32_t)(u * 64 + g * 16)
+                       : tok * (uint32_t)(NQ * 192) + (uint32_t)(u * 64 + g * 16);
+        fisd[i] = isd;
         fblk[i] = isd ? f / (2 * MT) : 0;
-        fbm[i] = isd ? 128 : 0;
-        fstep[i] = isd ? 0 : (g == 0 ? 48 : 0);
     }
     // gathers of record q (clamped to the last record) into registers, and
     // their stores into stage ST
@@ -1050,8 +1052,9 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
         const int qq = min(q, NQ - 1);
 #pragma unroll
         for (int i = 0; i < FPW; ++i) {
-            const int64_t o = (int64_t)(min(qq * 4 + fblk[i], p.NB - 1) * fbm[i] + qq * fstep[i]);
-            fr[i] = *(const v4i *)(fsrc[i] + o);
+            const uint8_t *base = fisd[i] ? p.xs + (int64_t)min(qq * 4 + fblk[i], p.NB - 1) * 128
+                                          : p.xsum + (int64_t)qq * 192;
+            fr[i] = *(const v4i *)(base + fvoff[i]);
         }
     };
     auto fstore = [&](auto ST) {
@@ -1063,17 +1066,22 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
 
     // ---- weight records: two register sets, record q + 1 loaded while q computes
     const int strip_base = sg * SPG + wave * C;
+    const uint8_t *srec[C];  // the wavefront's strips' first records (uniform)
+#pragma unroll
+    for (int j = 0; j < C; ++j) srec[j] = recs + (int64_t)min(strip_base + j, p.NS - 1) * NQ * kQ4RecBytes;
+    const uint32_t c_off = (uint32_t)lane * 16u, dm_off = (uint32_t)(lane & 15) * 16u;
     v4i bc[2][C], bd[2][C];
     auto gload_rec = [&](int q, v4i (&dc)[C], v4i (&dd)[C]) {
         const int qq = min(q, NQ - 1);
 #pragma unroll
         for (int j = 0; j < C; ++j) {
-            const int strip = min(strip_base + j, p.NS - 1);
-            const uint8_t *rec = recs + ((int64_t)strip * NQ + qq) * kQ4RecBytes;
+            const uint8_t *rec = srec[j] + qq * kQ4RecBytes;
             // plain loads (no non-temporal hint): an expert split into two
-            // chunks reads its records twice, the second time from cache
-            dc[j] = *(const v4i *)(rec + (uint32_t)lane * 16u);
-            dd[j] = *(const v4i *)(q < NQ ? rec + 1024 + (uint32_t)(lane & 15) * 16u : hdr + kHeaderBytes - 16);
+            // chunks reads its records twice, the second time from cache.
+            // Record NQ (odd NQ's last pair): (d, m) from the zero region,
+            // so it adds exactly zero.
+            dc[j] = *(const v4i *)(rec + c_off);
+            dd[j] = *(const v4i *)((q < NQ ? rec + 1024 : p.zeros) + dm_off);
         }
     };
 
@@ -1324,8 +1332,15 @@ __device__ void moe_split_token(const MoeSplit &sp, int t, int ltid, float *s_ma
             }
             const int q = pc >> 4;
 #pragma unroll
-            for (int u = 0; u < 3; ++u)
-                *(v4i *)(sp.xsum + (((int64_t)t * sp.NQ + q) * 3 + u) * 16) = v4i{(int)w[u][0], (int)w[u][1], 0, 0};
+            for (int u = 0; u < 3; ++u) {
+                // 64-byte entry: the four block sums, then 48 zero bytes (the
+                // m-term operand's other k-octets)
+                v4i *e = (v4i *)(sp.xsum + (((int64_t)t * sp.NQ + q) * 3 + u) * 64);
+                e[0] = v4i{(int)w[u][0], (int)w[u][1], 0, 0};
+                e[1] = v4i{0, 0, 0, 0};
+                e[2] = v4i{0, 0, 0, 0};
+                e[3] = v4i{0, 0, 0, 0};
+            }
         }
     }
 }
@@ -1339,7 +1354,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
         __shared__ float s_max[kSplitTokensPerGroup][4];
         const int grp = threadIdx.x >> 8;
         const int t = ((int)blockIdx.x - 1) * kSplitTokensPerGroup + grp;
-        if (blockIdx.x == 1 && threadIdx.x == 0) *(v4i *)sp.zero16 = v4i{0, 0, 0, 0};
+        if (blockIdx.x == 1 && threadIdx.x < 16) ((v4i *)sp.zeros)[threadIdx.x] = v4i{0, 0, 0, 0};
         // rows past R repeat row R - 1 (the same values, written again)
         moe_split_token(sp, min(t, sp.R - 1), threadIdx.x & 255, s_max[grp]);
         return;

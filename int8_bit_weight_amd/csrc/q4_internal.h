@@ -60,9 +60,9 @@ struct Q4Params {
     int64_t ldy_slot, ldy_token;
     // MoE activations split once per call by the routing launch
     const uint8_t *xs;        // [R][NB][2][4] 16-byte pieces: two fp16 terms of x * 2^sc[a]
-    const uint8_t *xsum;      // [R][NQ][3] 16 bytes: the record's four block sums (bf16 terms)
+    const uint8_t *xsum;      // [R][NQ][3] 64 bytes: the record's four block sums (bf16 terms), 48 zero bytes
     const int32_t *xsc;       // [R] scale exponents sc[a] (R activation rows, see MoeSplit)
-    const uint8_t *zero16;    // 16 zero bytes
+    const uint8_t *zeros;     // 256 zero bytes
 };
 
 // The MoE activation split (k_moe_route's extra workgroups): per token t,
@@ -88,7 +88,7 @@ struct MoeSplit {
     const float *X;
     int64_t ldx, ldx_slot;
     int T, R, per, K, NB, NQ, x_vec;
-    uint8_t *xs, *xsum, *zero16;
+    uint8_t *xs, *xsum, *zeros;
     int32_t *xsc;
 };
 
