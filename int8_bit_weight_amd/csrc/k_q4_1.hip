@@ -59,6 +59,17 @@ __device__ __forceinline__ v8bf decode8(uint32_t w) {
     return __builtin_bit_cast(v8bf, r);
 }
 
+// The same eight codes as exact fp16 values (the f16 form of the conversion).
+__device__ __forceinline__ v8h decode8h(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu;
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+    const v4i r = {__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false)),
+                   __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true)),
+                   __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false)),
+                   __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true))};
+    return __builtin_bit_cast(v8h, r);
+}
+
 // ---------------------------------------------------------------- repack ---
 // One thread per (record, lane chunk).  Canonical block of column n, block b:
 // 20 bytes at blocks + (n*NB + b)*20: d (bf16), m (bf16), 16 code bytes with
@@ -743,8 +754,8 @@ __global__ __launch_bounds__(W * 64) void k_q4_gemv1(Q4Params p) {
 }
 
 // ----------------------------------------- the product, 5 <= M <= 16 ---
-// One 16-row MFMA tile of activation rows, three MFMAs (one per bf16 term)
-// per block and strip, as in k_q4_mm.  A workgroup of WAVES wavefronts owns
+// One 16-row MFMA tile of activation rows, two MFMAs (one per fp16 term)
+// per block and strip.  A workgroup of WAVES wavefronts owns
 // WAVES * C strips and a k range of at most QMAX records; the grid splits
 // the k range S ways and k_q4_finalize adds the S partial sums.  What
 // differs from k_q4_mm is the order of the work: the workgroup splits the
@@ -755,9 +766,15 @@ __global__ __launch_bounds__(W * 64) void k_q4_gemv1(Q4Params p) {
 // activation loads, split and barrier sat between the weight loads and the
 // MFMAs.)
 //   * staging: piece (block bl, k-octet g, row r) = 8 activations, loaded
-//     with two 16-byte loads ahead of the record loads, split into the
-//     three bf16 terms and stored at sA[bl][term] in MFMA lane order (lane
-//     16 g + r).  Rows past M and blocks past K stage zeros.  The block
+//     with two 16-byte loads ahead of the record loads.  Each row first
+//     gets a power-of-two scale over the workgroup's k range (sc = 15 - e,
+//     max |x| = f 2^e, f in [0.5, 1); one barrier): every x 2^sc lies below
+//     2^15, and its two fp16 terms h0 = fp16(x 2^sc), h1 = fp16(x 2^sc - h0)
+//     hold it to ~2^-22 relative (the scaling and the subtraction are
+//     exact).  The terms are stored at sA[bl][term] in MFMA lane order (lane
+//     16 g + r), against the exact fp16 codes; the epilogue multiplies the
+//     d term by 2^-sc (each k split undoes its own scale).  Rows past M and
+//     blocks past K stage zeros.  The (unscaled) block
 //     sums (the four k-octets of a (row, block) lie in lanes r, r+16, r+32,
 //     r+48 of one wavefront) are split the same way into the m-term A
 //     operand: row r, block bl at byte 16 r + 2 (bl % 8) of sXM[bl / 8].
@@ -773,8 +790,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
     static_assert(R >= 1 && R <= QMAX, "record ring");
     constexpr int PPT = PIECES / NT;
     constexpr int SPG = WAVES * C;
-    __shared__ __attribute__((aligned(16))) uint8_t sA[NBLK][3][1024];
+    __shared__ __attribute__((aligned(16))) uint8_t sA[NBLK][2][1024];
     __shared__ __attribute__((aligned(16))) uint8_t sXM[NG][3][1024];
+    __shared__ float s_rmax[WAVES][16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -840,30 +858,47 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
         const int f = o / 768;
         *(v4i *)(&sXM[0][0][0] + f * 1024 + 256 + o % 768) = v4i{0, 0, 0, 0};
     }
+    // the row scales: a thread's pieces all belong to row tid % 16; its
+    // maximum, then the row's four k-octet lanes (xor 16, 32), then the
+    // wavefronts through LDS
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, xok[i] ? fabsf(xr[i][e]) : 0.0f);
+    am = fmaxf(am, __shfl_xor(am, 16));
+    am = fmaxf(am, __shfl_xor(am, 32));
+    if (lane < 16) s_rmax[wave][lane] = am;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    auto row_sc = [&](int row) {
+        float m = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) m = fmaxf(m, s_rmax[w][row]);
+        return m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;
+    };
+    const int sc = row_sc(tid & 15);
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
         const int pc = tid + i * NT;
         const int r = pc & 15, g = (pc >> 4) & 3, bl = pc >> 6;
         float bsum = 0.0f;
-        uint32_t w[3][4];
+        uint32_t w[2][4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
             const float x0 = xok[i] ? xr[i][e] : 0.0f;
             const float x1 = xok[i] ? xr[i][e + 1] : 0.0f;
             bsum += x0;
             bsum += x1;
-            const uint32_t t0 = pk_bf16(x0, x1);
-            const float r0 = x0 - bf16_lo_f32(t0), r1 = x1 - bf16_hi_f32(t0);
-            const uint32_t t1 = pk_bf16(r0, r1);
-            const uint32_t t2 = pk_bf16(r0 - bf16_lo_f32(t1), r1 - bf16_hi_f32(t1));
-            w[0][e >> 1] = t0;
-            w[1][e >> 1] = t1;
-            w[2][e >> 1] = t2;
+            const float s0 = __builtin_ldexpf(x0, sc), s1 = __builtin_ldexpf(x1, sc);
+            const v2h a0 = {(_Float16)s0, (_Float16)s1};
+            const v2h a1 = {(_Float16)(s0 - (float)a0[0]), (_Float16)(s1 - (float)a0[1])};
+            w[0][e >> 1] = __builtin_bit_cast(uint32_t, a0);
+            w[1][e >> 1] = __builtin_bit_cast(uint32_t, a1);
         }
         bsum += __shfl_xor(bsum, 16);
         bsum += __shfl_xor(bsum, 32);
 #pragma unroll
-        for (int t = 0; t < 3; ++t)
+        for (int t = 0; t < 2; ++t)
             *(v4i *)(&sA[bl][t][(g * 16 + r) * 16]) = v4i{(int)w[t][0], (int)w[t][1], (int)w[t][2], (int)w[t][3]};
         if (g == 0) {
             const uint32_t s0 = pk_bf16(bsum, 0.0f);
@@ -895,16 +930,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int bl = 4 * q + i;
-            v8bf a[3];
+            v8h a[2];
 #pragma unroll
-            for (int t = 0; t < 3; ++t) a[t] = *(const v8bf *)(&sA[bl][t][a_off]);
+            for (int t = 0; t < 2; ++t) a[t] = *(const v8h *)(&sA[bl][t][a_off]);
 #pragma unroll
             for (int j = 0; j < C; ++j) {
-                const v8bf bop = decode8((uint32_t)wc[sl][j][i]);
+                const v8h bop = decode8h((uint32_t)wc[sl][j][i]);
                 const float d = bf16_lo_f32((uint32_t)wd[sl][j][i]);
                 v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int t = 0; t < 3; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], bop, acc, 0, 0, 0);
+                for (int t = 0; t < 2; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bop, acc, 0, 0, 0);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc_y[j][v] = fmaf(d, acc[v], acc_y[j][v]);
             }
@@ -938,6 +973,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
         }
     }
 
+    int esc[4];  // -sc of this lane's output rows
+#pragma unroll
+    for (int v = 0; v < 4; ++v) esc[v] = -row_sc(4 * (lane >> 4) + v);
 #pragma unroll
     for (int j = 0; j < C; ++j)
 #pragma unroll
@@ -945,7 +983,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
             const int row = 4 * (lane >> 4) + v;
             const int n = (strip_base + j) * 16 + (lane & 15);
             if (row < M && n < p.N) {
-                const float val = acc_y[j][v] + acc_m[j][v];
+                const float val = __builtin_ldexpf(acc_y[j][v], esc[v]) + acc_m[j][v];
                 if (p.S == 1)
                     p.Y[(int64_t)row * p.ldy + n] = val;
                 else
