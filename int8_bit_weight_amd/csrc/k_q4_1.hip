@@ -1042,6 +1042,7 @@ __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ p
 // branch-taken path (the wait was only on the fall-through path), so every
 // chunk of <= 16 rows summed stale accumulator registers.
 // One job's product with MT 16-row tiles.
+constexpr int kMoeTileRows = 16;
 template <int MT, int WAVES, int C, bool PER_SLOT>
 __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t *sS1, const int *sTok,
                                         const int64_t *sYoff, const int *sYexp, int sg, int expert, int nrows) {
@@ -1220,10 +1221,11 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
 
 
 // The kernel: a job's chunk of <= 16 rows runs the one-tile copy of the
-// product (half the MFMA and VALU work of the two-tile copy), so that the
-// partial chunks, listed last by the routing, fill the tail of the grid.  The
-// copy is chosen at entry, before any MFMA: inside each copy no branch sits
-// between an MFMA and the instructions that read its result.
+// product (about half the MFMA and VALU work of the two-tile copy); the
+// routing lists these chunks last, so the workgroups dispatched once the
+// first ones finish get the cheapest jobs.  The copy is chosen at entry,
+// before any MFMA: inside each copy no branch sits between an MFMA and the
+// instructions that read its result.
 template <int WAVES, int C, int MINW, bool PER_SLOT>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_moe(Q4Params p) {
     constexpr int ROWS = 32, SPG = WAVES * C;
@@ -1262,7 +1264,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
         sYexp[tid] = -p.xsc[PER_SLOT ? pair : tk];
     }
     __syncthreads();
-    if (nrows <= 16)
+    if (nrows <= kMoeTileRows)
         moe_job<1, WAVES, C, PER_SLOT>(p, sS0, sS1, sTok, sYoff, sYexp, sg, expert, nrows);
     else
         moe_job<2, WAVES, C, PER_SLOT>(p, sS0, sS1, sTok, sYoff, sYexp, sg, expert, nrows);
@@ -1278,8 +1280,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 // depends on its own activation row only.  The scan is parallel: each thread
 // sums a run of consecutive experts, a wavefront scan and a scan of the
 // wavefront totals give every run its offsets.  The chunk table lists the
-// full chunks (rpc rows) of every expert first and the partial ones after
-// them, so that workgroups dispatched last get the smaller jobs.
+// full chunks (rpc rows) of every expert first, then the partial chunks of
+// more than 16 rows, then those of at most 16 rows.
 //
 // The launch's other workgroups split the activations for the grouped
 // product, four tokens per workgroup (256 threads each): the token's max |x|
@@ -1402,7 +1404,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
     int32_t *off = sh + E;       // [E] first sorted row of the expert
     int32_t *fill = sh + 2 * E;  // [E] rows scattered so far
     __shared__ int s_bad;
-    __shared__ int s_wsum[16][3];
+    __shared__ int s_wsum[16][4];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int P = T * n_used;
@@ -1435,62 +1437,74 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
     }
     if (bad) s_bad = 1;
     __syncthreads();
-    // ---- scan: thread t owns experts [t EPT, (t+1) EPT); pairs, full chunks
-    // and partial chunks
+    // ---- scan: thread t owns experts [t EPT, (t+1) EPT); pairs, full
+    // chunks, partial chunks of more than one tile of rows (the product's
+    // two-tile copy) and partial chunks of at most one tile (its one-tile
+    // copy, about half the work), listed in that order: the workgroups that
+    // start last, once the first ones finish, get the cheapest jobs
+    constexpr int small = kMoeTileRows;
     const int EPT = (E + 1023) / 1024;
     const int e0 = min(tid * EPT, E), e1 = min(e0 + EPT, E);
-    int lc = 0, lf = 0, lp = 0;
+    int lc = 0, lf = 0, lb = 0, ls = 0;
     for (int e = e0; e < e1; ++e) {
+        const int r = cnt[e] % rpc;
         lc += cnt[e];
         lf += cnt[e] / rpc;
-        lp += cnt[e] % rpc != 0;
+        lb += r > small;
+        ls += r != 0 && r <= small;
     }
-    int ic = lc, iF = lf, ip = lp;  // inclusive wavefront scans
+    int ic = lc, iF = lf, ib = lb, is = ls;  // inclusive wavefront scans
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        const int a = __shfl_up(ic, d), b = __shfl_up(iF, d), c = __shfl_up(ip, d);
+        const int a = __shfl_up(ic, d), b = __shfl_up(iF, d), c = __shfl_up(ib, d), f = __shfl_up(is, d);
         if (lane >= d) {
             ic += a;
             iF += b;
-            ip += c;
+            ib += c;
+            is += f;
         }
     }
     if (lane == 63) {
         s_wsum[wave][0] = ic;
         s_wsum[wave][1] = iF;
-        s_wsum[wave][2] = ip;
+        s_wsum[wave][2] = ib;
+        s_wsum[wave][3] = is;
     }
     __syncthreads();
-    int bc = 0, bf = 0, bp = 0, nfull = 0, npart = 0;  // earlier wavefronts; all wavefronts
+    // earlier wavefronts' totals; all wavefronts' totals
+    int bc = 0, bf = 0, bb = 0, bs = 0, nfull = 0, nbig = 0, nsmall = 0;
     for (int w = 0; w < 16; ++w) {
         if (w < wave) {
             bc += s_wsum[w][0];
             bf += s_wsum[w][1];
-            bp += s_wsum[w][2];
+            bb += s_wsum[w][2];
+            bs += s_wsum[w][3];
         }
         nfull += s_wsum[w][1];
-        npart += s_wsum[w][2];
+        nbig += s_wsum[w][2];
+        nsmall += s_wsum[w][3];
     }
-    int o = bc + ic - lc, fo = bf + iF - lf, po = nfull + bp + ip - lp;
+    int o = bc + ic - lc, fo = bf + iF - lf, bo = nfull + bb + ib - lb, so = nfull + nbig + bs + is - ls;
     for (int e = e0; e < e1; ++e) {
         off[e] = o;
-        const int c = cnt[e], nf = c / rpc;
+        const int c = cnt[e], nf = c / rpc, r = c % rpc;
         for (int k = 0; k < nf; ++k) {
             chunk_info[(fo + k) * 3 + 0] = e;
             chunk_info[(fo + k) * 3 + 1] = o + k * rpc;
             chunk_info[(fo + k) * 3 + 2] = rpc;
         }
         fo += nf;
-        if (c % rpc != 0) {
+        if (r != 0) {
+            int &po = r > small ? bo : so;
             chunk_info[po * 3 + 0] = e;
             chunk_info[po * 3 + 1] = o + nf * rpc;
-            chunk_info[po * 3 + 2] = c % rpc;
+            chunk_info[po * 3 + 2] = r;
             ++po;
         }
         o += c;
     }
     if (tid == 0) {
-        *nchunks = nfull + npart;
+        *nchunks = nfull + nbig + nsmall;
         *err = s_bad;
     }
     __syncthreads();
