@@ -379,7 +379,7 @@ qmm_status q4_1_matmul_id_per_slot(const float *X, int64_t n_tokens, int64_t K, 
  *   - A call whose workspace (qmm_q4_1_matmul_id_workspace_bytes) exceeds
  *     QMM_NOALLOC_SCRATCH_BYTES returns QMM_ERR_WORKSPACE before anything
  *     is enqueued (16 MiB covers e.g. 512 tokens x top-8 over 128 experts
- *     at K = 2048, which needs about 5.6 MiB).
+ *     at K = 2048, which needs about 4.5 MiB).
  *   - Every call on one GPU shares that GPU's array, and nothing in it needs
  *     to start at any value (each call writes everything it reads): calls
  *     that overlap in time on one GPU (different streams, or different host

@@ -97,7 +97,7 @@ MoePlan plan_q4_moe(int64_t T, int64_t n_used, int64_t E, int64_t K, int64_t N, 
     const Q4Layout L = q4_layout(K, N);
     pl.ws_xs_off = pl.ws_misc_off + 512;
     pl.ws_xsum_off = pl.ws_xs_off + round_up(R * L.NB * 128, 256);
-    pl.ws_xsc_off = pl.ws_xsum_off + round_up(R * L.NQ * 192, 256);
+    pl.ws_xsc_off = pl.ws_xsum_off + round_up(R * L.NQ * 64, 256);
     pl.ws_bytes = pl.ws_xsc_off + round_up(R * 4, 256);
     return pl;
 }
@@ -291,7 +291,7 @@ static qmm_status moe_call(const float *X, int64_t n_tokens, int64_t K, int64_t 
     if (expert_stride < (size_t)L.total || expert_stride % 256 != 0) return QMM_ERR_INVALID;
     // the product kernel addresses the split activations with 32-bit offsets
     const int64_t R = per_slot ? n_tokens * n_used : n_tokens;
-    if (R * L.NB * 128 > (int64_t)UINT32_MAX || R * L.NQ * 192 > (int64_t)UINT32_MAX) return QMM_ERR_UNSUPPORTED;
+    if (R * L.NB * 128 > (int64_t)UINT32_MAX || R * L.NQ * 64 > (int64_t)UINT32_MAX) return QMM_ERR_UNSUPPORTED;
     const MoePlan pl = plan_q4_moe(n_tokens, n_used, n_expert, K, N, per_slot);
     if (use_scratch) {
         // the library-owned array (allocation-free entry point)

@@ -1026,9 +1026,10 @@ __global__ __launch_bounds__(256) void k_q4_finalize(const float *__restrict__ p
 //   * d term, per block, strip and 16-row tile: two MFMAs
 //     (v_mfma_f32_16x16x32_f16: the fp16 terms against the exact fp16
 //     codes) into a fresh accumulator, then y += d * acc;
-//   * m term, per record, strip and tile: three bf16 MFMAs of the split
-//     block sums (k = block, k-octet 0; the other k-octets are copied from a
-//     zero piece) against the record's m values, accumulated into y;
+//   * m term, per record, strip and tile: one bf16 MFMA, accumulated into
+//     y, whose A operand holds the three bf16 terms of the record's four
+//     block sums in k-octets 0, 1, 2 (k = 8 term + block; the rest zero) and
+//     whose B operand holds the record's four m values in every k-octet;
 //   * the epilogue undoes the token's scale: Y = y * 2^-sc[t].
 // Rows past the chunk repeat its last row (their outputs are not stored);
 // blocks past K read the last block (their d = m = 0).  A chunk of <= 16
@@ -1048,7 +1049,7 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
                                         const int64_t *sYoff, const int *sYexp, int sg, int expert, int nrows) {
     constexpr int SPG = WAVES * C;
     constexpr int NFD = 4 * 2 * MT;  // d-term fragments per chunk: block x term x tile
-    constexpr int NFM = 3 * MT;      // m-term fragments: term x tile
+    constexpr int NFM = MT;          // m-term fragments: one per tile
     constexpr int FPW = (NFD + NFM + WAVES - 1) / WAVES;  // fragments copied per wavefront
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1060,12 +1061,12 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
     // ---- gather sources: fragment f = wave + WAVES i of the stage (clamped:
     // the wavefronts with fewer fragments store the last one again, the same
     // bytes to the same place); d term f = (block * 2 + term) * MT + tile,
-    // m term f - NFD = term * MT + tile.  Lane (row r, k-octet g) of a tile.
-    // Every load of the loop is a uniform base (the buffer and the record's
-    // offset, scalar registers) plus a per-lane 32-bit offset fixed for the
-    // job (the lane's row and k-octet): no vector address arithmetic per
-    // record.  The block sums' 64-byte entries hold zeros past their first 16
-    // bytes, so the k-octets 1..3 of the m-term operand read zeros.
+    // m term f - NFD = tile.  Lane (row r, k-octet g) of a tile.  Every load
+    // of the loop is a uniform base (the buffer and the record's offset,
+    // scalar registers) plus a per-lane 32-bit offset fixed for the job (the
+    // lane's row and k-octet): no vector address arithmetic per record.  A
+    // record's block-sum entry is 64 bytes, 16 per k-octet: term g's four
+    // sums and 8 zero bytes for g < 3, zeros for g = 3.
     const int r = lane & 15, g = lane >> 4;
     const int a_off = lane * 16;
     uint32_t fvoff[FPW];
@@ -1076,11 +1077,11 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
         const int f = min(wave + WAVES * i, NFD + NFM - 1);
         foff[i] = f * 1024;
         const bool isd = f < NFD;
-        const int u = isd ? (f / MT) & 1 : (f - NFD) / MT;
-        const int tile = isd ? f % MT : (f - NFD) % MT;
+        const int u = (f / MT) & 1;
+        const int tile = isd ? f % MT : f - NFD;
         const uint32_t tok = (uint32_t)sTok[tile * 16 + r];
         fvoff[i] = isd ? tok * (uint32_t)(p.NB * 128) + (uint32_t)(u * 64 + g * 16)
-                       : tok * (uint32_t)(NQ * 192) + (uint32_t)(u * 64 + g * 16);
+                       : tok * (uint32_t)(NQ * 64) + (uint32_t)(g * 16);
         fisd[i] = isd;
         fblk[i] = isd ? f / (2 * MT) : 0;
     }
@@ -1092,7 +1093,7 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
 #pragma unroll
         for (int i = 0; i < FPW; ++i) {
             const uint8_t *base = fisd[i] ? p.xs + (int64_t)min(qq * 4 + fblk[i], p.NB - 1) * 128
-                                          : p.xsum + (int64_t)qq * 192;
+                                          : p.xsum + (int64_t)qq * 64;
             fr[i] = *(const v4i *)(base + fvoff[i]);
         }
     };
@@ -1174,16 +1175,14 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            v8bf xm[3];
-#pragma unroll
-            for (int u = 0; u < 3; ++u) xm[u] = *(const v8bf *)(Mf + (u * MT + t) * 1024 + a_off);
+            const v8bf xm = *(const v8bf *)(Mf + t * 1024 + a_off);
 #pragma unroll
             for (int j = 0; j < C; ++j) {
+                // every lane of column n holds its m values: the same in each k-octet
                 const v4i mv = {(int)__builtin_amdgcn_perm((uint32_t)bd[st][j][1], (uint32_t)bd[st][j][0], 0x07060302u),
                                 (int)__builtin_amdgcn_perm((uint32_t)bd[st][j][3], (uint32_t)bd[st][j][2], 0x07060302u), 0, 0};
                 const v8bf mop = __builtin_bit_cast(v8bf, mv);
-#pragma unroll
-                for (int u = 0; u < 3; ++u) y[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm[u], mop, y[t][j], 0, 0, 0);
+                y[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, mop, y[t][j], 0, 0, 0);
             }
         }
         // chunk q + 1's pieces into the other stage (read after the next barrier)
@@ -1229,7 +1228,7 @@ __device__ __forceinline__ void moe_job(const Q4Params &p, uint8_t *sS0, uint8_t
 template <int WAVES, int C, int MINW, bool PER_SLOT>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_q4_moe(Q4Params p) {
     constexpr int ROWS = 32, SPG = WAVES * C;
-    constexpr int STAGE = (4 * 2 * 2 + 3 * 2) * 1024;  // the two-tile copy's fragments
+    constexpr int STAGE = (4 * 2 * 2 + 2) * 1024;  // the two-tile copy's fragments
     // stage = the chunk's fragments: d term [block][term][tile], then m term [term][tile]
     __shared__ __attribute__((aligned(16))) uint8_t sS0[STAGE], sS1[STAGE];
     __shared__ int sTok[ROWS];
@@ -1291,7 +1290,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 // relative (the scaling is exact; the subtraction is exact in fp32).  The
 // block sums of the scaled values (32 k, fixed order: 8 values per thread,
 // then the four k-octets) are split into three bf16 terms, as the m term's
-// A operand; four blocks (one record) per 16 bytes, the upper 8 zero.
+// A operand: one 64-byte entry per record, term u's four sums and 8 zero
+// bytes at 16 u, 16 zero bytes at 48.
 constexpr int kSplitTokensPerGroup = 4;
 __device__ void moe_split_token(const MoeSplit &sp, int t, int ltid, float *s_max) {
     const int lane = ltid & 63, wl = ltid >> 6;  // wavefront of the token (0..3)
@@ -1371,16 +1371,13 @@ __device__ void moe_split_token(const MoeSplit &sp, int t, int ltid, float *s_ma
                 w[2][k >> 1] = t2;
             }
             const int q = pc >> 4;
+            // the record's 64-byte entry, one k-octet of the m-term operand
+            // per 16 bytes: term u's four block sums and 8 zero bytes at
+            // 16 u, zeros in the last 16
+            v4i *e = (v4i *)(sp.xsum + ((int64_t)t * sp.NQ + q) * 64);
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                // 64-byte entry: the four block sums, then 48 zero bytes (the
-                // m-term operand's other k-octets)
-                v4i *e = (v4i *)(sp.xsum + (((int64_t)t * sp.NQ + q) * 3 + u) * 64);
-                e[0] = v4i{(int)w[u][0], (int)w[u][1], 0, 0};
-                e[1] = v4i{0, 0, 0, 0};
-                e[2] = v4i{0, 0, 0, 0};
-                e[3] = v4i{0, 0, 0, 0};
-            }
+            for (int u = 0; u < 3; ++u) e[u] = v4i{(int)w[u][0], (int)w[u][1], 0, 0};
+            e[3] = v4i{0, 0, 0, 0};
         }
     }
 }

@@ -60,7 +60,7 @@ struct Q4Params {
     int64_t ldy_slot, ldy_token;
     // MoE activations split once per call by the routing launch
     const uint8_t *xs;        // [R][NB][2][4] 16-byte pieces: two fp16 terms of x * 2^sc[a]
-    const uint8_t *xsum;      // [R][NQ][3] 64 bytes: the record's four block sums (bf16 terms), 48 zero bytes
+    const uint8_t *xsum;      // [R][NQ] 64 bytes: per bf16 term u < 3 the record's four block sums and 8 zero bytes, then 16 zero bytes
     const int32_t *xsc;       // [R] scale exponents sc[a] (R activation rows, see MoeSplit)
     const uint8_t *zeros;     // 256 zero bytes
 };
