@@ -1283,7 +1283,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 // more than 16 rows, then those of at most 16 rows.
 //
 // The launch's other workgroups split the activations for the grouped
-// product, four tokens per workgroup (256 threads each): the token's max |x|
+// product, 1024 / tpt tokens per workgroup, tpt = 64, 128 or 256 threads per
+// token (the token's 16-byte pieces rounded up to a power of two, at most
+// 256, so that few threads idle at small K): the token's max |x|
 // fixes a power-of-two scale 2^sc with sc = 15 - e (max |x| = f 2^e, f in
 // [0.5, 1)), so that every scaled value lies below 2^15 and the two fp16
 // terms h0 = fp16(x 2^sc), h1 = fp16(x 2^sc - h0) hold it to about 2^-22
@@ -1292,9 +1294,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(MINW
 // then the four k-octets) are split into three bf16 terms, as the m term's
 // A operand: one 64-byte entry per record, term u's four sums and 8 zero
 // bytes at 16 u, 16 zero bytes at 48.
-constexpr int kSplitTokensPerGroup = 4;
 __device__ void moe_split_token(const MoeSplit &sp, int t, int ltid, float *s_max) {
-    const int lane = ltid & 63, wl = ltid >> 6;  // wavefront of the token (0..3)
+    const int lane = ltid & 63, wl = ltid >> 6;  // wavefront of the token (0 .. tpt / 64 - 1)
+    const int tpt = sp.tpt;
     // activation row t: token t (shared form), or pair t = token * per + slot
     const float *xr = sp.X + (int64_t)(t / sp.per) * sp.ldx + (int64_t)(t % sp.per) * sp.ldx_slot;
     const int npc = sp.NQ * 16;  // pieces (block, k-octet), whole records
@@ -1315,7 +1317,7 @@ __device__ void moe_split_token(const MoeSplit &sp, int t, int ltid, float *s_ma
         }
     };
     float am = 0.0f;
-    for (int pc = ltid; pc < npc; pc += 256) {
+    for (int pc = ltid; pc < npc; pc += tpt) {
         float v[8];
         load8(pc, v);
 #pragma unroll
@@ -1325,10 +1327,11 @@ __device__ void moe_split_token(const MoeSplit &sp, int t, int ltid, float *s_ma
     for (int d = 32; d >= 1; d >>= 1) am = fmaxf(am, __shfl_xor(am, d));
     if (lane == 0) s_max[wl] = am;
     __syncthreads();
-    const float tm = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    float tm = s_max[0];
+    for (int w = 1; w < tpt / 64; ++w) tm = fmaxf(tm, s_max[w]);
     const int sc = 15 - __builtin_amdgcn_frexp_expf(tm);
     if (ltid == 0) sp.xsc[t] = sc;
-    for (int pc0 = 0; pc0 < npc; pc0 += 256) {  // uniform trip count: the shuffles below
+    for (int pc0 = 0; pc0 < npc; pc0 += tpt) {  // uniform trip count: the shuffles below
         const int pc = pc0 + ltid;
         const int b = pc >> 2, g = pc & 3;
         float v[8];
@@ -1388,12 +1391,12 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
                                                     int32_t *__restrict__ chunk_info, int32_t *__restrict__ nchunks,
                                                     int32_t *__restrict__ err, MoeSplit sp) {
     if (blockIdx.x > 0) {
-        __shared__ float s_max[kSplitTokensPerGroup][4];
-        const int grp = threadIdx.x >> 8;
-        const int t = ((int)blockIdx.x - 1) * kSplitTokensPerGroup + grp;
+        __shared__ float s_max[16][4];
+        const int grp = threadIdx.x / sp.tpt;
+        const int t = ((int)blockIdx.x - 1) * (1024 / sp.tpt) + grp;
         if (blockIdx.x == 1 && threadIdx.x < 16) ((v4i *)sp.zeros)[threadIdx.x] = v4i{0, 0, 0, 0};
         // rows past R repeat row R - 1 (the same values, written again)
-        moe_split_token(sp, min(t, sp.R - 1), threadIdx.x & 255, s_max[grp]);
+        moe_split_token(sp, min(t, sp.R - 1), threadIdx.x % sp.tpt, s_max[grp]);
         return;
     }
     extern __shared__ int32_t sh[];
@@ -1481,9 +1484,26 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
         nbig += s_wsum[w][2];
         nsmall += s_wsum[w][3];
     }
-    int o = bc + ic - lc, fo = bf + iF - lf, bo = nfull + bb + ib - lb, so = nfull + nbig + bs + is - ls;
+    const int o0 = bc + ic - lc;
+    for (int e = e0, o = o0; e < e1; o += cnt[e], ++e) off[e] = o;
+    // the scatter needs the offsets alone: an LDS barrier with no memory
+    // fence (a fence would wait for global stores to land, here and after the
+    // chunk table, which is written last so that its stores and the
+    // scatter's drain together)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // ---- scatter
+#pragma unroll
+    for (int u = 0; u < kRoutePairsPerThread; ++u) {
+        const int pr = tid + 1024 * u;
+        if (pr < P && ev[u] >= 0 && ev[u] < E) sorted[off[ev[u]] + atomicAdd(&fill[ev[u]], 1)] = pr;
+    }
+    for (int pr = tid + 1024 * kRoutePairsPerThread; pr < P; pr += 1024) {
+        const int e = ids[(int64_t)(pr / n_used) * ids_stride + pr % n_used];
+        if (e >= 0 && e < E) sorted[off[e] + atomicAdd(&fill[e], 1)] = pr;
+    }
+    // ---- chunk table
+    int o = o0, fo = bf + iF - lf, bo = nfull + bb + ib - lb, so = nfull + nbig + bs + is - ls;
     for (int e = e0; e < e1; ++e) {
-        off[e] = o;
         const int c = cnt[e], nf = c / rpc, r = c % rpc;
         for (int k = 0; k < nf; ++k) {
             chunk_info[(fo + k) * 3 + 0] = e;
@@ -1503,17 +1523,6 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
     if (tid == 0) {
         *nchunks = nfull + nbig + nsmall;
         *err = s_bad;
-    }
-    __syncthreads();
-    // ---- scatter
-#pragma unroll
-    for (int u = 0; u < kRoutePairsPerThread; ++u) {
-        const int pr = tid + 1024 * u;
-        if (pr < P && ev[u] >= 0 && ev[u] < E) sorted[off[ev[u]] + atomicAdd(&fill[ev[u]], 1)] = pr;
-    }
-    for (int pr = tid + 1024 * kRoutePairsPerThread; pr < P; pr += 1024) {
-        const int e = ids[(int64_t)(pr / n_used) * ids_stride + pr % n_used];
-        if (e >= 0 && e < E) sorted[off[e] + atomicAdd(&fill[e], 1)] = pr;
     }
 }
 
@@ -1611,10 +1620,13 @@ hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, i
                             int rpc, int32_t *sorted, int32_t *chunk_info, int32_t *nchunks, int32_t *err,
                             const MoeSplit &sp, hipStream_t s) {
     const size_t shmem = (size_t)E * 3 * sizeof(int32_t);
-    // workgroup 0 routes; workgroups 1.. split four activation rows each
-    const unsigned grid = 1u + (unsigned)ceil_div(sp.R, kSplitTokensPerGroup);
+    // workgroup 0 routes; workgroups 1.. split 1024 / tpt activation rows each
+    MoeSplit spl = sp;
+    const int npc = sp.NQ * 16;
+    spl.tpt = npc > 128 ? 256 : (npc > 64 ? 128 : 64);
+    const unsigned grid = 1u + (unsigned)ceil_div(sp.R, 1024 / spl.tpt);
     hipLaunchKernelGGL(k_moe_route, dim3(grid), dim3(1024), shmem, s, ids, ids_stride, (int)T, (int)n_used, (int)E,
-                       rpc, sorted, chunk_info, nchunks, err, sp);
+                       rpc, sorted, chunk_info, nchunks, err, spl);
     return hipGetLastError();
 }
 

@@ -88,6 +88,7 @@ struct MoeSplit {
     const float *X;
     int64_t ldx, ldx_slot;
     int T, R, per, K, NB, NQ, x_vec;
+    int tpt;  // threads per activation row (set by the launcher)
     uint8_t *xs, *xsum, *zeros;
     int32_t *xsc;
 };
