@@ -1385,6 +1385,23 @@ __device__ void moe_split_token(const MoeSplit &sp, int t, int ltid, float *s_ma
     }
 }
 
+// inclusive prefix sum over the 64 lanes of a wavefront: rows of 16 lanes
+// by DPP row shifts (bound_ctrl: a lane whose source lies before its row
+// adds 0), then the last lane of row 0 into row 1 and of row 2 into row 3
+// (row_bcast:15), and of row 1 into rows 2 and 3 (row_bcast:31); a row the
+// row mask leaves out adds `old`, 0
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add_src(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, true); }
+__device__ __forceinline__ int wave_incl_sum(int v) {
+    v += dpp_add_src<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_add_src<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_add_src<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_add_src<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_add_src<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_add_src<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 constexpr int kRoutePairsPerThread = 8;  // pairs held in registers per pass
 __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ ids, int64_t ids_stride, int T,
                                                     int n_used, int E, int rpc, int32_t *__restrict__ sorted,
@@ -1400,22 +1417,24 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
         return;
     }
     extern __shared__ int32_t sh[];
-    int32_t *cnt = sh;           // [E] pairs per expert
-    int32_t *off = sh + E;       // [E] first sorted row of the expert
-    int32_t *fill = sh + 2 * E;  // [E] rows scattered so far
+    int32_t *cnt = sh;           // [E] register-held pairs per expert (their ranks: the atomics' old values)
+    int32_t *cnt2 = sh + E;      // [E] pairs per expert past the register-held ones
+    int32_t *off = sh + 2 * E;   // [E] first sorted row of the expert
+    int32_t *fill = sh + 3 * E;  // [E] pairs of cnt2 scattered so far
     __shared__ int s_bad;
-    __shared__ int s_wsum[16][4];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int P = T * n_used;
     for (int e = tid; e < E; e += 1024) {
         cnt[e] = 0;
+        cnt2[e] = 0;
         fill[e] = 0;
     }
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    // ---- ids of the first pass in registers; larger P loops (re-reading)
-    int ev[kRoutePairsPerThread];
+    // ---- ids of the first pass in registers, each with its rank inside its
+    // expert (the counting atomic's old value); larger P loops (re-reading)
+    int ev[kRoutePairsPerThread], rk[kRoutePairsPerThread];
 #pragma unroll
     for (int u = 0; u < kRoutePairsPerThread; ++u) {
         const int pr = tid + 1024 * u;
@@ -1425,104 +1444,78 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t *__restrict__ 
 #pragma unroll
     for (int u = 0; u < kRoutePairsPerThread; ++u) {
         const int pr = tid + 1024 * u;
+        rk[u] = 0;
         if (pr < P) {
-            if (ev[u] >= 0 && ev[u] < E) atomicAdd(&cnt[ev[u]], 1);
+            if (ev[u] >= 0 && ev[u] < E) rk[u] = atomicAdd(&cnt[ev[u]], 1);
             else bad = true;
         }
     }
     for (int pr = tid + 1024 * kRoutePairsPerThread; pr < P; pr += 1024) {
         const int e = ids[(int64_t)(pr / n_used) * ids_stride + pr % n_used];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+        if (e >= 0 && e < E) atomicAdd(&cnt2[e], 1);
         else bad = true;
     }
     if (bad) s_bad = 1;
-    __syncthreads();
-    // ---- scan: thread t owns experts [t EPT, (t+1) EPT); pairs, full
-    // chunks, partial chunks of more than one tile of rows (the product's
-    // two-tile copy) and partial chunks of at most one tile (its one-tile
-    // copy, about half the work), listed in that order: the workgroups that
-    // start last, once the first ones finish, get the cheapest jobs
-    constexpr int small = kMoeTileRows;
-    const int EPT = (E + 1023) / 1024;
-    const int e0 = min(tid * EPT, E), e1 = min(e0 + EPT, E);
-    int lc = 0, lf = 0, lb = 0, ls = 0;
-    for (int e = e0; e < e1; ++e) {
-        const int r = cnt[e] % rpc;
-        lc += cnt[e];
-        lf += cnt[e] / rpc;
-        lb += r > small;
-        ls += r != 0 && r <= small;
-    }
-    int ic = lc, iF = lf, ib = lb, is = ls;  // inclusive wavefront scans
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int a = __shfl_up(ic, d), b = __shfl_up(iF, d), c = __shfl_up(ib, d), f = __shfl_up(is, d);
-        if (lane >= d) {
-            ic += a;
-            iF += b;
-            ib += c;
-            is += f;
-        }
-    }
-    if (lane == 63) {
-        s_wsum[wave][0] = ic;
-        s_wsum[wave][1] = iF;
-        s_wsum[wave][2] = ib;
-        s_wsum[wave][3] = is;
-    }
-    __syncthreads();
-    // earlier wavefronts' totals; all wavefronts' totals
-    int bc = 0, bf = 0, bb = 0, bs = 0, nfull = 0, nbig = 0, nsmall = 0;
-    for (int w = 0; w < 16; ++w) {
-        if (w < wave) {
-            bc += s_wsum[w][0];
-            bf += s_wsum[w][1];
-            bb += s_wsum[w][2];
-            bs += s_wsum[w][3];
-        }
-        nfull += s_wsum[w][1];
-        nbig += s_wsum[w][2];
-        nsmall += s_wsum[w][3];
-    }
-    const int o0 = bc + ic - lc;
-    for (int e = e0, o = o0; e < e1; o += cnt[e], ++e) off[e] = o;
-    // the scatter needs the offsets alone: an LDS barrier with no memory
-    // fence (a fence would wait for global stores to land, here and after the
-    // chunk table, which is written last so that its stores and the
-    // scatter's drain together)
+    // LDS barrier: the counts are LDS only (no memory fence)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // ---- scatter
+    // ---- scan and chunk table (wavefront 0; lane l owns experts
+    // [l EPW, (l+1) EPW)): pairs, full chunks, partial chunks of more than
+    // one tile of rows (the product's two-tile copy) and partial chunks of at
+    // most one tile (its one-tile copy, about half the work), listed in that
+    // order: the workgroups that start last, once the first ones finish, get
+    // the cheapest jobs
+    if (wave == 0) {
+        constexpr int small = kMoeTileRows;
+        const int EPW = (E + 63) / 64;
+        const int e0 = min(lane * EPW, E), e1 = min(e0 + EPW, E);
+        int lc = 0, lf = 0, lb = 0, ls = 0;
+        for (int e = e0; e < e1; ++e) {
+            const int c = cnt[e] + cnt2[e], r = c % rpc;
+            lc += c;
+            lf += c / rpc;
+            lb += r > small;
+            ls += r != 0 && r <= small;
+        }
+        const int ic = wave_incl_sum(lc), iF = wave_incl_sum(lf), ib = wave_incl_sum(lb), is = wave_incl_sum(ls);
+        const int nfull = __builtin_amdgcn_readlane(iF, 63), nbig = __builtin_amdgcn_readlane(ib, 63);
+        const int nsmall = __builtin_amdgcn_readlane(is, 63);
+        int o = ic - lc, fo = iF - lf, bo = nfull + ib - lb, so = nfull + nbig + is - ls;
+        for (int e = e0; e < e1; ++e) {
+            const int c = cnt[e] + cnt2[e], nf = c / rpc, r = c % rpc;
+            off[e] = o;
+            for (int k = 0; k < nf; ++k) {
+                chunk_info[(fo + k) * 3 + 0] = e;
+                chunk_info[(fo + k) * 3 + 1] = o + k * rpc;
+                chunk_info[(fo + k) * 3 + 2] = rpc;
+            }
+            fo += nf;
+            if (r != 0) {
+                int &po = r > small ? bo : so;
+                chunk_info[po * 3 + 0] = e;
+                chunk_info[po * 3 + 1] = o + nf * rpc;
+                chunk_info[po * 3 + 2] = r;
+                ++po;
+            }
+            o += c;
+        }
+        if (lane == 0) {
+            *nchunks = nfull + nbig + nsmall;
+            *err = s_bad;
+        }
+    }
+    // the scatter needs the offsets alone: an LDS barrier with no memory
+    // fence (a fence would wait for the chunk table's stores, which drain
+    // together with the scatter's)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // ---- scatter: register-held pairs at their rank, the others after them
 #pragma unroll
     for (int u = 0; u < kRoutePairsPerThread; ++u) {
         const int pr = tid + 1024 * u;
-        if (pr < P && ev[u] >= 0 && ev[u] < E) sorted[off[ev[u]] + atomicAdd(&fill[ev[u]], 1)] = pr;
+        if (pr < P && ev[u] >= 0 && ev[u] < E) sorted[off[ev[u]] + rk[u]] = pr;
     }
     for (int pr = tid + 1024 * kRoutePairsPerThread; pr < P; pr += 1024) {
         const int e = ids[(int64_t)(pr / n_used) * ids_stride + pr % n_used];
-        if (e >= 0 && e < E) sorted[off[e] + atomicAdd(&fill[e], 1)] = pr;
-    }
-    // ---- chunk table
-    int o = o0, fo = bf + iF - lf, bo = nfull + bb + ib - lb, so = nfull + nbig + bs + is - ls;
-    for (int e = e0; e < e1; ++e) {
-        const int c = cnt[e], nf = c / rpc, r = c % rpc;
-        for (int k = 0; k < nf; ++k) {
-            chunk_info[(fo + k) * 3 + 0] = e;
-            chunk_info[(fo + k) * 3 + 1] = o + k * rpc;
-            chunk_info[(fo + k) * 3 + 2] = rpc;
-        }
-        fo += nf;
-        if (r != 0) {
-            int &po = r > small ? bo : so;
-            chunk_info[po * 3 + 0] = e;
-            chunk_info[po * 3 + 1] = o + nf * rpc;
-            chunk_info[po * 3 + 2] = r;
-            ++po;
-        }
-        o += c;
-    }
-    if (tid == 0) {
-        *nchunks = nfull + nbig + nsmall;
-        *err = s_bad;
+        if (e >= 0 && e < E) sorted[off[e] + cnt[e] + atomicAdd(&fill[e], 1)] = pr;
     }
 }
 
@@ -1619,7 +1612,7 @@ hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t
 hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, int64_t n_used, int64_t E,
                             int rpc, int32_t *sorted, int32_t *chunk_info, int32_t *nchunks, int32_t *err,
                             const MoeSplit &sp, hipStream_t s) {
-    const size_t shmem = (size_t)E * 3 * sizeof(int32_t);
+    const size_t shmem = (size_t)E * 4 * sizeof(int32_t);
     // workgroup 0 routes; workgroups 1.. split 1024 / tpt activation rows each
     MoeSplit spl = sp;
     const int npc = sp.NQ * 16;

@@ -261,8 +261,10 @@ def test_moe_small_strided(q, orc):
 
 
 @pytest.mark.parametrize("E,K,N,T,n_used", [(20, 96, 40, 37, 4), (3, 32, 16, 1, 1), (9, 256, 300, 70, 8),
-                                             (128, 64, 48, 64, 8)])
+                                             (128, 64, 48, 64, 8), (700, 32, 16, 1100, 8)])
 def test_moe_shapes(q, orc, E, K, N, T, n_used):
+    """(700, ..., 1100, 8): 11 experts per lane of the routing scan and 8800
+    pairs, past the 8192 the routing holds in registers."""
     _moe_case(q, orc, E, K, N, T, n_used, seed=E + K + N + T)
 
 
@@ -396,7 +398,8 @@ def _moe_slot_case(q, orc, E, K, N, T, n_used, seed=0, pad=0):
 
 
 @pytest.mark.parametrize("E,K,N,T,n_used,pad", [(6, 64, 24, 10, 3, 0), (20, 96, 40, 37, 4, 1), (3, 32, 16, 1, 1, 0),
-                                                 (9, 768, 300, 70, 8, 4), (128, 64, 48, 64, 8, 0)])
+                                                 (9, 768, 300, 70, 8, 4), (128, 64, 48, 64, 8, 0),
+                                                 (700, 32, 16, 1100, 8, 0)])
 def test_moe_per_slot_shapes(q, orc, E, K, N, T, n_used, pad):
     """A row per (token, slot): ragged N, a partial last record (K = 96),
     unaligned rows (ldx_slot = K + 1), padded rows (K + 4), one token."""
