@@ -1625,15 +1625,18 @@ hipError_t launch_moe_route(const int32_t *ids, int64_t ids_stride, int64_t T, i
 
 hipError_t launch_q4_moe(const Q4Params &p, bool per_slot, int64_t max_chunks, hipStream_t s,
                          const char **variant) {
-    constexpr int WAVES = 8, C = 2;
+    // 4 wavefronts x 4 strips: each A fragment read from LDS feeds four
+    // strips' MFMAs (half the LDS reads per MFMA of 8 x 2, which tied the
+    // LDS bandwidth to the MFMA rate); 168 VGPRs, three workgroups per CU
+    constexpr int WAVES = 4, C = 4;
     const int64_t groups = ceil_div(p.NS, C * WAVES);
     *variant = "q4_moe_m32";
     // 8 XCDs x groups x (chunk slots per XCD)
     const dim3 g((unsigned)(8 * groups * ceil_div(max_chunks, 8))), b(WAVES * 64);
     if (per_slot)
-        hipLaunchKernelGGL((k_q4_moe<WAVES, C, 4, true>), g, b, 0, s, p);
+        hipLaunchKernelGGL((k_q4_moe<WAVES, C, 3, true>), g, b, 0, s, p);
     else
-        hipLaunchKernelGGL((k_q4_moe<WAVES, C, 4, false>), g, b, 0, s, p);
+        hipLaunchKernelGGL((k_q4_moe<WAVES, C, 3, false>), g, b, 0, s, p);
     return hipGetLastError();
 }
 
