@@ -806,15 +806,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
     const uint8_t *hdr = p.recs;
     const uint8_t *recs = hdr + kHeaderBytes;
 
-    // ---- activation loads (first: the staging waits for them alone)
+    // ---- activation loads (first: the staging waits for them alone).  Rows
+    // past M read row M - 1 (they reach only outputs that are never stored)
+    // and blocks past K read the last block, whose copies meet zero (d, m) in
+    // the padded records, so no value needs masking: the row maxima and the
+    // products of the real rows and blocks are those of the real values.
     float xr[PPT][8];
-    bool xok[PPT];
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
         const int pc = tid + i * NT;
         const int r = pc & 15, g = (pc >> 4) & 3, bl = pc >> 6;
         const int b = q0 * 4 + bl;
-        xok[i] = r < M && b < p.NB;
         const float *src = p.X + (int64_t)min(r, M - 1) * p.ldx + min(b, p.NB - 1) * 32 + g * 8;
         if (XVEC) {
             const v4f lo = *(const v4f *)src;
@@ -865,7 +867,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) am = fmaxf(am, xok[i] ? fabsf(xr[i][e]) : 0.0f);
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(xr[i][e]));
     am = fmaxf(am, __shfl_xor(am, 16));
     am = fmaxf(am, __shfl_xor(am, 32));
     if (lane < 16) s_rmax[wave][lane] = am;
@@ -885,8 +887,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
         uint32_t w[2][4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            const float x0 = xok[i] ? xr[i][e] : 0.0f;
-            const float x1 = xok[i] ? xr[i][e + 1] : 0.0f;
+            const float x0 = xr[i][e];
+            const float x1 = xr[i][e + 1];
             bsum += x0;
             bsum += x1;
             const float s0 = __builtin_ldexpf(x0, sc), s1 = __builtin_ldexpf(x1, sc);
