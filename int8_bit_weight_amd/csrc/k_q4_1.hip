@@ -774,7 +774,8 @@ __global__ __launch_bounds__(W * 64) void k_q4_gemv1(Q4Params p) {
 //     exact).  The terms are stored at sA[bl][term] in MFMA lane order (lane
 //     16 g + r), against the exact fp16 codes; the epilogue multiplies the
 //     d term by 2^-sc (each k split undoes its own scale).  Rows past M and
-//     blocks past K stage zeros.  The (unscaled) block
+//     blocks past K stage copies of row M - 1 and of the last block (outputs
+//     never stored; zero (d, m)).  The (unscaled) block
 //     sums (the four k-octets of a (row, block) lie in lanes r, r+16, r+32,
 //     r+48 of one wavefront) are split the same way into the m-term A
 //     operand: row r, block bl at byte 16 r + 2 (bl % 8) of sXM[bl / 8].
