@@ -261,10 +261,12 @@ def test_moe_small_strided(q, orc):
 
 
 @pytest.mark.parametrize("E,K,N,T,n_used", [(20, 96, 40, 37, 4), (3, 32, 16, 1, 1), (9, 256, 300, 70, 8),
-                                             (128, 64, 48, 64, 8), (700, 32, 16, 1100, 8)])
+                                             (128, 64, 48, 64, 8), (700, 32, 16, 1100, 8), (8192, 32, 16, 64, 8)])
 def test_moe_shapes(q, orc, E, K, N, T, n_used):
     """(700, ..., 1100, 8): 11 experts per lane of the routing scan and 8800
-    pairs, past the 8192 the routing holds in registers."""
+    pairs, past the 8192 the routing holds in registers; (8192, ...): the
+    largest expert count the call accepts (128 KB of routing tables in LDS,
+    128 experts per lane of the scan)."""
     _moe_case(q, orc, E, K, N, T, n_used, seed=E + K + N + T)
 
 
