@@ -398,7 +398,9 @@ const char *qmm_status_string(qmm_status s);
 /* hipError_t of the last failed HIP call on this thread (0 if none). */
 int qmm_last_hip_error(void);
 /* Name of the kernel variant the last call on this thread launched
- * (diagnostics; "" before the first call). */
+ * (diagnostics; "" before the first call).  With QMM_TRACE=1 in the
+ * environment when the library loads, every call also prints its variant
+ * (and the int8 products their launch plan) to stderr. */
 const char *qmm_last_variant(void);
 
 /*

@@ -12,8 +12,6 @@
 // second MFMA against an all-ones operand gives the block's row sums for the
 // m term.  The fp32 combination y += d*float(D) + m*float(S) is the only
 // rounding.
-#include <cstdlib>
-
 #include "q4_internal.h"
 
 namespace qmm {
@@ -118,28 +116,15 @@ hipError_t launch_q4q8_w(const Q4Q8Params &p, bool avec, hipStream_t s) {
 
 }  // namespace
 
-static int env_or(const char *name, int dflt) {
-    const char *v = std::getenv(name);
-    return (v && *v) ? std::atoi(v) : dflt;
-}
-
 hipError_t launch_q4_q8(const Q4Q8Params &p, hipStream_t s, const char **variant) {
     // 8 wavefronts per strip (4 below 16 records), 2 records in flight per
     // wavefront: measured best of 4/8/16 wavefronts x 2/4/8 records on the
     // 8B shapes (32 and 112 records per strip); deeper rings or more
     // wavefronts than records load clamped duplicates and were up to 6x
-    // slower.  QMM_Q4Q8_WAVES / QMM_Q4Q8_RING override the choice (tuning).
+    // slower
     const bool avec = ((uintptr_t)p.Xq % 8) == 0 && (p.ldq % 8) == 0;
     *variant = "q4_q8_m16";
-    static const int ow = env_or("QMM_Q4Q8_WAVES", 0), orr = env_or("QMM_Q4Q8_RING", 0);
-    const int w = ow ? ow : (p.NQ >= 16 ? 8 : 4);
-    const int rr = orr ? orr : 2;
-    if (w == 16) return rr == 2 ? launch_q4q8_w<16, 2>(p, avec, s) : rr == 8 ? launch_q4q8_w<16, 8>(p, avec, s)
-                                                                           : launch_q4q8_w<16, 4>(p, avec, s);
-    if (w == 8) return rr == 2 ? launch_q4q8_w<8, 2>(p, avec, s) : rr == 8 ? launch_q4q8_w<8, 8>(p, avec, s)
-                                                                         : launch_q4q8_w<8, 4>(p, avec, s);
-    return rr == 2 ? launch_q4q8_w<4, 2>(p, avec, s) : rr == 8 ? launch_q4q8_w<4, 8>(p, avec, s)
-                                                             : launch_q4q8_w<4, 4>(p, avec, s);
+    return p.NQ >= 16 ? launch_q4q8_w<8, 2>(p, avec, s) : launch_q4q8_w<4, 2>(p, avec, s);
 }
 
 }  // namespace qmm
