@@ -132,6 +132,10 @@ def test_moe_rejections(q):
     assert _moe(q, False, K=48, ldx=48) == UNS
     assert _moe(q, False, ws_bytes=16) == q.QMM_ERR_WORKSPACE
     assert _moe(q, False, T=0) == q.QMM_OK
+    # expert counts: at least one, at most 8192 (the routing tables live in LDS)
+    assert _moe(q, False, E=0) == INV
+    assert _moe(q, False, n_used=0) == INV
+    assert _moe(q, False, E=8193) == UNS
     # per-slot rows: ldx_slot >= K and the token stride covers n_used rows
     assert _moe(q, True, ldx_slot=63, ldx=128) == INV
     assert _moe(q, True, ldx_slot=64, ldx=127) == INV
