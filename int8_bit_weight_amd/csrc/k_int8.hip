@@ -775,8 +775,7 @@ hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t 
         return avec ? launch_decode_shape<2, true>(p, plan.waves, plan.tpw, s)
                     : launch_decode_shape<2, false>(p, plan.waves, plan.tpw, s);
     }
-    *variant = "int8_prefill_256x128";
-    return launch_int8_prefill(p, s);
+    return launch_int8_prefill(p, s, variant);
 }
 
 template <int WAVES, int E, int TPQ, int S, bool GROUPED>

@@ -487,13 +487,282 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
         }
 }
 
+
+// ------------------------------------------------ wide-tile prefill ---
+// 256 x 224 output tile (14 strips) per workgroup of 8 wavefronts in a 4 x 2
+// grid, each owning 64 rows x 112 columns: 4 x 7 tiles of
+// v_mfma_i32_16x16x64_i8 (112 int32 accumulators per lane), two wavefronts
+// per SIMD.  It serves shapes whose 256 x 224 tiles fill the CUs in fewer
+// rounds of work than the 256 x 128 ones (M = 2048, N = 14336: 512 tiles in
+// two rounds against 896 in three and a half), for 16-byte aligned A and
+// K % 128 == 0.  Per k step a workgroup copies 23 KB for 3.7 M int8
+// operations (the 256 x 128 tile: 24 KB for 4.2 M) and each wavefront reads
+// 11 KB of operands from LDS for its 28 MFMAs.
+//
+// A pair buffer holds two k steps: the 256 rows' activations in the pair
+// layout of k_int8_prefill (32 KiB) and the 14 strips' packed weight tiles of
+// both steps as stored (28 KiB); two pair buffers (120 KiB).  The 16 x 16 x
+// 64 operand of lane L is row (column) L % 16 and 16-k chunk L / 16 of the
+// step: for A, chunk c = 4 hs + L / 16 of the pair, in block row / 8 at slot
+// 8 (row % 8) + (c ^ swz), so 16 consecutive lanes touch 16 distinct 16-byte
+// bank groups; for B, chunk L of the tile.
+//
+// Pair q sits in buffer q % 2.  Step 2q reads the operands of step 2q+1 and
+// runs the MFMAs of step 2q.  Step 2q+1 waits for this wavefront's copies of
+// pair q+1 (the only ones in flight), then a barrier: every wavefront has
+// its copies of pair q+1 landed and its reads of buffer q % 2 done (step
+// 2q+1's operands were read during step 2q).  It then issues the copies of
+// pair q+2 into buffer q % 2, reads the operands of step 2q+2 from the other
+// buffer and runs its own MFMAs.  Copies and reads past the last pair read
+// clamped addresses and land in a buffer no later step reads.
+constexpr int PW_BN = 224, PW_S = PW_BN / kTileN;
+
+template <bool HAS_ZB, bool FLIP>
+__global__ __launch_bounds__(512) void k_int8_prefill_w(Int8GemmParams p) {
+    constexpr int SPA = 2 * PF_BM * kTileK;   // a pair's activations: 32 KiB
+    constexpr int SPB1 = PW_S * kTileBytes;  // one step's weight tiles: 14 KiB
+    constexpr int SP = SPA + 2 * SPB1;       // 60 KiB
+    __shared__ __attribute__((aligned(16))) int8_t sP0[SP], sP1[SP];
+    __shared__ __attribute__((aligned(16))) float s_rs[PF_BM];
+    __shared__ int32_t s_za[PF_BM];
+    __shared__ ColOps s_col[PW_BN];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    // tile order of k_int8_prefill: XCD-major renumbering, then groups of 4
+    // row tiles walked column by column
+    const int tiles_n = (p.NS + PW_S - 1) / PW_S;
+    const int tiles_m = (p.M + PF_BM - 1) / PF_BM;
+    int w = blockIdx.x;
+    if (gridDim.x % 8 == 0) w = (w % 8) * (gridDim.x / 8) + w / 8;
+    constexpr int GM = 4;
+    const int gq = w / (GM * tiles_n), gr = w % (GM * tiles_n);
+    const int gm = min(GM, tiles_m - gq * GM);
+    const int bm = gq * GM + gr % gm;
+    const int bn = gr / gm;
+    const int m0 = bm * PF_BM;
+    const int strip0 = bn * PW_S;
+    const int KT = p.KT, NP = KT / 2;
+
+    // copies of pair q, 8 per wavefront: activation blocks 4 w .. 4 w + 3
+    // (rows 32 w + 8 u + L / 8, whole 128-byte rows), and weight tiles
+    // i = w + 8 u of the pair's 28 (strip i % 14 of step i / 14; wavefronts
+    // 4..7 copy tile 27 again as their fourth: the same bytes to the same
+    // place)
+    const int a_r8 = lane >> 3;
+    const int a_c0 = (lane & 7) ^ pf_pair_swz(a_r8, 0), a_c1 = (lane & 7) ^ pf_pair_swz(a_r8, 1);
+    const int a_row0 = m0 + 32 * wave + a_r8;
+    const int8_t *bt_src[4];
+    int bt_dst[4], bt_hs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = min(wave + 8 * u, 2 * PW_S - 1);
+        const int sl = i % PW_S, hs = i / PW_S;
+        bt_src[u] = p.codes + (int64_t)min(strip0 + sl, p.NS - 1) * KT * kTileBytes + lane * 16;
+        bt_dst[u] = SPA + hs * SPB1 + sl * kTileBytes;
+        bt_hs[u] = hs;
+    }
+    auto copy_pair = [&](auto BUF, int q) {
+        int8_t *buf = decltype(BUF)::value ? sP1 : sP0;
+        const int kb0 = min(q * 2 * kTileK + a_c0 * 16, p.K - 16);
+        const int kb1 = min(q * 2 * kTileK + a_c1 * 16, p.K - 16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = min(a_row0 + 8 * u, p.M - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(p.A + (int64_t)row * p.lda + ((u & 1) ? kb1 : kb0)),
+                                             (__attribute__((address_space(3))) void *)(buf + (4 * wave + u) * 1024),
+                                             16, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kt = min(2 * q + bt_hs[u], KT - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(bt_src[u] + (int64_t)kt * kTileBytes),
+                                             (__attribute__((address_space(3))) void *)(buf + bt_dst[u]), 16, 0, 0);
+        }
+    };
+
+    // operand offsets: A of row tile t (adds 2 KiB per tile) and step hs; B of
+    // the wavefront's strip j (adds 1 KiB per strip) and step hs
+    int a_rd[2], b_rd[2];
+    {
+        const int R = lane & 15, r8 = R & 7, blk = 8 * wm + (R >> 3);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const int c = 4 * hs + (lane >> 4);
+            a_rd[hs] = blk * 1024 + (8 * r8 + (c ^ pf_pair_swz(r8, blk & 1))) * 16;
+            b_rd[hs] = SPA + hs * SPB1 + 7 * wn * kTileBytes + lane * 16;
+        }
+    }
+    v4i fa[2][4], fb[2][7];
+    auto read_ops = [&](auto F, auto HS, const int8_t *buf) {
+        constexpr int f = decltype(F)::value, hs = decltype(HS)::value;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) fa[f][t] = *(const v4i *)(buf + a_rd[hs] + t * 2048);
+#pragma unroll
+        for (int j = 0; j < 7; ++j) fb[f][j] = *(const v4i *)(buf + b_rd[hs] + j * kTileBytes);
+    };
+    v4i acc[4][7], accr[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        accr[t] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 7; ++j) acc[t][j] = v4i{0, 0, 0, 0};
+    }
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    auto mfmas = [&](auto F) {
+        constexpr int f = decltype(F)::value;
+        if constexpr (FLIP) {
+            // uint8 activations land unshifted: shift this step's operands
+#pragma unroll
+            for (int t = 0; t < 4; ++t) fa[f][t] ^= 0x80808080;
+        }
+#pragma unroll
+        for (int j = 0; j < 7; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t][j] = mfma_i8(fa[f][t], fb[f][j], acc[t][j]);
+        if constexpr (HAS_ZB) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) accr[t] = mfma_i8(fa[f][t], ones, accr[t]);
+        }
+    };
+    // instruction order of a step: the 11 operand reads (and, in odd steps,
+    // the 8 copies first) spread between the MFMAs
+    auto schedule = [&](auto ODD) {
+        constexpr int MFMA = 0x008, VMEM = 0x060, DS_RD = 0x100;
+        if constexpr (decltype(ODD)::value) {
+            static_for<8>([&](auto) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(VMEM, 1, 0);
+            });
+        }
+        static_for<11>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(MFMA, decltype(ODD)::value ? 9 : 17, 0);
+        if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
+    };
+
+    copy_pair(ic<0>{}, 0);
+    copy_pair(ic<1>{}, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<8>();
+    lds_barrier();
+    read_ops(ic<0>{}, ic<0>{}, sP0);
+    auto pair = [&](auto BUF, int q) {
+        constexpr int b = decltype(BUF)::value;
+        const int8_t *cur = b ? sP1 : sP0;
+        const int8_t *nxt = b ? sP0 : sP1;
+        // step 2q
+        read_ops(ic<1>{}, ic<1>{}, cur);
+        mfmas(ic<0>{});
+        schedule(ic<0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        // step 2q + 1
+        wait_vmcnt<0>();
+        lds_barrier();
+        copy_pair(BUF, q + 2);
+        read_ops(ic<0>{}, ic<0>{}, nxt);
+        mfmas(ic<1>{});
+        schedule(ic<1>{});
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int q = 0;
+    for (; q + 1 < NP; q += 2) {
+        pair(ic<0>{}, q);
+        pair(ic<1>{}, q + 1);
+    }
+    if (q < NP) pair(ic<0>{}, q);
+    wait_vmcnt<0>();
+
+    // ---- epilogue (as k_int8_prefill's): row and column operands in LDS
+    for (int r = tid; r < PF_BM; r += 512) {
+        const int m = min(m0 + r, p.M - 1);
+        const float v = *(p.row_scale ? p.row_scale + m : p.col_scale);
+        s_rs[r] = p.row_scale ? v : 1.0f;
+        s_za[r] = row_za(p, m);
+    }
+    if (tid < PW_BN) s_col[tid] = load_colops_c(p, strip0 * kTileN + tid);
+    __syncthreads();
+    const bool whole = m0 + PF_BM <= p.M && (strip0 + PW_S) * kTileN <= p.N;
+    // element e of tile (t, j): row 64 wm + 16 t + 4 (L / 16) + e, column
+    // 112 wn + 16 j + L % 16 of the workgroup's tile
+    if (!HAS_ZB && p.outputs == QMM_OUT_F32 && p.zAs == 0 && !p.za_row && whole) {
+        float cm[7], cb[7];
+#pragma unroll
+        for (int j = 0; j < 7; ++j) {
+            const ColOps c = s_col[112 * wn + 16 * j + (lane & 15)];
+            cm[j] = c.cs;
+            cb[j] = c.bias_f;
+        }
+        float *ybase = p.y_f32 + (int64_t)(m0 + 64 * wm + 4 * (lane >> 4)) * p.ld_f32 + strip0 * kTileN +
+                       112 * wn + (lane & 15);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const v4f rs = *(const v4f *)(&s_rs[64 * wm + 16 * t + 4 * (lane >> 4)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float *yrow = ybase + (int64_t)(16 * t + e) * p.ld_f32;
+#pragma unroll
+                for (int j = 0; j < 7; ++j) {
+                    const float mult = (rs[e] * cm[j]) * p.scale;
+                    yrow[16 * j] = fmaf((float)acc[t][j][e], mult, cb[j]);
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 7; ++j) {
+            const int cl = 112 * wn + 16 * j + (lane & 15);
+            const int n = strip0 * kTileN + cl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rl = 64 * wm + 16 * t + 4 * (lane >> 4) + e;
+                const int m = m0 + rl;
+                if (m < p.M && n < p.N)
+                    epilogue_store_c(p, m, n, (uint32_t)acc[t][j][e], HAS_ZB ? accr[t][e] : 0, HAS_ZB, s_rs[rl],
+                                     s_za[rl], s_col[cl]);
+            }
+        }
+}
+
 }  // namespace
 
-hipError_t launch_int8_prefill(const Int8GemmParams &p, hipStream_t s) {
+// The 256 x 224 tile where its tiles fill the CUs in fewer rounds of work:
+// each CU's share, rounds of tiles times strips per tile, against the 256 x
+// 128 tile's (aligned A, K % 128 == 0 only).
+static bool use_wide_tile(const Int8GemmParams &p) {
+    constexpr int64_t kCUs = 256;
+    if (!p.a_vec || p.K % (2 * kTileK) != 0) return false;
+    const int64_t tm = ceil_div(p.M, PF_BM);
+    const int64_t t128 = ceil_div(p.NS, PF_BN / kTileN) * tm, t224 = ceil_div(p.NS, PW_S) * tm;
+    return ceil_div(t224, kCUs) * PW_S < ceil_div(t128, kCUs) * (PF_BN / kTileN);
+}
+
+hipError_t launch_int8_prefill(const Int8GemmParams &p, hipStream_t s, const char **variant) {
+    const bool has_zb = p.zBs != 0 || p.zb_col;
+    if (use_wide_tile(p)) {
+        *variant = "int8_prefill_256x224";
+        const dim3 grid((unsigned)(ceil_div(p.NS, PW_S) * ceil_div(p.M, PF_BM))), b(512);
+        if (has_zb && p.a_u8)
+            hipLaunchKernelGGL((k_int8_prefill_w<true, true>), grid, b, 0, s, p);
+        else if (has_zb)
+            hipLaunchKernelGGL((k_int8_prefill_w<true, false>), grid, b, 0, s, p);
+        else if (p.a_u8)
+            hipLaunchKernelGGL((k_int8_prefill_w<false, true>), grid, b, 0, s, p);
+        else
+            hipLaunchKernelGGL((k_int8_prefill_w<false, false>), grid, b, 0, s, p);
+        return hipGetLastError();
+    }
+    *variant = "int8_prefill_256x128";
     dim3 grid((unsigned)(ceil_div(p.NS, PF_BN / kTileN) * ceil_div(p.M, PF_BM)));
     const bool fast = p.a_vec && (p.K % kTileK) == 0;
     const dim3 b(256);
-    if (p.zBs != 0 || p.zb_col) {
+    if (has_zb) {
         if (fast && p.a_u8)
             hipLaunchKernelGGL((k_int8_prefill<true, true, true>), grid, b, 0, s, p);
         else if (fast)

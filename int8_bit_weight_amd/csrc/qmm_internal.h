@@ -165,7 +165,7 @@ hipError_t launch_pack_b_raw(const void *B, int u8, int64_t ldb, const PackedBLa
 hipError_t launch_quantize_rows(const float *X, int64_t M, int64_t K, int64_t ldx, int8_t *Xq,
                                 int64_t ldq, float *row_scale, hipStream_t s);
 // the prefill kernel (M > 32), launched by launch_int8_gemm
-hipError_t launch_int8_prefill(const Int8GemmParams &p, hipStream_t s);
+hipError_t launch_int8_prefill(const Int8GemmParams &p, hipStream_t s, const char **variant);
 hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                             const char **variant);
 hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,

@@ -305,7 +305,7 @@ def _axis_case(q, orc, M, K, N, a_u8, b_u8, seed, expect_variant, zx=None, zw=No
     (1, 1024, 1024, True, False, "int8_decode_m16"), (16, 1056, 272, False, True, "int8_decode_m16"),
     (32, 3072, 1024, True, True, "int8_decode_m32"), (3, 100, 16400, True, False, "int8_decode_wide_m16"),
     (29, 1024, 16500, False, True, "int8_decode_wide_m32"), (256, 1024, 1024, False, False, "int8_prefill_256x128"),
-    (300, 200, 130, True, True, "int8_prefill_256x128")])
+    (300, 200, 130, True, True, "int8_prefill_256x128"), (300, 256, 16475, True, False, "int8_prefill_256x224")])
 def test_per_axis_zero_points(q, orc, M, K, N, a_u8, b_u8, variant):
     _axis_case(q, orc, M, K, N, a_u8, b_u8, seed=M * 3 + K + N, expect_variant=variant)
 
@@ -466,6 +466,59 @@ def test_prefill_full_compare(q, orc, M, K, N, zA, zB):
                expect_variant="int8_prefill_256x128")
 
 
+def _prefill_variant(M, K, N):
+    """The prefill tile the library picks (aligned A): 256 x 224 where its
+    tiles fill the 256 CUs in fewer rounds of work than 256 x 128 ones
+    (rounds times strips per tile) and K % 128 == 0."""
+    ns, tm = -(-N // 16), -(-M // 256)
+    t128, t224 = -(-ns // 8) * tm, -(-ns // 14) * tm
+    wide = K % 128 == 0 and -(-t224 // 256) * 14 < -(-t128 // 256) * 8
+    return "int8_prefill_256x224" if wide else "int8_prefill_256x128"
+
+
+@pytest.mark.parametrize("M,K,N,zA,zB,a_u8,req", [
+    (256, 128, 32777, 0, 0, False, False),    # one row tile, 2049 strips: ragged last tile
+    (300, 256, 16475, 7, -3, False, True),    # two row tiles (ragged M), zero points, int8 out
+    (200, 384, 32790, 200, 5, True, True),    # uint8 A, odd pair count (3 pairs)
+    (257, 128, 16480, 0, 9, False, False),    # zB only (row sums), one row past a tile
+    (256, 128, 32928, 0, 0, False, False)])   # whole tiles only (147 x 224 columns)
+def test_prefill_wide_tile(q, orc, M, K, N, zA, zB, a_u8, req):
+    """The 256 x 224 tile against the oracle: int32 bit-exact, fp32 within
+    2e-6 of max|Y|, int8 requant bit-exact, on shapes where it is picked."""
+    assert _prefill_variant(M, K, N) == "int8_prefill_256x224"
+    g = np.random.default_rng(M * 7 + K + N)
+    A = wl.uniform_u8(g, (M, K)) if a_u8 else wl.uniform_i8(g, (M, K))
+    B = wl.uniform_i8(g, (K, N))
+    rs = (g.uniform(0.5, 1.5, M) / 127).astype(np.float32)
+    requant = None
+    if req:
+        requant = dict(u8=False, bias_i32=g.integers(-3000, 3000, N).astype(np.int32), zp_out=3)
+    _gemm_case(q, orc, A, zA, B, zB, rs=rs, bias=wl.normal_f32(g, (N,)), scale=np.float32(0.001),
+               requant=requant, expect_variant="int8_prefill_256x224")
+
+
+def test_prefill_wide_tile_fp32_only(q, orc):
+    """The fp32-only epilogue of the 256 x 224 tile (no zero points, whole
+    tiles: the branch-free store path the M = 2048 prefill takes) and, on a
+    ragged shape, its general path, against the oracle."""
+    import torch
+    dev = torch_dev()
+    for M, K, N in ((256, 256, 32928), (260, 128, 16475)):
+        assert _prefill_variant(M, K, N) == "int8_prefill_256x224"
+        g = np.random.default_rng(M + N)
+        A = wl.uniform_i8(g, (M, K))
+        B = wl.uniform_i8(g, (K, N))
+        rs = (g.uniform(0.5, 1.5, M) / 127).astype(np.float32)
+        bias = wl.normal_f32(g, (N,))
+        p = q.pack_b_int8_raw(to_dev(B))
+        yf = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+        q.int8_gemm(to_dev(A), 0, p, 0, out_f32=yf, row_scale=to_dev(rs), bias_f32=to_dev(bias),
+                    scale=float(np.float32(0.01)))
+        assert q.last_variant() == "int8_prefill_256x224"
+        ref = orc.epilogue_f64(orc.int8_gemm_i64(A, 0, B, 0), rs, None, np.float32(0.01), bias)
+        assert max_rel_err(to_np(yf), ref) <= F32_TOL
+
+
 @pytest.mark.parametrize("shape", range(len(wl.PREFILL_SHAPES)))
 def test_prefill_full_size_sampled(q, orc, shape):
     """M = 2048 tokens at the 8B-class shapes: packB of fp32 N(0,0.02)
@@ -479,7 +532,11 @@ def test_prefill_full_size_sampled(q, orc, shape):
     y32 = torch.empty((wl.PREFILL_M, N), dtype=torch.int32, device=dev)
     yf = torch.empty((wl.PREFILL_M, N), dtype=torch.float32, device=dev)
     q.int8_gemm(to_dev(d["A"]), 0, p, 0, out_i32=y32, out_f32=yf, row_scale=to_dev(d["rs"]))
-    assert q.last_variant() == "int8_prefill_256x128"
+    assert q.last_variant() == _prefill_variant(wl.PREFILL_M, K, N)
+    # the benchmark's form: fp32 output alone (the branch-free epilogue)
+    yf1 = torch.empty((wl.PREFILL_M, N), dtype=torch.float32, device=dev)
+    q.int8_gemm(to_dev(d["A"]), 0, p, 0, out_f32=yf1, row_scale=to_dev(d["rs"]))
+    assert torch.equal(yf1, yf)
     g = np.random.default_rng(99 + shape)
     im = np.concatenate([g.integers(0, wl.PREFILL_M, 4096), [0, 0, wl.PREFILL_M - 1, wl.PREFILL_M - 1]])
     in_ = np.concatenate([g.integers(0, N, 4096), [0, N - 1, 0, N - 1]])
