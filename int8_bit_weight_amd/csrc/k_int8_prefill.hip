@@ -515,24 +515,28 @@ __global__ __launch_bounds__(256) void k_int8_prefill(Int8GemmParams p) {
 // pair q+2 into buffer q % 2, reads the operands of step 2q+2 from the other
 // buffer and runs its own MFMAs.  Copies and reads past the last pair read
 // clamped addresses and land in a buffer no later step reads.
-constexpr int PW_BN = 224, PW_S = PW_BN / kTileN;
+constexpr int PW_S = 14;  // strips of the wide tile (224 columns)
 
-template <bool HAS_ZB, bool FLIP>
+// S strips per tile (14: the 256 x 224 tile), S / 2 per wavefront column
+template <int S, bool HAS_ZB, bool FLIP>
 __global__ __launch_bounds__(512) void k_int8_prefill_w(Int8GemmParams p) {
+    constexpr int BN = 16 * S, JW = S / 2;
+    constexpr int NB = (2 * S + 7) / 8;  // weight-tile copies per wavefront and pair
+    static_assert(S % 2 == 0 && NB <= 4, "tile width");
     constexpr int SPA = 2 * PF_BM * kTileK;   // a pair's activations: 32 KiB
-    constexpr int SPB1 = PW_S * kTileBytes;  // one step's weight tiles: 14 KiB
-    constexpr int SP = SPA + 2 * SPB1;       // 60 KiB
+    constexpr int SPB1 = S * kTileBytes;     // one step's weight tiles (14 KiB at S = 14)
+    constexpr int SP = SPA + 2 * SPB1;       // 60 KiB at S = 14
     __shared__ __attribute__((aligned(16))) int8_t sP0[SP], sP1[SP];
     __shared__ __attribute__((aligned(16))) float s_rs[PF_BM];
     __shared__ int32_t s_za[PF_BM];
-    __shared__ ColOps s_col[PW_BN];
+    __shared__ ColOps s_col[BN];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     // tile order of k_int8_prefill: XCD-major renumbering, then groups of 4
     // row tiles walked column by column
-    const int tiles_n = (p.NS + PW_S - 1) / PW_S;
+    const int tiles_n = (p.NS + S - 1) / S;
     const int tiles_m = (p.M + PF_BM - 1) / PF_BM;
     int w = blockIdx.x;
     if (gridDim.x % 8 == 0) w = (w % 8) * (gridDim.x / 8) + w / 8;
@@ -542,23 +546,23 @@ __global__ __launch_bounds__(512) void k_int8_prefill_w(Int8GemmParams p) {
     const int bm = gq * GM + gr % gm;
     const int bn = gr / gm;
     const int m0 = bm * PF_BM;
-    const int strip0 = bn * PW_S;
+    const int strip0 = bn * S;
     const int KT = p.KT, NP = KT / 2;
 
-    // copies of pair q, 8 per wavefront: activation blocks 4 w .. 4 w + 3
+    // copies of pair q, 4 + NB per wavefront: activation blocks 4 w .. 4 w + 3
     // (rows 32 w + 8 u + L / 8, whole 128-byte rows), and weight tiles
-    // i = w + 8 u of the pair's 28 (strip i % 14 of step i / 14; wavefronts
-    // 4..7 copy tile 27 again as their fourth: the same bytes to the same
-    // place)
+    // i = w + 8 u of the pair's 2 S (strip i % S of step i / S; where 2 S is
+    // not a multiple of 8, the wavefronts past the last tile copy it again:
+    // the same bytes to the same place)
     const int a_r8 = lane >> 3;
     const int a_c0 = (lane & 7) ^ pf_pair_swz(a_r8, 0), a_c1 = (lane & 7) ^ pf_pair_swz(a_r8, 1);
     const int a_row0 = m0 + 32 * wave + a_r8;
-    const int8_t *bt_src[4];
-    int bt_dst[4], bt_hs[4];
+    const int8_t *bt_src[NB];
+    int bt_dst[NB], bt_hs[NB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = min(wave + 8 * u, 2 * PW_S - 1);
-        const int sl = i % PW_S, hs = i / PW_S;
+    for (int u = 0; u < NB; ++u) {
+        const int i = min(wave + 8 * u, 2 * S - 1);
+        const int sl = i % S, hs = i / S;
         bt_src[u] = p.codes + (int64_t)min(strip0 + sl, p.NS - 1) * KT * kTileBytes + lane * 16;
         bt_dst[u] = SPA + hs * SPB1 + sl * kTileBytes;
         bt_hs[u] = hs;
@@ -575,7 +579,7 @@ __global__ __launch_bounds__(512) void k_int8_prefill_w(Int8GemmParams p) {
                                              16, 0, 0);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const int kt = min(2 * q + bt_hs[u], KT - 1);
             __builtin_amdgcn_global_load_lds((const void *)(bt_src[u] + (int64_t)kt * kTileBytes),
                                              (__attribute__((address_space(3))) void *)(buf + bt_dst[u]), 16, 0, 0);
@@ -591,23 +595,23 @@ __global__ __launch_bounds__(512) void k_int8_prefill_w(Int8GemmParams p) {
         for (int hs = 0; hs < 2; ++hs) {
             const int c = 4 * hs + (lane >> 4);
             a_rd[hs] = blk * 1024 + (8 * r8 + (c ^ pf_pair_swz(r8, blk & 1))) * 16;
-            b_rd[hs] = SPA + hs * SPB1 + 7 * wn * kTileBytes + lane * 16;
+            b_rd[hs] = SPA + hs * SPB1 + JW * wn * kTileBytes + lane * 16;
         }
     }
-    v4i fa[2][4], fb[2][7];
+    v4i fa[2][4], fb[2][JW];
     auto read_ops = [&](auto F, auto HS, const int8_t *buf) {
         constexpr int f = decltype(F)::value, hs = decltype(HS)::value;
 #pragma unroll
         for (int t = 0; t < 4; ++t) fa[f][t] = *(const v4i *)(buf + a_rd[hs] + t * 2048);
 #pragma unroll
-        for (int j = 0; j < 7; ++j) fb[f][j] = *(const v4i *)(buf + b_rd[hs] + j * kTileBytes);
+        for (int j = 0; j < JW; ++j) fb[f][j] = *(const v4i *)(buf + b_rd[hs] + j * kTileBytes);
     };
-    v4i acc[4][7], accr[4];
+    v4i acc[4][JW], accr[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         accr[t] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < 7; ++j) acc[t][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < JW; ++j) acc[t][j] = v4i{0, 0, 0, 0};
     }
     const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
     auto mfmas = [&](auto F) {
@@ -618,7 +622,7 @@ __global__ __launch_bounds__(512) void k_int8_prefill_w(Int8GemmParams p) {
             for (int t = 0; t < 4; ++t) fa[f][t] ^= 0x80808080;
         }
 #pragma unroll
-        for (int j = 0; j < 7; ++j)
+        for (int j = 0; j < JW; ++j)
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[t][j] = mfma_i8(fa[f][t], fb[f][j], acc[t][j]);
         if constexpr (HAS_ZB) {
@@ -626,28 +630,29 @@ __global__ __launch_bounds__(512) void k_int8_prefill_w(Int8GemmParams p) {
             for (int t = 0; t < 4; ++t) accr[t] = mfma_i8(fa[f][t], ones, accr[t]);
         }
     };
-    // instruction order of a step: the 11 operand reads (and, in odd steps,
-    // the 8 copies first) spread between the MFMAs
+    // instruction order of a step: the 4 + JW operand reads (and, in odd
+    // steps, the 4 + NB copies first) spread between its 4 JW MFMAs
     auto schedule = [&](auto ODD) {
         constexpr int MFMA = 0x008, VMEM = 0x060, DS_RD = 0x100;
-        if constexpr (decltype(ODD)::value) {
-            static_for<8>([&](auto) {
+        constexpr int odd = decltype(ODD)::value, NC = odd ? 4 + NB : 0;
+        if constexpr (odd) {
+            static_for<NC>([&](auto) {
                 __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(VMEM, 1, 0);
             });
         }
-        static_for<11>([&](auto) {
+        static_for<4 + JW>([&](auto) {
             __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
             __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
         });
-        __builtin_amdgcn_sched_group_barrier(MFMA, decltype(ODD)::value ? 9 : 17, 0);
+        __builtin_amdgcn_sched_group_barrier(MFMA, 4 * JW - NC - (4 + JW), 0);
         if constexpr (HAS_ZB) __builtin_amdgcn_sched_group_barrier(MFMA, 4, 0);
     };
 
     copy_pair(ic<0>{}, 0);
     copy_pair(ic<1>{}, 1);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<8>();
+    wait_vmcnt<4 + NB>();
     lds_barrier();
     read_ops(ic<0>{}, ic<0>{}, sP0);
     auto pair = [&](auto BUF, int q) {
@@ -683,21 +688,21 @@ __global__ __launch_bounds__(512) void k_int8_prefill_w(Int8GemmParams p) {
         s_rs[r] = p.row_scale ? v : 1.0f;
         s_za[r] = row_za(p, m);
     }
-    if (tid < PW_BN) s_col[tid] = load_colops_c(p, strip0 * kTileN + tid);
+    if (tid < BN) s_col[tid] = load_colops_c(p, strip0 * kTileN + tid);
     __syncthreads();
-    const bool whole = m0 + PF_BM <= p.M && (strip0 + PW_S) * kTileN <= p.N;
+    const bool whole = m0 + PF_BM <= p.M && (strip0 + S) * kTileN <= p.N;
     // element e of tile (t, j): row 64 wm + 16 t + 4 (L / 16) + e, column
     // 112 wn + 16 j + L % 16 of the workgroup's tile
     if (!HAS_ZB && p.outputs == QMM_OUT_F32 && p.zAs == 0 && !p.za_row && whole) {
-        float cm[7], cb[7];
+        float cm[JW], cb[JW];
 #pragma unroll
-        for (int j = 0; j < 7; ++j) {
-            const ColOps c = s_col[112 * wn + 16 * j + (lane & 15)];
+        for (int j = 0; j < JW; ++j) {
+            const ColOps c = s_col[16 * JW * wn + 16 * j + (lane & 15)];
             cm[j] = c.cs;
             cb[j] = c.bias_f;
         }
         float *ybase = p.y_f32 + (int64_t)(m0 + 64 * wm + 4 * (lane >> 4)) * p.ld_f32 + strip0 * kTileN +
-                       112 * wn + (lane & 15);
+                       16 * JW * wn + (lane & 15);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const v4f rs = *(const v4f *)(&s_rs[64 * wm + 16 * t + 4 * (lane >> 4)]);
@@ -705,7 +710,7 @@ __global__ __launch_bounds__(512) void k_int8_prefill_w(Int8GemmParams p) {
             for (int e = 0; e < 4; ++e) {
                 float *yrow = ybase + (int64_t)(16 * t + e) * p.ld_f32;
 #pragma unroll
-                for (int j = 0; j < 7; ++j) {
+                for (int j = 0; j < JW; ++j) {
                     const float mult = (rs[e] * cm[j]) * p.scale;
                     yrow[16 * j] = fmaf((float)acc[t][j][e], mult, cb[j]);
                 }
@@ -716,8 +721,8 @@ __global__ __launch_bounds__(512) void k_int8_prefill_w(Int8GemmParams p) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int j = 0; j < 7; ++j) {
-            const int cl = 112 * wn + 16 * j + (lane & 15);
+        for (int j = 0; j < JW; ++j) {
+            const int cl = 16 * JW * wn + 16 * j + (lane & 15);
             const int n = strip0 * kTileN + cl;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -749,13 +754,13 @@ hipError_t launch_int8_prefill(const Int8GemmParams &p, hipStream_t s, const cha
         *variant = "int8_prefill_256x224";
         const dim3 grid((unsigned)(ceil_div(p.NS, PW_S) * ceil_div(p.M, PF_BM))), b(512);
         if (has_zb && p.a_u8)
-            hipLaunchKernelGGL((k_int8_prefill_w<true, true>), grid, b, 0, s, p);
+            hipLaunchKernelGGL((k_int8_prefill_w<PW_S, true, true>), grid, b, 0, s, p);
         else if (has_zb)
-            hipLaunchKernelGGL((k_int8_prefill_w<true, false>), grid, b, 0, s, p);
+            hipLaunchKernelGGL((k_int8_prefill_w<PW_S, true, false>), grid, b, 0, s, p);
         else if (p.a_u8)
-            hipLaunchKernelGGL((k_int8_prefill_w<false, true>), grid, b, 0, s, p);
+            hipLaunchKernelGGL((k_int8_prefill_w<PW_S, false, true>), grid, b, 0, s, p);
         else
-            hipLaunchKernelGGL((k_int8_prefill_w<false, false>), grid, b, 0, s, p);
+            hipLaunchKernelGGL((k_int8_prefill_w<PW_S, false, false>), grid, b, 0, s, p);
         return hipGetLastError();
     }
     *variant = "int8_prefill_256x128";
