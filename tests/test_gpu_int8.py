@@ -519,6 +519,40 @@ def test_prefill_wide_tile_fp32_only(q, orc):
         assert max_rel_err(to_np(yf), ref) <= F32_TOL
 
 
+def test_prefill_tile_boundaries(q, orc):
+    """Where the 256 x 224 tile does not apply: K % 128 == 64 (a pair count
+    that is not whole) keeps the 256 x 128 tile on a shape that would
+    otherwise take the wide one; and the dynamic (fp32-activation) form at
+    M > 32 quantises, then runs the wide tile, bit for bit the two-call
+    result."""
+    import torch
+    dev = torch_dev()
+    g = np.random.default_rng(5)
+    M, K, N = 256, 192, 32800
+    assert _prefill_variant(M, K, N) == "int8_prefill_256x128" and _prefill_variant(M, 256, N) != "int8_prefill_256x128"
+    A = wl.uniform_i8(g, (M, K))
+    B = wl.uniform_i8(g, (K, N))
+    _gemm_case(q, orc, A, 3, B, -2, rs=(g.uniform(0.5, 1.5, M) / 127).astype(np.float32),
+               expect_variant="int8_prefill_256x128")
+    M, K, N = 300, 256, 16475
+    W = wl.normal_f32(g, (K, N), 0.02)
+    X = wl.normal_f32(g, (M, K))
+    p = q.pack_b_int8(to_dev(W))
+    Xd = to_dev(X)
+    Xq, rs = q.quantize_rows_int8(Xd)
+    y2 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q.int8_gemm(Xq, 0, p, 0, out_f32=y2, row_scale=rs)
+    assert q.last_variant() == "int8_prefill_256x224"
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q.int8_gemm_dynamic(Xd, p, out_f32=y)
+    assert q.last_variant() == "int8_prefill_256x224"
+    assert torch.equal(y, y2)
+    Qb, sb, _ = orc.pack_b_int8(W)
+    Qa, sa = orc.quantize_rows_int8(X)
+    ref = orc.epilogue_f64(orc.int8_gemm_i64(Qa, 0, Qb, 0), sa, sb)
+    assert max_rel_err(to_np(y), ref) <= F32_TOL
+
+
 @pytest.mark.parametrize("shape", range(len(wl.PREFILL_SHAPES)))
 def test_prefill_full_size_sampled(q, orc, shape):
     """M = 2048 tokens at the 8B-class shapes: packB of fp32 N(0,0.02)
