@@ -313,6 +313,15 @@ static bool dynamic_fusable(int64_t M, int64_t K) {
 // Calls the wide decode takes (many columns) quantise in a launch of their
 // own: there the weight bytes per workgroup are few next to a quantisation in
 // every workgroup.
+// The wide decode (>= 1024 strips) quantises inside while the rows, rounded
+// up to a power of two, times K stay within 16384 values (at most 32 per
+// thread of its 512) and X allows aligned 16-byte loads.
+static bool dynamic_wide_fused(int64_t M, int64_t K, int64_t N, const float *X, int64_t ldx) {
+    int64_t mp = 1;
+    while (mp < M) mp <<= 1;
+    return use_wide(M, K, N) && mp * K <= 16384 && K % 4 == 0 && aligned(X, 16) && ldx % 4 == 0;
+}
+
 static bool dynamic_fused(int64_t M, int64_t K, int64_t N) {
     return dynamic_fusable(M, K) && !use_wide(M, K, N);
 }
@@ -388,6 +397,22 @@ qmm_status int8_gemm_dynamic(const float *X, int64_t M, int64_t K, int64_t ldx, 
         check_epilogue_ptrs(ep) != QMM_OK)
         return QMM_ERR_INVALID;
     hipStream_t s = (hipStream_t)stream;
+    if (dynamic_wide_fused(M, K, N, X, ldx)) {
+        // the wide decode with the quantisation inside: one launch
+        Int8GemmParams p{};
+        fill_params(p, M, K, N, packedB, ep);
+        p.X = X;
+        p.ldx = ldx;
+        p.x_vec = 1;
+        p.xq_out = Xq;
+        p.ldq = ldq;
+        p.rs_out = row_scale;
+        const char *variant = "";
+        st = hip_status(launch_int8_gemm_dynamic_wide(p, s, &variant));
+        g_last_variant = variant;
+        trace_gemm("int8_gemm_dynamic", variant, M, K, N, plan_int8_gemm(M, K, N));
+        return st;
+    }
     if (!dynamic_fused(M, K, N)) {
         // The row quantiser, then the product.
         int8_t *q = Xq;

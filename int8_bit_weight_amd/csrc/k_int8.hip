@@ -452,6 +452,121 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide(Int8GemmPa
         }
 }
 
+// Wide decode with the per-row quantisation inside (int8_gemm_dynamic over
+// >= 1024 strips, MP * K <= 16384): the quantiser and the product in one
+// launch.  The workgroup's 512 threads take MP rows (M rounded up to a power
+// of two), 512 / MP threads a row, each thread CPT 16-byte chunks of it at a
+// stride of 512 / MP chunks, so a wavefront's loads are contiguous.  The
+// chunk loads go out first, then the wavefront's weight tiles (as in
+// k_int8_decode_wide), so the row maxima wait for the activations alone.
+// Row maxima combine by DPP lane moves inside a wavefront and through LDS
+// across the wavefronts of a row; every thread then quantises its chunks
+// with the k_quantize_rows rule (bit for bit its codes and scales) straight
+// into the LDS copy of the rows' codes in operand order.  Rows past M
+// quantise row M - 1 again and operand rows past MP are never written: both
+// reach only outputs that are not stored; k past K multiplies the zero codes
+// of the padded weight.  Workgroup 0 also writes the codes and scales out
+// when asked.
+template <int MT, int D, int MP, int CPT>
+__global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide_q(Int8GemmParams p) {
+    constexpr int NT = kWideWaves * 64;
+    constexpr int TPR = NT / MP;             // threads per row
+    constexpr int L = TPR < 64 ? TPR : 64;   // lanes of a row in one wavefront
+    constexpr int WPR = TPR / L;             // wavefronts per row
+    static_assert(MP <= 16 * MT && (MP & (MP - 1)) == 0, "rows");
+    extern __shared__ v4i s_a[];  // [KT][MT][64]
+    __shared__ float s_amax[MP][WPR];
+    __shared__ float s_scale[MP];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int strip_raw = (int)blockIdx.x * kWideWaves + wave;
+    const bool strip_ok = strip_raw < p.NS;
+    const int strip = min(strip_raw, p.NS - 1);
+    const int8_t *codes = p.codes + (int64_t)strip * p.KT * kTileBytes + lane * 16;
+    const int last = p.KT - 1;
+
+    // the activation chunks of this thread: row r, chunks j + i TPR
+    const int r = tid / TPR, j = tid % TPR;
+    const int nch = p.K >> 2;
+    const float *xrow = p.X + (int64_t)min(r, p.M - 1) * p.ldx;
+    v4f xv[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) xv[i] = *(const v4f *)(xrow + 4 * min(j + i * TPR, nch - 1));
+    v4i bf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) bf[i] = *(const v4i *)(codes + (int64_t)min(i, last) * kTileBytes);
+    const ColOps col = load_colops_c(p, strip * kTileN + (lane & 15));
+
+    // row maxima (chunks past K count as zeros)
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+        if (j + i * TPR < nch)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a = fmaxf(a, fabsf(xv[i][e]));
+    a = group_max<L>(a);
+    if constexpr (WPR > 1) {
+        if (lane == 0) s_amax[r][wave % WPR] = a;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) a = fmaxf(a, s_amax[r][w]);
+    }
+    const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
+    const float y = 1.0f / s;
+    const bool fast = s >= 0x1p-100f && s <= 0x1p100f;
+    if (j == 0) {
+        s_scale[r] = s;
+        if (p.rs_out && blockIdx.x == 0 && r < p.M) p.rs_out[r] = s;
+    }
+    // codes into the operand copy: 4 codes of chunk c = k 4c .. 4c + 3 of
+    // row r sit in the 16-byte operand of (k tile, row tile, lane (4c % 64) / 16
+    // * 16 + r % 16) at byte 4c % 16
+    uint8_t *sa = (uint8_t *)s_a;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = j + i * TPR;
+        if (c < nch) {
+            const float xs[4] = {xv[i][0], xv[i][1], xv[i][2], xv[i][3]};
+            const uint32_t w = s > 0.0f ? quant4(xs, s, y, fast) : 0u;
+            const int k = 4 * c, kt = k >> 6, kk = k & 63;
+            const int op = (kt * MT + (r >> 4)) * 64 + (kk >> 4) * 16 + (r & 15);
+            *(uint32_t *)(sa + op * 16 + (kk & 15)) = w;
+            if (p.xq_out && blockIdx.x == 0 && r < p.M) {
+                int8_t *dst = p.xq_out + (int64_t)r * p.ldq + k;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[e] = (int8_t)(w >> (8 * e));
+            }
+        }
+    }
+    __syncthreads();
+
+    v4i acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
+    for (int kt0 = 0; kt0 < p.KT; kt0 += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            const int kt = kt0 + i;
+            if (kt < p.KT) {
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[t] = mfma_i8(s_a[(kt * MT + t) * 64 + lane], bf[i], acc[t]);
+            }
+            bf[i] = *(const v4i *)(codes + (int64_t)min(kt + D, last) * kTileBytes);
+        }
+    }
+
+    const int n = strip * kTileN + (lane & 15);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = t * 16 + 4 * (lane >> 4) + i;
+            if (strip_ok && m < p.M && n < p.N)
+                epilogue_store_c(p, m, n, (uint32_t)acc[t][i], 0, false, s_scale[min(m, MP - 1)], 0, col);
+        }
+}
+
 // Fused dynamic quantisation for small M x K (the planner takes it while
 // E * K <= 16384, E = rows of a row group rounded up to a power of two <= 16,
 // and K <= 4096; row groups run as the grid's second dimension).  A
@@ -709,6 +824,38 @@ hipError_t launch_wide(const Int8GemmParams &p, hipStream_t s) {
     return launch_wide_d<MT, 16, AVEC>(p, s);
 }
 
+template <int MT, int D, int MP>
+hipError_t launch_wide_q_mp(const Int8GemmParams &p, hipStream_t s) {
+    const dim3 grid((unsigned)ceil_div(p.NS, kWideWaves));
+    const size_t lds = (size_t)p.KT * MT * 64 * sizeof(v4i);
+    const int cpt = (int)ceil_div(p.K / 4, kWideWaves * 64 / MP);
+    if (cpt <= 1)
+        hipLaunchKernelGGL((k_int8_decode_wide_q<MT, D, MP, 1>), grid, dim3(kWideWaves * 64), lds, s, p);
+    else if (cpt <= 2)
+        hipLaunchKernelGGL((k_int8_decode_wide_q<MT, D, MP, 2>), grid, dim3(kWideWaves * 64), lds, s, p);
+    else if (cpt <= 4)
+        hipLaunchKernelGGL((k_int8_decode_wide_q<MT, D, MP, 4>), grid, dim3(kWideWaves * 64), lds, s, p);
+    else if (cpt <= 8)
+        hipLaunchKernelGGL((k_int8_decode_wide_q<MT, D, MP, 8>), grid, dim3(kWideWaves * 64), lds, s, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+template <int MT, int D>
+hipError_t launch_wide_q_d(const Int8GemmParams &p, hipStream_t s) {
+    // more than 16 rows: two row tiles, the rows rounded up to 32
+    if constexpr (MT == 2) {
+        return launch_wide_q_mp<2, D, 32>(p, s);
+    } else {
+        if (p.M <= 1) return launch_wide_q_mp<1, D, 1>(p, s);
+        if (p.M <= 2) return launch_wide_q_mp<1, D, 2>(p, s);
+        if (p.M <= 4) return launch_wide_q_mp<1, D, 4>(p, s);
+        if (p.M <= 8) return launch_wide_q_mp<1, D, 8>(p, s);
+        return launch_wide_q_mp<1, D, 16>(p, s);
+    }
+}
+
 // (waves, tiles per wave) pairs the planner uses: 4x1, 8x1, 16x1, 16x2, 16x4.
 template <int MT, bool AVEC>
 hipError_t launch_decode_shape(const Int8GemmParams &p, int waves, int tpw, hipStream_t s) {
@@ -844,6 +991,14 @@ hipError_t launch_dyn_rows(const Int8Plan &plan, const Int8GemmParams &p, const 
     if (rows <= 4) return launch_dyn_w<4, GROUPED>(p, dg, w, spw, v, s);
     if (rows <= 8) return launch_dyn_w<8, GROUPED>(p, dg, w, spw, v, s);
     return launch_dyn_w<16, GROUPED>(p, dg, w, spw, v, s);
+}
+
+hipError_t launch_int8_gemm_dynamic_wide(const Int8GemmParams &p, hipStream_t s, const char **variant) {
+    const int mt = p.M <= 16 ? 1 : 2;
+    *variant = mt == 1 ? "int8_dynamic_wide_m16" : "int8_dynamic_wide_m32";
+    if (p.KT * mt > kWideMaxTiles || p.K % 4 != 0 || !p.x_vec) return hipErrorInvalidValue;
+    if (mt == 1) return p.KT <= 8 ? launch_wide_q_d<1, 8>(p, s) : launch_wide_q_d<1, 16>(p, s);
+    return p.KT <= 8 ? launch_wide_q_d<2, 8>(p, s) : launch_wide_q_d<2, 16>(p, s);
 }
 
 hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,

@@ -168,6 +168,8 @@ hipError_t launch_quantize_rows(const float *X, int64_t M, int64_t K, int64_t ld
 hipError_t launch_int8_prefill(const Int8GemmParams &p, hipStream_t s, const char **variant);
 hipError_t launch_int8_gemm(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                             const char **variant);
+// the wide decode with the quantisation inside (aligned X, K % 4 == 0)
+hipError_t launch_int8_gemm_dynamic_wide(const Int8GemmParams &p, hipStream_t s, const char **variant);
 hipError_t launch_int8_gemm_dynamic(const Int8Plan &plan, Int8GemmParams p, hipStream_t s,
                                     const char **variant);
 // grouped form: p.NS is the total strip count of the items; p's per-weight

@@ -203,11 +203,83 @@ def test_wide_decode_unaligned_a(q, orc):
     assert np.array_equal(to_np(y), ref.astype(np.int32))
 
 
+def _wide_dynamic_variant(M, K, ldx=None, aligned=True):
+    """The form int8_gemm_dynamic takes over >= 1024 strips: the quantisation
+    inside the wide decode while the rows rounded up to a power of two times
+    K stay within 16384 (X 16-byte aligned, K and ldx multiples of 4), else
+    the row quantiser, then the wide decode."""
+    mp = 1
+    while mp < M:
+        mp *= 2
+    ldx = K if ldx is None else ldx
+    if mp * K <= 16384 and K % 4 == 0 and ldx % 4 == 0 and aligned:
+        return "int8_dynamic_wide_m16" if M <= 16 else "int8_dynamic_wide_m32"
+    return "int8_decode_wide_m16" if M <= 16 else "int8_decode_wide_m32"
+
+
+@pytest.mark.parametrize("M,K", [(1, 1024), (16, 1024), (32, 1024), (3, 1000), (5, 2048), (9, 1024), (4, 4096),
+                                 (1, 4000), (20, 512), (7, 1022)])
+def test_wide_decode_dynamic_fused(q, orc, M, K):
+    """int8_gemm_dynamic over many columns: with the quantisation inside the
+    wide decode (one launch) where the planner takes it, else the row
+    quantiser first.  Codes and row scales bit for bit the oracle's, fp32
+    outputs bit for bit the two-call form's, int32 the oracle's product."""
+    import torch
+    dev = torch_dev()
+    N = 16500
+    g = np.random.default_rng(M * 13 + K)
+    W = wl.normal_f32(g, (K, N), 0.02)
+    X = wl.normal_f32(g, (M, K))
+    if M > 2:
+        X[1] = 0.0                                        # an all-zero row: scale 0, codes 0
+        X[2, K // 3] = 50.0                               # a row maximum inside the row
+    p = q.pack_b_int8(to_dev(W))
+    Xd = to_dev(X)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    y32 = torch.empty((M, N), dtype=torch.int32, device=dev)
+    xq = torch.full((M, K), 99, dtype=torch.int8, device=dev)
+    rs = torch.full((M,), -1.0, dtype=torch.float32, device=dev)
+    q.int8_gemm_dynamic(Xd, p, out_f32=y, out_i32=y32, xq_out=xq, rs_out=rs)
+    assert q.last_variant() == _wide_dynamic_variant(M, K)
+    Qa, sa = orc.quantize_rows_int8(X)
+    assert np.array_equal(to_np(xq), Qa)
+    assert np.array_equal(to_np(rs).view(np.uint32), sa.view(np.uint32))
+    Xq2, rs2 = q.quantize_rows_int8(Xd)
+    y2 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q.int8_gemm(Xq2, 0, p, 0, out_f32=y2, row_scale=rs2)
+    assert np.array_equal(to_np(y).view(np.uint32), to_np(y2).view(np.uint32))
+    Qb, sb, _ = orc.pack_b_int8(W)
+    Y64 = orc.int8_gemm_i64(Qa, 0, Qb, 0)
+    assert np.array_equal(to_np(y32), Y64.astype(np.int32))
+    assert max_rel_err(to_np(y), orc.epilogue_f64(Y64, sa, sb)) <= F32_TOL
+
+
+def test_wide_decode_dynamic_unaligned_falls_back(q, orc):
+    """X not 16-byte aligned: the row quantiser, then the wide decode, with
+    the same bits as the aligned call."""
+    import torch
+    dev = torch_dev()
+    M, K, N = 4, 1024, 16400
+    g = np.random.default_rng(77)
+    W = wl.normal_f32(g, (K, N), 0.02)
+    X = wl.normal_f32(g, (M, K))
+    p = q.pack_b_int8(to_dev(W))
+    Xw = torch.zeros((M, K + 1), dtype=torch.float32, device=dev)
+    Xw[:, 1:] = to_dev(X)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q.int8_gemm_dynamic(Xw[:, 1:], p, out_f32=y)
+    assert q.last_variant() == "int8_decode_wide_m16"
+    ya = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q.int8_gemm_dynamic(to_dev(X), p, out_f32=ya)
+    assert q.last_variant() == "int8_dynamic_wide_m16"
+    assert torch.equal(y, ya)
+
+
 @pytest.mark.parametrize("M", [1, 16, 32])
 def test_wide_decode_dynamic(q, orc, M):
-    """int8_gemm_dynamic over many columns quantises in a launch of its own,
-    then the wide product: the same bits as quantize_rows_int8 + int8_gemm,
-    and the oracle's int32 product."""
+    """int8_gemm_dynamic over many columns (the quantisation inside the wide
+    decode, or in a launch of its own past 16384 row values): the same bits
+    as quantize_rows_int8 + int8_gemm, and the oracle's int32 product."""
     import torch
     dev = torch_dev()
     K, N = 1024, 16500
@@ -219,7 +291,7 @@ def test_wide_decode_dynamic(q, orc, M):
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
     y32 = torch.empty((M, N), dtype=torch.int32, device=dev)
     q.int8_gemm_dynamic(Xd, p, out_f32=y, out_i32=y32)
-    assert q.last_variant() == ("int8_decode_wide_m16" if M <= 16 else "int8_decode_wide_m32")
+    assert q.last_variant() == _wide_dynamic_variant(M, K)
     Xq2, rs2 = q.quantize_rows_int8(Xd)
     y2 = torch.empty((M, N), dtype=torch.float32, device=dev)
     q.int8_gemm(Xq2, 0, p, 0, out_f32=y2, row_scale=rs2)
@@ -235,8 +307,8 @@ def test_wide_decode_dynamic(q, orc, M):
 
 @pytest.mark.parametrize("M", [1, 16, 32])
 def test_wide_and_per_strip_forms_agree_bit_for_bit(q, M):
-    """One int8_gemm_dynamic call over 1040 strips (the wide form: the row
-    quantiser, then one wavefront per strip) gives, bit for bit, the fp32
+    """One int8_gemm_dynamic call over 1040 strips (the wide form: one
+    wavefront per strip, the quantisation inside or before it) gives, bit for bit, the fp32
     outputs of per-strip calls on column slices of the same weight (the fused
     quantising form at 128 and 96 strips, and the grouped form over the
     slices): per-column packing makes a slice's codes, scales and column sums
@@ -251,7 +323,7 @@ def test_wide_and_per_strip_forms_agree_bit_for_bit(q, M):
     whole = q.pack_b_int8(to_dev(W))
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
     q.int8_gemm_dynamic(Xd, whole, out_f32=y)
-    assert q.last_variant().startswith("int8_decode_wide")
+    assert q.last_variant() == _wide_dynamic_variant(M, K)
     cuts = [0, 2048, 3584]
     parts = [q.pack_b_int8(to_dev(np.ascontiguousarray(W[:, a:b]))) for a, b in zip(cuts[:-1], cuts[1:])]
     for (a, b), pk in zip(zip(cuts[:-1], cuts[1:]), parts):
