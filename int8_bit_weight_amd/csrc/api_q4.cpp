@@ -37,6 +37,18 @@ Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
         // At one row the kernel keeps all of a wavefront's records in flight
         // and the tail after the last data arrives is one wavefront's records,
         // so at most 4 records each where the workgroup size allows.
+        if (M == 1 && L.NQ <= 8 && L.NS >= 1024) {
+            // k_q4_gemv1_wide: a wavefront per strip over its whole k range,
+            // 8 strips per workgroup sharing one staging of the activations
+            pl.cs = 8;
+            pl.waves = 8;
+            pl.S = 1;
+            pl.qps = (int)L.NQ;
+            pl.grid = ceil_div(L.NS, 8);
+            pl.ws_part_off = 0;
+            pl.ws_bytes = 0;
+            return pl;
+        }
         pl.cs = 1;
         pl.waves = 16;
         const int64_t rmax = M == 1 && ceil_div(L.NQ, 16) <= 4 ? 4 : 8;

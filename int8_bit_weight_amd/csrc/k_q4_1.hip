@@ -753,6 +753,106 @@ __global__ __launch_bounds__(W * 64) void k_q4_gemv1(Q4Params p) {
     }
 }
 
+// M = 1 over many strips with at most 8 records each (K <= 1024, e.g. an
+// lm_head): 8 wavefronts per workgroup, each owning one 16-column strip over
+// its whole k range, so the activation terms and block sums are staged once
+// per workgroup for 8 strips (k_q4_gemv1 stages them once per strip) and no
+// wavefront's partial sum meets another's.  Wavefronts 0 and 1 stage records
+// 0-3 and 4-7 with k_q4_gemv1's rule (three bf16 terms, the same padded term
+// planes and block sums), one barrier, then every wavefront runs the records
+// of its strip, all loaded at the start, with k_q4_gemv1's per-block
+// arithmetic (one fma chain over the whole k range: no partial sums).
+template <bool XVEC>
+__global__ __launch_bounds__(512) void k_q4_gemv1_wide(Q4Params p) {
+    constexpr int W = 8, QMAX = 8, D = QMAX, XPL = 8;
+    constexpr int TPL = QMAX * 128 + 32;
+    __shared__ __attribute__((aligned(16))) uint16_t sT[3][TPL];
+    __shared__ __attribute__((aligned(16))) float sXS[QMAX * 4];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int strip_raw = (int)blockIdx.x * W + wave;
+    const int strip = min(strip_raw, p.NS - 1);
+    const int nq = p.NQ;
+    const uint8_t *hdr = p.recs;
+    const uint8_t *recs = hdr + kHeaderBytes;
+
+    // staging: wavefront w < 2 takes activations 512 w + 8 L .. + 7 (clamped
+    // inside the row: values past K meet zero-weight blocks)
+    float x[XPL];
+    if (wave < 2) {
+        const int k = min(512 * wave + XPL * lane, p.K - XPL);
+        if (XVEC) {
+#pragma unroll
+            for (int u = 0; u < XPL / 4; ++u) {
+                const v4f v = *(const v4f *)(p.X + k + 4 * u);
+                x[4 * u] = v[0]; x[4 * u + 1] = v[1]; x[4 * u + 2] = v[2]; x[4 * u + 3] = v[3];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < XPL; ++e) x[e] = p.X[k + e];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    v4i wc[D], wd[D];
+    static_for<D>([&](auto S) {
+        constexpr int q = decltype(S)::value;
+        const bool pad = q >= nq;
+        const uint8_t *rec = recs + ((int64_t)strip * nq + min(q, nq - 1)) * kQ4RecBytes;
+        wc[q] = *(const v4i *)(rec + (uint32_t)lane * 16u);
+        wd[q] = *(const v4i *)(pad ? hdr + kHeaderBytes - 16 : rec + 1024 + (uint32_t)(lane & 15) * 16u);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    if (wave < 2) {
+        uint32_t t[3][XPL / 2];
+        float bs = 0.0f;
+#pragma unroll
+        for (int e = 0; e < XPL; e += 2) {
+            const float x0 = x[e], x1 = x[e + 1];
+            bs += x0;
+            bs += x1;
+            const uint32_t t0 = pk_bf16(x0, x1);
+            const float r0 = x0 - bf16_lo_f32(t0), r1 = x1 - bf16_hi_f32(t0);
+            const uint32_t t1 = pk_bf16(r0, r1);
+            t[0][e >> 1] = t0;
+            t[1][e >> 1] = t1;
+            t[2][e >> 1] = pk_bf16(r0 - bf16_lo_f32(t1), r1 - bf16_hi_f32(t1));
+        }
+#pragma unroll
+        for (int tt = 0; tt < 3; ++tt)
+#pragma unroll
+            for (int u = 0; u < XPL / 8; ++u)
+                *(v4i *)(&sT[tt][512 * wave + XPL * lane + 8 * u]) =
+                    v4i{(int)t[tt][4 * u], (int)t[tt][4 * u + 1], (int)t[tt][4 * u + 2], (int)t[tt][4 * u + 3]};
+        // a block (32 values) is 4 lanes: the last of them holds the sum
+        bs += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bs), 0x111, 0xF, 0xF, true));
+        bs += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bs), 0x112, 0xF, 0xF, true));
+        if ((lane & 3) == 3) sXS[16 * wave + lane / 4] = bs;
+    }
+    // LDS barrier without a memory fence (the record loads stay in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    float y = 0.0f;
+    const int at = lane & 3, ag = lane >> 4;
+    const int a_rd = (at < 3 ? at : 2) * TPL + 8 * ag;
+    static_for<D>([&](auto S) {
+        constexpr int qi = decltype(S)::value;
+        const v4f xs4 = *(const v4f *)(&sXS[4 * qi]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v8bf a = *(const v8bf *)(&sT[0][0] + a_rd + qi * 128 + 32 * i);
+            const v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, decode8((uint32_t)wc[qi][i]),
+                                                                   v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            const uint32_t dm = (uint32_t)wd[qi][i];
+            y = fmaf(bf16_lo_f32(dm), (acc[0] + acc[1]) + acc[2], y);
+            y = fmaf(bf16_hi_f32(dm), xs4[i], y);
+            asm volatile("" : "+v"(y));
+        }
+    });
+    // lanes 0..15 hold the strip's columns (row 0 of the tile)
+    const int n = strip * 16 + lane;
+    if (lane < 16 && strip_raw < p.NS && n < p.N) p.Y[n] = y;
+}
+
 // ----------------------------------------- the product, 5 <= M <= 16 ---
 // One 16-row MFMA tile of activation rows, two MFMAs (one per fp16 term)
 // per block and strip.  A workgroup of WAVES wavefronts owns
@@ -1576,6 +1676,16 @@ hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t
             }
         };
         const bool one = p.M == 1 && p.qps <= 8;
+        if (cs == 8) {
+            // one row, at most 8 records per strip, 8 strips per workgroup
+            *variant = "q4_gemv_m1_wide";
+            if (p.M != 1 || p.NQ > 8 || waves != 8) return hipErrorInvalidValue;
+            if (p.x_vec)
+                hipLaunchKernelGGL((k_q4_gemv1_wide<true>), g, b, 0, s, p);
+            else
+                hipLaunchKernelGGL((k_q4_gemv1_wide<false>), g, b, 0, s, p);
+            return hipGetLastError();
+        }
         if (cs != 1) ok = false;
         else if (one && waves == 4) go1(ic<4>{});
         else if (one && waves == 8) go1(ic<8>{});

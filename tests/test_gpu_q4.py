@@ -117,6 +117,27 @@ def test_q4_matmul_row_remainders(q, orc, M, variant):
     _matmul_case(q, orc, M, 1024, 300, seed=M, variant=variant, zero_cols=(3,), zero_scale_blocks=True)
 
 
+@pytest.mark.parametrize("K,N", [(1024, 16400), (512, 16389), (96, 16390), (1024, 16384)])
+def test_q4_matmul_one_row_wide(q, orc, K, N):
+    """M = 1 over >= 1024 strips with at most 8 records each (an lm_head's
+    shape class): a wavefront per strip over its whole k range, 8 strips per
+    workgroup.  Ragged N (a last workgroup of fewer strips), 4 and 1 records
+    per strip, zero columns and zero-scale blocks, aligned and unaligned
+    activations, at the 1e-5 bound."""
+    import torch
+    seed = K + N
+    got, ref = _matmul_case(q, orc, 1, K, N, seed=seed, variant="q4_gemv_m1_wide", zero_cols=(3,),
+                            zero_scale_blocks=True)
+    blocks = _blocks(K, N, seed, zero_cols=(3,), zero_scale_blocks=True)
+    p = _repack(q, blocks, K, N)
+    X = wl.q4_activations(1, K, seed_index=seed)
+    Xw = torch.zeros((1, K + 1), dtype=torch.float32, device=torch_dev())
+    Xw[:, 1:] = to_dev(X)
+    c = to_np(q.q4_1_matmul(Xw[:, 1:], p))
+    assert q.last_variant() == "q4_gemv_m1_wide"
+    assert np.array_equal(c.view(np.uint32), got.view(np.uint32))
+
+
 def test_q4_matmul_one_row_paths(q, orc):
     """M = 1: the one-launch kernel (aligned and unaligned activations, bitwise
     repeatable), its fallback when a wavefront would hold more than 8 records,
