@@ -21,6 +21,14 @@ qmm_status record_status(hipError_t e, const char *variant);
 // in flight; the S partial results are summed in split order by a second
 // kernel.  Fewer splits at larger M keep the partial traffic (S*M*N floats)
 // small next to the weight bytes.
+// Past 4096 strips k_q4_mm16 (16 strips per workgroup) has more workgroups
+// than CUs: some CUs run several, each staging the same activations again,
+// and the strips spread unevenly, where the persistent form spreads them
+// evenly and stages once per CU.  Measured at K = 1024, M = 16 (us per call,
+// k_q4_mm16 / persistent): 4096 strips 13.9 / 15.4, 6144 21.7 / 19.6,
+// 8192 23.9 / 23.6, 9496 31.0 / 27.5, 16384 46.1 / 41.2.
+constexpr int64_t kWideMm16Strips = 4096;
+
 Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
     Q4Plan pl{};
     const Q4Layout L = q4_layout(K, N);
@@ -61,6 +69,18 @@ Q4Plan plan_q4_matmul(int64_t M, int64_t K, int64_t N) {
         pl.S = 1;
         pl.qps = (int)ceil_div(L.NQ, pl.waves);
         pl.grid = ceil_div(L.NS, pl.cs);
+        pl.ws_part_off = 0;
+        pl.ws_bytes = 0;
+        return pl;
+    }
+    if (pl.mt == 1 && L.NQ <= 8 && L.NS > kWideMm16Strips) {
+        // k_q4_mm16_wide: one workgroup per CU, each staging the whole k
+        // range once for its contiguous run of strips (k_q4_mm16 would need
+        // more workgroups than fit at once)
+        pl.cs = 1;
+        pl.S = 1;
+        pl.qps = (int)L.NQ;
+        pl.grid = 256;
         pl.ws_part_off = 0;
         pl.ws_bytes = 0;
         return pl;

@@ -853,6 +853,112 @@ __global__ __launch_bounds__(512) void k_q4_gemv1_wide(Q4Params p) {
     if (lane < 16 && strip_raw < p.NS && n < p.N) p.Y[n] = y;
 }
 
+// ------------------- staging shared by the 16-row whole-range kernels ---
+// k_q4_mm16 and k_q4_mm16_wide split the activations of their whole k range
+// (NBLK blocks from block b0) into LDS once.  Piece pc = (block bl, k-octet
+// g, row r) is 8 activations, pc = 64 bl + 16 g + r; thread tid holds pieces
+// tid + i NT.  Rows past M read row M - 1 (they reach only outputs that are
+// never stored) and blocks past K read the last block, whose copies meet
+// zero (d, m) in the padded records, so no value needs masking: the row
+// maxima and the products of the real rows and blocks are those of the real
+// values.
+template <int NT, int PPT, bool XVEC>
+__device__ __forceinline__ void load_pieces16(const float *X, int64_t ldx, int M, int NB, int tid, int b0,
+                                              float (&xr)[PPT][8]) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + i * NT;
+        const int r = pc & 15, g = (pc >> 4) & 3, bl = pc >> 6;
+        const int b = b0 + bl;
+        const float *src = X + (int64_t)min(r, M - 1) * ldx + min(b, NB - 1) * 32 + g * 8;
+        if (XVEC) {
+            const v4f lo = *(const v4f *)src;
+            const v4f hi = *(const v4f *)(src + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xr[i][e] = lo[e];
+                xr[i][4 + e] = hi[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[i][e] = src[e];
+        }
+    }
+}
+
+// The power-of-two scale exponent of a row from the wavefronts' row maxima.
+template <int WAVES>
+__device__ __forceinline__ int row_sc16(const float (*s_rmax)[16], int row) {
+    float m = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) m = fmaxf(m, s_rmax[w][row]);
+    return m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;
+}
+
+// The split of the held pieces: each row's scale exponent sc over the range
+// (one LDS barrier), then the two fp16 terms of x 2^sc at sA[bl][term] in
+// MFMA lane order and the unscaled block sums, three bf16 terms, into the
+// m-term operands sXM (row r, block bl at byte 16 r + 2 (bl % 8) of
+// sXM[bl / 8]; k-octets 1..3 of each operand stay zero).  Ends with an
+// LDS-only barrier (no memory fence: record loads may be in flight).
+template <int WAVES, int NBLK, int PPT>
+__device__ __forceinline__ void stage16(int tid, int lane, int wave, const float (&xr)[PPT][8],
+                                        uint8_t (*sA)[2][1024], uint8_t (*sXM)[3][1024], float (*s_rmax)[16]) {
+    constexpr int NT = WAVES * 64;
+    constexpr int NG = (NBLK + 7) / 8;
+    for (int o = tid * 16; o < NG * 3 * 768; o += NT * 16) {
+        const int f = o / 768;
+        *(v4i *)(&sXM[0][0][0] + f * 1024 + 256 + o % 768) = v4i{0, 0, 0, 0};
+    }
+    // a thread's pieces all belong to row tid % 16: its maximum, then the
+    // row's four k-octet lanes (xor 16, 32), then the wavefronts through LDS
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(xr[i][e]));
+    am = fmaxf(am, __shfl_xor(am, 16));
+    am = fmaxf(am, __shfl_xor(am, 32));
+    if (lane < 16) s_rmax[wave][lane] = am;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int sc = row_sc16<WAVES>(s_rmax, tid & 15);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + i * NT;
+        const int r = pc & 15, g = (pc >> 4) & 3, bl = pc >> 6;
+        float bsum = 0.0f;
+        uint32_t w[2][4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float x0 = xr[i][e];
+            const float x1 = xr[i][e + 1];
+            bsum += x0;
+            bsum += x1;
+            const float s0 = __builtin_ldexpf(x0, sc), s1 = __builtin_ldexpf(x1, sc);
+            const v2h a0 = {(_Float16)s0, (_Float16)s1};
+            const v2h a1 = {(_Float16)(s0 - (float)a0[0]), (_Float16)(s1 - (float)a0[1])};
+            w[0][e >> 1] = __builtin_bit_cast(uint32_t, a0);
+            w[1][e >> 1] = __builtin_bit_cast(uint32_t, a1);
+        }
+        bsum += __shfl_xor(bsum, 16);
+        bsum += __shfl_xor(bsum, 32);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            *(v4i *)(&sA[bl][t][(g * 16 + r) * 16]) = v4i{(int)w[t][0], (int)w[t][1], (int)w[t][2], (int)w[t][3]};
+        if (g == 0) {
+            const uint32_t s0 = pk_bf16(bsum, 0.0f);
+            const float sr = bsum - bf16_lo_f32(s0);
+            const uint32_t s1 = pk_bf16(sr, 0.0f);
+            const uint32_t s2 = pk_bf16(sr - bf16_lo_f32(s1), 0.0f);
+            uint8_t *xm = &sXM[bl >> 3][0][r * 16 + (bl & 7) * 2];
+            *(uint16_t *)(xm) = (uint16_t)s0;
+            *(uint16_t *)(xm + 1024) = (uint16_t)s1;
+            *(uint16_t *)(xm + 2048) = (uint16_t)s2;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ----------------------------------------- the product, 5 <= M <= 16 ---
 // One 16-row MFMA tile of activation rows, two MFMAs (one per fp16 term)
 // per block and strip.  A workgroup of WAVES wavefronts owns
@@ -907,31 +1013,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
     const uint8_t *hdr = p.recs;
     const uint8_t *recs = hdr + kHeaderBytes;
 
-    // ---- activation loads (first: the staging waits for them alone).  Rows
-    // past M read row M - 1 (they reach only outputs that are never stored)
-    // and blocks past K read the last block, whose copies meet zero (d, m) in
-    // the padded records, so no value needs masking: the row maxima and the
-    // products of the real rows and blocks are those of the real values.
+    // ---- activation loads (first: the staging waits for them alone)
     float xr[PPT][8];
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-        const int pc = tid + i * NT;
-        const int r = pc & 15, g = (pc >> 4) & 3, bl = pc >> 6;
-        const int b = q0 * 4 + bl;
-        const float *src = p.X + (int64_t)min(r, M - 1) * p.ldx + min(b, p.NB - 1) * 32 + g * 8;
-        if (XVEC) {
-            const v4f lo = *(const v4f *)src;
-            const v4f hi = *(const v4f *)(src + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xr[i][e] = lo[e];
-                xr[i][4 + e] = hi[e];
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xr[i][e] = src[e];
-        }
-    }
+    load_pieces16<NT, PPT, XVEC>(p.X, p.ldx, M, p.NB, tid, q0 * 4, xr);
 
     // every wavefront's activation loads go out before any record load: the
     // memory pipeline returns them in order, and the staging needs them first
@@ -955,68 +1039,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
 #pragma unroll
     for (int q = 0; q < R; ++q) gload_rec(q, wc[q], wd[q]);
 
-    // ---- staging.  k-octets 1..3 of the m-term operands stay zero (bytes
-    // 256.. of each fragment; the block sums fill bytes 0..255)
-    for (int o = tid * 16; o < NG * 3 * 768; o += NT * 16) {
-        const int f = o / 768;
-        *(v4i *)(&sXM[0][0][0] + f * 1024 + 256 + o % 768) = v4i{0, 0, 0, 0};
-    }
-    // the row scales: a thread's pieces all belong to row tid % 16; its
-    // maximum, then the row's four k-octet lanes (xor 16, 32), then the
-    // wavefronts through LDS
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < PPT; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(xr[i][e]));
-    am = fmaxf(am, __shfl_xor(am, 16));
-    am = fmaxf(am, __shfl_xor(am, 32));
-    if (lane < 16) s_rmax[wave][lane] = am;
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    auto row_sc = [&](int row) {
-        float m = 0.0f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) m = fmaxf(m, s_rmax[w][row]);
-        return m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;
-    };
-    const int sc = row_sc(tid & 15);
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-        const int pc = tid + i * NT;
-        const int r = pc & 15, g = (pc >> 4) & 3, bl = pc >> 6;
-        float bsum = 0.0f;
-        uint32_t w[2][4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            const float x0 = xr[i][e];
-            const float x1 = xr[i][e + 1];
-            bsum += x0;
-            bsum += x1;
-            const float s0 = __builtin_ldexpf(x0, sc), s1 = __builtin_ldexpf(x1, sc);
-            const v2h a0 = {(_Float16)s0, (_Float16)s1};
-            const v2h a1 = {(_Float16)(s0 - (float)a0[0]), (_Float16)(s1 - (float)a0[1])};
-            w[0][e >> 1] = __builtin_bit_cast(uint32_t, a0);
-            w[1][e >> 1] = __builtin_bit_cast(uint32_t, a1);
-        }
-        bsum += __shfl_xor(bsum, 16);
-        bsum += __shfl_xor(bsum, 32);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            *(v4i *)(&sA[bl][t][(g * 16 + r) * 16]) = v4i{(int)w[t][0], (int)w[t][1], (int)w[t][2], (int)w[t][3]};
-        if (g == 0) {
-            const uint32_t s0 = pk_bf16(bsum, 0.0f);
-            const float sr = bsum - bf16_lo_f32(s0);
-            const uint32_t s1 = pk_bf16(sr, 0.0f);
-            const uint32_t s2 = pk_bf16(sr - bf16_lo_f32(s1), 0.0f);
-            uint8_t *xm = &sXM[bl >> 3][0][r * 16 + (bl & 7) * 2];
-            *(uint16_t *)(xm) = (uint16_t)s0;
-            *(uint16_t *)(xm + 1024) = (uint16_t)s1;
-            *(uint16_t *)(xm + 2048) = (uint16_t)s2;
-        }
-    }
-    // LDS barrier without a memory fence: a fence would wait for the record
-    // loads still in flight
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // ---- staging (its last barrier is LDS-only: a memory fence would wait
+    // for the record loads still in flight)
+    stage16<WAVES, NBLK, PPT>(tid, lane, wave, xr, sA, sXM, s_rmax);
 
     // ---- the product
     v4f acc_y[C], acc_m[C];
@@ -1078,7 +1103,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
 
     int esc[4];  // -sc of this lane's output rows
 #pragma unroll
-    for (int v = 0; v < 4; ++v) esc[v] = -row_sc(4 * (lane >> 4) + v);
+    for (int v = 0; v < 4; ++v) esc[v] = -row_sc16<WAVES>(s_rmax, 4 * (lane >> 4) + v);
 #pragma unroll
     for (int j = 0; j < C; ++j)
 #pragma unroll
@@ -1093,6 +1118,115 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
                     p.part[((int64_t)job * M + row) * p.N + n] = val;
             }
         }
+}
+
+// 5 <= M <= 16 over many strips with at most 8 records each (K <= 1024,
+// e.g. an lm_head): a persistent form of k_q4_mm16.  The grid is at most one
+// workgroup per CU; workgroup b of G owns the strips [b NS / G,
+// (b + 1) NS / G), stages the activations of the whole k range once
+// (stage16) and each wavefront then runs the strips first + wave,
+// first + wave + WAVES, ... one at a time over their whole k range (per
+// block two fp16 MFMAs and y += d acc, the m term per two records, the
+// strip's outputs stored straight to Y: no k split).  The records stream
+// through 8 register slots: slot q holds record q of the current strip and,
+// once its four blocks are used, takes record q of the wavefront's next
+// strip, so the next strip's loads are in flight while the current one is
+// multiplied.  (k_q4_mm16 over more strips than CUs x 16 runs more
+// workgroups than CUs, and each of them stages the same activations again.)
+template <int WAVES, bool XVEC>
+__global__ __launch_bounds__(WAVES * 64) void k_q4_mm16_wide(Q4Params p) {
+    constexpr int NT = WAVES * 64, QMAX = 8, NBLK = 4 * QMAX, NG = NBLK / 8;
+    static_assert(NBLK * 64 % NT == 0, "pieces per thread");
+    constexpr int PPT = NBLK * 64 / NT;
+    __shared__ __attribute__((aligned(16))) uint8_t sA[NBLK][2][1024];
+    __shared__ __attribute__((aligned(16))) uint8_t sXM[NG][3][1024];
+    __shared__ float s_rmax[WAVES][16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = (int)gridDim.x;
+    const int first = (int)((int64_t)blockIdx.x * p.NS / G);
+    const int end = (int)((int64_t)(blockIdx.x + 1) * p.NS / G);
+    const int nst = max(0, (end - first - wave + WAVES - 1) / WAVES);  // this wavefront's strips
+    const int nq = p.NQ;
+    const uint8_t *hdr = p.recs;
+    const uint8_t *recs = hdr + kHeaderBytes;
+
+    float xr[PPT][8];
+    load_pieces16<NT, PPT, XVEC>(p.X, p.ldx, p.M, p.NB, tid, 0, xr);
+    // every wavefront's activation loads go out before any record load
+    __builtin_amdgcn_s_barrier();
+
+    // records past the k range take the last record's codes and the header's
+    // zero tail for (d, m): they add nothing
+    v4i wc[QMAX], wd[QMAX];
+    auto gload = [&](int st, int q, v4i &dc, v4i &dd) {
+        const uint8_t *rec = recs + ((int64_t)st * nq + min(q, nq - 1)) * kQ4RecBytes;
+        dc = __builtin_nontemporal_load((const v4i *)(rec + (uint32_t)lane * 16u));
+        dd = __builtin_nontemporal_load(
+            (const v4i *)(q < nq ? rec + 1024 + (uint32_t)(lane & 15) * 16u : hdr + kHeaderBytes - 16));
+    };
+    int strip = min(first + wave, p.NS - 1);
+    static_for<QMAX>([&](auto Q) {
+        constexpr int q = decltype(Q)::value;
+        gload(strip, q, wc[q], wd[q]);
+    });
+
+    stage16<WAVES, NBLK, PPT>(tid, lane, wave, xr, sA, sXM, s_rmax);
+
+    int esc[4];  // -sc of this lane's output rows
+#pragma unroll
+    for (int v = 0; v < 4; ++v) esc[v] = -row_sc16<WAVES>(s_rmax, 4 * (lane >> 4) + v);
+    const int a_off = lane * 16;
+
+    // one strip; NEXT: refill each slot with the same record of the
+    // wavefront's next strip (inlined: the slots must stay in registers)
+    auto run_strip = [&](auto NEXT) __attribute__((always_inline)) {
+        constexpr bool next = decltype(NEXT)::value;
+        const int ahead = strip + WAVES;
+        v4f acc_y = {0.0f, 0.0f, 0.0f, 0.0f}, acc_m = {0.0f, 0.0f, 0.0f, 0.0f};
+        uint32_t mw[2][2];  // m values of the last two records, bf16 pairs (k = block)
+        static_for<QMAX>([&](auto Q) {
+            constexpr int q = decltype(Q)::value;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int bl = 4 * q + i;
+                v8h a[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) a[t] = *(const v8h *)(&sA[bl][t][a_off]);
+                const v8h bop = decode8h((uint32_t)wc[q][i]);
+                const float d = bf16_lo_f32((uint32_t)wd[q][i]);
+                v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bop, acc, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc_y[v] = fmaf(d, acc[v], acc_y[v]);
+                asm volatile("" : "+v"(acc_y));
+            }
+            mw[q & 1][0] = __builtin_amdgcn_perm((uint32_t)wd[q][1], (uint32_t)wd[q][0], 0x07060302u);
+            mw[q & 1][1] = __builtin_amdgcn_perm((uint32_t)wd[q][3], (uint32_t)wd[q][2], 0x07060302u);
+            if constexpr (next) gload(ahead, q, wc[q], wd[q]);
+            if constexpr ((q & 1) != 0) {
+                v8bf xm[3];
+#pragma unroll
+                for (int t = 0; t < 3; ++t) xm[t] = *(const v8bf *)(&sXM[q >> 1][t][a_off]);
+                const v4i mv = {(int)mw[0][0], (int)mw[0][1], (int)mw[1][0], (int)mw[1][1]};
+                const v8bf mop = __builtin_bit_cast(v8bf, mv);
+#pragma unroll
+                for (int t = 0; t < 3; ++t) acc_m = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm[t], mop, acc_m, 0, 0, 0);
+            }
+        });
+        const int n = strip * 16 + (lane & 15);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int row = 4 * (lane >> 4) + v;
+            if (row < p.M && n < p.N) p.Y[(int64_t)row * p.ldy + n] = __builtin_ldexpf(acc_y[v], esc[v]) + acc_m[v];
+        }
+        strip += WAVES;
+    };
+    for (int i = 0; i + 1 < nst; ++i) run_strip(std::true_type{});
+    if (nst > 0) run_strip(std::false_type{});
 }
 
 // Sum of the k-split partials in split order.  Loads go out eight at a time
@@ -1695,6 +1829,16 @@ hipError_t launch_q4_dense(const Q4Params &p, int mt, int waves, int cs, int64_t
         else if (waves == 16) by_m(ic<16>{});
         else ok = false;
         if (!ok) return hipErrorInvalidValue;
+        return hipGetLastError();
+    } else if (mt == 1 && cs == 1) {
+        // k_q4_mm16_wide: one workgroup per CU at most, strips in contiguous
+        // ranges, the whole k range (at most 8 records) staged once
+        *variant = "q4_mm16_wide";
+        if (p.NQ > 8 || p.M > 16 || p.S != 1 || waves != 8 || grid > p.NS) return hipErrorInvalidValue;
+        if (p.x_vec)
+            hipLaunchKernelGGL((k_q4_mm16_wide<8, true>), g, b, 0, s, p);
+        else
+            hipLaunchKernelGGL((k_q4_mm16_wide<8, false>), g, b, 0, s, p);
         return hipGetLastError();
     } else if (mt == 1 && waves == 8) {
         // k_q4_mm16<8, 2, 8, 2, XVEC>: at most 8 records per workgroup, 2 in flight

@@ -94,7 +94,7 @@ struct MoeSplit {
 };
 
 struct Q4Plan {
-    int mt, waves, cs, S, qps;  // cs: strips per workgroup of the M <= 4 kernel
+    int mt, waves, cs, S, qps;  // cs: mt 0, strips per workgroup; mt 1, 1 = k_q4_mm16_wide
     int64_t grid, rows_per_launch;
     int64_t ws_part_off, ws_bytes;
 };

@@ -87,6 +87,7 @@ def test_lm_head_q4_1(q, orc, weight):
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
         ws = q.workspace(q.lib.qmm_q4_1_matmul_workspace_bytes(M, K, N), dev)
         q.q4_1_matmul(to_dev(X), p, out=y, ws=ws)
+        assert q.last_variant() == ("q4_gemv_m1_wide" if M == 1 else "q4_mm16_wide"), q.last_variant()
         got = to_np(y)
         assert np.isfinite(got).all()
         ref = orc.q4_1_matmul(X, bc, K, len(cols))

@@ -138,6 +138,39 @@ def test_q4_matmul_one_row_wide(q, orc, K, N):
     assert np.array_equal(c.view(np.uint32), got.view(np.uint32))
 
 
+@pytest.mark.parametrize("M,K,N", [(16, 96, 131200), (5, 512, 65557), (12, 160, 70001), (16, 1024, 65600)])
+def test_q4_matmul_rows_wide(q, orc, M, K, N):
+    """5 <= M <= 16 over more than 4096 strips with at most 8 records each
+    (an lm_head's shape class): the persistent form, one workgroup per CU
+    over a contiguous run of strips, each wavefront running its strips in
+    turn with the next strip's records loading.  1, 4, 2 and 8 records per
+    strip (160 = 5 blocks: a ragged last record), ragged N (a last
+    wavefront with fewer strips), zero columns and zero-scale blocks, at the
+    1e-5 bound; unaligned activations and a second call give the same
+    bits."""
+    import torch
+    seed = M + K + N
+    got, ref = _matmul_case(q, orc, M, K, N, seed=seed, variant="q4_mm16_wide", zero_cols=(3, N - 1),
+                            zero_scale_blocks=True)
+    blocks = _blocks(K, N, seed, zero_cols=(3, N - 1), zero_scale_blocks=True)
+    p = _repack(q, blocks, K, N)
+    X = wl.q4_activations(M, K, seed_index=seed)
+    again = to_np(q.q4_1_matmul(to_dev(X), p))
+    assert np.array_equal(again.view(np.uint32), got.view(np.uint32))
+    Xw = torch.zeros((M, K + 1), dtype=torch.float32, device=torch_dev())
+    Xw[:, 1:] = to_dev(X)
+    c = to_np(q.q4_1_matmul(Xw[:, 1:], p))
+    assert q.last_variant() == "q4_mm16_wide"
+    assert np.array_equal(c.view(np.uint32), got.view(np.uint32))
+
+
+def test_q4_matmul_rows_wide_threshold(q, orc):
+    """4096 strips still take the k-split kernel (one workgroup per CU);
+    4097 take the persistent form.  Both at the 1e-5 bound."""
+    _matmul_case(q, orc, 16, 128, 16 * 4096, seed=5, variant="q4_mm16")
+    _matmul_case(q, orc, 16, 128, 16 * 4096 + 1, seed=6, variant="q4_mm16_wide")
+
+
 def test_q4_matmul_one_row_paths(q, orc):
     """M = 1: the one-launch kernel (aligned and unaligned activations, bitwise
     repeatable), its fallback when a wavefront would hold more than 8 records,
