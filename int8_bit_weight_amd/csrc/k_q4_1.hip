@@ -1122,8 +1122,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
 
 // 5 <= M <= 16 over many strips with at most 8 records each (K <= 1024,
 // e.g. an lm_head): a persistent form of k_q4_mm16.  The grid is at most one
-// workgroup per CU; workgroup b of G owns the strips [b NS / G,
-// (b + 1) NS / G), stages the activations of the whole k range once
+// workgroup per CU; workgroup b of G owns a contiguous run of NS / G or
+// NS / G + 1 strips, stages the activations of the whole k range once
 // (stage16) and each wavefront then runs the strips first + wave,
 // first + wave + WAVES, ... one at a time over their whole k range (per
 // block two fp16 MFMAs and y += d acc, the m term per two records, the
@@ -1145,10 +1145,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16_wide(Q4Params p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G = (int)gridDim.x;
-    const int first = (int)((int64_t)blockIdx.x * p.NS / G);
-    const int end = (int)((int64_t)(blockIdx.x + 1) * p.NS / G);
-    const int nst = max(0, (end - first - wave + WAVES - 1) / WAVES);  // this wavefront's strips
+    // workgroup b of G: NS / G strips, one more for b < NS % G
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int sq = p.NS / G, sr = p.NS % G;
+    const int first = b * sq + min(b, sr);
+    const int cnt = sq + (b < sr ? 1 : 0);
+    const int nst = max(0, (cnt - wave + WAVES - 1) / WAVES);  // this wavefront's strips
     const int nq = p.NQ;
     const uint8_t *hdr = p.recs;
     const uint8_t *recs = hdr + kHeaderBytes;
