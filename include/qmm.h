@@ -296,7 +296,8 @@ size_t qmm_q4_1_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * relative Frobenius error against exact arithmetic is below 1e-5.
  * workspace: device, >= qmm_q4_1_matmul_workspace_bytes(M,K,N), 256-byte
  * aligned, any contents (the k-split partial sums).  That size is
- * 0 for M <= 4 (one launch, no partial sums), where workspace may be NULL.
+ * 0 for M <= 4, and for M <= 16 with K <= 1024 (one launch covers the whole
+ * k range: no partial sums); workspace may then be NULL.
  */
 qmm_status q4_1_matmul(const float *X, int64_t M, int64_t K, int64_t ldx,
                        const void *Wpacked, int64_t N, float *Y, int64_t ldy,

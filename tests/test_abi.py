@@ -59,6 +59,12 @@ def test_size_queries(q):
     assert q.lib.qmm_pack_b_int8_bytes(100, 17) == 64 + 128 * 32 + 8 * 32
     assert q.lib.qmm_int8_gemm_workspace_bytes(2048, 4096, 4096) == 0  # prefill: no split-K
     assert q.lib.qmm_int8_gemm_workspace_bytes(16, 1024, 1024) == 0  # decode: no cross-workgroup split
+    # q4_1: no partial sums at M <= 4, nor at M <= 16 with K <= 1024 (one launch
+    # covers the whole k range, the lm_head shape included); k splits otherwise
+    assert q.lib.qmm_q4_1_matmul_workspace_bytes(4, 14336, 4096) == 0
+    assert q.lib.qmm_q4_1_matmul_workspace_bytes(16, 1024, 151936) == 0
+    assert q.lib.qmm_q4_1_matmul_workspace_bytes(9, 1024, 300) == 0
+    assert q.lib.qmm_q4_1_matmul_workspace_bytes(16, 4096, 14336) == 4 * 16 * 14336 * 4
 
 
 FAKE = ctypes.c_void_p(4096)  # never dereferenced: each call below fails validation first
