@@ -467,37 +467,27 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide(Int8GemmPa
 // reach only outputs that are not stored; k past K multiplies the zero codes
 // of the padded weight.  Workgroup 0 also writes the codes and scales out
 // when asked.
-template <int MT, int D, int MP, int CPT>
-__global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide_q(Int8GemmParams p) {
-    constexpr int NT = kWideWaves * 64;
-    constexpr int TPR = NT / MP;             // threads per row
-    constexpr int L = TPR < 64 ? TPR : 64;   // lanes of a row in one wavefront
-    constexpr int WPR = TPR / L;             // wavefronts per row
-    static_assert(MP <= 16 * MT && (MP & (MP - 1)) == 0, "rows");
-    extern __shared__ v4i s_a[];  // [KT][MT][64]
-    __shared__ float s_amax[MP][WPR];
-    __shared__ float s_scale[MP];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int strip_raw = (int)blockIdx.x * kWideWaves + wave;
-    const bool strip_ok = strip_raw < p.NS;
-    const int strip = min(strip_raw, p.NS - 1);
-    const int8_t *codes = p.codes + (int64_t)strip * p.KT * kTileBytes + lane * 16;
-    const int last = p.KT - 1;
-
-    // the activation chunks of this thread: row r, chunks j + i TPR
+template <int MP, int CPT>
+__device__ __forceinline__ void wide_q_load(const Int8GemmParams &p, int tid, v4f (&xv)[CPT]) {
+    constexpr int TPR = kWideWaves * 64 / MP;
     const int r = tid / TPR, j = tid % TPR;
     const int nch = p.K >> 2;
     const float *xrow = p.X + (int64_t)min(r, p.M - 1) * p.ldx;
-    v4f xv[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) xv[i] = *(const v4f *)(xrow + 4 * min(j + i * TPR, nch - 1));
-    v4i bf[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) bf[i] = *(const v4i *)(codes + (int64_t)min(i, last) * kTileBytes);
-    const ColOps col = load_colops_c(p, strip * kTileN + (lane & 15));
+}
 
+// s_amax: [MP][wavefronts per row]; s_scale: [MP].  Ends with a barrier
+// (LDS only: the weight loads in flight are not waited for).
+template <int MT, int MP, int CPT>
+__device__ __forceinline__ void wide_q_quantize(const Int8GemmParams &p, int tid, int lane, int wave,
+                                                const v4f (&xv)[CPT], v4i *s_a, float *s_amax, float *s_scale) {
+    constexpr int TPR = kWideWaves * 64 / MP;  // threads per row
+    constexpr int L = TPR < 64 ? TPR : 64;     // lanes of a row in one wavefront
+    constexpr int WPR = TPR / L;               // wavefronts per row
+    static_assert(MP <= 16 * MT && (MP & (MP - 1)) == 0, "rows");
+    const int r = tid / TPR, j = tid % TPR;
+    const int nch = p.K >> 2;
     // row maxima (chunks past K count as zeros)
     float a = 0.0f;
 #pragma unroll
@@ -507,10 +497,10 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide_q(Int8Gemm
             for (int e = 0; e < 4; ++e) a = fmaxf(a, fabsf(xv[i][e]));
     a = group_max<L>(a);
     if constexpr (WPR > 1) {
-        if (lane == 0) s_amax[r][wave % WPR] = a;
+        if (lane == 0) s_amax[r * WPR + wave % WPR] = a;
         __syncthreads();
 #pragma unroll
-        for (int w = 0; w < WPR; ++w) a = fmaxf(a, s_amax[r][w]);
+        for (int w = 0; w < WPR; ++w) a = fmaxf(a, s_amax[r * WPR + w]);
     }
     const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
     const float y = 1.0f / s;
@@ -540,6 +530,30 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide_q(Int8Gemm
         }
     }
     __syncthreads();
+}
+
+template <int MT, int D, int MP, int CPT>
+__global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide_q(Int8GemmParams p) {
+    constexpr int WPR = (kWideWaves * 64 / MP) / ((kWideWaves * 64 / MP) < 64 ? (kWideWaves * 64 / MP) : 64);
+    extern __shared__ v4i s_a[];  // [KT][MT][64]
+    __shared__ float s_amax[MP * WPR];
+    __shared__ float s_scale[MP];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int strip_raw = (int)blockIdx.x * kWideWaves + wave;
+    const bool strip_ok = strip_raw < p.NS;
+    const int strip = min(strip_raw, p.NS - 1);
+    const int8_t *codes = p.codes + (int64_t)strip * p.KT * kTileBytes + lane * 16;
+    const int last = p.KT - 1;
+
+    v4f xv[CPT];
+    wide_q_load<MP, CPT>(p, tid, xv);
+    v4i bf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) bf[i] = *(const v4i *)(codes + (int64_t)min(i, last) * kTileBytes);
+    const ColOps col = load_colops_c(p, strip * kTileN + (lane & 15));
+    wide_q_quantize<MT, MP, CPT>(p, tid, lane, wave, xv, s_a, s_amax, s_scale);
 
     v4i acc[MT];
 #pragma unroll
@@ -565,6 +579,73 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide_q(Int8Gemm
             if (strip_ok && m < p.M && n < p.N)
                 epilogue_store_c(p, m, n, (uint32_t)acc[t][i], 0, false, s_scale[min(m, MP - 1)], 0, col);
         }
+}
+
+// A persistent form of k_int8_decode_wide_q for M <= 16 and K <= 1024 (at
+// most 16 k tiles) over many strips: two workgroups per CU (at most 128
+// VGPRs); workgroup b of G owns a contiguous run of NS / G or NS / G + 1
+// strips and quantises the rows once, then each wavefront runs the strips
+// first + wave, first + wave + 8, ... in turn.  Register slot i holds k tile i of the
+// current strip and, once it is multiplied, takes tile i of the wavefront's
+// next strip (the column operands of the next strip are loaded likewise), so
+// the next strip's loads are in flight while one is multiplied.  Per strip
+// the arithmetic and the epilogue are k_int8_decode_wide_q's.
+template <int MP, int CPT>
+__global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_int8_decode_wide_qp(
+    Int8GemmParams p) {
+    constexpr int D = 16;
+    constexpr int WPR = (kWideWaves * 64 / MP) / ((kWideWaves * 64 / MP) < 64 ? (kWideWaves * 64 / MP) : 64);
+    extern __shared__ v4i s_a[];  // [KT][64]
+    __shared__ float s_amax[MP * WPR];
+    __shared__ float s_scale[MP];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // workgroup b of G: NS / G strips, one more for b < NS % G
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int sq = p.NS / G, sr = p.NS % G;
+    const int first = b * sq + min(b, sr);
+    const int cnt = sq + (b < sr ? 1 : 0);
+    const int nst = max(0, (cnt - wave + kWideWaves - 1) / kWideWaves);  // this wavefront's strips
+    const int KT = p.KT, last = KT - 1;
+    const int8_t *codes = p.codes + lane * 16;
+    int strip = min(first + wave, p.NS - 1);
+
+    v4f xv[CPT];
+    wide_q_load<MP, CPT>(p, tid, xv);
+    v4i bf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) bf[i] = *(const v4i *)(codes + ((int64_t)strip * KT + min(i, last)) * kTileBytes);
+    ColOps col = load_colops_c(p, strip * kTileN + (lane & 15));
+    wide_q_quantize<1, MP, CPT>(p, tid, lane, wave, xv, s_a, s_amax, s_scale);
+    float rs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[i] = s_scale[min(4 * (lane >> 4) + i, MP - 1)];
+
+    // one strip; NEXT: refill the slots and column operands from the
+    // wavefront's next strip (inlined: the slots must stay in registers)
+    auto run_strip = [&](auto NEXT) __attribute__((always_inline)) {
+        constexpr bool next = decltype(NEXT)::value;
+        const int ahead = strip + kWideWaves;
+        v4i acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            if (i < KT) acc = mfma_i8(s_a[i * 64 + lane], bf[i], acc);
+            if constexpr (next) bf[i] = *(const v4i *)(codes + ((int64_t)ahead * KT + min(i, last)) * kTileBytes);
+        }
+        ColOps cn = col;
+        if constexpr (next) cn = load_colops_c(p, ahead * kTileN + (lane & 15));
+        const int n = strip * kTileN + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * (lane >> 4) + i;
+            if (m < p.M && n < p.N) epilogue_store_c(p, m, n, (uint32_t)acc[i], 0, false, rs[i], 0, col);
+        }
+        col = cn;
+        strip = ahead;
+    };
+    for (int i = 0; i + 1 < nst; ++i) run_strip(std::true_type{});
+    if (nst > 0) run_strip(std::false_type{});
 }
 
 // Fused dynamic quantisation for small M x K (the planner takes it while
@@ -993,10 +1074,41 @@ hipError_t launch_dyn_rows(const Int8Plan &plan, const Int8GemmParams &p, const 
     return launch_dyn_w<16, GROUPED>(p, dg, w, spw, v, s);
 }
 
+template <int MP>
+hipError_t launch_wide_qp_mp(const Int8GemmParams &p, unsigned grid, hipStream_t s) {
+    // K <= 1024: at most K / 4 = 256 chunks a row over 512 / MP threads, so
+    // CPT <= MP / 2 (1 below four rows)
+    const size_t lds = (size_t)p.KT * 64 * sizeof(v4i);
+    const int cpt = (int)ceil_div(p.K / 4, kWideWaves * 64 / MP);
+    auto go = [&](auto C) {
+        hipLaunchKernelGGL((k_int8_decode_wide_qp<MP, decltype(C)::value>), dim3(grid), dim3(kWideWaves * 64), lds,
+                           s, p);
+        return hipGetLastError();
+    };
+    if (cpt <= 1) return go(std::integral_constant<int, 1>{});
+    if constexpr (MP >= 4)
+        if (cpt <= 2) return go(std::integral_constant<int, 2>{});
+    if constexpr (MP >= 8)
+        if (cpt <= 4) return go(std::integral_constant<int, 4>{});
+    if constexpr (MP >= 16)
+        if (cpt <= 8) return go(std::integral_constant<int, 8>{});
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_int8_gemm_dynamic_wide(const Int8GemmParams &p, hipStream_t s, const char **variant) {
     const int mt = p.M <= 16 ? 1 : 2;
     *variant = mt == 1 ? "int8_dynamic_wide_m16" : "int8_dynamic_wide_m32";
     if (p.KT * mt > kWideMaxTiles || p.K % 4 != 0 || !p.x_vec) return hipErrorInvalidValue;
+    if (mt == 1 && p.KT <= 16 && p.NS >= kWidePersistStrips) {
+        // two workgroups per CU, each quantising the rows once
+        *variant = "int8_dynamic_wide_m16p";
+        const unsigned g = kWidePersistGrid;
+        if (p.M <= 1) return launch_wide_qp_mp<1>(p, g, s);
+        if (p.M <= 2) return launch_wide_qp_mp<2>(p, g, s);
+        if (p.M <= 4) return launch_wide_qp_mp<4>(p, g, s);
+        if (p.M <= 8) return launch_wide_qp_mp<8>(p, g, s);
+        return launch_wide_qp_mp<16>(p, g, s);
+    }
     if (mt == 1) return p.KT <= 8 ? launch_wide_q_d<1, 8>(p, s) : launch_wide_q_d<1, 16>(p, s);
     return p.KT <= 8 ? launch_wide_q_d<2, 8>(p, s) : launch_wide_q_d<2, 16>(p, s);
 }

@@ -142,6 +142,11 @@ struct DecodeGroups {
 // tiles), 64 KiB.  It is planned from this many 16-column strips on.
 constexpr int kWideWaves = 8;        // strips (wavefronts) per workgroup
 constexpr int kWideMaxTiles = 64;
+// persistent wide decode (k_int8_decode_wide_qp): its grid (two workgroups
+// per CU: measured 2-6 % faster than one on the lm_head), and the strips
+// from which it is taken (at least one per wavefront)
+constexpr int kWidePersistGrid = 512;
+constexpr int64_t kWidePersistStrips = 4096;
 constexpr int64_t kWideMinStrips = 1024;
 
 struct Int8Plan {

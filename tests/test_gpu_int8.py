@@ -203,16 +203,19 @@ def test_wide_decode_unaligned_a(q, orc):
     assert np.array_equal(to_np(y), ref.astype(np.int32))
 
 
-def _wide_dynamic_variant(M, K, ldx=None, aligned=True):
+def _wide_dynamic_variant(M, K, ldx=None, aligned=True, N=16500):
     """The form int8_gemm_dynamic takes over >= 1024 strips: the quantisation
     inside the wide decode while the rows rounded up to a power of two times
-    K stay within 16384 (X 16-byte aligned, K and ldx multiples of 4), else
-    the row quantiser, then the wide decode."""
+    K stay within 16384 (X 16-byte aligned, K and ldx multiples of 4), its
+    persistent form (two workgroups per CU) at M <= 16, K <= 1024 and >= 4096
+    strips; else the row quantiser, then the wide decode."""
     mp = 1
     while mp < M:
         mp *= 2
     ldx = K if ldx is None else ldx
     if mp * K <= 16384 and K % 4 == 0 and ldx % 4 == 0 and aligned:
+        if M <= 16 and K <= 1024 and (N + 15) // 16 >= 4096:
+            return "int8_dynamic_wide_m16p"
         return "int8_dynamic_wide_m16" if M <= 16 else "int8_dynamic_wide_m32"
     return "int8_decode_wide_m16" if M <= 16 else "int8_decode_wide_m32"
 
@@ -224,9 +227,23 @@ def test_wide_decode_dynamic_fused(q, orc, M, K):
     wide decode (one launch) where the planner takes it, else the row
     quantiser first.  Codes and row scales bit for bit the oracle's, fp32
     outputs bit for bit the two-call form's, int32 the oracle's product."""
+    _wide_fused_case(q, orc, M, K, 16500)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 1024, 65600), (16, 1024, 65541), (3, 1000, 70000), (9, 512, 65536),
+                                   (16, 64, 65536 + 16 * 7 + 3), (5, 1024, 16 * 4096)])
+def test_wide_decode_dynamic_persistent(q, orc, M, K, N):
+    """The persistent form (>= 4096 strips, M <= 16, K <= 1024): two
+    workgroups per CU, each quantising the rows once, each wavefront running its
+    strips in turn.  Ragged strip counts per workgroup and wavefront, ragged
+    N, K below one tile row (64) and not a multiple of 64; the same bars as
+    the one-strip-per-wavefront form."""
+    _wide_fused_case(q, orc, M, K, N)
+
+
+def _wide_fused_case(q, orc, M, K, N):
     import torch
     dev = torch_dev()
-    N = 16500
     g = np.random.default_rng(M * 13 + K)
     W = wl.normal_f32(g, (K, N), 0.02)
     X = wl.normal_f32(g, (M, K))
@@ -240,7 +257,7 @@ def test_wide_decode_dynamic_fused(q, orc, M, K):
     xq = torch.full((M, K), 99, dtype=torch.int8, device=dev)
     rs = torch.full((M,), -1.0, dtype=torch.float32, device=dev)
     q.int8_gemm_dynamic(Xd, p, out_f32=y, out_i32=y32, xq_out=xq, rs_out=rs)
-    assert q.last_variant() == _wide_dynamic_variant(M, K)
+    assert q.last_variant() == _wide_dynamic_variant(M, K, N=N)
     Qa, sa = orc.quantize_rows_int8(X)
     assert np.array_equal(to_np(xq), Qa)
     assert np.array_equal(to_np(rs).view(np.uint32), sa.view(np.uint32))

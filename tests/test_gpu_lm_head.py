@@ -62,7 +62,7 @@ def test_lm_head_int8(q, orc, weight):
         xq = torch.empty((M, K), dtype=torch.int8, device=dev)
         rs = torch.empty((M,), dtype=torch.float32, device=dev)
         q.int8_gemm_dynamic(to_dev(X), p, out_f32=y, out_i32=y32, xq_out=xq, rs_out=rs)
-        assert q.last_variant() == "int8_dynamic_wide_m16", q.last_variant()
+        assert q.last_variant() == "int8_dynamic_wide_m16p", q.last_variant()
         Qa, sa = orc.quantize_rows_int8(X)
         assert np.array_equal(to_np(xq), Qa)
         assert np.array_equal(to_np(rs).view(np.uint32), sa.view(np.uint32))
