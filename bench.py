@@ -84,10 +84,11 @@ def parse_args():
                     help="counter probe: one plain read of 1 GiB (the calibration read), then one eager step")
     ap.add_argument("--profile", action="store_true",
                     help="the timed leg alone (setup, graph capture, warm-up and timed replays)")
-    ap.add_argument("--profile-leg", choices=("decode", "prefill", "q4"), default="decode",
+    ap.add_argument("--profile-leg", choices=("decode", "prefill", "q4", "lmhead"), default="decode",
                     help="--profile: the decode step (default), the M = 2048 prefill shapes (each warmed up "
-                         "and then launched --steps times in a row), or the q4_1 calls (M = 1 and 16 on both "
-                         "shapes, then MUL_MAT_ID in both forms) over rings of weight copies")
+                         "and then launched --steps times in a row), the q4_1 calls (M = 1 and 16 on both "
+                         "shapes, then MUL_MAT_ID in both forms) over rings of weight copies, or the "
+                         "lm_head-shaped calls (int8 and q4_1, M = 1 and 16) over rings of weight copies")
     ap.add_argument("--summarize", metavar="DB", help="summarize a rocprofv3 database (no GPU needed)")
     ap.add_argument("--kernel", default="", help="--summarize: kernel name substring")
     ap.add_argument("--last", type=int, default=0, help="--summarize: only the last N matching dispatches")
@@ -278,6 +279,8 @@ def main() -> int:
         return profile_prefill(args, q, wl, torch, np, dev)
     if args.profile and args.profile_leg == "q4":
         return profile_q4(args, q, wl, torch, np, dev)
+    if args.profile and args.profile_leg == "lmhead":
+        return profile_lm_head(args, q, wl, torch, np, dev)
     layers = args.layers or wl.QWEN3_0_6B_LAYERS
     projs = wl.QWEN3_0_6B_PROJECTIONS
     rows = wl.DECODE_ROWS
@@ -519,6 +522,47 @@ def profile_q4(args, q, wl, torch, np, dev):
         res[name] = {"calls": 2 * len(rings), "algorithmic_bytes_per_call": q4_moe_bytes(wl, E, K, N, X, Y)}
         del rings, ed
     print(json.dumps({"profile": "q4", "calls": res}), flush=True)
+    return 0
+
+
+def profile_lm_head(args, q, wl, torch, np, dev):
+    """The lm_head-shaped calls alone, eager, in order (for rocprofv3): the
+    int8 path (int8_gemm_dynamic, fp32 out) at M = 1 and 16, one call on each
+    of 4 packed copies twice over (~623 MB), then the q4_1 path at M = 1 and
+    16, one call on each of 6 copies (~583 MB)."""
+    K, N = wl.LM_HEAD_K, wl.LM_HEAD_N
+    Wh = wl.lm_head_weight()
+    Wl = torch.from_numpy(Wh).to(dev)
+    ring = [q.pack_b_int8(Wl) for _ in range(4)]
+    del Wl
+    res = {}
+    for M in wl.LM_HEAD_ROWS:
+        X = torch.from_numpy(wl.lm_head_activations(M, seed_index=M)).to(dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for pk in ring * 2:
+            q.int8_gemm_dynamic(X, pk, out_f32=Y)
+        torch.cuda.synchronize()
+        res["int8_m%d" % M] = {"calls": 2 * len(ring), "variant": q.last_variant(),
+                               "algorithmic_bytes_per_call": launch_bytes(M, K, [N])}
+    del ring
+    bd = torch.from_numpy(wl.encode_q4_1(Wh).reshape(-1)).to(dev)
+    del Wh
+    ring = [q.q4_1_repack(bd, K, N) for _ in range(6)]
+    del bd
+    wbytes = ring[0].data.numel() - 64
+    for M in wl.LM_HEAD_ROWS:
+        X = torch.from_numpy(wl.lm_head_activations(M, seed_index=100 + M)).to(dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        wsq = q.workspace(q.lib.qmm_q4_1_matmul_workspace_bytes(M, K, N), dev)
+        torch.cuda.synchronize()
+        for W in ring:
+            q.q4_1_matmul(X, W, out=Y, ws=wsq)
+        torch.cuda.synchronize()
+        res["q4_1_m%d" % M] = {"calls": len(ring), "variant": q.last_variant(),
+                               "algorithmic_bytes_per_call": wbytes + 4 * M * K + 4 * M * N}
+    del ring
+    print(json.dumps({"profile": "lmhead", "calls": res}), flush=True)
     return 0
 
 
