@@ -79,18 +79,38 @@ __device__ __forceinline__ v4i load_a16(const Int8GemmParams &p, int row, int k0
 // Epilogue operands of column n (loaded for every thread; columns past N
 // read column N-1 and are never stored).  Null operands read a valid array
 // and are replaced by 0.
-__device__ __forceinline__ ColOps load_colops_c(const Int8GemmParams &p, int n) {
+// The column operands as loaded (every load in range: absent vectors read
+// another column vector instead), and the operands they give.  Kept apart so
+// that a kernel loading the next strip's operands ahead does not wait for
+// those loads where it selects.
+struct ColRaw {
+    int32_t colsum, bi, zb;
+    float cs, bf;
+};
+
+__device__ __forceinline__ ColRaw load_colraw(const Int8GemmParams &p, int n) {
     const int c = min(n, p.N - 1);
-    const float bf = (p.bias_f32 ? p.bias_f32 : p.col_scale)[c];
-    const int32_t bi = (p.bias_i32 ? p.bias_i32 : p.colsum)[c];
-    const int32_t zb = (p.zb_col ? p.zb_col : p.colsum)[c];
+    ColRaw r;
+    r.bf = (p.bias_f32 ? p.bias_f32 : p.col_scale)[c];
+    r.bi = (p.bias_i32 ? p.bias_i32 : p.colsum)[c];
+    r.zb = (p.zb_col ? p.zb_col : p.colsum)[c];
+    r.colsum = p.colsum[c];
+    r.cs = p.col_scale[c];
+    return r;
+}
+
+__device__ __forceinline__ ColOps colops_of(const Int8GemmParams &p, const ColRaw &r) {
     ColOps o;
-    o.colsum = p.colsum[c];
-    o.cs = p.col_scale[c];
-    o.bias_f = p.bias_f32 ? bf : 0.0f;
-    o.bias_i = p.bias_i32 ? bi : 0;
-    o.zb = p.zb_col ? zb - p.zb_off : p.zBs;
+    o.colsum = r.colsum;
+    o.cs = r.cs;
+    o.bias_f = p.bias_f32 ? r.bf : 0.0f;
+    o.bias_i = p.bias_i32 ? r.bi : 0;
+    o.zb = p.zb_col ? r.zb - p.zb_off : p.zBs;
     return o;
+}
+
+__device__ __forceinline__ ColOps load_colops_c(const Int8GemmParams &p, int n) {
+    return colops_of(p, load_colraw(p, n));
 }
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {

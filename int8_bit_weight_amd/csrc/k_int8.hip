@@ -589,13 +589,16 @@ __global__ __launch_bounds__(kWideWaves * 64) void k_int8_decode_wide_q(Int8Gemm
 // current strip and, once it is multiplied, takes tile i of the wavefront's
 // next strip (the column operands of the next strip are loaded likewise), so
 // the next strip's loads are in flight while one is multiplied.  Per strip
-// the arithmetic and the epilogue are k_int8_decode_wide_q's.
+// the arithmetic and the epilogue are k_int8_decode_wide_q's.  All 16 tiles
+// are multiplied whatever KT is: operand tiles KT..15 are zero in LDS (and
+// their weight slots re-read tile KT - 1), so no branch sits between an MFMA
+// and the instructions that read its result.
 template <int MP, int CPT>
 __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_int8_decode_wide_qp(
     Int8GemmParams p) {
     constexpr int D = 16;
     constexpr int WPR = (kWideWaves * 64 / MP) / ((kWideWaves * 64 / MP) < 64 ? (kWideWaves * 64 / MP) : 64);
-    extern __shared__ v4i s_a[];  // [KT][64]
+    __shared__ v4i s_a[D * 64];  // 16 operand tiles, those past KT zero
     __shared__ float s_amax[MP * WPR];
     __shared__ float s_scale[MP];
     const int tid = threadIdx.x;
@@ -616,7 +619,8 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
     v4i bf[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) bf[i] = *(const v4i *)(codes + ((int64_t)strip * KT + min(i, last)) * kTileBytes);
-    ColOps col = load_colops_c(p, strip * kTileN + (lane & 15));
+    ColRaw col = load_colraw(p, strip * kTileN + (lane & 15));
+    for (int u = KT * 64 + tid; u < D * 64; u += kWideWaves * 64) s_a[u] = v4i{0, 0, 0, 0};
     wide_q_quantize<1, MP, CPT>(p, tid, lane, wave, xv, s_a, s_amax, s_scale);
     float rs[4];
 #pragma unroll
@@ -630,16 +634,20 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
         v4i acc = {0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < D; ++i) {
-            if (i < KT) acc = mfma_i8(s_a[i * 64 + lane], bf[i], acc);
+            acc = mfma_i8(s_a[i * 64 + lane], bf[i], acc);
             if constexpr (next) bf[i] = *(const v4i *)(codes + ((int64_t)ahead * KT + min(i, last)) * kTileBytes);
+            // keeps each tile's operand read next to its MFMA (hoisted, the
+            // 16 reads held 64 more registers and spilled)
+            asm volatile("" ::: "memory");
         }
-        ColOps cn = col;
-        if constexpr (next) cn = load_colops_c(p, ahead * kTileN + (lane & 15));
+        ColRaw cn = col;
+        if constexpr (next) cn = load_colraw(p, ahead * kTileN + (lane & 15));
+        const ColOps co = colops_of(p, col);
         const int n = strip * kTileN + (lane & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * (lane >> 4) + i;
-            if (m < p.M && n < p.N) epilogue_store_c(p, m, n, (uint32_t)acc[i], 0, false, rs[i], 0, col);
+            if (m < p.M && n < p.N) epilogue_store_c(p, m, n, (uint32_t)acc[i], 0, false, rs[i], 0, co);
         }
         col = cn;
         strip = ahead;
@@ -1078,11 +1086,10 @@ template <int MP>
 hipError_t launch_wide_qp_mp(const Int8GemmParams &p, unsigned grid, hipStream_t s) {
     // K <= 1024: at most K / 4 = 256 chunks a row over 512 / MP threads, so
     // CPT <= MP / 2 (1 below four rows)
-    const size_t lds = (size_t)p.KT * 64 * sizeof(v4i);
     const int cpt = (int)ceil_div(p.K / 4, kWideWaves * 64 / MP);
     auto go = [&](auto C) {
-        hipLaunchKernelGGL((k_int8_decode_wide_qp<MP, decltype(C)::value>), dim3(grid), dim3(kWideWaves * 64), lds,
-                           s, p);
+        hipLaunchKernelGGL((k_int8_decode_wide_qp<MP, decltype(C)::value>), dim3(grid), dim3(kWideWaves * 64), 0, s,
+                           p);
         return hipGetLastError();
     };
     if (cpt <= 1) return go(std::integral_constant<int, 1>{});
