@@ -102,7 +102,8 @@ def _matmul_case(q, orc, M, K, N, seed, variant=None, **kw):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 32, 1), (1, 96, 17), (2, 64, 15), (16, 4096, 64), (17, 160, 300),
-                                   (33, 256, 40), (5, 1024, 33), (16, 32 * 44, 272), (64, 128, 48)])
+                                   (33, 256, 40), (5, 1024, 33), (16, 32 * 44, 272), (64, 128, 48),
+                                   (20, 2048, 303)])
 def test_q4_matmul_small(q, orc, M, K, N):
     _matmul_case(q, orc, M, K, N, seed=M * 7 + K + N, zero_cols=(3,), zero_scale_blocks=True)
 
@@ -211,7 +212,8 @@ def test_q4_matmul_one_row_paths(q, orc):
 
 
 @pytest.mark.parametrize("M,K,N,aligned", [(16, 1440, 300, True), (9, 1440, 300, False), (16, 256, 40, False),
-                                           (5, 32 * 37, 17, True), (12, 8192, 48, True)])
+                                           (5, 32 * 37, 17, True), (12, 8192, 48, True), (16, 1440, 301, True),
+                                           (7, 4096, 18, False)])
 def test_q4_matmul_m16_paths(q, orc, M, K, N, aligned):
     """5 <= M <= 16: whole k range staged at once.  K = 1440 (45 blocks):
     two k splits of 6 records, the second with a partial last record and two
@@ -230,6 +232,28 @@ def test_q4_matmul_m16_paths(q, orc, M, K, N, aligned):
     got = to_np(q.q4_1_matmul(Xd, p))
     assert q.last_variant() == "q4_mm16"
     _check(got, orc.q4_1_matmul(X, blocks, K, N))
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 1440, 300), (20, 2048, 300), (16, 4096, 256)])
+def test_q4_matmul_strided_output(q, orc, M, K, N):
+    """k-split sums written into an output of row stride N + 3 (no 16-byte
+    stores) and into one offset by a float: the same bits as the contiguous
+    output, and the columns past N untouched."""
+    import torch
+    dev = torch_dev()
+    blocks = _blocks(K, N, seed=M + K + N)
+    p = _repack(q, blocks, K, N)
+    X = to_dev(wl.q4_activations(M, K, seed_index=M + 3))
+    ref = to_np(q.q4_1_matmul(X, p))
+    buf = torch.full((M, N + 3), 7.0, dtype=torch.float32, device=dev)
+    q.q4_1_matmul(X, p, out=buf[:, :N])
+    got = to_np(buf)
+    assert np.array_equal(got[:, :N].view(np.uint32), ref.view(np.uint32))
+    assert (got[:, N:] == 7.0).all()
+    flat = torch.full((M * N + 1,), 7.0, dtype=torch.float32, device=dev)
+    q.q4_1_matmul(X, p, out=flat[1:].view(M, N))
+    assert np.array_equal(to_np(flat[1:]).reshape(M, N).view(np.uint32), ref.view(np.uint32))
+    assert to_np(flat[:1])[0] == 7.0
 
 
 def test_q4_matmul_variants_and_determinism(q, orc):
