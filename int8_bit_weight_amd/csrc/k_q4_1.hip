@@ -854,21 +854,24 @@ __global__ __launch_bounds__(512) void k_q4_gemv1_wide(Q4Params p) {
 }
 
 // ------------------- staging shared by the 16-row whole-range kernels ---
-// k_q4_mm16 and k_q4_mm16_wide split the activations of their whole k range
-// (NBLK blocks from block b0) into LDS once.  Piece pc = (block bl, k-octet
-// g, row r) is 8 activations, pc = 64 bl + 16 g + r; thread tid holds pieces
-// tid + i NT.  Rows past M read row M - 1 (they reach only outputs that are
-// never stored) and blocks past K read the last block, whose copies meet
-// zero (d, m) in the padded records, so no value needs masking: the row
-// maxima and the products of the real rows and blocks are those of the real
-// values.
-template <int NT, int PPT, bool XVEC>
-__device__ __forceinline__ void load_pieces16(const float *X, int64_t ldx, int M, int NB, int tid, int b0,
-                                              float (&xr)[PPT][8]) {
+// k_q4_mm16 and k_q4_mm16_wide (8 wavefronts) split the activations of their
+// whole k range (32 blocks from block b0) into LDS once.  Each wavefront
+// owns two rows, r = 2 wave + lane / 32; piece p = (block p / 4, k-octet
+// p % 4) of its row is 8 activations, and lane L holds pieces L % 32 + 32 i,
+// so a row's maximum, scale and block sums never leave its wavefront (no
+// barrier before the split).  Rows past M read row M - 1 (they reach only
+// outputs that are never stored) and blocks past K read the last block,
+// whose copies meet zero (d, m) in the padded records, so no value needs
+// masking: the row maxima and the products of the real rows and blocks are
+// those of the real values.
+template <int PPT, bool XVEC>
+__device__ __forceinline__ void load_pieces16(const float *X, int64_t ldx, int M, int NB, int lane, int wave,
+                                              int b0, float (&xr)[PPT][8]) {
+    const int r = 2 * wave + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-        const int pc = tid + i * NT;
-        const int r = pc & 15, g = (pc >> 4) & 3, bl = pc >> 6;
+        const int pc = (lane & 31) + 32 * i;
+        const int g = pc & 3, bl = pc >> 2;
         const int b = b0 + bl;
         const float *src = X + (int64_t)min(r, M - 1) * ldx + min(b, NB - 1) * 32 + g * 8;
         if (XVEC) {
@@ -886,46 +889,38 @@ __device__ __forceinline__ void load_pieces16(const float *X, int64_t ldx, int M
     }
 }
 
-// The power-of-two scale exponent of a row from the wavefronts' row maxima.
-template <int WAVES>
-__device__ __forceinline__ int row_sc16(const float (*s_rmax)[16], int row) {
-    float m = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) m = fmaxf(m, s_rmax[w][row]);
-    return m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;
-}
-
-// The split of the held pieces: each row's scale exponent sc over the range
-// (one LDS barrier), then the two fp16 terms of x 2^sc at sA[bl][term] in
-// MFMA lane order and the unscaled block sums, three bf16 terms, into the
-// m-term operands sXM (row r, block bl at byte 16 r + 2 (bl % 8) of
-// sXM[bl / 8]; k-octets 1..3 of each operand stay zero).  Ends with an
-// LDS-only barrier (no memory fence: record loads may be in flight).
+// The split of the held pieces: the row's scale exponent sc (sc = 15 - e for
+// max |x| = f 2^e, f in [0.5, 1); into s_sc[row] for the epilogue), then the
+// two fp16 terms of x 2^sc at sA[bl][term] in MFMA lane order and the
+// unscaled block sums (the four k-octets of a block lie in four consecutive
+// lanes), three bf16 terms, into the m-term operands sXM (row r, block bl at
+// byte 16 r + 2 (bl % 8) of sXM[bl / 8]; k-octets 1..3 of each operand stay
+// zero).  Ends with an LDS-only barrier (no memory fence: record loads may
+// be in flight).
 template <int WAVES, int NBLK, int PPT>
 __device__ __forceinline__ void stage16(int tid, int lane, int wave, const float (&xr)[PPT][8],
-                                        uint8_t (*sA)[2][1024], uint8_t (*sXM)[3][1024], float (*s_rmax)[16]) {
+                                        uint8_t (*sA)[2][1024], uint8_t (*sXM)[3][1024], int *s_sc) {
+    static_assert(WAVES == 8 && NBLK * 4 == 32 * PPT, "two rows per wavefront, 32 lanes a row");
     constexpr int NT = WAVES * 64;
     constexpr int NG = (NBLK + 7) / 8;
     for (int o = tid * 16; o < NG * 3 * 768; o += NT * 16) {
         const int f = o / 768;
         *(v4i *)(&sXM[0][0][0] + f * 1024 + 256 + o % 768) = v4i{0, 0, 0, 0};
     }
-    // a thread's pieces all belong to row tid % 16: its maximum, then the
-    // row's four k-octet lanes (xor 16, 32), then the wavefronts through LDS
+    const int r = 2 * wave + (lane >> 5);
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < PPT; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(xr[i][e]));
-    am = fmaxf(am, __shfl_xor(am, 16));
-    am = fmaxf(am, __shfl_xor(am, 32));
-    if (lane < 16) s_rmax[wave][lane] = am;
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int sc = row_sc16<WAVES>(s_rmax, tid & 15);
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) am = fmaxf(am, __shfl_xor(am, m));
+    const int sc = am > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(am) : 0;
+    if ((lane & 31) == 0) s_sc[r] = sc;
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-        const int pc = tid + i * NT;
-        const int r = pc & 15, g = (pc >> 4) & 3, bl = pc >> 6;
+        const int pc = (lane & 31) + 32 * i;
+        const int g = pc & 3, bl = pc >> 2;
         float bsum = 0.0f;
         uint32_t w[2][4];
 #pragma unroll
@@ -940,8 +935,8 @@ __device__ __forceinline__ void stage16(int tid, int lane, int wave, const float
             w[0][e >> 1] = __builtin_bit_cast(uint32_t, a0);
             w[1][e >> 1] = __builtin_bit_cast(uint32_t, a1);
         }
-        bsum += __shfl_xor(bsum, 16);
-        bsum += __shfl_xor(bsum, 32);
+        bsum += __shfl_xor(bsum, 1);
+        bsum += __shfl_xor(bsum, 2);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
             *(v4i *)(&sA[bl][t][(g * 16 + r) * 16]) = v4i{(int)w[t][0], (int)w[t][1], (int)w[t][2], (int)w[t][3]};
@@ -974,7 +969,8 @@ __device__ __forceinline__ void stage16(int tid, int lane, int wave, const float
 //   * staging: piece (block bl, k-octet g, row r) = 8 activations, loaded
 //     with two 16-byte loads ahead of the record loads.  Each row first
 //     gets a power-of-two scale over the workgroup's k range (sc = 15 - e,
-//     max |x| = f 2^e, f in [0.5, 1); one barrier): every x 2^sc lies below
+//     max |x| = f 2^e, f in [0.5, 1); a row's pieces all sit in one
+//     wavefront, so no barrier precedes the split): every x 2^sc lies below
 //     2^15, and its two fp16 terms h0 = fp16(x 2^sc), h1 = fp16(x 2^sc - h0)
 //     hold it to ~2^-22 relative (the scaling and the subtraction are
 //     exact).  The terms are stored at sA[bl][term] in MFMA lane order (lane
@@ -999,7 +995,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
     constexpr int SPG = WAVES * C;
     __shared__ __attribute__((aligned(16))) uint8_t sA[NBLK][2][1024];
     __shared__ __attribute__((aligned(16))) uint8_t sXM[NG][3][1024];
-    __shared__ float s_rmax[WAVES][16];
+    __shared__ int s_sc[16];  // the rows' scale exponents
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1015,7 +1011,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
 
     // ---- activation loads (first: the staging waits for them alone)
     float xr[PPT][8];
-    load_pieces16<NT, PPT, XVEC>(p.X, p.ldx, M, p.NB, tid, q0 * 4, xr);
+    load_pieces16<PPT, XVEC>(p.X, p.ldx, M, p.NB, lane, wave, q0 * 4, xr);
 
     // every wavefront's activation loads go out before any record load: the
     // memory pipeline returns them in order, and the staging needs them first
@@ -1041,7 +1037,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
 
     // ---- staging (its last barrier is LDS-only: a memory fence would wait
     // for the record loads still in flight)
-    stage16<WAVES, NBLK, PPT>(tid, lane, wave, xr, sA, sXM, s_rmax);
+    stage16<WAVES, NBLK, PPT>(tid, lane, wave, xr, sA, sXM, s_sc);
 
     // ---- the product
     v4f acc_y[C], acc_m[C];
@@ -1103,7 +1099,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16(Q4Params p) {
 
     int esc[4];  // -sc of this lane's output rows
 #pragma unroll
-    for (int v = 0; v < 4; ++v) esc[v] = -row_sc16<WAVES>(s_rmax, 4 * (lane >> 4) + v);
+    for (int v = 0; v < 4; ++v) esc[v] = -s_sc[4 * (lane >> 4) + v];
 #pragma unroll
     for (int j = 0; j < C; ++j)
 #pragma unroll
@@ -1140,7 +1136,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16_wide(Q4Params p) {
     constexpr int PPT = NBLK * 64 / NT;
     __shared__ __attribute__((aligned(16))) uint8_t sA[NBLK][2][1024];
     __shared__ __attribute__((aligned(16))) uint8_t sXM[NG][3][1024];
-    __shared__ float s_rmax[WAVES][16];
+    __shared__ int s_sc[16];  // the rows' scale exponents
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1156,7 +1152,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16_wide(Q4Params p) {
     const uint8_t *recs = hdr + kHeaderBytes;
 
     float xr[PPT][8];
-    load_pieces16<NT, PPT, XVEC>(p.X, p.ldx, p.M, p.NB, tid, 0, xr);
+    load_pieces16<PPT, XVEC>(p.X, p.ldx, p.M, p.NB, lane, wave, 0, xr);
     // every wavefront's activation loads go out before any record load
     __builtin_amdgcn_s_barrier();
 
@@ -1175,11 +1171,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_q4_mm16_wide(Q4Params p) {
         gload(strip, q, wc[q], wd[q]);
     });
 
-    stage16<WAVES, NBLK, PPT>(tid, lane, wave, xr, sA, sXM, s_rmax);
+    stage16<WAVES, NBLK, PPT>(tid, lane, wave, xr, sA, sXM, s_sc);
 
     int esc[4];  // -sc of this lane's output rows
 #pragma unroll
-    for (int v = 0; v < 4; ++v) esc[v] = -row_sc16<WAVES>(s_rmax, 4 * (lane >> 4) + v);
+    for (int v = 0; v < 4; ++v) esc[v] = -s_sc[4 * (lane >> 4) + v];
     const int a_off = lane * 16;
 
     // one strip; NEXT: refill each slot with the same record of the
