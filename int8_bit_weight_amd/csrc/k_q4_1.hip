@@ -798,8 +798,10 @@ __global__ __launch_bounds__(512) void k_q4_gemv1_wide(Q4Params p) {
         constexpr int q = decltype(S)::value;
         const bool pad = q >= nq;
         const uint8_t *rec = recs + ((int64_t)strip * nq + min(q, nq - 1)) * kQ4RecBytes;
-        wc[q] = *(const v4i *)(rec + (uint32_t)lane * 16u);
-        wd[q] = *(const v4i *)(pad ? hdr + kHeaderBytes - 16 : rec + 1024 + (uint32_t)(lane & 15) * 16u);
+        // non-temporal: each record is read once (19.5 -> 18.1 us on the lm_head)
+        wc[q] = __builtin_nontemporal_load((const v4i *)(rec + (uint32_t)lane * 16u));
+        wd[q] = __builtin_nontemporal_load(
+            (const v4i *)(pad ? hdr + kHeaderBytes - 16 : rec + 1024 + (uint32_t)(lane & 15) * 16u));
     });
     __builtin_amdgcn_sched_barrier(0);
     if (wave < 2) {
