@@ -618,7 +618,9 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
     wide_q_load<MP, CPT>(p, tid, xv);
     v4i bf[D];
 #pragma unroll
-    for (int i = 0; i < D; ++i) bf[i] = *(const v4i *)(codes + ((int64_t)strip * KT + min(i, last)) * kTileBytes);
+    // weight tiles non-temporal: each is read once (lm_head 29.7 -> 26.0 us at M = 1)
+    for (int i = 0; i < D; ++i)
+        bf[i] = __builtin_nontemporal_load((const v4i *)(codes + ((int64_t)strip * KT + min(i, last)) * kTileBytes));
     ColRaw col = load_colraw(p, strip * kTileN + (lane & 15));
     for (int u = KT * 64 + tid; u < D * 64; u += kWideWaves * 64) s_a[u] = v4i{0, 0, 0, 0};
     wide_q_quantize<1, MP, CPT>(p, tid, lane, wave, xv, s_a, s_amax, s_scale);
@@ -635,7 +637,8 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int i = 0; i < D; ++i) {
             acc = mfma_i8(s_a[i * 64 + lane], bf[i], acc);
-            if constexpr (next) bf[i] = *(const v4i *)(codes + ((int64_t)ahead * KT + min(i, last)) * kTileBytes);
+            if constexpr (next)
+                bf[i] = __builtin_nontemporal_load((const v4i *)(codes + ((int64_t)ahead * KT + min(i, last)) * kTileBytes));
             // keeps each tile's operand read next to its MFMA (hoisted, the
             // 16 reads held 64 more registers and spilled)
             asm volatile("" ::: "memory");
