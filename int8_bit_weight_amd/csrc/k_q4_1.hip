@@ -672,8 +672,10 @@ __global__ __launch_bounds__(W * 64) void k_q4_gemv1(Q4Params p) {
         const bool pad = q >= q1;
         const int qq = min(q, q1 - 1);
         const uint8_t *rec = recs + ((int64_t)strip * p.NQ + qq) * kQ4RecBytes;
-        wc[s] = *(const v4i *)(rec + (uint32_t)lane * 16u);
-        wd[s] = *(const v4i *)(pad ? hdr + kHeaderBytes - 16 : rec + 1024 + (uint32_t)(lane & 15) * 16u);
+        // non-temporal: each record is read once (4096 x 14336: 9.5 -> 8.9 us)
+        wc[s] = __builtin_nontemporal_load((const v4i *)(rec + (uint32_t)lane * 16u));
+        wd[s] = __builtin_nontemporal_load(
+            (const v4i *)(pad ? hdr + kHeaderBytes - 16 : rec + 1024 + (uint32_t)(lane & 15) * 16u));
     };
     float y = 0.0f;
     if (q0 < q1) {
